@@ -1,0 +1,337 @@
+/*
+ * kivi_oracle.c -- plain, slow CPU oracle for KIVI packed-KV decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY (see kivi_oracle.h).  Built with gcc, -O2,
+ * -ffp-contract=off and no fast-math, so every float operation below is one
+ * IEEE-754 binary32 (or binary64) operation in the order written.
+ *
+ * Method source: web page "Literature audit -- Group 2 (KV-cache compression
+ * primary sources)", section "1. KIVI -- kivi2024", list "Core algorithm
+ * (implementation-grade)"; "KIVI item N" below means item N of that list.
+ *
+ * Points the page leaves open, and the reading taken here:
+ *   - round(): round half to even (rintf in the default rounding mode).
+ *   - (X - z)/s: true IEEE fp32 division.
+ *   - max == min gives s = 0: all codes 0, zero = min, no division.
+ *   - codes are clamped to [0, 2^B - 1] (provably a no-op for finite input).
+ *   - scale and zero are stored as fp32.
+ *   - prefill with t % R == 0 quantizes every key (the prose rule "keep the
+ *     last t mod R keys"), leaving the key window empty.
+ *   - the cache is updated before attention runs, so attention sees all t
+ *     tokens, the newest included.
+ *   - the mask is additive, one fp32 per (batch row, token); a row whose
+ *     every score is -inf yields a zero output.
+ *   - GQA: query head hq reads KV head hq / (Hq / H).
+ *   - scores are divided by sqrt(head_dim).
+ */
+#include "kivi_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ fp16 */
+
+float kivi_oracle_half_to_float(uint16_t h) {
+  /* binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+  int sign = (h >> 15) & 1;
+  int expo = (h >> 10) & 0x1f;
+  int frac = h & 0x3ff;
+  double v;
+  if (expo == 0) {
+    v = ldexp((double)frac, -24);                 /* subnormal: frac * 2^-24 */
+  } else if (expo == 31) {
+    v = frac ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(1024 + frac), expo - 25);  /* (1 + frac/1024) 2^(e-15) */
+  }
+  return (float)(sign ? -v : v);                  /* exact: 11 bits fit */
+}
+
+/* -------------------------------------------------------------- quantizer */
+
+/* KIVI item 1: z = min(X), s = (max(X) - min(X)) / (2^B - 1),
+ * Q = round((X - z) / s).  All arithmetic in fp32. */
+void kivi_oracle_quantize_group(const float *x, int n, int bits, uint8_t *codes,
+                                float *scale, float *zero) {
+  float mn = x[0], mx = x[0];
+  for (int i = 1; i < n; ++i) {
+    if (x[i] < mn) mn = x[i];
+    if (x[i] > mx) mx = x[i];
+  }
+  const int qmax = (1 << bits) - 1;
+  const float s = (mx - mn) / (float)qmax;
+  const float z = mn;
+  for (int i = 0; i < n; ++i) {
+    int q = 0;
+    if (s != 0.0f) {
+      float r = rintf((x[i] - z) / s);
+      q = (int)r;
+      if (q < 0) q = 0;
+      if (q > qmax) q = qmax;
+    }
+    codes[i] = (uint8_t)q;
+  }
+  *scale = s;
+  *zero = z;
+}
+
+/* KIVI item 1: dequantization Q*s + z, as an fp32 product then an fp32 sum. */
+float kivi_oracle_dequant(uint32_t code, float scale, float zero) {
+  float p = (float)code * scale;
+  return p + zero;
+}
+
+/* ---------------------------------------------------------------- packing */
+
+void kivi_oracle_pack_codes(const uint8_t *codes, int n, int bits, uint32_t *words) {
+  const int per_word = 32 / bits;
+  const int n_words = (n + per_word - 1) / per_word;
+  for (int w = 0; w < n_words; ++w) words[w] = 0;
+  for (int e = 0; e < n; ++e)
+    words[e / per_word] |= (uint32_t)codes[e] << (bits * (e % per_word));
+}
+
+void kivi_oracle_unpack_codes(const uint32_t *words, int n, int bits, uint8_t *codes) {
+  const int per_word = 32 / bits;
+  const uint32_t mask = (1u << bits) - 1u;
+  for (int e = 0; e < n; ++e)
+    codes[e] = (uint8_t)((words[e / per_word] >> (bits * (e % per_word))) & mask);
+}
+
+/* Code of element e in a packed run (same bit order as the packer above). */
+static uint32_t code_at(const uint32_t *words, int e, int bits) {
+  const int per_word = 32 / bits;
+  return (words[e / per_word] >> (bits * (e % per_word))) & ((1u << bits) - 1u);
+}
+
+/* ---------------------------------------------------------------- layout */
+
+static int bits_ok(int bits) { return bits == 2 || bits == 4; }
+
+static int shape_ok(int D, int bits, int G) {
+  return bits_ok(bits) && G > 0 && D > 0 && (G % (32 / bits)) == 0 &&
+         (D % G) == 0 && G <= 256;
+}
+
+/* Quantize one key group -- G consecutive tokens of channel c -- and store it
+ * at group index g of the (b,h) slab.  KIVI item 2. */
+static void put_key_group(const float *x, int bits, int G, int D, int64_t cap,
+                          int64_t bh, int64_t g, int c, uint32_t *codes,
+                          float *scale, float *zero) {
+  uint8_t q[256];
+  float s, z;
+  kivi_oracle_quantize_group(x, G, bits, q, &s, &z);
+  const int64_t words = (int64_t)G * bits / 32;
+  const int64_t sz = (bh * (cap / G) + g) * D + c;
+  kivi_oracle_pack_codes(q, G, bits, codes + sz * words);
+  scale[sz] = s;
+  zero[sz] = z;
+}
+
+/* Quantize one value row -- all D channels of token tau, in groups of G
+ * consecutive channels -- and store it at row tau.  KIVI item 3. */
+static void put_value_row(const float *x, int bits, int G, int D, int64_t cap,
+                          int64_t bh, int64_t tau, uint32_t *codes,
+                          float *scale, float *zero) {
+  uint8_t q[1024];
+  const int64_t words = (int64_t)D * bits / 32;
+  for (int g = 0; g < D / G; ++g) {
+    float s, z;
+    kivi_oracle_quantize_group(x + g * G, G, bits, q + g * G, &s, &z);
+    scale[(bh * (D / G) + g) * cap + tau] = s;
+    zero[(bh * (D / G) + g) * cap + tau] = z;
+  }
+  kivi_oracle_pack_codes(q, D, bits, codes + (bh * cap + tau) * words);
+}
+
+int kivi_oracle_pack_keys(const uint16_t *k, int B, int H, int64_t T, int D,
+                          int bits, int G, uint32_t *codes, float *scale,
+                          float *zero, int64_t cap, int64_t off) {
+  if (!shape_ok(D, bits, G) || T < 0 || T % G || off < 0 || off % G ||
+      cap % G || off + T > cap)
+    return -1;
+  float x[256];
+  for (int64_t bh = 0; bh < (int64_t)B * H; ++bh)
+    for (int64_t g = 0; g < T / G; ++g)
+      for (int c = 0; c < D; ++c) {
+        for (int i = 0; i < G; ++i)
+          x[i] = kivi_oracle_half_to_float(k[(bh * T + g * G + i) * D + c]);
+        put_key_group(x, bits, G, D, cap, bh, off / G + g, c, codes, scale, zero);
+      }
+  return 0;
+}
+
+int kivi_oracle_pack_values(const uint16_t *v, int B, int H, int64_t T, int D,
+                            int bits, int G, uint32_t *codes, float *scale,
+                            float *zero, int64_t cap, int64_t off) {
+  if (!shape_ok(D, bits, G) || D > 1024 || T < 0 || off < 0 || off + T > cap)
+    return -1;
+  float x[1024];
+  for (int64_t bh = 0; bh < (int64_t)B * H; ++bh)
+    for (int64_t tau = 0; tau < T; ++tau) {
+      for (int c = 0; c < D; ++c)
+        x[c] = kivi_oracle_half_to_float(v[(bh * T + tau) * D + c]);
+      put_value_row(x, bits, G, D, cap, bh, off + tau, codes, scale, zero);
+    }
+  return 0;
+}
+
+/* ------------------------------------------------------------- the cache */
+
+static int cache_ok(const kivi_oracle_cache *c) {
+  return c && shape_ok(c->head_dim, c->k_bits, c->group) &&
+         shape_ok(c->head_dim, c->v_bits, c->group) && c->head_dim <= 1024 &&
+         c->residual > 0 && c->residual % c->group == 0 &&
+         c->capacity % c->group == 0 && c->n_tokens >= 0 &&
+         c->n_tokens <= c->capacity;
+}
+
+/* KIVI item 4, one token at a time.  For each arriving token tau:
+ *   values: the fp16 queue holds the last min(tau, R) values; adding tau
+ *           would make R+1, so when tau >= R the oldest (token tau-R, in slot
+ *           tau % R) is popped and quantized first;
+ *   both:   the new key and value go into slot tau % R;
+ *   keys:   the fp16 key buffer holds tokens [tau - tau%R, tau]; when it holds
+ *           R tokens the whole block is quantized and the buffer empties. */
+int kivi_oracle_append(kivi_oracle_cache *c, const uint16_t *k_new,
+                       const uint16_t *v_new, int64_t n_new) {
+  if (!cache_ok(c) || n_new < 0 || c->n_tokens + n_new > c->capacity) return -1;
+  const int D = c->head_dim, G = c->group, R = c->residual;
+  const int64_t BH = (int64_t)c->batch * c->n_kv_heads, cap = c->capacity;
+  float *x = (float *)malloc(sizeof(float) * (size_t)(R > D ? R : D));
+  if (!x) return -1;
+  for (int64_t i = 0; i < n_new; ++i) {
+    const int64_t tau = c->n_tokens;
+    const int64_t slot = tau % R;
+    for (int64_t bh = 0; bh < BH; ++bh) {
+      uint16_t *kres = c->k_res + bh * R * D;
+      uint16_t *vres = c->v_res + bh * R * D;
+      if (tau >= R) {  /* value queue would reach R+1: pop token tau-R */
+        for (int ch = 0; ch < D; ++ch) x[ch] = kivi_oracle_half_to_float(vres[slot * D + ch]);
+        put_value_row(x, c->v_bits, G, D, cap, bh, tau - R, c->v_codes,
+                      c->v_scale, c->v_zero);
+      }
+      memcpy(kres + slot * D, k_new + (bh * n_new + i) * D, sizeof(uint16_t) * D);
+      memcpy(vres + slot * D, v_new + (bh * n_new + i) * D, sizeof(uint16_t) * D);
+      if ((tau + 1) % R == 0) {  /* key buffer holds R tokens: quantize all */
+        const int64_t first = tau + 1 - R;
+        for (int ch = 0; ch < D; ++ch)
+          for (int g = 0; g < R / G; ++g) {
+            for (int j = 0; j < G; ++j)
+              x[j] = kivi_oracle_half_to_float(kres[(int64_t)(g * G + j) * D + ch]);
+            put_key_group(x, c->k_bits, G, D, cap, bh, first / G + g, ch,
+                          c->k_codes, c->k_scale, c->k_zero);
+          }
+      }
+    }
+    c->n_tokens = tau + 1;
+  }
+  free(x);
+  return 0;
+}
+
+/* Key tau of (bh) as the attention sees it: dequantized if its R-block has
+ * been quantized, else the fp16 value from the window. */
+static float key_at(const kivi_oracle_cache *c, int64_t bh, int64_t tau, int ch) {
+  const int64_t t = c->n_tokens, R = c->residual, G = c->group, D = c->head_dim;
+  const int64_t n_kq = t - t % R;
+  if (tau < n_kq) {
+    const int64_t words = G * c->k_bits / 32;
+    const int64_t sz = (bh * (c->capacity / G) + tau / G) * D + ch;
+    const uint32_t q = code_at(c->k_codes + sz * words, (int)(tau % G), c->k_bits);
+    return kivi_oracle_dequant(q, c->k_scale[sz], c->k_zero[sz]);
+  }
+  return kivi_oracle_half_to_float(c->k_res[(bh * R + tau % R) * D + ch]);
+}
+
+static float value_at(const kivi_oracle_cache *c, int64_t bh, int64_t tau, int ch) {
+  const int64_t t = c->n_tokens, R = c->residual, G = c->group, D = c->head_dim;
+  const int64_t n_vq = t > R ? t - R : 0;
+  if (tau < n_vq) {
+    const int64_t words = D * c->v_bits / 32;
+    const uint32_t q = code_at(c->v_codes + (bh * c->capacity + tau) * words, ch, c->v_bits);
+    const int64_t sz = (bh * (D / G) + ch / G) * c->capacity + tau;
+    return kivi_oracle_dequant(q, c->v_scale[sz], c->v_zero[sz]);
+  }
+  return kivi_oracle_half_to_float(c->v_res[(bh * R + tau % R) * D + ch]);
+}
+
+int kivi_oracle_materialize(const kivi_oracle_cache *c, float *k_hat, float *v_hat) {
+  if (!cache_ok(c)) return -1;
+  const int64_t BH = (int64_t)c->batch * c->n_kv_heads, t = c->n_tokens;
+  const int D = c->head_dim;
+  for (int64_t bh = 0; bh < BH; ++bh)
+    for (int64_t tau = 0; tau < t; ++tau)
+      for (int ch = 0; ch < D; ++ch) {
+        if (k_hat) k_hat[(bh * t + tau) * D + ch] = key_at(c, bh, tau, ch);
+        if (v_hat) v_hat[(bh * t + tau) * D + ch] = value_at(c, bh, tau, ch);
+      }
+  return 0;
+}
+
+/* KIVI item 5 for one (batch row, query head): scores q.K^T / sqrt(d) over
+ * every cached key (quantized ones dequantized, window ones in fp16), plus the
+ * mask, softmax, then the probability-weighted sum of the values.  The page's
+ * concat / split into quantized and full-precision parts is a partition of
+ * the same sums.  Element values are fp32; sums are fp64. */
+static int attend_one(const kivi_oracle_cache *c, const uint16_t *q, int n_q_heads,
+                      const float *mask, int b, int hq, double *score, float *out) {
+  const int D = c->head_dim;
+  const int64_t t = c->n_tokens;
+  const int n_rep = n_q_heads / c->n_kv_heads;
+  const int64_t bh = (int64_t)b * c->n_kv_heads + hq / n_rep;
+  float qv[1024];
+  for (int ch = 0; ch < D; ++ch)
+    qv[ch] = kivi_oracle_half_to_float(q[((int64_t)b * n_q_heads + hq) * D + ch]);
+  double m = -INFINITY;
+  for (int64_t tau = 0; tau < t; ++tau) {
+    double acc = 0.0;
+    for (int ch = 0; ch < D; ++ch) acc += (double)qv[ch] * (double)key_at(c, bh, tau, ch);
+    acc = acc / sqrt((double)D);
+    if (mask) acc += (double)mask[(int64_t)b * t + tau];
+    score[tau] = acc;
+    if (acc > m) m = acc;
+  }
+  for (int ch = 0; ch < D; ++ch) out[ch] = 0.0f;
+  if (t == 0 || m == -INFINITY) return 0;  /* empty or fully masked row */
+  double l = 0.0;
+  for (int64_t tau = 0; tau < t; ++tau) {
+    score[tau] = exp(score[tau] - m);
+    l += score[tau];
+  }
+  double o[1024];
+  for (int ch = 0; ch < D; ++ch) o[ch] = 0.0;
+  for (int64_t tau = 0; tau < t; ++tau) {
+    const double p = score[tau] / l;
+    for (int ch = 0; ch < D; ++ch) o[ch] += p * (double)value_at(c, bh, tau, ch);
+  }
+  for (int ch = 0; ch < D; ++ch) out[ch] = (float)o[ch];
+  return 0;
+}
+
+int kivi_oracle_decode_attn_heads(const kivi_oracle_cache *c, const uint16_t *q,
+                                  int n_q_heads, const float *mask, int b,
+                                  int h0, int h1, float *out) {
+  if (!cache_ok(c) || n_q_heads <= 0 || n_q_heads % c->n_kv_heads || b < 0 ||
+      b >= c->batch || h0 < 0 || h1 > n_q_heads || h0 > h1)
+    return -1;
+  double *score = (double *)malloc(sizeof(double) * (size_t)(c->n_tokens + 1));
+  if (!score) return -1;
+  for (int hq = h0; hq < h1; ++hq)
+    attend_one(c, q, n_q_heads, mask, b, hq, score, out + (int64_t)(hq - h0) * c->head_dim);
+  free(score);
+  return 0;
+}
+
+int kivi_oracle_decode_attn(const kivi_oracle_cache *c, const uint16_t *q,
+                            int n_q_heads, const float *mask, float *out) {
+  if (!cache_ok(c) || n_q_heads <= 0 || n_q_heads % c->n_kv_heads) return -1;
+  for (int b = 0; b < c->batch; ++b) {
+    int rc = kivi_oracle_decode_attn_heads(
+        c, q, n_q_heads, mask, b, 0, n_q_heads,
+        out + (int64_t)b * n_q_heads * c->head_dim);
+    if (rc) return rc;
+  }
+  return 0;
+}
