@@ -1,0 +1,331 @@
+// api.cpp -- the C ABI of libkivi.so: argument validation, planning of the
+// decode split, and kernel dispatch.  Declarations and the storage contract
+// are in include/kivi.h.
+//
+// Method source: web page "Literature audit -- Group 2 (KV-cache compression
+// primary sources)", section "1. KIVI -- kivi2024", list "Core algorithm
+// (implementation-grade)", items 1-5.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/kivi.h"
+#include "kivi_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return KIVI_OK;
+  return fail(KIVI_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool bits_ok(int bits) { return bits == 2 || bits == 4; }
+
+// Shape rules shared by every entry point.
+int check_shape(int32_t D, int32_t bits, int32_t G, const char *who) {
+  if (!bits_ok(bits)) return fail(KIVI_ERR_INVALID_ARG, "%s: bits must be 2 or 4 (got %d)", who, bits);
+  if (G <= 0 || G % (32 / bits) != 0 || G > 256)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: group %d must be a positive multiple of %d, at most 256",
+                who, G, 32 / bits);
+  if (D <= 0 || D > 256 || D % G != 0)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: head_dim %d must be a multiple of group %d, at most 256",
+                who, D, G);
+  return KIVI_OK;
+}
+
+int check_cache(const kivi_cache *c, const char *who) {
+  if (!c) return fail(KIVI_ERR_INVALID_ARG, "%s: cache is NULL", who);
+  if (c->batch <= 0 || c->n_kv_heads <= 0)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: batch and n_kv_heads must be positive", who);
+  int rc = check_shape(c->head_dim, c->k_bits, c->group, who);
+  if (rc) return rc;
+  rc = check_shape(c->head_dim, c->v_bits, c->group, who);
+  if (rc) return rc;
+  if (c->residual <= 0 || c->residual % c->group != 0)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: residual %d must be a positive multiple of group %d", who,
+                c->residual, c->group);
+  if (c->capacity <= 0 || c->capacity % c->residual != 0)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: capacity %lld must be a positive multiple of residual %d",
+                who, (long long)c->capacity, c->residual);
+  if (c->n_tokens < 0 || c->n_tokens > c->capacity)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: n_tokens %lld outside [0, capacity]", who,
+                (long long)c->n_tokens);
+  if (!c->k_codes || !c->k_scale || !c->k_zero || !c->v_codes || !c->v_scale || !c->v_zero ||
+      !c->k_res || !c->v_res)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: a cache array pointer is NULL", who);
+  return KIVI_OK;
+}
+
+int check_pack(const void *x, int32_t B, int32_t H, int64_t T, int32_t D, int32_t bits, int32_t G,
+               const void *codes, const void *scale, const void *zero, int64_t cap, int64_t off,
+               bool keys, const char *who) {
+  if (B <= 0 || H <= 0) return fail(KIVI_ERR_INVALID_ARG, "%s: B and H must be positive", who);
+  int rc = check_shape(D, bits, G, who);
+  if (rc) return rc;
+  if (T < 0 || off < 0) return fail(KIVI_ERR_INVALID_ARG, "%s: T and offset must be >= 0", who);
+  if (cap <= 0 || cap % G != 0)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: capacity %lld must be a positive multiple of group %d",
+                who, (long long)cap, G);
+  if (keys && (T % G != 0 || off % G != 0))
+    return fail(KIVI_ERR_INVALID_ARG, "%s: T (%lld) and offset (%lld) must be multiples of group %d",
+                who, (long long)T, (long long)off, G);
+  if (off + T > cap)
+    return fail(KIVI_ERR_CAPACITY, "%s: tokens [%lld, %lld) pass capacity %lld", who,
+                (long long)off, (long long)(off + T), (long long)cap);
+  if (T > 0 && (!x || !codes || !scale || !zero))
+    return fail(KIVI_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  return KIVI_OK;
+}
+
+int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
+
+constexpr int kGenericMinSplit = 256;
+constexpr int kTargetWorkgroups = 2048;
+
+struct Plan {
+  bool matrix = false;
+  int64_t n_main = 0;           // tokens [0, n_main) on the matrix kernel
+  int tps_matrix = 0;
+  int n_split_matrix = 0;
+  int64_t generic_begin = 0;    // tokens [generic_begin, t) on the scalar kernel
+  int tps_generic = 0;
+  int n_split_generic = 0;
+  int S_total = 0;
+};
+
+int head_chunks(int n_rep) { return (n_rep + 7) / 8; }
+
+// Split plan.  Deterministic in (shape, n_tokens, options).
+Plan make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
+               const kivi::DecodeArgs &a) {
+  Plan p;
+  const int64_t t = c->n_tokens;
+  const int n_rep = Hq / c->n_kv_heads;
+  p.matrix = path != KIVI_PATH_GENERIC && kivi::decode_matrix_supported(a);
+  if (p.matrix) {
+    p.n_main = (a.n_vq / 64) * 64;
+    if (p.n_main == 0) p.matrix = false;
+  }
+  const int64_t units = (int64_t)c->batch * c->n_kv_heads;
+  if (p.matrix) {
+    int64_t tps = tps_req;
+    if (tps == 0) {
+      const int64_t splits = max64(1, kTargetWorkgroups / units);
+      tps = ((p.n_main + splits - 1) / splits + 255) / 256 * 256;
+      tps = max64(tps, 256);
+    }
+    p.tps_matrix = (int)tps;
+    p.n_split_matrix = (int)((p.n_main + tps - 1) / tps);
+    p.generic_begin = p.n_main;
+  }
+  const int64_t rest = t - p.generic_begin;
+  int64_t tps = tps_req;
+  if (tps == 0) {
+    const int64_t gunits = units * head_chunks(n_rep);
+    const int64_t splits = max64(1, kTargetWorkgroups / gunits);
+    tps = ((rest + splits - 1) / splits + kGenericMinSplit - 1) / kGenericMinSplit * kGenericMinSplit;
+    tps = max64(tps, kGenericMinSplit);
+  }
+  p.tps_generic = (int)tps;
+  p.n_split_generic = (int)max64(1, (rest + tps - 1) / tps);
+  p.S_total = p.n_split_matrix + p.n_split_generic;
+  return p;
+}
+
+// Upper bound on partial slots for any n_tokens <= capacity.
+int64_t max_slots(const kivi_cache *c, int32_t tps_req) {
+  const int64_t step = tps_req > 0 ? tps_req : kGenericMinSplit;
+  // matrix splits over [0, n_main) plus scalar splits over the tail (at most
+  // 64 + 2R tokens, or the whole range when the matrix kernel is not used)
+  return (c->capacity + step - 1) / step + (64 + 2 * (int64_t)c->residual + step - 1) / step + 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kivi_status_string(int status) {
+  switch (status) {
+    case KIVI_OK: return "ok";
+    case KIVI_ERR_INVALID_ARG: return "invalid argument";
+    case KIVI_ERR_CAPACITY: return "capacity exceeded";
+    case KIVI_ERR_WORKSPACE: return "workspace too small";
+    case KIVI_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char *kivi_last_error(void) { return g_last_error.c_str(); }
+
+int kivi_pack_keys(const void *k_fp16, int32_t B, int32_t H, int64_t T, int32_t D, int32_t bits,
+                   int32_t group, uint32_t *codes, float *scale, float *zero,
+                   int64_t dst_capacity, int64_t dst_token_offset, void *stream) {
+  int rc = check_pack(k_fp16, B, H, T, D, bits, group, codes, scale, zero, dst_capacity,
+                      dst_token_offset, true, "kivi_pack_keys");
+  if (rc) return rc;
+  if (T == 0) return KIVI_OK;
+  kivi::TokenSource src{nullptr, (const uint16_t *)k_fp16, dst_token_offset, T, 1, D};
+  return hip_status(kivi::launch_key_groups(src, dst_token_offset / group, T / group,
+                                            (int64_t)B * H, bits, group, D, dst_capacity, codes,
+                                            scale, zero, (hipStream_t)stream),
+                    "kivi_pack_keys");
+}
+
+int kivi_pack_values(const void *v_fp16, int32_t B, int32_t H, int64_t T, int32_t D, int32_t bits,
+                     int32_t group, uint32_t *codes, float *scale, float *zero,
+                     int64_t dst_capacity, int64_t dst_token_offset, void *stream) {
+  int rc = check_pack(v_fp16, B, H, T, D, bits, group, codes, scale, zero, dst_capacity,
+                      dst_token_offset, false, "kivi_pack_values");
+  if (rc) return rc;
+  if (T == 0) return KIVI_OK;
+  kivi::TokenSource src{nullptr, (const uint16_t *)v_fp16, dst_token_offset, T, 1, D};
+  return hip_status(kivi::launch_value_rows(src, dst_token_offset, T, (int64_t)B * H, bits, group,
+                                            D, dst_capacity, codes, scale, zero,
+                                            (hipStream_t)stream),
+                    "kivi_pack_values");
+}
+
+int kivi_append(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp16, int64_t n_new,
+                void *stream) {
+  int rc = check_cache(c, "kivi_append");
+  if (rc) return rc;
+  if (n_new < 0) return fail(KIVI_ERR_INVALID_ARG, "kivi_append: n_new must be >= 0");
+  if (n_new == 0) return KIVI_OK;
+  if (!k_new_fp16 || !v_new_fp16) return fail(KIVI_ERR_INVALID_ARG, "kivi_append: NULL input");
+  if (c->n_tokens + n_new > c->capacity)
+    return fail(KIVI_ERR_CAPACITY, "kivi_append: %lld + %lld tokens pass capacity %lld",
+                (long long)c->n_tokens, (long long)n_new, (long long)c->capacity);
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t R = c->residual, G = c->group, D = c->head_dim;
+  const int64_t BH = (int64_t)c->batch * c->n_kv_heads;
+  const int64_t t0 = c->n_tokens, t1 = t0 + n_new;
+  const int64_t vq0 = max64(0, t0 - R), vq1 = max64(0, t1 - R);
+  const int64_t kq0 = t0 - t0 % R, kq1 = t1 - t1 % R;
+  // 1. values leaving the window (read old slots before they are reused)
+  kivi::TokenSource vsrc{c->v_res, (const uint16_t *)v_new_fp16, t0, n_new, (int32_t)R,
+                         (int32_t)D};
+  rc = hip_status(kivi::launch_value_rows(vsrc, vq0, vq1 - vq0, BH, c->v_bits, (int)G, (int)D,
+                                          c->capacity, c->v_codes, c->v_scale, c->v_zero, s),
+                  "kivi_append (values)");
+  if (rc) return rc;
+  // 2. complete R-blocks of keys
+  kivi::TokenSource ksrc{c->k_res, (const uint16_t *)k_new_fp16, t0, n_new, (int32_t)R,
+                         (int32_t)D};
+  rc = hip_status(kivi::launch_key_groups(ksrc, kq0 / G, (kq1 - kq0) / G, BH, c->k_bits, (int)G,
+                                          (int)D, c->capacity, c->k_codes, c->k_scale,
+                                          c->k_zero, s),
+                  "kivi_append (keys)");
+  if (rc) return rc;
+  // 3. the new tokens that stay in fp16 take their slots
+  rc = hip_status(kivi::launch_write_window((const uint16_t *)k_new_fp16,
+                                            (const uint16_t *)v_new_fp16, c->k_res, c->v_res, t0,
+                                            n_new, max64(kq1, t0), max64(vq1, t0), BH, (int)R,
+                                            (int)D, s),
+                  "kivi_append (window)");
+  if (rc) return rc;
+  c->n_tokens = t1;
+  return KIVI_OK;
+}
+
+size_t kivi_decode_attn_workspace_bytes_ex(const kivi_cache *c, int32_t n_q_heads,
+                                           int32_t tokens_per_split, int32_t path) {
+  if (check_cache(c, "kivi_decode_attn_workspace_bytes")) return 0;
+  if (n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0) return 0;
+  if (tokens_per_split < 0 || tokens_per_split % 64 != 0) return 0;
+  if (path < KIVI_PATH_AUTO || path > KIVI_PATH_MATRIX) return 0;
+  return (size_t)c->batch * n_q_heads * max_slots(c, tokens_per_split) * (c->head_dim + 2) *
+         sizeof(float);
+}
+
+size_t kivi_decode_attn_workspace_bytes(const kivi_cache *c, int32_t n_q_heads) {
+  return kivi_decode_attn_workspace_bytes_ex(c, n_q_heads, 0, KIVI_PATH_AUTO);
+}
+
+int kivi_decode_attn_ex(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads,
+                        const float *mask, float *out, void *workspace, size_t workspace_bytes,
+                        int32_t tokens_per_split, int32_t path, void *stream) {
+  const char *who = "kivi_decode_attn";
+  int rc = check_cache(c, who);
+  if (rc) return rc;
+  if (n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: n_q_heads %d must be a positive multiple of n_kv_heads %d",
+                who, n_q_heads, c->n_kv_heads);
+  if (!q_fp16 || !out) return fail(KIVI_ERR_INVALID_ARG, "%s: NULL q or out", who);
+  if (tokens_per_split < 0 || tokens_per_split % 64 != 0)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: tokens_per_split %d must be 0 or a positive multiple of 64",
+                who, tokens_per_split);
+  if (path < KIVI_PATH_AUTO || path > KIVI_PATH_MATRIX)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: unknown path %d", who, path);
+  const size_t need = kivi_decode_attn_workspace_bytes_ex(c, n_q_heads, tokens_per_split, path);
+  if (!workspace || workspace_bytes < need)
+    return fail(KIVI_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes,
+                need);
+
+  kivi::DecodeArgs a{};
+  a.k_codes = c->k_codes;
+  a.k_scale = c->k_scale;
+  a.k_zero = c->k_zero;
+  a.v_codes = c->v_codes;
+  a.v_scale = c->v_scale;
+  a.v_zero = c->v_zero;
+  a.k_res = c->k_res;
+  a.v_res = c->v_res;
+  a.q = (const uint16_t *)q_fp16;
+  a.mask = mask;
+  a.part = (float *)workspace;
+  a.out = out;
+  a.B = c->batch;
+  a.H = c->n_kv_heads;
+  a.D = c->head_dim;
+  a.kb = c->k_bits;
+  a.vb = c->v_bits;
+  a.G = c->group;
+  a.R = c->residual;
+  a.Hq = n_q_heads;
+  a.n_rep = n_q_heads / c->n_kv_heads;
+  a.cap = c->capacity;
+  a.t = c->n_tokens;
+  a.n_kq = a.t - a.t % a.R;
+  a.n_vq = max64(0, a.t - a.R);
+  a.sm_scale = 1.0f / sqrtf((float)a.D);
+
+  if (path == KIVI_PATH_MATRIX && !kivi::decode_matrix_supported(a))
+    return fail(KIVI_ERR_INVALID_ARG, "%s: the matrix-core kernel does not handle this shape", who);
+  const Plan p = make_plan(c, n_q_heads, tokens_per_split, path, a);
+  if (p.S_total > max_slots(c, tokens_per_split))
+    return fail(KIVI_ERR_WORKSPACE, "%s: internal split plan exceeds the workspace bound", who);
+  a.S_total = p.S_total;
+  hipStream_t s = (hipStream_t)stream;
+  if (p.matrix) {
+    rc = hip_status(kivi::launch_decode_matrix(a, p.n_main, p.tps_matrix, p.n_split_matrix, s),
+                    "kivi_decode_attn (matrix)");
+    if (rc) return rc;
+  }
+  rc = hip_status(kivi::launch_decode_generic(a, p.generic_begin, p.tps_generic,
+                                              p.n_split_generic, p.n_split_matrix, s),
+                  "kivi_decode_attn (scalar)");
+  if (rc) return rc;
+  return hip_status(kivi::launch_combine(a, s), "kivi_decode_attn (combine)");
+}
+
+int kivi_decode_attn(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, const float *mask,
+                     float *out, void *workspace, size_t workspace_bytes, void *stream) {
+  return kivi_decode_attn_ex(c, q_fp16, n_q_heads, mask, out, workspace, workspace_bytes, 0,
+                             KIVI_PATH_AUTO, stream);
+}
+
+}  // extern "C"

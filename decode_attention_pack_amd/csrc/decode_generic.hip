@@ -1,0 +1,226 @@
+// decode_generic.hip -- scalar (VALU) decode attention over the KIVI cache,
+// and the split-K log-sum-exp combine.
+//
+// Method source: web page "Literature audit -- Group 2 (KV-cache compression
+// primary sources)", section "1. KIVI -- kivi2024", list "Core algorithm
+// (implementation-grade)", item 5 (attention over quantized keys/values plus
+// the fp16 window) and item 4 (which tokens are quantized).
+//
+// This kernel handles any shape the ABI accepts.  It dequantizes one element
+// at a time and is meant for the fp16 window, ragged tails and shapes the
+// matrix-core kernel does not cover.  One workgroup owns a token range of one
+// (batch row, KV head) and up to 8 of that head's query heads, keeps an
+// online softmax (running max m, running sum l) and writes (acc[D], m, l) as
+// a partial; the combine kernel merges the partials of all splits.
+#include <math.h>
+
+#include "kivi_internal.hpp"
+
+namespace kivi {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kHeads = 8;     // query heads per workgroup
+constexpr int kChunk = 256;   // tokens per inner step (one per thread)
+
+// Key channel `c` of token `tau` as attention sees it.
+__device__ __forceinline__ float key_hat(const DecodeArgs &a, int64_t bh, int64_t tau, int c) {
+  if (tau < a.n_kq) {
+    const int per = 32 / a.kb;
+    const int words = a.G / per;
+    const int64_t g = tau / a.G;
+    const int e = (int)(tau - g * a.G);
+    const int64_t sz = (bh * (a.cap / a.G) + g) * a.D + c;
+    const uint32_t w = a.k_codes[sz * words + e / per];
+    const uint32_t code = (w >> (a.kb * (e % per))) & ((1u << a.kb) - 1u);
+    return __fadd_rn(__fmul_rn((float)code, a.k_scale[sz]), a.k_zero[sz]);
+  }
+  return h2f(a.k_res[(bh * a.R + tau % a.R) * a.D + c]);
+}
+
+// Value channel `c` of token `tau` as attention sees it.
+__device__ __forceinline__ float value_hat(const DecodeArgs &a, int64_t bh, int64_t tau, int c) {
+  if (tau < a.n_vq) {
+    const int per = 32 / a.vb;
+    const uint32_t w = a.v_codes[(bh * a.cap + tau) * (a.D / per) + c / per];
+    const uint32_t code = (w >> (a.vb * (c % per))) & ((1u << a.vb) - 1u);
+    const int64_t sz = (bh * (a.D / a.G) + c / a.G) * a.cap + tau;
+    return __fadd_rn(__fmul_rn((float)code, a.v_scale[sz]), a.v_zero[sz]);
+  }
+  return h2f(a.v_res[(bh * a.R + tau % a.R) * a.D + c]);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+}  // namespace
+
+// grid: (n_splits, H * head_chunks, B); block: 256.
+__global__ void __launch_bounds__(kThreads)
+decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int slot_base,
+                      int head_chunks) {
+  __shared__ float q_s[kHeads][256];
+  __shared__ float p_s[kHeads][kChunk];
+  __shared__ float stat_s[kHeads][2];   // new m, alpha
+  __shared__ float red_s[kThreads];
+
+  const int tid = threadIdx.x;
+  const int split = blockIdx.x;
+  const int h = blockIdx.y / head_chunks;
+  const int hc = blockIdx.y % head_chunks;
+  const int b = blockIdx.z;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int hq0 = h * a.n_rep + hc * kHeads;
+  const int nh = min(kHeads, a.n_rep - hc * kHeads);
+  const int D = a.D;
+
+  int64_t s0 = tok_begin + (int64_t)split * tokens_per_split;
+  int64_t s1 = s0 + tokens_per_split;
+  if (s1 > a.t) s1 = a.t;
+
+  for (int i = tid; i < kHeads * D; i += kThreads) {
+    const int j = i / D, c = i % D;
+    q_s[j][c] = j < nh ? h2f(a.q[((int64_t)b * a.Hq + hq0 + j) * D + c]) : 0.0f;
+  }
+
+  float m[kHeads], l[kHeads], acc[kHeads];
+#pragma unroll
+  for (int j = 0; j < kHeads; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.0f;
+    acc[j] = 0.0f;
+  }
+  const int c_own = tid % D;           // value channel owned in the V phase
+  const int n_par = kThreads / D;      // token parities sharing a channel
+  const int par = tid / D;
+  __syncthreads();
+
+  for (int64_t c0 = s0; c0 < s1; c0 += kChunk) {
+    // scores: one token per thread, all heads of the chunk at once
+    const int64_t tau = c0 + tid;
+    float sc[kHeads];
+#pragma unroll
+    for (int j = 0; j < kHeads; ++j) sc[j] = 0.0f;
+    if (tau < s1) {
+      for (int c = 0; c < D; ++c) {
+        const float k = key_hat(a, bh, tau, c);
+#pragma unroll
+        for (int j = 0; j < kHeads; ++j) sc[j] = fmaf(q_s[j][c], k, sc[j]);
+      }
+      const float mk = a.mask ? a.mask[(int64_t)b * a.t + tau] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < kHeads; ++j) sc[j] = sc[j] * a.sm_scale + mk;
+    } else {
+#pragma unroll
+      for (int j = 0; j < kHeads; ++j) sc[j] = -INFINITY;
+    }
+#pragma unroll
+    for (int j = 0; j < kHeads; ++j) p_s[j][tid] = sc[j];
+    __syncthreads();
+
+    // online softmax statistics, one wave per head
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int j = wave; j < nh; j += kThreads / 64) {
+      float cm = -INFINITY;
+      for (int i = lane; i < kChunk; i += 64) cm = fmaxf(cm, p_s[j][i]);
+      cm = wave_max(cm);
+      const float mn = fmaxf(m[j], cm);
+      float sum = 0.0f;
+      for (int i = lane; i < kChunk; i += 64) {
+        const float p = mn == -INFINITY ? 0.0f : expf(p_s[j][i] - mn);
+        p_s[j][i] = p;
+        sum += p;
+      }
+      sum = wave_sum(sum);
+      if (lane == 0) {
+        stat_s[j][0] = mn;
+        stat_s[j][1] = mn == -INFINITY ? 1.0f : expf(m[j] - mn);
+        red_s[j] = sum;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kHeads; ++j) {
+      if (j < nh) {
+        const float alpha = stat_s[j][1];
+        m[j] = stat_s[j][0];
+        l[j] = l[j] * alpha + red_s[j];
+        acc[j] *= alpha;
+      }
+    }
+
+    // values: thread owns channel c_own and every n_par-th token
+    const int64_t cend = (c0 + kChunk < s1) ? c0 + kChunk : s1;
+    for (int64_t tv = c0 + par; tv < cend; tv += n_par) {
+      const float v = value_hat(a, bh, tv, c_own);
+      const int i = (int)(tv - c0);
+#pragma unroll
+      for (int j = 0; j < kHeads; ++j) acc[j] = fmaf(p_s[j][i], v, acc[j]);
+    }
+    __syncthreads();
+  }
+
+  // merge the n_par token parities of each channel, then write the partial
+  for (int j = 0; j < nh; ++j) {
+    red_s[tid] = acc[j];
+    __syncthreads();
+    if (tid < D) {
+      float s = 0.0f;
+      for (int p = 0; p < n_par; ++p) s += red_s[p * D + tid];
+      float *dst = a.part + (((int64_t)b * a.Hq + hq0 + j) * a.S_total + slot_base + split) *
+                                (int64_t)(D + 2);
+      dst[tid] = s;
+      if (tid == 0) {
+        dst[D] = m[j];
+        dst[D + 1] = l[j];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// grid: B * Hq; block: D threads.  out = sum_i acc_i e^(m_i - M) / sum_i l_i e^(m_i - M).
+__global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
+  const int64_t row = blockIdx.x;
+  const int c = threadIdx.x;
+  const int D = a.D;
+  const float *p = a.part + row * a.S_total * (int64_t)(D + 2);
+  float M = -INFINITY;
+  for (int i = 0; i < a.S_total; ++i) M = fmaxf(M, p[i * (D + 2) + D]);
+  float L = 0.0f, o = 0.0f;
+  if (M != -INFINITY) {
+    for (int i = 0; i < a.S_total; ++i) {
+      const float mi = p[i * (D + 2) + D];
+      if (mi == -INFINITY) continue;
+      const float w = expf(mi - M);
+      L = fmaf(p[i * (D + 2) + D + 1], w, L);
+      o = fmaf(p[i * (D + 2) + c], w, o);
+    }
+  }
+  a.out[row * D + c] = L > 0.0f ? o / L : 0.0f;
+}
+
+hipError_t launch_decode_generic(const DecodeArgs &a, int64_t tok_begin, int tokens_per_split,
+                                 int n_splits, int slot_base, hipStream_t s) {
+  if (n_splits <= 0) return hipSuccess;
+  const int head_chunks = (a.n_rep + kHeads - 1) / kHeads;
+  dim3 grid((unsigned)n_splits, (unsigned)(a.H * head_chunks), (unsigned)a.B);
+  hipLaunchKernelGGL(decode_generic_kernel, grid, dim3(kThreads), 0, s, a, tok_begin,
+                     tokens_per_split, slot_base, head_chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const DecodeArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(a.B * a.Hq)), dim3((unsigned)a.D), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace kivi

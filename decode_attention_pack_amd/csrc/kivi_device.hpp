@@ -1,0 +1,51 @@
+// kivi_device.hpp -- device-side helpers shared by the KIVI HIP kernels.
+//
+// Method source: web page "Literature audit -- Group 2 (KV-cache compression
+// primary sources)", section "1. KIVI -- kivi2024", list "Core algorithm
+// (implementation-grade)" ("KIVI item N").
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kivi {
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+  return __half2float(__ushort_as_half(h));
+}
+
+// Where token tau of one (batch, head) slab comes from when it is quantized:
+// tokens below `t0` are read from the fp16 window `res` (slot tau % R); tokens
+// from `t0` on are read from the caller's input `inp`, whose row 0 is token
+// `t0`.  The pack entry points use only `inp`; append uses both.
+struct TokenSource {
+  const uint16_t *res;   // [BH][R][D] or nullptr
+  const uint16_t *inp;   // [BH][n_inp][D]
+  int64_t t0;            // first token held by `inp`
+  int64_t n_inp;         // rows of `inp` per slab
+  int32_t R;
+  int32_t D;
+  __device__ __forceinline__ const uint16_t *row(int64_t bh, int64_t tau) const {
+    if (tau < t0) return res + (bh * R + tau % R) * (int64_t)D;
+    return inp + (bh * n_inp + (tau - t0)) * (int64_t)D;
+  }
+};
+
+// KIVI item 1: the asymmetric round-to-nearest quantizer, bit-exact with an
+// fp32 CPU reference.  s = (max - min) / (2^B - 1) uses IEEE fp32 division
+// (the HIP default: correctly rounded), the code is round-half-to-even of
+// (x - min) / s, clamped to [0, 2^B - 1]; s == 0 gives code 0.
+__device__ __forceinline__ float group_scale(float mn, float mx, int bits) {
+  return (mx - mn) / (float)((1 << bits) - 1);
+}
+
+__device__ __forceinline__ uint32_t quant_code(float x, float z, float s, int bits) {
+  if (s == 0.0f) return 0u;
+  float r = rintf((x - z) / s);
+  const float qmax = (float)((1 << bits) - 1);
+  r = fminf(fmaxf(r, 0.0f), qmax);
+  return (uint32_t)r;
+}
+
+}  // namespace kivi

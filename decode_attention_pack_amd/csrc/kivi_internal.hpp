@@ -1,0 +1,64 @@
+// kivi_internal.hpp -- launchers behind the C ABI (host side declarations).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kivi_device.hpp"
+
+namespace kivi {
+
+// Quantize key groups [g_first, g_first + n_groups) of every (batch, head)
+// slab (BH slabs) from `src` into the key layout (KIVI item 2).
+hipError_t launch_key_groups(const TokenSource &src, int64_t g_first, int64_t n_groups,
+                             int64_t BH, int bits, int G, int D, int64_t cap,
+                             uint32_t *codes, float *scale, float *zero, hipStream_t s);
+
+// Quantize value rows [tau_first, tau_first + n_rows) of every slab from `src`
+// into the value layout (KIVI item 3).
+hipError_t launch_value_rows(const TokenSource &src, int64_t tau_first, int64_t n_rows,
+                             int64_t BH, int bits, int G, int D, int64_t cap,
+                             uint32_t *codes, float *scale, float *zero, hipStream_t s);
+
+// Copy new tokens into window slots: keys for tokens [k_from, t0 + n_new),
+// values for [v_from, t0 + n_new); token tau goes to slot tau % R.
+hipError_t launch_write_window(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_res,
+                               uint16_t *v_res, int64_t t0, int64_t n_new, int64_t k_from,
+                               int64_t v_from, int64_t BH, int R, int D, hipStream_t s);
+
+// Everything the decode kernels read.
+struct DecodeArgs {
+  const uint32_t *k_codes;
+  const float *k_scale;
+  const float *k_zero;
+  const uint32_t *v_codes;
+  const float *v_scale;
+  const float *v_zero;
+  const uint16_t *k_res;
+  const uint16_t *v_res;
+  const uint16_t *q;     // [B][Hq][D]
+  const float *mask;     // [B][t] or nullptr
+  float *part;           // partials [B][Hq][S_total][D + 2]: acc[D], m, l
+  float *out;            // [B][Hq][D]
+  int32_t B, H, D, kb, vb, G, R, Hq, n_rep;
+  int64_t cap, t, n_kq, n_vq;
+  float sm_scale;        // 1 / sqrt(D)
+  int32_t S_total;       // partial slots per (b, hq)
+};
+
+// Scalar kernel over tokens [tok_begin, t): `n_splits` splits of
+// `tokens_per_split`, writing partial slots [slot_base, slot_base + n_splits).
+hipError_t launch_decode_generic(const DecodeArgs &a, int64_t tok_begin, int tokens_per_split,
+                                 int n_splits, int slot_base, hipStream_t s);
+
+// Matrix-core kernel over tokens [0, n_main) (n_main % 64 == 0), writing
+// partial slots [0, n_splits).  Returns hipErrorInvalidValue for shapes it
+// does not handle.
+bool decode_matrix_supported(const DecodeArgs &a);
+hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int tokens_per_split,
+                                int n_splits, hipStream_t s);
+
+// Log-sum-exp merge of the S_total partial slots into `out`.
+hipError_t launch_combine(const DecodeArgs &a, hipStream_t s);
+
+}  // namespace kivi

@@ -1,0 +1,135 @@
+// pack.hip -- KIVI quantize-and-pack kernels for keys and values, and the
+// fp16 window copy used by append.
+//
+// Method source: web page "Literature audit -- Group 2 (KV-cache compression
+// primary sources)", section "1. KIVI -- kivi2024", list "Core algorithm
+// (implementation-grade)", items 1-4.
+#include "kivi_internal.hpp"
+
+namespace kivi {
+
+// KIVI item 2: one thread per (channel, key group).  A key group is G
+// consecutive tokens of one channel; its codes are packed along tokens.
+// Two passes over the group's tokens (min/max, then codes) keep the kernel
+// free of per-thread arrays; the second pass hits the caches.
+__global__ void __launch_bounds__(128)
+key_groups_kernel(TokenSource src, int64_t g_first, int bits, int G, int D, int64_t cap,
+                  uint32_t *__restrict__ codes, float *__restrict__ scale,
+                  float *__restrict__ zero) {
+  const int64_t bh = blockIdx.y;
+  const int64_t g = g_first + blockIdx.x;
+  const int64_t tau0 = g * G;
+  const int per = 32 / bits;
+  const int words = G / per;
+  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    float mn = h2f(src.row(bh, tau0)[c]);
+    float mx = mn;
+    for (int i = 1; i < G; ++i) {
+      const float x = h2f(src.row(bh, tau0 + i)[c]);
+      mn = x < mn ? x : mn;
+      mx = x > mx ? x : mx;
+    }
+    const float s = group_scale(mn, mx, bits);
+    const int64_t sz = (bh * (cap / G) + g) * D + c;
+    uint32_t *dst = codes + sz * words;
+    for (int w = 0; w < words; ++w) {
+      uint32_t word = 0;
+      for (int e = 0; e < per; ++e) {
+        const float x = h2f(src.row(bh, tau0 + w * per + e)[c]);
+        word |= quant_code(x, mn, s, bits) << (bits * e);
+      }
+      dst[w] = word;
+    }
+    scale[sz] = s;
+    zero[sz] = mn;
+  }
+}
+
+// KIVI item 3: one thread per (token, value group).  A value group is G
+// consecutive channels of one token; its codes are packed along channels.
+__global__ void __launch_bounds__(256)
+value_rows_kernel(TokenSource src, int64_t tau_first, int64_t n_rows, int bits, int G, int D,
+                  int64_t cap, uint32_t *__restrict__ codes, float *__restrict__ scale,
+                  float *__restrict__ zero) {
+  const int64_t bh = blockIdx.y;
+  const int64_t r = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+  if (r >= n_rows) return;
+  const int64_t tau = tau_first + r;
+  const int per = 32 / bits;
+  const int n_groups = D / G;
+  const uint16_t *row = src.row(bh, tau);
+  uint32_t *dst = codes + (bh * cap + tau) * (int64_t)(D / per);
+  for (int g = threadIdx.x >> 6; g < n_groups; g += 4) {
+    float mn = h2f(row[g * G]);
+    float mx = mn;
+    for (int i = 1; i < G; ++i) {
+      const float x = h2f(row[g * G + i]);
+      mn = x < mn ? x : mn;
+      mx = x > mx ? x : mx;
+    }
+    const float s = group_scale(mn, mx, bits);
+    for (int w = 0; w < G / per; ++w) {
+      uint32_t word = 0;
+      for (int e = 0; e < per; ++e)
+        word |= quant_code(h2f(row[g * G + w * per + e]), mn, s, bits) << (bits * e);
+      dst[(g * G) / per + w] = word;
+    }
+    scale[(bh * n_groups + g) * cap + tau] = s;
+    zero[(bh * n_groups + g) * cap + tau] = mn;
+  }
+}
+
+// Copy rows of the new keys / values into their window slots.
+__global__ void __launch_bounds__(256)
+write_window_kernel(const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
+                    uint16_t *__restrict__ k_res, uint16_t *__restrict__ v_res, int64_t t0,
+                    int64_t n_new, int64_t k_from, int64_t v_from, int R, int D) {
+  const int64_t bh = blockIdx.y;
+  const int64_t t1 = t0 + n_new;
+  const int64_t lo = k_from < v_from ? k_from : v_from;
+  const int64_t first = lo > t0 ? lo : t0;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t tau = first + idx / D;
+  const int c = (int)(idx % D);
+  if (tau >= t1) return;
+  const int64_t srow = (bh * n_new + (tau - t0)) * D + c;
+  const int64_t drow = (bh * R + tau % R) * D + c;
+  if (tau >= k_from) k_res[drow] = k_new[srow];
+  if (tau >= v_from) v_res[drow] = v_new[srow];
+}
+
+hipError_t launch_key_groups(const TokenSource &src, int64_t g_first, int64_t n_groups,
+                             int64_t BH, int bits, int G, int D, int64_t cap,
+                             uint32_t *codes, float *scale, float *zero, hipStream_t s) {
+  if (n_groups <= 0 || BH <= 0) return hipSuccess;
+  dim3 grid((unsigned)n_groups, (unsigned)BH);
+  hipLaunchKernelGGL(key_groups_kernel, grid, dim3(128), 0, s, src, g_first, bits, G, D, cap,
+                     codes, scale, zero);
+  return hipGetLastError();
+}
+
+hipError_t launch_value_rows(const TokenSource &src, int64_t tau_first, int64_t n_rows,
+                             int64_t BH, int bits, int G, int D, int64_t cap,
+                             uint32_t *codes, float *scale, float *zero, hipStream_t s) {
+  if (n_rows <= 0 || BH <= 0) return hipSuccess;
+  dim3 grid((unsigned)((n_rows + 63) / 64), (unsigned)BH);
+  hipLaunchKernelGGL(value_rows_kernel, grid, dim3(256), 0, s, src, tau_first, n_rows, bits, G,
+                     D, cap, codes, scale, zero);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_window(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_res,
+                               uint16_t *v_res, int64_t t0, int64_t n_new, int64_t k_from,
+                               int64_t v_from, int64_t BH, int R, int D, hipStream_t s) {
+  const int64_t t1 = t0 + n_new;
+  int64_t lo = k_from < v_from ? k_from : v_from;
+  if (lo < t0) lo = t0;
+  const int64_t n = (t1 - lo) * D;
+  if (n <= 0 || BH <= 0) return hipSuccess;
+  dim3 grid((unsigned)((n + 255) / 256), (unsigned)BH);
+  hipLaunchKernelGGL(write_window_kernel, grid, dim3(256), 0, s, k_new, v_new, k_res, v_res, t0,
+                     n_new, k_from, v_from, R, D);
+  return hipGetLastError();
+}
+
+}  // namespace kivi

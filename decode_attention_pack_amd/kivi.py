@@ -1,0 +1,217 @@
+"""Thin ctypes binding over libkivi.so (include/kivi.h).
+
+Argument marshalling only: torch tensors are checked for device, dtype, shape
+and contiguity, then their device pointers and the current HIP stream are
+handed to the C ABI.  Every step of the computation runs in the library's HIP
+kernels; there is no fallback.  If libkivi.so is missing the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkivi.so")
+
+KIVI_OK = 0
+KIVI_ERR_INVALID_ARG = -1
+KIVI_ERR_CAPACITY = -2
+KIVI_ERR_WORKSPACE = -3
+KIVI_ERR_HIP = -4
+KIVI_PATH_AUTO, KIVI_PATH_GENERIC, KIVI_PATH_MATRIX = 0, 1, 2
+
+EXPORTED = ("kivi_pack_keys", "kivi_pack_values", "kivi_append", "kivi_decode_attn",
+            "kivi_decode_attn_ex", "kivi_decode_attn_workspace_bytes",
+            "kivi_decode_attn_workspace_bytes_ex", "kivi_status_string", "kivi_last_error")
+
+
+class KiviError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{detail} (status {status})")
+        self.status = status
+
+
+class CCache(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32), ("group", ctypes.c_int32),
+        ("residual", ctypes.c_int32),
+        ("capacity", ctypes.c_int64), ("n_tokens", ctypes.c_int64),
+        ("k_codes", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("k_zero", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p), ("v_scale", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
+        ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libkivi.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m decode_attention_pack_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    for name in ("kivi_pack_keys", "kivi_pack_values"):
+        fn = getattr(L, name)
+        fn.argtypes = [P, i32, i32, i64, i32, i32, i32, P, P, P, i64, i64, P]
+        fn.restype = ctypes.c_int
+    L.kivi_append.argtypes = [ctypes.POINTER(CCache), P, P, i64, P]
+    L.kivi_append.restype = ctypes.c_int
+    L.kivi_decode_attn.argtypes = [ctypes.POINTER(CCache), P, i32, P, P, P, sz, P]
+    L.kivi_decode_attn.restype = ctypes.c_int
+    L.kivi_decode_attn_ex.argtypes = [ctypes.POINTER(CCache), P, i32, P, P, P, sz, i32, i32, P]
+    L.kivi_decode_attn_ex.restype = ctypes.c_int
+    L.kivi_decode_attn_workspace_bytes.argtypes = [ctypes.POINTER(CCache), i32]
+    L.kivi_decode_attn_workspace_bytes.restype = sz
+    L.kivi_decode_attn_workspace_bytes_ex.argtypes = [ctypes.POINTER(CCache), i32, i32, i32]
+    L.kivi_decode_attn_workspace_bytes_ex.restype = sz
+    L.kivi_status_string.argtypes = [ctypes.c_int]
+    L.kivi_status_string.restype = ctypes.c_char_p
+    L.kivi_last_error.argtypes = []
+    L.kivi_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != KIVI_OK:
+        raise KiviError(status, lib().kivi_last_error().decode())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _dev(t: torch.Tensor, dtype, shape, name):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def layout_shapes(B, H, D, kb, vb, G, R, cap):
+    """Shapes of the cache arrays (include/kivi.h storage layout)."""
+    return {
+        "k_codes": (B, H, cap // G, D, G * kb // 32),
+        "k_scale": (B, H, cap // G, D),
+        "k_zero": (B, H, cap // G, D),
+        "v_codes": (B, H, cap, D * vb // 32),
+        "v_scale": (B, H, D // G, cap),
+        "v_zero": (B, H, D // G, cap),
+        "k_res": (B, H, R, D),
+        "v_res": (B, H, R, D),
+    }
+
+
+_DT = {"k_codes": torch.int32, "k_scale": torch.float32, "k_zero": torch.float32,
+       "v_codes": torch.int32, "v_scale": torch.float32, "v_zero": torch.float32,
+       "k_res": torch.float16, "v_res": torch.float16}
+_ORDER = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_res", "v_res")
+
+
+class Cache:
+    """A KIVI cache in device memory (torch tensors) plus its C descriptor.
+
+    Codes are stored in int32 tensors holding the u32 words bit for bit.
+    """
+
+    def __init__(self, batch, n_kv_heads, head_dim, k_bits, v_bits, group, residual, capacity,
+                 device="cuda", arrays=None):
+        self.B, self.H, self.D = batch, n_kv_heads, head_dim
+        self.kb, self.vb, self.G, self.R, self.cap = k_bits, v_bits, group, residual, capacity
+        shapes = layout_shapes(batch, n_kv_heads, head_dim, k_bits, v_bits, group, residual,
+                               capacity)
+        if arrays is None:
+            arrays = {n: torch.empty(s, dtype=_DT[n], device=device) for n, s in shapes.items()}
+        for n in _ORDER:
+            _dev(arrays[n], _DT[n], shapes[n], n)
+        self.arrays = arrays
+        self.c = CCache(batch, n_kv_heads, head_dim, k_bits, v_bits, group, residual, capacity, 0,
+                        *[arrays[n].data_ptr() for n in _ORDER])
+
+    def __getattr__(self, name):
+        arrays = self.__dict__.get("arrays")
+        if arrays is not None and name in arrays:
+            return arrays[name]
+        raise AttributeError(name)
+
+    @property
+    def n_tokens(self) -> int:
+        return int(self.c.n_tokens)
+
+    def workspace_bytes(self, n_q_heads, tokens_per_split=0, path=KIVI_PATH_AUTO) -> int:
+        n = lib().kivi_decode_attn_workspace_bytes_ex(ctypes.byref(self.c), n_q_heads,
+                                                      tokens_per_split, path)
+        if n == 0:
+            raise KiviError(KIVI_ERR_INVALID_ARG, "invalid workspace query")
+        return int(n)
+
+    def new_workspace(self, n_q_heads, tokens_per_split=0, path=KIVI_PATH_AUTO):
+        n = self.workspace_bytes(n_q_heads, tokens_per_split, path)
+        return torch.empty(n, dtype=torch.uint8, device=self.k_codes.device)
+
+
+def kivi_pack_keys(k, bits, group, codes, scale, zero, dst_capacity, dst_token_offset=0,
+                   stream=None):
+    B, H, T, D = k.shape
+    shp = layout_shapes(B, H, D, bits, bits, group, 1, dst_capacity)
+    args = [_dev(k, torch.float16, None, "k"), B, H, T, D, bits, group,
+            _dev(codes, torch.int32, shp["k_codes"], "codes"),
+            _dev(scale, torch.float32, shp["k_scale"], "scale"),
+            _dev(zero, torch.float32, shp["k_zero"], "zero"), dst_capacity, dst_token_offset,
+            _stream(stream)]
+    _check(lib().kivi_pack_keys(*args))
+
+
+def kivi_pack_values(v, bits, group, codes, scale, zero, dst_capacity, dst_token_offset=0,
+                     stream=None):
+    B, H, T, D = v.shape
+    shp = layout_shapes(B, H, D, bits, bits, group, 1, dst_capacity)
+    args = [_dev(v, torch.float16, None, "v"), B, H, T, D, bits, group,
+            _dev(codes, torch.int32, shp["v_codes"], "codes"),
+            _dev(scale, torch.float32, shp["v_scale"], "scale"),
+            _dev(zero, torch.float32, shp["v_zero"], "zero"), dst_capacity, dst_token_offset,
+            _stream(stream)]
+    _check(lib().kivi_pack_values(*args))
+
+
+def kivi_append(cache: Cache, k_new, v_new, stream=None):
+    n = k_new.shape[2]
+    shape = (cache.B, cache.H, n, cache.D)
+    kp = _dev(k_new, torch.float16, shape, "k_new")
+    vp = _dev(v_new, torch.float16, shape, "v_new")
+    _check(lib().kivi_append(ctypes.byref(cache.c), kp, vp, n, _stream(stream)))
+
+
+def kivi_decode_attn(cache: Cache, q, mask=None, out=None, workspace=None, tokens_per_split=0,
+                     path=KIVI_PATH_AUTO, stream=None):
+    B, Hq, D = q.shape
+    qp = _dev(q, torch.float16, (cache.B, Hq, cache.D), "q")
+    mp = None
+    if mask is not None:
+        mp = _dev(mask, torch.float32, (cache.B, cache.n_tokens), "mask")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    op = _dev(out, torch.float32, (cache.B, Hq, cache.D), "out")
+    if workspace is None:
+        workspace = cache.new_workspace(Hq, tokens_per_split, path)
+    wp = _dev(workspace, torch.uint8, None, "workspace")
+    _check(lib().kivi_decode_attn_ex(ctypes.byref(cache.c), qp, Hq, mp, op, wp,
+                                     workspace.numel(), tokens_per_split, path, _stream(stream)))
+    return out

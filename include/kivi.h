@@ -1,0 +1,176 @@
+/*
+ * kivi.h -- C ABI of libkivi.so: KIVI 2/4-bit packed KV cache and decode
+ * attention read straight from it, for AMD Instinct MI355X (gfx950).
+ *
+ * Method source: web page "Literature audit -- Group 2 (KV-cache compression
+ * primary sources)", section "1. KIVI -- kivi2024", list "Core algorithm
+ * (implementation-grade)", items 1-6 ("KIVI item N" below), and the same
+ * section's note that the released code supports grouped-query attention.
+ *
+ * Conventions for every call
+ *   - Pointers marked (device) are HIP device pointers; everything else is
+ *     host memory.  The caller owns every buffer; the library allocates and
+ *     frees nothing.
+ *   - fp16 tensors are IEEE binary16, passed as untyped pointers.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default
+ *     stream.  Calls enqueue kernels and return without synchronizing.
+ *   - Arguments are validated on the host before any HIP call.  A rejected
+ *     call returns a negative status, enqueues nothing and changes nothing;
+ *     kivi_last_error() then describes the failure (per thread).
+ *   - Results are deterministic: no floating-point atomics, and the split of
+ *     the token range is a fixed function of the shape.
+ *
+ * Storage layout of a cache (b < batch, h < n_kv_heads, G = group,
+ * D = head_dim, R = residual, cap = capacity, kb/vb = key/value bits):
+ *   k_codes  u32 [B][H][cap/G][D][G*kb/32]  key group g of channel c: token
+ *                                           e (0 <= e < G) in word e/(32/kb),
+ *                                           bits kb*(e % (32/kb)) (KIVI item
+ *                                           2: per-channel groups of G
+ *                                           tokens, packed along tokens)
+ *   k_scale  f32 [B][H][cap/G][D]           one scale and one zero per key
+ *   k_zero   f32 [B][H][cap/G][D]           group
+ *   v_codes  u32 [B][H][cap][D*vb/32]       value token tau: channel e in
+ *                                           word e/(32/vb), bits vb*(e %
+ *                                           (32/vb)) (KIVI item 3: per-token
+ *                                           groups of G channels, packed
+ *                                           along channels)
+ *   v_scale  f32 [B][H][D/G][cap]           one scale and one zero per value
+ *   v_zero   f32 [B][H][D/G][cap]           group
+ *   k_res    fp16 [B][H][R][D]              the fp16 residual window (KIVI
+ *   v_res    fp16 [B][H][R][D]              item 4); token tau lives in slot
+ *                                           tau % R
+ * With t = n_tokens: keys [0, t - t%R) are in k_codes and keys [t - t%R, t)
+ * in k_res; values [0, max(0, t-R)) are in v_codes and the last min(t, R)
+ * values in v_res.
+ *
+ * Quantizer (KIVI item 1), bit-exact with an fp32 CPU reference: per group,
+ * z = min x, s = (max x - min x) / (2^B - 1) (IEEE fp32 division), code =
+ * clamp(round_half_even((x - z) / s), 0, 2^B - 1); a group with max == min
+ * stores s = 0 and all-zero codes.
+ */
+#ifndef KIVI_H
+#define KIVI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  KIVI_OK = 0,
+  KIVI_ERR_INVALID_ARG = -1, /* a shape, bit width, pointer or option is invalid */
+  KIVI_ERR_CAPACITY = -2,    /* the write would pass the cache capacity          */
+  KIVI_ERR_WORKSPACE = -3,   /* the workspace is smaller than required            */
+  KIVI_ERR_HIP = -4          /* a HIP launch failed (detail in kivi_last_error)   */
+};
+
+/* A KV cache for one attention layer.  Host struct; the array pointers are
+ * (device) memory owned by the caller, laid out as described above.  A new
+ * cache has n_tokens = 0 and needs no initialisation of its arrays.
+ * Constraints: k_bits, v_bits in {2, 4}; group % (32/bits) == 0 for both;
+ * head_dim % group == 0 and head_dim <= 256; residual % group == 0;
+ * capacity % residual == 0; 0 <= n_tokens <= capacity. */
+typedef struct kivi_cache {
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t k_bits;
+  int32_t v_bits;
+  int32_t group;     /* G: tokens per key group and channels per value group */
+  int32_t residual;  /* R: fp16 window length                              */
+  int64_t capacity;  /* maximum number of tokens                           */
+  int64_t n_tokens;  /* t: changed only by kivi_append                     */
+  uint32_t *k_codes;
+  float *k_scale;
+  float *k_zero;
+  uint32_t *v_codes;
+  float *v_scale;
+  float *v_zero;
+  uint16_t *k_res;
+  uint16_t *v_res;
+} kivi_cache;
+
+/* KIVI item 2: quantize keys per channel in groups of `group` consecutive
+ * tokens and pack the codes along tokens.
+ *   k_fp16   (device) fp16 [B][H][T][D], token-major.
+ *   codes, scale, zero  (device) destination arrays in the k_codes / k_scale
+ *            / k_zero layout above, sized for `dst_capacity` tokens.
+ *   The T tokens become destination tokens [dst_token_offset,
+ *   dst_token_offset + T).  Requires T % group == 0, dst_token_offset %
+ *   group == 0, dst_capacity % group == 0 and the range inside the capacity.
+ *   T == 0 is a no-op. */
+int kivi_pack_keys(const void *k_fp16, int32_t B, int32_t H, int64_t T, int32_t D,
+                   int32_t bits, int32_t group, uint32_t *codes, float *scale,
+                   float *zero, int64_t dst_capacity, int64_t dst_token_offset,
+                   void *stream);
+
+/* KIVI item 3: quantize values per token in groups of `group` consecutive
+ * channels and pack the codes along channels.
+ *   v_fp16   (device) fp16 [B][H][T][D].
+ *   codes, scale, zero  (device) destination arrays in the v_codes / v_scale
+ *            / v_zero layout above, sized for `dst_capacity` tokens.
+ *   Tokens go to rows [dst_token_offset, dst_token_offset + T). */
+int kivi_pack_values(const void *v_fp16, int32_t B, int32_t H, int64_t T, int32_t D,
+                     int32_t bits, int32_t group, uint32_t *codes, float *scale,
+                     float *zero, int64_t dst_capacity, int64_t dst_token_offset,
+                     void *stream);
+
+/* KIVI item 4: append n_new tokens to the cache through the fp16 window.
+ * The result is bit-identical to appending them one at a time: for each
+ * token tau, if tau >= R the value in slot tau % R (token tau - R) is
+ * quantized into v_codes first; the new key and value then take slot tau % R;
+ * when tau + 1 is a multiple of R the R keys of the window are quantized
+ * into k_codes.  Appending T tokens to an empty cache is the prefill rule:
+ * keys [0, T - T%R) and values [0, T - R) quantized, the rest kept in fp16.
+ *   k_new_fp16, v_new_fp16  (device) fp16 [B][H][n_new][D].
+ *   n_new >= 0; KIVI_ERR_CAPACITY if n_tokens + n_new > capacity.
+ * On success c->n_tokens grows by n_new (on the host, at once; the kernels
+ * run in stream order). */
+int kivi_append(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp16,
+                int64_t n_new, void *stream);
+
+/* Bytes of workspace kivi_decode_attn needs for this cache shape and query
+ * head count at any n_tokens up to the capacity. 0 on invalid arguments. */
+size_t kivi_decode_attn_workspace_bytes(const kivi_cache *c, int32_t n_q_heads);
+
+/* KIVI item 5: one decode step of attention over the cache.  For query head
+ * hq of batch row b (KV head hq / (n_q_heads / n_kv_heads)):
+ *   s_tau = q . K_tau / sqrt(D) + mask[b][tau]   for tau < t,
+ *   out   = sum_tau softmax(s)_tau V_tau,
+ * where K_tau, V_tau are the dequantized codes (code * scale + zero) where
+ * quantized and the fp16 window values otherwise.  A row whose scores are
+ * all -inf gives zeros; t == 0 gives zeros.
+ *   q_fp16    (device) fp16 [B][n_q_heads][D]; n_q_heads % n_kv_heads == 0.
+ *   mask      (device) f32 [B][n_tokens] additive, indexed by token, or NULL.
+ *   out       (device) f32 [B][n_q_heads][D].
+ *   workspace (device) at least kivi_decode_attn_workspace_bytes() bytes.
+ * Append first, then attend: the cache must already hold the current token. */
+int kivi_decode_attn(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads,
+                     const float *mask, float *out, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/* Same as kivi_decode_attn with explicit tuning, for tests and sweeps:
+ *   tokens_per_split  0 = automatic, else a positive multiple of 64.
+ *   path              KIVI_PATH_AUTO, KIVI_PATH_GENERIC (scalar kernel for
+ *                     every token) or KIVI_PATH_MATRIX (matrix-core kernel
+ *                     where the shape allows; rejected where it does not).
+ * The workspace must hold kivi_decode_attn_workspace_bytes_ex() bytes. */
+enum { KIVI_PATH_AUTO = 0, KIVI_PATH_GENERIC = 1, KIVI_PATH_MATRIX = 2 };
+int kivi_decode_attn_ex(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads,
+                        const float *mask, float *out, void *workspace,
+                        size_t workspace_bytes, int32_t tokens_per_split,
+                        int32_t path, void *stream);
+size_t kivi_decode_attn_workspace_bytes_ex(const kivi_cache *c, int32_t n_q_heads,
+                                           int32_t tokens_per_split, int32_t path);
+
+/* Static description of a status code. */
+const char *kivi_status_string(int status);
+/* Detail of the last failing call on this thread ("" if none). */
+const char *kivi_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KIVI_H */

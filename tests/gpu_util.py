@@ -1,0 +1,79 @@
+"""Helpers for the GPU parity tests: build the same cache on the device
+(through the C ABI) and in the CPU oracle, and compare them."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from decode_attention_pack_amd import kivi
+
+# Attention tolerance: |gpu - ref| <= ATOL + RTOL * |ref| elementwise.
+ATOL = 2e-3
+RTOL = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True, file=sys.stderr)
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def gpu_cache(w, capacity=None) -> kivi.Cache:
+    cap = w.capacity if capacity is None else capacity
+    return kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, cap)
+
+
+def oracle_cache(w, B=None, H=None, capacity=None) -> oracle.Cache:
+    return oracle.Cache(w.B if B is None else B, w.Hkv if H is None else H, w.D, w.k_bits,
+                        w.v_bits, w.G, w.R, w.capacity if capacity is None else capacity)
+
+
+def b16(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a).view(np.uint16)
+
+
+def compare_slab(g: kivi.Cache, b: int, h: int, o: oracle.Cache, ob: int = 0, oh: int = 0):
+    """Bitwise comparison of the valid part of slab (b, h) of the GPU cache
+    with slab (ob, oh) of the oracle cache."""
+    t = g.n_tokens
+    assert o.n_tokens == t
+    R, G = g.R, g.G
+    n_kq, n_vq = t - t % R, max(0, t - R)
+    gk = host(g.k_codes[b, h, :n_kq // G]).view(np.uint32)
+    assert np.array_equal(gk, o.k_codes[ob, oh, :n_kq // G]), "key codes"
+    assert np.array_equal(host(g.k_scale[b, h, :n_kq // G]).view(np.uint32),
+                          o.k_scale[ob, oh, :n_kq // G].view(np.uint32)), "key scales"
+    assert np.array_equal(host(g.k_zero[b, h, :n_kq // G]).view(np.uint32),
+                          o.k_zero[ob, oh, :n_kq // G].view(np.uint32)), "key zeros"
+    gv = host(g.v_codes[b, h, :n_vq]).view(np.uint32)
+    assert np.array_equal(gv, o.v_codes[ob, oh, :n_vq]), "value codes"
+    assert np.array_equal(host(g.v_scale[b, h, :, :n_vq]).view(np.uint32),
+                          o.v_scale[ob, oh, :, :n_vq].view(np.uint32)), "value scales"
+    assert np.array_equal(host(g.v_zero[b, h, :, :n_vq]).view(np.uint32),
+                          o.v_zero[ob, oh, :, :n_vq].view(np.uint32)), "value zeros"
+    kslots = [tau % R for tau in range(n_kq, t)]
+    vslots = [tau % R for tau in range(n_vq, t)]
+    gkr = host(g.k_res[b, h]).view(np.uint16)
+    gvr = host(g.v_res[b, h]).view(np.uint16)
+    assert np.array_equal(gkr[kslots], o.k_res[ob, oh][kslots]), "key window"
+    assert np.array_equal(gvr[vslots], o.v_res[ob, oh][vslots]), "value window"
+
+
+def assert_close(got: np.ndarray, ref: np.ndarray, what: str = ""):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = np.abs(got - ref)
+    bad = err > ATOL + RTOL * np.abs(ref)
+    rel = err / np.maximum(np.abs(ref), 1e-30)
+    say(f"  {what}: max abs {err.max():.3e}, max rel {rel.max():.3e}, n={ref.size}")
+    assert not np.isnan(got).any(), f"{what}: NaN"
+    assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} outside tolerance; max abs {err.max()}"

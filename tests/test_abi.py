@@ -1,0 +1,135 @@
+"""The C ABI without a GPU: libkivi.so loads, exports every function that
+include/kivi.h declares, and rejects invalid arguments on the host before any
+HIP call (so these tests never touch a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kivi.h")
+LIB = os.path.join(ROOT, "decode_attention_pack_amd", "libkivi.so")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kivi_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB):
+        from decode_attention_pack_amd import build
+        build.build()
+    from decode_attention_pack_amd import kivi
+    return kivi.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert {"kivi_pack_keys", "kivi_pack_values", "kivi_append", "kivi_decode_attn"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    from decode_attention_pack_amd import kivi
+    assert set(kivi.EXPORTED) == set(names)
+
+
+def test_status_strings(L):
+    assert L.kivi_status_string(0) == b"ok"
+    assert L.kivi_status_string(-3) == b"workspace too small"
+    assert L.kivi_status_string(7) == b"unknown status"
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def _pack(L, fn, **kw):
+    a = dict(x=FAKE, B=1, H=1, T=64, D=128, bits=2, G=32, cap=128, off=0)
+    a.update(kw)
+    return getattr(L, fn)(a["x"], a["B"], a["H"], a["T"], a["D"], a["bits"], a["G"], FAKE, FAKE,
+                          FAKE, a["cap"], a["off"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=3), -1), (dict(bits=8), -1), (dict(G=24), -1), (dict(D=100), -1),
+    (dict(D=512), -1), (dict(T=33), -1), (dict(off=16), -1), (dict(cap=100), -1),
+    (dict(T=-1), -1), (dict(B=0), -1), (dict(T=96, off=64), -2), (dict(x=None), -1),
+])
+def test_pack_keys_rejects(L, kw, status):
+    assert _pack(L, "kivi_pack_keys", **kw) == status
+    assert L.kivi_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=1), -1), (dict(G=12, bits=4), -1), (dict(T=129), -2), (dict(T=65, off=64), -2),
+])
+def test_pack_values_rejects(L, kw, status):
+    assert _pack(L, "kivi_pack_values", **kw) == status
+
+
+def test_zero_tokens_is_a_no_op(L):
+    # valid arguments with T == 0 return before any launch
+    assert _pack(L, "kivi_pack_keys", T=0) == 0
+    assert _pack(L, "kivi_pack_values", T=0) == 0
+
+
+def _cache(**kw):
+    from decode_attention_pack_amd.kivi import CCache
+    a = dict(batch=1, n_kv_heads=2, head_dim=128, k_bits=2, v_bits=2, group=32, residual=128,
+             capacity=1024, n_tokens=0)
+    a.update(kw)
+    c = CCache(a["batch"], a["n_kv_heads"], a["head_dim"], a["k_bits"], a["v_bits"], a["group"],
+               a["residual"], a["capacity"], a["n_tokens"], *([0x1000] * 8))
+    return c
+
+
+@pytest.mark.parametrize("kw", [dict(k_bits=3), dict(v_bits=5), dict(residual=48),
+                                dict(capacity=1000), dict(n_tokens=-1), dict(n_tokens=2048),
+                                dict(batch=0), dict(head_dim=100), dict(group=20)])
+def test_append_rejects_bad_cache(L, kw):
+    c = _cache(**kw)
+    assert L.kivi_append(ctypes.byref(c), FAKE, FAKE, 1, None) == -1
+
+
+def test_append_capacity_and_no_op(L):
+    c = _cache(n_tokens=1000)
+    assert L.kivi_append(ctypes.byref(c), FAKE, FAKE, 25, None) == -2
+    assert c.n_tokens == 1000
+    assert L.kivi_append(ctypes.byref(c), FAKE, FAKE, 0, None) == 0
+    assert L.kivi_append(ctypes.byref(c), FAKE, FAKE, -1, None) == -1
+    assert L.kivi_append(ctypes.byref(c), None, FAKE, 1, None) == -1
+    assert L.kivi_append(None, FAKE, FAKE, 1, None) == -1
+
+
+def test_workspace_queries(L):
+    c = _cache(n_tokens=300)
+    n = L.kivi_decode_attn_workspace_bytes(ctypes.byref(c), 8)
+    assert n > 0 and n % (130 * 4) == 0
+    assert L.kivi_decode_attn_workspace_bytes(ctypes.byref(c), 3) == 0      # 3 % 2 != 0
+    assert L.kivi_decode_attn_workspace_bytes_ex(ctypes.byref(c), 8, 100, 0) == 0
+    assert L.kivi_decode_attn_workspace_bytes_ex(ctypes.byref(c), 8, 64, 9) == 0
+    # a smaller split never needs less workspace than the automatic plan's bound
+    assert L.kivi_decode_attn_workspace_bytes_ex(ctypes.byref(c), 8, 64, 0) >= n
+
+
+def test_decode_rejects(L):
+    c = _cache(n_tokens=300)
+    n = L.kivi_decode_attn_workspace_bytes(ctypes.byref(c), 4)
+    ok = dict(q=FAKE, hq=4, out=FAKE, ws=FAKE, nbytes=n, tps=0, path=0)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.kivi_decode_attn_ex(ctypes.byref(c), a["q"], a["hq"], None, a["out"], a["ws"],
+                                     a["nbytes"], a["tps"], a["path"], None)
+
+    assert call(hq=3) == -1
+    assert call(q=None) == -1
+    assert call(out=None) == -1
+    assert call(nbytes=n - 1) == -3
+    assert call(ws=None) == -3
+    assert call(tps=96) == -1
+    assert call(path=5) == -1
+    assert L.kivi_decode_attn(None, FAKE, 4, None, FAKE, FAKE, n, None) == -1

@@ -1,0 +1,164 @@
+"""GPU parity of kivi_decode_attn against the CPU oracle (KIVI item 5 of the
+page "Literature audit -- Group 2", section 1, "Core algorithm"): outputs
+within 2e-3 + 1e-3*|ref| elementwise; packed stores bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_pack_amd import kivi, synth
+from tests.gpu_util import assert_close, b16, compare_slab, dev, host, say
+from tests.textbook import dense_attention
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+PATHS = [kivi.KIVI_PATH_AUTO, kivi.KIVI_PATH_GENERIC]
+
+
+def _run_workload(w, slabs, paths=PATHS):
+    """Prefill + one decode step of workload w on the GPU; the oracle rebuilds
+    the sampled (batch, kv head) slabs alone and checks them."""
+    inp = synth.make_inputs(w)
+    g = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
+    say(f"{w.name}: prefill {w.T0} + 1 step")
+    kivi.kivi_append(g, dev(inp["k0"]), dev(inp["v0"]))
+    kivi.kivi_append(g, dev(inp["k_steps"][0]), dev(inp["v_steps"][0]))
+    q = inp["q_steps"][0]
+    outs = {p: host(kivi.kivi_decode_attn(g, dev(q), path=p)) for p in paths}
+    rep = w.Hq // w.Hkv
+    for b, h in slabs:
+        o = oracle.Cache(1, 1, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
+        o.append(b16(inp["k0"][b:b + 1, h:h + 1]), b16(inp["v0"][b:b + 1, h:h + 1]))
+        o.append(b16(inp["k_steps"][0][b:b + 1, h:h + 1]), b16(inp["v_steps"][0][b:b + 1, h:h + 1]))
+        compare_slab(g, b, h, o)
+        ref = o.decode_attn(b16(q[b:b + 1, h * rep:(h + 1) * rep]))[0]
+        for p, out in outs.items():
+            assert_close(out[b, h * rep:(h + 1) * rep], ref, f"{w.name} path {p} b{b} kv{h}")
+    return g, outs
+
+
+def test_tiny():
+    _run_workload(synth.WORKLOADS[1], [(0, 0)])
+
+
+def test_kivi4_b64():
+    w = synth.WORKLOADS[3]
+    _run_workload(w, [(0, 0), (63, 31), (17, 9)])
+
+
+def test_llama3_gqa_32k():
+    w = synth.WORKLOADS[4]
+    _run_workload(w, [(0, 0), (3, 7), (2, 5)])
+
+
+def test_long_128k():
+    w = synth.WORKLOADS[5]
+    _run_workload(w, [(0, 0), (0, 7), (0, 3)])
+
+
+def _small_case(rng, B, H, rep, D, kb, vb, G, R, t):
+    K = (rng.standard_normal((B, H, t, D)) * rng.uniform(0.5, 15, (1, H, 1, D))).astype(np.float16)
+    V = rng.standard_normal((B, H, t, D)).astype(np.float16)
+    q = rng.standard_normal((B, H * rep, D)).astype(np.float16)
+    cap = max(R, ((t + R - 1) // R) * R)
+    g = kivi.Cache(B, H, D, kb, vb, G, R, cap)
+    o = oracle.Cache(B, H, D, kb, vb, G, R, cap)
+    if t:
+        kivi.kivi_append(g, dev(K), dev(V))
+        o.append(b16(K), b16(V))
+    return g, o, q
+
+
+@pytest.mark.parametrize("t", [0, 1, 31, 32, 33, 64, 95, 96, 97, 127, 128, 129, 200, 255, 256,
+                               257, 511, 640, 1000])
+@pytest.mark.parametrize("rep", [1, 4])
+def test_lengths_around_boundaries(t, rep):
+    rng = np.random.default_rng(t * 10 + rep)
+    g, o, q = _small_case(rng, 2, 2, rep, 128, 2, 2, 32, 64, t)
+    ref = o.decode_attn(b16(q))
+    for p in PATHS:
+        out = host(kivi.kivi_decode_attn(g, dev(q), path=p))
+        assert_close(out, ref, f"t={t} rep={rep} path={p}")
+
+
+@pytest.mark.parametrize("rep", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("kb,vb", [(2, 2), (4, 4), (2, 4), (4, 2)])
+def test_head_groups_and_bits(rep, kb, vb):
+    rng = np.random.default_rng(rep * 7 + kb + 3 * vb)
+    g, o, q = _small_case(rng, 2, 2, rep, 128, kb, vb, 32, 128, 777)
+    ref = o.decode_attn(b16(q))
+    for p in PATHS:
+        assert_close(host(kivi.kivi_decode_attn(g, dev(q), path=p)), ref, f"rep={rep} kb={kb} vb={vb}")
+
+
+@pytest.mark.parametrize("D,G", [(64, 32), (256, 32), (128, 64), (128, 128)])
+def test_head_dims_and_groups(D, G):
+    rng = np.random.default_rng(D + G)
+    g, o, q = _small_case(rng, 1, 2, 2, D, 2, 2, G, 128, 600)
+    ref = o.decode_attn(b16(q))
+    assert_close(host(kivi.kivi_decode_attn(g, dev(q))), ref, f"D={D} G={G}")
+
+
+def test_mask():
+    rng = np.random.default_rng(8)
+    g, o, q = _small_case(rng, 2, 2, 4, 128, 2, 2, 32, 128, 900)
+    t = g.n_tokens
+    m = np.where(rng.random((2, t)) < 0.3, -np.inf, rng.standard_normal((2, t))).astype(np.float32)
+    m[1, :] = -np.inf                      # a fully masked batch row
+    ref = o.decode_attn(b16(q), m)
+    for p in PATHS:
+        out = host(kivi.kivi_decode_attn(g, dev(q), mask=dev(m), path=p))
+        assert not np.isnan(out).any() and not out[1].any()
+        assert_close(out, ref, f"mask path={p}")
+    zero = host(kivi.kivi_decode_attn(g, dev(q), mask=dev(np.zeros((2, t), np.float32))))
+    assert np.array_equal(zero, host(kivi.kivi_decode_attn(g, dev(q))))
+
+
+def test_split_invariance():
+    """Different split counts agree to within rounding (P12)."""
+    rng = np.random.default_rng(12)
+    g, o, q = _small_case(rng, 1, 2, 4, 128, 2, 2, 32, 128, 5000)
+    base = host(kivi.kivi_decode_attn(g, dev(q)))
+    for tps in (64, 256, 1024, 4096):
+        for p in PATHS:
+            out = host(kivi.kivi_decode_attn(g, dev(q), tokens_per_split=tps, path=p))
+            np.testing.assert_allclose(out, base, atol=2e-5, rtol=1e-5)
+
+
+def test_gqa_equals_repeated_kv_mha():
+    rng = np.random.default_rng(13)
+    B, H, rep, D, t = 1, 2, 4, 128, 1500
+    K = rng.standard_normal((B, H, t, D)).astype(np.float16)
+    V = rng.standard_normal((B, H, t, D)).astype(np.float16)
+    q = dev(rng.standard_normal((B, H * rep, D)).astype(np.float16))
+    g = kivi.Cache(B, H, D, 2, 2, 32, 128, 1536)
+    kivi.kivi_append(g, dev(K), dev(V))
+    m = kivi.Cache(B, H * rep, D, 2, 2, 32, 128, 1536)
+    kivi.kivi_append(m, dev(np.repeat(K, rep, axis=1)), dev(np.repeat(V, rep, axis=1)))
+    np.testing.assert_allclose(host(kivi.kivi_decode_attn(g, q)), host(kivi.kivi_decode_attn(m, q)),
+                               atol=1e-5, rtol=1e-5)
+
+
+def test_grid_exact_inputs_match_dense_attention():
+    """Keys/values that quantize losslessly: GPU attention over the packed
+    cache equals dense attention over the original fp16 tensors."""
+    rng = np.random.default_rng(21)
+    B, H, rep, D, G, R, t = 1, 2, 2, 128, 32, 128, 640
+    n_kq = t - t % R
+    s = 2.0 ** rng.integers(-3, 1, (B, H, n_kq // G, 1, D))
+    z = s * rng.integers(-20, 20, (B, H, n_kq // G, 1, D))
+    k = rng.integers(0, 4, (B, H, n_kq // G, G, D))
+    k[:, :, :, 0, :], k[:, :, :, 1, :] = 0, 3
+    K = (z + k * s).reshape(B, H, n_kq, D).astype(np.float16)
+    sv = 2.0 ** rng.integers(-3, 1, (B, H, t, D // G, 1))
+    zv = sv * rng.integers(-20, 20, (B, H, t, D // G, 1))
+    kv = rng.integers(0, 4, (B, H, t, D // G, G))
+    kv[..., 0], kv[..., 1] = 0, 3
+    V = (zv + kv * sv).reshape(B, H, t, D).astype(np.float16)
+    q = rng.standard_normal((B, H * rep, D)).astype(np.float16)
+    g = kivi.Cache(B, H, D, 2, 2, G, R, t + R)
+    kivi.kivi_append(g, dev(K), dev(V[:, :, :n_kq]))
+    ref = dense_attention(q.astype(np.float32), K.astype(np.float32), V[:, :, :n_kq].astype(np.float32))
+    for p in PATHS:
+        assert_close(host(kivi.kivi_decode_attn(g, dev(q), path=p)), ref, f"grid path={p}")
