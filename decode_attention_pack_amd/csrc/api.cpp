@@ -94,6 +94,7 @@ int check_pack(const void *x, int32_t B, int32_t H, int64_t T, int32_t D, int32_
 int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
 
 constexpr int kGenericMinSplit = 256;
+constexpr int kMatrixBlock = 128;   // tokens per block of the matrix-core kernel
 constexpr int kTargetWorkgroups = 2048;
 
 struct Plan {
@@ -117,12 +118,12 @@ Plan make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
   const int n_rep = Hq / c->n_kv_heads;
   p.matrix = path != KIVI_PATH_GENERIC && kivi::decode_matrix_supported(a);
   if (p.matrix) {
-    p.n_main = (a.n_vq / 64) * 64;
+    p.n_main = (a.n_vq / kMatrixBlock) * kMatrixBlock;
     if (p.n_main == 0) p.matrix = false;
   }
   const int64_t units = (int64_t)c->batch * c->n_kv_heads;
   if (p.matrix) {
-    int64_t tps = tps_req;
+    int64_t tps = (tps_req + kMatrixBlock - 1) / kMatrixBlock * kMatrixBlock;
     if (tps == 0) {
       const int64_t splits = max64(1, kTargetWorkgroups / units);
       tps = ((p.n_main + splits - 1) / splits + 255) / 256 * 256;
@@ -150,8 +151,9 @@ Plan make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
 int64_t max_slots(const kivi_cache *c, int32_t tps_req) {
   const int64_t step = tps_req > 0 ? tps_req : kGenericMinSplit;
   // matrix splits over [0, n_main) plus scalar splits over the tail (at most
-  // 64 + 2R tokens, or the whole range when the matrix kernel is not used)
-  return (c->capacity + step - 1) / step + (64 + 2 * (int64_t)c->residual + step - 1) / step + 1;
+  // one block + R tokens, or the whole range when the matrix kernel is not used)
+  return (c->capacity + step - 1) / step +
+         (kMatrixBlock + 2 * (int64_t)c->residual + step - 1) / step + 1;
 }
 
 }  // namespace
