@@ -21,6 +21,9 @@ FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-x", "hip",
     # keep the compiler away from packed FP32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # every rounding step as written: no implicit fusion of a multiply with an
+    # add or a narrowing conversion (kernels call fmaf where they want one)
+    "-ffp-contract=off",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

@@ -99,11 +99,11 @@ constexpr int kTargetWorkgroups = 2048;
 
 struct Plan {
   bool matrix = false;
-  int64_t n_main = 0;           // tokens [0, n_main) on the matrix kernel
+  int64_t n_main = 0;           // tokens [0, n_main) in the matrix kernel's block role
   int tps_matrix = 0;
   int n_split_matrix = 0;
-  int64_t generic_begin = 0;    // tokens [generic_begin, t) on the scalar kernel
-  int tps_generic = 0;
+  int n_window = 0;             // 64-token chunks of [n_main, t) in its window role
+  int tps_generic = 0;          // scalar kernel (shapes the matrix kernel does not cover)
   int n_split_generic = 0;
   int S_total = 0;
 };
@@ -116,13 +116,10 @@ Plan make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
   Plan p;
   const int64_t t = c->n_tokens;
   const int n_rep = Hq / c->n_kv_heads;
+  const int64_t units = (int64_t)c->batch * c->n_kv_heads;
   p.matrix = path != KIVI_PATH_GENERIC && kivi::decode_matrix_supported(a);
   if (p.matrix) {
     p.n_main = (a.n_vq / kMatrixBlock) * kMatrixBlock;
-    if (p.n_main == 0) p.matrix = false;
-  }
-  const int64_t units = (int64_t)c->batch * c->n_kv_heads;
-  if (p.matrix) {
     int64_t tps = (tps_req + kMatrixBlock - 1) / kMatrixBlock * kMatrixBlock;
     if (tps == 0) {
       const int64_t splits = max64(1, kTargetWorkgroups / units);
@@ -131,29 +128,29 @@ Plan make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
     }
     p.tps_matrix = (int)tps;
     p.n_split_matrix = (int)((p.n_main + tps - 1) / tps);
-    p.generic_begin = p.n_main;
+    p.n_window = kivi::decode_matrix_window_chunks(a, p.n_main);
+    p.S_total = p.n_split_matrix + p.n_window;
+    return p;
   }
-  const int64_t rest = t - p.generic_begin;
   int64_t tps = tps_req;
   if (tps == 0) {
     const int64_t gunits = units * head_chunks(n_rep);
     const int64_t splits = max64(1, kTargetWorkgroups / gunits);
-    tps = ((rest + splits - 1) / splits + kGenericMinSplit - 1) / kGenericMinSplit * kGenericMinSplit;
+    tps = ((t + splits - 1) / splits + kGenericMinSplit - 1) / kGenericMinSplit * kGenericMinSplit;
     tps = max64(tps, kGenericMinSplit);
   }
   p.tps_generic = (int)tps;
-  p.n_split_generic = (int)max64(1, (rest + tps - 1) / tps);
-  p.S_total = p.n_split_matrix + p.n_split_generic;
+  p.n_split_generic = (int)max64(1, (t + tps - 1) / tps);
+  p.S_total = p.n_split_generic;
   return p;
 }
 
 // Upper bound on partial slots for any n_tokens <= capacity.
 int64_t max_slots(const kivi_cache *c, int32_t tps_req) {
   const int64_t step = tps_req > 0 ? tps_req : kGenericMinSplit;
-  // matrix splits over [0, n_main) plus scalar splits over the tail (at most
-  // one block + R tokens, or the whole range when the matrix kernel is not used)
-  return (c->capacity + step - 1) / step +
-         (kMatrixBlock + 2 * (int64_t)c->residual + step - 1) / step + 1;
+  // splits over the capacity, plus the matrix kernel's window chunks (its
+  // window is at most one block + R tokens long)
+  return (c->capacity + step - 1) / step + (kMatrixBlock + (int64_t)c->residual + 63) / 64 + 1;
 }
 
 }  // namespace
@@ -315,11 +312,10 @@ int kivi_decode_attn_ex(const kivi_cache *c, const void *q_fp16, int32_t n_q_hea
   if (p.matrix) {
     rc = hip_status(kivi::launch_decode_matrix(a, p.n_main, p.tps_matrix, p.n_split_matrix, s),
                     "kivi_decode_attn (matrix)");
-    if (rc) return rc;
+  } else {
+    rc = hip_status(kivi::launch_decode_generic(a, 0, p.tps_generic, p.n_split_generic, 0, s),
+                    "kivi_decode_attn (scalar)");
   }
-  rc = hip_status(kivi::launch_decode_generic(a, p.generic_begin, p.tps_generic,
-                                              p.n_split_generic, p.n_split_matrix, s),
-                  "kivi_decode_attn (scalar)");
   if (rc) return rc;
   return hip_status(kivi::launch_combine(a, s), "kivi_decode_attn (combine)");
 }

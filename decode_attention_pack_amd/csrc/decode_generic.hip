@@ -187,25 +187,57 @@ decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int
   }
 }
 
-// grid: B * Hq; block: D threads.  out = sum_i acc_i e^(m_i - M) / sum_i l_i e^(m_i - M).
+// grid: B * Hq; block: 256.  out = sum_i acc_i e^(m_i - M) / sum_i l_i e^(m_i - M)
+// with M = max_i m_i, over the S_total partial slots of one (batch, query head).
 __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
+  __shared__ float w_s[256];
+  __shared__ float red_s[256];
   const int64_t row = blockIdx.x;
-  const int c = threadIdx.x;
-  const int D = a.D;
-  const float *p = a.part + row * a.S_total * (int64_t)(D + 2);
+  const int tid = threadIdx.x;
+  const int D = a.D, S = a.S_total, stride = D + 2;
+  const float *p = a.part + row * S * (int64_t)stride;
+
   float M = -INFINITY;
-  for (int i = 0; i < a.S_total; ++i) M = fmaxf(M, p[i * (D + 2) + D]);
+  for (int i = tid; i < S; i += 256) M = fmaxf(M, p[(int64_t)i * stride + D]);
+  M = wave_max(M);
+  if ((tid & 63) == 0) red_s[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
+  __syncthreads();
+
+  const int c = tid % D, par = tid / D, n_par = 256 / D;
   float L = 0.0f, o = 0.0f;
-  if (M != -INFINITY) {
-    for (int i = 0; i < a.S_total; ++i) {
-      const float mi = p[i * (D + 2) + D];
-      if (mi == -INFINITY) continue;
-      const float w = expf(mi - M);
-      L = fmaf(p[i * (D + 2) + D + 1], w, L);
-      o = fmaf(p[i * (D + 2) + c], w, o);
+  for (int base = 0; base < S; base += 256) {
+    const int i = base + tid;
+    float w = 0.0f;
+    if (i < S && M != -INFINITY) {
+      const float mi = p[(int64_t)i * stride + D];
+      if (mi != -INFINITY) {
+        w = expf(mi - M);
+        L = fmaf(p[(int64_t)i * stride + D + 1], w, L);
+      }
     }
+    w_s[tid] = w;
+    __syncthreads();
+    const int cnt = min(256, S - base);
+    if (par < n_par) {
+#pragma unroll 8
+      for (int k = par; k < cnt; k += n_par) o = fmaf(p[(int64_t)(base + k) * stride + c], w_s[k], o);
+    }
+    __syncthreads();
   }
-  a.out[row * D + c] = L > 0.0f ? o / L : 0.0f;
+  L = wave_sum(L);
+  if ((tid & 63) == 0) red_s[tid >> 6] = L;
+  __syncthreads();
+  L = red_s[0] + red_s[1] + red_s[2] + red_s[3];
+  __syncthreads();
+  red_s[tid] = par < n_par ? o : 0.0f;
+  __syncthreads();
+  if (tid < D) {
+    float sum = 0.0f;
+    for (int q = 0; q < n_par; ++q) sum += red_s[q * D + tid];
+    a.out[row * D + tid] = L > 0.0f ? sum / L : 0.0f;
+  }
 }
 
 hipError_t launch_decode_generic(const DecodeArgs &a, int64_t tok_begin, int tokens_per_split,
@@ -219,7 +251,7 @@ hipError_t launch_decode_generic(const DecodeArgs &a, int64_t tok_begin, int tok
 }
 
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(a.B * a.Hq)), dim3((unsigned)a.D), 0, s, a);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(a.B * a.Hq)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -5,10 +5,12 @@
 // Method source: web page "Literature audit -- Group 2 (KV-cache compression
 // primary sources)", section "1. KIVI -- kivi2024", list "Core algorithm
 // (implementation-grade)", item 5: scores q.deq(K)^T over the quantized keys,
-// softmax, then P.deq(V) over the quantized values.  This kernel covers the
-// tokens whose key AND value are both quantized, in blocks of 128 tokens; the
-// fp16 window and the ragged tail go to the scalar kernel, and the combine
-// kernel merges both.
+// softmax, then P.deq(V) over the quantized values.  The matrix-core role of
+// this kernel covers the tokens whose key AND value are both quantized, in
+// whole blocks of 128 tokens; a second role, in the same launch, covers the
+// rest (the fp16 window and the quantized tokens past the last whole block)
+// with scalar arithmetic.  Each workgroup writes a partial (acc, m, l) and
+// the combine kernel merges them.
 //
 // Algebra.  With a key group's scale s and zero z (per channel c, 32 tokens),
 //   q . K_tau = sum_c (q_c s_c) code_{c,tau} + sum_c q_c z_c,
@@ -27,10 +29,15 @@
 // 16 columns of 4-bit nibbles across a 16-lane group, which puts a pair of
 // codes per nibble exactly where the MFMA B operand wants it: a lane then
 // holds, for one token (keys) or one channel (values), the codes of 16
-// consecutive contraction indices.  Masking a dword with 0x00030003-style
-// masks places two codes in the low mantissa bits of two fp16 halves, i.e. as
-// the subnormal value code * 2^(pos - 24); the position factor 2^pos is taken
-// out of the matching A element, and 2^-24 out of the result.
+// consecutive contraction indices.  A shift and an and-or place a code c in
+// the top mantissa bits of an fp16 1.0, giving the exact normal value 1 + c/4
+// (low code of a nibble) or 1 + c/16 (high code); a packed fp16 subtraction
+// of 1 leaves c/4 or c/16, exact and normal (or zero).  Two encodings that
+// skip the subtraction lose accuracy on the matrix core: codes as fp16
+// subnormals (it keeps only ~14 bits when it adds the two products of one
+// register whose B halves are subnormal), and 1 + c/4 with the sum of A
+// removed afterwards (the large constant part cancels, and the rounding of
+// the fp32 accumulation is magnified 4x and 16x).
 #include <math.h>
 
 #include "kivi_internal.hpp"
@@ -100,16 +107,18 @@ __device__ __forceinline__ i2 tr4(const uint32_t *p) {
   return __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i2 *)p);
 }
 
-// B operand from one transposed dword: even (low 2 bits of each nibble) and
-// odd (high 2 bits, which come out 4x larger) halves.  Element 2r+e of the
-// result holds nibble r+4e.
+// B operand from one transposed dword holding nibbles 0..7.  Element 2r+e of
+// `be` is c/4 for the low code c of nibble r+4e, element 2r+e of `bo` is c/16
+// for its high code (exact fp16 values).
 __device__ __forceinline__ void split_codes(uint32_t x, h8 &be, h8 &bo) {
-  const uint32_t x8 = x >> 8;
   typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-  u4 e = {x & 0x00030003u, x & 0x00300030u, x8 & 0x00030003u, x8 & 0x00300030u};
-  u4 o = {x & 0x000C000Cu, x & 0x00C000C0u, x8 & 0x000C000Cu, x8 & 0x00C000C0u};
-  be = __builtin_bit_cast(h8, e);
-  bo = __builtin_bit_cast(h8, o);
+  const uint32_t l8 = x << 8, l4 = x << 4, r4 = x >> 4, r8 = x >> 8;
+  const uint32_t ONE = 0x3C003C00u, ME = 0x03000300u, MO = 0x00C000C0u;
+  u4 e = {(l8 & ME) | ONE, (l4 & ME) | ONE, (x & ME) | ONE, (r4 & ME) | ONE};
+  u4 o = {(l4 & MO) | ONE, (x & MO) | ONE, (r4 & MO) | ONE, (r8 & MO) | ONE};
+  const h8 one = {1, 1, 1, 1, 1, 1, 1, 1};
+  be = __builtin_bit_cast(h8, e) - one;
+  bo = __builtin_bit_cast(h8, o) - one;
 }
 
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
@@ -152,33 +161,52 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// hi/lo fp16 split of x*y: hi = rn16(x*y), lo = rn16(x*y - hi).
-__device__ __forceinline__ void split_mul(float x, float y, _Float16 &hi, _Float16 &lo) {
-  hi = (_Float16)(x * y);
-  lo = (_Float16)__builtin_fmaf(x, y, -(float)hi);
+// hi/lo fp16 split of two products x0*y0, x1*y1 (one A-operand register):
+// hi = the fp32 product truncated to fp16, lo = rn16(exact product - hi), so
+// hi + lo carries ~21 significant bits.  hi comes from an intrinsic the
+// compiler cannot re-derive: were the register's hi and the hi subtracted for
+// lo rounded in two different ways, lo would carry their difference, a whole
+// fp16 ulp, as error.
+__device__ __forceinline__ void split_mul2(float x0, float y0, float x1, float y1, h8 &hi,
+                                           h8 &lo, int k) {
+  const auto h = __builtin_amdgcn_cvt_pkrtz(x0 * y0, x1 * y1);
+  hi[k] = (_Float16)h[0];
+  hi[k + 1] = (_Float16)h[1];
+  lo[k] = (_Float16)__builtin_fmaf(x0, y0, -(float)h[0]);
+  lo[k + 1] = (_Float16)__builtin_fmaf(x1, y1, -(float)h[1]);
 }
 
 }  // namespace
 
 // grid: (n_split, H, B); block: one wave.  Split `split` covers tokens
 // [split * tps, min(n_main, (split + 1) * tps)).
+// LDS of the kernel.  Separate objects, so the compiler can tell that writes
+// to the small arrays never touch the stage buffer being filled by DMA.
+struct Lds {
+  Stage *st;           // [2]
+  float (*p)[kBT];     // [4][kBT] probabilities of the block, per query head
+  float *bias;         // [16]: sum q z per A row
+  float *zt;           // [16]: sum p z per A row
+  float *alpha;        // [4]
+  float (*q)[kD];      // [4][kD] (window role)
+};
+
+// Matrix-core role: split `split` covers the fully quantized tokens
+// [split * tps, min(n_main, (split + 1) * tps)) in blocks of 128.
 template <int NREP>
-__global__ void __launch_bounds__(64)
-decode_matrix_kernel(DecodeArgs a, int64_t n_main, int tps) {
+__device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, int tps,
+                                           int split, const Lds &L) {
   static_assert(NREP == 1 || NREP == 2 || NREP == 4, "query heads per KV head");
   constexpr int GA = 16 / NREP;       // key groups per A operand
-  // Separate objects, so the compiler can tell that writes to the small
-  // arrays never touch the stage buffer being filled by DMA.
-  __shared__ Stage sm_st[2];
-  __shared__ __attribute__((aligned(16))) float sm_p[4][kBT];   // probabilities, per head
-  __shared__ __attribute__((aligned(16))) float sm_bias[16];
-  __shared__ __attribute__((aligned(16))) float sm_zt[16];
-  __shared__ __attribute__((aligned(16))) float sm_alpha[4];
+  Stage *sm_st = L.st;
+  float (*sm_p)[kBT] = L.p;
+  float *sm_bias = L.bias;
+  float *sm_zt = L.zt;
+  float *sm_alpha = L.alpha;
 
   const int lane = threadIdx.x;
   const int i = lane & 15;
   const int kg = lane >> 4;
-  const int split = blockIdx.x;
   const int hk = blockIdx.y;
   const int b = blockIdx.z;
   const int64_t bh = (int64_t)b * a.H + hk;
@@ -206,7 +234,7 @@ decode_matrix_kernel(DecodeArgs a, int64_t n_main, int tps) {
     for (int ks = 0; ks < 4; ++ks) {
       const int c0 = 64 * (ks >> 1) + 16 * kg + 8 * (ks & 1);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) qa[ks][j] = h2f(q[c0 + j]) * ((j & 1) ? 0.0625f : 1.0f);
+      for (int j = 0; j < 8; ++j) qa[ks][j] = h2f(q[c0 + j]);
     }
   }
 
@@ -217,16 +245,16 @@ decode_matrix_kernel(DecodeArgs a, int64_t n_main, int tps) {
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) qmax = fmaxf(qmax, fabsf(qa[ks][j]) * ((j & 1) ? 16.0f : 1.0f));
+    for (int j = 0; j < 8; ++j) qmax = fmaxf(qmax, fabsf(qa[ks][j]));
   qmax = row_max(qmax);
   qmax = fmaxf(qmax, __shfl_xor(qmax, 16));
   qmax = fmaxf(qmax, __shfl_xor(qmax, 32));
   int ek_run = 0;
 
   const float LOG2E = 1.4426950408889634f;
-  const float c_even = 16777216.0f * a.sm_scale * LOG2E;   // 2^24 / sqrt(D) * log2(e)
-  const float c_odd = 0.25f * c_even;
-  const float c_bias = a.sm_scale * LOG2E;
+  const float c_bias = a.sm_scale * LOG2E;                 // 1/sqrt(D) * log2(e)
+  const float c_even = 4.0f * c_bias;                      // 1 + c/4 codes
+  const float c_odd = 16.0f * c_bias;                      // 1 + c/16 codes
 
   // The value-side A operand is p * s_v * 2^ev, with the power of two ev set
   // per block from the block's largest value scale so that the fp16 split
@@ -234,7 +262,7 @@ decode_matrix_kernel(DecodeArgs a, int64_t n_main, int tps) {
   int ev_run = 0;
   float m_run = -INFINITY;     // running max (log2 units), head h_s
   float l_run = 0.0f;          // this lane's share of the running sum
-  float zt_e = 0.0f, zt_o = 0.0f;   // value zero-point sums, row (h_v, c_v)
+  float zt = 0.0f;    // value zero-point sum  sum p' z, row (h_v, c_v)
   f4 dv[4][2];
 #pragma unroll
   for (int g = 0; g < 4; ++g) dv[g][0] = dv[g][1] = (f4){0, 0, 0, 0};
@@ -311,7 +339,7 @@ decode_matrix_kernel(DecodeArgs a, int64_t n_main, int tps) {
 
     // ---- key side: A = hi/lo(q s), bias = q . z
     h8 ah[4], al[4];
-    float be_e = 0.0f, be_o = 0.0f;
+    float bz = 0.0f;   // sum q z over this lane's channels
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int c0 = 64 * (ks >> 1) + 16 * kg + 8 * (ks & 1);
@@ -319,20 +347,18 @@ decode_matrix_kernel(DecodeArgs a, int64_t n_main, int tps) {
       const float *zp = st.kz + g_a * kD + c0;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        split_mul2(qa[ks][r], sp[r], qa[ks][r + 4], sp[r + 4], ah[ks], al[ks], 2 * r);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int j = r + 4 * e;
-          _Float16 hi, lo;
-          split_mul(qa[ks][j], sp[j], hi, lo);
-          ah[ks][2 * r + e] = hi;
-          al[ks][2 * r + e] = lo;
-          if (j & 1) be_o = fmaf(qa[ks][j], zp[j], be_o);
-          else be_e = fmaf(qa[ks][j], zp[j], be_e);
+          bz = fmaf(qa[ks][j], zp[j], bz);
         }
       }
     }
-    float bias = group_sum(fmaf(16.0f, be_o, be_e));
-    if (kg == 0) sm_bias[i] = bias;
+    // scores: even tokens 4 D 2^-ek + sum q z, odd tokens 16 D 2^-ek + sum q z
+    // (qa, hence D and bz, carry 2^ek)
+    bz = group_sum(bz);
+    if (kg == 0) sm_bias[i] = bz;
 
     f4 dk[4][2];
 #pragma unroll
@@ -357,15 +383,15 @@ decode_matrix_kernel(DecodeArgs a, int64_t n_main, int tps) {
 
     // ---- scores and online softmax (lanes holding head h_s)
     if (k_valid) {
-      const f4 bias4 = *(const f4 *)(sm_bias + 4 * kg);
+      const f4 bz4 = *(const f4 *)(sm_bias + 4 * kg);
       const float un = __builtin_amdgcn_ldexpf(1.0f, -ek_run);    // undo 2^ek
       float s2[4][2];
       float bmax = -INFINITY;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float bb = bias4[g] * (c_bias * un);
-        s2[g][0] = fmaf(dk[g][0][g], c_even * un, bb);
-        s2[g][1] = fmaf(dk[g][1][g], c_odd * un, bb);
+        const float zb = bz4[g] * (c_bias * un);
+        s2[g][0] = fmaf(dk[g][0][g], c_even * un, zb);
+        s2[g][1] = fmaf(dk[g][1][g], c_odd * un, zb);
         s2[g][0] += mk[g][0];
         s2[g][1] += mk[g][1];
         bmax = fmaxf(bmax, fmaxf(s2[g][0], s2[g][1]));
@@ -375,13 +401,12 @@ decode_matrix_kernel(DecodeArgs a, int64_t n_main, int tps) {
       const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
       float lsum = 0.0f;
       const float sc_e = __builtin_amdgcn_ldexpf(1.0f, ev);        // 2^ev
-      const float sc_o = __builtin_amdgcn_ldexpf(1.0f, ev - 4);    // odd tokens: / 16
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const float p0 = m_new == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s2[g][0] - m_new);
         const float p1 = m_new == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s2[g][1] - m_new);
         lsum += p0 + p1;
-        float2 pp = make_float2(p0 * sc_e, p1 * sc_o);
+        float2 pp = make_float2(p0 * sc_e, p1 * sc_e);
         *(float2 *)(&sm_p[h_s][32 * g + 2 * i]) = pp;
       }
       l_run = fmaf(l_run, alpha, lsum);
@@ -402,8 +427,7 @@ decode_matrix_kernel(DecodeArgs a, int64_t n_main, int tps) {
         dv[g][1][g] *= av;
       }
       const float ar = sm_alpha[h_v] * rescale;
-      zt_e *= ar;
-      zt_o *= ar;
+      zt *= ar;
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -416,15 +440,11 @@ decode_matrix_kernel(DecodeArgs a, int64_t n_main, int tps) {
         const float *zp = st.vz + c_v * kBT + t0;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
+          split_mul2(pp[r], sp[r], pp[r + 4], sp[r + 4], vh[d], vl[d], 2 * r);
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int j = r + 4 * e;
-            _Float16 hi, lo;
-            split_mul(pp[j], sp[j], hi, lo);
-            vh[d][2 * r + e] = hi;
-            vl[d][2 * r + e] = lo;
-            if (j & 1) zt_o = fmaf(pp[j], zp[j], zt_o);
-            else zt_e = fmaf(pp[j], zp[j], zt_e);
+            zt = fmaf(pp[j], zp[j], zt);
           }
         }
       }
@@ -445,8 +465,10 @@ decode_matrix_kernel(DecodeArgs a, int64_t n_main, int tps) {
   }
 
   // ---- write the partial (acc[128], m, l) of each query head
-  const float zt = group_sum(fmaf(16.0f, zt_o, zt_e));
-  if (kg == 0) sm_zt[i] = zt;
+  zt = group_sum(zt);
+  if (kg == 0) {
+    sm_zt[i] = zt;
+  }
   const float l_head = row_sum(l_run);
   wave_lds_sync();
   const int slot_stride = kD + 2;
@@ -454,12 +476,11 @@ decode_matrix_kernel(DecodeArgs a, int64_t n_main, int tps) {
     const f4 z4 = *(const f4 *)(sm_zt + 4 * kg);
     float *dst = a.part + (((int64_t)b * a.Hq + hk * NREP + kg) * a.S_total + split) * slot_stride;
     const float unit = __builtin_amdgcn_ldexpf(1.0f, -ev_run);      // undo 2^ev
-    const float ce = __builtin_amdgcn_ldexpf(1.0f, 24 - ev_run);    // and the code's 2^-24
-    const float co = __builtin_amdgcn_ldexpf(1.0f, 22 - ev_run);    // odd channels came out 4x
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      float2 o = make_float2(fmaf(dv[g][0][g], ce, z4[g] * unit),
-                             fmaf(dv[g][1][g], co, z4[g] * unit));
+      // even channels: 4 D + sum p z; odd channels: 16 D + sum p z
+      float2 o = make_float2(fmaf(4.0f, dv[g][0][g], z4[g]) * unit,
+                             fmaf(16.0f, dv[g][1][g], z4[g]) * unit);
       *(float2 *)(dst + 32 * g + 2 * i) = o;
     }
   }
@@ -470,26 +491,217 @@ decode_matrix_kernel(DecodeArgs a, int64_t n_main, int tps) {
   }
 }
 
+// Window role: the tokens of one slab that the block role does not cover --
+// the fp16 window and the quantized tokens past the last full block -- in
+// chunks of 64: tokens [n_main + 64 chunk, min(t, n_main + 64 chunk + 64)).
+// Everything the chunk needs is copied to LDS with one batch of DMA, then
+// each lane scores one token (scalar fp32) and accumulates two channels.
+template <int NREP>
+__device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main, int chunk,
+                                            int slot, const Lds &L) {
+  const int j = threadIdx.x;
+  const int hk = blockIdx.y;
+  const int b = blockIdx.z;
+  const int64_t bh = (int64_t)b * a.H + hk;
+  const int64_t Ta = n_main + 64 * (int64_t)chunk;
+  const int64_t Tb = Ta + 64 < a.t ? Ta + 64 : a.t;
+  const int n = (int)(Tb - Ta);
+  const int64_t kq_end = a.n_kq < Ta ? Ta : (a.n_kq > Tb ? Tb : a.n_kq);
+  const int64_t vq_end = a.n_vq < Ta ? Ta : (a.n_vq > Tb ? Tb : a.n_vq);
+  const int n_qk = (int)(kq_end - Ta), n_fk = (int)(Tb - kq_end);   // n_qk in {0, 32, 64}
+  const int n_qv = (int)(vq_end - Ta), n_fv = (int)(Tb - vq_end);
+  const int nqg = n_qk / kG;
+  const int nqv4 = (n_qv + 3) / 4;
+  // 16-byte DMA units of each region, in LDS order
+  const int u_krow = 0;
+  const int u_kc = u_krow + n_fk * 16;
+  const int u_ks = u_kc + nqg * 64;
+  const int u_kz = u_ks + nqg * 32;
+  const int u_vrow = u_kz + nqg * 32;
+  const int u_vc = u_vrow + n_fv * 16;
+  const int u_vs = u_vc + n_qv * 2;
+  const int u_vz = u_vs + 4 * nqv4;
+  const int u_end = u_vz + 4 * nqv4;           // <= 2048 units = 32 KB
+  char *lds = (char *)L.st;
+  for (int base = 0; base < u_end; base += 64) {
+    const int u = base + j;
+    if (u < u_end) {
+      const void *src;
+      if (u < u_kc) {
+        const int r = u / 16, part = u % 16;
+        src = a.k_res + ((bh * a.R + (kq_end + r) % a.R) * kD + part * 8);
+      } else if (u < u_ks) {
+        const int x = u - u_kc;
+        src = a.k_codes + ((bh * (a.cap / kG) + Ta / kG + x / 64) * 256 + (x % 64) * 4);
+      } else if (u < u_kz) {
+        const int x = u - u_ks;
+        src = a.k_scale + ((bh * (a.cap / kG) + Ta / kG + x / 32) * kD + (x % 32) * 4);
+      } else if (u < u_vrow) {
+        const int x = u - u_kz;
+        src = a.k_zero + ((bh * (a.cap / kG) + Ta / kG + x / 32) * kD + (x % 32) * 4);
+      } else if (u < u_vc) {
+        const int x = u - u_vrow;
+        src = a.v_res + ((bh * a.R + (vq_end + x / 16) % a.R) * kD + (x % 16) * 8);
+      } else if (u < u_vs) {
+        const int x = u - u_vc;
+        src = a.v_codes + ((bh * a.cap + Ta + x / 2) * 8 + (x % 2) * 4);
+      } else if (u < u_vz) {
+        const int x = u - u_vs;
+        src = a.v_scale + ((bh * 4 + x / nqv4) * a.cap + Ta + (x % nqv4) * 4);
+      } else {
+        const int x = u - u_vz;
+        src = a.v_zero + ((bh * 4 + x / nqv4) * a.cap + Ta + (x % nqv4) * 4);
+      }
+      load_lds(src, (lds_void *)(lds + (size_t)base * 16));
+    }
+  }
+  const uint16_t *q = a.q + ((int64_t)b * a.Hq + hk * NREP) * kD;
+  for (int e = j; e < NREP * kD; e += 64) L.q[e / kD][e % kD] = h2f(q[e]);
+  wait_staged();
+  wave_lds_sync();
+
+  const float LOG2E = 1.4426950408889634f;
+  // ---- scores: lane j scores token Ta + j for every head
+  float sc[NREP];
+#pragma unroll
+  for (int h = 0; h < NREP; ++h) sc[h] = 0.0f;
+  if (j < n) {
+    const int64_t tau = Ta + j;
+    if (tau < kq_end) {
+      const int gi = j / kG;
+      const int e = (int)(tau % kG);
+      const uint32_t *kc = (const uint32_t *)(lds + (size_t)u_kc * 16) + gi * 256 + e / 16;
+      const float *ks = (const float *)(lds + (size_t)u_ks * 16) + gi * kD;
+      const float *kz = (const float *)(lds + (size_t)u_kz * 16) + gi * kD;
+      const int sh = 2 * (e % 16);
+      for (int c = 0; c < kD; c += 4) {
+        const f4 s4 = *(const f4 *)(ks + c);
+        const f4 z4 = *(const f4 *)(kz + c);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float code = (float)((kc[(c + u) * 2] >> sh) & 3u);
+          const float kh = __fadd_rn(__fmul_rn(code, s4[u]), z4[u]);
+#pragma unroll
+          for (int h = 0; h < NREP; ++h) sc[h] = fmaf(L.q[h][c + u], kh, sc[h]);
+        }
+      }
+    } else {
+      const uint16_t *row = (const uint16_t *)(lds + (size_t)u_krow * 16) + (tau - kq_end) * kD;
+      for (int c = 0; c < kD; ++c) {
+        const float kh = h2f(row[c]);
+#pragma unroll
+        for (int h = 0; h < NREP; ++h) sc[h] = fmaf(L.q[h][c], kh, sc[h]);
+      }
+    }
+    const float mk = a.mask ? a.mask[(int64_t)b * a.t + tau] : 0.0f;
+#pragma unroll
+    for (int h = 0; h < NREP; ++h) sc[h] = (sc[h] * a.sm_scale + mk) * LOG2E;
+  } else {
+#pragma unroll
+    for (int h = 0; h < NREP; ++h) sc[h] = -INFINITY;
+  }
+  // ---- softmax over the chunk, per head
+  float mh[NREP], lh[NREP];
+#pragma unroll
+  for (int h = 0; h < NREP; ++h) {
+    float m = row_max(sc[h]);
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    const float pj = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sc[h] - m);
+    L.p[h][j] = pj;
+    mh[h] = m;
+    lh[h] = group_sum(row_sum(pj));
+  }
+  wave_lds_sync();
+  // ---- values: lane j owns channels 2j and 2j+1
+  float o[NREP][2];
+#pragma unroll
+  for (int h = 0; h < NREP; ++h) o[h][0] = o[h][1] = 0.0f;
+  const int c0 = 2 * j;
+  const int gch = c0 / kG;
+  const uint32_t *vc = (const uint32_t *)(lds + (size_t)u_vc * 16);
+  const float *vs = (const float *)(lds + (size_t)u_vs * 16) + gch * nqv4 * 4;
+  const float *vz = (const float *)(lds + (size_t)u_vz * 16) + gch * nqv4 * 4;
+  const uint16_t *vrow = (const uint16_t *)(lds + (size_t)u_vrow * 16);
+  for (int t = 0; t < n; ++t) {
+    float v0, v1;
+    if (t < n_qv) {
+      const uint32_t w = vc[t * 8 + c0 / 16] >> (2 * (c0 % 16));
+      v0 = __fadd_rn(__fmul_rn((float)(w & 3u), vs[t]), vz[t]);
+      v1 = __fadd_rn(__fmul_rn((float)((w >> 2) & 3u), vs[t]), vz[t]);
+    } else {
+      const uint32_t hv = *(const uint32_t *)(vrow + (t - n_qv) * kD + c0);
+      v0 = h2f((uint16_t)(hv & 0xFFFFu));
+      v1 = h2f((uint16_t)(hv >> 16));
+    }
+#pragma unroll
+    for (int h = 0; h < NREP; ++h) {
+      const float pt = L.p[h][t];
+      o[h][0] = fmaf(pt, v0, o[h][0]);
+      o[h][1] = fmaf(pt, v1, o[h][1]);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < NREP; ++h) {
+    float *dst = a.part + (((int64_t)b * a.Hq + hk * NREP + h) * a.S_total + slot) * (kD + 2);
+    *(float2 *)(dst + c0) = make_float2(o[h][0], o[h][1]);
+    if (j == 0) {
+      dst[kD] = mh[h] == -INFINITY ? -INFINITY : mh[h] * 0.6931471805599453f;
+      dst[kD + 1] = lh[h];
+    }
+  }
+}
+
+// grid: (n_window + n_split, H, B); block: one wave.  Workgroups
+// [0, n_window) take the window role (dispatched first, so they overlap the
+// longer block role), the rest the block role.
+template <int NREP>
+__global__ void __launch_bounds__(64)
+decode_matrix_kernel(DecodeArgs a, int64_t n_main, int tps, int n_split, int n_window) {
+  __shared__ Stage sm_st[2];
+  __shared__ __attribute__((aligned(16))) float sm_p[4][kBT];
+  __shared__ __attribute__((aligned(16))) float sm_bias[16];
+  __shared__ __attribute__((aligned(16))) float sm_zt[16];
+  __shared__ __attribute__((aligned(16))) float sm_alpha[4];
+  __shared__ __attribute__((aligned(16))) float sm_q[4][kD];
+  const Lds L{sm_st, sm_p, sm_bias, sm_zt, sm_alpha, sm_q};
+  const int x = blockIdx.x;
+  if (x < n_window)
+    window_role<NREP>(a, n_main, x, n_split + x, L);
+  else
+    block_role<NREP>(a, n_main, tps, x - n_window, L);
+}
+
 bool decode_matrix_supported(const DecodeArgs &a) {
   return a.kb == 2 && a.vb == 2 && a.G == kG && a.D == kD &&
          (a.n_rep == 1 || a.n_rep == 2 || a.n_rep == 4);
 }
 
+int decode_matrix_window_chunks(const DecodeArgs &a, int64_t n_main) {
+  return (int)((a.t - n_main + 63) / 64);
+}
+
 hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int tokens_per_split,
                                 int n_splits, hipStream_t s) {
-  if (!decode_matrix_supported(a) || n_main % kBT != 0 || tokens_per_split % kBT != 0)
+  if (!decode_matrix_supported(a) || n_main % kBT != 0 || tokens_per_split % kBT != 0 ||
+      n_main > a.n_vq)
     return hipErrorInvalidValue;
-  if (n_splits <= 0) return hipSuccess;
-  dim3 grid((unsigned)n_splits, (unsigned)a.H, (unsigned)a.B);
+  const int n_window = decode_matrix_window_chunks(a, n_main);
+  if (n_splits + n_window <= 0) return hipSuccess;
+  if (n_splits + n_window > a.S_total) return hipErrorInvalidValue;
+  dim3 grid((unsigned)(n_window + n_splits), (unsigned)a.H, (unsigned)a.B);
   switch (a.n_rep) {
     case 1:
-      hipLaunchKernelGGL(decode_matrix_kernel<1>, grid, dim3(64), 0, s, a, n_main, tokens_per_split);
+      hipLaunchKernelGGL(decode_matrix_kernel<1>, grid, dim3(64), 0, s, a, n_main,
+                         tokens_per_split, n_splits, n_window);
       break;
     case 2:
-      hipLaunchKernelGGL(decode_matrix_kernel<2>, grid, dim3(64), 0, s, a, n_main, tokens_per_split);
+      hipLaunchKernelGGL(decode_matrix_kernel<2>, grid, dim3(64), 0, s, a, n_main,
+                         tokens_per_split, n_splits, n_window);
       break;
     default:
-      hipLaunchKernelGGL(decode_matrix_kernel<4>, grid, dim3(64), 0, s, a, n_main, tokens_per_split);
+      hipLaunchKernelGGL(decode_matrix_kernel<4>, grid, dim3(64), 0, s, a, n_main,
+                         tokens_per_split, n_splits, n_window);
       break;
   }
   return hipGetLastError();

@@ -51,10 +51,13 @@ struct DecodeArgs {
 hipError_t launch_decode_generic(const DecodeArgs &a, int64_t tok_begin, int tokens_per_split,
                                  int n_splits, int slot_base, hipStream_t s);
 
-// Matrix-core kernel over tokens [0, n_main) (n_main % 64 == 0), writing
-// partial slots [0, n_splits).  Returns hipErrorInvalidValue for shapes it
-// does not handle.
+// Matrix-core kernel for 2-bit caches with G = 32, D = 128 and 1, 2 or 4
+// query heads per KV head.  Returns hipErrorInvalidValue for other shapes.
 bool decode_matrix_supported(const DecodeArgs &a);
+// Window chunks (64 tokens each) that cover tokens [n_main, t).
+int decode_matrix_window_chunks(const DecodeArgs &a, int64_t n_main);
+// One launch: block role over [0, n_main) in n_splits splits (partial slots
+// [0, n_splits)), window role over [n_main, t) (slots after those).
 hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int tokens_per_split,
                                 int n_splits, hipStream_t s);
 
