@@ -28,6 +28,33 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["decode_attention_pack_amd/csrc/" + f for f in
+                  ("api.cpp", "decode_matrix.hip", "decode_generic.hip", "kivi_internal.hpp",
+                   "kivi_device.hpp")] + ["decode_attention_pack_amd/build.py"]
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the sources and build flags of the attention kernels."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per attention launch from the committed counter record of this
+    workload, or None when there is none or the kernels changed since."""
+    path = os.path.join(PROFILES, f"traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
 
 
 def attn_bytes(w, t: int) -> int:
@@ -90,7 +117,12 @@ def main():
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--layers", type=int, default=0, help="layer replicas (0 = auto, >= 1 GiB)")
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 scalar kernel, 2 matrix kernel")
+    ap.add_argument("--tokens-per-split", type=int, default=0,
+                    help="split size of the attention call (0 = the library's automatic plan)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="after the timed steps, run one plain device-to-device copy of this "
+                         "many MiB (a known-size reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the KIVI decode path "
@@ -133,7 +165,7 @@ def main():
     v1 = torch.from_numpy(inp["v_steps"][0]).to(dev)
     q = torch.from_numpy(inp["q_steps"][0]).to(dev)
     out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
-    ws = caches[0].new_workspace(w.Hq, 0, args.path)
+    ws = caches[0].new_workspace(w.Hq, args.tokens_per_split, args.path)
     torch.cuda.synchronize()
 
     def step(i, ev=None):
@@ -142,7 +174,8 @@ def main():
         kivi.kivi_append(c, k1, v1, stream=stream)
         if ev is not None:
             ev[0].record(stream)
-        kivi.kivi_decode_attn(c, q, out=out, workspace=ws, path=args.path, stream=stream)
+        kivi.kivi_decode_attn(c, q, out=out, workspace=ws, tokens_per_split=args.tokens_per_split,
+                              path=args.path, stream=stream)
         if ev is not None:
             ev[1].record(stream)
         return attn_bytes(w, t_before + 1), append_bytes(w, t_before)
@@ -164,6 +197,12 @@ def main():
         p_bytes += pb
     stop.record(stream)
     torch.cuda.synchronize()
+    if args.calibration_copy_mib > 0:
+        src = torch.empty(args.calibration_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     total_ms = start.elapsed_time(stop)
     attn_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
     ms_step = total_ms / args.steps
@@ -195,7 +234,7 @@ def main():
         "attn_pct_of_peak": round(100 * attn_gbps / HBM_PEAK_GBPS, 1),
         "roofline": {"bound": "hbm", "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(w.name),
                      "kernel": "kivi_decode_attn launch (split kernel + combine)",
                      "bytes_per_launch": a_bytes // args.steps},
     }

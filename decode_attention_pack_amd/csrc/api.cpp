@@ -95,14 +95,14 @@ int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
 
 constexpr int kGenericMinSplit = 256;
 constexpr int kMatrixBlock = 128;   // tokens per block of the matrix-core kernel
-constexpr int kTargetWorkgroups = 2048;
+constexpr int kTargetWorkgroups = 4096;
 
 struct Plan {
   bool matrix = false;
   int64_t n_main = 0;           // tokens [0, n_main) in the matrix kernel's block role
   int tps_matrix = 0;
   int n_split_matrix = 0;
-  int n_window = 0;             // 64-token chunks of [n_main, t) in its window role
+  int n_window = 0;             // 32-token chunks of [n_main, t) in its window role
   int tps_generic = 0;          // scalar kernel (shapes the matrix kernel does not cover)
   int n_split_generic = 0;
   int S_total = 0;
@@ -117,14 +117,15 @@ Plan make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
   const int64_t t = c->n_tokens;
   const int n_rep = Hq / c->n_kv_heads;
   const int64_t units = (int64_t)c->batch * c->n_kv_heads;
-  p.matrix = path != KIVI_PATH_GENERIC && kivi::decode_matrix_supported(a);
+  p.matrix = path != KIVI_PATH_GENERIC && t > 0 && kivi::decode_matrix_supported(a);
   if (p.matrix) {
     p.n_main = (a.n_vq / kMatrixBlock) * kMatrixBlock;
     int64_t tps = (tps_req + kMatrixBlock - 1) / kMatrixBlock * kMatrixBlock;
     if (tps == 0) {
+      // whole blocks per split, about kTargetWorkgroups workgroups in all
       const int64_t splits = max64(1, kTargetWorkgroups / units);
-      tps = ((p.n_main + splits - 1) / splits + 255) / 256 * 256;
-      tps = max64(tps, 256);
+      const int64_t blocks = p.n_main / kMatrixBlock;
+      tps = max64(1, (blocks + splits - 1) / splits) * kMatrixBlock;
     }
     p.tps_matrix = (int)tps;
     p.n_split_matrix = (int)((p.n_main + tps - 1) / tps);
@@ -147,11 +148,13 @@ Plan make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
 
 // Upper bound on partial slots for any n_tokens <= capacity.
 int64_t max_slots(const kivi_cache *c, int32_t tps_req) {
-  const int64_t step = tps_req > 0 ? tps_req : kGenericMinSplit;
+  // automatic plans split at least kMatrixBlock tokens at a time
+  const int64_t step = tps_req > 0 ? tps_req : kMatrixBlock;
   // splits over the capacity, plus the matrix kernel's window chunks (its
   // window is at most one block + R tokens long)
-  return (c->capacity + step - 1) / step + (kMatrixBlock + (int64_t)c->residual + 63) / 64 + 1;
+  return (c->capacity + step - 1) / step + (kMatrixBlock + (int64_t)c->residual + 31) / 32 + 1;
 }
+
 
 }  // namespace
 
@@ -246,7 +249,8 @@ size_t kivi_decode_attn_workspace_bytes_ex(const kivi_cache *c, int32_t n_q_head
   if (n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0) return 0;
   if (tokens_per_split < 0 || tokens_per_split % 64 != 0) return 0;
   if (path < KIVI_PATH_AUTO || path > KIVI_PATH_MATRIX) return 0;
-  return (size_t)c->batch * n_q_heads * max_slots(c, tokens_per_split) * (c->head_dim + 2) *
+  // partial slots: acc[D], m, l, padded to D + 4 floats (16-byte rows)
+  return (size_t)c->batch * n_q_heads * max_slots(c, tokens_per_split) * (c->head_dim + 4) *
          sizeof(float);
 }
 
@@ -309,13 +313,12 @@ int kivi_decode_attn_ex(const kivi_cache *c, const void *q_fp16, int32_t n_q_hea
     return fail(KIVI_ERR_WORKSPACE, "%s: internal split plan exceeds the workspace bound", who);
   a.S_total = p.S_total;
   hipStream_t s = (hipStream_t)stream;
-  if (p.matrix) {
+  if (p.matrix)
     rc = hip_status(kivi::launch_decode_matrix(a, p.n_main, p.tps_matrix, p.n_split_matrix, s),
                     "kivi_decode_attn (matrix)");
-  } else {
+  else
     rc = hip_status(kivi::launch_decode_generic(a, 0, p.tps_generic, p.n_split_generic, 0, s),
                     "kivi_decode_attn (scalar)");
-  }
   if (rc) return rc;
   return hip_status(kivi::launch_combine(a, s), "kivi_decode_attn (combine)");
 }

@@ -176,7 +176,7 @@ decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int
       float s = 0.0f;
       for (int p = 0; p < n_par; ++p) s += red_s[p * D + tid];
       float *dst = a.part + (((int64_t)b * a.Hq + hq0 + j) * a.S_total + slot_base + split) *
-                                (int64_t)(D + 2);
+                                (int64_t)(D + 4);
       dst[tid] = s;
       if (tid == 0) {
         dst[D] = m[j];
@@ -187,56 +187,79 @@ decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int
   }
 }
 
-// grid: B * Hq; block: 256.  out = sum_i acc_i e^(m_i - M) / sum_i l_i e^(m_i - M)
-// with M = max_i m_i, over the S_total partial slots of one (batch, query head).
+// grid: (B * Hq, ceil(D / 32)); block: 256.
+// out = sum_s acc_s e^(m_s - M) / sum_s l_s e^(m_s - M), M = max_s m_s, over
+// the S_total partial slots of one (batch row, query head).  Thread
+// (slot group sg = tid / 8, channel quad cq = tid % 8) merges slots
+// s = sg (mod 32) for 4 channels with a running maximum, loading up to 8 of
+// its slots at once; the 32 slot groups are then merged through LDS.  A
+// workgroup covers 32 channels, so most rows need one round trip to memory.
 __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
-  __shared__ float w_s[256];
-  __shared__ float red_s[256];
+  __shared__ float red_m[32];
+  __shared__ float red_l[32];
+  __shared__ float4 red_o[32][8];
   const int64_t row = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int D = a.D, S = a.S_total, stride = D + 2;
+  const int sg = threadIdx.x >> 3, cq = threadIdx.x & 7;
+  const int D = a.D, S = a.S_total, stride = D + 4;
+  const int c = blockIdx.y * 32 + cq * 4;
+  const bool c_ok = c < D;               // D is a multiple of 8
   const float *p = a.part + row * S * (int64_t)stride;
 
-  float M = -INFINITY;
-  for (int i = tid; i < S; i += 256) M = fmaxf(M, p[(int64_t)i * stride + D]);
-  M = wave_max(M);
-  if ((tid & 63) == 0) red_s[tid >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
-  __syncthreads();
-
-  const int c = tid % D, par = tid / D, n_par = 256 / D;
-  float L = 0.0f, o = 0.0f;
-  for (int base = 0; base < S; base += 256) {
-    const int i = base + tid;
-    float w = 0.0f;
-    if (i < S && M != -INFINITY) {
-      const float mi = p[(int64_t)i * stride + D];
-      if (mi != -INFINITY) {
-        w = expf(mi - M);
-        L = fmaf(p[(int64_t)i * stride + D + 1], w, L);
+  float M = -INFINITY, L = 0.0f;
+  float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int s0 = sg; s0 < S; s0 += 32 * 8) {
+    float2 ml[8];
+    float4 acc[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + 32 * u;
+      ml[u] = make_float2(-INFINITY, 0.0f);
+      acc[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (s < S) {
+        const float *ps = p + (int64_t)s * stride;
+        ml[u] = *(const float2 *)(ps + D);
+        if (c_ok) acc[u] = *(const float4 *)(ps + c);
       }
     }
-    w_s[tid] = w;
-    __syncthreads();
-    const int cnt = min(256, S - base);
-    if (par < n_par) {
-#pragma unroll 8
-      for (int k = par; k < cnt; k += n_par) o = fmaf(p[(int64_t)(base + k) * stride + c], w_s[k], o);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (ml[u].x == -INFINITY) continue;
+      const float Mn = fmaxf(M, ml[u].x);
+      const float r = __expf(M - Mn);     // 0 while M = -inf
+      const float w = __expf(ml[u].x - Mn);
+      L = fmaf(L, r, ml[u].y * w);
+      o.x = fmaf(o.x, r, acc[u].x * w);
+      o.y = fmaf(o.y, r, acc[u].y * w);
+      o.z = fmaf(o.z, r, acc[u].z * w);
+      o.w = fmaf(o.w, r, acc[u].w * w);
+      M = Mn;
     }
-    __syncthreads();
   }
-  L = wave_sum(L);
-  if ((tid & 63) == 0) red_s[tid >> 6] = L;
+  if (cq == 0) {
+    red_m[sg] = M;
+    red_l[sg] = L;
+  }
+  red_o[sg][cq] = o;
   __syncthreads();
-  L = red_s[0] + red_s[1] + red_s[2] + red_s[3];
-  __syncthreads();
-  red_s[tid] = par < n_par ? o : 0.0f;
-  __syncthreads();
-  if (tid < D) {
-    float sum = 0.0f;
-    for (int q = 0; q < n_par; ++q) sum += red_s[q * D + tid];
-    a.out[row * D + tid] = L > 0.0f ? sum / L : 0.0f;
+  if (sg == 0 && c_ok) {
+    float Mx = -INFINITY;
+    for (int k = 0; k < 32; ++k) Mx = fmaxf(Mx, red_m[k]);
+    float Lt = 0.0f;
+    float4 ot = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (Mx != -INFINITY) {
+      for (int k = 0; k < 32; ++k) {
+        if (red_m[k] == -INFINITY) continue;
+        const float w = __expf(red_m[k] - Mx);
+        Lt = fmaf(red_l[k], w, Lt);
+        const float4 v = red_o[k][cq];
+        ot.x = fmaf(v.x, w, ot.x);
+        ot.y = fmaf(v.y, w, ot.y);
+        ot.z = fmaf(v.z, w, ot.z);
+        ot.w = fmaf(v.w, w, ot.w);
+      }
+    }
+    const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
+    *(float4 *)(a.out + row * D + c) = make_float4(ot.x * inv, ot.y * inv, ot.z * inv, ot.w * inv);
   }
 }
 
@@ -251,7 +274,9 @@ hipError_t launch_decode_generic(const DecodeArgs &a, int64_t tok_begin, int tok
 }
 
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(a.B * a.Hq)), dim3(256), 0, s, a);
+  if (a.D % 8 != 0 || a.S_total <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(a.B * a.Hq), (unsigned)((a.D + 31) / 32)),
+                     dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -5,39 +5,44 @@
 // Method source: web page "Literature audit -- Group 2 (KV-cache compression
 // primary sources)", section "1. KIVI -- kivi2024", list "Core algorithm
 // (implementation-grade)", item 5: scores q.deq(K)^T over the quantized keys,
-// softmax, then P.deq(V) over the quantized values.  The matrix-core role of
-// this kernel covers the tokens whose key AND value are both quantized, in
-// whole blocks of 128 tokens; a second role, in the same launch, covers the
-// rest (the fp16 window and the quantized tokens past the last whole block)
-// with scalar arithmetic.  Each workgroup writes a partial (acc, m, l) and
-// the combine kernel merges them.
+// softmax, then P.deq(V) over the quantized values, plus the fp16 window.
+//
+// One launch does the whole call.  Its workgroups (one wave each) take one of
+// two roles for one (batch row, KV head) slab:
+//  * block role: the tokens whose key AND value are both quantized, in whole
+//    blocks of 128, on the matrix cores (one split of the slab each);
+//  * window role: the rest -- the fp16 window and the quantized tokens past
+//    the last whole block -- 32 tokens per workgroup, scalar fp32.
+// Each workgroup writes a partial (acc[128], m, l) per query head; the
+// combine kernel merges them with the log-sum-exp rule.
 //
 // Algebra.  With a key group's scale s and zero z (per channel c, 32 tokens),
 //   q . K_tau = sum_c (q_c s_c) code_{c,tau} + sum_c q_c z_c,
 // and for values (scale/zero per token tau and 32-channel group),
 //   sum_tau p_tau V_{tau,c} = sum_tau (p_tau s_tau) code_{tau,c} + sum_tau p_tau z_tau.
 // The first sums are dense contractions with small-integer codes, done on the
-// matrix cores as fp16 x fp16 -> fp32 products.  Codes 0..3 are exact as fp16
+// matrix cores as fp16 x fp16 -> fp32 products.  The codes are exact fp16
 // values; the fp32 factors (q s) and (p s) are split into an fp16 high part
-// and an fp16 low part (the rounding residual), each multiplied in its own
-// MFMA, which keeps about 22 significant bits.  The zero-point sums are plain
-// fp32 dot products.
+// and an fp16 low part, each multiplied in its own MFMA, which keeps about 21
+// significant bits.  The zero-point sums are plain fp32 dot products.
 //
 // Operand delivery.  The 2-bit codes are packed along tokens for keys and
 // along channels for values, i.e. along the axis that is NOT contracted.  The
 // gfx950 LDS transpose read (ds_read_b64_tr_b4) turns 16 rows of 64 bits into
 // 16 columns of 4-bit nibbles across a 16-lane group, which puts a pair of
 // codes per nibble exactly where the MFMA B operand wants it: a lane then
-// holds, for one token (keys) or one channel (values), the codes of 16
-// consecutive contraction indices.  A shift and an and-or place a code c in
-// the top mantissa bits of an fp16 1.0, giving the exact normal value 1 + c/4
-// (low code of a nibble) or 1 + c/16 (high code); a packed fp16 subtraction
-// of 1 leaves c/4 or c/16, exact and normal (or zero).  Two encodings that
-// skip the subtraction lose accuracy on the matrix core: codes as fp16
-// subnormals (it keeps only ~14 bits when it adds the two products of one
-// register whose B halves are subnormal), and 1 + c/4 with the sum of A
-// removed afterwards (the large constant part cancels, and the rounding of
-// the fp32 accumulation is magnified 4x and 16x).
+// holds, for one token pair (keys) or one channel pair (values), the codes of
+// 16 consecutive contraction indices.  A nibble masked down to one code is an
+// FP4 (E2M1) number of value code/2, and the gfx950 packed FP4 -> FP16
+// conversion with scale 2 turns two such nibbles into two exact fp16 codes in
+// one instruction.
+//
+// Memory pipeline.  A block's key part (codes, scales, zeros: 8 KB) and value
+// part (8 KB) have one LDS buffer each, filled by global->LDS DMA.  The next
+// block's key part is requested as soon as the current one has been read into
+// registers, and likewise for the value part, so each DMA overlaps the other
+// half's arithmetic.  With ~19 KB of LDS per workgroup, eight workgroups (two
+// waves per SIMD) fit on a CU.
 #include <math.h>
 
 #include "kivi_internal.hpp"
@@ -47,121 +52,166 @@ namespace kivi {
 namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef int i2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) i2 lds_i2;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kD = 128;
 constexpr int kG = 32;
-constexpr int kBT = 128;   // tokens per block
-#ifndef KIVI_MATRIX_KEY_LO
-#define KIVI_MATRIX_KEY_LO 1
-#endif
-#ifndef KIVI_MATRIX_VALUE_LO
-#define KIVI_MATRIX_VALUE_LO 1
-#endif
+constexpr int kBT = 128;       // tokens per block (block role)
+constexpr int kWT = 32;        // tokens per chunk (window role)
+constexpr int kStageDma = 8;   // DMA instructions per key or value part
 
-// One block of the packed cache, staged in LDS exactly as it sits in HBM
-// (except the value scale/zero, gathered per channel group).
-struct alignas(16) Stage {
+// A block's key part and value part in LDS, as they sit in HBM (the value
+// scale/zero gathered per channel group).
+struct alignas(16) KStage {
   uint32_t kc[1024];   // 4 key groups x 128 channels x 2 words
   float ks[512];       // [4 groups][128 channels]
   float kz[512];
+};
+struct alignas(16) VStage {
   uint32_t vc[1024];   // 128 tokens x 8 words
   float vs[512];       // [4 channel groups][128 tokens]
   float vz[512];
 };
 
-
-__device__ __forceinline__ void load_lds(const void *g, lds_void *l) {
+__device__ __forceinline__ void dma16(const void *g, lds_void *l) {
   __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
 }
+__device__ __forceinline__ void dma4(const void *g, lds_void *l) {
+  __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
+}
 
-// Stage block `blk` (tokens [128 blk, 128 blk + 128)) of slab bh.
-__device__ __forceinline__ void stage_block(const DecodeArgs &a, int64_t bh, int64_t blk,
-                                           Stage *s, int lane) {
-  const int64_t tau0 = blk * kBT;
-  const int64_t g0 = tau0 / kG;
-  const uint32_t *kc = a.k_codes + (bh * (a.cap / kG) + g0) * (kD * 2);
-  const float *ks = a.k_scale + (bh * (a.cap / kG) + g0) * kD;
-  const float *kz = a.k_zero + (bh * (a.cap / kG) + g0) * kD;
-  const uint32_t *vc = a.v_codes + (bh * a.cap + tau0) * 8;
+// Key part of block `blk` (tokens [128 blk, 128 blk + 128)) of slab bh:
+// kStageDma DMA instructions, plus 2 for the mask when there is one.
+template <bool MASKED>
+__device__ __forceinline__ void stage_keys(const DecodeArgs &a, int64_t bh, int64_t blk,
+                                           KStage *s, float *mask_s, int lane) {
+  const int64_t base = bh * (a.cap / kG) + blk * (kBT / kG);
+  const uint32_t *kc = a.k_codes + base * (kD * 2);
+  const float *ks = a.k_scale + base * kD;
+  const float *kz = a.k_zero + base * kD;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    load_lds(kc + i * 256 + lane * 4, (lds_void *)(s->kc + i * 256));
-    load_lds(vc + i * 256 + lane * 4, (lds_void *)(s->vc + i * 256));
-  }
+  for (int i = 0; i < 4; ++i) dma16(kc + i * 256 + lane * 4, (lds_void *)(s->kc + i * 256));
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    load_lds(ks + i * 256 + lane * 4, (lds_void *)(s->ks + i * 256));
-    load_lds(kz + i * 256 + lane * 4, (lds_void *)(s->kz + i * 256));
-    const int gch = 2 * i + (lane >> 5);
-    const int64_t off = (bh * 4 + gch) * a.cap + tau0 + (lane & 31) * 4;
-    load_lds(a.v_scale + off, (lds_void *)(s->vs + i * 256));
-    load_lds(a.v_zero + off, (lds_void *)(s->vz + i * 256));
+    dma16(ks + i * 256 + lane * 4, (lds_void *)(s->ks + i * 256));
+    dma16(kz + i * 256 + lane * 4, (lds_void *)(s->kz + i * 256));
+  }
+  if (MASKED) {
+    // dword copies: a mask row need not be 16-byte aligned
+    const float *m = a.mask + (bh / a.H) * a.t + blk * kBT;
+    dma4(m + lane, (lds_void *)mask_s);
+    dma4(m + 64 + lane, (lds_void *)(mask_s + 64));
   }
 }
 
-__device__ __forceinline__ i2 tr4(const uint32_t *p) {
-  return __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i2 *)p);
+// Value part of block `blk`: kStageDma DMA instructions.
+__device__ __forceinline__ void stage_values(const DecodeArgs &a, int64_t bh, int64_t blk,
+                                             VStage *s, int lane) {
+  const int64_t tau0 = blk * kBT;
+  const uint32_t *vc = a.v_codes + (bh * a.cap + tau0) * 8;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dma16(vc + i * 256 + lane * 4, (lds_void *)(s->vc + i * 256));
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int gch = 2 * i + (lane >> 5);
+    const int64_t off = (bh * 4 + gch) * a.cap + tau0 + (lane & 31) * 4;
+    dma16(a.v_scale + off, (lds_void *)(s->vs + i * 256));
+    dma16(a.v_zero + off, (lds_void *)(s->vz + i * 256));
+  }
 }
 
-// B operand from one transposed dword holding nibbles 0..7.  Element 2r+e of
-// `be` is c/4 for the low code c of nibble r+4e, element 2r+e of `bo` is c/16
-// for its high code (exact fp16 values).
-__device__ __forceinline__ void split_codes(uint32_t x, h8 &be, h8 &bo) {
-  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-  const uint32_t l8 = x << 8, l4 = x << 4, r4 = x >> 4, r8 = x >> 8;
-  const uint32_t ONE = 0x3C003C00u, ME = 0x03000300u, MO = 0x00C000C0u;
-  u4 e = {(l8 & ME) | ONE, (l4 & ME) | ONE, (x & ME) | ONE, (r4 & ME) | ONE};
-  u4 o = {(l4 & MO) | ONE, (x & MO) | ONE, (r4 & MO) | ONE, (r8 & MO) | ONE};
-  const h8 one = {1, 1, 1, 1, 1, 1, 1, 1};
-  be = __builtin_bit_cast(h8, e) - one;
-  bo = __builtin_bit_cast(h8, o) - one;
+// LDS transpose read, issued as inline assembly: the compiler's builtin for it
+// carries no information on which LDS object it reads, so the compiler would
+// wait for every DMA in flight (into either buffer) before it.  Its result is
+// only valid after wait_regs() on it.
+__device__ __forceinline__ i2 tr4(const uint32_t *p) {
+  i2 r;
+  const uint32_t addr = (uint32_t)(uintptr_t)(lds_void *)p;
+  asm volatile("ds_read_b64_tr_b4 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+
+// Wait for this wave's LDS reads, including the transpose reads whose
+// results are in x[0..7].
+__device__ __forceinline__ void wait_regs(i2 (&x)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]),
+                 "+v"(x[6]), "+v"(x[7])::"memory");
+}
+
+// B operands from one transposed dword holding nibbles 0..7 (two codes
+// each): element n of `be` is the low code of nibble n, element n of `bo`
+// its high code, as exact fp16 integers 0..3.
+__device__ __forceinline__ void codes_to_b(uint32_t x, h8 &be, h8 &bo) {
+  const uint32_t lo = x & 0x33333333u;
+  const uint32_t hi = (x >> 2) & 0x33333333u;
+  const h2v e0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo, 2.0f, 0);
+  const h2v e1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo, 2.0f, 1);
+  const h2v e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo, 2.0f, 2);
+  const h2v e3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo, 2.0f, 3);
+  const h2v o0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(hi, 2.0f, 0);
+  const h2v o1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(hi, 2.0f, 1);
+  const h2v o2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(hi, 2.0f, 2);
+  const h2v o3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(hi, 2.0f, 3);
+  be = (h8){e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
+  bo = (h8){o0[0], o0[1], o1[0], o1[1], o2[0], o2[1], o3[0], o3[1]};
 }
 
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Reductions over the 16 lanes of a row (DPP row rotations by 8, 4, 2, 1).
+#define KIVI_ROR(v, c) \
+  __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), c, 0xF, 0xF, false))
 __device__ __forceinline__ float row_max(float v) {
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false)));
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false)));
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false)));
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false)));
+  v = fmaxf(v, KIVI_ROR(v, 0x128));
+  v = fmaxf(v, KIVI_ROR(v, 0x124));
+  v = fmaxf(v, KIVI_ROR(v, 0x122));
+  v = fmaxf(v, KIVI_ROR(v, 0x121));
   return v;
 }
-
 __device__ __forceinline__ float row_sum(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false));
+  v += KIVI_ROR(v, 0x128);
+  v += KIVI_ROR(v, 0x124);
+  v += KIVI_ROR(v, 0x122);
+  v += KIVI_ROR(v, 0x121);
+  return v;
+}
+#undef KIVI_ROR
+
+// Sum / max over the 4 lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float group_sum(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
   return v;
 }
 
 // The workgroup is a single wave, whose LDS accesses complete in order, so
 // sharing data through LDS between its lanes needs only the wave's own LDS
 // operations to finish -- not the memory fence of a workgroup barrier, which
-// would also wait for the prefetch DMA in flight.
+// would also wait for the DMA in flight.
 __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-// Wait for this wave's outstanding global->LDS copies.
-__device__ __forceinline__ void wait_staged() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// Wait until at most N of this wave's vector-memory operations (DMA
+// included) are outstanding; they complete in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Sum over the 4 lane groups (lanes l, l^16, l^32, l^48).
-__device__ __forceinline__ float group_sum(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
-}
-
-// hi/lo fp16 split of two products x0*y0, x1*y1 (one A-operand register):
+// hi/lo fp16 split of two products x0*y0, x1*y1 into elements k, k+1:
 // hi = the fp32 product truncated to fp16, lo = rn16(exact product - hi), so
 // hi + lo carries ~21 significant bits.  hi comes from an intrinsic the
 // compiler cannot re-derive: were the register's hi and the hi subtracted for
@@ -176,33 +226,33 @@ __device__ __forceinline__ void split_mul2(float x0, float y0, float x1, float y
   lo[k + 1] = (_Float16)__builtin_fmaf(x1, y1, -(float)h[1]);
 }
 
+__device__ __forceinline__ float max8(f4 a, f4 b) {
+  return fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])),
+               fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])));
+}
+
 }  // namespace
 
-// grid: (n_split, H, B); block: one wave.  Split `split` covers tokens
-// [split * tps, min(n_main, (split + 1) * tps)).
-// LDS of the kernel.  Separate objects, so the compiler can tell that writes
-// to the small arrays never touch the stage buffer being filled by DMA.
+// LDS of the kernel.  Separate objects, so the compiler can tell that LDS
+// accesses of the arithmetic never touch a buffer being filled by DMA.
 struct Lds {
-  Stage *st;           // [2]
-  float (*p)[kBT];     // [4][kBT] probabilities of the block, per query head
-  float *bias;         // [16]: sum q z per A row
-  float *zt;           // [16]: sum p z per A row
+  KStage *ks;          // key part of the block (window role: its key staging)
+  VStage *vs;          // value part (window role: its value staging)
+  float (*p)[kBT];     // [4][128] probabilities of the block (window role: q)
+  float *mask;         // [128] mask of the block (window role: probabilities)
+  float *bias;         // [16] per A row: sum q z (keys), then sum p z (values)
   float *alpha;        // [4]
-  float (*q)[kD];      // [4][kD] (window role)
 };
 
 // Matrix-core role: split `split` covers the fully quantized tokens
 // [split * tps, min(n_main, (split + 1) * tps)) in blocks of 128.
-template <int NREP>
+template <int NREP, bool MASKED>
 __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, int tps,
-                                           int split, const Lds &L) {
+                                           int split, const Lds &L, KStage *__restrict__ kbuf,
+                                           VStage *__restrict__ vbuf) {
   static_assert(NREP == 1 || NREP == 2 || NREP == 4, "query heads per KV head");
   constexpr int GA = 16 / NREP;       // key groups per A operand
-  Stage *sm_st = L.st;
-  float (*sm_p)[kBT] = L.p;
-  float *sm_bias = L.bias;
-  float *sm_zt = L.zt;
-  float *sm_alpha = L.alpha;
+  constexpr int KDMA = kStageDma + (MASKED ? 2 : 0);
 
   const int lane = threadIdx.x;
   const int i = lane & 15;
@@ -215,10 +265,10 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
   if (blk_end * kBT > n_main) blk_end = n_main / kBT;
 
   // --- roles of this lane
-  // A operand of the key contraction: row m = i is (head h_a, group slot g_a)
+  // key A operand: row m = i is (head h_a, key group g_a)
   const int h_a = min(i / GA, NREP - 1);
   const int g_a = (i % GA) & 3;
-  // A operand of the value contraction: row m = i is (head h_v, channel group c_v)
+  // value A operand: row m = i is (head h_v, channel group c_v)
   const int h_v = min(i / 4, NREP - 1);
   const int c_v = i & 3;
   // score / output lanes: rows 4 kg .. 4 kg + 3 of the MFMA result
@@ -226,7 +276,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
   const int h_s = (kg * NREP) / 4;               // head of the scores this lane holds
   const bool v_valid = kg < NREP;                // head of the outputs this lane holds = kg
 
-  // q of head h_a at this lane's 32 key channels, odd channels scaled by 1/16
+  // q of head h_a at this lane's 32 key channels c0(ks) + j
   float qa[4][8];
   {
     const uint16_t *q = a.q + ((int64_t)b * a.Hq + hk * NREP + h_a) * kD;
@@ -237,92 +287,62 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
       for (int j = 0; j < 8; ++j) qa[ks][j] = h2f(q[c0 + j]);
     }
   }
-
-  // The key-side A operand is q * s_k * 2^ek, with ek kept so that the
-  // largest |q| times the block's largest key scale stays below 2^14 (no fp16
-  // overflow for any fp16 input range).  qa carries the current 2^ek.
+  // The key A operand is q * s_k * 2^ek, with ek kept so that the largest |q|
+  // times the block's largest key scale stays below 2^14 (no fp16 overflow,
+  // and small products stay clear of the fp16 subnormal range); qa carries
+  // the current 2^ek.
   float qmax = 0.0f;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
     for (int j = 0; j < 8; ++j) qmax = fmaxf(qmax, fabsf(qa[ks][j]));
-  qmax = row_max(qmax);
-  qmax = fmaxf(qmax, __shfl_xor(qmax, 16));
-  qmax = fmaxf(qmax, __shfl_xor(qmax, 32));
+  qmax = group_max(row_max(qmax));
   int ek_run = 0;
 
   const float LOG2E = 1.4426950408889634f;
-  const float c_bias = a.sm_scale * LOG2E;                 // 1/sqrt(D) * log2(e)
-  const float c_even = 4.0f * c_bias;                      // 1 + c/4 codes
-  const float c_odd = 16.0f * c_bias;                      // 1 + c/16 codes
+  const float c_bias = a.sm_scale * LOG2E;    // scores in log2 units
 
-  // The value-side A operand is p * s_v * 2^ev, with the power of two ev set
-  // per block from the block's largest value scale so that the fp16 split
-  // stays in the normal range (p can be as small as 2^-20 and still matter).
+  // The value A operand is p * s_v * 2^ev, ev set per block from the block's
+  // largest value scale (p <= 1), for the same reasons.  zt (sum p z) stays
+  // in plain units.
   int ev_run = 0;
   float m_run = -INFINITY;     // running max (log2 units), head h_s
   float l_run = 0.0f;          // this lane's share of the running sum
-  float zt = 0.0f;    // value zero-point sum  sum p' z, row (h_v, c_v)
+  float zt = 0.0f;             // sum p z, value A row (h_v, c_v)
   f4 dv[4][2];
 #pragma unroll
   for (int g = 0; g < 4; ++g) dv[g][0] = dv[g][1] = (f4){0, 0, 0, 0};
 
-  if (blk_begin < blk_end) stage_block(a, bh, blk_begin, &sm_st[0], lane);
+  if (blk_begin < blk_end) {
+    stage_keys<MASKED>(a, bh, blk_begin, kbuf, L.mask, lane);
+    stage_values(a, bh, blk_begin, vbuf, lane);
+  }
 
   for (int64_t blk = blk_begin; blk < blk_end; ++blk) {
-    const int cur = (int)((blk - blk_begin) & 1);
-    wait_staged();
-    const Stage &st = sm_st[cur];
-    // Transposed code reads first: the LDS transpose read carries no alias
-    // information, so the compiler orders it behind every outstanding LDS
-    // DMA; issuing the next block's DMA after these reads keeps it in flight
-    // during the arithmetic below.
-    i2 xk[4][2], xv[2][4];
+    const bool has_next = blk + 1 < blk_end;
+    // ================= key half =================
+    wait_vm<kStageDma>();            // key part of blk in; its value part may still fly
+    const KStage &kst = *kbuf;
+    i2 xk[8];                        // [group g][64-channel half rho]
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int rho = 0; rho < 2; ++rho)
-        xk[g][rho] = tr4(st.kc + g * 256 + (64 * rho + 16 * kg + i) * 2);
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        xv[u][g] = tr4(st.vc + (32 * kg + 16 * u + i) * 8 + g * 2);
-    // mask values of this lane's tokens, read before the DMA is issued (a
-    // plain load would otherwise wait for the whole DMA to land)
+        xk[2 * g + rho] = tr4(kst.kc + g * 256 + (64 * rho + 16 * kg + i) * 2);
     float mk[4][2];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) mk[g][0] = mk[g][1] = 0.0f;
-    if (a.mask) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float2 m2 = *(const float2 *)(a.mask + (int64_t)b * a.t + blk * kBT + 32 * g + 2 * i);
+    for (int g = 0; g < 4; ++g) {
+      if (MASKED) {
+        const float2 m2 = *(const float2 *)(L.mask + 32 * g + 2 * i);
         mk[g][0] = m2.x * LOG2E;
         mk[g][1] = m2.y * LOG2E;
+      } else {
+        mk[g][0] = mk[g][1] = 0.0f;
       }
     }
-    // largest value scale of the block -> exponent ev for this block
-    int ev;
     {
-      const f4 v0 = *(const f4 *)(st.vs + lane * 8);
-      const f4 v1 = *(const f4 *)(st.vs + lane * 8 + 4);
-      float mx = fmaxf(fmaxf(fmaxf(v0[0], v0[1]), fmaxf(v0[2], v0[3])),
-                       fmaxf(fmaxf(v1[0], v1[1]), fmaxf(v1[2], v1[3])));
-      mx = row_max(mx);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // mx < 2^e with e = frexp exponent; p <= 1, so p * s * 2^(14 - e) < 2^14
-      ev = mx > 0.0f ? 14 - __builtin_amdgcn_frexp_expf(mx) : 0;
-      ev = __builtin_amdgcn_readfirstlane(ev);
-    }
-    {
-      const f4 k0 = *(const f4 *)(st.ks + lane * 8);
-      const f4 k1 = *(const f4 *)(st.ks + lane * 8 + 4);
-      float mx = fmaxf(fmaxf(fmaxf(k0[0], k0[1]), fmaxf(k0[2], k0[3])),
-                       fmaxf(fmaxf(k1[0], k1[1]), fmaxf(k1[2], k1[3])));
-      mx = row_max(mx);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float mx = max8(*(const f4 *)(kst.ks + lane * 8), *(const f4 *)(kst.ks + lane * 8 + 4));
+      mx = group_max(row_max(mx));
       const float prod = mx * qmax;
       int ek = prod > 0.0f ? 14 - __builtin_amdgcn_frexp_expf(prod) : ek_run;
       ek = __builtin_amdgcn_readfirstlane(ek);
@@ -335,30 +355,31 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
         ek_run = ek;
       }
     }
-    if (blk + 1 < blk_end) stage_block(a, bh, blk + 1, &sm_st[cur ^ 1], lane);
-
-    // ---- key side: A = hi/lo(q s), bias = q . z
+    // A = hi/lo(q s) for rows (h_a, g_a); bias = q . z
     h8 ah[4], al[4];
-    float bz = 0.0f;   // sum q z over this lane's channels
+    float bz = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int c0 = 64 * (ks >> 1) + 16 * kg + 8 * (ks & 1);
-      const float *sp = st.ks + g_a * kD + c0;
-      const float *zp = st.kz + g_a * kD + c0;
+      const f4 s0 = *(const f4 *)(kst.ks + g_a * kD + c0);
+      const f4 s1 = *(const f4 *)(kst.ks + g_a * kD + c0 + 4);
+      const f4 z0 = *(const f4 *)(kst.kz + g_a * kD + c0);
+      const f4 z1 = *(const f4 *)(kst.kz + g_a * kD + c0 + 4);
+      const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+      const float zv[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        split_mul2(qa[ks][r], sp[r], qa[ks][r + 4], sp[r + 4], ah[ks], al[ks], 2 * r);
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int j = r + 4 * e;
-          bz = fmaf(qa[ks][j], zp[j], bz);
-        }
+      for (int j = 0; j < 8; j += 2) {
+        split_mul2(qa[ks][j], sv[j], qa[ks][j + 1], sv[j + 1], ah[ks], al[ks], j);
+        bz = fmaf(qa[ks][j], zv[j], bz);
+        bz = fmaf(qa[ks][j + 1], zv[j + 1], bz);
       }
     }
-    // scores: even tokens 4 D 2^-ek + sum q z, odd tokens 16 D 2^-ek + sum q z
-    // (qa, hence D and bz, carry 2^ek)
+    // every read of the key part has completed: request the next one
+    wait_regs(xk);
+    if (has_next) stage_keys<MASKED>(a, bh, blk + 1, kbuf, L.mask, lane);
+
     bz = group_sum(bz);
-    if (kg == 0) sm_bias[i] = bz;
+    if (kg == 0) L.bias[i] = bz;
 
     f4 dk[4][2];
 #pragma unroll
@@ -366,99 +387,123 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
       dk[g][0] = dk[g][1] = (f4){0, 0, 0, 0};
 #pragma unroll
       for (int rho = 0; rho < 2; ++rho) {
-        const i2 x = xk[g][rho];
+        const i2 x = xk[2 * g + rho];
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
           h8 be, bo;
-          split_codes((uint32_t)x[d], be, bo);
+          codes_to_b((uint32_t)x[d], be, bo);
           const int ks = 2 * rho + d;
           dk[g][0] = mfma(ah[ks], be, dk[g][0]);
-          if (KIVI_MATRIX_KEY_LO) dk[g][0] = mfma(al[ks], be, dk[g][0]);
           dk[g][1] = mfma(ah[ks], bo, dk[g][1]);
-          if (KIVI_MATRIX_KEY_LO) dk[g][1] = mfma(al[ks], bo, dk[g][1]);
+          dk[g][0] = mfma(al[ks], be, dk[g][0]);
+          dk[g][1] = mfma(al[ks], bo, dk[g][1]);
         }
       }
     }
     wave_lds_sync();
 
-    // ---- scores and online softmax (lanes holding head h_s)
+    // scores (even / odd token of each pair) and online softmax, head h_s
     if (k_valid) {
-      const f4 bz4 = *(const f4 *)(sm_bias + 4 * kg);
-      const float un = __builtin_amdgcn_ldexpf(1.0f, -ek_run);    // undo 2^ek
+      const f4 bz4 = *(const f4 *)(L.bias + 4 * kg);
+      const float cs = c_bias * __builtin_amdgcn_ldexpf(1.0f, -ek_run);   // undo 2^ek
       float s2[4][2];
       float bmax = -INFINITY;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float zb = bz4[g] * (c_bias * un);
-        s2[g][0] = fmaf(dk[g][0][g], c_even * un, zb);
-        s2[g][1] = fmaf(dk[g][1][g], c_odd * un, zb);
-        s2[g][0] += mk[g][0];
-        s2[g][1] += mk[g][1];
+        s2[g][0] = fmaf(dk[g][0][g] + bz4[g], cs, mk[g][0]);
+        s2[g][1] = fmaf(dk[g][1][g] + bz4[g], cs, mk[g][1]);
         bmax = fmaxf(bmax, fmaxf(s2[g][0], s2[g][1]));
       }
       bmax = row_max(bmax);
       const float m_new = fmaxf(m_run, bmax);
       const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
       float lsum = 0.0f;
-      const float sc_e = __builtin_amdgcn_ldexpf(1.0f, ev);        // 2^ev
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const float p0 = m_new == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s2[g][0] - m_new);
         const float p1 = m_new == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s2[g][1] - m_new);
         lsum += p0 + p1;
-        float2 pp = make_float2(p0 * sc_e, p1 * sc_e);
-        *(float2 *)(&sm_p[h_s][32 * g + 2 * i]) = pp;
+        *(float2 *)(&L.p[h_s][32 * g + 2 * i]) = make_float2(p0, p1);
       }
       l_run = fmaf(l_run, alpha, lsum);
       m_run = m_new;
-      if (i == 0) sm_alpha[h_s] = alpha;
+      if (i == 0) L.alpha[h_s] = alpha;
     }
-    wave_lds_sync();
 
-    // ---- value side: A = hi/lo(p s), zero-point sums p . z
+    // ================= value half =================
+    if (has_next)
+      wait_vm<KDMA>();               // value part of blk in; the next key part may fly
+    else
+      wait_vm<0>();
+    wave_lds_sync();
+    const VStage &vst = *vbuf;
+    i2 xv[8];                        // [32-token half u][channel group g]
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        xv[4 * u + g] = tr4(vst.vc + (32 * kg + 16 * u + i) * 8 + g * 2);
+    int ev;
     {
-      // accumulators are in units of 2^ev_run; move them to 2^ev
+      float mx = max8(*(const f4 *)(vst.vs + lane * 8), *(const f4 *)(vst.vs + lane * 8 + 4));
+      mx = group_max(row_max(mx));
+      // mx < 2^e with e the frexp exponent; p <= 1, so p * s * 2^(14 - e) < 2^14
+      ev = mx > 0.0f ? 14 - __builtin_amdgcn_frexp_expf(mx) : 0;
+      ev = __builtin_amdgcn_readfirstlane(ev);
+    }
+    {
+      // accumulators in units of 2^ev_run move to 2^ev
       const float rescale = __builtin_amdgcn_ldexpf(1.0f, ev - ev_run);
       ev_run = ev;
-      const float av = (v_valid ? sm_alpha[kg] : 1.0f) * rescale;
+      const float av = (v_valid ? L.alpha[kg] : 1.0f) * rescale;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         dv[g][0][g] *= av;
         dv[g][1][g] *= av;
       }
-      const float ar = sm_alpha[h_v] * rescale;
-      zt *= ar;
+      zt *= L.alpha[h_v];
     }
+    const float sc_e = __builtin_amdgcn_ldexpf(1.0f, ev);
+    h8 vh[2][2], vl[2][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      h8 vh[2], vl[2];
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
         const int t0 = 32 * kg + 16 * u + 8 * d;
-        const float *pp = &sm_p[h_v][t0];
-        const float *sp = st.vs + c_v * kBT + t0;
-        const float *zp = st.vz + c_v * kBT + t0;
+        const f4 p0 = *(const f4 *)(&L.p[h_v][t0]);
+        const f4 p1 = *(const f4 *)(&L.p[h_v][t0 + 4]);
+        const f4 s0 = *(const f4 *)(vst.vs + c_v * kBT + t0);
+        const f4 s1 = *(const f4 *)(vst.vs + c_v * kBT + t0 + 4);
+        const f4 z0 = *(const f4 *)(vst.vz + c_v * kBT + t0);
+        const f4 z1 = *(const f4 *)(vst.vz + c_v * kBT + t0 + 4);
+        const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+        const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+        const float zv[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          split_mul2(pp[r], sp[r], pp[r + 4], sp[r + 4], vh[d], vl[d], 2 * r);
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int j = r + 4 * e;
-            zt = fmaf(pp[j], zp[j], zt);
-          }
+        for (int j = 0; j < 8; j += 2) {
+          split_mul2(pv[j], sv[j] * sc_e, pv[j + 1], sv[j + 1] * sc_e, vh[u][d], vl[u][d], j);
+          zt = fmaf(pv[j], zv[j], zt);
+          zt = fmaf(pv[j + 1], zv[j + 1], zt);
         }
       }
+    }
+    // every read of the value part has completed: request the next one
+    wait_regs(xv);
+    if (has_next) stage_values(a, bh, blk + 1, vbuf, lane);
+
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const i2 x = xv[u][g];
+        const i2 x = xv[4 * u + g];
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
           h8 be, bo;
-          split_codes((uint32_t)x[d], be, bo);
-          dv[g][0] = mfma(vh[d], be, dv[g][0]);
-          if (KIVI_MATRIX_VALUE_LO) dv[g][0] = mfma(vl[d], be, dv[g][0]);
-          dv[g][1] = mfma(vh[d], bo, dv[g][1]);
-          if (KIVI_MATRIX_VALUE_LO) dv[g][1] = mfma(vl[d], bo, dv[g][1]);
+          codes_to_b((uint32_t)x[d], be, bo);
+          dv[g][0] = mfma(vh[u][d], be, dv[g][0]);
+          dv[g][1] = mfma(vh[u][d], bo, dv[g][1]);
+          dv[g][0] = mfma(vl[u][d], be, dv[g][0]);
+          dv[g][1] = mfma(vl[u][d], bo, dv[g][1]);
         }
       }
     }
@@ -466,151 +511,160 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
 
   // ---- write the partial (acc[128], m, l) of each query head
   zt = group_sum(zt);
-  if (kg == 0) {
-    sm_zt[i] = zt;
-  }
+  wave_lds_sync();
+  if (kg == 0) L.bias[i] = zt;
   const float l_head = row_sum(l_run);
   wave_lds_sync();
-  const int slot_stride = kD + 2;
+  const int slot_stride = kD + 4;
   if (v_valid) {
-    const f4 z4 = *(const f4 *)(sm_zt + 4 * kg);
+    const f4 z4 = *(const f4 *)(L.bias + 4 * kg);
     float *dst = a.part + (((int64_t)b * a.Hq + hk * NREP + kg) * a.S_total + split) * slot_stride;
     const float unit = __builtin_amdgcn_ldexpf(1.0f, -ev_run);      // undo 2^ev
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      // even channels: 4 D + sum p z; odd channels: 16 D + sum p z
-      float2 o = make_float2(fmaf(4.0f, dv[g][0][g], z4[g]) * unit,
-                             fmaf(16.0f, dv[g][1][g], z4[g]) * unit);
-      *(float2 *)(dst + 32 * g + 2 * i) = o;
+      *(float2 *)(dst + 32 * g + 2 * i) =
+          make_float2(fmaf(dv[g][0][g], unit, z4[g]), fmaf(dv[g][1][g], unit, z4[g]));
     }
   }
   if (k_valid && i == 0) {
     float *dst = a.part + (((int64_t)b * a.Hq + hk * NREP + h_s) * a.S_total + split) * slot_stride;
-    dst[kD] = m_run == -INFINITY ? -INFINITY : m_run * 0.6931471805599453f;
-    dst[kD + 1] = l_head;
+    *(float2 *)(dst + kD) = make_float2(m_run == -INFINITY ? -INFINITY : m_run * 0.6931471805599453f,
+                                        l_head);
   }
 }
 
-// Window role: the tokens of one slab that the block role does not cover --
-// the fp16 window and the quantized tokens past the last full block -- in
-// chunks of 64: tokens [n_main + 64 chunk, min(t, n_main + 64 chunk + 64)).
-// Everything the chunk needs is copied to LDS with one batch of DMA, then
-// each lane scores one token (scalar fp32) and accumulates two channels.
-template <int NREP>
+// Window role: tokens [Ta, Tb) = [n_main + 32 chunk, min(t, n_main + 32 chunk + 32))
+// of one slab -- fp16 window tokens and quantized tokens past the last whole
+// block.  The chunk's key data goes to the key buffer and its value data to
+// the value buffer, in one batch of DMA; then each lane scores one token over
+// half of the channels (scalar fp32) and accumulates two output channels.
+template <int NREP, bool MASKED>
 __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main, int chunk,
                                             int slot, const Lds &L) {
   const int j = threadIdx.x;
   const int hk = blockIdx.y;
   const int b = blockIdx.z;
   const int64_t bh = (int64_t)b * a.H + hk;
-  const int64_t Ta = n_main + 64 * (int64_t)chunk;
-  const int64_t Tb = Ta + 64 < a.t ? Ta + 64 : a.t;
+  const int64_t Ta = n_main + (int64_t)kWT * chunk;
+  const int64_t Tb = Ta + kWT < a.t ? Ta + kWT : a.t;
   const int n = (int)(Tb - Ta);
-  const int64_t kq_end = a.n_kq < Ta ? Ta : (a.n_kq > Tb ? Tb : a.n_kq);
+  // keys: Ta and n_kq are multiples of 32, so the chunk is one whole
+  // quantized key group or consists of fp16 window rows
+  const bool kq = Ta < a.n_kq;
+  // values: [Ta, vq_end) quantized, [vq_end, Tb) fp16
   const int64_t vq_end = a.n_vq < Ta ? Ta : (a.n_vq > Tb ? Tb : a.n_vq);
-  const int n_qk = (int)(kq_end - Ta), n_fk = (int)(Tb - kq_end);   // n_qk in {0, 32, 64}
   const int n_qv = (int)(vq_end - Ta), n_fv = (int)(Tb - vq_end);
-  const int nqg = n_qk / kG;
   const int nqv4 = (n_qv + 3) / 4;
-  // 16-byte DMA units of each region, in LDS order
-  const int u_krow = 0;
-  const int u_kc = u_krow + n_fk * 16;
-  const int u_ks = u_kc + nqg * 64;
-  const int u_kz = u_ks + nqg * 32;
-  const int u_vrow = u_kz + nqg * 32;
-  const int u_vc = u_vrow + n_fv * 16;
-  const int u_vs = u_vc + n_qv * 2;
-  const int u_vz = u_vs + 4 * nqv4;
-  const int u_end = u_vz + 4 * nqv4;           // <= 2048 units = 32 KB
-  char *lds = (char *)L.st;
-  for (int base = 0; base < u_end; base += 64) {
+
+  // ---- DMA, in 16-byte units.  Key buffer: codes (64 units), scale and zero
+  // (32 + 32), or n fp16 rows (16 units each) -- at most 512 units = 8 KB.
+  char *kl = (char *)L.ks;
+  const int ku_end = kq ? 128 : n * 16;
+  for (int base = 0; base < ku_end; base += 64) {
     const int u = base + j;
-    if (u < u_end) {
+    if (u < ku_end) {
       const void *src;
-      if (u < u_kc) {
-        const int r = u / 16, part = u % 16;
-        src = a.k_res + ((bh * a.R + (kq_end + r) % a.R) * kD + part * 8);
-      } else if (u < u_ks) {
-        const int x = u - u_kc;
-        src = a.k_codes + ((bh * (a.cap / kG) + Ta / kG + x / 64) * 256 + (x % 64) * 4);
-      } else if (u < u_kz) {
-        const int x = u - u_ks;
-        src = a.k_scale + ((bh * (a.cap / kG) + Ta / kG + x / 32) * kD + (x % 32) * 4);
-      } else if (u < u_vrow) {
-        const int x = u - u_kz;
-        src = a.k_zero + ((bh * (a.cap / kG) + Ta / kG + x / 32) * kD + (x % 32) * 4);
-      } else if (u < u_vc) {
-        const int x = u - u_vrow;
-        src = a.v_res + ((bh * a.R + (vq_end + x / 16) % a.R) * kD + (x % 16) * 8);
-      } else if (u < u_vs) {
-        const int x = u - u_vc;
-        src = a.v_codes + ((bh * a.cap + Ta + x / 2) * 8 + (x % 2) * 4);
+      if (kq) {
+        const int64_t grp = bh * (a.cap / kG) + Ta / kG;
+        if (u < 64)
+          src = a.k_codes + grp * 256 + u * 4;
+        else if (u < 96)
+          src = a.k_scale + grp * kD + (u - 64) * 4;
+        else
+          src = a.k_zero + grp * kD + (u - 96) * 4;
+      } else {
+        src = a.k_res + ((bh * a.R + (Ta + u / 16) % a.R) * kD + (u % 16) * 8);
+      }
+      dma16(src, (lds_void *)(kl + (size_t)base * 16));
+    }
+  }
+  // value buffer: codes (2 units per token), scale and zero (4 channel
+  // groups x nqv4 units each), then fp16 rows (16 units each) -- at most 512
+  char *vl = (char *)L.vs;
+  const int u_vs = n_qv * 2;
+  const int u_vz = u_vs + 4 * nqv4;
+  const int u_vrow = u_vz + 4 * nqv4;
+  const int vu_end = u_vrow + n_fv * 16;
+  for (int base = 0; base < vu_end; base += 64) {
+    const int u = base + j;
+    if (u < vu_end) {
+      const void *src;
+      if (u < u_vs) {
+        src = a.v_codes + ((bh * a.cap + Ta + u / 2) * 8 + (u % 2) * 4);
       } else if (u < u_vz) {
         const int x = u - u_vs;
         src = a.v_scale + ((bh * 4 + x / nqv4) * a.cap + Ta + (x % nqv4) * 4);
-      } else {
+      } else if (u < u_vrow) {
         const int x = u - u_vz;
         src = a.v_zero + ((bh * 4 + x / nqv4) * a.cap + Ta + (x % nqv4) * 4);
+      } else {
+        const int x = u - u_vrow;
+        src = a.v_res + ((bh * a.R + (vq_end + x / 16) % a.R) * kD + (x % 16) * 8);
       }
-      load_lds(src, (lds_void *)(lds + (size_t)base * 16));
+      dma16(src, (lds_void *)(vl + (size_t)base * 16));
     }
   }
+  // q of the NREP heads, kept in the probability buffer (unused by this role)
+  float(*q_s)[kD] = L.p;
   const uint16_t *q = a.q + ((int64_t)b * a.Hq + hk * NREP) * kD;
-  for (int e = j; e < NREP * kD; e += 64) L.q[e / kD][e % kD] = h2f(q[e]);
-  wait_staged();
+  for (int e = j; e < NREP * kD; e += 64) q_s[e / kD][e % kD] = h2f(q[e]);
+  wait_vm<0>();
   wave_lds_sync();
 
   const float LOG2E = 1.4426950408889634f;
-  // ---- scores: lane j scores token Ta + j for every head
+  // ---- scores: lane j scores token Ta + (j & 31) over channels [64 hf, 64 hf + 64)
+  const int tj = j & 31, hf = j >> 5;
   float sc[NREP];
 #pragma unroll
   for (int h = 0; h < NREP; ++h) sc[h] = 0.0f;
-  if (j < n) {
-    const int64_t tau = Ta + j;
-    if (tau < kq_end) {
-      const int gi = j / kG;
-      const int e = (int)(tau % kG);
-      const uint32_t *kc = (const uint32_t *)(lds + (size_t)u_kc * 16) + gi * 256 + e / 16;
-      const float *ks = (const float *)(lds + (size_t)u_ks * 16) + gi * kD;
-      const float *kz = (const float *)(lds + (size_t)u_kz * 16) + gi * kD;
-      const int sh = 2 * (e % 16);
-      for (int c = 0; c < kD; c += 4) {
+  if (tj < n) {
+    if (kq) {
+      const uint32_t *kc = (const uint32_t *)kl + tj / 16;
+      const float *ks = (const float *)(kl + 64 * 16);
+      const float *kz = (const float *)(kl + 96 * 16);
+      const int sh = 2 * (tj % 16);
+      for (int c = 64 * hf; c < 64 * hf + 64; c += 4) {
         const f4 s4 = *(const f4 *)(ks + c);
         const f4 z4 = *(const f4 *)(kz + c);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const float code = (float)((kc[(c + u) * 2] >> sh) & 3u);
-          const float kh = __fadd_rn(__fmul_rn(code, s4[u]), z4[u]);
+          const float kh = code * s4[u] + z4[u];
 #pragma unroll
-          for (int h = 0; h < NREP; ++h) sc[h] = fmaf(L.q[h][c + u], kh, sc[h]);
+          for (int h = 0; h < NREP; ++h) sc[h] = fmaf(q_s[h][c + u], kh, sc[h]);
         }
       }
     } else {
-      const uint16_t *row = (const uint16_t *)(lds + (size_t)u_krow * 16) + (tau - kq_end) * kD;
-      for (int c = 0; c < kD; ++c) {
+      const uint16_t *row = (const uint16_t *)kl + tj * kD;
+      for (int c = 64 * hf; c < 64 * hf + 64; ++c) {
         const float kh = h2f(row[c]);
 #pragma unroll
-        for (int h = 0; h < NREP; ++h) sc[h] = fmaf(L.q[h][c], kh, sc[h]);
+        for (int h = 0; h < NREP; ++h) sc[h] = fmaf(q_s[h][c], kh, sc[h]);
       }
     }
-    const float mk = a.mask ? a.mask[(int64_t)b * a.t + tau] : 0.0f;
+  }
+#pragma unroll
+  for (int h = 0; h < NREP; ++h) sc[h] += __shfl_xor(sc[h], 32);
+  if (tj < n) {
+    const float mk = MASKED ? a.mask[(int64_t)b * a.t + Ta + tj] : 0.0f;
 #pragma unroll
     for (int h = 0; h < NREP; ++h) sc[h] = (sc[h] * a.sm_scale + mk) * LOG2E;
   } else {
 #pragma unroll
     for (int h = 0; h < NREP; ++h) sc[h] = -INFINITY;
   }
-  // ---- softmax over the chunk, per head
+  // ---- softmax over the chunk, per head (lanes j and j ^ 32 hold the same token)
+  float *p_s = L.mask;    // [NREP][32]
   float mh[NREP], lh[NREP];
 #pragma unroll
   for (int h = 0; h < NREP; ++h) {
     float m = row_max(sc[h]);
     m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
     const float pj = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sc[h] - m);
-    L.p[h][j] = pj;
+    if (hf == 0) p_s[h * kWT + tj] = pj;
     mh[h] = m;
-    lh[h] = group_sum(row_sum(pj));
+    const float l = row_sum(pj);
+    lh[h] = l + __shfl_xor(l, 16);
   }
   wave_lds_sync();
   // ---- values: lane j owns channels 2j and 2j+1
@@ -619,16 +673,16 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
   for (int h = 0; h < NREP; ++h) o[h][0] = o[h][1] = 0.0f;
   const int c0 = 2 * j;
   const int gch = c0 / kG;
-  const uint32_t *vc = (const uint32_t *)(lds + (size_t)u_vc * 16);
-  const float *vs = (const float *)(lds + (size_t)u_vs * 16) + gch * nqv4 * 4;
-  const float *vz = (const float *)(lds + (size_t)u_vz * 16) + gch * nqv4 * 4;
-  const uint16_t *vrow = (const uint16_t *)(lds + (size_t)u_vrow * 16);
+  const uint32_t *vc = (const uint32_t *)vl;
+  const float *vsc = (const float *)(vl + (size_t)u_vs * 16) + gch * nqv4 * 4;
+  const float *vz = (const float *)(vl + (size_t)u_vz * 16) + gch * nqv4 * 4;
+  const uint16_t *vrow = (const uint16_t *)(vl + (size_t)u_vrow * 16);
   for (int t = 0; t < n; ++t) {
     float v0, v1;
     if (t < n_qv) {
       const uint32_t w = vc[t * 8 + c0 / 16] >> (2 * (c0 % 16));
-      v0 = __fadd_rn(__fmul_rn((float)(w & 3u), vs[t]), vz[t]);
-      v1 = __fadd_rn(__fmul_rn((float)((w >> 2) & 3u), vs[t]), vz[t]);
+      v0 = (float)(w & 3u) * vsc[t] + vz[t];
+      v1 = (float)((w >> 2) & 3u) * vsc[t] + vz[t];
     } else {
       const uint32_t hv = *(const uint32_t *)(vrow + (t - n_qv) * kD + c0);
       v0 = h2f((uint16_t)(hv & 0xFFFFu));
@@ -636,40 +690,39 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
     }
 #pragma unroll
     for (int h = 0; h < NREP; ++h) {
-      const float pt = L.p[h][t];
+      const float pt = p_s[h * kWT + t];
       o[h][0] = fmaf(pt, v0, o[h][0]);
       o[h][1] = fmaf(pt, v1, o[h][1]);
     }
   }
 #pragma unroll
   for (int h = 0; h < NREP; ++h) {
-    float *dst = a.part + (((int64_t)b * a.Hq + hk * NREP + h) * a.S_total + slot) * (kD + 2);
+    float *dst = a.part + (((int64_t)b * a.Hq + hk * NREP + h) * a.S_total + slot) * (kD + 4);
     *(float2 *)(dst + c0) = make_float2(o[h][0], o[h][1]);
-    if (j == 0) {
-      dst[kD] = mh[h] == -INFINITY ? -INFINITY : mh[h] * 0.6931471805599453f;
-      dst[kD + 1] = lh[h];
-    }
+    if (j == 0)
+      *(float2 *)(dst + kD) =
+          make_float2(mh[h] == -INFINITY ? -INFINITY : mh[h] * 0.6931471805599453f, lh[h]);
   }
 }
 
 // grid: (n_window + n_split, H, B); block: one wave.  Workgroups
 // [0, n_window) take the window role (dispatched first, so they overlap the
 // longer block role), the rest the block role.
-template <int NREP>
-__global__ void __launch_bounds__(64)
+template <int NREP, bool MASKED>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 decode_matrix_kernel(DecodeArgs a, int64_t n_main, int tps, int n_split, int n_window) {
-  __shared__ Stage sm_st[2];
+  __shared__ KStage sm_k;
+  __shared__ VStage sm_v;
   __shared__ __attribute__((aligned(16))) float sm_p[4][kBT];
+  __shared__ __attribute__((aligned(16))) float sm_mask[kBT];
   __shared__ __attribute__((aligned(16))) float sm_bias[16];
-  __shared__ __attribute__((aligned(16))) float sm_zt[16];
   __shared__ __attribute__((aligned(16))) float sm_alpha[4];
-  __shared__ __attribute__((aligned(16))) float sm_q[4][kD];
-  const Lds L{sm_st, sm_p, sm_bias, sm_zt, sm_alpha, sm_q};
+  const Lds L{&sm_k, &sm_v, sm_p, sm_mask, sm_bias, sm_alpha};
   const int x = blockIdx.x;
   if (x < n_window)
-    window_role<NREP>(a, n_main, x, n_split + x, L);
+    window_role<NREP, MASKED>(a, n_main, x, n_split + x, L);
   else
-    block_role<NREP>(a, n_main, tps, x - n_window, L);
+    block_role<NREP, MASKED>(a, n_main, tps, x - n_window, L, &sm_k, &sm_v);
 }
 
 bool decode_matrix_supported(const DecodeArgs &a) {
@@ -678,31 +731,39 @@ bool decode_matrix_supported(const DecodeArgs &a) {
 }
 
 int decode_matrix_window_chunks(const DecodeArgs &a, int64_t n_main) {
-  return (int)((a.t - n_main + 63) / 64);
+  return (int)((a.t - n_main + kWT - 1) / kWT);
+}
+
+template <int NREP>
+static void launch_rep(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main, int tps,
+                       int n_splits, int n_window) {
+  if (a.mask)
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, true>), grid, dim3(64), 0, s, a, n_main, tps,
+                       n_splits, n_window);
+  else
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, false>), grid, dim3(64), 0, s, a, n_main, tps,
+                       n_splits, n_window);
 }
 
 hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int tokens_per_split,
                                 int n_splits, hipStream_t s) {
-  if (!decode_matrix_supported(a) || n_main % kBT != 0 || tokens_per_split % kBT != 0 ||
-      n_main > a.n_vq)
+  if (!decode_matrix_supported(a) || a.t <= 0 || n_main < 0 ||
+      n_main % kBT != 0 || n_main > a.n_vq || tokens_per_split <= 0 ||
+      tokens_per_split % kBT != 0 || n_splits < 0)
     return hipErrorInvalidValue;
+  // every block is in some split, and every split holds at least one block
+  if ((int64_t)n_splits * tokens_per_split < n_main ||
+      (n_splits > 0 && (int64_t)(n_splits - 1) * tokens_per_split >= n_main))
+    return hipErrorInvalidValue;
+  // the window role's key staging assumes whole key groups below n_kq
+  if (a.n_kq % kG != 0) return hipErrorInvalidValue;
   const int n_window = decode_matrix_window_chunks(a, n_main);
-  if (n_splits + n_window <= 0) return hipSuccess;
-  if (n_splits + n_window > a.S_total) return hipErrorInvalidValue;
+  if (n_splits + n_window <= 0 || n_splits + n_window > a.S_total) return hipErrorInvalidValue;
   dim3 grid((unsigned)(n_window + n_splits), (unsigned)a.H, (unsigned)a.B);
   switch (a.n_rep) {
-    case 1:
-      hipLaunchKernelGGL(decode_matrix_kernel<1>, grid, dim3(64), 0, s, a, n_main,
-                         tokens_per_split, n_splits, n_window);
-      break;
-    case 2:
-      hipLaunchKernelGGL(decode_matrix_kernel<2>, grid, dim3(64), 0, s, a, n_main,
-                         tokens_per_split, n_splits, n_window);
-      break;
-    default:
-      hipLaunchKernelGGL(decode_matrix_kernel<4>, grid, dim3(64), 0, s, a, n_main,
-                         tokens_per_split, n_splits, n_window);
-      break;
+    case 1: launch_rep<1>(a, grid, s, n_main, tokens_per_split, n_splits, n_window); break;
+    case 2: launch_rep<2>(a, grid, s, n_main, tokens_per_split, n_splits, n_window); break;
+    default: launch_rep<4>(a, grid, s, n_main, tokens_per_split, n_splits, n_window); break;
   }
   return hipGetLastError();
 }

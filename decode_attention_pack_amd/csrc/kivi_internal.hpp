@@ -38,7 +38,7 @@ struct DecodeArgs {
   const uint16_t *v_res;
   const uint16_t *q;     // [B][Hq][D]
   const float *mask;     // [B][t] or nullptr
-  float *part;           // partials [B][Hq][S_total][D + 2]: acc[D], m, l
+  float *part;           // partials [B][Hq][S_total][D + 4]: acc[D], m, l, (pad)
   float *out;            // [B][Hq][D]
   int32_t B, H, D, kb, vb, G, R, Hq, n_rep;
   int64_t cap, t, n_kq, n_vq;
@@ -54,7 +54,7 @@ hipError_t launch_decode_generic(const DecodeArgs &a, int64_t tok_begin, int tok
 // Matrix-core kernel for 2-bit caches with G = 32, D = 128 and 1, 2 or 4
 // query heads per KV head.  Returns hipErrorInvalidValue for other shapes.
 bool decode_matrix_supported(const DecodeArgs &a);
-// Window chunks (64 tokens each) that cover tokens [n_main, t).
+// Window chunks (32 tokens each) that cover tokens [n_main, t).
 int decode_matrix_window_chunks(const DecodeArgs &a, int64_t n_main);
 // One launch: block role over [0, n_main) in n_splits splits (partial slots
 // [0, n_splits)), window role over [n_main, t) (slots after those).
