@@ -217,6 +217,26 @@ int kivi_append(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp16, i
   const int64_t t0 = c->n_tokens, t1 = t0 + n_new;
   const int64_t vq0 = max64(0, t0 - R), vq1 = max64(0, t1 - R);
   const int64_t kq0 = t0 - t0 % R, kq1 = t1 - t1 % R;
+  if (n_new == 1 && kivi::append_one_supported((int)D, (int)G, c->v_bits)) {
+    // decode step: one fused kernel, plus the key block when this token completes one
+    rc = hip_status(kivi::launch_append_one((const uint16_t *)k_new_fp16,
+                                            (const uint16_t *)v_new_fp16, c->k_res, c->v_res, t0,
+                                            BH, (int)R, (int)D, (int)G, c->v_bits, c->capacity,
+                                            kq1 == kq0, c->v_codes, c->v_scale, c->v_zero, s),
+                    "kivi_append (step)");
+    if (rc) return rc;
+    if (kq1 > kq0) {
+      kivi::TokenSource ksrc{c->k_res, (const uint16_t *)k_new_fp16, t0, 1, (int32_t)R,
+                             (int32_t)D};
+      rc = hip_status(kivi::launch_key_groups(ksrc, kq0 / G, (kq1 - kq0) / G, BH, c->k_bits,
+                                              (int)G, (int)D, c->capacity, c->k_codes,
+                                              c->k_scale, c->k_zero, s),
+                      "kivi_append (keys)");
+      if (rc) return rc;
+    }
+    c->n_tokens = t1;
+    return KIVI_OK;
+  }
   // 1. values leaving the window (read old slots before they are reused)
   kivi::TokenSource vsrc{c->v_res, (const uint16_t *)v_new_fp16, t0, n_new, (int32_t)R,
                          (int32_t)D};

@@ -26,6 +26,19 @@ hipError_t launch_write_window(const uint16_t *k_new, const uint16_t *v_new, uin
                                uint16_t *v_res, int64_t t0, int64_t n_new, int64_t k_from,
                                int64_t v_from, int64_t BH, int R, int D, hipStream_t s);
 
+// Single-token append (the decode step), fused into one kernel: pops the
+// value leaving the window into the value layout and writes the new key and
+// value into their window slot (the key only if `key_to_window`).  Shapes:
+// G and 32 / bits powers of two of at most 64, D <= 256.
+__host__ __device__ inline bool append_one_supported(int D, int G, int bits) {
+  const int per = 32 / bits;
+  return D <= 256 && G <= 64 && (G & (G - 1)) == 0 && per <= G && D % G == 0;
+}
+hipError_t launch_append_one(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_res,
+                             uint16_t *v_res, int64_t t0, int64_t BH, int R, int D, int G,
+                             int bits, int64_t cap, bool key_to_window, uint32_t *codes,
+                             float *scale, float *zero, hipStream_t s);
+
 // Everything the decode kernels read.
 struct DecodeArgs {
   const uint32_t *k_codes;

@@ -98,6 +98,61 @@ write_window_kernel(const uint16_t *__restrict__ k_new, const uint16_t *__restri
   if (tau >= v_from) v_res[drow] = v_new[srow];
 }
 
+// One decode step of append (one new token per slab), fused: quantize the
+// value that leaves the window (KIVI item 3; token t0 - R, when t0 >= R),
+// then put the new value -- and the new key, unless it completes a key block
+// -- into slot t0 % R (KIVI item 4).  grid: BH; block: D threads rounded up
+// to a wave, thread c owns channel c.  Group min/max and the packing of codes
+// into words are lane reductions, so G and 32 / bits must be powers of two
+// no larger than a wave.
+__global__ void __launch_bounds__(256)
+append_one_kernel(const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
+                  uint16_t *__restrict__ k_res, uint16_t *__restrict__ v_res, int64_t t0,
+                  int R, int D, int G, int bits, int64_t cap, bool key_to_window,
+                  uint32_t *__restrict__ codes, float *__restrict__ scale,
+                  float *__restrict__ zero) {
+  const int64_t bh = blockIdx.x;
+  const int c = threadIdx.x;
+  const bool on = c < D;
+  const int64_t slot = (bh * R + t0 % R) * D + c;
+  if (t0 >= R) {
+    // every lane of a group takes part in the reductions; lanes past D hold
+    // a copy of channel 0 of their group's wave and write nothing
+    const float x = h2f(v_res[on ? slot : (bh * R + t0 % R) * D]);
+    float mn = x, mx = x;
+    for (int o = 1; o < G; o <<= 1) {
+      mn = fminf(mn, __shfl_xor(mn, o));
+      mx = fmaxf(mx, __shfl_xor(mx, o));
+    }
+    const float sc = group_scale(mn, mx, bits);
+    const int per = 32 / bits;
+    uint32_t w = quant_code(x, mn, sc, bits) << (bits * (c % per));
+    for (int o = 1; o < per; o <<= 1) w |= __shfl_xor(w, o);
+    const int64_t tau = t0 - R;
+    if (on && c % per == 0) codes[(bh * cap + tau) * (int64_t)(D / per) + c / per] = w;
+    if (on && c % G == 0) {
+      const int64_t sz = (bh * (D / G) + c / G) * cap + tau;
+      scale[sz] = sc;
+      zero[sz] = mn;
+    }
+  }
+  if (on) {
+    v_res[slot] = v_new[bh * D + c];
+    if (key_to_window) k_res[slot] = k_new[bh * D + c];
+  }
+}
+
+hipError_t launch_append_one(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_res,
+                             uint16_t *v_res, int64_t t0, int64_t BH, int R, int D, int G,
+                             int bits, int64_t cap, bool key_to_window, uint32_t *codes,
+                             float *scale, float *zero, hipStream_t s) {
+  if (!append_one_supported(D, G, bits) || BH <= 0) return hipErrorInvalidValue;
+  const int threads = (D + 63) / 64 * 64;
+  hipLaunchKernelGGL(append_one_kernel, dim3((unsigned)BH), dim3(threads), 0, s, k_new, v_new,
+                     k_res, v_res, t0, R, D, G, bits, cap, key_to_window, codes, scale, zero);
+  return hipGetLastError();
+}
+
 hipError_t launch_key_groups(const TokenSource &src, int64_t g_first, int64_t n_groups,
                              int64_t BH, int bits, int G, int D, int64_t cap,
                              uint32_t *codes, float *scale, float *zero, hipStream_t s) {

@@ -37,6 +37,30 @@ def test_append_random_chunks(kb, vb, R, D):
                 compare_slab(g, b, h, o, b, h)
 
 
+@pytest.mark.parametrize("kb,vb,G,D,R", [(2, 2, 16, 64, 32), (4, 4, 64, 128, 64), (2, 4, 32, 96, 64),
+                                         (4, 2, 48, 96, 48), (2, 2, 128, 256, 128)])
+def test_single_token_appends(kb, vb, G, D, R):
+    """Decode-step appends (one token per call) through both the fused
+    single-token kernel (G a power of two <= 64) and the general path (other
+    G), across the key-block and window-wrap boundaries."""
+    rng = np.random.default_rng(G * 7 + D + kb)
+    B, H = 2, 2
+    t_end = 2 * R + 3
+    cap = ((t_end + R - 1) // R) * R
+    K = rng.standard_normal((B, H, t_end, D)).astype(np.float16)
+    V = (rng.standard_normal((B, H, t_end, D)) * 3).astype(np.float16)
+    g = kivi.Cache(B, H, D, kb, vb, G, R, cap)
+    o = oracle.Cache(B, H, D, kb, vb, G, R, cap)
+    for t in range(t_end):
+        kivi.kivi_append(g, dev(K[:, :, t:t + 1]), dev(V[:, :, t:t + 1]))
+        o.append(b16(K[:, :, t:t + 1]), b16(V[:, :, t:t + 1]))
+        if t % 5 == 4 or t >= t_end - 3 or (t + 1) % R <= 1:
+            torch.cuda.synchronize()
+            for b in range(B):
+                for h in range(H):
+                    compare_slab(g, b, h, o, b, h)
+
+
 def test_prefill_equals_single_appends_on_gpu():
     rng = np.random.default_rng(3)
     B, H, D, G, R, T = 1, 2, 128, 32, 128, 300
