@@ -81,6 +81,43 @@ def append_bytes(w, t_before: int) -> int:
     return per * w.B * w.Hkv
 
 
+def pack_bytes(w, T: int, bits: int) -> int:
+    """Algorithmic bytes of packing T tokens of keys (or values): fp16 in,
+    codes + fp32 scale/zero out."""
+    return w.B * w.Hkv * (T * w.D * 2 + T * w.D * bits // 8 + (T // w.G) * w.D * 8)
+
+
+def time_pack(w, inp, dev, stream, reps: int = 5):
+    """Full-prefill pack pass (kivi_pack_keys, kivi_pack_values) in us and GB/s."""
+    import torch
+
+    from decode_attention_pack_amd import kivi
+    T = w.T0 - w.T0 % w.G
+    k = torch.from_numpy(inp["k0"][:, :, :T]).to(dev).contiguous()
+    v = torch.from_numpy(inp["v0"][:, :, :T]).to(dev).contiguous()
+    out = {}
+    for name, x, bits in (("keys", k, w.k_bits), ("values", v, w.v_bits)):
+        shp = kivi.layout_shapes(w.B, w.Hkv, w.D, bits, bits, w.G, 1, T)
+        pre = "k_" if name == "keys" else "v_"
+        codes = torch.empty(shp[pre + "codes"], dtype=torch.int32, device=dev)
+        scale = torch.empty(shp[pre + "scale"], dtype=torch.float32, device=dev)
+        zero = torch.empty(shp[pre + "zero"], dtype=torch.float32, device=dev)
+        fn = kivi.kivi_pack_keys if name == "keys" else kivi.kivi_pack_values
+        fn(x, bits, w.G, codes, scale, zero, T, 0, stream=stream)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn(x, bits, w.G, codes, scale, zero, T, 0, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        out[name] = {"tokens": T, "us": round(us, 2),
+                     "GBps": round(pack_bytes(w, T, bits) / us / 1e3, 1)}
+    return out
+
+
 def cpu_baseline(w, inp, budget_s: float = 12.0):
     """Time the CPU oracle on (batch, KV head) slabs until ~budget_s of work."""
     import oracle
@@ -120,6 +157,7 @@ def main():
     ap.add_argument("--tokens-per-split", type=int, default=0,
                     help="split size of the attention call (0 = the library's automatic plan)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-pack", action="store_true", help="skip the full-prefill pack pass")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device-to-device copy of this "
                          "many MiB (a known-size reference for hardware byte counters)")
@@ -238,6 +276,10 @@ def main():
                      "kernel": "kivi_decode_attn launch (split kernel + combine)",
                      "bytes_per_launch": a_bytes // args.steps},
     }
+    if not args.no_pack:
+        del caches, base
+        torch.cuda.empty_cache()
+        line["pack_full_prefill"] = time_pack(w, inp, dev, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(line), flush=True)
