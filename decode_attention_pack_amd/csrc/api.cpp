@@ -180,6 +180,11 @@ int kivi_pack_keys(const void *k_fp16, int32_t B, int32_t H, int64_t T, int32_t 
                       dst_token_offset, true, "kivi_pack_keys");
   if (rc) return rc;
   if (T == 0) return KIVI_OK;
+  if (kivi::pack_tiles_supported(D, group, bits))
+    return hip_status(kivi::launch_key_tiles((const uint16_t *)k_fp16, T, T, dst_token_offset / group,
+                                             (int64_t)B * H, bits, group, D, dst_capacity, codes,
+                                             scale, zero, (hipStream_t)stream),
+                      "kivi_pack_keys");
   kivi::TokenSource src{nullptr, (const uint16_t *)k_fp16, dst_token_offset, T, 1, D};
   return hip_status(kivi::launch_key_groups(src, dst_token_offset / group, T / group,
                                             (int64_t)B * H, bits, group, D, dst_capacity, codes,
@@ -194,6 +199,11 @@ int kivi_pack_values(const void *v_fp16, int32_t B, int32_t H, int64_t T, int32_
                       dst_token_offset, false, "kivi_pack_values");
   if (rc) return rc;
   if (T == 0) return KIVI_OK;
+  if (kivi::pack_tiles_supported(D, group, bits))
+    return hip_status(kivi::launch_value_tokens((const uint16_t *)v_fp16, T, T, dst_token_offset,
+                                                (int64_t)B * H, bits, group, D, dst_capacity,
+                                                codes, scale, zero, (hipStream_t)stream),
+                      "kivi_pack_values");
   kivi::TokenSource src{nullptr, (const uint16_t *)v_fp16, dst_token_offset, T, 1, D};
   return hip_status(kivi::launch_value_rows(src, dst_token_offset, T, (int64_t)B * H, bits, group,
                                             D, dst_capacity, codes, scale, zero,
@@ -234,6 +244,27 @@ int kivi_append(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp16, i
                       "kivi_append (keys)");
       if (rc) return rc;
     }
+    c->n_tokens = t1;
+    return KIVI_OK;
+  }
+  if (t0 == 0 && kivi::pack_tiles_supported((int)D, (int)G, c->v_bits) &&
+      kivi::pack_tiles_supported((int)D, (int)G, c->k_bits)) {
+    // prefill into an empty cache: every quantized token comes from the input
+    rc = hip_status(kivi::launch_value_tokens((const uint16_t *)v_new_fp16, n_new, vq1, 0, BH,
+                                              c->v_bits, (int)G, (int)D, c->capacity,
+                                              c->v_codes, c->v_scale, c->v_zero, s),
+                    "kivi_append (values)");
+    if (rc) return rc;
+    rc = hip_status(kivi::launch_key_tiles((const uint16_t *)k_new_fp16, n_new, kq1, 0, BH, c->k_bits,
+                                           (int)G, (int)D, c->capacity, c->k_codes, c->k_scale,
+                                           c->k_zero, s),
+                    "kivi_append (keys)");
+    if (rc) return rc;
+    rc = hip_status(kivi::launch_write_window((const uint16_t *)k_new_fp16,
+                                              (const uint16_t *)v_new_fp16, c->k_res, c->v_res,
+                                              t0, n_new, kq1, vq1, BH, (int)R, (int)D, s),
+                    "kivi_append (window)");
+    if (rc) return rc;
     c->n_tokens = t1;
     return KIVI_OK;
   }

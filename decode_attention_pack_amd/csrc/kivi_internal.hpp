@@ -26,6 +26,19 @@ hipError_t launch_write_window(const uint16_t *k_new, const uint16_t *v_new, uin
                                uint16_t *v_res, int64_t t0, int64_t n_new, int64_t k_from,
                                int64_t v_from, int64_t BH, int R, int D, hipStream_t s);
 
+// Pack fast paths for a contiguous fp16 input [BH][T][D] (the pack entry
+// points): key tiles (T % G == 0; groups g_first.. of the destination) and
+// value tokens (destination tokens tau_first..).  Shapes: D in {64, 128, 256},
+// G a power of two with G * D * 2 <= 16 KB and G <= 64.
+bool pack_tiles_supported(int D, int G, int bits);
+// x holds T_in rows per slab; the first n_rows are packed.
+hipError_t launch_key_tiles(const uint16_t *x, int64_t T_in, int64_t n_rows, int64_t g_first,
+                            int64_t BH, int bits, int G, int D, int64_t cap, uint32_t *codes,
+                            float *scale, float *zero, hipStream_t s);
+hipError_t launch_value_tokens(const uint16_t *x, int64_t T_in, int64_t n_rows, int64_t tau_first,
+                               int64_t BH, int bits, int G, int D, int64_t cap, uint32_t *codes,
+                               float *scale, float *zero, hipStream_t s);
+
 // Single-token append (the decode step), fused into one kernel: pops the
 // value leaving the window into the value layout and writes the new key and
 // value into their window slot (the key only if `key_to_window`).  Shapes:

@@ -98,6 +98,152 @@ write_window_kernel(const uint16_t *__restrict__ k_new, const uint16_t *__restri
   if (tau >= v_from) v_res[drow] = v_new[srow];
 }
 
+// KIVI item 2, fast path for whole groups of a contiguous fp16 input (the
+// pack entry point): one workgroup per (key group, slab).  The G x D tile is
+// staged in LDS with 16-byte loads, then thread c reduces and packs channel c
+// (codes of one channel are contiguous, so the stores coalesce across threads).
+// grid: (n_groups, BH); block: D threads (D a multiple of 64, G * D * 2 bytes
+// of LDS).
+template <int G, int D>
+__global__ void __launch_bounds__(D)
+key_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t g_first, int bits,
+                 int64_t cap, uint32_t *__restrict__ codes, float *__restrict__ scale,
+                 float *__restrict__ zero) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[G][D];
+  const int64_t bh = blockIdx.y;
+  const int64_t g = blockIdx.x;                     // group within the input
+  const uint16_t *src = x + (bh * T_in + g * G) * (int64_t)D;
+  constexpr int kChunks = G * D / 8;                // 16-byte chunks of the tile
+  for (int i = threadIdx.x; i < kChunks; i += D)
+    *(uint4 *)(&tile[0][0] + i * 8) = *(const uint4 *)(src + i * 8);
+  __syncthreads();
+  const int c = threadIdx.x;
+  float mn = h2f(tile[0][c]), mx = mn;
+#pragma unroll
+  for (int i = 1; i < G; ++i) {
+    const float v = h2f(tile[i][c]);
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, v);
+  }
+  const float s = group_scale(mn, mx, bits);
+  const int per = 32 / bits;
+  const int words = G / per;
+  const int64_t sz = (bh * (cap / G) + g_first + g) * D + c;
+  uint32_t *dst = codes + sz * words;
+  for (int w = 0; w < words; ++w) {
+    uint32_t word = 0;
+    for (int e = 0; e < per; ++e)
+      word |= quant_code(h2f(tile[w * per + e][c]), mn, s, bits) << (bits * e);
+    dst[w] = word;
+  }
+  scale[sz] = s;
+  zero[sz] = mn;
+}
+
+// KIVI item 3, fast path for a contiguous fp16 input: one workgroup per 64
+// tokens of one slab.  The 64 x D tile is staged in LDS (rows padded by 16
+// bytes against bank conflicts); thread (group g, token t) then reduces and
+// packs its G channels, so for each group the 64 scales / zeros of the tile
+// are one contiguous store, and the code words of the tile form one
+// contiguous run.  grid: (ceil(n_rows / 64), BH); block: 256.
+template <int D, int G>
+__global__ void __launch_bounds__(256)
+value_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t n_rows,
+                   int64_t tau_first, int bits, int64_t cap, uint32_t *__restrict__ codes,
+                   float *__restrict__ scale, float *__restrict__ zero) {
+  constexpr int kRow = D + 8;                       // halves per LDS row (16-byte pad)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kRow];
+  const int64_t bh = blockIdx.y;
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const int rows = (int)(n_rows - r0 < 64 ? n_rows - r0 : 64);
+  constexpr int kChunks = 64 * D / 8;               // 16-byte chunks of a full tile
+  for (int i = threadIdx.x; i < kChunks; i += 256) {
+    const int t = i / (D / 8), k = i % (D / 8);
+    if (t < rows)
+      *(uint4 *)(tile + t * kRow + k * 8) =
+          *(const uint4 *)(x + (bh * T_in + r0 + t) * (int64_t)D + k * 8);
+  }
+  __syncthreads();
+  const int t = threadIdx.x & 63;
+  const int per = 32 / bits;
+  constexpr int n_groups = D / G;
+  for (int g = threadIdx.x >> 6; g < n_groups; g += 4) {
+    if (t >= rows) continue;
+    // the group's G channels, 8 per 16-byte LDS read
+    uint16_t v16[G];
+#pragma unroll
+    for (int k = 0; k < G / 8; ++k)
+      *(uint4 *)(v16 + 8 * k) = *(const uint4 *)(tile + t * kRow + g * G + 8 * k);
+    float mn = h2f(v16[0]), mx = mn;
+#pragma unroll
+    for (int i = 1; i < G; ++i) {
+      const float v = h2f(v16[i]);
+      mn = fminf(mn, v);
+      mx = fmaxf(mx, v);
+    }
+    const float s = group_scale(mn, mx, bits);
+    const int64_t tau = tau_first + r0 + t;
+    uint32_t *dst = codes + (bh * cap + tau) * (int64_t)(D / per) + (g * G) / per;
+    for (int w = 0; w < G / per; ++w) {
+      uint32_t word = 0;
+      for (int e = 0; e < per; ++e)
+        word |= quant_code(h2f(v16[w * per + e]), mn, s, bits) << (bits * e);
+      dst[w] = word;
+    }
+    const int64_t sz = (bh * n_groups + g) * cap + tau;
+    scale[sz] = s;
+    zero[sz] = mn;
+  }
+}
+
+bool pack_tiles_supported(int D, int G, int bits) {
+  const int per = 32 / bits;
+  if (!(D == 64 || D == 128 || D == 256)) return false;
+  const int cpl = D / 64;
+  if ((G & (G - 1)) != 0 || G < 16 || G < cpl || per < cpl || D % G != 0) return false;
+  return G * D * 2 <= 16384 && G <= 64;
+}
+
+hipError_t launch_key_tiles(const uint16_t *x, int64_t T_in, int64_t n_rows, int64_t g_first,
+                            int64_t BH, int bits, int G, int D, int64_t cap, uint32_t *codes,
+                            float *scale, float *zero, hipStream_t s) {
+  const int64_t n_groups = n_rows / G;
+  if (n_groups <= 0 || BH <= 0) return hipSuccess;
+  if (!pack_tiles_supported(D, G, bits) || n_rows % G != 0 || n_rows > T_in)
+    return hipErrorInvalidValue;
+  dim3 grid((unsigned)n_groups, (unsigned)BH);
+#define KIVI_KT(GG, DD)                                                                        \
+  if (G == GG && D == DD) {                                                                     \
+    hipLaunchKernelGGL((key_tiles_kernel<GG, DD>), grid, dim3(DD), 0, s, x, T_in, g_first,    \
+                       bits, cap, codes, scale, zero);                                          \
+    return hipGetLastError();                                                                   \
+  }
+  KIVI_KT(16, 64) KIVI_KT(32, 64) KIVI_KT(64, 64)
+  KIVI_KT(16, 128) KIVI_KT(32, 128) KIVI_KT(64, 128)
+  KIVI_KT(16, 256) KIVI_KT(32, 256)
+#undef KIVI_KT
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_value_tokens(const uint16_t *x, int64_t T_in, int64_t n_rows, int64_t tau_first,
+                               int64_t BH, int bits, int G, int D, int64_t cap, uint32_t *codes,
+                               float *scale, float *zero, hipStream_t s) {
+  if (n_rows <= 0 || BH <= 0) return hipSuccess;
+  if (!pack_tiles_supported(D, G, bits) || n_rows > T_in) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((n_rows + 63) / 64), (unsigned)BH);
+#define KIVI_VT(DD, GG)                                                                         \
+  if (D == DD && G == GG) {                                                                     \
+    hipLaunchKernelGGL((value_tiles_kernel<DD, GG>), grid, dim3(256), 0, s, x, T_in, n_rows,    \
+                       tau_first, bits, cap, codes, scale, zero);                               \
+    return hipGetLastError();                                                                   \
+  }
+  KIVI_VT(64, 16) KIVI_VT(64, 32) KIVI_VT(64, 64)
+  KIVI_VT(128, 16) KIVI_VT(128, 32) KIVI_VT(128, 64)
+  KIVI_VT(256, 16) KIVI_VT(256, 32) KIVI_VT(256, 64)
+#undef KIVI_VT
+  return hipErrorInvalidValue;
+}
+
 // One decode step of append (one new token per slab), fused: quantize the
 // value that leaves the window (KIVI item 3; token t0 - R, when t0 >= R),
 // then put the new value -- and the new key, unless it completes a key block

@@ -52,6 +52,15 @@ def test_pack_small(bits, G, D):
             assert _same(g_[sl], r_[sl])
 
 
+@pytest.mark.parametrize("bits,G,D", [(2, 16, 256), (4, 16, 64), (2, 48, 96), (4, 8, 64),
+                                      (2, 128, 256), (4, 64, 256)])
+def test_pack_other_shapes(bits, G, D):
+    """Shapes on both sides of the fast-path limits (power-of-two G <= 64, at
+    most 16 KB per key tile, D in {64, 128, 256}); the rest take the general
+    kernels."""
+    test_pack_small(bits, G, D)
+
+
 def test_pack_values_ragged_rows():
     rng = np.random.default_rng(5)
     x = rng.standard_normal((1, 2, 77, 128)).astype(np.float16)
