@@ -187,19 +187,36 @@ decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int
   }
 }
 
+// Merge of two log-sum-exp partials (m, l, acc): the result has m = max of
+// the two and both sums rescaled to it; an empty partial has m = -inf.
+__device__ __forceinline__ void lse_merge(float &m, float &l, float4 &o, float m2, float l2,
+                                          float4 o2) {
+  const float mn = fmaxf(m, m2);
+  const float f1 = m == -INFINITY ? 0.0f : __expf(m - mn);
+  const float f2 = m2 == -INFINITY ? 0.0f : __expf(m2 - mn);
+  l = l * f1 + l2 * f2;
+  o.x = o.x * f1 + o2.x * f2;
+  o.y = o.y * f1 + o2.y * f2;
+  o.z = o.z * f1 + o2.z * f2;
+  o.w = o.w * f1 + o2.w * f2;
+  m = mn;
+}
+
 // grid: (B * Hq, ceil(D / 32)); block: 256.
 // out = sum_s acc_s e^(m_s - M) / sum_s l_s e^(m_s - M), M = max_s m_s, over
 // the S_total partial slots of one (batch row, query head).  Thread
-// (slot group sg = tid / 8, channel quad cq = tid % 8) merges slots
-// s = sg (mod 32) for 4 channels with a running maximum, loading up to 8 of
-// its slots at once; the 32 slot groups are then merged through LDS.  A
-// workgroup covers 32 channels, so most rows need one round trip to memory.
+// (slot group sg = 8 wave + lane / 8, channel quad cq = lane % 8) merges
+// slots s = sg (mod 32) for 4 channels with a running maximum, loading up to
+// 8 of its slots at once; the 8 slot groups of a wave merge through lane
+// shuffles and the 4 waves through LDS.  A workgroup covers 32 channels, so
+// most rows need one round trip to memory.
 __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
-  __shared__ float red_m[32];
-  __shared__ float red_l[32];
-  __shared__ float4 red_o[32][8];
+  __shared__ float red_m[4][8];
+  __shared__ float red_l[4][8];
+  __shared__ float4 red_o[4][8];
   const int64_t row = blockIdx.x;
-  const int sg = threadIdx.x >> 3, cq = threadIdx.x & 7;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sg = wave * 8 + (lane >> 3), cq = lane & 7;
   const int D = a.D, S = a.S_total, stride = D + 4;
   const int c = blockIdx.y * 32 + cq * 4;
   const bool c_ok = c < D;               // D is a multiple of 8
@@ -224,42 +241,31 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (ml[u].x == -INFINITY) continue;
-      const float Mn = fmaxf(M, ml[u].x);
-      const float r = __expf(M - Mn);     // 0 while M = -inf
-      const float w = __expf(ml[u].x - Mn);
-      L = fmaf(L, r, ml[u].y * w);
-      o.x = fmaf(o.x, r, acc[u].x * w);
-      o.y = fmaf(o.y, r, acc[u].y * w);
-      o.z = fmaf(o.z, r, acc[u].z * w);
-      o.w = fmaf(o.w, r, acc[u].w * w);
-      M = Mn;
+      lse_merge(M, L, o, ml[u].x, ml[u].y, acc[u]);
     }
   }
-  if (cq == 0) {
-    red_m[sg] = M;
-    red_l[sg] = L;
+  // the 8 slot groups of this wave: lanes with the same channel quad
+#pragma unroll
+  for (int off = 8; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(M, off), l2 = __shfl_xor(L, off);
+    const float4 o2 = make_float4(__shfl_xor(o.x, off), __shfl_xor(o.y, off),
+                                  __shfl_xor(o.z, off), __shfl_xor(o.w, off));
+    lse_merge(M, L, o, m2, l2, o2);
   }
-  red_o[sg][cq] = o;
+  if (lane < 8) {
+    red_m[wave][lane] = M;
+    red_l[wave][lane] = L;
+    red_o[wave][lane] = o;
+  }
   __syncthreads();
-  if (sg == 0 && c_ok) {
-    float Mx = -INFINITY;
-    for (int k = 0; k < 32; ++k) Mx = fmaxf(Mx, red_m[k]);
-    float Lt = 0.0f;
-    float4 ot = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if (Mx != -INFINITY) {
-      for (int k = 0; k < 32; ++k) {
-        if (red_m[k] == -INFINITY) continue;
-        const float w = __expf(red_m[k] - Mx);
-        Lt = fmaf(red_l[k], w, Lt);
-        const float4 v = red_o[k][cq];
-        ot.x = fmaf(v.x, w, ot.x);
-        ot.y = fmaf(v.y, w, ot.y);
-        ot.z = fmaf(v.z, w, ot.z);
-        ot.w = fmaf(v.w, w, ot.w);
-      }
-    }
-    const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
-    *(float4 *)(a.out + row * D + c) = make_float4(ot.x * inv, ot.y * inv, ot.z * inv, ot.w * inv);
+  if (threadIdx.x < 8 && c_ok) {
+    M = red_m[0][cq];
+    L = red_l[0][cq];
+    o = red_o[0][cq];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) lse_merge(M, L, o, red_m[w][cq], red_l[w][cq], red_o[w][cq]);
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    *(float4 *)(a.out + row * D + c) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
   }
 }
 

@@ -62,9 +62,10 @@ constexpr int kG = 32;
 constexpr int kBT = 128;       // tokens per block (block role)
 constexpr int kWT = 32;        // tokens per chunk (window role)
 constexpr int kStageDma = 8;   // DMA instructions per key or value part
+constexpr int kPRow = 132;     // floats per probability row in LDS (16-byte pad)
 
-// A block's key part and value part in LDS, as they sit in HBM (the value
-// scale/zero gathered per channel group).
+// A block's key part and value part in LDS: codes as they sit in HBM, the
+// scale and zero rows rotated (see rot_chunk).
 struct alignas(16) KStage {
   uint32_t kc[1024];   // 4 key groups x 128 channels x 2 words
   float ks[512];       // [4 groups][128 channels]
@@ -79,47 +80,83 @@ struct alignas(16) VStage {
 __device__ __forceinline__ void dma16(const void *g, lds_void *l) {
   __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
 }
-__device__ __forceinline__ void dma4(const void *g, lds_void *l) {
-  __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
+
+// Global->LDS copy of 16 bytes per lane from a uniform base plus a 32-bit
+// per-lane byte offset, so the hardware takes the base from scalar registers
+// and the streams share a few offset registers.
+__device__ __forceinline__ void dma16o(const void *base, uint32_t off, lds_void *l) {
+  __builtin_amdgcn_global_load_lds((const char *)base + off, l, 16, 0, 0);
 }
+__device__ __forceinline__ void dma4o(const void *base, uint32_t off, lds_void *l) {
+  __builtin_amdgcn_global_load_lds((const char *)base + off, l, 4, 0, 0);
+}
+
+// Rows of 128 floats (a key group's scales or zeros over channels, a value
+// channel group's scales or zeros over tokens) are stored in LDS rotated:
+// 16-byte chunk k of row r sits at chunk (k + r) % 32.  Lanes that read the
+// same columns of different rows then hit different LDS banks.
+__device__ __forceinline__ int rot_chunk(int r, int k) { return (k + r) & 31; }
+// float offset, within a block of four rows, of columns [c, c + 4) of row r
+__device__ __forceinline__ int rot_off(int r, int c) { return r * 128 + rot_chunk(r, c >> 2) * 4; }
+
+// Per-lane byte offsets of the block DMA.  One DMA instruction fills two
+// rotated rows (lanes 0-31 row 2i, lanes 32-63 row 2i + 1): lane l writes
+// LDS chunk l % 32 of its row, so it reads source chunk (l % 32 - row) % 32.
+// lin: lane * 16 (unrotated runs); krot[i]: key scale/zero rows 2i, 2i + 1
+// (contiguous in HBM); vrot[i]: value scale/zero rows 2i, 2i + 1 (cap floats
+// apart in HBM).
+struct DmaOffsets {
+  uint32_t lin;
+  uint32_t krot[2];
+  uint32_t vrot[2];
+  __device__ DmaOffsets(const DecodeArgs &a, int lane) : lin((uint32_t)lane * 16u) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = 2 * i + (lane >> 5);
+      const uint32_t src = (uint32_t)((lane - row) & 31) * 16u;
+      krot[i] = (uint32_t)(lane >> 5) * 512u + src;
+      vrot[i] = (uint32_t)((int64_t)(lane >> 5) * a.cap * 4) + src;
+    }
+  }
+};
 
 // Key part of block `blk` (tokens [128 blk, 128 blk + 128)) of slab bh:
 // kStageDma DMA instructions, plus 2 for the mask when there is one.
 template <bool MASKED>
 __device__ __forceinline__ void stage_keys(const DecodeArgs &a, int64_t bh, int64_t blk,
-                                           KStage *s, float *mask_s, int lane) {
+                                           KStage *s, float *mask_s, const DmaOffsets &o,
+                                           int lane) {
   const int64_t base = bh * (a.cap / kG) + blk * (kBT / kG);
   const uint32_t *kc = a.k_codes + base * (kD * 2);
   const float *ks = a.k_scale + base * kD;
   const float *kz = a.k_zero + base * kD;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dma16(kc + i * 256 + lane * 4, (lds_void *)(s->kc + i * 256));
+  for (int i = 0; i < 4; ++i) dma16o(kc + i * 256, o.lin, (lds_void *)(s->kc + i * 256));
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    dma16(ks + i * 256 + lane * 4, (lds_void *)(s->ks + i * 256));
-    dma16(kz + i * 256 + lane * 4, (lds_void *)(s->kz + i * 256));
+    dma16o(ks + i * 256, o.krot[i], (lds_void *)(s->ks + i * 256));
+    dma16o(kz + i * 256, o.krot[i], (lds_void *)(s->kz + i * 256));
   }
   if (MASKED) {
     // dword copies: a mask row need not be 16-byte aligned
     const float *m = a.mask + (bh / a.H) * a.t + blk * kBT;
-    dma4(m + lane, (lds_void *)mask_s);
-    dma4(m + 64 + lane, (lds_void *)(mask_s + 64));
+    dma4o(m, (uint32_t)lane * 4u, (lds_void *)mask_s);
+    dma4o(m + 64, (uint32_t)lane * 4u, (lds_void *)(mask_s + 64));
   }
 }
 
 // Value part of block `blk`: kStageDma DMA instructions.
 __device__ __forceinline__ void stage_values(const DecodeArgs &a, int64_t bh, int64_t blk,
-                                             VStage *s, int lane) {
+                                             VStage *s, const DmaOffsets &o) {
   const int64_t tau0 = blk * kBT;
   const uint32_t *vc = a.v_codes + (bh * a.cap + tau0) * 8;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dma16(vc + i * 256 + lane * 4, (lds_void *)(s->vc + i * 256));
+  for (int i = 0; i < 4; ++i) dma16o(vc + i * 256, o.lin, (lds_void *)(s->vc + i * 256));
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int gch = 2 * i + (lane >> 5);
-    const int64_t off = (bh * 4 + gch) * a.cap + tau0 + (lane & 31) * 4;
-    dma16(a.v_scale + off, (lds_void *)(s->vs + i * 256));
-    dma16(a.v_zero + off, (lds_void *)(s->vz + i * 256));
+    const int64_t off = (bh * 4 + 2 * i) * a.cap + tau0;
+    dma16o(a.v_scale + off, o.vrot[i], (lds_void *)(s->vs + i * 256));
+    dma16o(a.v_zero + off, o.vrot[i], (lds_void *)(s->vz + i * 256));
   }
 }
 
@@ -132,6 +169,22 @@ __device__ __forceinline__ i2 tr4(const uint32_t *p) {
   const uint32_t addr = (uint32_t)(uintptr_t)(lds_void *)p;
   asm volatile("ds_read_b64_tr_b4 %0, %1" : "=v"(r) : "v"(addr));
   return r;
+}
+
+// The four 16-byte pieces of q a lane uses (byte offsets 0, 16, 128, 144 from
+// p in LDS), read as inline assembly for the same reason as tr4, and waited
+// for before returning.
+__device__ __forceinline__ void q_reads(const uint16_t *p, uint4 (&w)[4]) {
+  const uint32_t addr = (uint32_t)(uintptr_t)(lds_void *)p;
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:16\n\t"
+      "ds_read_b128 %2, %4 offset:128\n\t"
+      "ds_read_b128 %3, %4 offset:144\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3])
+      : "v"(addr)
+      : "memory");
 }
 
 // Wait for this wave's LDS reads, including the transpose reads whose
@@ -238,7 +291,7 @@ __device__ __forceinline__ float max8(f4 a, f4 b) {
 struct Lds {
   KStage *ks;          // key part of the block (window role: its key staging)
   VStage *vs;          // value part (window role: its value staging)
-  float (*p)[kBT];     // [4][128] probabilities of the block (window role: q)
+  float (*p)[kPRow];   // [4][kPRow] probabilities of the block (window role: q)
   float *mask;         // [128] mask of the block (window role: probabilities)
   float *bias;         // [16] per A row: sum q z (keys), then sum p z (values)
   float *alpha;        // [4]
@@ -248,7 +301,8 @@ struct Lds {
 // [split * tps, min(n_main, (split + 1) * tps)) in blocks of 128.
 template <int NREP, bool MASKED>
 __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, int tps,
-                                           int split, const Lds &L, KStage *__restrict__ kbuf,
+                                           int split, int hk, int b, const Lds &L,
+                                           KStage *__restrict__ kbuf,
                                            VStage *__restrict__ vbuf) {
   static_assert(NREP == 1 || NREP == 2 || NREP == 4, "query heads per KV head");
   constexpr int GA = 16 / NREP;       // key groups per A operand
@@ -257,8 +311,6 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
   const int lane = threadIdx.x;
   const int i = lane & 15;
   const int kg = lane >> 4;
-  const int hk = blockIdx.y;
-  const int b = blockIdx.z;
   const int64_t bh = (int64_t)b * a.H + hk;
   const int64_t blk_begin = (int64_t)split * tps / kBT;
   int64_t blk_end = ((int64_t)split + 1) * tps / kBT;
@@ -276,15 +328,32 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
   const int h_s = (kg * NREP) / 4;               // head of the scores this lane holds
   const bool v_valid = kg < NREP;                // head of the outputs this lane holds = kg
 
-  // q of head h_a at this lane's 32 key channels c0(ks) + j
+  // q of the NREP heads (NREP rows of 256 bytes, contiguous) is copied into
+  // the probability buffer by the first DMA, ahead of the first block's
+  // copies; vmcnt completes in order, so waiting for q alone lets the block
+  // stream in meanwhile.  Every split holds at least one block
+  // (launch_decode_matrix rejects plans where one does not), so the copies
+  // are unconditional.  Lanes past the q rows re-read the last 16 bytes.
+  const DmaOffsets dmo(a, lane);
+  const uint16_t *q_lds = (const uint16_t *)&L.p[0][0];
+  dma16o(a.q + ((int64_t)b * a.Hq + hk * NREP) * kD, (uint32_t)min(lane, NREP * 16 - 1) * 16u,
+         (lds_void *)&L.p[0][0]);
+  stage_keys<MASKED>(a, bh, blk_begin, kbuf, L.mask, dmo, lane);
+  stage_values(a, bh, blk_begin, vbuf, dmo);
+  wait_vm<KDMA + kStageDma>();
+
+  // q of head h_a at this lane's 32 key channels c0(ks) + j, with
+  // c0(ks) = 64 (ks / 2) + 16 kg + 8 (ks % 2)
   float qa[4][8];
-  {
-    const uint16_t *q = a.q + ((int64_t)b * a.Hq + hk * NREP + h_a) * kD;
+  uint4 qw[4];
+  q_reads(q_lds + h_a * kD + 16 * kg, qw);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int c0 = 64 * (ks >> 1) + 16 * kg + 8 * (ks & 1);
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint32_t ww[4] = {qw[ks].x, qw[ks].y, qw[ks].z, qw[ks].w};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) qa[ks][j] = h2f(q[c0 + j]);
+    for (int j = 0; j < 4; ++j) {
+      qa[ks][2 * j] = h2f((uint16_t)(ww[j] & 0xffffu));
+      qa[ks][2 * j + 1] = h2f((uint16_t)(ww[j] >> 16));
     }
   }
   // The key A operand is q * s_k * 2^ek, with ek kept so that the largest |q|
@@ -313,11 +382,6 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
 #pragma unroll
   for (int g = 0; g < 4; ++g) dv[g][0] = dv[g][1] = (f4){0, 0, 0, 0};
 
-  if (blk_begin < blk_end) {
-    stage_keys<MASKED>(a, bh, blk_begin, kbuf, L.mask, lane);
-    stage_values(a, bh, blk_begin, vbuf, lane);
-  }
-
   for (int64_t blk = blk_begin; blk < blk_end; ++blk) {
     const bool has_next = blk + 1 < blk_end;
     // ================= key half =================
@@ -341,6 +405,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
       }
     }
     {
+      // the row maximum does not depend on the rotation
       float mx = max8(*(const f4 *)(kst.ks + lane * 8), *(const f4 *)(kst.ks + lane * 8 + 4));
       mx = group_max(row_max(mx));
       const float prod = mx * qmax;
@@ -361,10 +426,10 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int c0 = 64 * (ks >> 1) + 16 * kg + 8 * (ks & 1);
-      const f4 s0 = *(const f4 *)(kst.ks + g_a * kD + c0);
-      const f4 s1 = *(const f4 *)(kst.ks + g_a * kD + c0 + 4);
-      const f4 z0 = *(const f4 *)(kst.kz + g_a * kD + c0);
-      const f4 z1 = *(const f4 *)(kst.kz + g_a * kD + c0 + 4);
+      const f4 s0 = *(const f4 *)(kst.ks + rot_off(g_a, c0));
+      const f4 s1 = *(const f4 *)(kst.ks + rot_off(g_a, c0 + 4));
+      const f4 z0 = *(const f4 *)(kst.kz + rot_off(g_a, c0));
+      const f4 z1 = *(const f4 *)(kst.kz + rot_off(g_a, c0 + 4));
       const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
       const float zv[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
 #pragma unroll
@@ -376,7 +441,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
     }
     // every read of the key part has completed: request the next one
     wait_regs(xk);
-    if (has_next) stage_keys<MASKED>(a, bh, blk + 1, kbuf, L.mask, lane);
+    if (has_next) stage_keys<MASKED>(a, bh, blk + 1, kbuf, L.mask, dmo, lane);
 
     bz = group_sum(bz);
     if (kg == 0) L.bias[i] = bz;
@@ -397,6 +462,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
           dk[g][1] = mfma(ah[ks], bo, dk[g][1]);
           dk[g][0] = mfma(al[ks], be, dk[g][0]);
           dk[g][1] = mfma(al[ks], bo, dk[g][1]);
+          __builtin_amdgcn_sched_barrier(0);   // as on the value side
         }
       }
     }
@@ -472,10 +538,10 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
         const int t0 = 32 * kg + 16 * u + 8 * d;
         const f4 p0 = *(const f4 *)(&L.p[h_v][t0]);
         const f4 p1 = *(const f4 *)(&L.p[h_v][t0 + 4]);
-        const f4 s0 = *(const f4 *)(vst.vs + c_v * kBT + t0);
-        const f4 s1 = *(const f4 *)(vst.vs + c_v * kBT + t0 + 4);
-        const f4 z0 = *(const f4 *)(vst.vz + c_v * kBT + t0);
-        const f4 z1 = *(const f4 *)(vst.vz + c_v * kBT + t0 + 4);
+        const f4 s0 = *(const f4 *)(vst.vs + rot_off(c_v, t0));
+        const f4 s1 = *(const f4 *)(vst.vs + rot_off(c_v, t0 + 4));
+        const f4 z0 = *(const f4 *)(vst.vz + rot_off(c_v, t0));
+        const f4 z1 = *(const f4 *)(vst.vz + rot_off(c_v, t0 + 4));
         const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
         const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
         const float zv[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
@@ -489,7 +555,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
     }
     // every read of the value part has completed: request the next one
     wait_regs(xv);
-    if (has_next) stage_values(a, bh, blk + 1, vbuf, lane);
+    if (has_next) stage_values(a, bh, blk + 1, vbuf, dmo);
 
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -504,6 +570,10 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
           dv[g][1] = mfma(vh[u][d], bo, dv[g][1]);
           dv[g][0] = mfma(vl[u][d], be, dv[g][0]);
           dv[g][1] = mfma(vl[u][d], bo, dv[g][1]);
+          // convert one dword of codes at a time: the matrix core works on
+          // these four products while the next conversion issues, and the
+          // converted operands never pile up in registers
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
@@ -540,10 +610,8 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
 // half of the channels (scalar fp32) and accumulates two output channels.
 template <int NREP, bool MASKED>
 __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main, int chunk,
-                                            int slot, const Lds &L) {
+                                            int slot, int hk, int b, const Lds &L) {
   const int j = threadIdx.x;
-  const int hk = blockIdx.y;
-  const int b = blockIdx.z;
   const int64_t bh = (int64_t)b * a.H + hk;
   const int64_t Ta = n_main + (int64_t)kWT * chunk;
   const int64_t Tb = Ta + kWT < a.t ? Ta + kWT : a.t;
@@ -605,7 +673,7 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
     }
   }
   // q of the NREP heads, kept in the probability buffer (unused by this role)
-  float(*q_s)[kD] = L.p;
+  float(*q_s)[kPRow] = L.p;
   const uint16_t *q = a.q + ((int64_t)b * a.Hq + hk * NREP) * kD;
   for (int e = j; e < NREP * kD; e += 64) q_s[e / kD][e % kD] = h2f(q[e]);
   wait_vm<0>();
@@ -705,29 +773,41 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
   }
 }
 
-// grid: (n_window + n_split, H, B); block: one wave.  Workgroups
-// [0, n_window) take the window role (dispatched first, so they overlap the
-// longer block role), the rest the block role.
+// grid: n_window * H * B + n_split * H * B workgroups of one wave, in one
+// dimension.  All window-role workgroups come first (chunk fastest, then KV
+// head, then batch), so every one of them starts with the first workgroups
+// and finishes under the longer block role instead of trailing it; then the
+// block-role workgroups (split fastest, then KV head, then batch).
 template <int NREP, bool MASKED>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 decode_matrix_kernel(DecodeArgs a, int64_t n_main, int tps, int n_split, int n_window) {
   __shared__ KStage sm_k;
   __shared__ VStage sm_v;
-  __shared__ __attribute__((aligned(16))) float sm_p[4][kBT];
+  __shared__ __attribute__((aligned(16))) float sm_p[4][kPRow];
   __shared__ __attribute__((aligned(16))) float sm_mask[kBT];
   __shared__ __attribute__((aligned(16))) float sm_bias[16];
   __shared__ __attribute__((aligned(16))) float sm_alpha[4];
   const Lds L{&sm_k, &sm_v, sm_p, sm_mask, sm_bias, sm_alpha};
-  const int x = blockIdx.x;
-  if (x < n_window)
-    window_role<NREP, MASKED>(a, n_main, x, n_split + x, L);
-  else
-    block_role<NREP, MASKED>(a, n_main, tps, x - n_window, L, &sm_k, &sm_v);
+  const uint32_t lin = blockIdx.x;
+  const uint32_t n_win_all = (uint32_t)n_window * (uint32_t)(a.H * a.B);
+  if (lin < n_win_all) {
+    const uint32_t x = lin % (uint32_t)n_window, r = lin / (uint32_t)n_window;
+    window_role<NREP, MASKED>(a, n_main, (int)x, n_split + (int)x, (int)(r % (uint32_t)a.H),
+                              (int)(r / (uint32_t)a.H), L);
+  } else {
+    const uint32_t l2 = lin - n_win_all;
+    const uint32_t split = l2 % (uint32_t)n_split, r = l2 / (uint32_t)n_split;
+    block_role<NREP, MASKED>(a, n_main, tps, (int)split, (int)(r % (uint32_t)a.H),
+                             (int)(r / (uint32_t)a.H), L, &sm_k, &sm_v);
+  }
 }
 
 bool decode_matrix_supported(const DecodeArgs &a) {
+  // the value scale/zero DMA takes a 32-bit per-lane byte offset of cap * 4
+  // q is copied 16 bytes at a time
   return a.kb == 2 && a.vb == 2 && a.G == kG && a.D == kD &&
-         (a.n_rep == 1 || a.n_rep == 2 || a.n_rep == 4);
+         (a.n_rep == 1 || a.n_rep == 2 || a.n_rep == 4) && a.cap < ((int64_t)1 << 29) &&
+         ((uintptr_t)a.q & 15) == 0;
 }
 
 int decode_matrix_window_chunks(const DecodeArgs &a, int64_t n_main) {
@@ -759,7 +839,9 @@ hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int tokens_
   if (a.n_kq % kG != 0) return hipErrorInvalidValue;
   const int n_window = decode_matrix_window_chunks(a, n_main);
   if (n_splits + n_window <= 0 || n_splits + n_window > a.S_total) return hipErrorInvalidValue;
-  dim3 grid((unsigned)(n_window + n_splits), (unsigned)a.H, (unsigned)a.B);
+  const int64_t n_wg = ((int64_t)n_window + n_splits) * a.H * a.B;
+  if (n_wg > ((int64_t)1 << 26)) return hipErrorInvalidValue;   // 64-thread groups, 32-bit ids
+  dim3 grid((unsigned)n_wg);
   switch (a.n_rep) {
     case 1: launch_rep<1>(a, grid, s, n_main, tokens_per_split, n_splits, n_window); break;
     case 2: launch_rep<2>(a, grid, s, n_main, tokens_per_split, n_splits, n_window); break;
