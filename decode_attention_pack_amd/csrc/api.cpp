@@ -95,7 +95,13 @@ int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
 
 constexpr int kGenericMinSplit = 256;
 constexpr int kMatrixBlock = 128;   // tokens per block of the matrix-core kernel
-constexpr int kTargetWorkgroups = 4096;
+constexpr int kTargetWorkgroups = 4096;   // scalar kernel
+// Matrix kernel: block-role workgroups to aim for.  One wave per SIMD (1024
+// on 256 CUs) streaming longer splits measures faster than two waves per
+// SIMD with half the splits each; when the window role already fills more
+// than that many slots, twice as many shorter splits keep the SIMDs busy
+// while those finish.
+constexpr int kMatrixWorkgroups = 1024;
 
 struct Plan {
   bool matrix = false;
@@ -120,16 +126,19 @@ Plan make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
   p.matrix = path != KIVI_PATH_GENERIC && t > 0 && kivi::decode_matrix_supported(a);
   if (p.matrix) {
     p.n_main = (a.n_vq / kMatrixBlock) * kMatrixBlock;
+    p.n_window = kivi::decode_matrix_window_chunks(a, p.n_main);
     int64_t tps = (tps_req + kMatrixBlock - 1) / kMatrixBlock * kMatrixBlock;
     if (tps == 0) {
-      // whole blocks per split, about kTargetWorkgroups workgroups in all
-      const int64_t splits = max64(1, kTargetWorkgroups / units);
+      // whole blocks per split, about kMatrixWorkgroups block-role workgroups
+      const int64_t window_wgs = (int64_t)p.n_window * units;
+      const int64_t target = window_wgs > kMatrixWorkgroups ? 2 * kMatrixWorkgroups
+                                                            : kMatrixWorkgroups;
+      const int64_t splits = max64(1, target / units);
       const int64_t blocks = p.n_main / kMatrixBlock;
       tps = max64(1, (blocks + splits - 1) / splits) * kMatrixBlock;
     }
     p.tps_matrix = (int)tps;
     p.n_split_matrix = (int)((p.n_main + tps - 1) / tps);
-    p.n_window = kivi::decode_matrix_window_chunks(a, p.n_main);
     p.S_total = p.n_split_matrix + p.n_window;
     return p;
   }

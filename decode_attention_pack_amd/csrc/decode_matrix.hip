@@ -213,6 +213,17 @@ __device__ __forceinline__ void codes_to_b(uint32_t x, h8 &be, h8 &bo) {
   bo = (h8){o0[0], o0[1], o1[0], o1[1], o2[0], o2[1], o3[0], o3[1]};
 }
 
+// Schedule of a block's 64 products: each MFMA is followed by three VALU
+// instructions (the code conversions of a later MFMA group among them), so
+// the vector unit issues while the matrix core works instead of after it.
+__device__ __forceinline__ void mfma_valu_interleave() {
+#pragma unroll
+  for (int k = 0; k < 64; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
+  }
+}
+
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -338,8 +349,17 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
   const uint16_t *q_lds = (const uint16_t *)&L.p[0][0];
   dma16o(a.q + ((int64_t)b * a.Hq + hk * NREP) * kD, (uint32_t)min(lane, NREP * 16 - 1) * 16u,
          (lds_void *)&L.p[0][0]);
-  stage_keys<MASKED>(a, bh, blk_begin, kbuf, L.mask, dmo, lane);
-  stage_values(a, bh, blk_begin, vbuf, dmo);
+  // The split's blocks are visited from a starting block that a hash of
+  // (slab, split) picks, wrapping around.  Every slab's arrays sit a multiple
+  // of the capacity apart, so workgroups walking their splits in lock-step
+  // from the first block hit HBM channels in step for some capacities (13%
+  // slower at 257 x 128 tokens); scattered starting points break that up.
+  // The order only changes the rounding order of the online softmax.
+  const int64_t nblk = blk_end - blk_begin;
+  const int64_t rot =
+      (int64_t)((((uint32_t)bh * 2654435761u) ^ ((uint32_t)split * 2246822519u)) >> 8) % nblk;
+  stage_keys<MASKED>(a, bh, blk_begin + rot, kbuf, L.mask, dmo, lane);
+  stage_values(a, bh, blk_begin + rot, vbuf, dmo);
   wait_vm<KDMA + kStageDma>();
 
   // q of head h_a at this lane's 32 key channels c0(ks) + j, with
@@ -382,10 +402,11 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
 #pragma unroll
   for (int g = 0; g < 4; ++g) dv[g][0] = dv[g][1] = (f4){0, 0, 0, 0};
 
-  for (int64_t blk = blk_begin; blk < blk_end; ++blk) {
-    const bool has_next = blk + 1 < blk_end;
+  for (int64_t it = 0; it < nblk; ++it) {
+    const bool has_next = it + 1 < nblk;
+    const int64_t nxt = blk_begin + (it + 1 + rot) % nblk;   // the block staged next
     // ================= key half =================
-    wait_vm<kStageDma>();            // key part of blk in; its value part may still fly
+    wait_vm<kStageDma>();            // key part of this block in; its value part may still fly
     const KStage &kst = *kbuf;
     i2 xk[8];                        // [group g][64-channel half rho]
 #pragma unroll
@@ -441,7 +462,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
     }
     // every read of the key part has completed: request the next one
     wait_regs(xk);
-    if (has_next) stage_keys<MASKED>(a, bh, blk + 1, kbuf, L.mask, dmo, lane);
+    if (has_next) stage_keys<MASKED>(a, bh, nxt, kbuf, L.mask, dmo, lane);
 
     bz = group_sum(bz);
     if (kg == 0) L.bias[i] = bz;
@@ -462,10 +483,10 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
           dk[g][1] = mfma(ah[ks], bo, dk[g][1]);
           dk[g][0] = mfma(al[ks], be, dk[g][0]);
           dk[g][1] = mfma(al[ks], bo, dk[g][1]);
-          __builtin_amdgcn_sched_barrier(0);   // as on the value side
         }
       }
     }
+    mfma_valu_interleave();
     wave_lds_sync();
 
     // scores (even / odd token of each pair) and online softmax, head h_s
@@ -498,7 +519,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
 
     // ================= value half =================
     if (has_next)
-      wait_vm<KDMA>();               // value part of blk in; the next key part may fly
+      wait_vm<KDMA>();               // value part of this block in; the next key part may fly
     else
       wait_vm<0>();
     wave_lds_sync();
@@ -555,7 +576,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
     }
     // every read of the value part has completed: request the next one
     wait_regs(xv);
-    if (has_next) stage_values(a, bh, blk + 1, vbuf, dmo);
+    if (has_next) stage_values(a, bh, nxt, vbuf, dmo);
 
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -570,13 +591,10 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
           dv[g][1] = mfma(vh[u][d], bo, dv[g][1]);
           dv[g][0] = mfma(vl[u][d], be, dv[g][0]);
           dv[g][1] = mfma(vl[u][d], bo, dv[g][1]);
-          // convert one dword of codes at a time: the matrix core works on
-          // these four products while the next conversion issues, and the
-          // converted operands never pile up in registers
-          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
+    mfma_valu_interleave();
   }
 
   // ---- write the partial (acc[128], m, l) of each query head

@@ -215,3 +215,47 @@ def kivi_decode_attn(cache: Cache, q, mask=None, out=None, workspace=None, token
     _check(lib().kivi_decode_attn_ex(ctypes.byref(cache.c), qp, Hq, mp, op, wp,
                                      workspace.numel(), tokens_per_split, path, _stream(stream)))
     return out
+
+
+class BoundCall:
+    """A library call whose arguments were checked and marshalled once.
+
+    Calling it re-issues the same call on the same tensors (their contents may
+    change between calls; the cache descriptor is passed by reference, so the
+    token count the library keeps in it stays current).  For loops that issue
+    the same call many times, where per-call argument checks would cost more
+    host time than the kernels take.
+    """
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, tuple(args), keep
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+
+
+def bind_append(cache: Cache, k_new, v_new, stream=None) -> BoundCall:
+    n = k_new.shape[2]
+    shape = (cache.B, cache.H, n, cache.D)
+    kp = _dev(k_new, torch.float16, shape, "k_new")
+    vp = _dev(v_new, torch.float16, shape, "v_new")
+    return BoundCall(lib().kivi_append, [ctypes.byref(cache.c), kp, vp, n, _stream(stream)],
+                     (cache, k_new, v_new))
+
+
+def bind_decode_attn(cache: Cache, q, out, workspace, mask=None, tokens_per_split=0,
+                     path=KIVI_PATH_AUTO, stream=None) -> BoundCall:
+    """Bound kivi_decode_attn; the mask, when given, must already cover every
+    token the cache will hold when the call is issued (its row length is the
+    token count at binding time)."""
+    Hq = q.shape[1]
+    qp = _dev(q, torch.float16, (cache.B, Hq, cache.D), "q")
+    mp = None
+    if mask is not None:
+        mp = _dev(mask, torch.float32, (cache.B, cache.n_tokens), "mask")
+    op = _dev(out, torch.float32, (cache.B, Hq, cache.D), "out")
+    wp = _dev(workspace, torch.uint8, None, "workspace")
+    return BoundCall(lib().kivi_decode_attn_ex,
+                     [ctypes.byref(cache.c), qp, Hq, mp, op, wp, workspace.numel(), tokens_per_split,
+                      path, _stream(stream)], (cache, q, mask, out, workspace))
+
