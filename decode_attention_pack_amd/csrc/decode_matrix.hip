@@ -247,16 +247,36 @@ __device__ __forceinline__ float row_sum(float v) {
 }
 #undef KIVI_ROR
 
-// Sum / max over the 4 lane groups (lanes l, l^16, l^32, l^48).
+// Sum / max over the 4 lane groups (lanes l, l^16, l^32, l^48), with the
+// gfx950 lane-swap instructions instead of LDS permutes.  For a and b holding
+// the same value x, v_permlane16_swap leaves rows (x0, x0, x2, x2) in a and
+// (x1, x1, x3, x3) in b (a row is 16 lanes), so a + b holds x[l] + x[l ^ 16]
+// in every lane; v_permlane32_swap does the same for halves (l ^ 32).  Inline
+// assembly: the compiler builtin for these returns the first register twice
+// in this toolchain.  The nops cover the VALU-write/swap-read hazard.
+__device__ __forceinline__ void lane_swap16(float &a, float &b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void lane_swap32(float &a, float &b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
 __device__ __forceinline__ float group_sum(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  float a = v, b = v;
+  lane_swap16(a, b);
+  v = a + b;
+  a = v;
+  b = v;
+  lane_swap32(a, b);
+  return a + b;
 }
 __device__ __forceinline__ float group_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  float a = v, b = v;
+  lane_swap16(a, b);
+  v = fmaxf(a, b);
+  a = v;
+  b = v;
+  lane_swap32(a, b);
+  return fmaxf(a, b);
 }
 
 // The workgroup is a single wave, whose LDS accesses complete in order, so
@@ -796,8 +816,11 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
 // head, then batch), so every one of them starts with the first workgroups
 // and finishes under the longer block role instead of trailing it; then the
 // block-role workgroups (split fastest, then KV head, then batch).
+// The masked variant holds the block's mask in registers as well; it may use
+// more than half the register file (one wave per SIMD) rather than spill, since
+// a spill reload inside the block loop would wait for every DMA in flight.
 template <int NREP, bool MASKED>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MASKED ? 1 : 2)))
 decode_matrix_kernel(DecodeArgs a, int64_t n_main, int tps, int n_split, int n_window) {
   __shared__ KStage sm_k;
   __shared__ VStage sm_v;
