@@ -21,35 +21,8 @@ namespace kivi {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kHeads = 8;     // query heads per workgroup
+constexpr int kHeads = 8;     // most query heads per workgroup
 constexpr int kChunk = 256;   // tokens per inner step (one per thread)
-
-// Key channel `c` of token `tau` as attention sees it.
-__device__ __forceinline__ float key_hat(const DecodeArgs &a, int64_t bh, int64_t tau, int c) {
-  if (tau < a.n_kq) {
-    const int per = 32 / a.kb;
-    const int words = a.G / per;
-    const int64_t g = tau / a.G;
-    const int e = (int)(tau - g * a.G);
-    const int64_t sz = (bh * (a.cap / a.G) + g) * a.D + c;
-    const uint32_t w = a.k_codes[sz * words + e / per];
-    const uint32_t code = (w >> (a.kb * (e % per))) & ((1u << a.kb) - 1u);
-    return __fadd_rn(__fmul_rn((float)code, a.k_scale[sz]), a.k_zero[sz]);
-  }
-  return h2f(a.k_res[(bh * a.R + tau % a.R) * a.D + c]);
-}
-
-// Value channel `c` of token `tau` as attention sees it.
-__device__ __forceinline__ float value_hat(const DecodeArgs &a, int64_t bh, int64_t tau, int c) {
-  if (tau < a.n_vq) {
-    const int per = 32 / a.vb;
-    const uint32_t w = a.v_codes[(bh * a.cap + tau) * (a.D / per) + c / per];
-    const uint32_t code = (w >> (a.vb * (c % per))) & ((1u << a.vb) - 1u);
-    const int64_t sz = (bh * (a.D / a.G) + c / a.G) * a.cap + tau;
-    return __fadd_rn(__fmul_rn((float)code, a.v_scale[sz]), a.v_zero[sz]);
-  }
-  return h2f(a.v_res[(bh * a.R + tau % a.R) * a.D + c]);
-}
 
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -63,13 +36,16 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 }  // namespace
 
-// grid: (n_splits, H * head_chunks, B); block: 256.
+// grid: (n_splits, H * head_chunks, B); block: 256.  NH (1, 2, 4 or 8) query
+// heads per workgroup: the smallest power of two covering the heads per KV
+// head, up to 8, so that MHA shapes do not carry 8 heads' worth of products.
+template <int NH>
 __global__ void __launch_bounds__(kThreads)
 decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int slot_base,
                       int head_chunks) {
-  __shared__ float q_s[kHeads][256];
-  __shared__ float p_s[kHeads][kChunk];
-  __shared__ float stat_s[kHeads][2];   // new m, alpha
+  __shared__ float q_s[NH][256];
+  __shared__ float p_s[NH][kChunk];
+  __shared__ float stat_s[NH][2];   // new m, alpha
   __shared__ float red_s[kThreads];
 
   const int tid = threadIdx.x;
@@ -78,22 +54,22 @@ decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int
   const int hc = blockIdx.y % head_chunks;
   const int b = blockIdx.z;
   const int64_t bh = (int64_t)b * a.H + h;
-  const int hq0 = h * a.n_rep + hc * kHeads;
-  const int nh = min(kHeads, a.n_rep - hc * kHeads);
+  const int hq0 = h * a.n_rep + hc * NH;
+  const int nh = min(NH, a.n_rep - hc * NH);
   const int D = a.D;
 
   int64_t s0 = tok_begin + (int64_t)split * tokens_per_split;
   int64_t s1 = s0 + tokens_per_split;
   if (s1 > a.t) s1 = a.t;
 
-  for (int i = tid; i < kHeads * D; i += kThreads) {
+  for (int i = tid; i < NH * D; i += kThreads) {
     const int j = i / D, c = i % D;
     q_s[j][c] = j < nh ? h2f(a.q[((int64_t)b * a.Hq + hq0 + j) * D + c]) : 0.0f;
   }
 
-  float m[kHeads], l[kHeads], acc[kHeads];
+  float m[NH], l[NH], acc[NH];
 #pragma unroll
-  for (int j = 0; j < kHeads; ++j) {
+  for (int j = 0; j < NH; ++j) {
     m[j] = -INFINITY;
     l[j] = 0.0f;
     acc[j] = 0.0f;
@@ -101,29 +77,60 @@ decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int
   const int c_own = tid % D;           // value channel owned in the V phase
   const int n_par = kThreads / D;      // token parities sharing a channel
   const int par = tid / D;
+  // value code word, bit offset, scale and zero rows of channel c_own
+  const int vper = 32 / a.vb;
+  const int64_t vwords = D / vper;     // code words per token
+  const uint32_t *vcw = a.v_codes + bh * a.cap * vwords + c_own / vper;
+  const int vsh = a.vb * (c_own % vper);
+  const uint32_t vmsk = (1u << a.vb) - 1u;
+  const float *vsc = a.v_scale + (bh * (D / a.G) + c_own / a.G) * a.cap;
+  const float *vzr = a.v_zero + (bh * (D / a.G) + c_own / a.G) * a.cap;
   __syncthreads();
 
   for (int64_t c0 = s0; c0 < s1; c0 += kChunk) {
     // scores: one token per thread, all heads of the chunk at once
     const int64_t tau = c0 + tid;
-    float sc[kHeads];
+    float sc[NH];
 #pragma unroll
-    for (int j = 0; j < kHeads; ++j) sc[j] = 0.0f;
+    for (int j = 0; j < NH; ++j) sc[j] = 0.0f;
     if (tau < s1) {
-      for (int c = 0; c < D; ++c) {
-        const float k = key_hat(a, bh, tau, c);
+      // key channel c of token tau as attention sees it: code * scale + zero
+      // (fp32 multiply, then add) below n_kq, else the fp16 window row; the
+      // per-token index arithmetic (group, word, bit offset) is done once
+      if (tau < a.n_kq) {
+        const int per = 32 / a.kb;
+        const int words = a.G / per;
+        const int64_t g = tau / a.G;
+        const int e = (int)(tau - g * a.G);
+        const int64_t zb = (bh * (a.cap / a.G) + g) * D;
+        const uint32_t *cw = a.k_codes + zb * words + e / per;
+        const float *ks = a.k_scale + zb;
+        const float *kz = a.k_zero + zb;
+        const int sh = a.kb * (e % per);
+        const uint32_t msk = (1u << a.kb) - 1u;
+        for (int c = 0; c < D; ++c) {
+          const uint32_t code = (cw[c * words] >> sh) & msk;
+          const float k = __fadd_rn(__fmul_rn((float)code, ks[c]), kz[c]);
 #pragma unroll
-        for (int j = 0; j < kHeads; ++j) sc[j] = fmaf(q_s[j][c], k, sc[j]);
+          for (int j = 0; j < NH; ++j) sc[j] = fmaf(q_s[j][c], k, sc[j]);
+        }
+      } else {
+        const uint16_t *row = a.k_res + (bh * a.R + tau % a.R) * D;
+        for (int c = 0; c < D; ++c) {
+          const float k = h2f(row[c]);
+#pragma unroll
+          for (int j = 0; j < NH; ++j) sc[j] = fmaf(q_s[j][c], k, sc[j]);
+        }
       }
       const float mk = a.mask ? a.mask[(int64_t)b * a.t + tau] : 0.0f;
 #pragma unroll
-      for (int j = 0; j < kHeads; ++j) sc[j] = sc[j] * a.sm_scale + mk;
+      for (int j = 0; j < NH; ++j) sc[j] = sc[j] * a.sm_scale + mk;
     } else {
 #pragma unroll
-      for (int j = 0; j < kHeads; ++j) sc[j] = -INFINITY;
+      for (int j = 0; j < NH; ++j) sc[j] = -INFINITY;
     }
 #pragma unroll
-    for (int j = 0; j < kHeads; ++j) p_s[j][tid] = sc[j];
+    for (int j = 0; j < NH; ++j) p_s[j][tid] = sc[j];
     __syncthreads();
 
     // online softmax statistics, one wave per head
@@ -148,7 +155,7 @@ decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kHeads; ++j) {
+    for (int j = 0; j < NH; ++j) {
       if (j < nh) {
         const float alpha = stat_s[j][1];
         m[j] = stat_s[j][0];
@@ -157,13 +164,21 @@ decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int
       }
     }
 
-    // values: thread owns channel c_own and every n_par-th token
+    // values: thread owns channel c_own and every n_par-th token; value
+    // channel c_own of token tv is code * scale + zero below n_vq, else the
+    // fp16 window row
     const int64_t cend = (c0 + kChunk < s1) ? c0 + kChunk : s1;
     for (int64_t tv = c0 + par; tv < cend; tv += n_par) {
-      const float v = value_hat(a, bh, tv, c_own);
+      float v;
+      if (tv < a.n_vq) {
+        const uint32_t code = (vcw[tv * vwords] >> vsh) & vmsk;
+        v = __fadd_rn(__fmul_rn((float)code, vsc[tv]), vzr[tv]);
+      } else {
+        v = h2f(a.v_res[(bh * a.R + tv % a.R) * D + c_own]);
+      }
       const int i = (int)(tv - c0);
 #pragma unroll
-      for (int j = 0; j < kHeads; ++j) acc[j] = fmaf(p_s[j][i], v, acc[j]);
+      for (int j = 0; j < NH; ++j) acc[j] = fmaf(p_s[j][i], v, acc[j]);
     }
     __syncthreads();
   }
@@ -274,8 +289,18 @@ hipError_t launch_decode_generic(const DecodeArgs &a, int64_t tok_begin, int tok
   if (n_splits <= 0) return hipSuccess;
   const int head_chunks = (a.n_rep + kHeads - 1) / kHeads;
   dim3 grid((unsigned)n_splits, (unsigned)(a.H * head_chunks), (unsigned)a.B);
-  hipLaunchKernelGGL(decode_generic_kernel, grid, dim3(kThreads), 0, s, a, tok_begin,
-                     tokens_per_split, slot_base, head_chunks);
+  if (a.n_rep == 1)
+    hipLaunchKernelGGL(decode_generic_kernel<1>, grid, dim3(kThreads), 0, s, a, tok_begin,
+                       tokens_per_split, slot_base, head_chunks);
+  else if (a.n_rep == 2)
+    hipLaunchKernelGGL(decode_generic_kernel<2>, grid, dim3(kThreads), 0, s, a, tok_begin,
+                       tokens_per_split, slot_base, head_chunks);
+  else if (a.n_rep <= 4)
+    hipLaunchKernelGGL(decode_generic_kernel<4>, grid, dim3(kThreads), 0, s, a, tok_begin,
+                       tokens_per_split, slot_base, head_chunks);
+  else
+    hipLaunchKernelGGL(decode_generic_kernel<kHeads>, grid, dim3(kThreads), 0, s, a, tok_begin,
+                       tokens_per_split, slot_base, head_chunks);
   return hipGetLastError();
 }
 
