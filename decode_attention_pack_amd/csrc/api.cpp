@@ -95,6 +95,11 @@ int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
 
 constexpr int kGenericMinSplit = 256;
 constexpr int kMatrixBlock = 128;   // tokens per block of the matrix-core kernel
+constexpr int kVectorStep = 128;    // tokens per step of the vector kernel's four waves
+// Vector kernel: workgroups to aim for.  Three waves per SIMD hold 768
+// workgroups at once; fewer, longer splits measure faster than twice as
+// many short ones (less per-split set-up and merge work).
+constexpr int kVectorWorkgroups = 2048;
 constexpr int kTargetWorkgroups = 4096;   // scalar kernel
 // Matrix kernel: block-role workgroups to aim for.  One wave per SIMD (1024
 // on 256 CUs) streaming longer splits measures faster than two waves per
@@ -109,7 +114,8 @@ struct Plan {
   int tps_matrix = 0;
   int n_split_matrix = 0;
   int n_window = 0;             // 32-token chunks of [n_main, t) in its window role
-  int tps_generic = 0;          // scalar kernel (shapes the matrix kernel does not cover)
+  bool vector = false;          // vector kernel instead of the scalar one
+  int tps_generic = 0;          // vector / scalar kernel (shapes the matrix kernel does not cover)
   int n_split_generic = 0;
   int S_total = 0;
 };
@@ -123,7 +129,8 @@ Plan make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
   const int64_t t = c->n_tokens;
   const int n_rep = Hq / c->n_kv_heads;
   const int64_t units = (int64_t)c->batch * c->n_kv_heads;
-  p.matrix = path != KIVI_PATH_GENERIC && t > 0 && kivi::decode_matrix_supported(a);
+  p.matrix = (path == KIVI_PATH_AUTO || path == KIVI_PATH_MATRIX) && t > 0 &&
+             kivi::decode_matrix_supported(a);
   if (p.matrix) {
     p.n_main = (a.n_vq / kMatrixBlock) * kMatrixBlock;
     p.n_window = kivi::decode_matrix_window_chunks(a, p.n_main);
@@ -142,8 +149,15 @@ Plan make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
     p.S_total = p.n_split_matrix + p.n_window;
     return p;
   }
+  p.vector = (path == KIVI_PATH_AUTO || path == KIVI_PATH_VECTOR) &&
+             kivi::decode_vector_supported(a);
   int64_t tps = tps_req;
-  if (tps == 0) {
+  if (tps == 0 && p.vector) {
+    // whole 4-group steps (one group per wave), about kVectorWorkgroups
+    // workgroups
+    const int64_t splits = max64(1, kVectorWorkgroups / units);
+    tps = max64(1, ((t + splits - 1) / splits + kVectorStep - 1) / kVectorStep) * kVectorStep;
+  } else if (tps == 0) {
     const int64_t gunits = units * head_chunks(n_rep);
     const int64_t splits = max64(1, kTargetWorkgroups / gunits);
     tps = ((t + splits - 1) / splits + kGenericMinSplit - 1) / kGenericMinSplit * kGenericMinSplit;
@@ -308,7 +322,7 @@ size_t kivi_decode_attn_workspace_bytes_ex(const kivi_cache *c, int32_t n_q_head
   if (check_cache(c, "kivi_decode_attn_workspace_bytes")) return 0;
   if (n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0) return 0;
   if (tokens_per_split < 0 || tokens_per_split % 64 != 0) return 0;
-  if (path < KIVI_PATH_AUTO || path > KIVI_PATH_MATRIX) return 0;
+  if (path < KIVI_PATH_AUTO || path > KIVI_PATH_VECTOR) return 0;
   // partial slots: acc[D], m, l, padded to D + 4 floats (16-byte rows)
   return (size_t)c->batch * n_q_heads * max_slots(c, tokens_per_split) * (c->head_dim + 4) *
          sizeof(float);
@@ -331,7 +345,7 @@ int kivi_decode_attn_ex(const kivi_cache *c, const void *q_fp16, int32_t n_q_hea
   if (tokens_per_split < 0 || tokens_per_split % 64 != 0)
     return fail(KIVI_ERR_INVALID_ARG, "%s: tokens_per_split %d must be 0 or a positive multiple of 64",
                 who, tokens_per_split);
-  if (path < KIVI_PATH_AUTO || path > KIVI_PATH_MATRIX)
+  if (path < KIVI_PATH_AUTO || path > KIVI_PATH_VECTOR)
     return fail(KIVI_ERR_INVALID_ARG, "%s: unknown path %d", who, path);
   const size_t need = kivi_decode_attn_workspace_bytes_ex(c, n_q_heads, tokens_per_split, path);
   if (!workspace || workspace_bytes < need)
@@ -368,6 +382,8 @@ int kivi_decode_attn_ex(const kivi_cache *c, const void *q_fp16, int32_t n_q_hea
 
   if (path == KIVI_PATH_MATRIX && !kivi::decode_matrix_supported(a))
     return fail(KIVI_ERR_INVALID_ARG, "%s: the matrix-core kernel does not handle this shape", who);
+  if (path == KIVI_PATH_VECTOR && !kivi::decode_vector_supported(a))
+    return fail(KIVI_ERR_INVALID_ARG, "%s: the vector kernel does not handle this shape", who);
   const Plan p = make_plan(c, n_q_heads, tokens_per_split, path, a);
   if (p.S_total > max_slots(c, tokens_per_split))
     return fail(KIVI_ERR_WORKSPACE, "%s: internal split plan exceeds the workspace bound", who);
@@ -376,10 +392,15 @@ int kivi_decode_attn_ex(const kivi_cache *c, const void *q_fp16, int32_t n_q_hea
   if (p.matrix)
     rc = hip_status(kivi::launch_decode_matrix(a, p.n_main, p.tps_matrix, p.n_split_matrix, s),
                     "kivi_decode_attn (matrix)");
+  else if (p.vector)
+    rc = hip_status(kivi::launch_decode_vector(a, p.tps_generic, p.n_split_generic, s),
+                    "kivi_decode_attn (vector)");
   else
     rc = hip_status(kivi::launch_decode_generic(a, 0, p.tps_generic, p.n_split_generic, 0, s),
                     "kivi_decode_attn (scalar)");
   if (rc) return rc;
+  // a single vector-kernel split writes the output itself
+  if (p.vector && p.n_split_generic == 1) return KIVI_OK;
   return hip_status(kivi::launch_combine(a, s), "kivi_decode_attn (combine)");
 }
 

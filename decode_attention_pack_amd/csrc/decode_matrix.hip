@@ -46,6 +46,7 @@
 #include <math.h>
 
 #include "kivi_internal.hpp"
+#include "lane_ops.hpp"
 
 namespace kivi {
 
@@ -226,57 +227,6 @@ __device__ __forceinline__ void mfma_valu_interleave() {
 
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-// Reductions over the 16 lanes of a row (DPP row rotations by 8, 4, 2, 1).
-#define KIVI_ROR(v, c) \
-  __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), c, 0xF, 0xF, false))
-__device__ __forceinline__ float row_max(float v) {
-  v = fmaxf(v, KIVI_ROR(v, 0x128));
-  v = fmaxf(v, KIVI_ROR(v, 0x124));
-  v = fmaxf(v, KIVI_ROR(v, 0x122));
-  v = fmaxf(v, KIVI_ROR(v, 0x121));
-  return v;
-}
-__device__ __forceinline__ float row_sum(float v) {
-  v += KIVI_ROR(v, 0x128);
-  v += KIVI_ROR(v, 0x124);
-  v += KIVI_ROR(v, 0x122);
-  v += KIVI_ROR(v, 0x121);
-  return v;
-}
-#undef KIVI_ROR
-
-// Sum / max over the 4 lane groups (lanes l, l^16, l^32, l^48), with the
-// gfx950 lane-swap instructions instead of LDS permutes.  For a and b holding
-// the same value x, v_permlane16_swap leaves rows (x0, x0, x2, x2) in a and
-// (x1, x1, x3, x3) in b (a row is 16 lanes), so a + b holds x[l] + x[l ^ 16]
-// in every lane; v_permlane32_swap does the same for halves (l ^ 32).  Inline
-// assembly: the compiler builtin for these returns the first register twice
-// in this toolchain.  The nops cover the VALU-write/swap-read hazard.
-__device__ __forceinline__ void lane_swap16(float &a, float &b) {
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ void lane_swap32(float &a, float &b) {
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ float group_sum(float v) {
-  float a = v, b = v;
-  lane_swap16(a, b);
-  v = a + b;
-  a = v;
-  b = v;
-  lane_swap32(a, b);
-  return a + b;
-}
-__device__ __forceinline__ float group_max(float v) {
-  float a = v, b = v;
-  lane_swap16(a, b);
-  v = fmaxf(a, b);
-  a = v;
-  b = v;
-  lane_swap32(a, b);
-  return fmaxf(a, b);
 }
 
 // The workgroup is a single wave, whose LDS accesses complete in order, so

@@ -1,0 +1,465 @@
+// decode_vector.hip -- vector-unit decode attention over the KIVI cache for
+// head_dim 128, group size 32, 2- or 4-bit key and value codes and one or
+// two query heads per KV head (the MHA and 2-way GQA shapes, which give the
+// matrix cores too little to do).
+//
+// Method source: web page "Literature audit -- Group 2 (KV-cache compression
+// primary sources)", section "1. KIVI -- kivi2024", list "Core algorithm
+// (implementation-grade)", item 5 (attention over quantized keys/values plus
+// the fp16 window), item 4 (which tokens are quantized) and items 2-3
+// (per-channel key groups, per-token value groups).
+//
+// Work split.  A workgroup (4 waves) owns a token range of one (batch row,
+// KV head) slab and its NH query heads.  Wave w takes the 32-token groups
+// w, w + 4, ... of the range and keeps its own online softmax (m, l, acc),
+// so the token loop has no workgroup barrier; the four waves merge once at
+// the end and write one (acc[128], m, l) partial for the split combine.
+//
+// Keys, per 32-token group: lane i owns channels 2i and 2i+1 and reads
+// their codes for all 32 tokens with one or two 16-byte loads (the group's
+// codes are one contiguous block of 128 channel rows).  For each 16-token
+// half it forms 16 partial dot products (q_c s_c) code + q_c z_c over its
+// two channels; a reduce-scatter across the 64 lanes (lane swaps for lane
+// bits 5 and 4, DPP mirrors for bits 3 and 2, quad swaps for bits 1 and 0)
+// leaves the score of token i >> 2 of the half in lane i.
+//
+// Values: lane i takes token i >> 2 of each half and channel quarter i & 3
+// (32 channels, which are one value group: one scale and zero per token),
+// reads the quarter's codes with one 8- or 16-byte load and accumulates
+// p s code into 32 registers; the zero-point term p z is kept per lane and
+// added once at the end.  The fp16 windows are read in the same lane
+// layouts.
+#include <math.h>
+
+#include "kivi_internal.hpp"
+#include "lane_ops.hpp"
+
+namespace kivi {
+
+namespace {
+
+constexpr int kVD = 128;       // head_dim
+constexpr int kVG = 32;        // group size (tokens of a key group, channels of a value group)
+constexpr int kVWaves = 4;
+constexpr int kVThreads = 64 * kVWaves;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Bytes 0, 1 (HI false) or 2, 3 (HI true) of x, each holding a code 0..15,
+// as floats.  Read as an fp8 E4M3 number, a byte c < 16 is c * 2^-9 (the
+// subnormals and the first binade are evenly spaced), so the scaled
+// conversion by 2^9 returns c exactly, two codes per instruction.
+template <bool HI>
+__device__ __forceinline__ f32x2 code_pair(uint32_t x) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)x, 512.0f, HI);
+}
+
+// Codes of one 32-bit word as floats, code k (bits [BITS k, BITS k + BITS))
+// in f[k].
+template <int BITS>
+__device__ __forceinline__ void unpack_word(uint32_t w, float (&f)[32 / BITS]) {
+  if constexpr (BITS == 4) {
+    // byte i of lo holds code 2i, byte i of hi code 2i + 1
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    const f32x2 a = code_pair<false>(lo), b = code_pair<true>(lo);
+    const f32x2 c = code_pair<false>(hi), d = code_pair<true>(hi);
+    f[0] = a.x; f[2] = a.y; f[4] = b.x; f[6] = b.y;
+    f[1] = c.x; f[3] = c.y; f[5] = d.x; f[7] = d.y;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      // byte i of m holds code 4i + r
+      const uint32_t m = (w >> (2 * r)) & 0x03030303u;
+      const f32x2 a = code_pair<false>(m), b = code_pair<true>(m);
+      f[r] = a.x; f[4 + r] = a.y; f[8 + r] = b.x; f[12 + r] = b.y;
+    }
+  }
+}
+
+template <int N4>
+__device__ __forceinline__ void load_words(const uint32_t *p, uint32_t *w) {
+#pragma unroll
+  for (int i = 0; i < N4; ++i) {
+    const uint4 v = *(const uint4 *)(p + 4 * i);
+    w[4 * i] = v.x;
+    w[4 * i + 1] = v.y;
+    w[4 * i + 2] = v.z;
+    w[4 * i + 3] = v.w;
+  }
+}
+
+// Reduce-scatter of the 16 per-lane partial sums v[e] (e = token of a
+// 16-token half) over all 64 lanes: returns, in lane i, the sum over every
+// lane of v[i >> 2].  Lane bit 5 picks token bit 3, lane bit 4 token bit 2
+// (lane swaps), lane bits 3 and 2 token bits 1 and 0 (a row mirror and a
+// half-row mirror pair each lane with one whose bit differs); the four lanes
+// of a quad then hold partial sums of the same token and add up.
+__device__ __forceinline__ float reduce_tokens(float (&v)[16], int lane) {
+  lane_swap32x4(v[0], v[8], v[1], v[9], v[2], v[10], v[3], v[11]);
+  lane_swap32x4(v[4], v[12], v[5], v[13], v[6], v[14], v[7], v[15]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] += v[i + 8];
+  lane_swap16x4(v[0], v[4], v[1], v[5], v[2], v[6], v[3], v[7]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] += v[i + 4];
+  const bool b3 = lane & 8, b2 = lane & 4;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float x = b3 ? v[i + 2] : v[i], y = b3 ? v[i] : v[i + 2];
+    v[i] = x + dpp_mov<0x140>(y);   // row mirror
+  }
+  {
+    const float x = b2 ? v[1] : v[0], y = b2 ? v[0] : v[1];
+    v[0] = x + dpp_mov<0x141>(y);   // half-row mirror
+  }
+  float r = v[0] + dpp_mov<0xB1>(v[0]);   // quad_perm [1, 0, 3, 2]
+  return r + dpp_mov<0x4E>(r);            // quad_perm [2, 3, 0, 1]
+}
+
+__device__ __forceinline__ float wave_max_all(float v) { return group_max(row_max(v)); }
+__device__ __forceinline__ float wave_sum_all(float v) { return group_sum(row_sum(v)); }
+
+__device__ __forceinline__ float uniform(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+}  // namespace
+
+// grid: (n_splits, H * head_chunks, B); block: 256 (4 waves).
+template <int KB, int VB, int NH>
+__global__ void __launch_bounds__(kVThreads)
+decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int direct) {
+  __shared__ float red_s[kVWaves][NH][kVD];
+  __shared__ float stat_s[kVWaves][NH][2];
+
+  constexpr int KPW = 32 / KB;   // key tokens per code word
+  constexpr int KWH = KB / 2;    // key code words per channel and 16-token half
+  constexpr int VPW = 32 / VB;   // value channels per code word
+  constexpr int VWQ = VB;        // value code words per token and 32-channel quarter
+
+  const int lane = threadIdx.x & 63;
+  // wave-uniform, so that group indices and their branches stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int split = blockIdx.x;
+  const int h = blockIdx.y / head_chunks;
+  const int hc = blockIdx.y % head_chunks;
+  const int b = blockIdx.z;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int hq0 = h * a.n_rep + hc * NH;
+  const int qd = lane & 3;    // value channels 32 qd .. 32 qd + 31 (one value group)
+  const int tq = lane >> 2;   // token of each 16-token half this lane scores and accumulates
+
+  const int64_t s0 = (int64_t)split * tokens_per_split;
+  const int64_t s1 = min(s0 + (int64_t)tokens_per_split, a.t);
+  const int64_t g_end = (s1 + kVG - 1) / kVG;
+
+  // q of channels 2 lane, 2 lane + 1, times 1/sqrt(D)
+  float q0[NH], q1[NH];
+#pragma unroll
+  for (int j = 0; j < NH; ++j) {
+    const uint32_t qq = *(const uint32_t *)(a.q + ((int64_t)b * a.Hq + hq0 + j) * kVD + 2 * lane);
+    q0[j] = h2f((uint16_t)(qq & 0xFFFFu)) * a.sm_scale;
+    q1[j] = h2f((uint16_t)(qq >> 16)) * a.sm_scale;
+  }
+
+  float m[NH], lsum[NH], acc[NH][32], az[NH];
+#pragma unroll
+  for (int j = 0; j < NH; ++j) {
+    m[j] = -INFINITY;
+    lsum[j] = 0.0f;
+    az[j] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) acc[j][c] = 0.0f;
+  }
+
+  const int64_t kgroups = a.cap / kVG;
+  const uint32_t *kcodes = a.k_codes + bh * kgroups * (kVD * KB) + lane * (2 * KB);
+  const float *kscale = a.k_scale + bh * kgroups * kVD + 2 * lane;
+  const float *kzero = a.k_zero + bh * kgroups * kVD + 2 * lane;
+  const uint16_t *kres = a.k_res + bh * a.R * kVD + 2 * lane;
+  const uint32_t *vcodes = a.v_codes + bh * a.cap * (kVD * VB / 32) + qd * VWQ;
+  const float *vscale = a.v_scale + (bh * (kVD / kVG) + qd) * a.cap;
+  const float *vzero = a.v_zero + (bh * (kVD / kVG) + qd) * a.cap;
+  const uint16_t *vres = a.v_res + bh * a.R * kVD + qd * 32;
+
+  // The code, scale and zero words of a group (and the mask entries of the
+  // lane's tokens) are loaded one group ahead, so their latency overlaps the
+  // arithmetic of the group before.  The loads are unconditional: every
+  // group below g_end lies inside the capacity (the words of a window group
+  // are loaded and not used) and the mask index is clamped to the last token.
+  struct Raw {
+    uint32_t kw[2 * KB];
+    float2 ks, kz;
+    uint32_t vw[2][VWQ];
+    float vs[2], vz[2], mk[2];
+  };
+  auto fetch = [&](int64_t g, Raw &r) {
+    load_words<KB / 2>(kcodes + g * (kVD * KB), r.kw);
+    r.ks = *(const float2 *)(kscale + g * kVD);
+    r.kz = *(const float2 *)(kzero + g * kVD);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int64_t tau = g * kVG + 16 * hh + tq;
+      const uint32_t *src = vcodes + tau * (kVD * VB / 32);
+      if constexpr (VWQ == 4) {
+        const uint4 v = *(const uint4 *)src;
+        r.vw[hh][0] = v.x;
+        r.vw[hh][1] = v.y;
+        r.vw[hh][2] = v.z;
+        r.vw[hh][3] = v.w;
+      } else {
+        const uint2 v = *(const uint2 *)src;
+        r.vw[hh][0] = v.x;
+        r.vw[hh][1] = v.y;
+      }
+      r.vs[hh] = vscale[tau];
+      r.vz[hh] = vzero[tau];
+      r.mk[hh] = a.mask ? a.mask[(int64_t)b * a.t + min(tau, a.t - 1)] : 0.0f;
+    }
+  };
+
+  // one 32-token group: scores, online softmax update, value accumulation
+  auto process = [&](int64_t gi, const Raw &cur) __attribute__((always_inline)) {
+    const int64_t t0 = gi * kVG;
+    const bool quantized = t0 < a.n_kq;   // n_kq is a multiple of the group size
+    float qs0[NH], qs1[NH], qz[NH];
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+      qs0[j] = q0[j] * cur.ks.x;
+      qs1[j] = q1[j] * cur.ks.y;
+      qz[j] = fmaf(q1[j], cur.kz.y, q0[j] * cur.kz.x);
+    }
+    // fp16 key window: token tau sits in row tau mod R; R is a multiple of
+    // the group size, so the group's tokens sit in consecutive rows
+    const int row0 = quantized ? 0 : (int)((uint32_t)t0 % (uint32_t)a.R);
+
+    float sc[NH][2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      float part[NH][16];
+      if (quantized) {
+#pragma unroll
+        for (int j = 0; j < NH; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) part[j][e] = qz[j];
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch) {
+#pragma unroll
+          for (int wi = 0; wi < KWH; ++wi) {
+            float f[KPW];
+            unpack_word<KB>(cur.kw[ch * KB + hh * KWH + wi], f);
+#pragma unroll
+            for (int k = 0; k < KPW; ++k)
+#pragma unroll
+              for (int j = 0; j < NH; ++j)
+                part[j][wi * KPW + k] =
+                    fmaf(ch ? qs1[j] : qs0[j], f[k], part[j][wi * KPW + k]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t tau = t0 + 16 * hh + e;
+          // rows past the split end are inside the window array; their
+          // products are dropped
+          const uint32_t kk = *(const uint32_t *)(kres + (row0 + 16 * hh + e) * kVD);
+          const float k0 = tau < s1 ? h2f((uint16_t)(kk & 0xFFFFu)) : 0.0f;
+          const float k1 = tau < s1 ? h2f((uint16_t)(kk >> 16)) : 0.0f;
+#pragma unroll
+          for (int j = 0; j < NH; ++j) part[j][e] = fmaf(q1[j], k1, q0[j] * k0);
+        }
+      }
+      const bool valid = t0 + 16 * hh + tq < s1;
+#pragma unroll
+      for (int j = 0; j < NH; ++j) {
+        const float v = reduce_tokens(part[j], lane) + cur.mk[hh];
+        sc[j][hh] = valid ? v : -INFINITY;
+      }
+    }
+
+    // online softmax of this wave over the group's 32 tokens
+    float p[NH][2];
+#pragma unroll
+    for (int j = 0; j < NH; ++j) {
+      const float gmax = uniform(wave_max_all(fmaxf(sc[j][0], sc[j][1])));
+      if (gmax > m[j]) {
+        const float alpha = m[j] == -INFINITY ? 0.0f : __expf(m[j] - gmax);
+        lsum[j] *= alpha;
+        az[j] *= alpha;
+#pragma unroll
+        for (int c = 0; c < 32; ++c) acc[j][c] *= alpha;
+        m[j] = gmax;
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) p[j][hh] = m[j] == -INFINITY ? 0.0f : __expf(sc[j][hh] - m[j]);
+      lsum[j] += p[j][0] + p[j][1];
+    }
+
+    // values of token tq of each half, channels 32 qd .. 32 qd + 31
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int64_t tau = t0 + 16 * hh + tq;
+      if (tau < s1) {
+        if (tau < a.n_vq) {
+          float ps[NH];
+#pragma unroll
+          for (int j = 0; j < NH; ++j) {
+            ps[j] = p[j][hh] * cur.vs[hh];
+            az[j] = fmaf(p[j][hh], cur.vz[hh], az[j]);
+          }
+#pragma unroll
+          for (int wi = 0; wi < VWQ; ++wi) {
+            float f[VPW];
+            unpack_word<VB>(cur.vw[hh][wi], f);
+#pragma unroll
+            for (int k = 0; k < VPW; ++k)
+#pragma unroll
+              for (int j = 0; j < NH; ++j)
+                acc[j][wi * VPW + k] = fmaf(ps[j], f[k], acc[j][wi * VPW + k]);
+          }
+        } else {
+          const uint16_t *row = vres + ((uint32_t)tau % (uint32_t)a.R) * kVD;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint4 v = *(const uint4 *)(row + 8 * i);
+            const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const float x0 = h2f((uint16_t)(vv[k] & 0xFFFFu));
+              const float x1 = h2f((uint16_t)(vv[k] >> 16));
+#pragma unroll
+              for (int j = 0; j < NH; ++j) {
+                acc[j][8 * i + 2 * k] = fmaf(p[j][hh], x0, acc[j][8 * i + 2 * k]);
+                acc[j][8 * i + 2 * k + 1] = fmaf(p[j][hh], x1, acc[j][8 * i + 2 * k + 1]);
+              }
+            }
+          }
+        }
+      }
+    }
+  };
+
+  // two register sets alternate as the current group and the one ahead
+  const int64_t g_first = s0 / kVG + wave;
+  Raw ra, rb;
+  if (g_first < g_end) fetch(g_first, ra);
+  for (int64_t gi = g_first; gi < g_end;) {
+    fetch(min(gi + kVWaves, g_end - 1), rb);
+    process(gi, ra);
+    gi += kVWaves;
+    if (gi >= g_end) break;
+    fetch(min(gi + kVWaves, g_end - 1), ra);
+    process(gi, rb);
+    gi += kVWaves;
+  }
+
+  // Per wave: fold in the zero-point sum, then sum acc over the 16 token
+  // lanes of each channel quarter (lane bits 5..2).  Bits 5 and 4 scatter
+  // the 32 channels (lane swaps); bits 3 and 2 are summed whole (rotations
+  // by 4 and 8 within a row), leaving channels 32 qd + 16 b5 + 8 b4 + i
+  // (i < 8) in the four lanes of that (b5, b4, qd).
+#pragma unroll
+  for (int j = 0; j < NH; ++j) {
+    float *v = acc[j];
+#pragma unroll
+    for (int c = 0; c < 32; ++c) v[c] += az[j];
+#pragma unroll
+    for (int i = 0; i < 16; i += 4)
+      lane_swap32x4(v[i], v[i + 16], v[i + 1], v[i + 17], v[i + 2], v[i + 18], v[i + 3], v[i + 19]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] += v[i + 16];
+    lane_swap16x4(v[0], v[8], v[1], v[9], v[2], v[10], v[3], v[11]);
+    lane_swap16x4(v[4], v[12], v[5], v[13], v[6], v[14], v[7], v[15]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float x = v[i] + v[i + 8];
+      x += dpp_mov<0x124>(x);
+      x += dpp_mov<0x128>(x);
+      v[i] = x;
+    }
+    // lane bits 3..2 pick which two of the eight sums this lane stores
+    const int base = 32 * qd + 16 * ((lane >> 5) & 1) + 8 * ((lane >> 4) & 1);
+    const int k = (lane >> 2) & 3;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((i >> 1) == k) red_s[wave][j][base + i] = v[i];
+    const float l_w = wave_sum_all(lsum[j]) * 0.25f;   // every token sits in four lanes
+    if (lane == 0) {
+      stat_s[wave][j][0] = m[j];
+      stat_s[wave][j][1] = l_w;
+    }
+  }
+  __syncthreads();
+
+  // merge the four waves and write the partial (acc, m, l) of this split
+  for (int i = threadIdx.x; i < NH * kVD; i += kVThreads) {
+    const int j = i / kVD, c = i % kVD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kVWaves; ++w) M = fmaxf(M, stat_s[w][j][0]);
+    float o = 0.0f, L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kVWaves; ++w) {
+      const float mw = stat_s[w][j][0];
+      const float f = mw == -INFINITY ? 0.0f : __expf(mw - M);
+      o = fmaf(red_s[w][j][c], f, o);
+      L = fmaf(stat_s[w][j][1], f, L);
+    }
+    if (direct) {
+      // a single split: this is the whole softmax, normalized here
+      a.out[((int64_t)b * a.Hq + hq0 + j) * kVD + c] = o * (L > 0.0f ? 1.0f / L : 0.0f);
+    } else {
+      float *dst =
+          a.part + (((int64_t)b * a.Hq + hq0 + j) * a.S_total + split) * (int64_t)(kVD + 4);
+      dst[c] = o;
+      if (c == 0) {
+        dst[kVD] = M;
+        dst[kVD + 1] = L;
+      }
+    }
+  }
+}
+
+bool decode_vector_supported(const DecodeArgs &a) {
+  // 16-byte code loads: the slab offsets are multiples of 16 bytes when the
+  // arrays are; q is read 4 bytes at a time
+  const bool aligned = ((uintptr_t)a.k_codes & 15) == 0 && ((uintptr_t)a.v_codes & 15) == 0 &&
+                       ((uintptr_t)a.v_res & 15) == 0 && ((uintptr_t)a.k_res & 3) == 0 &&
+                       ((uintptr_t)a.k_scale & 7) == 0 &&
+                       ((uintptr_t)a.k_zero & 7) == 0 && ((uintptr_t)a.q & 3) == 0;
+  return a.D == kVD && a.G == kVG && (a.kb == 2 || a.kb == 4) && (a.vb == 2 || a.vb == 4) &&
+         (a.n_rep == 1 || a.n_rep == 2) && a.R % kVG == 0 && a.cap % kVG == 0 &&
+         a.cap < ((int64_t)1 << 31) && aligned;
+}
+
+template <int KB, int VB>
+static void launch_bits(const DecodeArgs &a, dim3 grid, int tps, int direct, hipStream_t s) {
+  if (a.n_rep == 1)
+    hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 1>), grid, dim3(kVThreads), 0, s, a, tps, 1,
+                       direct);
+  else
+    hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 2>), grid, dim3(kVThreads), 0, s, a, tps, 1,
+                       direct);
+}
+
+// With a single split (n_splits == 1) the kernel writes the normalized
+// output itself and no combine pass is needed; otherwise it writes one
+// partial per split.
+hipError_t launch_decode_vector(const DecodeArgs &a, int tokens_per_split, int n_splits,
+                                hipStream_t s) {
+  if (n_splits <= 0) return hipSuccess;
+  if (!decode_vector_supported(a) || tokens_per_split % kVG != 0) return hipErrorInvalidValue;
+  dim3 grid((unsigned)n_splits, (unsigned)a.H, (unsigned)a.B);
+  const int direct = n_splits == 1;
+  if (a.kb == 2 && a.vb == 2)
+    launch_bits<2, 2>(a, grid, tokens_per_split, direct, s);
+  else if (a.kb == 2)
+    launch_bits<2, 4>(a, grid, tokens_per_split, direct, s);
+  else if (a.vb == 2)
+    launch_bits<4, 2>(a, grid, tokens_per_split, direct, s);
+  else
+    launch_bits<4, 4>(a, grid, tokens_per_split, direct, s);
+  return hipGetLastError();
+}
+
+}  // namespace kivi

@@ -79,6 +79,10 @@ hipError_t launch_decode_generic(const DecodeArgs &a, int64_t tok_begin, int tok
 
 // Matrix-core kernel for 2-bit caches with G = 32, D = 128 and 1, 2 or 4
 // query heads per KV head.  Returns hipErrorInvalidValue for other shapes.
+bool decode_vector_supported(const DecodeArgs &a);
+hipError_t launch_decode_vector(const DecodeArgs &a, int tokens_per_split, int n_splits,
+                                hipStream_t s);
+
 bool decode_matrix_supported(const DecodeArgs &a);
 // Window chunks (32 tokens each) that cover tokens [n_main, t).
 int decode_matrix_window_chunks(const DecodeArgs &a, int64_t n_main);

@@ -20,7 +20,7 @@ KIVI_ERR_INVALID_ARG = -1
 KIVI_ERR_CAPACITY = -2
 KIVI_ERR_WORKSPACE = -3
 KIVI_ERR_HIP = -4
-KIVI_PATH_AUTO, KIVI_PATH_GENERIC, KIVI_PATH_MATRIX = 0, 1, 2
+KIVI_PATH_AUTO, KIVI_PATH_GENERIC, KIVI_PATH_MATRIX, KIVI_PATH_VECTOR = 0, 1, 2, 3
 
 EXPORTED = ("kivi_pack_keys", "kivi_pack_values", "kivi_append", "kivi_decode_attn",
             "kivi_decode_attn_ex", "kivi_decode_attn_workspace_bytes",

@@ -153,11 +153,17 @@ int kivi_decode_attn(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads,
 
 /* Same as kivi_decode_attn with explicit tuning, for tests and sweeps:
  *   tokens_per_split  0 = automatic, else a positive multiple of 64.
- *   path              KIVI_PATH_AUTO, KIVI_PATH_GENERIC (scalar kernel for
- *                     every token) or KIVI_PATH_MATRIX (matrix-core kernel
- *                     where the shape allows; rejected where it does not).
+ *   path              KIVI_PATH_AUTO (the matrix-core kernel where the shape
+ *                     allows, else the vector kernel where it allows, else
+ *                     the scalar kernel), KIVI_PATH_GENERIC (scalar kernel
+ *                     for every token), KIVI_PATH_MATRIX (matrix-core
+ *                     kernel: 2-bit codes, head_dim 128, G 32, 1, 2 or 4
+ *                     query heads per KV head) or KIVI_PATH_VECTOR (vector
+ *                     kernel: 2- or 4-bit codes, head_dim 128, G 32, R a
+ *                     multiple of 32, 1 or 2 query heads per KV head).  A
+ *                     forced path the shape does not allow is rejected.
  * The workspace must hold kivi_decode_attn_workspace_bytes_ex() bytes. */
-enum { KIVI_PATH_AUTO = 0, KIVI_PATH_GENERIC = 1, KIVI_PATH_MATRIX = 2 };
+enum { KIVI_PATH_AUTO = 0, KIVI_PATH_GENERIC = 1, KIVI_PATH_MATRIX = 2, KIVI_PATH_VECTOR = 3 };
 int kivi_decode_attn_ex(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads,
                         const float *mask, float *out, void *workspace,
                         size_t workspace_bytes, int32_t tokens_per_split,

@@ -16,7 +16,17 @@ pytestmark = [pytest.mark.gpu,
 PATHS = [kivi.KIVI_PATH_AUTO, kivi.KIVI_PATH_GENERIC]
 
 
-def _run_workload(w, slabs, paths=PATHS):
+def vector_ok(D, kb, vb, G, R, rep, cap):
+    """Shapes the vector kernel takes (the ABI rejects it elsewhere)."""
+    return (D == 128 and G == 32 and kb in (2, 4) and vb in (2, 4) and rep in (1, 2)
+            and R % 32 == 0 and cap % 32 == 0)
+
+
+def paths_for(D, kb, vb, G, R, rep, cap):
+    return PATHS + ([kivi.KIVI_PATH_VECTOR] if vector_ok(D, kb, vb, G, R, rep, cap) else [])
+
+
+def _run_workload(w, slabs, paths=None):
     """Prefill + one decode step of workload w on the GPU; the oracle rebuilds
     the sampled (batch, kv head) slabs alone and checks them."""
     inp = synth.make_inputs(w)
@@ -25,8 +35,10 @@ def _run_workload(w, slabs, paths=PATHS):
     kivi.kivi_append(g, dev(inp["k0"]), dev(inp["v0"]))
     kivi.kivi_append(g, dev(inp["k_steps"][0]), dev(inp["v_steps"][0]))
     q = inp["q_steps"][0]
-    outs = {p: host(kivi.kivi_decode_attn(g, dev(q), path=p)) for p in paths}
     rep = w.Hq // w.Hkv
+    if paths is None:
+        paths = paths_for(w.D, w.k_bits, w.v_bits, w.G, w.R, rep, w.capacity)
+    outs = {p: host(kivi.kivi_decode_attn(g, dev(q), path=p)) for p in paths}
     for b, h in slabs:
         o = oracle.Cache(1, 1, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
         o.append(b16(inp["k0"][b:b + 1, h:h + 1]), b16(inp["v0"][b:b + 1, h:h + 1]))
@@ -77,7 +89,7 @@ def test_lengths_around_boundaries(t, rep):
     rng = np.random.default_rng(t * 10 + rep)
     g, o, q = _small_case(rng, 2, 2, rep, 128, 2, 2, 32, 64, t)
     ref = o.decode_attn(b16(q))
-    for p in PATHS:
+    for p in paths_for(128, 2, 2, 32, 64, rep, g.cap):
         out = host(kivi.kivi_decode_attn(g, dev(q), path=p))
         assert_close(out, ref, f"t={t} rep={rep} path={p}")
 
@@ -88,7 +100,7 @@ def test_head_groups_and_bits(rep, kb, vb):
     rng = np.random.default_rng(rep * 7 + kb + 3 * vb)
     g, o, q = _small_case(rng, 2, 2, rep, 128, kb, vb, 32, 128, 777)
     ref = o.decode_attn(b16(q))
-    for p in PATHS:
+    for p in paths_for(128, kb, vb, 32, 128, rep, g.cap):
         assert_close(host(kivi.kivi_decode_attn(g, dev(q), path=p)), ref, f"rep={rep} kb={kb} vb={vb}")
 
 
@@ -100,14 +112,15 @@ def test_head_dims_and_groups(D, G):
     assert_close(host(kivi.kivi_decode_attn(g, dev(q))), ref, f"D={D} G={G}")
 
 
-def test_mask():
-    rng = np.random.default_rng(8)
-    g, o, q = _small_case(rng, 2, 2, 4, 128, 2, 2, 32, 128, 900)
+@pytest.mark.parametrize("rep,kb,vb", [(4, 2, 2), (2, 4, 4), (1, 4, 2)])
+def test_mask(rep, kb, vb):
+    rng = np.random.default_rng(8 + rep)
+    g, o, q = _small_case(rng, 2, 2, rep, 128, kb, vb, 32, 128, 900)
     t = g.n_tokens
     m = np.where(rng.random((2, t)) < 0.3, -np.inf, rng.standard_normal((2, t))).astype(np.float32)
     m[1, :] = -np.inf                      # a fully masked batch row
     ref = o.decode_attn(b16(q), m)
-    for p in PATHS:
+    for p in paths_for(128, kb, vb, 32, 128, rep, g.cap):
         out = host(kivi.kivi_decode_attn(g, dev(q), mask=dev(m), path=p))
         assert not np.isnan(out).any() and not out[1].any()
         assert_close(out, ref, f"mask path={p}")
@@ -119,14 +132,16 @@ def test_mask():
 # largest, keeping about 16 bits below it (measured on gfx950), so a different
 # split of the tokens changes the rounding of the matrix kernel at ~1e-4.
 SPLIT_TOL = {kivi.KIVI_PATH_GENERIC: dict(atol=2e-5, rtol=1e-5),
+             kivi.KIVI_PATH_VECTOR: dict(atol=2e-5, rtol=1e-5),
              kivi.KIVI_PATH_AUTO: dict(atol=2e-4, rtol=1e-3)}
 
 
-def test_split_invariance():
+@pytest.mark.parametrize("rep,kb,vb", [(4, 2, 2), (1, 4, 4), (2, 2, 4)])
+def test_split_invariance(rep, kb, vb):
     """Different split counts agree to within rounding (P12)."""
-    rng = np.random.default_rng(12)
-    g, o, q = _small_case(rng, 1, 2, 4, 128, 2, 2, 32, 128, 5000)
-    for p in PATHS:
+    rng = np.random.default_rng(12 + rep)
+    g, o, q = _small_case(rng, 1, 2, rep, 128, kb, vb, 32, 128, 5000)
+    for p in paths_for(128, kb, vb, 32, 128, rep, g.cap):
         base = host(kivi.kivi_decode_attn(g, dev(q), path=p))
         for tps in (64, 256, 1024, 4096):
             out = host(kivi.kivi_decode_attn(g, dev(q), tokens_per_split=tps, path=p))
@@ -167,17 +182,18 @@ def test_grid_exact_inputs_match_dense_attention():
     g = kivi.Cache(B, H, D, 2, 2, G, R, t + R)
     kivi.kivi_append(g, dev(K), dev(V[:, :, :n_kq]))
     ref = dense_attention(q.astype(np.float32), K.astype(np.float32), V[:, :, :n_kq].astype(np.float32))
-    for p in PATHS:
+    for p in paths_for(D, 2, 2, G, R, rep, t + R):
         assert_close(host(kivi.kivi_decode_attn(g, dev(q), path=p)), ref, f"grid path={p}")
 
 
 @pytest.mark.parametrize("kscale,vscale", [(1e-3, 1.0), (40.0, 1.0), (1.0, 1e-3), (1.0, 300.0),
                                            (200.0, 50.0)])
-def test_value_ranges(kscale, vscale):
-    """Key/value magnitudes far from N(0, 1): both kernels stay within the
+@pytest.mark.parametrize("rep", [4, 2])
+def test_value_ranges(kscale, vscale, rep):
+    """Key/value magnitudes far from N(0, 1): every kernel stays within the
     tolerance (the matrix kernel rescales its fp16 operands per block)."""
-    rng = np.random.default_rng(int(kscale * 7 + vscale * 3))
-    B, H, rep, D, t = 1, 2, 4, 128, 3000
+    rng = np.random.default_rng(int(kscale * 7 + vscale * 3) + rep)
+    B, H, D, t = 1, 2, 128, 3000
     K = (rng.standard_normal((B, H, t, D)) * kscale).astype(np.float16)
     V = (rng.standard_normal((B, H, t, D)) * vscale).astype(np.float16)
     q = rng.standard_normal((B, H * rep, D)).astype(np.float16)
@@ -186,7 +202,7 @@ def test_value_ranges(kscale, vscale):
     kivi.kivi_append(g, dev(K), dev(V))
     o.append(b16(K), b16(V))
     ref = o.decode_attn(b16(q))
-    for p in PATHS:
+    for p in paths_for(D, 2, 2, 32, 128, rep, 3072):
         out = host(kivi.kivi_decode_attn(g, dev(q), path=p))
         assert_close(out, ref, f"kscale={kscale} vscale={vscale} path={p}",
                      value_scale=max(1.0, vscale))
@@ -200,3 +216,26 @@ def test_matrix_and_scalar_paths_agree_closely():
         a = host(kivi.kivi_decode_attn(g, dev(q), path=kivi.KIVI_PATH_MATRIX))
         s = host(kivi.kivi_decode_attn(g, dev(q), path=kivi.KIVI_PATH_GENERIC))
         np.testing.assert_allclose(a, s, atol=5e-4, rtol=1e-3)
+
+
+@pytest.mark.parametrize("kb,vb", [(2, 2), (4, 4), (2, 4), (4, 2)])
+def test_vector_and_scalar_paths_agree_closely(kb, vb):
+    """The vector kernel (fp32 throughout; scores as sum (q s) code + q z, a
+    different rounding order) stays within 2e-4 of the scalar kernel, ten
+    times inside the oracle tolerance, over many splits and a ragged window."""
+    rng = np.random.default_rng(41 + kb + 3 * vb)
+    for rep, t in ((1, 4001), (2, 2500)):
+        g, o, q = _small_case(rng, 2, 3, rep, 128, kb, vb, 32, 128, t)
+        for tps in (0, 64, 192, 8192):   # 8192: one split, output written directly
+            v = host(kivi.kivi_decode_attn(g, dev(q), tokens_per_split=tps,
+                                           path=kivi.KIVI_PATH_VECTOR))
+            s = host(kivi.kivi_decode_attn(g, dev(q), tokens_per_split=tps,
+                                           path=kivi.KIVI_PATH_GENERIC))
+            np.testing.assert_allclose(v, s, atol=2e-4, rtol=1e-3, err_msg=f"rep={rep} tps={tps}")
+
+
+def test_vector_path_rejects_other_shapes():
+    rng = np.random.default_rng(5)
+    g, _, q = _small_case(rng, 1, 2, 4, 128, 2, 2, 32, 128, 300)
+    with pytest.raises(kivi.KiviError):
+        kivi.kivi_decode_attn(g, dev(q), path=kivi.KIVI_PATH_VECTOR)
