@@ -260,11 +260,6 @@ __device__ __forceinline__ void split_mul2(float x0, float y0, float x1, float y
   lo[k + 1] = (_Float16)__builtin_fmaf(x1, y1, -(float)h[1]);
 }
 
-__device__ __forceinline__ float max8(f4 a, f4 b) {
-  return fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])),
-               fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])));
-}
-
 }  // namespace
 
 // LDS of the kernel.  Separate objects, so the compiler can tell that LDS
@@ -346,25 +341,33 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
       qa[ks][2 * j + 1] = h2f((uint16_t)(ww[j] >> 16));
     }
   }
-  // The key A operand is q * s_k * 2^ek, with ek kept so that the largest |q|
-  // times the block's largest key scale stays below 2^14 (no fp16 overflow,
-  // and small products stay clear of the fp16 subnormal range); qa carries
-  // the current 2^ek.
+  // The key A operand is q * s_k * 2^ek with one exponent ek for the whole
+  // workgroup.  A key scale is (max - min) / 3 of fp16 values, so it is below
+  // 2^16; with max |q| < 2^e, every product q s 2^ek stays below 2^14 for
+  // ek = -2 - e, whatever the block -- no fp16 overflow for any fp16 input.
+  // Products small enough to fall into the fp16 subnormal range keep an
+  // absolute error below 2^-25 2^-ek, far under the attention tolerance.
   float qmax = 0.0f;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
     for (int j = 0; j < 8; ++j) qmax = fmaxf(qmax, fabsf(qa[ks][j]));
   qmax = group_max(row_max(qmax));
-  int ek_run = 0;
+  const int ek = __builtin_amdgcn_readfirstlane(-2 - __builtin_amdgcn_frexp_expf(qmax));
+  {
+    const float f = __builtin_amdgcn_ldexpf(1.0f, ek);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qa[ks][j] *= f;
+  }
 
   const float LOG2E = 1.4426950408889634f;
   const float c_bias = a.sm_scale * LOG2E;    // scores in log2 units
 
-  // The value A operand is p * s_v * 2^ev, ev set per block from the block's
-  // largest value scale (p <= 1), for the same reasons.  zt (sum p z) stays
-  // in plain units.
-  int ev_run = 0;
+  // The value A operand is p * s_v, unscaled: p <= 1 and a value scale of
+  // fp16 values is below 2^16, so it never overflows fp16.  zt (sum p z)
+  // stays in fp32.
   float m_run = -INFINITY;     // running max (log2 units), head h_s
   float l_run = 0.0f;          // this lane's share of the running sum
   float zt = 0.0f;             // sum p z, value A row (h_v, c_v)
@@ -393,22 +396,6 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
         mk[g][1] = m2.y * LOG2E;
       } else {
         mk[g][0] = mk[g][1] = 0.0f;
-      }
-    }
-    {
-      // the row maximum does not depend on the rotation
-      float mx = max8(*(const f4 *)(kst.ks + lane * 8), *(const f4 *)(kst.ks + lane * 8 + 4));
-      mx = group_max(row_max(mx));
-      const float prod = mx * qmax;
-      int ek = prod > 0.0f ? 14 - __builtin_amdgcn_frexp_expf(prod) : ek_run;
-      ek = __builtin_amdgcn_readfirstlane(ek);
-      if (ek != ek_run) {
-        const float f = __builtin_amdgcn_ldexpf(1.0f, ek - ek_run);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) qa[ks][j] *= f;
-        ek_run = ek;
       }
     }
     // A = hi/lo(q s) for rows (h_a, g_a); bias = q . z
@@ -462,7 +449,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
     // scores (even / odd token of each pair) and online softmax, head h_s
     if (k_valid) {
       const f4 bz4 = *(const f4 *)(L.bias + 4 * kg);
-      const float cs = c_bias * __builtin_amdgcn_ldexpf(1.0f, -ek_run);   // undo 2^ek
+      const float cs = c_bias * __builtin_amdgcn_ldexpf(1.0f, -ek);   // undo 2^ek
       float s2[4][2];
       float bmax = -INFINITY;
 #pragma unroll
@@ -500,19 +487,9 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
 #pragma unroll
       for (int g = 0; g < 4; ++g)
         xv[4 * u + g] = tr4(vst.vc + (32 * kg + 16 * u + i) * 8 + g * 2);
-    int ev;
     {
-      float mx = max8(*(const f4 *)(vst.vs + lane * 8), *(const f4 *)(vst.vs + lane * 8 + 4));
-      mx = group_max(row_max(mx));
-      // mx < 2^e with e the frexp exponent; p <= 1, so p * s * 2^(14 - e) < 2^14
-      ev = mx > 0.0f ? 14 - __builtin_amdgcn_frexp_expf(mx) : 0;
-      ev = __builtin_amdgcn_readfirstlane(ev);
-    }
-    {
-      // accumulators in units of 2^ev_run move to 2^ev
-      const float rescale = __builtin_amdgcn_ldexpf(1.0f, ev - ev_run);
-      ev_run = ev;
-      const float av = (v_valid ? L.alpha[kg] : 1.0f) * rescale;
+      // accumulators follow the running maximum
+      const float av = v_valid ? L.alpha[kg] : 1.0f;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         dv[g][0][g] *= av;
@@ -520,7 +497,6 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
       }
       zt *= L.alpha[h_v];
     }
-    const float sc_e = __builtin_amdgcn_ldexpf(1.0f, ev);
     h8 vh[2][2], vl[2][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -538,7 +514,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
         const float zv[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
 #pragma unroll
         for (int j = 0; j < 8; j += 2) {
-          split_mul2(pv[j], sv[j] * sc_e, pv[j + 1], sv[j + 1] * sc_e, vh[u][d], vl[u][d], j);
+          split_mul2(pv[j], sv[j], pv[j + 1], sv[j + 1], vh[u][d], vl[u][d], j);
           zt = fmaf(pv[j], zv[j], zt);
           zt = fmaf(pv[j + 1], zv[j + 1], zt);
         }
@@ -577,11 +553,10 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
   if (v_valid) {
     const f4 z4 = *(const f4 *)(L.bias + 4 * kg);
     float *dst = a.part + (((int64_t)b * a.Hq + hk * NREP + kg) * a.S_total + split) * slot_stride;
-    const float unit = __builtin_amdgcn_ldexpf(1.0f, -ev_run);      // undo 2^ev
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       *(float2 *)(dst + 32 * g + 2 * i) =
-          make_float2(fmaf(dv[g][0][g], unit, z4[g]), fmaf(dv[g][1][g], unit, z4[g]));
+          make_float2(dv[g][0][g] + z4[g], dv[g][1][g] + z4[g]);
     }
   }
   if (k_valid && i == 0) {
