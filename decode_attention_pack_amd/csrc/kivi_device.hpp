@@ -48,4 +48,19 @@ __device__ __forceinline__ uint32_t quant_code(float x, float z, float s, int bi
   return (uint32_t)r;
 }
 
+// The same code as quant_code, with the division done once per group: r is
+// v_rcp_f32(s) (relative error <= 2^-23).  q = (x - z) * r then lies within
+// |(x - z) / s| * 2^-21.5 < 1e-5 of the correctly rounded quotient (codes are
+// at most 15), so both round to the same integer unless q is within 1e-5 of
+// a half-integer; those rare elements take the exact IEEE division.
+__device__ __forceinline__ uint32_t quant_code_r(float x, float z, float s, float r, int bits) {
+  if (s == 0.0f) return 0u;
+  const float u = x - z;
+  float q = rintf(u * r);
+  if (fabsf(u * r - q) > 0.49999f) q = rintf(u / s);
+  const float qmax = (float)((1 << bits) - 1);
+  q = fminf(fmaxf(q, 0.0f), qmax);
+  return (uint32_t)q;
+}
+
 }  // namespace kivi

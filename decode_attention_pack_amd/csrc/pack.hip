@@ -104,10 +104,10 @@ write_window_kernel(const uint16_t *__restrict__ k_new, const uint16_t *__restri
 // (codes of one channel are contiguous, so the stores coalesce across threads).
 // grid: (n_groups, BH); block: D threads (D a multiple of 64, G * D * 2 bytes
 // of LDS).
-template <int G, int D>
+template <int G, int D, int BITS>
 __global__ void __launch_bounds__(D)
-key_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t g_first, int bits,
-                 int64_t cap, uint32_t *__restrict__ codes, float *__restrict__ scale,
+key_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t g_first, int64_t cap,
+                 uint32_t *__restrict__ codes, float *__restrict__ scale,
                  float *__restrict__ zero) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[G][D];
   const int64_t bh = blockIdx.y;
@@ -118,22 +118,26 @@ key_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t g_first, 
     *(uint4 *)(&tile[0][0] + i * 8) = *(const uint4 *)(src + i * 8);
   __syncthreads();
   const int c = threadIdx.x;
-  float mn = h2f(tile[0][c]), mx = mn;
+  float v[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) v[i] = h2f(tile[i][c]);
+  float mn = v[0], mx = v[0];
 #pragma unroll
   for (int i = 1; i < G; ++i) {
-    const float v = h2f(tile[i][c]);
-    mn = fminf(mn, v);
-    mx = fmaxf(mx, v);
+    mn = fminf(mn, v[i]);
+    mx = fmaxf(mx, v[i]);
   }
-  const float s = group_scale(mn, mx, bits);
-  const int per = 32 / bits;
-  const int words = G / per;
+  const float s = group_scale(mn, mx, BITS);
+  const float r = __builtin_amdgcn_rcpf(s);
+  constexpr int per = 32 / BITS;
+  constexpr int words = G / per;
   const int64_t sz = (bh * (cap / G) + g_first + g) * D + c;
   uint32_t *dst = codes + sz * words;
+#pragma unroll
   for (int w = 0; w < words; ++w) {
     uint32_t word = 0;
-    for (int e = 0; e < per; ++e)
-      word |= quant_code(h2f(tile[w * per + e][c]), mn, s, bits) << (bits * e);
+#pragma unroll
+    for (int e = 0; e < per; ++e) word |= quant_code_r(v[w * per + e], mn, s, r, BITS) << (BITS * e);
     dst[w] = word;
   }
   scale[sz] = s;
@@ -146,10 +150,10 @@ key_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t g_first, 
 // packs its G channels, so for each group the 64 scales / zeros of the tile
 // are one contiguous store, and the code words of the tile form one
 // contiguous run.  grid: (ceil(n_rows / 64), BH); block: 256.
-template <int D, int G>
+template <int D, int G, int BITS>
 __global__ void __launch_bounds__(256)
 value_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t n_rows,
-                   int64_t tau_first, int bits, int64_t cap, uint32_t *__restrict__ codes,
+                   int64_t tau_first, int64_t cap, uint32_t *__restrict__ codes,
                    float *__restrict__ scale, float *__restrict__ zero) {
   constexpr int kRow = D + 8;                       // halves per LDS row (16-byte pad)
   __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kRow];
@@ -165,29 +169,34 @@ value_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t n_rows,
   }
   __syncthreads();
   const int t = threadIdx.x & 63;
-  const int per = 32 / bits;
+  if (t >= rows) return;
+  constexpr int per = 32 / BITS;
   constexpr int n_groups = D / G;
   for (int g = threadIdx.x >> 6; g < n_groups; g += 4) {
-    if (t >= rows) continue;
     // the group's G channels, 8 per 16-byte LDS read
     uint16_t v16[G];
 #pragma unroll
     for (int k = 0; k < G / 8; ++k)
       *(uint4 *)(v16 + 8 * k) = *(const uint4 *)(tile + t * kRow + g * G + 8 * k);
-    float mn = h2f(v16[0]), mx = mn;
+    float v[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) v[i] = h2f(v16[i]);
+    float mn = v[0], mx = v[0];
 #pragma unroll
     for (int i = 1; i < G; ++i) {
-      const float v = h2f(v16[i]);
-      mn = fminf(mn, v);
-      mx = fmaxf(mx, v);
+      mn = fminf(mn, v[i]);
+      mx = fmaxf(mx, v[i]);
     }
-    const float s = group_scale(mn, mx, bits);
+    const float s = group_scale(mn, mx, BITS);
+    const float r = __builtin_amdgcn_rcpf(s);
     const int64_t tau = tau_first + r0 + t;
     uint32_t *dst = codes + (bh * cap + tau) * (int64_t)(D / per) + (g * G) / per;
+#pragma unroll
     for (int w = 0; w < G / per; ++w) {
       uint32_t word = 0;
+#pragma unroll
       for (int e = 0; e < per; ++e)
-        word |= quant_code(h2f(v16[w * per + e]), mn, s, bits) << (bits * e);
+        word |= quant_code_r(v[w * per + e], mn, s, r, BITS) << (BITS * e);
       dst[w] = word;
     }
     const int64_t sz = (bh * n_groups + g) * cap + tau;
@@ -214,8 +223,12 @@ hipError_t launch_key_tiles(const uint16_t *x, int64_t T_in, int64_t n_rows, int
   dim3 grid((unsigned)n_groups, (unsigned)BH);
 #define KIVI_KT(GG, DD)                                                                        \
   if (G == GG && D == DD) {                                                                     \
-    hipLaunchKernelGGL((key_tiles_kernel<GG, DD>), grid, dim3(DD), 0, s, x, T_in, g_first,    \
-                       bits, cap, codes, scale, zero);                                          \
+    if (bits == 2)                                                                              \
+      hipLaunchKernelGGL((key_tiles_kernel<GG, DD, 2>), grid, dim3(DD), 0, s, x, T_in,        \
+                         g_first, cap, codes, scale, zero);                                     \
+    else                                                                                        \
+      hipLaunchKernelGGL((key_tiles_kernel<GG, DD, 4>), grid, dim3(DD), 0, s, x, T_in,        \
+                         g_first, cap, codes, scale, zero);                                     \
     return hipGetLastError();                                                                   \
   }
   KIVI_KT(16, 64) KIVI_KT(32, 64) KIVI_KT(64, 64)
@@ -233,8 +246,12 @@ hipError_t launch_value_tokens(const uint16_t *x, int64_t T_in, int64_t n_rows, 
   dim3 grid((unsigned)((n_rows + 63) / 64), (unsigned)BH);
 #define KIVI_VT(DD, GG)                                                                         \
   if (D == DD && G == GG) {                                                                     \
-    hipLaunchKernelGGL((value_tiles_kernel<DD, GG>), grid, dim3(256), 0, s, x, T_in, n_rows,    \
-                       tau_first, bits, cap, codes, scale, zero);                               \
+    if (bits == 2)                                                                              \
+      hipLaunchKernelGGL((value_tiles_kernel<DD, GG, 2>), grid, dim3(256), 0, s, x, T_in,      \
+                         n_rows, tau_first, cap, codes, scale, zero);                           \
+    else                                                                                        \
+      hipLaunchKernelGGL((value_tiles_kernel<DD, GG, 4>), grid, dim3(256), 0, s, x, T_in,      \
+                         n_rows, tau_first, cap, codes, scale, zero);                           \
     return hipGetLastError();                                                                   \
   }
   KIVI_VT(64, 16) KIVI_VT(64, 32) KIVI_VT(64, 64)

@@ -79,6 +79,11 @@ def _edge_tensor(rng, T, D):
     x[0, 0, :, 2] = rng.choice([-65504.0, 65504.0, 6e-8, -6e-8], T)  # extremes
     x[0, 0, 5, :] = np.linspace(-2, 2, D)
     x[0, 0, :, 3] = rng.standard_normal(T) * 1e-6        # subnormal-scale group
+    # exact ties for 4-bit codes ((x - min) / s = k + 1/2 with s = 1): along
+    # tokens for a key group, along channels for value groups
+    x[0, 0, :, 4] = np.tile([0.0, 15.0, 0.5, 7.5, 14.5, 3.5, 1.0, 2.5], T // 8)
+    x[0, 0, 7, :] = np.tile([0.0, 15.0, 0.5, 7.5, 14.5, 3.5, 1.0, 2.5], D // 8)
+    x[0, 0, 9, :] = np.tile([0.0, 3.0, 0.5, 1.5, 2.5, 1.0, 2.0, 0.25], D // 8)
     return x.astype(np.float16)
 
 
