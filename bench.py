@@ -3,17 +3,20 @@ packed cache) on one MI355X, reported as achieved HBM GB/s and us/step.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
 
-A step appends one token to the cache of one layer and runs kivi_decode_attn
-over it.  Steps rotate over L layer replicas (L x footprint >= 1 GiB) so the
-256 MB Infinity Cache cannot serve the working set; inputs are resident in HBM
-before the timed region starts.  `value` is the algorithmic bytes a step must
-move (packed codes + fp32 scale/zero + fp16 window + q + out, plus the
-append's bytes) divided by the measured step time (HIP events at the two
-ends of the K timed steps).  `roofline` covers the attention launch alone (its
-split kernel and combine): a second timed loop issues K attention calls back
-to back over the same replicas, with HIP events on the stream the library
-launches on around rounds of calls, and divides by the call count.  `cpu_baseline` times the CPU oracle on
-a bounded sample of (batch, KV head) slabs of the same workload.
+A step appends one token to the cache of one layer and attends over it with
+kivi_decode_step, which runs the append inside the attention launch where the
+shape allows (--unfused: kivi_append, then kivi_decode_attn).  Steps rotate
+over L layer replicas (L x footprint >= 1 GiB) so the 256 MB Infinity Cache
+cannot serve the working set; inputs are resident in HBM before the timed
+region starts.  `value` is the algorithmic bytes a step must move (packed
+codes + fp32 scale/zero + fp16 window + q + out, plus the append's bytes)
+divided by the measured step time (HIP events at the two ends of the K timed
+steps).  `roofline` covers the attention launch alone (its split kernel and
+combine): a second timed loop issues K kivi_decode_attn calls back to back
+over the same replicas, with HIP events on the stream the library launches on
+around rounds of calls, and divides by the call count.  `cpu_baseline` times
+the CPU oracle on a bounded sample of (batch, KV head) slabs of the same
+workload.
 """
 from __future__ import annotations
 
@@ -158,6 +161,8 @@ def main():
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 scalar kernel, 2 matrix kernel")
     ap.add_argument("--tokens-per-split", type=int, default=0,
                     help="split size of the attention call (0 = the library's automatic plan)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time a step as kivi_append + kivi_decode_attn instead of kivi_decode_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-pack", action="store_true", help="skip the full-prefill pack pass")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -214,11 +219,18 @@ def main():
     decodes = [kivi.bind_decode_attn(c, q, out, ws, tokens_per_split=args.tokens_per_split,
                                      path=args.path, stream=stream) for c in caches]
 
+    # the fused step (kivi_decode_step) takes the automatic plan
+    fused = not args.unfused and args.path == 0 and args.tokens_per_split == 0
+    fused_steps = [kivi.bind_decode_step(c, k1, v1, q, out, ws, stream=stream) for c in caches]
+
     def step(i):
         c = caches[i % L]
         t_before = c.n_tokens
-        appends[i % L]()
-        decodes[i % L]()
+        if fused:
+            fused_steps[i % L]()
+        else:
+            appends[i % L]()
+            decodes[i % L]()
         return attn_bytes(w, t_before + 1), append_bytes(w, t_before)
 
     for i in range(args.warmup):
@@ -285,6 +297,7 @@ def main():
                    "head_dim": w.D, "context": w.T0 + 1, "k_bits": w.k_bits, "v_bits": w.v_bits,
                    "group": w.G, "residual": w.R, "layers_rotated": L,
                    "storage": "packed codes, fp32 scale/zero, fp16 window; fp16 q"},
+        "step_call": "kivi_decode_step" if fused else "kivi_append + kivi_decode_attn",
         "us_per_step": round(ms_step * 1e3, 2),
         "attn_us": round(attn_avg_ms * 1e3, 2),
         "attn_us_rounds_min_p50_max": [round(float(np.percentile(attn_ms, p)) * 1e3, 2)

@@ -126,13 +126,17 @@ int head_chunks(int n_rep) { return (n_rep + 7) / 8; }
 Plan make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
                const kivi::DecodeArgs &a) {
   Plan p;
-  const int64_t t = c->n_tokens;
+  const int64_t t = a.t;
   const int n_rep = Hq / c->n_kv_heads;
   const int64_t units = (int64_t)c->batch * c->n_kv_heads;
   p.matrix = (path == KIVI_PATH_AUTO || path == KIVI_PATH_MATRIX) && t > 0 &&
              kivi::decode_matrix_supported(a);
   if (p.matrix) {
-    p.n_main = (a.n_vq / kMatrixBlock) * kMatrixBlock;
+    // whole blocks of quantized keys and values; in a fused step the value
+    // leaving the window (token t_new - R) is quantized by the window role, so
+    // the blocks stop before it
+    const int64_t n_lim = a.t_new >= a.R ? a.t_new - a.R : a.n_vq;
+    p.n_main = (n_lim / kMatrixBlock) * kMatrixBlock;
     p.n_window = kivi::decode_matrix_window_chunks(a, p.n_main);
     int64_t tps = (tps_req + kMatrixBlock - 1) / kMatrixBlock * kMatrixBlock;
     if (tps == 0) {
@@ -332,10 +336,19 @@ size_t kivi_decode_attn_workspace_bytes(const kivi_cache *c, int32_t n_q_heads) 
   return kivi_decode_attn_workspace_bytes_ex(c, n_q_heads, 0, KIVI_PATH_AUTO);
 }
 
-int kivi_decode_attn_ex(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads,
-                        const float *mask, float *out, void *workspace, size_t workspace_bytes,
-                        int32_t tokens_per_split, int32_t path, void *stream) {
-  const char *who = "kivi_decode_attn";
+}  // extern "C"
+
+namespace {
+
+// Validation, planning and launch of an attention call.  With k_new and v_new
+// set, the launch is a fused decode step: it also appends token c->n_tokens
+// (the caller has checked that the matrix kernel takes the shape, that the
+// token completes no key block, and the capacity) and attends over
+// c->n_tokens + 1 tokens; the caller advances n_tokens on success.
+int decode_call(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, const float *mask,
+                float *out, void *workspace, size_t workspace_bytes, int32_t tokens_per_split,
+                int32_t path, void *stream, const void *k_new, const void *v_new,
+                const char *who) {
   int rc = check_cache(c, who);
   if (rc) return rc;
   if (n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0)
@@ -375,7 +388,11 @@ int kivi_decode_attn_ex(const kivi_cache *c, const void *q_fp16, int32_t n_q_hea
   a.Hq = n_q_heads;
   a.n_rep = n_q_heads / c->n_kv_heads;
   a.cap = c->capacity;
-  a.t = c->n_tokens;
+  const bool fused = k_new != nullptr;
+  a.t = c->n_tokens + (fused ? 1 : 0);
+  a.k_new = (const uint16_t *)k_new;
+  a.v_new = (const uint16_t *)v_new;
+  a.t_new = fused ? c->n_tokens : -1;
   a.n_kq = a.t - a.t % a.R;
   a.n_vq = max64(0, a.t - a.R);
   a.sm_scale = 1.0f / sqrtf((float)a.D);
@@ -385,6 +402,8 @@ int kivi_decode_attn_ex(const kivi_cache *c, const void *q_fp16, int32_t n_q_hea
   if (path == KIVI_PATH_VECTOR && !kivi::decode_vector_supported(a))
     return fail(KIVI_ERR_INVALID_ARG, "%s: the vector kernel does not handle this shape", who);
   const Plan p = make_plan(c, n_q_heads, tokens_per_split, path, a);
+  if (fused && !p.matrix)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: internal: fused step without the matrix kernel", who);
   if (p.S_total > max_slots(c, tokens_per_split))
     return fail(KIVI_ERR_WORKSPACE, "%s: internal split plan exceeds the workspace bound", who);
   a.S_total = p.S_total;
@@ -404,10 +423,67 @@ int kivi_decode_attn_ex(const kivi_cache *c, const void *q_fp16, int32_t n_q_hea
   return hip_status(kivi::launch_combine(a, s), "kivi_decode_attn (combine)");
 }
 
+}  // namespace
+
+extern "C" {
+
+int kivi_decode_attn_ex(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads,
+                        const float *mask, float *out, void *workspace, size_t workspace_bytes,
+                        int32_t tokens_per_split, int32_t path, void *stream) {
+  return decode_call(c, q_fp16, n_q_heads, mask, out, workspace, workspace_bytes,
+                     tokens_per_split, path, stream, nullptr, nullptr, "kivi_decode_attn");
+}
+
 int kivi_decode_attn(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, const float *mask,
                      float *out, void *workspace, size_t workspace_bytes, void *stream) {
   return kivi_decode_attn_ex(c, q_fp16, n_q_heads, mask, out, workspace, workspace_bytes, 0,
                              KIVI_PATH_AUTO, stream);
+}
+
+int kivi_decode_step(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp16,
+                     const void *q_fp16, int32_t n_q_heads, const float *mask, float *out,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+  const char *who = "kivi_decode_step";
+  int rc = check_cache(c, who);
+  if (rc) return rc;
+  if (!k_new_fp16 || !v_new_fp16 || !q_fp16 || !out)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: NULL k_new, v_new, q or out", who);
+  if (n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: n_q_heads %d must be a positive multiple of n_kv_heads %d",
+                who, n_q_heads, c->n_kv_heads);
+  if (c->n_tokens + 1 > c->capacity)
+    return fail(KIVI_ERR_CAPACITY, "%s: the cache is full (%lld tokens)", who,
+                (long long)c->capacity);
+  // the workspace is checked before anything runs, so that a failing call
+  // leaves the cache as it was
+  const size_t need = kivi_decode_attn_workspace_bytes_ex(c, n_q_heads, 0, KIVI_PATH_AUTO);
+  if (!workspace || workspace_bytes < need)
+    return fail(KIVI_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes,
+                need);
+  kivi::DecodeArgs probe{};
+  probe.kb = c->k_bits;
+  probe.vb = c->v_bits;
+  probe.G = c->group;
+  probe.D = c->head_dim;
+  probe.n_rep = n_q_heads / c->n_kv_heads;
+  probe.cap = c->capacity;
+  probe.q = (const uint16_t *)q_fp16;
+  const bool fused = kivi::decode_matrix_supported(probe) &&
+                     (c->n_tokens + 1) % c->residual != 0 &&
+                     ((uintptr_t)k_new_fp16 & 15) == 0 && ((uintptr_t)v_new_fp16 & 15) == 0;
+  if (!fused) {
+    // a token that completes a key block, or a shape the matrix kernel does
+    // not take: the append, then the attention call
+    rc = kivi_append(c, k_new_fp16, v_new_fp16, 1, stream);
+    if (rc) return rc;
+    return kivi_decode_attn_ex(c, q_fp16, n_q_heads, mask, out, workspace, workspace_bytes, 0,
+                               KIVI_PATH_AUTO, stream);
+  }
+  rc = decode_call(c, q_fp16, n_q_heads, mask, out, workspace, workspace_bytes, 0, KIVI_PATH_AUTO,
+                   stream, k_new_fp16, v_new_fp16, who);
+  if (rc) return rc;
+  c->n_tokens += 1;
+  return KIVI_OK;
 }
 
 }  // extern "C"

@@ -604,7 +604,9 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
         else
           src = a.k_zero + grp * kD + (u - 96) * 4;
       } else {
-        src = a.k_res + ((bh * a.R + (Ta + u / 16) % a.R) * kD + (u % 16) * 8);
+        const int64_t tok = Ta + u / 16;
+        src = tok == a.t_new ? a.k_new + (bh * kD + (u % 16) * 8)
+                             : a.k_res + ((bh * a.R + tok % a.R) * kD + (u % 16) * 8);
       }
       dma16(src, (lds_void *)(kl + (size_t)base * 16));
     }
@@ -630,16 +632,63 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
         src = a.v_zero + ((bh * 4 + x / nqv4) * a.cap + Ta + (x % nqv4) * 4);
       } else {
         const int x = u - u_vrow;
-        src = a.v_res + ((bh * a.R + (vq_end + x / 16) % a.R) * kD + (x % 16) * 8);
+        const int64_t tok = vq_end + x / 16;
+        src = tok == a.t_new ? a.v_new + (bh * kD + (x % 16) * 8)
+                             : a.v_res + ((bh * a.R + tok % a.R) * kD + (x % 16) * 8);
       }
       dma16(src, (lds_void *)(vl + (size_t)base * 16));
     }
   }
+  // Fused decode step.  The value that leaves the window with this token
+  // (t_pop = t_new - R, the last quantized value) is read from its window
+  // slot -- lane j holds channels 2j, 2j + 1 -- and quantized below; the
+  // new token's value and key are read from the inputs.
+  const int64_t t_pop = a.t_new >= a.R ? a.t_new - a.R : -1;
+  const bool pop_here = t_pop >= Ta && t_pop < vq_end;
+  const bool new_here = a.t_new >= Ta && a.t_new < Tb;
+  const int64_t wslot = a.t_new >= 0 ? a.t_new % a.R : 0;   // window slot of the new token
+  uint16_t *slot_v = const_cast<uint16_t *>(a.v_res) + (bh * a.R + wslot) * kD + 2 * j;
+  uint32_t popped = 0, nv = 0, nk = 0;
+  if (pop_here) popped = *(const uint32_t *)slot_v;
+  if (pop_here || new_here) nv = *(const uint32_t *)(a.v_new + bh * kD + 2 * j);
+  if (new_here) nk = *(const uint32_t *)(a.k_new + bh * kD + 2 * j);
   // q of the NREP heads, kept in the probability buffer (unused by this role)
   float(*q_s)[kPRow] = L.p;
   const uint16_t *q = a.q + ((int64_t)b * a.Hq + hk * NREP) * kD;
   for (int e = j; e < NREP * kD; e += 64) q_s[e / kD][e % kD] = h2f(q[e]);
   wait_vm<0>();
+  if (pop_here) {
+    // KIVI item 3 on the popped value: 16 lanes per 32-channel group, the
+    // quantizer of the pack kernels.  Its codes, scales and zeros replace
+    // what the DMA brought for that row (not yet written) and go to the cache.
+    const float x0 = h2f((uint16_t)(popped & 0xFFFFu)), x1 = h2f((uint16_t)(popped >> 16));
+    const float mn = row_min(fminf(x0, x1));
+    const float mx = row_max(fmaxf(x0, x1));
+    const float sc = group_scale(mn, mx, 2);
+    uint32_t w = (quant_code(x0, mn, sc, 2) | (quant_code(x1, mn, sc, 2) << 2)) << (4 * (j & 7));
+    w |= __shfl_xor(w, 1);
+    w |= __shfl_xor(w, 2);
+    w |= __shfl_xor(w, 4);
+    const int xr = (int)(t_pop - Ta);
+    const int gch = j >> 4;
+    if ((j & 7) == 0) {
+      ((uint32_t *)vl)[xr * 8 + (j >> 3)] = w;
+      const_cast<uint32_t *>(a.v_codes)[(bh * a.cap + t_pop) * 8 + (j >> 3)] = w;
+    }
+    if ((j & 15) == 0) {
+      ((float *)(vl + (size_t)u_vs * 16))[gch * nqv4 * 4 + xr] = sc;
+      ((float *)(vl + (size_t)u_vz * 16))[gch * nqv4 * 4 + xr] = mn;
+      const int64_t sz = (bh * 4 + gch) * a.cap + t_pop;
+      const_cast<float *>(a.v_scale)[sz] = sc;
+      const_cast<float *>(a.v_zero)[sz] = mn;
+    }
+    // the slot now takes the new value (this lane read its old contents above)
+    *(uint32_t *)slot_v = nv;
+  }
+  if (new_here) {
+    if (t_pop < 0) *(uint32_t *)slot_v = nv;   // no value left the window: the slot is free
+    *(uint32_t *)(const_cast<uint16_t *>(a.k_res) + (bh * a.R + wslot) * kD + 2 * j) = nk;
+  }
   wave_lds_sync();
 
   const float LOG2E = 1.4426950408889634f;
@@ -803,6 +852,13 @@ hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int tokens_
     return hipErrorInvalidValue;
   // the window role's key staging assumes whole key groups below n_kq
   if (a.n_kq % kG != 0) return hipErrorInvalidValue;
+  // a fused step appends token t - 1, never completes a key block, and keeps
+  // the value it pushes out of the window (token t - 1 - R) out of the block
+  // role, whose workgroups read quantized values from the cache
+  if (a.t_new >= 0) {
+    if (a.t_new != a.t - 1 || a.t % a.R == 0 || !a.k_new || !a.v_new) return hipErrorInvalidValue;
+    if (a.t_new >= a.R && n_main > a.t_new - a.R) return hipErrorInvalidValue;
+  }
   const int n_window = decode_matrix_window_chunks(a, n_main);
   if (n_splits + n_window <= 0 || n_splits + n_window > a.S_total) return hipErrorInvalidValue;
   const int64_t n_wg = ((int64_t)n_window + n_splits) * a.H * a.B;

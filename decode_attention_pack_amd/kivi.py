@@ -24,7 +24,8 @@ KIVI_PATH_AUTO, KIVI_PATH_GENERIC, KIVI_PATH_MATRIX, KIVI_PATH_VECTOR = 0, 1, 2,
 
 EXPORTED = ("kivi_pack_keys", "kivi_pack_values", "kivi_append", "kivi_decode_attn",
             "kivi_decode_attn_ex", "kivi_decode_attn_workspace_bytes",
-            "kivi_decode_attn_workspace_bytes_ex", "kivi_status_string", "kivi_last_error")
+            "kivi_decode_attn_workspace_bytes_ex", "kivi_decode_step", "kivi_status_string",
+            "kivi_last_error")
 
 
 class KiviError(RuntimeError):
@@ -68,6 +69,8 @@ def lib():
     L.kivi_decode_attn.restype = ctypes.c_int
     L.kivi_decode_attn_ex.argtypes = [ctypes.POINTER(CCache), P, i32, P, P, P, sz, i32, i32, P]
     L.kivi_decode_attn_ex.restype = ctypes.c_int
+    L.kivi_decode_step.argtypes = [ctypes.POINTER(CCache), P, P, P, i32, P, P, P, sz, P]
+    L.kivi_decode_step.restype = ctypes.c_int
     L.kivi_decode_attn_workspace_bytes.argtypes = [ctypes.POINTER(CCache), i32]
     L.kivi_decode_attn_workspace_bytes.restype = sz
     L.kivi_decode_attn_workspace_bytes_ex.argtypes = [ctypes.POINTER(CCache), i32, i32, i32]
@@ -217,6 +220,29 @@ def kivi_decode_attn(cache: Cache, q, mask=None, out=None, workspace=None, token
     return out
 
 
+def kivi_decode_step(cache: Cache, k_new, v_new, q, mask=None, out=None, workspace=None,
+                     stream=None):
+    """Append one token ([B][H][1][D] or [B][H][D] fp16) and attend over the
+    resulting cache in one library call; returns out."""
+    B, Hq, D = q.shape
+    shape = (cache.B, cache.H, cache.D)
+    kp = _dev(k_new.reshape(shape), torch.float16, shape, "k_new")
+    vp = _dev(v_new.reshape(shape), torch.float16, shape, "v_new")
+    qp = _dev(q, torch.float16, (cache.B, Hq, cache.D), "q")
+    mp = None
+    if mask is not None:
+        mp = _dev(mask, torch.float32, (cache.B, cache.n_tokens + 1), "mask")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    op = _dev(out, torch.float32, (cache.B, Hq, cache.D), "out")
+    if workspace is None:
+        workspace = cache.new_workspace(Hq)
+    wp = _dev(workspace, torch.uint8, None, "workspace")
+    _check(lib().kivi_decode_step(ctypes.byref(cache.c), kp, vp, qp, Hq, mp, op, wp,
+                                  workspace.numel(), _stream(stream)))
+    return out
+
+
 class BoundCall:
     """A library call whose arguments were checked and marshalled once.
 
@@ -259,3 +285,16 @@ def bind_decode_attn(cache: Cache, q, out, workspace, mask=None, tokens_per_spli
                      [ctypes.byref(cache.c), qp, Hq, mp, op, wp, workspace.numel(), tokens_per_split,
                       path, _stream(stream)], (cache, q, mask, out, workspace))
 
+
+def bind_decode_step(cache: Cache, k_new, v_new, q, out, workspace, stream=None) -> BoundCall:
+    """Bound kivi_decode_step (no mask)."""
+    Hq = q.shape[1]
+    shape = (cache.B, cache.H, cache.D)
+    kp = _dev(k_new.reshape(shape), torch.float16, shape, "k_new")
+    vp = _dev(v_new.reshape(shape), torch.float16, shape, "v_new")
+    qp = _dev(q, torch.float16, (cache.B, Hq, cache.D), "q")
+    op = _dev(out, torch.float32, (cache.B, Hq, cache.D), "out")
+    wp = _dev(workspace, torch.uint8, None, "workspace")
+    return BoundCall(lib().kivi_decode_step,
+                     [ctypes.byref(cache.c), kp, vp, qp, Hq, None, op, wp, workspace.numel(),
+                      _stream(stream)], (cache, k_new, v_new, q, out, workspace))

@@ -171,6 +171,27 @@ int kivi_decode_attn_ex(const kivi_cache *c, const void *q_fp16, int32_t n_q_hea
 size_t kivi_decode_attn_workspace_bytes_ex(const kivi_cache *c, int32_t n_q_heads,
                                            int32_t tokens_per_split, int32_t path);
 
+/* KIVI items 4 and 5 in one call: one decode step that appends one token
+ * and attends over the cache that results, i.e. the same cache state and
+ * (within the attention tolerance) the same output as
+ *   kivi_append(c, k_new, v_new, 1); kivi_decode_attn(c, q, ...).
+ * Where the matrix-core kernel takes the shape (2-bit keys and values,
+ * head_dim 128, G 32, 1, 2 or 4 query heads per KV head, 16-byte aligned
+ * k_new and v_new) and the token completes no key block ((n_tokens + 1) % R
+ * != 0), the append runs inside the attention launch: the new key and value
+ * are read from k_new / v_new, the value that leaves the window is quantized
+ * by the workgroup that attends over it, and the cache writes happen where
+ * no other workgroup reads.  Otherwise the two calls above run in turn.
+ *   k_new_fp16, v_new_fp16  (device) fp16 [B][H][D], the new token.
+ *   q_fp16, out             as for kivi_decode_attn.
+ *   mask                    (device) f32 [B][n_tokens + 1] or NULL.
+ *   workspace               at least kivi_decode_attn_workspace_bytes().
+ * KIVI_ERR_CAPACITY if the cache is full; the workspace is checked before
+ * anything runs.  On success c->n_tokens grows by one. */
+int kivi_decode_step(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp16,
+                     const void *q_fp16, int32_t n_q_heads, const float *mask,
+                     float *out, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *kivi_status_string(int status);
 /* Detail of the last failing call on this thread ("" if none). */

@@ -1,0 +1,154 @@
+"""GPU parity of kivi_decode_step -- one decode step that appends a token and
+attends over the resulting cache (KIVI items 4 and 5 of the page "Literature
+audit -- Group 2", section 1, "Core algorithm") -- against the CPU oracle's
+append followed by its attention: outputs within 2e-3 + 1e-3*|ref|
+elementwise, packed stores and window rows bit for bit.
+
+The sequences cross every case of the fused path: steps before any value
+leaves the window, the first value to leave it, a popped token at a block
+boundary of the attention kernel (n_vq a multiple of 128), and the steps that
+complete a key block (which run as append + attention)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_pack_amd import kivi, synth
+from tests.gpu_util import assert_close, b16, compare_slab, dev, host, say
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def _steps(rep, R, T0, n_steps, masked, kb=2, vb=2, B=2, H=2, D=128, G=32, seed=0):
+    rng = np.random.default_rng(seed + 7 * rep + R + T0)
+    t_end = T0 + n_steps
+    cap = ((t_end + R - 1) // R) * R
+    scale = rng.uniform(0.5, 15, (1, H, 1, D))
+    K = (rng.standard_normal((B, H, t_end, D)) * scale).astype(np.float16)
+    V = rng.standard_normal((B, H, t_end, D)).astype(np.float16)
+    g = kivi.Cache(B, H, D, kb, vb, G, R, cap)
+    o = oracle.Cache(B, H, D, kb, vb, G, R, cap)
+    if T0:
+        kivi.kivi_append(g, dev(K[:, :, :T0]), dev(V[:, :, :T0]))
+        o.append(b16(K[:, :, :T0]), b16(V[:, :, :T0]))
+    ws = g.new_workspace(H * rep)
+    say(f"decode_step rep={rep} R={R} T0={T0} steps={n_steps} masked={masked} kb={kb} vb={vb}")
+    for i in range(n_steps):
+        t = T0 + i
+        q = rng.standard_normal((B, H * rep, D)).astype(np.float16)
+        k1 = np.ascontiguousarray(K[:, :, t:t + 1])
+        v1 = np.ascontiguousarray(V[:, :, t:t + 1])
+        mask = None
+        if masked:
+            mask = np.where(rng.random((B, t + 1)) < 0.2, -np.inf,
+                            rng.standard_normal((B, t + 1))).astype(np.float32)
+            mask[:, -1] = 0.0
+        out = host(kivi.kivi_decode_step(g, dev(k1), dev(v1), dev(q),
+                                         None if mask is None else dev(mask), workspace=ws))
+        o.append(b16(k1), b16(v1))
+        ref = o.decode_attn(b16(q), mask)
+        assert g.n_tokens == t + 1
+        assert_close(out, ref, f"step t={t + 1}")
+        if i % 16 == 15 or i == n_steps - 1 or (t + 1) % R in (0, 1):
+            torch.cuda.synchronize()
+            for b in range(B):
+                for h in range(H):
+                    compare_slab(g, b, h, o, b, h)
+
+
+@pytest.mark.parametrize("rep,R,T0,n_steps", [
+    (4, 128, 120, 150),     # first pops, a key block at 128 and 256, n_vq = 128 at t = 256
+    (1, 32, 3, 80),         # short window: many pops and key blocks
+    (2, 64, 500, 70),       # blocks in the block role from the start
+    (4, 128, 1, 20),        # nearly empty cache: nothing in the block role
+])
+def test_decode_step_matches_oracle(rep, R, T0, n_steps):
+    _steps(rep, R, T0, n_steps, masked=False)
+
+
+def test_decode_step_masked():
+    _steps(4, 128, 250, 12, masked=True)
+
+
+@pytest.mark.parametrize("kb,vb,rep", [(4, 4, 1), (2, 2, 8)])
+def test_decode_step_other_shapes(kb, vb, rep):
+    """Shapes the matrix kernel does not take run as append + attention."""
+    _steps(rep, 64, 100, 20, masked=False, kb=kb, vb=vb)
+
+
+def test_decode_step_equals_append_then_attend():
+    """Fused and unfused steps leave bit-identical caches and outputs within
+    rounding-order differences."""
+    rng = np.random.default_rng(11)
+    B, H, D, R, rep, T0, n = 2, 4, 128, 128, 4, 1000, 140
+    cap = ((T0 + n + R - 1) // R) * R
+    K = rng.standard_normal((B, H, T0 + n, D)).astype(np.float16)
+    V = rng.standard_normal((B, H, T0 + n, D)).astype(np.float16)
+    a = kivi.Cache(B, H, D, 2, 2, 32, R, cap)
+    u = kivi.Cache(B, H, D, 2, 2, 32, R, cap)
+    for c in (a, u):
+        kivi.kivi_append(c, dev(K[:, :, :T0]), dev(V[:, :, :T0]))
+    for i in range(n):
+        t = T0 + i
+        q = dev(rng.standard_normal((B, H * rep, D)).astype(np.float16))
+        k1, v1 = dev(K[:, :, t:t + 1]), dev(V[:, :, t:t + 1])
+        fa = host(kivi.kivi_decode_step(a, k1, v1, q))
+        kivi.kivi_append(u, k1, v1)
+        fu = host(kivi.kivi_decode_attn(u, q))
+        np.testing.assert_allclose(fa, fu, atol=1e-4, rtol=1e-4, err_msg=f"t={t + 1}")
+    torch.cuda.synchronize()
+    assert a.n_tokens == u.n_tokens == T0 + n
+    for name in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero"):
+        ga, gu = host(getattr(a, name)), host(getattr(u, name))
+        if name.startswith("k"):
+            n_kq = a.n_tokens - a.n_tokens % R
+            sl = (slice(None), slice(None), slice(0, n_kq // 32))
+        elif name == "v_codes":
+            sl = (slice(None), slice(None), slice(0, a.n_tokens - R))
+        else:
+            sl = (slice(None), slice(None), slice(None), slice(0, a.n_tokens - R))
+        assert np.array_equal(ga[sl].view(np.uint32), gu[sl].view(np.uint32)), name
+
+
+def test_decode_step_rejects_full_cache_and_small_workspace():
+    rng = np.random.default_rng(3)
+    B, H, D, R = 1, 1, 128, 32
+    g = kivi.Cache(B, H, D, 2, 2, 32, R, R)
+    x = rng.standard_normal((B, H, R, D)).astype(np.float16)
+    kivi.kivi_append(g, dev(x), dev(x))
+    k1 = dev(x[:, :, :1])
+    q = dev(rng.standard_normal((B, H, D)).astype(np.float16))
+    with pytest.raises(kivi.KiviError):
+        kivi.kivi_decode_step(g, k1, k1, q)
+    g2 = kivi.Cache(B, H, D, 2, 2, 32, R, 4 * R)
+    kivi.kivi_append(g2, dev(x), dev(x))
+    with pytest.raises(kivi.KiviError):
+        kivi.kivi_decode_step(g2, k1, k1, q, workspace=torch.empty(16, dtype=torch.uint8,
+                                                                    device="cuda"))
+    assert g2.n_tokens == R
+
+
+@pytest.mark.parametrize("index", [4])
+def test_decode_step_full_workload(index):
+    """Two fused steps on the full 32k GQA workload, in the configuration the
+    benchmark times; the oracle rebuilds three sampled slabs alone."""
+    w = synth.WORKLOADS[index]
+    inp = synth.make_inputs(w.replace(steps=2))
+    g = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
+    say(f"{w.name}: prefill {w.T0} + 2 fused steps")
+    kivi.kivi_append(g, dev(inp["k0"]), dev(inp["v0"]))
+    rep = w.Hq // w.Hkv
+    outs = []
+    for s in range(2):
+        outs.append(host(kivi.kivi_decode_step(g, dev(inp["k_steps"][s]), dev(inp["v_steps"][s]),
+                                               dev(inp["q_steps"][s]))))
+    for b, h in [(0, 0), (3, 7), (1, 4)]:
+        o = oracle.Cache(1, 1, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
+        o.append(b16(inp["k0"][b:b + 1, h:h + 1]), b16(inp["v0"][b:b + 1, h:h + 1]))
+        for s in range(2):
+            o.append(b16(inp["k_steps"][s][b:b + 1, h:h + 1]),
+                     b16(inp["v_steps"][s][b:b + 1, h:h + 1]))
+            ref = o.decode_attn(b16(inp["q_steps"][s][b:b + 1, h * rep:(h + 1) * rep]))[0]
+            assert_close(outs[s][b, h * rep:(h + 1) * rep], ref, f"{w.name} step {s} b{b} kv{h}")
+        compare_slab(g, b, h, o, 0, 0)
