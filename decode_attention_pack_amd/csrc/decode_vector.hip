@@ -128,6 +128,7 @@ __device__ __forceinline__ float uniform(float v) {
 // grid: (n_splits, H * head_chunks, B); block: 256 (4 waves).
 template <int KB, int VB, int NH>
 __global__ void __launch_bounds__(kVThreads)
+    __attribute__((amdgpu_waves_per_eu(NH == 1 ? 3 : 2)))   // one head: 3 waves per SIMD
 decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int direct) {
   __shared__ float red_s[kVWaves][NH][kVD];
   __shared__ float stat_s[kVWaves][NH][2];
@@ -149,9 +150,11 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
   const int qd = lane & 3;    // value channels 32 qd .. 32 qd + 31 (one value group)
   const int tq = lane >> 2;   // token of each 16-token half this lane scores and accumulates
 
-  const int64_t s0 = (int64_t)split * tokens_per_split;
-  const int64_t s1 = min(s0 + (int64_t)tokens_per_split, a.t);
-  const int64_t g_end = (s1 + kVG - 1) / kVG;
+  // token and group indices within a slab fit 32 bits (cap < 2^26)
+  const int s0 = split * tokens_per_split;
+  const int s1 = (int)min((int64_t)s0 + tokens_per_split, a.t);
+  const int g_end = (s1 + kVG - 1) / kVG;
+  const int t_all = (int)a.t, n_kq = (int)a.n_kq, n_vq = (int)a.n_vq, R = a.R;
 
   // q of channels 2 lane, 2 lane + 1, times 1/sqrt(D)
   float q0[NH], q1[NH];
@@ -172,15 +175,25 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
     for (int c = 0; c < 32; ++c) acc[j][c] = 0.0f;
   }
 
+  // Slab base pointers (wave-uniform, so they stay in scalar registers) and
+  // 32-bit per-lane byte offsets: each load is a scalar base plus one
+  // 32-bit vector offset, with no 64-bit address arithmetic per lane.
   const int64_t kgroups = a.cap / kVG;
-  const uint32_t *kcodes = a.k_codes + bh * kgroups * (kVD * KB) + lane * (2 * KB);
-  const float *kscale = a.k_scale + bh * kgroups * kVD + 2 * lane;
-  const float *kzero = a.k_zero + bh * kgroups * kVD + 2 * lane;
-  const uint16_t *kres = a.k_res + bh * a.R * kVD + 2 * lane;
-  const uint32_t *vcodes = a.v_codes + bh * a.cap * (kVD * VB / 32) + qd * VWQ;
-  const float *vscale = a.v_scale + (bh * (kVD / kVG) + qd) * a.cap;
-  const float *vzero = a.v_zero + (bh * (kVD / kVG) + qd) * a.cap;
-  const uint16_t *vres = a.v_res + bh * a.R * kVD + qd * 32;
+  const char *kcodes = (const char *)(a.k_codes + bh * kgroups * (kVD * KB));
+  const char *kscale = (const char *)(a.k_scale + bh * kgroups * kVD);
+  const char *kzero = (const char *)(a.k_zero + bh * kgroups * kVD);
+  const char *kres = (const char *)(a.k_res + bh * a.R * kVD);
+  const char *vcodes = (const char *)(a.v_codes + bh * a.cap * (kVD * VB / 32));
+  const char *vscale = (const char *)(a.v_scale + bh * (kVD / kVG) * a.cap);
+  const char *vzero = (const char *)(a.v_zero + bh * (kVD / kVG) * a.cap);
+  const char *vres = (const char *)(a.v_res + bh * a.R * kVD);
+  const char *mrow = a.mask ? (const char *)(a.mask + (int64_t)b * a.t) : nullptr;
+  const uint32_t kc_lane = (uint32_t)lane * (2 * KB) * 4u;
+  const uint32_t ks_lane = (uint32_t)lane * 8u;
+  const uint32_t kr_lane = (uint32_t)lane * 4u;
+  const uint32_t vc_lane = (uint32_t)qd * VWQ * 4u;
+  const uint32_t vs_lane = (uint32_t)qd * (uint32_t)a.cap * 4u;
+  const uint32_t vr_lane = (uint32_t)qd * 64u;
 
   // The code, scale and zero words of a group (and the mask entries of the
   // lane's tokens) are loaded one group ahead, so their latency overlaps the
@@ -193,14 +206,15 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
     uint32_t vw[2][VWQ];
     float vs[2], vz[2], mk[2];
   };
-  auto fetch = [&](int64_t g, Raw &r) {
-    load_words<KB / 2>(kcodes + g * (kVD * KB), r.kw);
-    r.ks = *(const float2 *)(kscale + g * kVD);
-    r.kz = *(const float2 *)(kzero + g * kVD);
+  auto fetch = [&](int g, Raw &r) {
+    load_words<KB / 2>((const uint32_t *)(kcodes + ((uint32_t)g * (kVD * KB * 4u) + kc_lane)),
+                       r.kw);
+    r.ks = *(const float2 *)(kscale + ((uint32_t)g * (kVD * 4u) + ks_lane));
+    r.kz = *(const float2 *)(kzero + ((uint32_t)g * (kVD * 4u) + ks_lane));
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const int64_t tau = g * kVG + 16 * hh + tq;
-      const uint32_t *src = vcodes + tau * (kVD * VB / 32);
+      const uint32_t tau = (uint32_t)(g * kVG + 16 * hh + tq);
+      const uint32_t *src = (const uint32_t *)(vcodes + (tau * (kVD * VB / 8u) + vc_lane));
       if constexpr (VWQ == 4) {
         const uint4 v = *(const uint4 *)src;
         r.vw[hh][0] = v.x;
@@ -212,16 +226,16 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
         r.vw[hh][0] = v.x;
         r.vw[hh][1] = v.y;
       }
-      r.vs[hh] = vscale[tau];
-      r.vz[hh] = vzero[tau];
-      r.mk[hh] = a.mask ? a.mask[(int64_t)b * a.t + min(tau, a.t - 1)] : 0.0f;
+      r.vs[hh] = *(const float *)(vscale + (vs_lane + tau * 4u));
+      r.vz[hh] = *(const float *)(vzero + (vs_lane + tau * 4u));
+      r.mk[hh] = mrow ? *(const float *)(mrow + (uint32_t)min((int)tau, t_all - 1) * 4u) : 0.0f;
     }
   };
 
   // one 32-token group: scores, online softmax update, value accumulation
-  auto process = [&](int64_t gi, const Raw &cur) __attribute__((always_inline)) {
-    const int64_t t0 = gi * kVG;
-    const bool quantized = t0 < a.n_kq;   // n_kq is a multiple of the group size
+  auto process = [&](int gi, const Raw &cur) __attribute__((always_inline)) {
+    const int t0 = gi * kVG;
+    const bool quantized = t0 < n_kq;     // n_kq is a multiple of the group size
     float qs0[NH], qs1[NH], qz[NH];
 #pragma unroll
     for (int j = 0; j < NH; ++j) {
@@ -231,7 +245,7 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
     }
     // fp16 key window: token tau sits in row tau mod R; R is a multiple of
     // the group size, so the group's tokens sit in consecutive rows
-    const int row0 = quantized ? 0 : (int)((uint32_t)t0 % (uint32_t)a.R);
+    const int row0 = quantized ? 0 : (int)((uint32_t)t0 % (uint32_t)R);
 
     float sc[NH][2];
 #pragma unroll
@@ -259,10 +273,11 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
       } else {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int64_t tau = t0 + 16 * hh + e;
+          const int tau = t0 + 16 * hh + e;
           // rows past the split end are inside the window array; their
           // products are dropped
-          const uint32_t kk = *(const uint32_t *)(kres + (row0 + 16 * hh + e) * kVD);
+          const uint32_t kk =
+              *(const uint32_t *)(kres + ((uint32_t)(row0 + 16 * hh + e) * (kVD * 2u) + kr_lane));
           const float k0 = tau < s1 ? h2f((uint16_t)(kk & 0xFFFFu)) : 0.0f;
           const float k1 = tau < s1 ? h2f((uint16_t)(kk >> 16)) : 0.0f;
 #pragma unroll
@@ -298,9 +313,9 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
     // values of token tq of each half, channels 32 qd .. 32 qd + 31
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const int64_t tau = t0 + 16 * hh + tq;
+      const int tau = t0 + 16 * hh + tq;
       if (tau < s1) {
-        if (tau < a.n_vq) {
+        if (tau < n_vq) {
           float ps[NH];
 #pragma unroll
           for (int j = 0; j < NH; ++j) {
@@ -318,7 +333,8 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
                 acc[j][wi * VPW + k] = fmaf(ps[j], f[k], acc[j][wi * VPW + k]);
           }
         } else {
-          const uint16_t *row = vres + ((uint32_t)tau % (uint32_t)a.R) * kVD;
+          const uint16_t *row =
+              (const uint16_t *)(vres + (((uint32_t)tau % (uint32_t)R) * (kVD * 2u) + vr_lane));
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const uint4 v = *(const uint4 *)(row + 8 * i);
@@ -340,10 +356,10 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
   };
 
   // two register sets alternate as the current group and the one ahead
-  const int64_t g_first = s0 / kVG + wave;
+  const int g_first = s0 / kVG + wave;
   Raw ra, rb;
   if (g_first < g_end) fetch(g_first, ra);
-  for (int64_t gi = g_first; gi < g_end;) {
+  for (int gi = g_first; gi < g_end;) {
     fetch(min(gi + kVWaves, g_end - 1), rb);
     process(gi, ra);
     gi += kVWaves;
@@ -429,7 +445,7 @@ bool decode_vector_supported(const DecodeArgs &a) {
                        ((uintptr_t)a.k_zero & 7) == 0 && ((uintptr_t)a.q & 3) == 0;
   return a.D == kVD && a.G == kVG && (a.kb == 2 || a.kb == 4) && (a.vb == 2 || a.vb == 4) &&
          (a.n_rep == 1 || a.n_rep == 2) && a.R % kVG == 0 && a.cap % kVG == 0 &&
-         a.cap < ((int64_t)1 << 31) && aligned;
+         a.cap < ((int64_t)1 << 26) && aligned;
 }
 
 template <int KB, int VB>
