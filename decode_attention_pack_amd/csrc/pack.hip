@@ -169,10 +169,14 @@ value_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t n_rows,
   }
   __syncthreads();
   const int t = threadIdx.x & 63;
-  if (t >= rows) return;
   constexpr int per = 32 / BITS;
   constexpr int n_groups = D / G;
+  constexpr int kWords = D / per;                   // code words per token row
+  // code rows of the tile, staged here and stored as one contiguous run
+  // (16-byte stores; the launcher checks the alignment)
+  __shared__ __attribute__((aligned(16))) uint32_t out_s[64 * kWords];
   for (int g = threadIdx.x >> 6; g < n_groups; g += 4) {
+    if (t >= rows) continue;
     // the group's G channels, 8 per 16-byte LDS read
     uint16_t v16[G];
 #pragma unroll
@@ -190,7 +194,7 @@ value_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t n_rows,
     const float s = group_scale(mn, mx, BITS);
     const float r = __builtin_amdgcn_rcpf(s);
     const int64_t tau = tau_first + r0 + t;
-    uint32_t *dst = codes + (bh * cap + tau) * (int64_t)(D / per) + (g * G) / per;
+    uint32_t *dst = out_s + t * kWords + (g * G) / per;
 #pragma unroll
     for (int w = 0; w < G / per; ++w) {
       uint32_t word = 0;
@@ -203,6 +207,11 @@ value_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t n_rows,
     scale[sz] = s;
     zero[sz] = mn;
   }
+  __syncthreads();
+  // the tile's rows are consecutive tokens of one slab: one contiguous run
+  uint32_t *run = codes + (bh * cap + tau_first + r0) * (int64_t)kWords;
+  for (int i = threadIdx.x; i < rows * kWords / 4; i += 256)
+    *(uint4 *)(run + 4 * i) = *(const uint4 *)(out_s + 4 * i);
 }
 
 bool pack_tiles_supported(int D, int G, int bits) {
@@ -243,6 +252,12 @@ hipError_t launch_value_tokens(const uint16_t *x, int64_t T_in, int64_t n_rows, 
                                float *scale, float *zero, hipStream_t s) {
   if (n_rows <= 0 || BH <= 0) return hipSuccess;
   if (!pack_tiles_supported(D, G, bits) || n_rows > T_in) return hipErrorInvalidValue;
+  if (((uintptr_t)codes & 15) != 0) {
+    // the tile kernel stores 16-byte runs of code rows; any other
+    // destination takes the per-row kernel
+    TokenSource src{nullptr, x, tau_first, T_in, 1, D};
+    return launch_value_rows(src, tau_first, n_rows, BH, bits, G, D, cap, codes, scale, zero, s);
+  }
   dim3 grid((unsigned)((n_rows + 63) / 64), (unsigned)BH);
 #define KIVI_VT(DD, GG)                                                                         \
   if (D == DD && G == GG) {                                                                     \

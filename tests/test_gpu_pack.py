@@ -13,11 +13,15 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 
-def _gpu_pack(x16, bits, G, cap, off, keys):
+def _gpu_pack(x16, bits, G, cap, off, keys, codes_offset=0):
+    """Pack on the GPU; codes_offset > 0 places the code array that many
+    words into a larger buffer (a destination that is not 16-byte aligned)."""
     B, H, T, D = x16.shape
     shp = kivi.layout_shapes(B, H, D, bits, bits, G, 1, cap)
     n = "k" if keys else "v"
-    codes = torch.zeros(shp[f"{n}_codes"], dtype=torch.int32, device="cuda")
+    n_codes = int(np.prod(shp[f"{n}_codes"]))
+    buf = torch.zeros(n_codes + codes_offset, dtype=torch.int32, device="cuda")
+    codes = buf[codes_offset:].view(shp[f"{n}_codes"])
     scale = torch.zeros(shp[f"{n}_scale"], dtype=torch.float32, device="cuda")
     zero = torch.zeros(shp[f"{n}_zero"], dtype=torch.float32, device="cuda")
     fn = kivi.kivi_pack_keys if keys else kivi.kivi_pack_values
@@ -59,6 +63,19 @@ def test_pack_other_shapes(bits, G, D):
     most 16 KB per key tile, D in {64, 128, 256}); the rest take the general
     kernels."""
     test_pack_small(bits, G, D)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_pack_values_unaligned_destination(bits):
+    """A code array 4 bytes past a 16-byte boundary takes the per-row kernel;
+    the result is the same bit for bit."""
+    rng = np.random.default_rng(9 + bits)
+    x = rng.standard_normal((2, 3, 70, 128)).astype(np.float16)
+    got = _gpu_pack(x, bits, 32, 128, 5, False, codes_offset=1)
+    ref = oracle.pack_values(b16(x), bits, 32, cap=128, offset=5)
+    assert _same(got[0][:, :, 5:75], ref[0][:, :, 5:75])
+    assert _same(got[1][..., 5:75], ref[1][..., 5:75])
+    assert _same(got[2][..., 5:75], ref[2][..., 5:75])
 
 
 def test_pack_values_ragged_rows():
