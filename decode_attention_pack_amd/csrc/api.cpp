@@ -342,9 +342,9 @@ namespace {
 
 // Validation, planning and launch of an attention call.  With k_new and v_new
 // set, the launch is a fused decode step: it also appends token c->n_tokens
-// (the caller has checked that the matrix kernel takes the shape, that the
-// token completes no key block, and the capacity) and attends over
-// c->n_tokens + 1 tokens; the caller advances n_tokens on success.
+// (the caller has checked that the matrix kernel takes the shape, and the
+// capacity) and attends over c->n_tokens + 1 tokens; the caller advances
+// n_tokens on success.
 int decode_call(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, const float *mask,
                 float *out, void *workspace, size_t workspace_bytes, int32_t tokens_per_split,
                 int32_t path, void *stream, const void *k_new, const void *v_new,
@@ -469,11 +469,10 @@ int kivi_decode_step(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp
   probe.cap = c->capacity;
   probe.q = (const uint16_t *)q_fp16;
   const bool fused = kivi::decode_matrix_supported(probe) &&
-                     (c->n_tokens + 1) % c->residual != 0 &&
                      ((uintptr_t)k_new_fp16 & 15) == 0 && ((uintptr_t)v_new_fp16 & 15) == 0;
   if (!fused) {
-    // a token that completes a key block, or a shape the matrix kernel does
-    // not take: the append, then the attention call
+    // a shape the matrix kernel does not take: the append, then the
+    // attention call
     rc = kivi_append(c, k_new_fp16, v_new_fp16, 1, stream);
     if (rc) return rc;
     return kivi_decode_attn_ex(c, q_fp16, n_q_heads, mask, out, workspace, workspace_bytes, 0,

@@ -582,6 +582,10 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
   // keys: Ta and n_kq are multiples of 32, so the chunk is one whole
   // quantized key group or consists of fp16 window rows
   const bool kq = Ta < a.n_kq;
+  // A fused step whose token completes a key block quantizes keys [t - R, t)
+  // in this launch: each of those chunks stages its 32 fp16 rows and turns
+  // them into its key group below (kq_now).
+  const bool kq_now = a.t_new >= 0 && a.t % a.R == 0 && Ta >= a.t - a.R;
   // values: [Ta, vq_end) quantized, [vq_end, Tb) fp16
   const int64_t vq_end = a.n_vq < Ta ? Ta : (a.n_vq > Tb ? Tb : a.n_vq);
   const int n_qv = (int)(vq_end - Ta), n_fv = (int)(Tb - vq_end);
@@ -590,12 +594,12 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
   // ---- DMA, in 16-byte units.  Key buffer: codes (64 units), scale and zero
   // (32 + 32), or n fp16 rows (16 units each) -- at most 512 units = 8 KB.
   char *kl = (char *)L.ks;
-  const int ku_end = kq ? 128 : n * 16;
+  const int ku_end = kq && !kq_now ? 128 : n * 16;
   for (int base = 0; base < ku_end; base += 64) {
     const int u = base + j;
     if (u < ku_end) {
       const void *src;
-      if (kq) {
+      if (kq && !kq_now) {
         const int64_t grp = bh * (a.cap / kG) + Ta / kG;
         if (u < 64)
           src = a.k_codes + grp * 256 + u * 4;
@@ -688,6 +692,45 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
   if (new_here) {
     if (t_pop < 0) *(uint32_t *)slot_v = nv;   // no value left the window: the slot is free
     *(uint32_t *)(const_cast<uint16_t *>(a.k_res) + (bh * a.R + wslot) * kD + 2 * j) = nk;
+  }
+  if (kq_now) {
+    // KIVI item 2 on this chunk's key group (32 tokens; n == 32): lane j
+    // takes channels 2j and 2j + 1 over the staged rows -- min/max, then the
+    // codes, with the quantizer of the append path.  The codes, scales and
+    // zeros replace the rows in LDS in the layout of a staged key group and
+    // go to the cache.
+    const uint32_t *rows = (const uint32_t *)kl + j;   // row r at rows[r * 64]
+    float mn0, mx0, mn1, mx1;
+    {
+      const uint32_t w = rows[0];
+      mn0 = mx0 = h2f((uint16_t)(w & 0xFFFFu));
+      mn1 = mx1 = h2f((uint16_t)(w >> 16));
+    }
+    for (int r = 1; r < kWT; ++r) {
+      const uint32_t w = rows[r * 64];
+      const float x0 = h2f((uint16_t)(w & 0xFFFFu)), x1 = h2f((uint16_t)(w >> 16));
+      mn0 = x0 < mn0 ? x0 : mn0;
+      mx0 = x0 > mx0 ? x0 : mx0;
+      mn1 = x1 < mn1 ? x1 : mn1;
+      mx1 = x1 > mx1 ? x1 : mx1;
+    }
+    const float sc0 = group_scale(mn0, mx0, 2), sc1 = group_scale(mn1, mx1, 2);
+    uint32_t cw[4] = {0u, 0u, 0u, 0u};   // channel 2j: words 0, 1; channel 2j + 1: words 2, 3
+    for (int r = 0; r < kWT; ++r) {
+      const uint32_t w = rows[r * 64];
+      const int sh = 2 * (r & 15), hw = r >> 4;
+      cw[hw] |= quant_code(h2f((uint16_t)(w & 0xFFFFu)), mn0, sc0, 2) << sh;
+      cw[2 + hw] |= quant_code(h2f((uint16_t)(w >> 16)), mn1, sc1, 2) << sh;
+    }
+    wave_lds_sync();   // every lane's row reads are done before the rows are overwritten
+    const uint4 c4 = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+    *(uint4 *)((uint32_t *)kl + 4 * j) = c4;                       // codes: 2 words per channel
+    *(float2 *)((float *)(kl + 64 * 16) + 2 * j) = make_float2(sc0, sc1);
+    *(float2 *)((float *)(kl + 96 * 16) + 2 * j) = make_float2(mn0, mn1);
+    const int64_t grp = bh * (a.cap / kG) + Ta / kG;
+    *(uint4 *)(const_cast<uint32_t *>(a.k_codes) + grp * 256 + 4 * j) = c4;
+    *(float2 *)(const_cast<float *>(a.k_scale) + grp * kD + 2 * j) = make_float2(sc0, sc1);
+    *(float2 *)(const_cast<float *>(a.k_zero) + grp * kD + 2 * j) = make_float2(mn0, mn1);
   }
   wave_lds_sync();
 
@@ -852,12 +895,14 @@ hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int tokens_
     return hipErrorInvalidValue;
   // the window role's key staging assumes whole key groups below n_kq
   if (a.n_kq % kG != 0) return hipErrorInvalidValue;
-  // a fused step appends token t - 1, never completes a key block, and keeps
-  // the value it pushes out of the window (token t - 1 - R) out of the block
-  // role, whose workgroups read quantized values from the cache
+  // a fused step appends token t - 1 and keeps the value it pushes out of the
+  // window (token t - 1 - R) out of the block role, whose workgroups read
+  // quantized values from the cache; when the token completes a key block,
+  // the window role quantizes keys [t - R, t), which lie above n_main
   if (a.t_new >= 0) {
-    if (a.t_new != a.t - 1 || a.t % a.R == 0 || !a.k_new || !a.v_new) return hipErrorInvalidValue;
+    if (a.t_new != a.t - 1 || !a.k_new || !a.v_new) return hipErrorInvalidValue;
     if (a.t_new >= a.R && n_main > a.t_new - a.R) return hipErrorInvalidValue;
+    if (a.t % a.R == 0 && n_main > a.t - a.R) return hipErrorInvalidValue;
   }
   const int n_window = decode_matrix_window_chunks(a, n_main);
   if (n_splits + n_window <= 0 || n_splits + n_window > a.S_total) return hipErrorInvalidValue;

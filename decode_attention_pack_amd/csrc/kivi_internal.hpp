@@ -71,12 +71,14 @@ struct DecodeArgs {
   float sm_scale;        // 1 / sqrt(D)
   int32_t S_total;       // partial slots per (b, hq)
   // Fused decode step (matrix kernel only): t_new >= 0 is the token this
-  // launch appends (t_new = t - 1, t not a multiple of R).  Its key and value
-  // come from k_new / v_new ([B][H][D] fp16) instead of the window slots; the
-  // value it pushes out of the window (token t_new - R, when t_new >= R) is
-  // quantized by the window-role workgroup that attends over it, which stores
-  // it in the cache and then puts the new value into its slot.  t_new = -1:
-  // a plain attention call that writes nothing to the cache.
+  // launch appends (t_new = t - 1).  Its key and value come from k_new /
+  // v_new ([B][H][D] fp16) instead of the window slots; the value it pushes
+  // out of the window (token t_new - R, when t_new >= R) is quantized by the
+  // window-role workgroup that attends over it, which stores it in the cache
+  // and then puts the new value into its slot; when t is a multiple of R,
+  // the window-role workgroups of keys [t - R, t) quantize their key groups
+  // and store them.  t_new = -1: a plain attention call that writes nothing
+  // to the cache.
   const uint16_t *k_new;
   const uint16_t *v_new;
   int64_t t_new;

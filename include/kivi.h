@@ -178,11 +178,11 @@ size_t kivi_decode_attn_workspace_bytes_ex(const kivi_cache *c, int32_t n_q_head
  *   kivi_append(c, k_new, v_new, 1); kivi_decode_attn(c, q, ...).
  * Where the matrix-core kernel takes the shape (2-bit keys and values,
  * head_dim 128, G 32, 1, 2 or 4 query heads per KV head, 16-byte aligned
- * k_new and v_new) and the token completes no key block ((n_tokens + 1) % R
- * != 0), the append runs inside the attention launch: the new key and value
- * are read from k_new / v_new, the value that leaves the window is quantized
- * by the workgroup that attends over it, and the cache writes happen where
- * no other workgroup reads.  Otherwise the two calls above run in turn.
+ * k_new and v_new), the append runs inside the attention launch: the new
+ * key and value are read from k_new / v_new, the value that leaves the
+ * window and a key block the token completes are quantized by the
+ * workgroups that attend over them, and the cache writes happen where no
+ * other workgroup reads.  Otherwise the two calls above run in turn.
  *   k_new_fp16, v_new_fp16  (device) fp16 [B][H][D], the new token.
  *   q_fp16, out             as for kivi_decode_attn.
  *   mask                    (device) f32 [B][n_tokens + 1] or NULL.

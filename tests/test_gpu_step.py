@@ -7,7 +7,7 @@ elementwise, packed stores and window rows bit for bit.
 The sequences cross every case of the fused path: steps before any value
 leaves the window, the first value to leave it, a popped token at a block
 boundary of the attention kernel (n_vq a multiple of 128), and the steps that
-complete a key block (which run as append + attention)."""
+complete a key block (quantized inside the launch)."""
 import numpy as np
 import pytest
 import torch
@@ -58,7 +58,7 @@ def _steps(rep, R, T0, n_steps, masked, kb=2, vb=2, B=2, H=2, D=128, G=32, seed=
 
 
 @pytest.mark.parametrize("rep,R,T0,n_steps", [
-    (4, 128, 120, 150),     # first pops, a key block at 128 and 256, n_vq = 128 at t = 256
+    (4, 128, 120, 150),     # first pops, key blocks at 128 and 256, n_vq = 128 at t = 256
     (1, 32, 3, 80),         # short window: many pops and key blocks
     (2, 64, 500, 70),       # blocks in the block role from the start
     (4, 128, 1, 20),        # nearly empty cache: nothing in the block role
