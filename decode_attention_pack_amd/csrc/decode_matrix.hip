@@ -663,8 +663,9 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
   wait_vm<0>();
   if (pop_here) {
     // KIVI item 3 on the popped value: 16 lanes per 32-channel group, the
-    // quantizer of the pack kernels.  Its codes, scales and zeros replace
-    // what the DMA brought for that row (not yet written) and go to the cache.
+    // bit-exact quantizer (IEEE division, round half to even).  Its codes,
+    // scales and zeros replace what the DMA brought for that row (not yet
+    // written) and go to the cache.
     const float x0 = h2f((uint16_t)(popped & 0xFFFFu)), x1 = h2f((uint16_t)(popped >> 16));
     const float mn = row_min(fminf(x0, x1));
     const float mx = row_max(fmaxf(x0, x1));
