@@ -134,3 +134,30 @@ def test_decode_rejects(L):
     assert call(tps=96) == -1
     assert call(path=5) == -1
     assert L.kivi_decode_attn(None, FAKE, 4, None, FAKE, FAKE, n, None) == -1
+
+
+def test_decode_step_rejects(L):
+    """kivi_decode_step checks every argument before anything runs and leaves
+    the token count unchanged on failure."""
+    c = _cache(n_tokens=300)
+    n = L.kivi_decode_attn_workspace_bytes(ctypes.byref(c), 4)
+    ok = dict(k=FAKE, v=FAKE, q=FAKE, hq=4, out=FAKE, ws=FAKE, nbytes=n)
+
+    def call(cache=c, **kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.kivi_decode_step(ctypes.byref(cache), a["k"], a["v"], a["q"], a["hq"], None,
+                                  a["out"], a["ws"], a["nbytes"], None)
+
+    assert call(k=None) == -1
+    assert call(v=None) == -1
+    assert call(q=None) == -1
+    assert call(out=None) == -1
+    assert call(hq=3) == -1
+    assert call(nbytes=n - 1) == -3
+    assert call(ws=None) == -3
+    full = _cache(n_tokens=1024)
+    assert call(cache=full) == -2
+    assert call(cache=_cache(k_bits=3)) == -1
+    assert c.n_tokens == 300 and full.n_tokens == 1024
+    assert L.kivi_decode_step(None, FAKE, FAKE, FAKE, 4, None, FAKE, FAKE, n, None) == -1
