@@ -81,7 +81,7 @@ typedef struct kivi_cache {
   int32_t group;     /* G: tokens per key group and channels per value group */
   int32_t residual;  /* R: fp16 window length                              */
   int64_t capacity;  /* maximum number of tokens                           */
-  int64_t n_tokens;  /* t: changed only by kivi_append                     */
+  int64_t n_tokens;  /* t: changed only by kivi_append, kivi_decode_step */
   uint32_t *k_codes;
   float *k_scale;
   float *k_zero;
