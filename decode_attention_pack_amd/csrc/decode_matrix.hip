@@ -667,8 +667,8 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
     // scales and zeros replace what the DMA brought for that row (not yet
     // written) and go to the cache.
     const float x0 = h2f((uint16_t)(popped & 0xFFFFu)), x1 = h2f((uint16_t)(popped >> 16));
-    const float mn = row_min(fminf(x0, x1));
-    const float mx = row_max(fmaxf(x0, x1));
+    float mn = first_min(x0, x1), mx = first_max(x0, x1);   // channel 2j comes first
+    lanes_first_min_max(mn, mx, j, 16);
     const float sc = group_scale(mn, mx, 2);
     uint32_t w = (quant_code(x0, mn, sc, 2) | (quant_code(x1, mn, sc, 2) << 2)) << (4 * (j & 7));
     w |= __shfl_xor(w, 1);

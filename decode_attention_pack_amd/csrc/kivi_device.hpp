@@ -32,6 +32,31 @@ struct TokenSource {
   }
 };
 
+// Group minimum and maximum with the rule of a sequential scan in element
+// order: on ties the earlier element wins.  Values only tie with a
+// different bit pattern for +0.0 / -0.0, where the stored zero point (and a
+// constant group's scale) keeps the sign of the first zero, as in the fp32
+// CPU reference.
+__device__ __forceinline__ float first_min(float mn, float x) { return x < mn ? x : mn; }
+__device__ __forceinline__ float first_max(float mx, float x) { return x > mx ? x : mx; }
+
+// The same over aligned groups of `width` lanes (a power of two, at most 64)
+// holding consecutive elements in lane order: a butterfly in which the lane
+// block with the lower indices wins ties, so every lane ends with the result
+// of the sequential scan.
+__device__ __forceinline__ void lanes_first_min_max(float &mn, float &mx, int lane, int width) {
+  for (int o = 1; o < width; o <<= 1) {
+    const float pmn = __shfl_xor(mn, o), pmx = __shfl_xor(mx, o);
+    if ((lane & o) == 0) {   // this lane's block comes first
+      mn = pmn < mn ? pmn : mn;
+      mx = pmx > mx ? pmx : mx;
+    } else {
+      mn = mn < pmn ? mn : pmn;
+      mx = mx > pmx ? mx : pmx;
+    }
+  }
+}
+
 // KIVI item 1: the asymmetric round-to-nearest quantizer, bit-exact with an
 // fp32 CPU reference.  s = (max - min) / (2^B - 1) uses IEEE fp32 division
 // (the HIP default: correctly rounded), the code is round-half-to-even of

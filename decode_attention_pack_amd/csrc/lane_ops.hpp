@@ -24,13 +24,6 @@ __device__ __forceinline__ float row_max(float v) {
   v = fmaxf(v, dpp_mov<0x121>(v));
   return v;
 }
-__device__ __forceinline__ float row_min(float v) {
-  v = fminf(v, dpp_mov<0x128>(v));
-  v = fminf(v, dpp_mov<0x124>(v));
-  v = fminf(v, dpp_mov<0x122>(v));
-  v = fminf(v, dpp_mov<0x121>(v));
-  return v;
-}
 __device__ __forceinline__ float row_sum(float v) {
   v += dpp_mov<0x128>(v);
   v += dpp_mov<0x124>(v);

@@ -124,8 +124,8 @@ key_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t g_first, 
   float mn = v[0], mx = v[0];
 #pragma unroll
   for (int i = 1; i < G; ++i) {
-    mn = fminf(mn, v[i]);
-    mx = fmaxf(mx, v[i]);
+    mn = first_min(mn, v[i]);
+    mx = first_max(mx, v[i]);
   }
   const float s = group_scale(mn, mx, BITS);
   const float r = __builtin_amdgcn_rcpf(s);
@@ -188,8 +188,8 @@ value_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t n_rows,
     float mn = v[0], mx = v[0];
 #pragma unroll
     for (int i = 1; i < G; ++i) {
-      mn = fminf(mn, v[i]);
-      mx = fmaxf(mx, v[i]);
+      mn = first_min(mn, v[i]);
+      mx = first_max(mx, v[i]);
     }
     const float s = group_scale(mn, mx, BITS);
     const float r = __builtin_amdgcn_rcpf(s);
@@ -298,10 +298,7 @@ append_one_kernel(const uint16_t *__restrict__ k_new, const uint16_t *__restrict
     // a copy of channel 0 of their group's wave and write nothing
     const float x = h2f(v_res[on ? slot : (bh * R + t0 % R) * D]);
     float mn = x, mx = x;
-    for (int o = 1; o < G; o <<= 1) {
-      mn = fminf(mn, __shfl_xor(mn, o));
-      mx = fmaxf(mx, __shfl_xor(mx, o));
-    }
+    lanes_first_min_max(mn, mx, c, G);
     const float sc = group_scale(mn, mx, bits);
     const int per = 32 / bits;
     uint32_t w = quant_code(x, mn, sc, bits) << (bits * (c % per));

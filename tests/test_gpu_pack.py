@@ -101,7 +101,17 @@ def _edge_tensor(rng, T, D):
     x[0, 0, :, 4] = np.tile([0.0, 15.0, 0.5, 7.5, 14.5, 3.5, 1.0, 2.5], T // 8)
     x[0, 0, 7, :] = np.tile([0.0, 15.0, 0.5, 7.5, 14.5, 3.5, 1.0, 2.5], D // 8)
     x[0, 0, 9, :] = np.tile([0.0, 3.0, 0.5, 1.5, 2.5, 1.0, 2.0, 0.25], D // 8)
-    return x.astype(np.float16)
+    # signed zeros at the group minimum, in both orders, and all-zero groups
+    # of mixed sign: the stored zero point (and scale) keep the first zero
+    x = x.astype(np.float16)
+    pz, nz = np.float16(0.0), np.float16(-0.0)
+    x[0, 0, :, 6] = np.tile(np.array([pz, nz, 1, 2], np.float16), T // 4)
+    x[0, 0, 32:, 6] = np.tile(np.array([nz, pz, 1, 2], np.float16), (T - 32) // 4)
+    x[0, 0, :, 7] = np.tile(np.array([nz, pz], np.float16), T // 2)
+    x[0, 0, 11, :] = np.tile(np.array([pz, nz, 3, 1], np.float16), D // 4)
+    x[0, 0, 12, :] = np.tile(np.array([nz, pz, 2, 1], np.float16), D // 4)
+    x[0, 0, 13, :] = np.tile(np.array([pz, nz], np.float16), D // 2)
+    return x
 
 
 @pytest.mark.parametrize("bits", [2, 4])

@@ -20,13 +20,33 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 
-def _steps(rep, R, T0, n_steps, masked, kb=2, vb=2, B=2, H=2, D=128, G=32, seed=0):
+def _signed_zeros(X, rng):
+    """Put +0.0 / -0.0 ties at the minimum of some value groups (along
+    channels) and key groups (along tokens), in both orders."""
+    B, H, T, D = X.shape
+    pz, nz = np.float16(0.0), np.float16(-0.0)
+    for tau in rng.choice(T, size=max(1, T // 8), replace=False):
+        c0 = 32 * int(rng.integers(D // 32))
+        X[:, :, tau, c0:c0 + 32] = np.abs(X[:, :, tau, c0:c0 + 32])
+        X[:, :, tau, c0] = pz if tau % 2 else nz
+        X[:, :, tau, c0 + 1] = nz if tau % 2 else pz
+    for c in rng.choice(D, size=4, replace=False):
+        X[:, :, :, c] = np.abs(X[:, :, :, c])
+        X[:, :, 0::32, c] = pz if c % 2 else nz
+        X[:, :, 1::32, c] = nz if c % 2 else pz
+    return X
+
+
+def _steps(rep, R, T0, n_steps, masked, kb=2, vb=2, B=2, H=2, D=128, G=32, seed=0,
+           zeros=False):
     rng = np.random.default_rng(seed + 7 * rep + R + T0)
     t_end = T0 + n_steps
     cap = ((t_end + R - 1) // R) * R
     scale = rng.uniform(0.5, 15, (1, H, 1, D))
     K = (rng.standard_normal((B, H, t_end, D)) * scale).astype(np.float16)
     V = rng.standard_normal((B, H, t_end, D)).astype(np.float16)
+    if zeros:
+        K, V = _signed_zeros(K, rng), _signed_zeros(V, rng)
     g = kivi.Cache(B, H, D, kb, vb, G, R, cap)
     o = oracle.Cache(B, H, D, kb, vb, G, R, cap)
     if T0:
@@ -66,6 +86,14 @@ def _steps(rep, R, T0, n_steps, masked, kb=2, vb=2, B=2, H=2, D=128, G=32, seed=
 ])
 def test_decode_step_matches_oracle(rep, R, T0, n_steps):
     _steps(rep, R, T0, n_steps, masked=False)
+
+
+@pytest.mark.parametrize("rep,R,bits", [(4, 32, 2), (1, 64, 2), (1, 64, 4)])
+def test_decode_step_signed_zeros(rep, R, bits):
+    """Groups whose minimum is a +0.0 / -0.0 tie, quantized by the prefill and
+    by the steps -- inside the fused launch at 2 bits (popped values,
+    completed key blocks), by kivi_append at 4 bits: bit for bit."""
+    _steps(rep, R, 40, 3 * R, masked=False, zeros=True, kb=bits, vb=bits)
 
 
 def test_decode_step_masked():

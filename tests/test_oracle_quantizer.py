@@ -87,6 +87,22 @@ def test_constant_group():
             assert oracle.dequant(0, s, z) == x[0]
 
 
+def test_signed_zero_minimum_keeps_the_first_zero():
+    """Reading of the group minimum for +0.0 / -0.0 ties (the pages leave it
+    open): a scan in element order keeps the first of equal values, so the
+    stored zero point -- and a constant group's scale -- carry the sign of
+    the first zero.  Values are unaffected (+0.0 == -0.0)."""
+    bits_of = lambda v: np.float32(v).view(np.uint32)
+    for first, second in ((0.0, -0.0), (-0.0, 0.0)):
+        x = np.array([first, second] + [1.0, 2.0] * 15, np.float32)
+        codes, s, z = oracle.quantize_group(x, 2)
+        assert bits_of(z) == bits_of(first) and z == 0.0
+        assert codes[:2].tolist() == [0, 0]
+        y = np.array([first, second] * 16, np.float32)      # all zeros, mixed signs
+        codes, s, z = oracle.quantize_group(y, 4)
+        assert bits_of(z) == bits_of(first) and s == 0.0 and not codes.any()
+
+
 def test_tie_breaks_to_even_in_a_full_group():
     """P4: a 32-element group whose ratios hit k + 1/2 exactly."""
     x = np.array([0.0, 3.0] + [0.5, 1.5, 2.5] * 10, np.float32)
