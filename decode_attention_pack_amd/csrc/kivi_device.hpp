@@ -40,6 +40,28 @@ struct TokenSource {
 __device__ __forceinline__ float first_min(float mn, float x) { return x < mn ? x : mn; }
 __device__ __forceinline__ float first_max(float mx, float x) { return x > mx ? x : mx; }
 
+// Group minimum and maximum of v[0..N) with the sequential rule, using the
+// hardware min/max: they can differ from the sequential scan only when the
+// result is a zero (+0.0 / -0.0 ties), and then the scan's answer is the
+// first zero in element order, found by a second pass that rarely runs.
+template <int N>
+__device__ __forceinline__ void group_first_min_max(const float (&v)[N], float &mn, float &mx) {
+  mn = v[0];
+  mx = v[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) {
+    mn = fminf(mn, v[i]);
+    mx = fmaxf(mx, v[i]);
+  }
+  if (mn == 0.0f || mx == 0.0f) {
+    float z = 0.0f;
+    for (int i = N - 1; i >= 0; --i)
+      if (v[i] == 0.0f) z = v[i];        // ends at the first zero
+    if (mn == 0.0f) mn = z;
+    if (mx == 0.0f) mx = z;
+  }
+}
+
 // The same over aligned groups of `width` lanes (a power of two, at most 64)
 // holding consecutive elements in lane order: a butterfly in which the lane
 // block with the lower indices wins ties, so every lane ends with the result

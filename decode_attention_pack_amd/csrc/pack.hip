@@ -121,12 +121,8 @@ key_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t g_first, 
   float v[G];
 #pragma unroll
   for (int i = 0; i < G; ++i) v[i] = h2f(tile[i][c]);
-  float mn = v[0], mx = v[0];
-#pragma unroll
-  for (int i = 1; i < G; ++i) {
-    mn = first_min(mn, v[i]);
-    mx = first_max(mx, v[i]);
-  }
+  float mn, mx;
+  group_first_min_max(v, mn, mx);
   const float s = group_scale(mn, mx, BITS);
   const float r = __builtin_amdgcn_rcpf(s);
   constexpr int per = 32 / BITS;
@@ -185,12 +181,8 @@ value_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t n_rows,
     float v[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) v[i] = h2f(v16[i]);
-    float mn = v[0], mx = v[0];
-#pragma unroll
-    for (int i = 1; i < G; ++i) {
-      mn = first_min(mn, v[i]);
-      mx = first_max(mx, v[i]);
-    }
+    float mn, mx;
+    group_first_min_max(v, mn, mx);
     const float s = group_scale(mn, mx, BITS);
     const float r = __builtin_amdgcn_rcpf(s);
     const int64_t tau = tau_first + r0 + t;
