@@ -182,3 +182,33 @@ def test_decode_step_full_workload(index):
             ref = o.decode_attn(b16(inp["q_steps"][s][b:b + 1, h * rep:(h + 1) * rep]))[0]
             assert_close(outs[s][b, h * rep:(h + 1) * rep], ref, f"{w.name} step {s} b{b} kv{h}")
         compare_slab(g, b, h, o, 0, 0)
+
+
+def test_decode_step_llama2_sequence():
+    """The Llama-2-7B-shaped workload as fused steps: 4064-token prefill, then
+    64 calls of kivi_decode_step.  Step 32 reaches t = 4096, so its launch
+    quantizes a key block and every step pops a value.  Three sampled (batch,
+    head) slabs are checked bit for bit after every step, and their attention
+    against the oracle."""
+    w = synth.WORKLOADS[2]
+    inp = synth.make_inputs(w)
+    g = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
+    say(f"{w.name}: prefill {w.T0} + {w.steps} fused steps")
+    kivi.kivi_append(g, dev(inp["k0"]), dev(inp["v0"]))
+    slabs = [(0, 0), (w.B - 1, w.Hkv - 1), (3, 17)]
+    orc = {}
+    for b, h in slabs:
+        o = oracle.Cache(1, 1, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
+        o.append(b16(inp["k0"][b:b + 1, h:h + 1]), b16(inp["v0"][b:b + 1, h:h + 1]))
+        orc[(b, h)] = o
+    ws = g.new_workspace(w.Hq)
+    for step in range(w.steps):
+        q = inp["q_steps"][step]
+        out = host(kivi.kivi_decode_step(g, dev(inp["k_steps"][step]), dev(inp["v_steps"][step]),
+                                         dev(q), workspace=ws))
+        for (b, h), o in orc.items():
+            o.append(b16(inp["k_steps"][step][b:b + 1, h:h + 1]),
+                     b16(inp["v_steps"][step][b:b + 1, h:h + 1]))
+            compare_slab(g, b, h, o)
+            ref = o.decode_attn(b16(q[b:b + 1, h:h + 1]))
+            assert_close(out[b, h], ref[0, 0], f"step {step} t={g.n_tokens} b{b} h{h}")
