@@ -94,6 +94,22 @@ def test_lengths_around_boundaries(t, rep):
         assert_close(out, ref, f"t={t} rep={rep} path={p}")
 
 
+@pytest.mark.parametrize("R", [32, 96])
+@pytest.mark.parametrize("t", [31, 95, 96, 97, 191, 192, 255, 256, 383, 384, 385, 1000, 2977])
+@pytest.mark.parametrize("rep", [1, 4])
+def test_window_lengths_of_the_ablation(R, t, rep):
+    """Window lengths the pages' ablation uses besides 128: R = 96 is not a
+    multiple of the matrix kernel's 128-token block, so the quantized-key and
+    quantized-value limits fall inside a block."""
+    rng = np.random.default_rng(t * 3 + R + rep)
+    g, o, q = _small_case(rng, 2, 2, rep, 128, 2, 2, 32, R, t)
+    ref = o.decode_attn(b16(q))
+    for p in paths_for(128, 2, 2, 32, R, rep, g.cap):
+        assert_close(host(kivi.kivi_decode_attn(g, dev(q), path=p)), ref, f"R={R} t={t} rep={rep} path={p}")
+    assert_close(host(kivi.kivi_decode_attn(g, dev(q), path=kivi.KIVI_PATH_MATRIX)), ref,
+                 f"R={R} t={t} rep={rep} matrix")
+
+
 @pytest.mark.parametrize("rep", [1, 2, 3, 4, 8, 16])
 @pytest.mark.parametrize("kb,vb", [(2, 2), (4, 4), (2, 4), (4, 2)])
 def test_head_groups_and_bits(rep, kb, vb):

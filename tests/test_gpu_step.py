@@ -83,6 +83,8 @@ def _steps(rep, R, T0, n_steps, masked, kb=2, vb=2, B=2, H=2, D=128, G=32, seed=
     (2, 64, 500, 70),       # blocks in the block role from the start
     (4, 128, 1, 20),        # nearly empty cache: nothing in the block role
     (2, 64, 0, 70),         # the first token of an empty cache, then the first pop
+    (4, 96, 300, 200),      # R = 96: key blocks and pops off the 128-token block grid
+    (1, 96, 0, 200),
 ])
 def test_decode_step_matches_oracle(rep, R, T0, n_steps):
     _steps(rep, R, T0, n_steps, masked=False)
