@@ -99,71 +99,108 @@ write_window_kernel(const uint16_t *__restrict__ k_new, const uint16_t *__restri
 }
 
 // KIVI item 2, fast path for whole groups of a contiguous fp16 input (the
-// pack entry point): one workgroup per (key group, slab).  The G x D tile is
-// staged in LDS with 16-byte loads, then thread c reduces and packs channel c
-// (codes of one channel are contiguous, so the stores coalesce across threads).
-// grid: (n_groups, BH); block: D threads (D a multiple of 64, G * D * 2 bytes
-// of LDS).
+// pack entry point): one wave per (key group, slab).  Lane l reads channels
+// [l D/64, (l + 1) D/64) of the group's G token rows straight from memory --
+// each load instruction of the wave covers one whole row -- then reduces and
+// packs them.  The code words of adjacent channels are adjacent, so the wave
+// stores one contiguous run (16 bytes per lane where the alignment allows).
+// grid: (n_groups, BH); block: 64 threads.
 template <int G, int D, int BITS>
-__global__ void __launch_bounds__(D)
+__global__ void __launch_bounds__(64)
 key_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t g_first, int64_t cap,
                  uint32_t *__restrict__ codes, float *__restrict__ scale,
                  float *__restrict__ zero) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[G][D];
+  constexpr int CPT = D / 64;                       // channels per thread
+  static_assert(CPT == 1 || CPT == 2 || CPT == 4, "head_dim 64, 128 or 256");
   const int64_t bh = blockIdx.y;
   const int64_t g = blockIdx.x;                     // group within the input
-  const uint16_t *src = x + (bh * T_in + g * G) * (int64_t)D;
-  constexpr int kChunks = G * D / 8;                // 16-byte chunks of the tile
-  for (int i = threadIdx.x; i < kChunks; i += D)
-    *(uint4 *)(&tile[0][0] + i * 8) = *(const uint4 *)(src + i * 8);
-  __syncthreads();
-  const int c = threadIdx.x;
-  float v[G];
+  const int c0 = threadIdx.x * CPT;
+  const uint16_t *src = x + (bh * T_in + g * G) * (int64_t)D + c0;
+  float v[CPT][G];
+  if constexpr (CPT == 1) {
+    uint16_t w[G];
 #pragma unroll
-  for (int i = 0; i < G; ++i) v[i] = h2f(tile[i][c]);
-  float mn, mx;
-  group_first_min_max(v, mn, mx);
-  const float s = group_scale(mn, mx, BITS);
-  const float r = __builtin_amdgcn_rcpf(s);
+    for (int i = 0; i < G; ++i) w[i] = src[i * D];
+#pragma unroll
+    for (int i = 0; i < G; ++i) v[0][i] = h2f(w[i]);
+  } else if constexpr (CPT == 2) {
+    uint32_t w[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) w[i] = *(const uint32_t *)(src + i * D);
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      v[0][i] = h2f((uint16_t)(w[i] & 0xffffu));
+      v[1][i] = h2f((uint16_t)(w[i] >> 16));
+    }
+  } else {
+    uint2 w[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) w[i] = *(const uint2 *)(src + i * D);
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      v[0][i] = h2f((uint16_t)(w[i].x & 0xffffu));
+      v[1][i] = h2f((uint16_t)(w[i].x >> 16));
+      v[2][i] = h2f((uint16_t)(w[i].y & 0xffffu));
+      v[3][i] = h2f((uint16_t)(w[i].y >> 16));
+    }
+  }
   constexpr int per = 32 / BITS;
   constexpr int words = G / per;
-  const int64_t sz = (bh * (cap / G) + g_first + g) * D + c;
-  uint32_t *dst = codes + sz * words;
+  const int64_t sz = (bh * (cap / G) + g_first + g) * D + c0;
+  uint32_t out[CPT * words];
+  float sv[CPT], zv[CPT];
 #pragma unroll
-  for (int w = 0; w < words; ++w) {
-    uint32_t word = 0;
+  for (int k = 0; k < CPT; ++k) {
+    float mn, mx;
+    group_first_min_max(v[k], mn, mx);
+    const float s = group_scale(mn, mx, BITS);
+    const float r = __builtin_amdgcn_rcpf(s);
 #pragma unroll
-    for (int e = 0; e < per; ++e) word |= quant_code_r(v[w * per + e], mn, s, r, BITS) << (BITS * e);
-    dst[w] = word;
+    for (int w = 0; w < words; ++w) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < per; ++e)
+        word |= quant_code_r(v[k][w * per + e], mn, s, r, BITS) << (BITS * e);
+      out[k * words + w] = word;
+    }
+    sv[k] = s;
+    zv[k] = mn;
   }
-  scale[sz] = s;
-  zero[sz] = mn;
+  uint32_t *dst = codes + sz * words;
+  if constexpr ((CPT * words) % 4 == 0) {
+    if (((uintptr_t)codes & 15) == 0) {
+#pragma unroll
+      for (int w = 0; w < CPT * words; w += 4)
+        *(uint4 *)(dst + w) = make_uint4(out[w], out[w + 1], out[w + 2], out[w + 3]);
+    } else {
+#pragma unroll
+      for (int w = 0; w < CPT * words; ++w) dst[w] = out[w];
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < CPT * words; ++w) dst[w] = out[w];
+  }
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    scale[sz + k] = sv[k];
+    zero[sz + k] = zv[k];
+  }
 }
 
 // KIVI item 3, fast path for a contiguous fp16 input: one workgroup per 64
-// tokens of one slab.  The 64 x D tile is staged in LDS (rows padded by 16
-// bytes against bank conflicts); thread (group g, token t) then reduces and
-// packs its G channels, so for each group the 64 scales / zeros of the tile
-// are one contiguous store, and the code words of the tile form one
-// contiguous run.  grid: (ceil(n_rows / 64), BH); block: 256.
+// tokens of one slab.  Thread (group g, token t) reads its G channels
+// straight from memory with 16-byte loads, then reduces and packs them, so
+// for each group the 64 scales / zeros of the tile are one contiguous store;
+// the code rows of the tile are staged in LDS and stored as one contiguous
+// run.  grid: (ceil(n_rows / 64), BH); block: 256.
 template <int D, int G, int BITS>
 __global__ void __launch_bounds__(256)
 value_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t n_rows,
                    int64_t tau_first, int64_t cap, uint32_t *__restrict__ codes,
                    float *__restrict__ scale, float *__restrict__ zero) {
-  constexpr int kRow = D + 8;                       // halves per LDS row (16-byte pad)
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * kRow];
   const int64_t bh = blockIdx.y;
   const int64_t r0 = (int64_t)blockIdx.x * 64;
   const int rows = (int)(n_rows - r0 < 64 ? n_rows - r0 : 64);
-  constexpr int kChunks = 64 * D / 8;               // 16-byte chunks of a full tile
-  for (int i = threadIdx.x; i < kChunks; i += 256) {
-    const int t = i / (D / 8), k = i % (D / 8);
-    if (t < rows)
-      *(uint4 *)(tile + t * kRow + k * 8) =
-          *(const uint4 *)(x + (bh * T_in + r0 + t) * (int64_t)D + k * 8);
-  }
-  __syncthreads();
   const int t = threadIdx.x & 63;
   constexpr int per = 32 / BITS;
   constexpr int n_groups = D / G;
@@ -173,11 +210,12 @@ value_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t n_rows,
   __shared__ __attribute__((aligned(16))) uint32_t out_s[64 * kWords];
   for (int g = threadIdx.x >> 6; g < n_groups; g += 4) {
     if (t >= rows) continue;
-    // the group's G channels, 8 per 16-byte LDS read
+    // the group's G channels of token t, straight from memory
     uint16_t v16[G];
+    const uint16_t *src = x + (bh * T_in + r0 + t) * (int64_t)D + g * G;
 #pragma unroll
     for (int k = 0; k < G / 8; ++k)
-      *(uint4 *)(v16 + 8 * k) = *(const uint4 *)(tile + t * kRow + g * G + 8 * k);
+      *(uint4 *)(v16 + 8 * k) = *(const uint4 *)(src + 8 * k);
     float v[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) v[i] = h2f(v16[i]);
@@ -225,10 +263,10 @@ hipError_t launch_key_tiles(const uint16_t *x, int64_t T_in, int64_t n_rows, int
 #define KIVI_KT(GG, DD)                                                                        \
   if (G == GG && D == DD) {                                                                     \
     if (bits == 2)                                                                              \
-      hipLaunchKernelGGL((key_tiles_kernel<GG, DD, 2>), grid, dim3(DD), 0, s, x, T_in,        \
+      hipLaunchKernelGGL((key_tiles_kernel<GG, DD, 2>), grid, dim3(64), 0, s, x, T_in,        \
                          g_first, cap, codes, scale, zero);                                     \
     else                                                                                        \
-      hipLaunchKernelGGL((key_tiles_kernel<GG, DD, 4>), grid, dim3(DD), 0, s, x, T_in,        \
+      hipLaunchKernelGGL((key_tiles_kernel<GG, DD, 4>), grid, dim3(64), 0, s, x, T_in,        \
                          g_first, cap, codes, scale, zero);                                     \
     return hipGetLastError();                                                                   \
   }
