@@ -170,8 +170,9 @@ def main():
                          "many MiB (a known-size reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the KIVI decode path "
-                                   "needs no collectives (see DESIGN.md for how it would shard)",
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: each GPU of a "
+                                   "multi-GPU deployment holds whole (batch row, KV head) slabs "
+                                   "and decodes them with no collectives",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
