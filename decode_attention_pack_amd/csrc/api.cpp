@@ -47,10 +47,17 @@ int check_shape(int32_t D, int32_t bits, int32_t G, const char *who) {
   return KIVI_OK;
 }
 
+// Slabs (batch rows x heads) index the second grid dimension of the pack and
+// append kernels, whose limit is 65535 workgroups.
+constexpr int64_t kMaxSlabs = 65535;
+
 int check_cache(const kivi_cache *c, const char *who) {
   if (!c) return fail(KIVI_ERR_INVALID_ARG, "%s: cache is NULL", who);
   if (c->batch <= 0 || c->n_kv_heads <= 0)
     return fail(KIVI_ERR_INVALID_ARG, "%s: batch and n_kv_heads must be positive", who);
+  if ((int64_t)c->batch * c->n_kv_heads > kMaxSlabs)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: batch x n_kv_heads = %lld passes %lld", who,
+                (long long)c->batch * c->n_kv_heads, (long long)kMaxSlabs);
   int rc = check_shape(c->head_dim, c->k_bits, c->group, who);
   if (rc) return rc;
   rc = check_shape(c->head_dim, c->v_bits, c->group, who);
@@ -74,6 +81,9 @@ int check_pack(const void *x, int32_t B, int32_t H, int64_t T, int32_t D, int32_
                const void *codes, const void *scale, const void *zero, int64_t cap, int64_t off,
                bool keys, const char *who) {
   if (B <= 0 || H <= 0) return fail(KIVI_ERR_INVALID_ARG, "%s: B and H must be positive", who);
+  if ((int64_t)B * H > kMaxSlabs)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: B x H = %lld passes %lld", who, (long long)B * H,
+                (long long)kMaxSlabs);
   int rc = check_shape(D, bits, G, who);
   if (rc) return rc;
   if (T < 0 || off < 0) return fail(KIVI_ERR_INVALID_ARG, "%s: T and offset must be >= 0", who);

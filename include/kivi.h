@@ -71,7 +71,8 @@ enum {
  * cache has n_tokens = 0 and needs no initialisation of its arrays.
  * Constraints: k_bits, v_bits in {2, 4}; group % (32/bits) == 0 for both;
  * head_dim % group == 0 and head_dim <= 256; residual % group == 0;
- * capacity % residual == 0; 0 <= n_tokens <= capacity. */
+ * capacity % residual == 0; 0 <= n_tokens <= capacity;
+ * batch * n_kv_heads <= 65535. */
 typedef struct kivi_cache {
   int32_t batch;
   int32_t n_kv_heads;
@@ -99,8 +100,8 @@ typedef struct kivi_cache {
  *            / k_zero layout above, sized for `dst_capacity` tokens.
  *   The T tokens become destination tokens [dst_token_offset,
  *   dst_token_offset + T).  Requires T % group == 0, dst_token_offset %
- *   group == 0, dst_capacity % group == 0 and the range inside the capacity.
- *   T == 0 is a no-op. */
+ *   group == 0, dst_capacity % group == 0, the range inside the capacity and
+ *   B * H <= 65535.  T == 0 is a no-op. */
 int kivi_pack_keys(const void *k_fp16, int32_t B, int32_t H, int64_t T, int32_t D,
                    int32_t bits, int32_t group, uint32_t *codes, float *scale,
                    float *zero, int64_t dst_capacity, int64_t dst_token_offset,
@@ -111,7 +112,9 @@ int kivi_pack_keys(const void *k_fp16, int32_t B, int32_t H, int64_t T, int32_t 
  *   v_fp16   (device) fp16 [B][H][T][D].
  *   codes, scale, zero  (device) destination arrays in the v_codes / v_scale
  *            / v_zero layout above, sized for `dst_capacity` tokens.
- *   Tokens go to rows [dst_token_offset, dst_token_offset + T). */
+ *   Tokens go to rows [dst_token_offset, dst_token_offset + T); the same
+ *   constraints on shapes and B * H as for keys, without the multiples of
+ *   the group on T and the offset. */
 int kivi_pack_values(const void *v_fp16, int32_t B, int32_t H, int64_t T, int32_t D,
                      int32_t bits, int32_t group, uint32_t *codes, float *scale,
                      float *zero, int64_t dst_capacity, int64_t dst_token_offset,

@@ -56,6 +56,7 @@ def _pack(L, fn, **kw):
     (dict(bits=3), -1), (dict(bits=8), -1), (dict(G=24), -1), (dict(D=100), -1),
     (dict(D=512), -1), (dict(T=33), -1), (dict(off=16), -1), (dict(cap=100), -1),
     (dict(T=-1), -1), (dict(B=0), -1), (dict(T=96, off=64), -2), (dict(x=None), -1),
+    (dict(B=65536), -1), (dict(B=256, H=256), -1),
 ])
 def test_pack_keys_rejects(L, kw, status):
     assert _pack(L, "kivi_pack_keys", **kw) == status
@@ -87,7 +88,8 @@ def _cache(**kw):
 
 @pytest.mark.parametrize("kw", [dict(k_bits=3), dict(v_bits=5), dict(residual=48),
                                 dict(capacity=1000), dict(n_tokens=-1), dict(n_tokens=2048),
-                                dict(batch=0), dict(head_dim=100), dict(group=20)])
+                                dict(batch=0), dict(head_dim=100), dict(group=20),
+                                dict(batch=32768, n_kv_heads=2)])
 def test_append_rejects_bad_cache(L, kw):
     c = _cache(**kw)
     assert L.kivi_append(ctypes.byref(c), FAKE, FAKE, 1, None) == -1
