@@ -141,3 +141,21 @@ def test_pack_full_prefill(index):
             ref = fn(b16(x[b:b + 1, h:h + 1]), w.k_bits, w.G, cap=cap)
             for g_, r_ in zip(got, ref):
                 assert _same(g_[b:b + 1, h:h + 1], r_), (keys, b, h)
+
+
+def test_pack_most_slabs():
+    """65535 slabs (batch x heads), the most a pack call accepts: every slab
+    is one workgroup row of the launch grid.  Three sampled slabs against the
+    oracle, bit for bit (one slab more is rejected on the host, which the
+    ABI tests check)."""
+    rng = np.random.default_rng(65535)
+    B, H, T, D, G, bits = 65535, 1, 32, 64, 32, 2
+    x = rng.standard_normal((B, H, T, D)).astype(np.float16)
+    say(f"pack {B} slabs of {T} tokens")
+    for keys in (True, False):
+        got = _gpu_pack(x, bits, G, T, 0, keys)
+        fn = oracle.pack_keys if keys else oracle.pack_values
+        for b in (0, B // 2 + 7, B - 1):
+            ref = fn(b16(x[b:b + 1]), bits, G, cap=T, offset=0)
+            for g_, r_ in zip(got, ref):
+                assert _same(g_[b:b + 1], r_), (keys, b)
