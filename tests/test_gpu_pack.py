@@ -57,7 +57,8 @@ def test_pack_small(bits, G, D):
 
 
 @pytest.mark.parametrize("bits,G,D", [(2, 16, 256), (4, 16, 64), (2, 48, 96), (4, 8, 64),
-                                      (2, 128, 256), (4, 64, 256)])
+                                      (2, 128, 256), (4, 64, 256), (2, 32, 256), (4, 32, 256),
+                                      (4, 16, 256)])
 def test_pack_other_shapes(bits, G, D):
     """Shapes on both sides of the fast-path limits (power-of-two G <= 64, at
     most 16 KB per key tile, D in {64, 128, 256}); the rest take the general
