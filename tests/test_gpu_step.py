@@ -214,3 +214,34 @@ def test_decode_step_llama2_sequence():
             compare_slab(g, b, h, o)
             ref = o.decode_attn(b16(q[b:b + 1, h:h + 1]))
             assert_close(out[b, h], ref[0, 0], f"step {step} t={g.n_tokens} b{b} h{h}")
+
+
+def test_decode_step_32k_key_block():
+    """The 32k GQA workload's shape from 8 tokens before a key-block boundary:
+    ten fused steps, the eighth of which completes the block (t = 33024) and
+    quantizes it inside the launch.  Three sampled slabs bit for bit after
+    every step, and their attention against the oracle."""
+    w = synth.WORKLOADS[4].replace(T0=33024 - 8, steps=10)
+    assert (w.T0 + 8) % w.R == 0
+    inp = synth.make_inputs(w)
+    g = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
+    say(f"{w.name}: prefill {w.T0} + {w.steps} fused steps across t = {w.T0 + 8}")
+    kivi.kivi_append(g, dev(inp["k0"]), dev(inp["v0"]))
+    rep = w.Hq // w.Hkv
+    slabs = [(0, 0), (w.B - 1, w.Hkv - 1), (2, 5)]
+    orc = {}
+    for b, h in slabs:
+        o = oracle.Cache(1, 1, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
+        o.append(b16(inp["k0"][b:b + 1, h:h + 1]), b16(inp["v0"][b:b + 1, h:h + 1]))
+        orc[(b, h)] = o
+    ws = g.new_workspace(w.Hq)
+    for step in range(w.steps):
+        q = inp["q_steps"][step]
+        out = host(kivi.kivi_decode_step(g, dev(inp["k_steps"][step]), dev(inp["v_steps"][step]),
+                                         dev(q), workspace=ws))
+        for (b, h), o in orc.items():
+            o.append(b16(inp["k_steps"][step][b:b + 1, h:h + 1]),
+                     b16(inp["v_steps"][step][b:b + 1, h:h + 1]))
+            compare_slab(g, b, h, o)
+            ref = o.decode_attn(b16(q[b:b + 1, h * rep:(h + 1) * rep]))[0]
+            assert_close(out[b, h * rep:(h + 1) * rep], ref, f"step {step} t={g.n_tokens} b{b} kv{h}")
