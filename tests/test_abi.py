@@ -163,3 +163,13 @@ def test_decode_step_rejects(L):
     assert call(cache=_cache(k_bits=3)) == -1
     assert c.n_tokens == 300 and full.n_tokens == 1024
     assert L.kivi_decode_step(None, FAKE, FAKE, FAKE, 4, None, FAKE, FAKE, n, None) == -1
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without libkivi.so every call raises; nothing falls back to another
+    implementation."""
+    from decode_attention_pack_amd import kivi
+    monkeypatch.setattr(kivi, "_lib", None)
+    monkeypatch.setattr(kivi, "LIB_PATH", str(tmp_path / "libkivi.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        kivi.lib()
