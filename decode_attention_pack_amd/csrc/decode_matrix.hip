@@ -214,17 +214,6 @@ __device__ __forceinline__ void codes_to_b(uint32_t x, h8 &be, h8 &bo) {
   bo = (h8){o0[0], o0[1], o1[0], o1[1], o2[0], o2[1], o3[0], o3[1]};
 }
 
-// Schedule of a block's 64 products: each MFMA is followed by three VALU
-// instructions (the code conversions of a later MFMA group among them), so
-// the vector unit issues while the matrix core works instead of after it.
-__device__ __forceinline__ void mfma_valu_interleave() {
-#pragma unroll
-  for (int k = 0; k < 64; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
-  }
-}
-
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -443,7 +432,6 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
         }
       }
     }
-    mfma_valu_interleave();
     wave_lds_sync();
 
     // scores (even / odd token of each pair) and online softmax, head h_s
@@ -540,7 +528,6 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
         }
       }
     }
-    mfma_valu_interleave();
   }
 
   // ---- write the partial (acc[128], m, l) of each query head
