@@ -128,7 +128,7 @@ __device__ __forceinline__ float uniform(float v) {
 // grid: (n_splits, H * head_chunks, B); block: 256 (4 waves).
 template <int KB, int VB, int NH>
 __global__ void __launch_bounds__(kVThreads)
-    __attribute__((amdgpu_waves_per_eu(NH == 1 ? 3 : 2)))   // one head: 3 waves per SIMD
+    __attribute__((amdgpu_waves_per_eu(2)))   // two waves per SIMD: the compiler may use 256 VGPRs
 decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int direct) {
   __shared__ float red_s[kVWaves][NH][kVD];
   __shared__ float stat_s[kVWaves][NH][2];
