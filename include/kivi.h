@@ -161,7 +161,8 @@ int kivi_decode_attn(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads,
  *                     the scalar kernel), KIVI_PATH_GENERIC (scalar kernel
  *                     for every token), KIVI_PATH_MATRIX (matrix-core
  *                     kernel: 2-bit codes, head_dim 128, G 32, 1, 2 or 4
- *                     query heads per KV head) or KIVI_PATH_VECTOR (vector
+ *                     query heads per KV head, capacity below 2^29 tokens,
+ *                     16-byte aligned q) or KIVI_PATH_VECTOR (vector
  *                     kernel: 2- or 4-bit codes, head_dim 128, G 32, R a
  *                     multiple of 32, 1 or 2 query heads per KV head,
  *                     capacity below 2^26 tokens).  A
@@ -180,8 +181,9 @@ size_t kivi_decode_attn_workspace_bytes_ex(const kivi_cache *c, int32_t n_q_head
  * (within the attention tolerance) the same output as
  *   kivi_append(c, k_new, v_new, 1); kivi_decode_attn(c, q, ...).
  * Where the matrix-core kernel takes the shape (2-bit keys and values,
- * head_dim 128, G 32, 1, 2 or 4 query heads per KV head, 16-byte aligned
- * k_new and v_new), the append runs inside the attention launch: the new
+ * head_dim 128, G 32, 1, 2 or 4 query heads per KV head, capacity below
+ * 2^29 tokens, 16-byte aligned q, k_new and v_new), the append runs inside
+ * the attention launch: the new
  * key and value are read from k_new / v_new, the value that leaves the
  * window and a key block the token completes are quantized by the
  * workgroups that attend over them, and the cache writes happen where no
