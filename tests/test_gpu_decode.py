@@ -255,3 +255,29 @@ def test_vector_path_rejects_other_shapes():
     g, _, q = _small_case(rng, 1, 2, 4, 128, 2, 2, 32, 128, 300)
     with pytest.raises(kivi.KiviError):
         kivi.kivi_decode_attn(g, dev(q), path=kivi.KIVI_PATH_VECTOR)
+
+
+def test_most_slabs_append_and_decode():
+    """65535 slabs (batch x KV heads), the most a cache may hold: prefill,
+    one appended token, and attention through every path the shape allows,
+    checked on three sampled slabs against the oracle."""
+    rng = np.random.default_rng(4242)
+    B, H, D, G, R, t0 = 65535, 1, 128, 32, 32, 40
+    cap = 64
+    K = rng.standard_normal((B, H, t0 + 1, D), dtype=np.float32).astype(np.float16)
+    V = rng.standard_normal((B, H, t0 + 1, D), dtype=np.float32).astype(np.float16)
+    q = rng.standard_normal((B, H, D), dtype=np.float32).astype(np.float16)
+    say(f"{B} slabs: prefill {t0} + 1 token")
+    g = kivi.Cache(B, H, D, 2, 2, G, R, cap)
+    kivi.kivi_append(g, dev(K[:, :, :t0]), dev(V[:, :, :t0]))
+    kivi.kivi_append(g, dev(K[:, :, t0:]), dev(V[:, :, t0:]))
+    outs = {p: host(kivi.kivi_decode_attn(g, dev(q), path=p))
+            for p in paths_for(D, 2, 2, G, R, 1, cap) + [kivi.KIVI_PATH_MATRIX]}
+    for b in (0, B // 2 + 3, B - 1):
+        o = oracle.Cache(1, 1, D, 2, 2, G, R, cap)
+        o.append(b16(K[b:b + 1, :, :t0]), b16(V[b:b + 1, :, :t0]))
+        o.append(b16(K[b:b + 1, :, t0:]), b16(V[b:b + 1, :, t0:]))
+        compare_slab(g, b, 0, o)
+        ref = o.decode_attn(b16(q[b:b + 1]))
+        for p, out in outs.items():
+            assert_close(out[b:b + 1], ref, f"slab {b} path {p}")
