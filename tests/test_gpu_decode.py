@@ -281,3 +281,29 @@ def test_most_slabs_append_and_decode():
         ref = o.decode_attn(b16(q[b:b + 1]))
         for p, out in outs.items():
             assert_close(out[b:b + 1], ref, f"slab {b} path {p}")
+
+
+def test_llama3_gqa_32k_masked():
+    """The full 32k GQA workload with an additive mask (a fifth of the tokens
+    at -inf, the rest N(0, 1)): the masked instantiation of the matrix kernel,
+    whose workgroups stage each block's mask row by DMA, against the oracle on
+    three sampled slabs."""
+    w = synth.WORKLOADS[4]
+    inp = synth.make_inputs(w)
+    g = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
+    say(f"{w.name}: prefill {w.T0} + 1 step, masked")
+    kivi.kivi_append(g, dev(inp["k0"]), dev(inp["v0"]))
+    kivi.kivi_append(g, dev(inp["k_steps"][0]), dev(inp["v_steps"][0]))
+    t = g.n_tokens
+    rng = np.random.default_rng(77)
+    mask = np.where(rng.random((w.B, t)) < 0.2, -np.inf,
+                    rng.standard_normal((w.B, t))).astype(np.float32)
+    q = inp["q_steps"][0]
+    rep = w.Hq // w.Hkv
+    out = host(kivi.kivi_decode_attn(g, dev(q), mask=dev(mask)))
+    for b, h in [(0, 0), (w.B - 1, w.Hkv - 1), (2, 5)]:
+        o = oracle.Cache(1, 1, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
+        o.append(b16(inp["k0"][b:b + 1, h:h + 1]), b16(inp["v0"][b:b + 1, h:h + 1]))
+        o.append(b16(inp["k_steps"][0][b:b + 1, h:h + 1]), b16(inp["v_steps"][0][b:b + 1, h:h + 1]))
+        ref = o.decode_attn(b16(q[b:b + 1, h * rep:(h + 1) * rep]), mask[b:b + 1])[0]
+        assert_close(out[b, h * rep:(h + 1) * rep], ref, f"masked b{b} kv{h}")
