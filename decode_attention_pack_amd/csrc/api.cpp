@@ -160,7 +160,8 @@ Plan make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
     }
     p.tps_matrix = (int)tps;
     p.n_split_matrix = (int)((p.n_main + tps - 1) / tps);
-    p.S_total = p.n_split_matrix + p.n_window;
+    // two waves per split, one partial slot each
+    p.S_total = 2 * p.n_split_matrix + p.n_window;
     return p;
   }
   p.vector = (path == KIVI_PATH_AUTO || path == KIVI_PATH_VECTOR) &&
@@ -187,9 +188,10 @@ Plan make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
 int64_t max_slots(const kivi_cache *c, int32_t tps_req) {
   // automatic plans split at least kMatrixBlock tokens at a time
   const int64_t step = tps_req > 0 ? tps_req : kMatrixBlock;
-  // splits over the capacity, plus the matrix kernel's window chunks (its
-  // window is at most one block + R tokens long)
-  return (c->capacity + step - 1) / step + (kMatrixBlock + (int64_t)c->residual + 31) / 32 + 1;
+  // splits over the capacity (two partial slots per matrix-kernel split),
+  // plus the matrix kernel's window chunks (its window is at most one block +
+  // R tokens long)
+  return 2 * ((c->capacity + step - 1) / step) + (kMatrixBlock + (int64_t)c->residual + 31) / 32 + 1;
 }
 
 

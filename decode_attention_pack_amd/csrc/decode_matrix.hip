@@ -266,20 +266,29 @@ struct Lds {
 // [split * tps, min(n_main, (split + 1) * tps)) in blocks of 128.
 template <int NREP, bool MASKED>
 __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, int tps,
-                                           int split, int hk, int b, const Lds &L,
+                                           int split, int wave, int hk, int b, const Lds &L,
                                            KStage *__restrict__ kbuf,
                                            VStage *__restrict__ vbuf) {
   static_assert(NREP == 1 || NREP == 2 || NREP == 4, "query heads per KV head");
   constexpr int GA = 16 / NREP;       // key groups per A operand
   constexpr int KDMA = kStageDma + (MASKED ? 2 : 0);
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int i = lane & 15;
   const int kg = lane >> 4;
   const int64_t bh = (int64_t)b * a.H + hk;
   const int64_t blk_begin = (int64_t)split * tps / kBT;
   int64_t blk_end = ((int64_t)split + 1) * tps / kBT;
   if (blk_end * kBT > n_main) blk_end = n_main / kBT;
+  if (blk_end - blk_begin <= wave) {
+    // a one-block split leaves the second wave nothing: an empty partial
+    if (lane < NREP) {
+      float *dst = a.part + (((int64_t)b * a.Hq + hk * NREP + lane) * a.S_total + 2 * split + wave) *
+                                (kD + 4);
+      *(float2 *)(dst + kD) = make_float2(-INFINITY, 0.0f);
+    }
+    return;
+  }
 
   // --- roles of this lane
   // key A operand: row m = i is (head h_a, key group g_a)
@@ -312,8 +321,14 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
   const int64_t nblk = blk_end - blk_begin;
   const int64_t rot =
       (int64_t)((((uint32_t)bh * 2654435761u) ^ ((uint32_t)split * 2246822519u)) >> 8) % nblk;
-  stage_keys<MASKED>(a, bh, blk_begin + rot, kbuf, L.mask, dmo, lane);
-  stage_values(a, bh, blk_begin + rot, vbuf, dmo);
+  // The two waves of the workgroup share the split: wave w takes the blocks
+  // at positions w, w + 2, ... of the rotated order and writes partial slot
+  // 2 split + w.
+  const int slot = 2 * split + wave;
+  const int64_t nb_w = (nblk - wave + 1) / 2;
+  const int64_t first = blk_begin + (wave + rot) % nblk;
+  stage_keys<MASKED>(a, bh, first, kbuf, L.mask, dmo, lane);
+  stage_values(a, bh, first, vbuf, dmo);
   wait_vm<KDMA + kStageDma>();
 
   // q of head h_a at this lane's 32 key channels c0(ks) + j, with
@@ -364,9 +379,9 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
 #pragma unroll
   for (int g = 0; g < 4; ++g) dv[g][0] = dv[g][1] = (f4){0, 0, 0, 0};
 
-  for (int64_t it = 0; it < nblk; ++it) {
-    const bool has_next = it + 1 < nblk;
-    const int64_t nxt = blk_begin + (it + 1 + rot) % nblk;   // the block staged next
+  for (int64_t it = 0; it < nb_w; ++it) {
+    const bool has_next = it + 1 < nb_w;
+    const int64_t nxt = blk_begin + (wave + 2 * (it + 1) + rot) % nblk;   // the block staged next
     // ================= key half =================
     wait_vm<kStageDma>();            // key part of this block in; its value part may still fly
     const KStage &kst = *kbuf;
@@ -539,7 +554,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
   const int slot_stride = kD + 4;
   if (v_valid) {
     const f4 z4 = *(const f4 *)(L.bias + 4 * kg);
-    float *dst = a.part + (((int64_t)b * a.Hq + hk * NREP + kg) * a.S_total + split) * slot_stride;
+    float *dst = a.part + (((int64_t)b * a.Hq + hk * NREP + kg) * a.S_total + slot) * slot_stride;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       *(float2 *)(dst + 32 * g + 2 * i) =
@@ -547,7 +562,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
     }
   }
   if (k_valid && i == 0) {
-    float *dst = a.part + (((int64_t)b * a.Hq + hk * NREP + h_s) * a.S_total + split) * slot_stride;
+    float *dst = a.part + (((int64_t)b * a.Hq + hk * NREP + h_s) * a.S_total + slot) * slot_stride;
     *(float2 *)(dst + kD) = make_float2(m_run == -INFINITY ? -INFINITY : m_run * 0.6931471805599453f,
                                         l_head);
   }
@@ -561,7 +576,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
 template <int NREP, bool MASKED>
 __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main, int chunk,
                                             int slot, int hk, int b, const Lds &L) {
-  const int j = threadIdx.x;
+  const int j = threadIdx.x & 63;
   const int64_t bh = (int64_t)b * a.H + hk;
   const int64_t Ta = n_main + (int64_t)kWT * chunk;
   const int64_t Tb = Ta + kWT < a.t ? Ta + kWT : a.t;
@@ -816,35 +831,39 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
   }
 }
 
-// grid: n_window * H * B + n_split * H * B workgroups of one wave, in one
-// dimension.  All window-role workgroups come first (chunk fastest, then KV
-// head, then batch), so every one of them starts with the first workgroups
-// and finishes under the longer block role instead of trailing it; then the
-// block-role workgroups (split fastest, then KV head, then batch).
+// grid: ceil(n_window / 2) * H * B + n_split * H * B workgroups of two
+// waves, in one dimension.  All window-role workgroups come first (chunk pair
+// fastest, then KV head, then batch), so every one of them starts with the
+// first workgroups and finishes under the longer block role instead of
+// trailing it; then the block-role workgroups (split fastest, then KV head,
+// then batch).  Each wave has LDS of its own and never waits for the other.
 // The masked variant holds the block's mask in registers as well; it may use
 // more than half the register file (one wave per SIMD) rather than spill, since
 // a spill reload inside the block loop would wait for every DMA in flight.
 template <int NREP, bool MASKED>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MASKED ? 1 : 2)))
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(MASKED ? 1 : 2)))
 decode_matrix_kernel(DecodeArgs a, int64_t n_main, int tps, int n_split, int n_window) {
-  __shared__ KStage sm_k;
-  __shared__ VStage sm_v;
-  __shared__ __attribute__((aligned(16))) float sm_p[4][kPRow];
-  __shared__ __attribute__((aligned(16))) float sm_mask[kBT];
-  __shared__ __attribute__((aligned(16))) float sm_bias[16];
-  __shared__ __attribute__((aligned(16))) float sm_alpha[4];
-  const Lds L{&sm_k, &sm_v, sm_p, sm_mask, sm_bias, sm_alpha};
+  __shared__ KStage sm_k[2];
+  __shared__ VStage sm_v[2];
+  __shared__ __attribute__((aligned(16))) float sm_p[2][4][kPRow];
+  __shared__ __attribute__((aligned(16))) float sm_mask[2][kBT];
+  __shared__ __attribute__((aligned(16))) float sm_bias[2][16];
+  __shared__ __attribute__((aligned(16))) float sm_alpha[2][4];
+  const int w = threadIdx.x >> 6;
+  const Lds L{&sm_k[w], &sm_v[w], sm_p[w], sm_mask[w], sm_bias[w], sm_alpha[w]};
   const uint32_t lin = blockIdx.x;
-  const uint32_t n_win_all = (uint32_t)n_window * (uint32_t)(a.H * a.B);
+  const uint32_t n_pairs = ((uint32_t)n_window + 1) / 2;
+  const uint32_t n_win_all = n_pairs * (uint32_t)(a.H * a.B);
   if (lin < n_win_all) {
-    const uint32_t x = lin % (uint32_t)n_window, r = lin / (uint32_t)n_window;
-    window_role<NREP, MASKED>(a, n_main, (int)x, n_split + (int)x, (int)(r % (uint32_t)a.H),
-                              (int)(r / (uint32_t)a.H), L);
+    const uint32_t x = 2 * (lin % n_pairs) + (uint32_t)w, r = lin / n_pairs;
+    if (x < (uint32_t)n_window)
+      window_role<NREP, MASKED>(a, n_main, (int)x, 2 * n_split + (int)x, (int)(r % (uint32_t)a.H),
+                                (int)(r / (uint32_t)a.H), L);
   } else {
     const uint32_t l2 = lin - n_win_all;
     const uint32_t split = l2 % (uint32_t)n_split, r = l2 / (uint32_t)n_split;
-    block_role<NREP, MASKED>(a, n_main, tps, (int)split, (int)(r % (uint32_t)a.H),
-                             (int)(r / (uint32_t)a.H), L, &sm_k, &sm_v);
+    block_role<NREP, MASKED>(a, n_main, tps, (int)split, w, (int)(r % (uint32_t)a.H),
+                             (int)(r / (uint32_t)a.H), L, &sm_k[w], &sm_v[w]);
   }
 }
 
@@ -864,10 +883,10 @@ template <int NREP>
 static void launch_rep(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main, int tps,
                        int n_splits, int n_window) {
   if (a.mask)
-    hipLaunchKernelGGL((decode_matrix_kernel<NREP, true>), grid, dim3(64), 0, s, a, n_main, tps,
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, true>), grid, dim3(128), 0, s, a, n_main, tps,
                        n_splits, n_window);
   else
-    hipLaunchKernelGGL((decode_matrix_kernel<NREP, false>), grid, dim3(64), 0, s, a, n_main, tps,
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, false>), grid, dim3(128), 0, s, a, n_main, tps,
                        n_splits, n_window);
 }
 
@@ -893,9 +912,9 @@ hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int tokens_
     if (a.t % a.R == 0 && n_main > a.t - a.R) return hipErrorInvalidValue;
   }
   const int n_window = decode_matrix_window_chunks(a, n_main);
-  if (n_splits + n_window <= 0 || n_splits + n_window > a.S_total) return hipErrorInvalidValue;
-  const int64_t n_wg = ((int64_t)n_window + n_splits) * a.H * a.B;
-  if (n_wg > ((int64_t)1 << 26)) return hipErrorInvalidValue;   // 64-thread groups, 32-bit ids
+  if (n_splits + n_window <= 0 || 2 * n_splits + n_window > a.S_total) return hipErrorInvalidValue;
+  const int64_t n_wg = (((int64_t)n_window + 1) / 2 + n_splits) * a.H * a.B;
+  if (n_wg > ((int64_t)1 << 25)) return hipErrorInvalidValue;   // 128-thread groups, 32-bit ids
   dim3 grid((unsigned)n_wg);
   switch (a.n_rep) {
     case 1: launch_rep<1>(a, grid, s, n_main, tokens_per_split, n_splits, n_window); break;
