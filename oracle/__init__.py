@@ -44,6 +44,10 @@ def _load():
     i32, i64 = ctypes.c_int32, ctypes.c_int64
     lib.kivi_oracle_half_to_float.argtypes = [ctypes.c_uint16]
     lib.kivi_oracle_half_to_float.restype = ctypes.c_float
+    lib.kivi_oracle_float_to_half.argtypes = [ctypes.c_float, P]
+    lib.kivi_oracle_float_to_half.restype = ctypes.c_int
+    lib.kivi_oracle_record_bytes.argtypes = [i32, i32, i32, i32]
+    lib.kivi_oracle_record_bytes.restype = i64
     lib.kivi_oracle_quantize_group.argtypes = [P, i32, i32, P, P, P]
     lib.kivi_oracle_quantize_group.restype = None
     lib.kivi_oracle_dequant.argtypes = [ctypes.c_uint32, ctypes.c_float, ctypes.c_float]
@@ -54,7 +58,7 @@ def _load():
     lib.kivi_oracle_unpack_codes.restype = None
     for name in ("kivi_oracle_pack_keys", "kivi_oracle_pack_values"):
         fn = getattr(lib, name)
-        fn.argtypes = [P, i32, i32, i64, i32, i32, i32, P, P, P, i64, i64]
+        fn.argtypes = [P, P, i64, i64]
         fn.restype = ctypes.c_int
     lib.kivi_oracle_append.argtypes = [P, P, P, i64]
     lib.kivi_oracle_append.restype = ctypes.c_int
@@ -83,10 +87,59 @@ class _CCache(ctypes.Structure):
         ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32), ("group", ctypes.c_int32),
         ("residual", ctypes.c_int32),
         ("capacity", ctypes.c_int64), ("n_tokens", ctypes.c_int64),
-        ("k_codes", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("k_zero", ctypes.c_void_p),
-        ("v_codes", ctypes.c_void_p), ("v_scale", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
-        ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
+        ("blocks", ctypes.c_void_p), ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
     ]
+
+
+TOKENS_PER_RECORD = 128
+
+
+def record_bytes(D: int, kb: int, vb: int, G: int) -> int:
+    """Bytes of one 128-token record (0 for a shape the layout does not take)."""
+    return int(_load().kivi_oracle_record_bytes(D, kb, vb, G))
+
+
+def record_sections(D: int, kb: int, vb: int, G: int):
+    """(name, byte offset, byte size) of the sections of a record, in order."""
+    n, g = TOKENS_PER_RECORD, TOKENS_PER_RECORD // G
+    sizes = [("k_codes", n * D * kb // 8), ("k_scale", g * D * 4), ("k_zero", g * D * 2),
+             ("v_codes", n * D * vb // 8), ("v_scale", (D // G) * n * 4),
+             ("v_zero", (D // G) * n * 2)]
+    out, off = [], 0
+    for name, size in sizes:
+        out.append((name, off, size))
+        off += size
+    return out
+
+
+def unpack_records(blocks, B, H, cap, D, kb, vb, G):
+    """Re-index a record array ([B][H][cap/128][record] bytes) into the
+    logical arrays: k_codes [B][H][cap/G][D][G*kb/32] u32, k_scale, k_zero
+    [B][H][cap/G][D] (f32, f16), v_codes [B][H][cap][D*vb/32] u32, v_scale,
+    v_zero [B][H][D/G][cap] (f32, f16).  Copies; no arithmetic."""
+    n = TOKENS_PER_RECORD
+    nb = cap // n
+    rb = sum(size for _, _, size in record_sections(D, kb, vb, G))
+    raw = np.ascontiguousarray(blocks).view(np.uint8).reshape(B, H, nb, rb)
+    sec = {name: raw[..., off:off + size] for name, off, size in record_sections(D, kb, vb, G)}
+    g = n // G
+
+    def cast(x, dtype):
+        return np.ascontiguousarray(x).view(dtype)
+
+    out = {}
+    out["k_codes"] = cast(sec["k_codes"], np.uint32).reshape(B, H, nb * g, D, G * kb // 32)
+    out["k_scale"] = cast(sec["k_scale"], np.float32).reshape(B, H, nb * g, D)
+    out["k_zero"] = cast(sec["k_zero"], np.float16).reshape(B, H, nb * g, D)
+    out["v_codes"] = cast(sec["v_codes"], np.uint32).reshape(B, H, nb * n, D * vb // 32)
+    vs = cast(sec["v_scale"], np.float32).reshape(B, H, nb, D // G, n)
+    out["v_scale"] = np.ascontiguousarray(vs.transpose(0, 1, 3, 2, 4)).reshape(B, H, D // G, cap)
+    vz = cast(sec["v_zero"], np.float16).reshape(B, H, nb, D // G, n)
+    out["v_zero"] = np.ascontiguousarray(vz.transpose(0, 1, 3, 2, 4)).reshape(B, H, D // G, cap)
+    return out
+
+
+LOGICAL = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero")
 
 
 def half_to_float(bits: int) -> float:
@@ -122,80 +175,80 @@ def unpack_codes(words, n: int, bits: int):
     return codes
 
 
-def layout_shapes(B, H, D, kb, vb, G, R, cap):
-    """Array shapes of the cache storage contract."""
-    return {
-        "k_codes": (B, H, cap // G, D, G * kb // 32),
-        "k_scale": (B, H, cap // G, D),
-        "k_zero": (B, H, cap // G, D),
-        "v_codes": (B, H, cap, D * vb // 32),
-        "v_scale": (B, H, D // G, cap),
-        "v_zero": (B, H, D // G, cap),
-        "k_res": (B, H, R, D),
-        "v_res": (B, H, R, D),
-    }
+def float_to_half(value) -> int:
+    """Bit pattern of an fp32 value that is exactly an fp16 value."""
+    out = np.zeros(1, np.uint16)
+    if _load().kivi_oracle_float_to_half(float(value), _ptr(out)):
+        raise ValueError(f"{value!r} has no exact fp16 form")
+    return int(out[0])
 
 
-_DTYPES = {"k_codes": np.uint32, "k_scale": np.float32, "k_zero": np.float32,
-           "v_codes": np.uint32, "v_scale": np.float32, "v_zero": np.float32,
-           "k_res": np.uint16, "v_res": np.uint16}
+def _round_cap(t: int) -> int:
+    return max(TOKENS_PER_RECORD, -(-t // TOKENS_PER_RECORD) * TOKENS_PER_RECORD)
 
 
-def pack_keys(k_fp16, bits: int, G: int, cap: int | None = None, offset: int = 0, out=None):
-    """KIVI item 2.  k_fp16: uint16 [B][H][T][D] -> (codes, scale, zero)."""
+def pack_keys(k_fp16, bits: int, G: int, cap: int | None = None, offset: int = 0):
+    """KIVI item 2 into a fresh zero-filled record array.  k_fp16: uint16
+    [B][H][T][D] -> logical (codes, scale, zero) over the capacity (a multiple
+    of 128, by default the smallest that holds offset + T)."""
     k = _req(k_fp16, np.uint16)
     B, H, T, D = k.shape
-    cap = T + offset if cap is None else cap
-    if out is None:
-        codes = np.zeros((B, H, cap // G, D, G * bits // 32), np.uint32)
-        scale = np.zeros((B, H, cap // G, D), np.float32)
-        zero = np.zeros((B, H, cap // G, D), np.float32)
-    else:
-        codes, scale, zero = out
-    rc = _load().kivi_oracle_pack_keys(_ptr(k), B, H, T, D, bits, G, _ptr(codes), _ptr(scale),
-                                       _ptr(zero), cap, offset)
-    if rc:
+    cap = _round_cap(T + offset) if cap is None else cap
+    c = Cache(B, H, D, bits, bits, G, G, cap)
+    if _load().kivi_oracle_pack_keys(ctypes.byref(c._c), _ptr(k), T, offset):
         raise ValueError("oracle pack_keys rejected its arguments")
-    return codes, scale, zero
+    return c.k_codes, c.k_scale, c.k_zero
 
 
-def pack_values(v_fp16, bits: int, G: int, cap: int | None = None, offset: int = 0, out=None):
-    """KIVI item 3.  v_fp16: uint16 [B][H][T][D] -> (codes, scale, zero)."""
+def pack_values(v_fp16, bits: int, G: int, cap: int | None = None, offset: int = 0):
+    """KIVI item 3 into a fresh zero-filled record array.  v_fp16: uint16
+    [B][H][T][D] -> logical (codes, scale, zero)."""
     v = _req(v_fp16, np.uint16)
     B, H, T, D = v.shape
-    cap = T + offset if cap is None else cap
-    if out is None:
-        codes = np.zeros((B, H, cap, D * bits // 32), np.uint32)
-        scale = np.zeros((B, H, D // G, cap), np.float32)
-        zero = np.zeros((B, H, D // G, cap), np.float32)
-    else:
-        codes, scale, zero = out
-    rc = _load().kivi_oracle_pack_values(_ptr(v), B, H, T, D, bits, G, _ptr(codes), _ptr(scale),
-                                         _ptr(zero), cap, offset)
-    if rc:
+    cap = _round_cap(T + offset) if cap is None else cap
+    c = Cache(B, H, D, bits, bits, G, G, cap)
+    if _load().kivi_oracle_pack_values(ctypes.byref(c._c), _ptr(v), T, offset):
         raise ValueError("oracle pack_values rejected its arguments")
-    return codes, scale, zero
+    return c.v_codes, c.v_scale, c.v_zero
 
 
 class Cache:
-    """Host-memory KIVI cache driven by the oracle (numpy arrays, zero-filled)."""
+    """Host-memory KIVI cache driven by the oracle (numpy arrays, zero-filled).
+
+    ``arrays`` holds the storage itself: ``blocks`` (the record array, bytes),
+    ``k_res`` and ``v_res``.  The logical arrays ``k_codes`` ... ``v_zero``
+    are re-indexed copies of the records (see unpack_records)."""
 
     def __init__(self, batch, n_kv_heads, head_dim, k_bits, v_bits, group, residual, capacity):
         self.B, self.H, self.D = batch, n_kv_heads, head_dim
         self.kb, self.vb, self.G, self.R, self.cap = k_bits, v_bits, group, residual, capacity
-        shapes = layout_shapes(batch, n_kv_heads, head_dim, k_bits, v_bits, group, residual,
-                               capacity)
-        self.arrays = {n: np.zeros(s, _DTYPES[n]) for n, s in shapes.items()}
+        rb = record_bytes(head_dim, k_bits, v_bits, group)
+        if rb == 0 or capacity % TOKENS_PER_RECORD:
+            raise ValueError("shape or capacity outside the record layout")
+        self.arrays = {
+            "blocks": np.zeros((batch, n_kv_heads, capacity // TOKENS_PER_RECORD, rb), np.uint8),
+            "k_res": np.zeros((batch, n_kv_heads, residual, head_dim), np.uint16),
+            "v_res": np.zeros((batch, n_kv_heads, residual, head_dim), np.uint16),
+        }
         self._c = _CCache(batch, n_kv_heads, head_dim, k_bits, v_bits, group, residual,
-                          capacity, 0, *[_ptr(self.arrays[n]) for n in
-                                         ("k_codes", "k_scale", "k_zero", "v_codes",
-                                          "v_scale", "v_zero", "k_res", "v_res")])
+                          capacity, 0, _ptr(self.arrays["blocks"]), _ptr(self.arrays["k_res"]),
+                          _ptr(self.arrays["v_res"]))
 
     def __getattr__(self, name):
         arrays = self.__dict__.get("arrays")
-        if arrays is not None and name in arrays:
+        if arrays is None:
+            raise AttributeError(name)
+        if name in arrays:
             return arrays[name]
+        if name in LOGICAL:
+            return unpack_records(arrays["blocks"], self.B, self.H, self.cap, self.D, self.kb,
+                                  self.vb, self.G)[name]
         raise AttributeError(name)
+
+    def logical(self):
+        """All six logical arrays at once."""
+        return unpack_records(self.arrays["blocks"], self.B, self.H, self.cap, self.D, self.kb,
+                              self.vb, self.G)
 
     @property
     def n_tokens(self) -> int:

@@ -14,7 +14,8 @@
  *   - (X - z)/s: true IEEE fp32 division.
  *   - max == min gives s = 0: all codes 0, zero = min, no division.
  *   - codes are clamped to [0, 2^B - 1] (provably a no-op for finite input).
- *   - scale and zero are stored as fp32.
+ *   - a scale is stored as fp32; a zero point (the group minimum, which is
+ *     an fp16 input value) is stored as that fp16 value, exactly.
  *   - prefill with t % R == 0 quantizes every key (the prose rule "keep the
  *     last t mod R keys"), leaving the key window empty.
  *   - the cache is updated before attention runs, so attention sees all t
@@ -46,6 +47,28 @@ float kivi_oracle_half_to_float(uint16_t h) {
     v = ldexp((double)(1024 + frac), expo - 25);  /* (1 + frac/1024) 2^(e-15) */
   }
   return (float)(sign ? -v : v);                  /* exact: 11 bits fit */
+}
+
+/* An fp32 value that is exactly a binary16 value -> its bit pattern.  The
+ * zero points stored in the cache are such values (minima of fp16 inputs).
+ * Returns 0 and the pattern, or -1 when the value has no exact fp16 form. */
+int kivi_oracle_float_to_half(float f, uint16_t *out) {
+  const uint16_t sign = signbit(f) ? 0x8000u : 0u;
+  const double a = fabs((double)f);
+  if (a == 0.0) { *out = sign; return 0; }
+  if (!(a <= 65504.0)) return -1;                       /* inf, nan, too large */
+  if (a < ldexp(1.0, -14)) {                            /* subnormal: frac 2^-24 */
+    const double frac = ldexp(a, 24);
+    if (frac != floor(frac)) return -1;
+    *out = (uint16_t)(sign | (uint16_t)frac);
+    return 0;
+  }
+  int ex;
+  (void)frexp(a, &ex);                                  /* a = m 2^ex, m in [0.5, 1) */
+  const double frac = (ldexp(a, 1 - ex) - 1.0) * 1024.0; /* a = (1 + frac/1024) 2^(ex-1) */
+  if (frac != floor(frac)) return -1;
+  *out = (uint16_t)(sign | (uint16_t)((ex - 1 + 15) << 10) | (uint16_t)frac);
+  return 0;
 }
 
 /* -------------------------------------------------------------- quantizer */
@@ -111,80 +134,152 @@ static int bits_ok(int bits) { return bits == 2 || bits == 4; }
 
 static int shape_ok(int D, int bits, int G) {
   return bits_ok(bits) && G > 0 && D > 0 && (G % (32 / bits)) == 0 &&
-         (D % G) == 0 && G <= 256;
+         (D % G) == 0 && (128 % G) == 0 && D <= 1024;
 }
 
-/* Quantize one key group -- G consecutive tokens of channel c -- and store it
- * at group index g of the (b,h) slab.  KIVI item 2. */
-static void put_key_group(const float *x, int bits, int G, int D, int64_t cap,
-                          int64_t bh, int64_t g, int c, uint32_t *codes,
-                          float *scale, float *zero) {
-  uint8_t q[256];
-  float s, z;
-  kivi_oracle_quantize_group(x, G, bits, q, &s, &z);
-  const int64_t words = (int64_t)G * bits / 32;
-  const int64_t sz = (bh * (cap / G) + g) * D + c;
-  kivi_oracle_pack_codes(q, G, bits, codes + sz * words);
-  scale[sz] = s;
-  zero[sz] = z;
-}
+#define TOKENS_PER_RECORD 128
 
-/* Quantize one value row -- all D channels of token tau, in groups of G
- * consecutive channels -- and store it at row tau.  KIVI item 3. */
-static void put_value_row(const float *x, int bits, int G, int D, int64_t cap,
-                          int64_t bh, int64_t tau, uint32_t *codes,
-                          float *scale, float *zero) {
-  uint8_t q[1024];
-  const int64_t words = (int64_t)D * bits / 32;
-  for (int g = 0; g < D / G; ++g) {
-    float s, z;
-    kivi_oracle_quantize_group(x + g * G, G, bits, q + g * G, &s, &z);
-    scale[(bh * (D / G) + g) * cap + tau] = s;
-    zero[(bh * (D / G) + g) * cap + tau] = z;
-  }
-  kivi_oracle_pack_codes(q, D, bits, codes + (bh * cap + tau) * words);
-}
+/* Byte offsets of the sections of a record (kivi_oracle.h). */
+typedef struct {
+  int64_t kc, ks, kz, vc, vs, vz, size;
+} record_t;
 
-int kivi_oracle_pack_keys(const uint16_t *k, int B, int H, int64_t T, int D,
-                          int bits, int G, uint32_t *codes, float *scale,
-                          float *zero, int64_t cap, int64_t off) {
-  if (!shape_ok(D, bits, G) || T < 0 || T % G || off < 0 || off % G ||
-      cap % G || off + T > cap)
-    return -1;
-  float x[256];
-  for (int64_t bh = 0; bh < (int64_t)B * H; ++bh)
-    for (int64_t g = 0; g < T / G; ++g)
-      for (int c = 0; c < D; ++c) {
-        for (int i = 0; i < G; ++i)
-          x[i] = kivi_oracle_half_to_float(k[(bh * T + g * G + i) * D + c]);
-        put_key_group(x, bits, G, D, cap, bh, off / G + g, c, codes, scale, zero);
-      }
+static int record_of(int D, int kb, int vb, int G, record_t *r) {
+  if (!shape_ok(D, kb, G) || !shape_ok(D, vb, G)) return -1;
+  const int64_t groups = TOKENS_PER_RECORD / G;
+  r->kc = 0;
+  r->ks = r->kc + (int64_t)TOKENS_PER_RECORD * D * kb / 8;
+  r->kz = r->ks + groups * D * 4;
+  r->vc = r->kz + groups * D * 2;
+  r->vs = r->vc + (int64_t)TOKENS_PER_RECORD * D * vb / 8;
+  r->vz = r->vs + (int64_t)(D / G) * TOKENS_PER_RECORD * 4;
+  r->size = r->vz + (int64_t)(D / G) * TOKENS_PER_RECORD * 2;
   return 0;
 }
 
-int kivi_oracle_pack_values(const uint16_t *v, int B, int H, int64_t T, int D,
-                            int bits, int G, uint32_t *codes, float *scale,
-                            float *zero, int64_t cap, int64_t off) {
-  if (!shape_ok(D, bits, G) || D > 1024 || T < 0 || off < 0 || off + T > cap)
-    return -1;
-  float x[1024];
-  for (int64_t bh = 0; bh < (int64_t)B * H; ++bh)
-    for (int64_t tau = 0; tau < T; ++tau) {
-      for (int c = 0; c < D; ++c)
-        x[c] = kivi_oracle_half_to_float(v[(bh * T + tau) * D + c]);
-      put_value_row(x, bits, G, D, cap, bh, off + tau, codes, scale, zero);
-    }
+int64_t kivi_oracle_record_bytes(int D, int k_bits, int v_bits, int G) {
+  record_t r;
+  return record_of(D, k_bits, v_bits, G, &r) ? 0 : r.size;
+}
+
+/* Start of the record holding token tau of slab bh. */
+static uint8_t *record_at(const kivi_oracle_cache *c, const record_t *r, int64_t bh,
+                          int64_t tau) {
+  return c->blocks + (bh * (c->capacity / TOKENS_PER_RECORD) + tau / TOKENS_PER_RECORD) * r->size;
+}
+
+/* Where key group g (tokens g G .. g G + G - 1) of channel ch of slab bh is
+ * stored: its code words, scale and zero. */
+typedef struct {
+  uint32_t *codes;
+  float *scale;
+  uint16_t *zero;
+} key_slot_t;
+
+static key_slot_t key_slot(const kivi_oracle_cache *c, const record_t *r, int64_t bh,
+                           int64_t g, int ch) {
+  const int G = c->group, D = c->head_dim;
+  uint8_t *rec = record_at(c, r, bh, g * G);
+  const int64_t local = ((g * G) % TOKENS_PER_RECORD) / G;   /* group within the record */
+  const int64_t i = local * D + ch;
+  key_slot_t k;
+  k.codes = (uint32_t *)(rec + r->kc) + i * (G * c->k_bits / 32);
+  k.scale = (float *)(rec + r->ks) + i;
+  k.zero = (uint16_t *)(rec + r->kz) + i;
+  return k;
+}
+
+/* Where token tau of slab bh keeps its value codes, and the scale / zero of
+ * its channel group gc. */
+static uint32_t *value_codes(const kivi_oracle_cache *c, const record_t *r, int64_t bh,
+                             int64_t tau) {
+  uint8_t *rec = record_at(c, r, bh, tau);
+  return (uint32_t *)(rec + r->vc) + (tau % TOKENS_PER_RECORD) * (c->head_dim * c->v_bits / 32);
+}
+static float *value_scale(const kivi_oracle_cache *c, const record_t *r, int64_t bh,
+                          int64_t tau, int gc) {
+  uint8_t *rec = record_at(c, r, bh, tau);
+  return (float *)(rec + r->vs) + gc * TOKENS_PER_RECORD + tau % TOKENS_PER_RECORD;
+}
+static uint16_t *value_zero(const kivi_oracle_cache *c, const record_t *r, int64_t bh,
+                            int64_t tau, int gc) {
+  uint8_t *rec = record_at(c, r, bh, tau);
+  return (uint16_t *)(rec + r->vz) + gc * TOKENS_PER_RECORD + tau % TOKENS_PER_RECORD;
+}
+
+/* Quantize one key group -- G consecutive tokens of channel ch -- and store it
+ * at group index g of slab bh.  KIVI item 2. */
+static int put_key_group(const kivi_oracle_cache *c, const record_t *r, const float *x,
+                         int64_t bh, int64_t g, int ch) {
+  uint8_t q[TOKENS_PER_RECORD];
+  float s, z;
+  kivi_oracle_quantize_group(x, c->group, c->k_bits, q, &s, &z);
+  key_slot_t k = key_slot(c, r, bh, g, ch);
+  kivi_oracle_pack_codes(q, c->group, c->k_bits, k.codes);
+  *k.scale = s;
+  return kivi_oracle_float_to_half(z, k.zero);
+}
+
+/* Quantize one value row -- all D channels of token tau, in groups of G
+ * consecutive channels -- and store it.  KIVI item 3. */
+static int put_value_row(const kivi_oracle_cache *c, const record_t *r, const float *x,
+                         int64_t bh, int64_t tau) {
+  uint8_t q[1024];
+  const int D = c->head_dim, G = c->group;
+  for (int g = 0; g < D / G; ++g) {
+    float s, z;
+    kivi_oracle_quantize_group(x + g * G, G, c->v_bits, q + g * G, &s, &z);
+    *value_scale(c, r, bh, tau, g) = s;
+    if (kivi_oracle_float_to_half(z, value_zero(c, r, bh, tau, g))) return -1;
+  }
+  kivi_oracle_pack_codes(q, D, c->v_bits, value_codes(c, r, bh, tau));
   return 0;
 }
 
 /* ------------------------------------------------------------- the cache */
 
 static int cache_ok(const kivi_oracle_cache *c) {
-  return c && shape_ok(c->head_dim, c->k_bits, c->group) &&
-         shape_ok(c->head_dim, c->v_bits, c->group) && c->head_dim <= 1024 &&
-         c->residual > 0 && c->residual % c->group == 0 &&
-         c->capacity % c->group == 0 && c->n_tokens >= 0 &&
-         c->n_tokens <= c->capacity;
+  record_t r;
+  return c && c->blocks && c->k_res && c->v_res &&
+         record_of(c->head_dim, c->k_bits, c->v_bits, c->group, &r) == 0 &&
+         c->residual > 0 && c->residual % c->group == 0 && c->capacity > 0 &&
+         c->capacity % TOKENS_PER_RECORD == 0 && c->capacity % c->residual == 0 &&
+         c->n_tokens >= 0 && c->n_tokens <= c->capacity;
+}
+
+int kivi_oracle_pack_keys(const kivi_oracle_cache *dst, const uint16_t *k, int64_t T,
+                          int64_t off) {
+  record_t r;
+  if (!cache_ok(dst) || T < 0 || off < 0 || T % dst->group || off % dst->group ||
+      off + T > dst->capacity)
+    return -1;
+  record_of(dst->head_dim, dst->k_bits, dst->v_bits, dst->group, &r);
+  const int D = dst->head_dim, G = dst->group;
+  float x[TOKENS_PER_RECORD];
+  for (int64_t bh = 0; bh < (int64_t)dst->batch * dst->n_kv_heads; ++bh)
+    for (int64_t g = 0; g < T / G; ++g)
+      for (int ch = 0; ch < D; ++ch) {
+        for (int i = 0; i < G; ++i)
+          x[i] = kivi_oracle_half_to_float(k[(bh * T + g * G + i) * D + ch]);
+        if (put_key_group(dst, &r, x, bh, off / G + g, ch)) return -1;
+      }
+  return 0;
+}
+
+int kivi_oracle_pack_values(const kivi_oracle_cache *dst, const uint16_t *v, int64_t T,
+                            int64_t off) {
+  record_t r;
+  if (!cache_ok(dst) || T < 0 || off < 0 || off + T > dst->capacity) return -1;
+  record_of(dst->head_dim, dst->k_bits, dst->v_bits, dst->group, &r);
+  const int D = dst->head_dim;
+  float x[1024];
+  for (int64_t bh = 0; bh < (int64_t)dst->batch * dst->n_kv_heads; ++bh)
+    for (int64_t tau = 0; tau < T; ++tau) {
+      for (int ch = 0; ch < D; ++ch)
+        x[ch] = kivi_oracle_half_to_float(v[(bh * T + tau) * D + ch]);
+      if (put_value_row(dst, &r, x, bh, off + tau)) return -1;
+    }
+  return 0;
 }
 
 /* KIVI item 4, one token at a time.  For each arriving token tau:
@@ -196,21 +291,23 @@ static int cache_ok(const kivi_oracle_cache *c) {
  *           R tokens the whole block is quantized and the buffer empties. */
 int kivi_oracle_append(kivi_oracle_cache *c, const uint16_t *k_new,
                        const uint16_t *v_new, int64_t n_new) {
+  record_t r;
   if (!cache_ok(c) || n_new < 0 || c->n_tokens + n_new > c->capacity) return -1;
+  record_of(c->head_dim, c->k_bits, c->v_bits, c->group, &r);
   const int D = c->head_dim, G = c->group, R = c->residual;
-  const int64_t BH = (int64_t)c->batch * c->n_kv_heads, cap = c->capacity;
+  const int64_t BH = (int64_t)c->batch * c->n_kv_heads;
   float *x = (float *)malloc(sizeof(float) * (size_t)(R > D ? R : D));
   if (!x) return -1;
-  for (int64_t i = 0; i < n_new; ++i) {
+  int rc = 0;
+  for (int64_t i = 0; i < n_new && rc == 0; ++i) {
     const int64_t tau = c->n_tokens;
     const int64_t slot = tau % R;
-    for (int64_t bh = 0; bh < BH; ++bh) {
+    for (int64_t bh = 0; bh < BH && rc == 0; ++bh) {
       uint16_t *kres = c->k_res + bh * R * D;
       uint16_t *vres = c->v_res + bh * R * D;
       if (tau >= R) {  /* value queue would reach R+1: pop token tau-R */
         for (int ch = 0; ch < D; ++ch) x[ch] = kivi_oracle_half_to_float(vres[slot * D + ch]);
-        put_value_row(x, c->v_bits, G, D, cap, bh, tau - R, c->v_codes,
-                      c->v_scale, c->v_zero);
+        rc |= put_value_row(c, &r, x, bh, tau - R);
       }
       memcpy(kres + slot * D, k_new + (bh * n_new + i) * D, sizeof(uint16_t) * D);
       memcpy(vres + slot * D, v_new + (bh * n_new + i) * D, sizeof(uint16_t) * D);
@@ -220,52 +317,54 @@ int kivi_oracle_append(kivi_oracle_cache *c, const uint16_t *k_new,
           for (int g = 0; g < R / G; ++g) {
             for (int j = 0; j < G; ++j)
               x[j] = kivi_oracle_half_to_float(kres[(int64_t)(g * G + j) * D + ch]);
-            put_key_group(x, c->k_bits, G, D, cap, bh, first / G + g, ch,
-                          c->k_codes, c->k_scale, c->k_zero);
+            rc |= put_key_group(c, &r, x, bh, first / G + g, ch);
           }
       }
     }
     c->n_tokens = tau + 1;
   }
   free(x);
-  return 0;
+  return rc ? -1 : 0;
 }
 
 /* Key tau of (bh) as the attention sees it: dequantized if its R-block has
  * been quantized, else the fp16 value from the window. */
-static float key_at(const kivi_oracle_cache *c, int64_t bh, int64_t tau, int ch) {
+static float key_at(const kivi_oracle_cache *c, const record_t *r, int64_t bh, int64_t tau,
+                    int ch) {
   const int64_t t = c->n_tokens, R = c->residual, G = c->group, D = c->head_dim;
   const int64_t n_kq = t - t % R;
   if (tau < n_kq) {
-    const int64_t words = G * c->k_bits / 32;
-    const int64_t sz = (bh * (c->capacity / G) + tau / G) * D + ch;
-    const uint32_t q = code_at(c->k_codes + sz * words, (int)(tau % G), c->k_bits);
-    return kivi_oracle_dequant(q, c->k_scale[sz], c->k_zero[sz]);
+    key_slot_t k = key_slot(c, r, bh, tau / G, ch);
+    const uint32_t q = code_at(k.codes, (int)(tau % G), c->k_bits);
+    return kivi_oracle_dequant(q, *k.scale, kivi_oracle_half_to_float(*k.zero));
   }
   return kivi_oracle_half_to_float(c->k_res[(bh * R + tau % R) * D + ch]);
 }
 
-static float value_at(const kivi_oracle_cache *c, int64_t bh, int64_t tau, int ch) {
+static float value_at(const kivi_oracle_cache *c, const record_t *r, int64_t bh, int64_t tau,
+                      int ch) {
   const int64_t t = c->n_tokens, R = c->residual, G = c->group, D = c->head_dim;
   const int64_t n_vq = t > R ? t - R : 0;
   if (tau < n_vq) {
-    const int64_t words = D * c->v_bits / 32;
-    const uint32_t q = code_at(c->v_codes + (bh * c->capacity + tau) * words, ch, c->v_bits);
-    const int64_t sz = (bh * (D / G) + ch / G) * c->capacity + tau;
-    return kivi_oracle_dequant(q, c->v_scale[sz], c->v_zero[sz]);
+    const uint32_t q = code_at(value_codes(c, r, bh, tau), ch, c->v_bits);
+    const int gc = (int)(ch / G);
+    return kivi_oracle_dequant(q, *value_scale(c, r, bh, tau, gc),
+                               kivi_oracle_half_to_float(*value_zero(c, r, bh, tau, gc)));
   }
   return kivi_oracle_half_to_float(c->v_res[(bh * R + tau % R) * D + ch]);
 }
 
 int kivi_oracle_materialize(const kivi_oracle_cache *c, float *k_hat, float *v_hat) {
+  record_t r;
   if (!cache_ok(c)) return -1;
+  record_of(c->head_dim, c->k_bits, c->v_bits, c->group, &r);
   const int64_t BH = (int64_t)c->batch * c->n_kv_heads, t = c->n_tokens;
   const int D = c->head_dim;
   for (int64_t bh = 0; bh < BH; ++bh)
     for (int64_t tau = 0; tau < t; ++tau)
       for (int ch = 0; ch < D; ++ch) {
-        if (k_hat) k_hat[(bh * t + tau) * D + ch] = key_at(c, bh, tau, ch);
-        if (v_hat) v_hat[(bh * t + tau) * D + ch] = value_at(c, bh, tau, ch);
+        if (k_hat) k_hat[(bh * t + tau) * D + ch] = key_at(c, &r, bh, tau, ch);
+        if (v_hat) v_hat[(bh * t + tau) * D + ch] = value_at(c, &r, bh, tau, ch);
       }
   return 0;
 }
@@ -281,13 +380,15 @@ static int attend_one(const kivi_oracle_cache *c, const uint16_t *q, int n_q_hea
   const int64_t t = c->n_tokens;
   const int n_rep = n_q_heads / c->n_kv_heads;
   const int64_t bh = (int64_t)b * c->n_kv_heads + hq / n_rep;
+  record_t r;
+  record_of(D, c->k_bits, c->v_bits, c->group, &r);
   float qv[1024];
   for (int ch = 0; ch < D; ++ch)
     qv[ch] = kivi_oracle_half_to_float(q[((int64_t)b * n_q_heads + hq) * D + ch]);
   double m = -INFINITY;
   for (int64_t tau = 0; tau < t; ++tau) {
     double acc = 0.0;
-    for (int ch = 0; ch < D; ++ch) acc += (double)qv[ch] * (double)key_at(c, bh, tau, ch);
+    for (int ch = 0; ch < D; ++ch) acc += (double)qv[ch] * (double)key_at(c, &r, bh, tau, ch);
     acc = acc / sqrt((double)D);
     if (mask) acc += (double)mask[(int64_t)b * t + tau];
     score[tau] = acc;
@@ -304,7 +405,7 @@ static int attend_one(const kivi_oracle_cache *c, const uint16_t *q, int n_q_hea
   for (int ch = 0; ch < D; ++ch) o[ch] = 0.0;
   for (int64_t tau = 0; tau < t; ++tau) {
     const double p = score[tau] / l;
-    for (int ch = 0; ch < D; ++ch) o[ch] += p * (double)value_at(c, bh, tau, ch);
+    for (int ch = 0; ch < D; ++ch) o[ch] += p * (double)value_at(c, &r, bh, tau, ch);
   }
   for (int ch = 0; ch < D; ++ch) out[ch] = (float)o[ch];
   return 0;

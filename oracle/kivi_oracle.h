@@ -13,15 +13,27 @@
  * Every pointer is a host pointer.  fp16 data is passed as raw IEEE binary16
  * bit patterns (uint16_t).  All arrays are owned by the caller.
  *
- * Storage layout (the same contract the GPU library follows; the packing
- * direction is the page's: keys packed along tokens, values along channels):
- *   key codes   u32 [B][H][cap/G][D][G*kb/32]   token e of a group at word
- *                                               e/(32/kb), bits kb*(e%(32/kb))
- *   key scale   f32 [B][H][cap/G][D]            (and key zero, same shape)
- *   value codes u32 [B][H][cap][D*vb/32]        channel e at word e/(32/vb),
- *                                               bits vb*(e%(32/vb))
- *   value scale f32 [B][H][D/G][cap]            (and value zero, same shape)
- *   key/value residual fp16 [B][H][R][D]        token tau in slot tau % R
+ * Storage layout (the same contract the GPU library follows).  The quantized
+ * part of each (batch row b, KV head h) slab is a run of records, one per 128
+ * consecutive tokens: record j of slab bh holds tokens [128 j, 128 j + 128)
+ * and sits at byte ((bh * (cap/128)) + j) * RB of the `blocks` array, where
+ * RB = kivi_oracle_record_bytes(D, kb, vb, G).  A record holds, in order:
+ *   key codes   u32 [128/G][D][G*kb/32]  key group g (tokens 128 j + G g ..)
+ *                                        of channel c: its token e at word
+ *                                        e/(32/kb), bits kb*(e%(32/kb))
+ *                                        (KIVI item 2: per-channel groups of G
+ *                                        tokens, packed along tokens)
+ *   key scales  f32 [128/G][D]
+ *   key zeros   f16 [128/G][D]           the group minimum, an fp16 input
+ *                                        value, stored exactly
+ *   value codes u32 [128][D*vb/32]       token tau: channel e at word
+ *                                        e/(32/vb), bits vb*(e%(32/vb))
+ *                                        (KIVI item 3: per-token groups of G
+ *                                        channels, packed along channels)
+ *   value scales f32 [D/G][128]
+ *   value zeros  f16 [D/G][128]
+ * G divides 128; cap is a multiple of 128.
+ *   key/value residual fp16 [B][H][R][D]  token tau in slot tau % R
  */
 #ifndef KIVI_ORACLE_H
 #define KIVI_ORACLE_H
@@ -37,13 +49,17 @@ typedef struct kivi_oracle_cache {
   int32_t k_bits, v_bits, group, residual;
   int64_t capacity;
   int64_t n_tokens;
-  uint32_t *k_codes; float *k_scale, *k_zero;
-  uint32_t *v_codes; float *v_scale, *v_zero;
+  uint8_t *blocks;             /* [B][H][cap/128] records */
   uint16_t *k_res, *v_res;
 } kivi_oracle_cache;
 
+/* Bytes of one 128-token record; 0 for shapes the layout does not take. */
+int64_t kivi_oracle_record_bytes(int D, int k_bits, int v_bits, int G);
+
 /* binary16 bit pattern -> float (exact). */
 float kivi_oracle_half_to_float(uint16_t h);
+/* float holding a binary16 value -> its bit pattern; 0, or -1 if inexact. */
+int kivi_oracle_float_to_half(float f, uint16_t *out);
 
 /* KIVI item 1: asymmetric round-to-nearest group quantizer. */
 void kivi_oracle_quantize_group(const float *x, int n, int bits, uint8_t *codes,
@@ -56,17 +72,17 @@ void kivi_oracle_pack_codes(const uint8_t *codes, int n, int bits, uint32_t *wor
 void kivi_oracle_unpack_codes(const uint32_t *words, int n, int bits, uint8_t *codes);
 
 /* KIVI item 2: per-channel key quantization, G consecutive tokens per group.
- * k: fp16 [B][H][T][D]; T % G == 0; dst_token_offset % G == 0.  Writes groups
- * [off/G, (off+T)/G) of a destination with capacity `cap`.  Returns 0 or -1. */
-int kivi_oracle_pack_keys(const uint16_t *k, int B, int H, int64_t T, int D,
-                          int bits, int G, uint32_t *codes, float *scale,
-                          float *zero, int64_t cap, int64_t dst_token_offset);
+ * k: fp16 [B][H][T][D] (B, H, D from dst); T % G == 0; off % G == 0.  Writes
+ * the key sections for tokens [off, off + T) of dst's records; nothing else
+ * of dst changes.  Returns 0 or -1. */
+int kivi_oracle_pack_keys(const kivi_oracle_cache *dst, const uint16_t *k, int64_t T,
+                          int64_t off);
 
 /* KIVI item 3: per-token value quantization, G consecutive channels per group.
- * v: fp16 [B][H][T][D].  Writes rows [off, off+T).  Returns 0 or -1. */
-int kivi_oracle_pack_values(const uint16_t *v, int B, int H, int64_t T, int D,
-                            int bits, int G, uint32_t *codes, float *scale,
-                            float *zero, int64_t cap, int64_t dst_token_offset);
+ * v: fp16 [B][H][T][D].  Writes the value sections for tokens [off, off + T).
+ * Returns 0 or -1. */
+int kivi_oracle_pack_values(const kivi_oracle_cache *dst, const uint16_t *v, int64_t T,
+                            int64_t off);
 
 /* KIVI item 4: append n_new tokens (k_new, v_new: fp16 [B][H][n_new][D]) one
  * at a time through the fp16 residual window.  Returns 0 or -1. */

@@ -22,7 +22,8 @@ def _filled(B, H, D, G, R, t, kb=2, vb=2, seed=0, kscale=1.0):
     rng = np.random.default_rng(seed)
     K = _rand(rng, (B, H, t, D), kscale)
     V = _rand(rng, (B, H, t, D))
-    cap = ((t + R) // R + 1) * R
+    m = int(np.lcm(R, oracle.TOKENS_PER_RECORD))
+    cap = (t // m + 1) * m
     c = oracle.Cache(B, H, D, kb, vb, G, R, cap)
     c.append(K.view(np.uint16), V.view(np.uint16))
     return c, K, V
@@ -150,6 +151,6 @@ def test_heads_entry_matches_full():
 
 
 def test_empty_cache_gives_zeros():
-    c = oracle.Cache(1, 1, 32, 2, 2, 32, 32, 64)
+    c = oracle.Cache(1, 1, 32, 2, 2, 32, 32, 128)
     out = c.decode_attn(np.zeros((1, 1, 32), np.uint16))
     assert not out.any()

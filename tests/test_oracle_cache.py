@@ -11,6 +11,12 @@ import pytest
 import oracle
 
 
+def _cap(t, R):
+    """Smallest capacity >= t that is a multiple of R and of the 128-token record."""
+    m = np.lcm(R, oracle.TOKENS_PER_RECORD)
+    return int(max(m, -(-t // m) * m))
+
+
 def _rand(rng, shape):
     return rng.standard_normal(shape).astype(np.float16)
 
@@ -31,17 +37,19 @@ def _check_invariants(cache, K, V):
         assert np.array_equal(cache.v_res[:, :, tau % R], Vb[:, :, tau])
     if n_kq:
         kc, ks, kz = oracle.pack_keys(Kb[:, :, :n_kq], cache.kb, G)
-        assert np.array_equal(cache.k_codes[:, :, :n_kq // G], kc)
-        assert np.array_equal(cache.k_scale[:, :, :n_kq // G], ks)
-        assert np.array_equal(cache.k_zero[:, :, :n_kq // G], kz)
+        ng = n_kq // G
+        assert np.array_equal(cache.k_codes[:, :, :ng], kc[:, :, :ng])
+        assert np.array_equal(cache.k_scale[:, :, :ng], ks[:, :, :ng])
+        assert np.array_equal(cache.k_zero[:, :, :ng].view(np.uint16), kz[:, :, :ng].view(np.uint16))
     # nothing beyond the quantized prefix has been written
     assert not cache.k_codes[:, :, n_kq // G:].any()
     assert not cache.k_scale[:, :, n_kq // G:].any()
     if n_vq:
         vc, vs, vz = oracle.pack_values(Vb[:, :, :n_vq], cache.vb, G)
-        assert np.array_equal(cache.v_codes[:, :, :n_vq], vc)
-        assert np.array_equal(cache.v_scale[:, :, :, :n_vq], vs)
-        assert np.array_equal(cache.v_zero[:, :, :, :n_vq], vz)
+        assert np.array_equal(cache.v_codes[:, :, :n_vq], vc[:, :, :n_vq])
+        assert np.array_equal(cache.v_scale[:, :, :, :n_vq], vs[:, :, :, :n_vq])
+        assert np.array_equal(cache.v_zero[:, :, :, :n_vq].view(np.uint16),
+                              vz[:, :, :, :n_vq].view(np.uint16))
     assert not cache.v_codes[:, :, n_vq:].any()
     assert not cache.v_scale[:, :, :, n_vq:].any()
 
@@ -51,7 +59,7 @@ def test_window_invariants_random_chunks(kb, vb, R):
     rng = np.random.default_rng(R + kb * 10 + vb)
     B, H, D, G = 2, 2, 64, 32
     t_end = 3 * R + 5
-    cap = ((t_end + R - 1) // R) * R
+    cap = _cap(t_end, R)
     K = _rand(rng, (B, H, t_end, D))
     V = _rand(rng, (B, H, t_end, D))
     cache = oracle.Cache(B, H, D, kb, vb, G, R, cap)
@@ -82,7 +90,7 @@ def test_prefill_equals_single_appends_equals_slicing(T):
     """P7: append(T) == T x append(1) == the prefill slicing rule, bit for bit."""
     rng = np.random.default_rng(T)
     B, H, D, G, R = 2, 2, 64, 32, 32
-    cap = 160
+    cap = 256
     K = _rand(rng, (B, H, T, D)).view(np.uint16)
     V = _rand(rng, (B, H, T, D)).view(np.uint16)
     a = oracle.Cache(B, H, D, 2, 2, G, R, cap)
@@ -107,7 +115,7 @@ def test_prefill_multiple_of_R_leaves_key_window_empty():
     rng = np.random.default_rng(1)
     K = _rand(rng, (1, 1, 64, 32)).view(np.uint16)
     V = _rand(rng, (1, 1, 64, 32)).view(np.uint16)
-    c = oracle.Cache(1, 1, 32, 2, 2, 32, 32, 96)
+    c = oracle.Cache(1, 1, 32, 2, 2, 32, 32, 128)
     c.append(K, V)
     kh, vh = c.materialize()
     assert c.k_scale[0, 0, :2].all()          # both key groups quantized
@@ -117,8 +125,8 @@ def test_prefill_multiple_of_R_leaves_key_window_empty():
 
 
 def test_capacity_and_argument_errors():
-    c = oracle.Cache(1, 1, 32, 2, 2, 32, 32, 64)
-    x = np.zeros((1, 1, 65, 32), np.uint16)
+    c = oracle.Cache(1, 1, 32, 2, 2, 32, 32, 128)
+    x = np.zeros((1, 1, 129, 32), np.uint16)
     with pytest.raises(ValueError):
         c.append(x, x)
     with pytest.raises(ValueError):

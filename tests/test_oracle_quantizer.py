@@ -158,13 +158,62 @@ def test_layout_case():
     vc, vs, vz = oracle.pack_values(x.view(np.uint16), 2, 32)
     kwords = [int(w, 16) for w in case["key_words_by_channel_mod4"]]
     vwords = [int(w, 16) for w in case["value_words_by_token_mod4"]]
-    assert kc.shape == (1, 1, 1, 32, 2) and vc.shape == (1, 1, 32, 2)
+    assert kc.shape == (1, 1, 4, 32, 2) and vc.shape == (1, 1, 128, 2)
     for ch in range(32):
         assert kc[0, 0, 0, ch].tolist() == [kwords[ch % 4]] * 2
         assert ks[0, 0, 0, ch] == 1.0 and kz[0, 0, 0, ch] == 0.0
+    assert not kc[0, 0, 1:].any() and not ks[0, 0, 1:].any()
     for t in range(32):
         assert vc[0, 0, t].tolist() == [vwords[t % 4]] * 2
         assert vs[0, 0, 0, t] == 1.0 and vz[0, 0, 0, t] == 0.0
+    assert not vc[0, 0, 32:].any() and not vs[0, 0, 0, 32:].any()
+
+
+def test_record_case():
+    """The record layout: section offsets and raw record bytes worked out by
+    hand (tests/golden/pack_layout.json, record_case)."""
+    case = _golden("pack_layout.json")["record_case"]
+    shp = case["shape"]
+    D, G, cap = shp["D"], shp["G"], shp["capacity"]
+    off = case["section_offsets"]
+    assert oracle.record_bytes(D, shp["k_bits"], shp["v_bits"], G) == off["record_bytes"]
+    assert [(n, o) for n, o, _ in oracle.record_sections(D, 2, 2, G)] == \
+        [(n, off[n]) for n in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero")]
+    tau = np.arange(32)[:, None]
+    ch = np.arange(32)[None, :]
+    x = (((tau + ch) % 4) - 1.5).astype(np.float16)[None, None]   # [1][1][32][32]
+    c = oracle.Cache(1, 1, D, 2, 2, G, 32, cap)
+    c.append(x.view(np.uint16), x.view(np.uint16))      # t = 32 = R: keys quantized, values not
+    rec = c.blocks[0, 0, 0]
+    for e in case["bytes"]:
+        if "value" in e["what"]:
+            continue
+        got = bytes(rec[e["offset"]:e["offset"] + len(e["hex"]) // 2]).hex()
+        assert got == e["hex"], e["what"]
+    d = oracle.Cache(1, 1, D, 2, 2, G, 32, cap)
+    d.append(np.concatenate([x, x], axis=2).view(np.uint16),
+             np.concatenate([x, x], axis=2).view(np.uint16))  # t = 64: values 0..31 popped
+    rec = d.blocks[0, 0, 0]
+    for e in case["bytes"]:
+        if "value" not in e["what"]:
+            continue
+        got = bytes(rec[e["offset"]:e["offset"] + len(e["hex"]) // 2]).hex()
+        assert got == e["hex"], e["what"]
+
+
+def test_float_to_half_round_trips_every_finite_pattern():
+    """Zero points are stored as fp16: the oracle's exact float -> fp16
+    conversion inverts the fp16 widening for every finite pattern, and
+    refuses a value with no fp16 form."""
+    pats = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = pats.view(np.float16)
+    for p, v in zip(pats[::97], vals[::97]):
+        if np.isfinite(v):
+            assert oracle.float_to_half(np.float32(v)) == int(p)
+    assert oracle.float_to_half(np.float32(-0.0)) == 0x8000
+    assert oracle.float_to_half(np.float32(2 ** -24)) == 0x0001
+    with pytest.raises(ValueError):
+        oracle.float_to_half(np.float32(1.0 + 2 ** -20))
 
 
 def test_pack_keys_groups_along_tokens():
