@@ -8,15 +8,20 @@ kivi_decode_step, which runs the append inside the attention launch where the
 shape allows (--unfused: kivi_append, then kivi_decode_attn).  Steps rotate
 over L layer replicas (L x footprint >= 1 GiB) so the 256 MB Infinity Cache
 cannot serve the working set; inputs are resident in HBM before the timed
-region starts.  `value` is the algorithmic bytes a step must move (packed
-codes + fp32 scale/zero + fp16 window + q + out, plus the append's bytes)
+region starts.  Every replica runs at the context the workload states: its
+token count (a host-side field of the cache descriptor) is set back to the
+prefill length once it has taken the workload's decode steps, so the timed
+steps attend over the stated context, not a growing one.
+
+`value` is the algorithmic bytes a step must move (packed codes + fp32
+scales + fp16 zero points + fp16 window + q + out, plus the append's bytes)
 divided by the measured step time (HIP events at the two ends of the K timed
-steps).  `roofline` covers the attention launch alone (its split kernel and
-combine): a second timed loop issues K kivi_decode_attn calls back to back
-over the same replicas, with HIP events on the stream the library launches on
-around rounds of calls, and divides by the call count.  `cpu_baseline` times
-the CPU oracle on a bounded sample of (batch, KV head) slabs of the same
-workload.
+steps).  `roofline` covers the attention launch alone: a second timed loop
+issues kivi_decode_attn calls back to back over the same replicas, in at
+least three rounds, with HIP events on the stream the library launches on
+around each round.  `cpu_baseline` times the CPU oracle on a bounded sample
+of (batch, KV head) slabs of the same workload, on one host thread and on
+every host core (one slab per thread).
 """
 from __future__ import annotations
 
@@ -34,9 +39,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["decode_attention_pack_amd/csrc/" + f for f in
-                  ("api.cpp", "decode_matrix.hip", "decode_generic.hip", "kivi_internal.hpp",
-                   "kivi_device.hpp")] + ["decode_attention_pack_amd/build.py"]
+KERNEL_SOURCES = sorted(
+    "decode_attention_pack_amd/csrc/" + f
+    for f in os.listdir(os.path.join(ROOT, "decode_attention_pack_amd", "csrc"))
+    if f.endswith((".hip", ".cpp", ".hpp"))) + ["decode_attention_pack_amd/build.py"]
 
 
 def kernel_source_hash() -> str:
@@ -68,8 +74,9 @@ def attn_bytes(w, t: int) -> int:
     n_kq = t - t % R
     n_vq = max(0, t - R)
     rep = w.Hq // w.Hkv
-    per = (n_kq * D * w.k_bits // 8 + (n_kq // G) * D * 8
-           + n_vq * D * w.v_bits // 8 + n_vq * (D // G) * 8
+    # fp32 scale + fp16 zero per group
+    per = (n_kq * D * w.k_bits // 8 + (n_kq // G) * D * 6
+           + n_vq * D * w.v_bits // 8 + n_vq * (D // G) * 6
            + ((t % R) + min(t, R)) * D * 2
            + rep * D * 2 + rep * D * 4)
     return per * w.B * w.Hkv
@@ -80,16 +87,16 @@ def append_bytes(w, t_before: int) -> int:
     R, G, D = w.R, w.G, w.D
     per = 2 * D * 2 + 2 * D * 2                       # read k, v; write window slots
     if t_before >= R:                                 # value leaves the window
-        per += D * 2 + D * w.v_bits // 8 + (D // G) * 8
+        per += D * 2 + D * w.v_bits // 8 + (D // G) * 6
     if (t_before + 1) % R == 0:                       # key block quantized
-        per += R * D * 2 + R * D * w.k_bits // 8 + (R // G) * D * 8
+        per += R * D * 2 + R * D * w.k_bits // 8 + (R // G) * D * 6
     return per * w.B * w.Hkv
 
 
 def pack_bytes(w, T: int, bits: int) -> int:
     """Algorithmic bytes of packing T tokens of keys (or values): fp16 in,
-    codes + fp32 scale/zero out."""
-    return w.B * w.Hkv * (T * w.D * 2 + T * w.D * bits // 8 + (T // w.G) * w.D * 8)
+    codes + fp32 scales + fp16 zeros out."""
+    return w.B * w.Hkv * (T * w.D * 2 + T * w.D * bits // 8 + (T // w.G) * w.D * 6)
 
 
 def time_pack(w, inp, dev, stream, reps: int = 5):
@@ -98,23 +105,20 @@ def time_pack(w, inp, dev, stream, reps: int = 5):
 
     from decode_attention_pack_amd import kivi
     T = w.T0 - w.T0 % w.G
+    cap = -(-T // 128) * 128
     k = torch.from_numpy(inp["k0"][:, :, :T]).to(dev).contiguous()
     v = torch.from_numpy(inp["v0"][:, :, :T]).to(dev).contiguous()
+    dst = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.G, cap)
     out = {}
     for name, x, bits in (("keys", k, w.k_bits), ("values", v, w.v_bits)):
-        shp = kivi.layout_shapes(w.B, w.Hkv, w.D, bits, bits, w.G, 1, T)
-        pre = "k_" if name == "keys" else "v_"
-        codes = torch.empty(shp[pre + "codes"], dtype=torch.int32, device=dev)
-        scale = torch.empty(shp[pre + "scale"], dtype=torch.float32, device=dev)
-        zero = torch.empty(shp[pre + "zero"], dtype=torch.float32, device=dev)
         fn = kivi.kivi_pack_keys if name == "keys" else kivi.kivi_pack_values
-        fn(x, bits, w.G, codes, scale, zero, T, 0, stream=stream)
+        fn(dst, x, 0, stream=stream)
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(reps):
-            fn(x, bits, w.G, codes, scale, zero, T, 0, stream=stream)
+            fn(dst, x, 0, stream=stream)
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
@@ -123,32 +127,77 @@ def time_pack(w, inp, dev, stream, reps: int = 5):
     return out
 
 
-def cpu_baseline(w, inp, budget_s: float = 12.0):
-    """Time the CPU oracle on (batch, KV head) slabs until ~budget_s of work."""
+def host_cpu():
+    """CPU model and the cores this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return model, cores
+
+
+def cpu_baseline(w, inp, budget_s: float = 10.0):
+    """Time the CPU oracle on (batch, KV head) slabs of the workload: first on
+    one thread until ~budget_s of work, then the same slabs on every host core
+    (one slab per thread; the oracle's C code runs outside the GIL)."""
+    import concurrent.futures
+
     import oracle
     rep = w.Hq // w.Hkv
-    slabs = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
     t = w.T0 + 1
-    done, spent = 0, 0.0
     q = inp["q_steps"][0]
-    for b, h in slabs:
+    model, n_cores = host_cpu()
+
+    def build(bh):
+        b, h = bh
         o = oracle.Cache(1, 1, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
         o.append(inp["k0"][b:b + 1, h:h + 1].view(np.uint16), inp["v0"][b:b + 1, h:h + 1].view(np.uint16))
         o.append(inp["k_steps"][0][b:b + 1, h:h + 1].view(np.uint16),
                  inp["v_steps"][0][b:b + 1, h:h + 1].view(np.uint16))
-        qs = np.ascontiguousarray(q[b:b + 1, h * rep:(h + 1) * rep]).view(np.uint16)
+        return o
+
+    def attend(bh, o):
+        b, h = bh
+        o.decode_attn(np.ascontiguousarray(q[b:b + 1, h * rep:(h + 1) * rep]).view(np.uint16))
+
+    slabs = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
+    done, spent = [], 0.0
+    for bh in slabs:
+        o = build(bh)
         t0 = time.perf_counter()
-        o.decode_attn(qs)
+        attend(bh, o)
         spent += time.perf_counter() - t0
-        done += 1
+        done.append((bh, o))
         if spent >= budget_s:
             break
     slab_bytes = attn_bytes(w, t) / (w.B * w.Hkv)
-    return {"value": round(slab_bytes * done / spent / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{done} of {w.B * w.Hkv} (batch, kv-head) slabs of {w.name}, one decode "
-                      f"step at context {t} ({rep} query heads each), single-threaded C oracle, "
-                      f"{spent:.1f} s"}
+    res = {"value": round(slab_bytes * len(done) / spent / 1e9, 4), "unit": "GB/s", "cores": 1,
+           "kind": "oracle",
+           "sample": f"{len(done)} of {w.B * w.Hkv} (batch, kv-head) slabs of {w.name}, one decode "
+                     f"step at context {t} ({rep} query heads each), single-threaded C oracle, "
+                     f"{spent:.1f} s",
+           "host_cpu": model, "host_cores": n_cores}
+    # the same sample on every core: each thread runs whole slabs
+    reps = max(1, n_cores // max(1, len(done)))
+    work = [bh_o for bh_o in done for _ in range(reps)]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=n_cores) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(lambda x: attend(*x), work))
+        wall = time.perf_counter() - t0
+    res["all_cores"] = {"value": round(slab_bytes * len(work) / wall / 1e9, 4), "unit": "GB/s",
+                        "cores": n_cores,
+                        "sample": f"{len(work)} slab attention calls ({len(done)} slabs x {reps}) "
+                                  f"on {n_cores} threads, {wall:.1f} s wall"}
+    return res
 
 
 def main():
@@ -186,15 +235,17 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
 
-    total = args.warmup + args.steps
-    # one replica's footprint at the prefill length
-    probe = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R,
-                       ((w.T0 + 2 * w.R) // w.R) * w.R)
+    # Each replica takes the workload's decode steps (contexts T0 + 1 ..
+    # T0 + steps), then its token count is set back to T0: the cache then
+    # holds T0 tokens again as far as every kernel is concerned (the data the
+    # steps wrote stays, and the next steps overwrite it).
+    n_cyc = w.steps
+    m = w.R * 128 // math.gcd(w.R, 128)
+    cap = -(-(w.T0 + n_cyc) // m) * m
+    probe = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, cap)
     footprint = sum(a.numel() * a.element_size() for a in probe.arrays.values())
     del probe
     L = args.layers or max(2, math.ceil((1 << 30) / footprint))
-    per_layer = math.ceil(total / L) + 1
-    cap = ((w.T0 + per_layer + w.R - 1) // w.R) * w.R
     print(f"# {w.name}: footprint {footprint / 1e6:.1f} MB/layer, {L} layers, capacity {cap}",
           file=sys.stderr, flush=True)
 
@@ -223,10 +274,14 @@ def main():
     # the fused step (kivi_decode_step) takes the automatic plan
     fused = not args.unfused and args.path == 0 and args.tokens_per_split == 0
     fused_steps = [kivi.bind_decode_step(c, k1, v1, q, out, ws, stream=stream) for c in caches]
+    contexts = set()
 
     def step(i):
         c = caches[i % L]
+        if c.n_tokens >= w.T0 + n_cyc:
+            c.c.n_tokens = w.T0
         t_before = c.n_tokens
+        contexts.add(t_before + 1)
         if fused:
             fused_steps[i % L]()
         else:
@@ -234,9 +289,18 @@ def main():
             decodes[i % L]()
         return attn_bytes(w, t_before + 1), append_bytes(w, t_before)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    # warm-up: the requested steps, and at least ~1 s of back-to-back steps
+    # (with fewer, the clocks have not settled and the first timed calls run
+    # slower)
+    t_w = time.perf_counter()
+    i = 0
+    while i < args.warmup or time.perf_counter() - t_w < 1.0:
+        for _ in range(50):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
+    i0 = i
+    contexts.clear()
 
     # timed region 1: K whole steps (append + attention), events at its ends only
     start = torch.cuda.Event(enable_timing=True)
@@ -244,27 +308,29 @@ def main():
     a_bytes = p_bytes = 0
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(args.steps):
-        ab, pb = step(args.warmup + i)
+    for j in range(args.steps):
+        ab, pb = step(i0 + j)
         a_bytes += ab
         p_bytes += pb
     stop.record(stream)
     torch.cuda.synchronize()
-    # timed region 2: the attention launch alone, K calls back to back over the
-    # same replicas (no append in between), in rounds of 25 calls so that the
-    # spread across rounds can be reported
-    n_rounds = max(1, args.steps // 25)
-    per_round = max(1, args.steps // n_rounds)
+    step_contexts = sorted(contexts)
+    # timed region 2: the attention launch alone, back to back over the same
+    # replicas (no append in between), in 5 rounds of 50 calls whatever K is,
+    # so that the spread across rounds is reported
+    n_rounds, per_round = 5, 50
     a2_bytes = 0
     rounds_ms = []
+    attn_contexts = set()
     for r in range(n_rounds):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(per_round):
-            c = caches[(r * per_round + i) % L]
-            decodes[(r * per_round + i) % L]()
+        for j in range(per_round):
+            c = caches[(r * per_round + j) % L]
+            decodes[(r * per_round + j) % L]()
             a2_bytes += attn_bytes(w, c.n_tokens)
+            attn_contexts.add(c.n_tokens)
         e1.record(stream)
         rounds_ms.append((e0, e1))
     torch.cuda.synchronize()
@@ -292,17 +358,24 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "fp16",
+        "dtype_detail": ("2/4-bit integer codes; fp16 x fp16 matrix products whose fp32 "
+                         "scale-folded operands are split into fp16 high and low parts; fp32 "
+                         "accumulation, softmax and output"),
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
-                   "head_dim": w.D, "context": w.T0 + 1, "k_bits": w.k_bits, "v_bits": w.v_bits,
+                   "head_dim": w.D, "context": w.T0 + 1, "decode_steps": n_cyc,
+                   "k_bits": w.k_bits, "v_bits": w.v_bits,
                    "group": w.G, "residual": w.R, "layers_rotated": L,
-                   "storage": "packed codes, fp32 scale/zero, fp16 window; fp16 q"},
+                   "storage": "128-token records: packed codes, fp32 scales, fp16 zero points; "
+                              "fp16 window; fp16 q"},
         "step_call": "kivi_decode_step" if fused else "kivi_append + kivi_decode_attn",
+        "step_contexts_min_max": [step_contexts[0], step_contexts[-1]],
         "us_per_step": round(ms_step * 1e3, 2),
         "attn_us": round(attn_avg_ms * 1e3, 2),
         "attn_us_rounds_min_p50_max": [round(float(np.percentile(attn_ms, p)) * 1e3, 2)
                                        for p in (0, 50, 100)],
+        "attn_contexts_min_max": [min(attn_contexts), max(attn_contexts)],
         "attn_pct_of_peak": round(100 * attn_gbps / HBM_PEAK_GBPS, 1),
         "roofline": {"bound": "hbm", "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
@@ -311,7 +384,7 @@ def main():
                      "bytes_per_launch": a2_bytes // (n_rounds * per_round)},
     }
     if not args.no_pack:
-        del caches, base
+        del caches, base, appends, decodes, fused_steps
         torch.cuda.empty_cache()
         line["pack_full_prefill"] = time_pack(w, inp, dev, stream)
     if not args.no_cpu_baseline:

@@ -24,6 +24,10 @@ FLAGS = [
     # every rounding step as written: no implicit fusion of a multiply with an
     # add or a narrowing conversion (kernels call fmaf where they want one)
     "-ffp-contract=off",
+    # a work-counter draw by one lane stays one atomic whose result is read
+    # where the kernel reads it (the atomic optimizer would read it back at
+    # once, waiting for every memory operation in flight)
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

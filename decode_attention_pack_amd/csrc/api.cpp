@@ -9,6 +9,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <string>
 
 #include "../../include/kivi.h"
@@ -38,9 +39,9 @@ bool bits_ok(int bits) { return bits == 2 || bits == 4; }
 // Shape rules shared by every entry point.
 int check_shape(int32_t D, int32_t bits, int32_t G, const char *who) {
   if (!bits_ok(bits)) return fail(KIVI_ERR_INVALID_ARG, "%s: bits must be 2 or 4 (got %d)", who, bits);
-  if (G <= 0 || G % (32 / bits) != 0 || G > 256)
-    return fail(KIVI_ERR_INVALID_ARG, "%s: group %d must be a positive multiple of %d, at most 256",
-                who, G, 32 / bits);
+  if (G <= 0 || G % (32 / bits) != 0 || kivi::kRecTokens % G != 0)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: group %d must divide %d and be a multiple of %d", who, G,
+                kivi::kRecTokens, 32 / bits);
   if (D <= 0 || D > 256 || D % G != 0)
     return fail(KIVI_ERR_INVALID_ARG, "%s: head_dim %d must be a multiple of group %d, at most 256",
                 who, D, G);
@@ -65,39 +66,37 @@ int check_cache(const kivi_cache *c, const char *who) {
   if (c->residual <= 0 || c->residual % c->group != 0)
     return fail(KIVI_ERR_INVALID_ARG, "%s: residual %d must be a positive multiple of group %d", who,
                 c->residual, c->group);
-  if (c->capacity <= 0 || c->capacity % c->residual != 0)
-    return fail(KIVI_ERR_INVALID_ARG, "%s: capacity %lld must be a positive multiple of residual %d",
-                who, (long long)c->capacity, c->residual);
+  if (c->capacity <= 0 || c->capacity % c->residual != 0 || c->capacity % kivi::kRecTokens != 0)
+    return fail(KIVI_ERR_INVALID_ARG,
+                "%s: capacity %lld must be a positive multiple of residual %d and of %d", who,
+                (long long)c->capacity, c->residual, kivi::kRecTokens);
   if (c->n_tokens < 0 || c->n_tokens > c->capacity)
     return fail(KIVI_ERR_INVALID_ARG, "%s: n_tokens %lld outside [0, capacity]", who,
                 (long long)c->n_tokens);
-  if (!c->k_codes || !c->k_scale || !c->k_zero || !c->v_codes || !c->v_scale || !c->v_zero ||
-      !c->k_res || !c->v_res)
+  if (!c->blocks || !c->k_res || !c->v_res)
     return fail(KIVI_ERR_INVALID_ARG, "%s: a cache array pointer is NULL", who);
+  if (((uintptr_t)c->blocks & 15) != 0 || ((uintptr_t)c->k_res & 15) != 0 ||
+      ((uintptr_t)c->v_res & 15) != 0)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: blocks, k_res and v_res must be 16-byte aligned", who);
   return KIVI_OK;
 }
 
-int check_pack(const void *x, int32_t B, int32_t H, int64_t T, int32_t D, int32_t bits, int32_t G,
-               const void *codes, const void *scale, const void *zero, int64_t cap, int64_t off,
-               bool keys, const char *who) {
-  if (B <= 0 || H <= 0) return fail(KIVI_ERR_INVALID_ARG, "%s: B and H must be positive", who);
-  if ((int64_t)B * H > kMaxSlabs)
-    return fail(KIVI_ERR_INVALID_ARG, "%s: B x H = %lld passes %lld", who, (long long)B * H,
-                (long long)kMaxSlabs);
-  int rc = check_shape(D, bits, G, who);
+kivi::Layout layout_of(const kivi_cache *c) {
+  return kivi::make_layout(c->blocks, c->head_dim, c->k_bits, c->v_bits, c->group, c->capacity);
+}
+
+int check_pack(const kivi_cache *dst, const void *x, int64_t T, int64_t off, bool keys,
+               const char *who) {
+  int rc = check_cache(dst, who);
   if (rc) return rc;
   if (T < 0 || off < 0) return fail(KIVI_ERR_INVALID_ARG, "%s: T and offset must be >= 0", who);
-  if (cap <= 0 || cap % G != 0)
-    return fail(KIVI_ERR_INVALID_ARG, "%s: capacity %lld must be a positive multiple of group %d",
-                who, (long long)cap, G);
-  if (keys && (T % G != 0 || off % G != 0))
+  if (keys && (T % dst->group != 0 || off % dst->group != 0))
     return fail(KIVI_ERR_INVALID_ARG, "%s: T (%lld) and offset (%lld) must be multiples of group %d",
-                who, (long long)T, (long long)off, G);
-  if (off + T > cap)
+                who, (long long)T, (long long)off, dst->group);
+  if (off + T > dst->capacity)
     return fail(KIVI_ERR_CAPACITY, "%s: tokens [%lld, %lld) pass capacity %lld", who,
-                (long long)off, (long long)(off + T), (long long)cap);
-  if (T > 0 && (!x || !codes || !scale || !zero))
-    return fail(KIVI_ERR_INVALID_ARG, "%s: NULL pointer", who);
+                (long long)off, (long long)(off + T), (long long)dst->capacity);
+  if (T > 0 && !x) return fail(KIVI_ERR_INVALID_ARG, "%s: NULL input", who);
   return KIVI_OK;
 }
 
@@ -111,18 +110,26 @@ constexpr int kVectorStep = 128;    // tokens per step of the vector kernel's fo
 // many short ones (less per-split set-up and merge work).
 constexpr int kVectorWorkgroups = 2048;
 constexpr int kTargetWorkgroups = 4096;   // scalar kernel
-// Matrix kernel: block-role workgroups to aim for.  One wave per SIMD (1024
-// on 256 CUs) streaming longer splits measures faster than two waves per
-// SIMD with half the splits each; when the window role already fills more
-// than that many slots, twice as many shorter splits keep the SIMDs busy
-// while those finish.
-constexpr int kMatrixWorkgroups = 1024;
+// Compute units of the current device (the matrix kernel plans one
+// workgroup per CU); 256 when it cannot be queried.
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
 
 struct Plan {
   bool matrix = false;
   int64_t n_main = 0;           // tokens [0, n_main) in the matrix kernel's block role
-  int tps_matrix = 0;
-  int n_split_matrix = 0;
+  int n_groups_matrix = 0;      // matrix-kernel workgroups per slab
   int n_window = 0;             // 32-token chunks of [n_main, t) in its window role
   bool vector = false;          // vector kernel instead of the scalar one
   int tps_generic = 0;          // vector / scalar kernel (shapes the matrix kernel does not cover)
@@ -131,6 +138,8 @@ struct Plan {
 };
 
 int head_chunks(int n_rep) { return (n_rep + 7) / 8; }
+
+int64_t ceil_div(int64_t x, int64_t y) { return (x + y - 1) / y; }
 
 // Split plan.  Deterministic in (shape, n_tokens, options).
 Plan make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
@@ -148,20 +157,23 @@ Plan make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
     const int64_t n_lim = a.t_new >= a.R ? a.t_new - a.R : a.n_vq;
     p.n_main = (n_lim / kMatrixBlock) * kMatrixBlock;
     p.n_window = kivi::decode_matrix_window_chunks(a, p.n_main);
-    int64_t tps = (tps_req + kMatrixBlock - 1) / kMatrixBlock * kMatrixBlock;
-    if (tps == 0) {
-      // whole blocks per split, about kMatrixWorkgroups block-role workgroups
-      const int64_t window_wgs = (int64_t)p.n_window * units;
-      const int64_t target = window_wgs > kMatrixWorkgroups ? 2 * kMatrixWorkgroups
-                                                            : kMatrixWorkgroups;
-      const int64_t splits = max64(1, target / units);
-      const int64_t blocks = p.n_main / kMatrixBlock;
-      tps = max64(1, (blocks + splits - 1) / splits) * kMatrixBlock;
+    const int64_t blocks = p.n_main / kMatrixBlock;
+    const int waves = kivi::decode_matrix_waves(a);
+    int64_t groups;
+    if (tps_req == 0) {
+      // one workgroup per CU (two for the four-wave masked variant), no more
+      // than the blocks and window chunks keep busy
+      const int64_t per_cu = 8 / waves;
+      const int64_t target = max64(1, device_cus() * per_cu / units);
+      groups = std::min(target, max64(1, ceil_div(blocks + p.n_window, waves)));
+    } else {
+      // a workgroup per tps_req tokens (rounded up to whole blocks)
+      const int64_t tps = ceil_div(tps_req, kMatrixBlock) * kMatrixBlock;
+      groups = max64(1, ceil_div(p.n_main, tps));
     }
-    p.tps_matrix = (int)tps;
-    p.n_split_matrix = (int)((p.n_main + tps - 1) / tps);
-    // two waves per split, one partial slot each
-    p.S_total = 2 * p.n_split_matrix + p.n_window;
+    p.n_groups_matrix = (int)groups;
+    // one partial slot per wave, then one per window chunk
+    p.S_total = (int)(groups * waves + p.n_window);
     return p;
   }
   p.vector = (path == KIVI_PATH_AUTO || path == KIVI_PATH_VECTOR) &&
@@ -186,14 +198,20 @@ Plan make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
 
 // Upper bound on partial slots for any n_tokens <= capacity.
 int64_t max_slots(const kivi_cache *c, int32_t tps_req) {
-  // automatic plans split at least kMatrixBlock tokens at a time
-  const int64_t step = tps_req > 0 ? tps_req : kMatrixBlock;
-  // splits over the capacity (two partial slots per matrix-kernel split),
-  // plus the matrix kernel's window chunks (its window is at most one block +
-  // R tokens long)
-  return 2 * ((c->capacity + step - 1) / step) + (kMatrixBlock + (int64_t)c->residual + 31) / 32 + 1;
+  // the matrix kernel's window is at most one block + R tokens long
+  const int64_t n_window = (kMatrixBlock + (int64_t)c->residual + 31) / 32 + 1;
+  const int64_t blocks = ceil_div(c->capacity, kMatrixBlock);
+  if (tps_req == 0) {
+    // matrix kernel: at most ceil((blocks + window) / waves) workgroups of at
+    // most 8 waves; the other kernels split at least 128 tokens at a time
+    return blocks + 2 * n_window + 8 + 1;
+  }
+  // matrix kernel: one workgroup of at most 8 waves per tps_req tokens
+  // (rounded up to whole blocks); the other kernels: one slot per split
+  const int64_t m = 8 * ceil_div(c->capacity, ceil_div(tps_req, kMatrixBlock) * kMatrixBlock);
+  const int64_t g = ceil_div(c->capacity, tps_req);
+  return std::max(m, g) + 8 + n_window + 1;
 }
-
 
 }  // namespace
 
@@ -212,41 +230,43 @@ const char *kivi_status_string(int status) {
 
 const char *kivi_last_error(void) { return g_last_error.c_str(); }
 
-int kivi_pack_keys(const void *k_fp16, int32_t B, int32_t H, int64_t T, int32_t D, int32_t bits,
-                   int32_t group, uint32_t *codes, float *scale, float *zero,
-                   int64_t dst_capacity, int64_t dst_token_offset, void *stream) {
-  int rc = check_pack(k_fp16, B, H, T, D, bits, group, codes, scale, zero, dst_capacity,
-                      dst_token_offset, true, "kivi_pack_keys");
+size_t kivi_record_bytes(int32_t head_dim, int32_t k_bits, int32_t v_bits, int32_t group) {
+  if (head_dim <= 0 || head_dim > 256) return 0;
+  return (size_t)kivi::make_layout(nullptr, head_dim, k_bits, v_bits, group, 0).rec;
+}
+
+int kivi_pack_keys(const kivi_cache *dst, const void *k_fp16, int64_t T, int64_t dst_token_offset,
+                   void *stream) {
+  int rc = check_pack(dst, k_fp16, T, dst_token_offset, true, "kivi_pack_keys");
   if (rc) return rc;
   if (T == 0) return KIVI_OK;
-  if (kivi::pack_tiles_supported(D, group, bits))
-    return hip_status(kivi::launch_key_tiles((const uint16_t *)k_fp16, T, T, dst_token_offset / group,
-                                             (int64_t)B * H, bits, group, D, dst_capacity, codes,
-                                             scale, zero, (hipStream_t)stream),
+  const kivi::Layout L = layout_of(dst);
+  const int64_t BH = (int64_t)dst->batch * dst->n_kv_heads;
+  const int G = dst->group, D = dst->head_dim;
+  if (kivi::pack_tiles_supported(D, G, dst->k_bits))
+    return hip_status(kivi::launch_key_tiles((const uint16_t *)k_fp16, T, T, dst_token_offset / G,
+                                             BH, L, (hipStream_t)stream),
                       "kivi_pack_keys");
   kivi::TokenSource src{nullptr, (const uint16_t *)k_fp16, dst_token_offset, T, 1, D};
-  return hip_status(kivi::launch_key_groups(src, dst_token_offset / group, T / group,
-                                            (int64_t)B * H, bits, group, D, dst_capacity, codes,
-                                            scale, zero, (hipStream_t)stream),
+  return hip_status(kivi::launch_key_groups(src, dst_token_offset / G, T / G, BH, L,
+                                            (hipStream_t)stream),
                     "kivi_pack_keys");
 }
 
-int kivi_pack_values(const void *v_fp16, int32_t B, int32_t H, int64_t T, int32_t D, int32_t bits,
-                     int32_t group, uint32_t *codes, float *scale, float *zero,
-                     int64_t dst_capacity, int64_t dst_token_offset, void *stream) {
-  int rc = check_pack(v_fp16, B, H, T, D, bits, group, codes, scale, zero, dst_capacity,
-                      dst_token_offset, false, "kivi_pack_values");
+int kivi_pack_values(const kivi_cache *dst, const void *v_fp16, int64_t T,
+                     int64_t dst_token_offset, void *stream) {
+  int rc = check_pack(dst, v_fp16, T, dst_token_offset, false, "kivi_pack_values");
   if (rc) return rc;
   if (T == 0) return KIVI_OK;
-  if (kivi::pack_tiles_supported(D, group, bits))
+  const kivi::Layout L = layout_of(dst);
+  const int64_t BH = (int64_t)dst->batch * dst->n_kv_heads;
+  const int G = dst->group, D = dst->head_dim;
+  if (kivi::pack_tiles_supported(D, G, dst->v_bits))
     return hip_status(kivi::launch_value_tokens((const uint16_t *)v_fp16, T, T, dst_token_offset,
-                                                (int64_t)B * H, bits, group, D, dst_capacity,
-                                                codes, scale, zero, (hipStream_t)stream),
+                                                BH, L, (hipStream_t)stream),
                       "kivi_pack_values");
   kivi::TokenSource src{nullptr, (const uint16_t *)v_fp16, dst_token_offset, T, 1, D};
-  return hip_status(kivi::launch_value_rows(src, dst_token_offset, T, (int64_t)B * H, bits, group,
-                                            D, dst_capacity, codes, scale, zero,
-                                            (hipStream_t)stream),
+  return hip_status(kivi::launch_value_rows(src, dst_token_offset, T, BH, L, (hipStream_t)stream),
                     "kivi_pack_values");
 }
 
@@ -261,6 +281,7 @@ int kivi_append(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp16, i
     return fail(KIVI_ERR_CAPACITY, "kivi_append: %lld + %lld tokens pass capacity %lld",
                 (long long)c->n_tokens, (long long)n_new, (long long)c->capacity);
   hipStream_t s = (hipStream_t)stream;
+  const kivi::Layout L = layout_of(c);
   const int64_t R = c->residual, G = c->group, D = c->head_dim;
   const int64_t BH = (int64_t)c->batch * c->n_kv_heads;
   const int64_t t0 = c->n_tokens, t1 = t0 + n_new;
@@ -270,16 +291,13 @@ int kivi_append(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp16, i
     // decode step: one fused kernel, plus the key block when this token completes one
     rc = hip_status(kivi::launch_append_one((const uint16_t *)k_new_fp16,
                                             (const uint16_t *)v_new_fp16, c->k_res, c->v_res, t0,
-                                            BH, (int)R, (int)D, (int)G, c->v_bits, c->capacity,
-                                            kq1 == kq0, c->v_codes, c->v_scale, c->v_zero, s),
+                                            BH, (int)R, kq1 == kq0, L, s),
                     "kivi_append (step)");
     if (rc) return rc;
     if (kq1 > kq0) {
       kivi::TokenSource ksrc{c->k_res, (const uint16_t *)k_new_fp16, t0, 1, (int32_t)R,
                              (int32_t)D};
-      rc = hip_status(kivi::launch_key_groups(ksrc, kq0 / G, (kq1 - kq0) / G, BH, c->k_bits,
-                                              (int)G, (int)D, c->capacity, c->k_codes,
-                                              c->k_scale, c->k_zero, s),
+      rc = hip_status(kivi::launch_key_groups(ksrc, kq0 / G, (kq1 - kq0) / G, BH, L, s),
                       "kivi_append (keys)");
       if (rc) return rc;
     }
@@ -289,14 +307,11 @@ int kivi_append(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp16, i
   if (t0 == 0 && kivi::pack_tiles_supported((int)D, (int)G, c->v_bits) &&
       kivi::pack_tiles_supported((int)D, (int)G, c->k_bits)) {
     // prefill into an empty cache: every quantized token comes from the input
-    rc = hip_status(kivi::launch_value_tokens((const uint16_t *)v_new_fp16, n_new, vq1, 0, BH,
-                                              c->v_bits, (int)G, (int)D, c->capacity,
-                                              c->v_codes, c->v_scale, c->v_zero, s),
+    rc = hip_status(kivi::launch_value_tokens((const uint16_t *)v_new_fp16, n_new, vq1, 0, BH, L,
+                                              s),
                     "kivi_append (values)");
     if (rc) return rc;
-    rc = hip_status(kivi::launch_key_tiles((const uint16_t *)k_new_fp16, n_new, kq1, 0, BH, c->k_bits,
-                                           (int)G, (int)D, c->capacity, c->k_codes, c->k_scale,
-                                           c->k_zero, s),
+    rc = hip_status(kivi::launch_key_tiles((const uint16_t *)k_new_fp16, n_new, kq1, 0, BH, L, s),
                     "kivi_append (keys)");
     if (rc) return rc;
     rc = hip_status(kivi::launch_write_window((const uint16_t *)k_new_fp16,
@@ -310,16 +325,13 @@ int kivi_append(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp16, i
   // 1. values leaving the window (read old slots before they are reused)
   kivi::TokenSource vsrc{c->v_res, (const uint16_t *)v_new_fp16, t0, n_new, (int32_t)R,
                          (int32_t)D};
-  rc = hip_status(kivi::launch_value_rows(vsrc, vq0, vq1 - vq0, BH, c->v_bits, (int)G, (int)D,
-                                          c->capacity, c->v_codes, c->v_scale, c->v_zero, s),
+  rc = hip_status(kivi::launch_value_rows(vsrc, vq0, vq1 - vq0, BH, L, s),
                   "kivi_append (values)");
   if (rc) return rc;
   // 2. complete R-blocks of keys
   kivi::TokenSource ksrc{c->k_res, (const uint16_t *)k_new_fp16, t0, n_new, (int32_t)R,
                          (int32_t)D};
-  rc = hip_status(kivi::launch_key_groups(ksrc, kq0 / G, (kq1 - kq0) / G, BH, c->k_bits, (int)G,
-                                          (int)D, c->capacity, c->k_codes, c->k_scale,
-                                          c->k_zero, s),
+  rc = hip_status(kivi::launch_key_groups(ksrc, kq0 / G, (kq1 - kq0) / G, BH, L, s),
                   "kivi_append (keys)");
   if (rc) return rc;
   // 3. the new tokens that stay in fp16 take their slots
@@ -378,12 +390,7 @@ int decode_call(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, cons
                 need);
 
   kivi::DecodeArgs a{};
-  a.k_codes = c->k_codes;
-  a.k_scale = c->k_scale;
-  a.k_zero = c->k_zero;
-  a.v_codes = c->v_codes;
-  a.v_scale = c->v_scale;
-  a.v_zero = c->v_zero;
+  a.L = layout_of(c);
   a.k_res = c->k_res;
   a.v_res = c->v_res;
   a.q = (const uint16_t *)q_fp16;
@@ -421,7 +428,7 @@ int decode_call(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, cons
   a.S_total = p.S_total;
   hipStream_t s = (hipStream_t)stream;
   if (p.matrix)
-    rc = hip_status(kivi::launch_decode_matrix(a, p.n_main, p.tps_matrix, p.n_split_matrix, s),
+    rc = hip_status(kivi::launch_decode_matrix(a, p.n_main, p.n_groups_matrix, s),
                     "kivi_decode_attn (matrix)");
   else if (p.vector)
     rc = hip_status(kivi::launch_decode_vector(a, p.tps_generic, p.n_split_generic, s),
@@ -473,6 +480,9 @@ int kivi_decode_step(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp
     return fail(KIVI_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes,
                 need);
   kivi::DecodeArgs probe{};
+  probe.L = layout_of(c);
+  probe.k_res = c->k_res;
+  probe.v_res = c->v_res;
   probe.kb = c->k_bits;
   probe.vb = c->v_bits;
   probe.G = c->group;

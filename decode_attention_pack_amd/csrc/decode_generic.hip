@@ -77,14 +77,13 @@ decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int
   const int c_own = tid % D;           // value channel owned in the V phase
   const int n_par = kThreads / D;      // token parities sharing a channel
   const int par = tid / D;
-  // value code word, bit offset, scale and zero rows of channel c_own
+  // value code word, bit offset and channel group of channel c_own
   const int vper = 32 / a.vb;
-  const int64_t vwords = D / vper;     // code words per token
-  const uint32_t *vcw = a.v_codes + bh * a.cap * vwords + c_own / vper;
+  const int vword = c_own / vper;
   const int vsh = a.vb * (c_own % vper);
   const uint32_t vmsk = (1u << a.vb) - 1u;
-  const float *vsc = a.v_scale + (bh * (D / a.G) + c_own / a.G) * a.cap;
-  const float *vzr = a.v_zero + (bh * (D / a.G) + c_own / a.G) * a.cap;
+  const int vgrp = c_own / a.G;
+  const Layout &L = a.L;
   __syncthreads();
 
   for (int64_t c0 = s0; c0 < s1; c0 += kChunk) {
@@ -102,15 +101,15 @@ decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int
         const int words = a.G / per;
         const int64_t g = tau / a.G;
         const int e = (int)(tau - g * a.G);
-        const int64_t zb = (bh * (a.cap / a.G) + g) * D;
-        const uint32_t *cw = a.k_codes + zb * words + e / per;
-        const float *ks = a.k_scale + zb;
-        const float *kz = a.k_zero + zb;
+        // the group's channels are consecutive in its record
+        const uint32_t *cw = L.key_codes(bh, g, 0) + e / per;
+        const float *ks = L.key_scale(bh, g, 0);
+        const uint16_t *kz = L.key_zero(bh, g, 0);
         const int sh = a.kb * (e % per);
         const uint32_t msk = (1u << a.kb) - 1u;
         for (int c = 0; c < D; ++c) {
           const uint32_t code = (cw[c * words] >> sh) & msk;
-          const float k = __fadd_rn(__fmul_rn((float)code, ks[c]), kz[c]);
+          const float k = __fadd_rn(__fmul_rn((float)code, ks[c]), h2f(kz[c]));
 #pragma unroll
           for (int j = 0; j < NH; ++j) sc[j] = fmaf(q_s[j][c], k, sc[j]);
         }
@@ -171,8 +170,9 @@ decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int
     for (int64_t tv = c0 + par; tv < cend; tv += n_par) {
       float v;
       if (tv < a.n_vq) {
-        const uint32_t code = (vcw[tv * vwords] >> vsh) & vmsk;
-        v = __fadd_rn(__fmul_rn((float)code, vsc[tv]), vzr[tv]);
+        const uint32_t code = (L.value_codes(bh, tv)[vword] >> vsh) & vmsk;
+        v = __fadd_rn(__fmul_rn((float)code, *L.value_scale(bh, tv, vgrp)),
+                      h2f(*L.value_zero(bh, tv, vgrp)));
       } else {
         v = h2f(a.v_res[(bh * a.R + tv % a.R) * D + c_own]);
       }

@@ -7,14 +7,17 @@
 // (implementation-grade)", item 5: scores q.deq(K)^T over the quantized keys,
 // softmax, then P.deq(V) over the quantized values, plus the fp16 window.
 //
-// One launch does the whole call.  Its workgroups (one wave each) take one of
-// two roles for one (batch row, KV head) slab:
-//  * block role: the tokens whose key AND value are both quantized, in whole
-//    blocks of 128, on the matrix cores (one split of the slab each);
-//  * window role: the rest -- the fp16 window and the quantized tokens past
-//    the last whole block -- 32 tokens per workgroup, scalar fp32.
-// Each workgroup writes a partial (acc[128], m, l) per query head; the
-// combine kernel merges them with the log-sum-exp rule.
+// One launch does the whole call.  A workgroup of eight waves (one per CU,
+// each wave with LDS of its own) takes a share of one (batch row, KV head)
+// slab; its waves draw the share's work items from a counter in LDS:
+//  * window chunks: the fp16 window and the quantized tokens past the last
+//    whole block, 32 tokens each, scalar fp32 (drawn first);
+//  * blocks: tokens whose key AND value are both quantized, 128 at a time,
+//    on the matrix cores.
+// Waves that issue faster (the oldest on a SIMD) take more items, so the
+// share ends at about the same time on every wave.  Each wave writes a
+// partial (acc[128], m, l) per query head for its blocks and one per window
+// chunk; the combine kernel merges them with the log-sum-exp rule.
 //
 // Algebra.  With a key group's scale s and zero z (per channel c, 32 tokens),
 //   q . K_tau = sum_c (q_c s_c) code_{c,tau} + sum_c q_c z_c,
@@ -38,12 +41,14 @@
 // one instruction.
 //
 // Memory pipeline.  A block's key part (codes, scales, zeros: 8 KB) and value
-// part (8 KB) have one LDS buffer each, filled by global->LDS DMA.  The next
-// block's key part is requested as soon as the current one has been read into
-// registers, and likewise for the value part, so each DMA overlaps the other
-// half's arithmetic.  With ~19 KB of LDS per workgroup, eight workgroups (two
-// waves per SIMD) fit on a CU.
+// part (8 KB) have one LDS buffer each per wave, filled by global->LDS DMA.
+// The next block's key part is requested as soon as the current one has been
+// read into registers, and likewise for the value part, so each DMA overlaps
+// the other half's arithmetic.  With ~19 KB of LDS per wave, the eight waves
+// (two per SIMD) of one workgroup fill a CU.
 #include <math.h>
+
+#include <type_traits>
 
 #include "kivi_internal.hpp"
 #include "lane_ops.hpp"
@@ -62,34 +67,77 @@ constexpr int kD = 128;
 constexpr int kG = 32;
 constexpr int kBT = 128;       // tokens per block (block role)
 constexpr int kWT = 32;        // tokens per chunk (window role)
-constexpr int kStageDma = 8;   // DMA instructions per key or value part
+constexpr int kStageDma = 7;   // DMA instructions per key or value part
+// A record of the packed store at this shape (2-bit keys and values, G 32,
+// head_dim 128): byte offsets of its sections and its size.
+constexpr int kRecKc = 0, kRecKs = 4096, kRecKz = 6144;
+constexpr int kRecVc = 7168, kRecVs = 11264, kRecVz = 13312, kRecBytes = 14336;
 constexpr int kPRow = 132;     // floats per probability row in LDS (16-byte pad)
 
-// A block's key part and value part in LDS: codes as they sit in HBM, the
-// scale and zero rows rotated (see rot_chunk).
+// A block's key part and value part in LDS: codes as they sit in the
+// record, the scale and zero rows rotated (see rot_chunk, zrot_off).  The
+// window role stages up to 8 KB in each (32 fp16 rows), hence the padding.
 struct alignas(16) KStage {
   uint32_t kc[1024];   // 4 key groups x 128 channels x 2 words
   float ks[512];       // [4 groups][128 channels]
-  float kz[512];
+  uint16_t kz[512];    // [4 groups][128 channels], fp16
+  uint32_t pad[256];
 };
 struct alignas(16) VStage {
   uint32_t vc[1024];   // 128 tokens x 8 words
   float vs[512];       // [4 channel groups][128 tokens]
-  float vz[512];
+  uint16_t vz[512];    // [4 channel groups][128 tokens], fp16
+  uint32_t pad[256];
 };
 
-__device__ __forceinline__ void dma16(const void *g, lds_void *l) {
-  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+// Global->LDS copies (16 or 4 bytes per lane; lane l's bytes land at LDS
+// offset 16 l (4 l) from `l`).  They are written as inline assembly with the
+// LDS address in M0, so that the compiler does not track them: it cannot
+// tell which LDS buffer a copy fills, and would make every LDS read wait
+// for all copies in flight, including those filling the other buffer.  The
+// kernel waits for them itself (wait_vm), counting every vector-memory
+// operation it issues.  The instructions have no result registers.  Each
+// starts with five wait states, which the hardware needs between a VALU
+// write of an SGPR (the readfirstlane of the base address) and a
+// vector-memory read of it, and between an M0 write and an LDS DMA; the
+// compiler inserts them for its own instructions but cannot see into
+// inline assembly.
+//   dma16:   per-lane 64-bit source address
+//   dma16o:  uniform base + per-lane 32-bit byte offset (the base stays in
+//            scalar registers)
+//   dma16nt: the same with the nontemporal hint, for the record stream: each
+//            record is read once per call, and streaming it past the caches
+//            measured ~13% more HBM bandwidth (6.6 against 5.85 TB/s for a
+//            plain read of the records)
+//   dma4o:   4 bytes per lane, uniform base + offset
+__device__ __forceinline__ uint32_t lds_m0(lds_void *l) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l);
 }
-
-// Global->LDS copy of 16 bytes per lane from a uniform base plus a 32-bit
-// per-lane byte offset, so the hardware takes the base from scalar registers
-// and the streams share a few offset registers.
+// A wave-uniform address, moved to scalar registers.
+__device__ __forceinline__ const void *uniform_ptr(const void *p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void dma16(const void *g, lds_void *l) {
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_m0(l))
+               : "memory");
+}
 __device__ __forceinline__ void dma16o(const void *base, uint32_t off, lds_void *l) {
-  __builtin_amdgcn_global_load_lds((const char *)base + off, l, 16, 0, 0);
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
+               "{m0}"(lds_m0(l))
+               : "memory");
+}
+__device__ __forceinline__ void dma16nt(const void *base, uint32_t off, lds_void *l) {
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(off), "s"(uniform_ptr(base)),
+               "{m0}"(lds_m0(l))
+               : "memory");
 }
 __device__ __forceinline__ void dma4o(const void *base, uint32_t off, lds_void *l) {
-  __builtin_amdgcn_global_load_lds((const char *)base + off, l, 4, 0, 0);
+  asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
+               "{m0}"(lds_m0(l))
+               : "memory");
 }
 
 // Rows of 128 floats (a key group's scales or zeros over channels, a value
@@ -99,27 +147,36 @@ __device__ __forceinline__ void dma4o(const void *base, uint32_t off, lds_void *
 __device__ __forceinline__ int rot_chunk(int r, int k) { return (k + r) & 31; }
 // float offset, within a block of four rows, of columns [c, c + 4) of row r
 __device__ __forceinline__ int rot_off(int r, int c) { return r * 128 + rot_chunk(r, c >> 2) * 4; }
+// Rows of 128 fp16 zeros (256 bytes) are rotated the same way over their 16
+// chunks: the half offset of columns [c, c + 8) (c a multiple of 8) of row r.
+__device__ __forceinline__ int zrot_off(int r, int c) { return r * 128 + (((c >> 3) + r) & 15) * 8; }
 
 // Per-lane byte offsets of the block DMA.  One DMA instruction fills two
-// rotated rows (lanes 0-31 row 2i, lanes 32-63 row 2i + 1): lane l writes
-// LDS chunk l % 32 of its row, so it reads source chunk (l % 32 - row) % 32.
-// lin: lane * 16 (unrotated runs); krot[i]: key scale/zero rows 2i, 2i + 1
-// (contiguous in HBM); vrot[i]: value scale/zero rows 2i, 2i + 1 (cap floats
-// apart in HBM).
+// rotated rows of 128 floats (lanes 0-31 row 2i, lanes 32-63 row 2i + 1):
+// lane l writes LDS chunk l % 32 of its row, so it reads source chunk
+// (l % 32 - row) % 32.  One instruction fills the four rotated rows of 128
+// fp16 zeros (16 lanes per row) the same way.
+// lin: lane * 16 (unrotated runs); rot[i]: scale rows 2i, 2i + 1; zrot: the
+// zero rows.
 struct DmaOffsets {
   uint32_t lin;
-  uint32_t krot[2];
-  uint32_t vrot[2];
-  __device__ DmaOffsets(const DecodeArgs &a, int lane) : lin((uint32_t)lane * 16u) {
+  uint32_t rot[2];
+  uint32_t zrot;
+  __device__ DmaOffsets(int lane) : lin((uint32_t)lane * 16u) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = 2 * i + (lane >> 5);
-      const uint32_t src = (uint32_t)((lane - row) & 31) * 16u;
-      krot[i] = (uint32_t)(lane >> 5) * 512u + src;
-      vrot[i] = (uint32_t)((int64_t)(lane >> 5) * a.cap * 4) + src;
+      rot[i] = (uint32_t)(lane >> 5) * 512u + (uint32_t)((lane - row) & 31) * 16u;
     }
+    const int zr = lane >> 4;
+    zrot = (uint32_t)zr * 256u + (uint32_t)(((lane & 15) - zr) & 15) * 16u;
   }
 };
+
+// Start of record `blk` (tokens [128 blk, 128 blk + 128)) of slab bh.
+__device__ __forceinline__ const uint8_t *record_of(const DecodeArgs &a, int64_t bh, int64_t blk) {
+  return a.L.blocks + (bh * a.L.nrec + blk) * (int64_t)kRecBytes;
+}
 
 // Key part of block `blk` (tokens [128 blk, 128 blk + 128)) of slab bh:
 // kStageDma DMA instructions, plus 2 for the mask when there is one.
@@ -127,17 +184,13 @@ template <bool MASKED>
 __device__ __forceinline__ void stage_keys(const DecodeArgs &a, int64_t bh, int64_t blk,
                                            KStage *s, float *mask_s, const DmaOffsets &o,
                                            int lane) {
-  const int64_t base = bh * (a.cap / kG) + blk * (kBT / kG);
-  const uint32_t *kc = a.k_codes + base * (kD * 2);
-  const float *ks = a.k_scale + base * kD;
-  const float *kz = a.k_zero + base * kD;
+  const uint8_t *rec = record_of(a, bh, blk);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dma16o(kc + i * 256, o.lin, (lds_void *)(s->kc + i * 256));
+  for (int i = 0; i < 4; ++i) dma16nt(rec + kRecKc + i * 1024, o.lin, (lds_void *)(s->kc + i * 256));
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    dma16o(ks + i * 256, o.krot[i], (lds_void *)(s->ks + i * 256));
-    dma16o(kz + i * 256, o.krot[i], (lds_void *)(s->kz + i * 256));
-  }
+  for (int i = 0; i < 2; ++i)
+    dma16nt(rec + kRecKs + i * 1024, o.rot[i], (lds_void *)(s->ks + i * 256));
+  dma16nt(rec + kRecKz, o.zrot, (lds_void *)s->kz);
   if (MASKED) {
     // dword copies: a mask row need not be 16-byte aligned
     const float *m = a.mask + (bh / a.H) * a.t + blk * kBT;
@@ -149,16 +202,13 @@ __device__ __forceinline__ void stage_keys(const DecodeArgs &a, int64_t bh, int6
 // Value part of block `blk`: kStageDma DMA instructions.
 __device__ __forceinline__ void stage_values(const DecodeArgs &a, int64_t bh, int64_t blk,
                                              VStage *s, const DmaOffsets &o) {
-  const int64_t tau0 = blk * kBT;
-  const uint32_t *vc = a.v_codes + (bh * a.cap + tau0) * 8;
+  const uint8_t *rec = record_of(a, bh, blk);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dma16o(vc + i * 256, o.lin, (lds_void *)(s->vc + i * 256));
+  for (int i = 0; i < 4; ++i) dma16nt(rec + kRecVc + i * 1024, o.lin, (lds_void *)(s->vc + i * 256));
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int64_t off = (bh * 4 + 2 * i) * a.cap + tau0;
-    dma16o(a.v_scale + off, o.vrot[i], (lds_void *)(s->vs + i * 256));
-    dma16o(a.v_zero + off, o.vrot[i], (lds_void *)(s->vz + i * 256));
-  }
+  for (int i = 0; i < 2; ++i)
+    dma16nt(rec + kRecVs + i * 1024, o.rot[i], (lds_void *)(s->vs + i * 256));
+  dma16nt(rec + kRecVz, o.zrot, (lds_void *)s->vz);
 }
 
 // LDS transpose read, issued as inline assembly: the compiler's builtin for it
@@ -262,12 +312,33 @@ struct Lds {
   float *alpha;        // [4]
 };
 
-// Matrix-core role: split `split` covers the fully quantized tokens
-// [split * tps, min(n_main, (split + 1) * tps)) in blocks of 128.
+// The workgroup's waves take their work -- window chunks first, then blocks
+// -- from a counter in LDS: item = the counter's value before the wave's
+// add.  Faster waves take more items, which evens out the differences in
+// issue share between the waves of a CU.  Lane 0 adds; every lane gets the
+// item.
+__device__ __forceinline__ int draw_item(int *ctr, int lane) {
+  int v = 0;
+  if (lane == 0) v = atomicAdd(ctr, 1);
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+// The blocks of one workgroup: block index j (0 <= j < nb) stands for block
+// b0 + (j + rot) % nb of the slab; the counter's item n_skip + j is block j.
+struct BlockShare {
+  int64_t b0, nb, rot;
+  int n_skip;
+  int *ctr;
+};
+
+// Matrix-core role: blocks of the workgroup's share (tokens whose key and
+// value are both quantized, 128 per block), starting with block `first` and
+// continuing with the blocks the wave draws, accumulated into the partial
+// in slot `slot`.
 template <int NREP, bool MASKED>
-__device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, int tps,
-                                           int split, int wave, int hk, int b, const Lds &L,
-                                           KStage *__restrict__ kbuf,
+__device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare &sh,
+                                           int64_t first, int slot, int hk, int b,
+                                           const Lds &L, KStage *__restrict__ kbuf,
                                            VStage *__restrict__ vbuf) {
   static_assert(NREP == 1 || NREP == 2 || NREP == 4, "query heads per KV head");
   constexpr int GA = 16 / NREP;       // key groups per A operand
@@ -277,14 +348,10 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
   const int i = lane & 15;
   const int kg = lane >> 4;
   const int64_t bh = (int64_t)b * a.H + hk;
-  const int64_t blk_begin = (int64_t)split * tps / kBT;
-  int64_t blk_end = ((int64_t)split + 1) * tps / kBT;
-  if (blk_end * kBT > n_main) blk_end = n_main / kBT;
-  if (blk_end - blk_begin <= wave) {
-    // a one-block split leaves the second wave nothing: an empty partial
+  if (first >= sh.nb) {
+    // no block for this wave: an empty partial
     if (lane < NREP) {
-      float *dst = a.part + (((int64_t)b * a.Hq + hk * NREP + lane) * a.S_total + 2 * split + wave) *
-                                (kD + 4);
+      float *dst = a.part + (((int64_t)b * a.Hq + hk * NREP + lane) * a.S_total + slot) * (kD + 4);
       *(float2 *)(dst + kD) = make_float2(-INFINITY, 0.0f);
     }
     return;
@@ -304,32 +371,19 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
 
   // q of the NREP heads (NREP rows of 256 bytes, contiguous) is copied into
   // the probability buffer by the first DMA, ahead of the first block's
-  // copies; vmcnt completes in order, so waiting for q alone lets the block
-  // stream in meanwhile.  Every split holds at least one block
-  // (launch_decode_matrix rejects plans where one does not), so the copies
-  // are unconditional.  Lanes past the q rows re-read the last 16 bytes.
-  const DmaOffsets dmo(a, lane);
+  // copies; the copies complete in order, so waiting for q alone lets the
+  // block stream in meanwhile.  Lanes past the q rows re-read the last 16
+  // bytes.
+  const DmaOffsets dmo(lane);
   const uint16_t *q_lds = (const uint16_t *)&L.p[0][0];
   dma16o(a.q + ((int64_t)b * a.Hq + hk * NREP) * kD, (uint32_t)min(lane, NREP * 16 - 1) * 16u,
          (lds_void *)&L.p[0][0]);
-  // The split's blocks are visited from a starting block that a hash of
-  // (slab, split) picks, wrapping around.  Every slab's arrays sit a multiple
-  // of the capacity apart, so workgroups walking their splits in lock-step
-  // from the first block hit HBM channels in step for some capacities (13%
-  // slower at 257 x 128 tokens); scattered starting points break that up.
-  // The order only changes the rounding order of the online softmax.
-  const int64_t nblk = blk_end - blk_begin;
-  const int64_t rot =
-      (int64_t)((((uint32_t)bh * 2654435761u) ^ ((uint32_t)split * 2246822519u)) >> 8) % nblk;
-  // The two waves of the workgroup share the split: wave w takes the blocks
-  // at positions w, w + 2, ... of the rotated order and writes partial slot
-  // 2 split + w.
-  const int slot = 2 * split + wave;
-  const int64_t nb_w = (nblk - wave + 1) / 2;
-  const int64_t first = blk_begin + (wave + rot) % nblk;
-  stage_keys<MASKED>(a, bh, first, kbuf, L.mask, dmo, lane);
-  stage_values(a, bh, first, vbuf, dmo);
-  wait_vm<KDMA + kStageDma>();
+  {
+    const int64_t blk = sh.b0 + (first + sh.rot) % sh.nb;
+    stage_keys<MASKED>(a, bh, blk, kbuf, L.mask, dmo, lane);
+    stage_values(a, bh, blk, vbuf, dmo);
+  }
+  wait_vm<KDMA + kStageDma>();   // q
 
   // q of head h_a at this lane's 32 key channels c0(ks) + j, with
   // c0(ks) = 64 (ks / 2) + 16 kg + 8 (ks % 2)
@@ -379,11 +433,12 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
 #pragma unroll
   for (int g = 0; g < 4; ++g) dv[g][0] = dv[g][1] = (f4){0, 0, 0, 0};
 
-  for (int64_t it = 0; it < nb_w; ++it) {
-    const bool has_next = it + 1 < nb_w;
-    const int64_t nxt = blk_begin + (wave + 2 * (it + 1) + rot) % nblk;   // the block staged next
+  // One block, whose key part has arrived.  With a next block (block nxt),
+  // its key part and then its value part are requested as soon as this
+  // block's key part and value part have been read into registers.
+  auto block = [&](auto next_tag, int64_t nxt) __attribute__((always_inline)) {
+    constexpr bool has_next = decltype(next_tag)::value;
     // ================= key half =================
-    wait_vm<kStageDma>();            // key part of this block in; its value part may still fly
     const KStage &kst = *kbuf;
     i2 xk[8];                        // [group g][64-channel half rho]
 #pragma unroll
@@ -410,20 +465,18 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
       const int c0 = 64 * (ks >> 1) + 16 * kg + 8 * (ks & 1);
       const f4 s0 = *(const f4 *)(kst.ks + rot_off(g_a, c0));
       const f4 s1 = *(const f4 *)(kst.ks + rot_off(g_a, c0 + 4));
-      const f4 z0 = *(const f4 *)(kst.kz + rot_off(g_a, c0));
-      const f4 z1 = *(const f4 *)(kst.kz + rot_off(g_a, c0 + 4));
+      const h8 zv = *(const h8 *)(kst.kz + zrot_off(g_a, c0));
       const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-      const float zv[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
         split_mul2(qa[ks][j], sv[j], qa[ks][j + 1], sv[j + 1], ah[ks], al[ks], j);
-        bz = fmaf(qa[ks][j], zv[j], bz);
-        bz = fmaf(qa[ks][j + 1], zv[j + 1], bz);
+        bz = fmaf(qa[ks][j], (float)zv[j], bz);
+        bz = fmaf(qa[ks][j + 1], (float)zv[j + 1], bz);
       }
     }
     // every read of the key part has completed: request the next one
     wait_regs(xk);
-    if (has_next) stage_keys<MASKED>(a, bh, nxt, kbuf, L.mask, dmo, lane);
+    if constexpr (has_next) stage_keys<MASKED>(a, bh, nxt, kbuf, L.mask, dmo, lane);
 
     bz = group_sum(bz);
     if (kg == 0) L.bias[i] = bz;
@@ -478,7 +531,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
     }
 
     // ================= value half =================
-    if (has_next)
+    if constexpr (has_next)
       wait_vm<KDMA>();               // value part of this block in; the next key part may fly
     else
       wait_vm<0>();
@@ -500,6 +553,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
       }
       zt *= L.alpha[h_v];
     }
+    // A = hi/lo(p s) for rows (h_v, c_v); zt += p . z
     h8 vh[2][2], vl[2][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -510,22 +564,20 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
         const f4 p1 = *(const f4 *)(&L.p[h_v][t0 + 4]);
         const f4 s0 = *(const f4 *)(vst.vs + rot_off(c_v, t0));
         const f4 s1 = *(const f4 *)(vst.vs + rot_off(c_v, t0 + 4));
-        const f4 z0 = *(const f4 *)(vst.vz + rot_off(c_v, t0));
-        const f4 z1 = *(const f4 *)(vst.vz + rot_off(c_v, t0 + 4));
+        const h8 zv = *(const h8 *)(vst.vz + zrot_off(c_v, t0));
         const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
         const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-        const float zv[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
 #pragma unroll
         for (int j = 0; j < 8; j += 2) {
           split_mul2(pv[j], sv[j], pv[j + 1], sv[j + 1], vh[u][d], vl[u][d], j);
-          zt = fmaf(pv[j], zv[j], zt);
-          zt = fmaf(pv[j + 1], zv[j + 1], zt);
+          zt = fmaf(pv[j], (float)zv[j], zt);
+          zt = fmaf(pv[j + 1], (float)zv[j + 1], zt);
         }
       }
     }
     // every read of the value part has completed: request the next one
     wait_regs(xv);
-    if (has_next) stage_values(a, bh, nxt, vbuf, dmo);
+    if constexpr (has_next) stage_values(a, bh, nxt, vbuf, dmo);
 
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -543,7 +595,16 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, int64_t n_main, 
         }
       }
     }
+  };
+  // The next block is drawn once this block's key part is in; the draw is an
+  // LDS atomic, so its wait passes over the copies in flight.
+  for (;;) {
+    wait_vm<kStageDma>();   // key part of this block in
+    const int64_t nxt = draw_item(sh.ctr, lane) - sh.n_skip;
+    if (nxt >= sh.nb) break;
+    block(std::true_type{}, sh.b0 + (nxt + sh.rot) % sh.nb);
   }
+  block(std::false_type{}, 0);
 
   // ---- write the partial (acc[128], m, l) of each query head
   zt = group_sum(zt);
@@ -591,24 +652,29 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
   // values: [Ta, vq_end) quantized, [vq_end, Tb) fp16
   const int64_t vq_end = a.n_vq < Ta ? Ta : (a.n_vq > Tb ? Tb : a.n_vq);
   const int n_qv = (int)(vq_end - Ta), n_fv = (int)(Tb - vq_end);
-  const int nqv4 = (n_qv + 3) / 4;
+  const int nqv4 = (n_qv + 3) / 4;    // 16-byte units of fp32 scales per channel group
+  const int nqv8 = (n_qv + 7) / 8;    // 16-byte units of fp16 zeros per channel group
+  // the chunk lies in one record (Ta is a multiple of 32), at token lt of it
+  const uint8_t *rec = record_of(a, bh, Ta / kBT);
+  const int lt = (int)(Ta % kBT);
 
-  // ---- DMA, in 16-byte units.  Key buffer: codes (64 units), scale and zero
-  // (32 + 32), or n fp16 rows (16 units each) -- at most 512 units = 8 KB.
+  // ---- DMA, in 16-byte units.  Key buffer: codes (64 units), scales (32)
+  // and fp16 zeros (16), or n fp16 rows (16 units each) -- at most 512 units
+  // = 8 KB.
   char *kl = (char *)L.ks;
-  const int ku_end = kq && !kq_now ? 128 : n * 16;
+  const int ku_end = kq && !kq_now ? 112 : n * 16;
   for (int base = 0; base < ku_end; base += 64) {
     const int u = base + j;
     if (u < ku_end) {
       const void *src;
       if (kq && !kq_now) {
-        const int64_t grp = bh * (a.cap / kG) + Ta / kG;
+        const int lg = lt / kG;    // key group within the record
         if (u < 64)
-          src = a.k_codes + grp * 256 + u * 4;
+          src = rec + kRecKc + lg * 1024 + u * 16;
         else if (u < 96)
-          src = a.k_scale + grp * kD + (u - 64) * 4;
+          src = rec + kRecKs + lg * 512 + (u - 64) * 16;
         else
-          src = a.k_zero + grp * kD + (u - 96) * 4;
+          src = rec + kRecKz + lg * 256 + (u - 96) * 16;
       } else {
         const int64_t tok = Ta + u / 16;
         src = tok == a.t_new ? a.k_new + (bh * kD + (u % 16) * 8)
@@ -617,25 +683,26 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
       dma16(src, (lds_void *)(kl + (size_t)base * 16));
     }
   }
-  // value buffer: codes (2 units per token), scale and zero (4 channel
-  // groups x nqv4 units each), then fp16 rows (16 units each) -- at most 512
+  // value buffer: codes (2 units per token), scales (4 channel groups x
+  // nqv4 units), fp16 zeros (4 x nqv8 units), then fp16 rows (16 units each)
+  // -- at most 512
   char *vl = (char *)L.vs;
   const int u_vs = n_qv * 2;
   const int u_vz = u_vs + 4 * nqv4;
-  const int u_vrow = u_vz + 4 * nqv4;
+  const int u_vrow = u_vz + 4 * nqv8;
   const int vu_end = u_vrow + n_fv * 16;
   for (int base = 0; base < vu_end; base += 64) {
     const int u = base + j;
     if (u < vu_end) {
       const void *src;
       if (u < u_vs) {
-        src = a.v_codes + ((bh * a.cap + Ta + u / 2) * 8 + (u % 2) * 4);
+        src = rec + kRecVc + (lt + u / 2) * 32 + (u % 2) * 16;
       } else if (u < u_vz) {
         const int x = u - u_vs;
-        src = a.v_scale + ((bh * 4 + x / nqv4) * a.cap + Ta + (x % nqv4) * 4);
+        src = rec + kRecVs + ((x / nqv4) * kBT + lt) * 4 + (x % nqv4) * 16;
       } else if (u < u_vrow) {
         const int x = u - u_vz;
-        src = a.v_zero + ((bh * 4 + x / nqv4) * a.cap + Ta + (x % nqv4) * 4);
+        src = rec + kRecVz + ((x / nqv8) * kBT + lt) * 2 + (x % nqv8) * 16;
       } else {
         const int x = u - u_vrow;
         const int64_t tok = vq_end + x / 16;
@@ -680,14 +747,14 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
     const int gch = j >> 4;
     if ((j & 7) == 0) {
       ((uint32_t *)vl)[xr * 8 + (j >> 3)] = w;
-      const_cast<uint32_t *>(a.v_codes)[(bh * a.cap + t_pop) * 8 + (j >> 3)] = w;
+      a.L.value_codes(bh, t_pop)[j >> 3] = w;
     }
     if ((j & 15) == 0) {
+      const uint16_t zh = f2h_bits(mn);
       ((float *)(vl + (size_t)u_vs * 16))[gch * nqv4 * 4 + xr] = sc;
-      ((float *)(vl + (size_t)u_vz * 16))[gch * nqv4 * 4 + xr] = mn;
-      const int64_t sz = (bh * 4 + gch) * a.cap + t_pop;
-      const_cast<float *>(a.v_scale)[sz] = sc;
-      const_cast<float *>(a.v_zero)[sz] = mn;
+      ((uint16_t *)(vl + (size_t)u_vz * 16))[gch * nqv8 * 8 + xr] = zh;
+      *a.L.value_scale(bh, t_pop, gch) = sc;
+      *a.L.value_zero(bh, t_pop, gch) = zh;
     }
     // the slot now takes the new value (this lane read its old contents above)
     *(uint32_t *)slot_v = nv;
@@ -728,12 +795,13 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
     wave_lds_sync();   // every lane's row reads are done before the rows are overwritten
     const uint4 c4 = make_uint4(cw[0], cw[1], cw[2], cw[3]);
     *(uint4 *)((uint32_t *)kl + 4 * j) = c4;                       // codes: 2 words per channel
+    const uint32_t z2 = (uint32_t)f2h_bits(mn0) | ((uint32_t)f2h_bits(mn1) << 16);
     *(float2 *)((float *)(kl + 64 * 16) + 2 * j) = make_float2(sc0, sc1);
-    *(float2 *)((float *)(kl + 96 * 16) + 2 * j) = make_float2(mn0, mn1);
-    const int64_t grp = bh * (a.cap / kG) + Ta / kG;
-    *(uint4 *)(const_cast<uint32_t *>(a.k_codes) + grp * 256 + 4 * j) = c4;
-    *(float2 *)(const_cast<float *>(a.k_scale) + grp * kD + 2 * j) = make_float2(sc0, sc1);
-    *(float2 *)(const_cast<float *>(a.k_zero) + grp * kD + 2 * j) = make_float2(mn0, mn1);
+    *((uint32_t *)(kl + 96 * 16) + j) = z2;
+    const int64_t grp = Ta / kG;
+    *(uint4 *)a.L.key_codes(bh, grp, 2 * j) = c4;
+    *(float2 *)a.L.key_scale(bh, grp, 2 * j) = make_float2(sc0, sc1);
+    *(uint32_t *)a.L.key_zero(bh, grp, 2 * j) = z2;
   }
   wave_lds_sync();
 
@@ -747,11 +815,13 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
     if (kq) {
       const uint32_t *kc = (const uint32_t *)kl + tj / 16;
       const float *ks = (const float *)(kl + 64 * 16);
-      const float *kz = (const float *)(kl + 96 * 16);
+      const uint16_t *kz = (const uint16_t *)(kl + 96 * 16);
       const int sh = 2 * (tj % 16);
       for (int c = 64 * hf; c < 64 * hf + 64; c += 4) {
         const f4 s4 = *(const f4 *)(ks + c);
-        const f4 z4 = *(const f4 *)(kz + c);
+        const uint2 zz = *(const uint2 *)(kz + c);
+        const float z4[4] = {h2f((uint16_t)(zz.x & 0xFFFFu)), h2f((uint16_t)(zz.x >> 16)),
+                             h2f((uint16_t)(zz.y & 0xFFFFu)), h2f((uint16_t)(zz.y >> 16))};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const float code = (float)((kc[(c + u) * 2] >> sh) & 3u);
@@ -801,14 +871,15 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
   const int gch = c0 / kG;
   const uint32_t *vc = (const uint32_t *)vl;
   const float *vsc = (const float *)(vl + (size_t)u_vs * 16) + gch * nqv4 * 4;
-  const float *vz = (const float *)(vl + (size_t)u_vz * 16) + gch * nqv4 * 4;
+  const uint16_t *vz = (const uint16_t *)(vl + (size_t)u_vz * 16) + gch * nqv8 * 8;
   const uint16_t *vrow = (const uint16_t *)(vl + (size_t)u_vrow * 16);
   for (int t = 0; t < n; ++t) {
     float v0, v1;
     if (t < n_qv) {
       const uint32_t w = vc[t * 8 + c0 / 16] >> (2 * (c0 % 16));
-      v0 = (float)(w & 3u) * vsc[t] + vz[t];
-      v1 = (float)((w >> 2) & 3u) * vsc[t] + vz[t];
+      const float zt = h2f(vz[t]);
+      v0 = (float)(w & 3u) * vsc[t] + zt;
+      v1 = (float)((w >> 2) & 3u) * vsc[t] + zt;
     } else {
       const uint32_t hv = *(const uint32_t *)(vrow + (t - n_qv) * kD + c0);
       v0 = h2f((uint16_t)(hv & 0xFFFFu));
@@ -831,47 +902,70 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
   }
 }
 
-// grid: ceil(n_window / 2) * H * B + n_split * H * B workgroups of two
-// waves, in one dimension.  All window-role workgroups come first (chunk pair
-// fastest, then KV head, then batch), so every one of them starts with the
-// first workgroups and finishes under the longer block role instead of
-// trailing it; then the block-role workgroups (split fastest, then KV head,
-// then batch).  Each wave has LDS of its own and never waits for the other.
-// The masked variant holds the block's mask in registers as well; it may use
-// more than half the register file (one wave per SIMD) rather than spill, since
-// a spill reload inside the block loop would wait for every DMA in flight.
+// grid: n_groups workgroups of W waves per slab, n_groups * B * H in all
+// (W = 8: one workgroup per CU; the masked variant, whose registers allow
+// one wave per SIMD, W = 4).  Workgroup s of slab sl is lin = s (B H) +
+// (sl + s) % (B H), so consecutive workgroups belong to different slabs and
+// every slab's workgroups spread over the XCDs.  Its share: blocks
+// [s nblk / n_groups, (s + 1) nblk / n_groups) and window chunks s, s +
+// n_groups, ...; its waves draw the chunks first, then the blocks, from the
+// counter in LDS, so waves that run faster take more of them.  Partial
+// slots: s W + w for wave w's blocks, n_groups W + x for window chunk x.
+// The masked variant holds the block's mask in registers as well; it may
+// use more than half the register file rather than spill, since a spill
+// reload inside the block loop would wait for every DMA in flight.
 template <int NREP, bool MASKED>
-__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(MASKED ? 1 : 2)))
-decode_matrix_kernel(DecodeArgs a, int64_t n_main, int tps, int n_split, int n_window) {
-  __shared__ KStage sm_k[2];
-  __shared__ VStage sm_v[2];
-  __shared__ __attribute__((aligned(16))) float sm_p[2][4][kPRow];
-  __shared__ __attribute__((aligned(16))) float sm_mask[2][kBT];
-  __shared__ __attribute__((aligned(16))) float sm_bias[2][16];
-  __shared__ __attribute__((aligned(16))) float sm_alpha[2][4];
-  const int w = threadIdx.x >> 6;
+__global__ void __launch_bounds__(MASKED ? 256 : 512)
+    __attribute__((amdgpu_waves_per_eu(MASKED ? 1 : 2)))
+    decode_matrix_kernel(DecodeArgs a, int64_t n_main, int n_groups, int n_window) {
+  constexpr int W = MASKED ? 4 : 8;
+  __shared__ KStage sm_k[W];
+  __shared__ VStage sm_v[W];
+  __shared__ __attribute__((aligned(16))) float sm_p[W][4][kPRow];
+  __shared__ __attribute__((aligned(16))) float sm_mask[W][kBT];
+  __shared__ __attribute__((aligned(16))) float sm_bias[W][16];
+  __shared__ __attribute__((aligned(16))) float sm_alpha[W][4];
+  __shared__ int sm_ctr;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const Lds L{&sm_k[w], &sm_v[w], sm_p[w], sm_mask[w], sm_bias[w], sm_alpha[w]};
+  const uint32_t n_slabs = (uint32_t)a.B * (uint32_t)a.H;
   const uint32_t lin = blockIdx.x;
-  const uint32_t n_pairs = ((uint32_t)n_window + 1) / 2;
-  const uint32_t n_win_all = n_pairs * (uint32_t)(a.H * a.B);
-  if (lin < n_win_all) {
-    const uint32_t x = 2 * (lin % n_pairs) + (uint32_t)w, r = lin / n_pairs;
-    if (x < (uint32_t)n_window)
-      window_role<NREP, MASKED>(a, n_main, (int)x, 2 * n_split + (int)x, (int)(r % (uint32_t)a.H),
-                                (int)(r / (uint32_t)a.H), L);
-  } else {
-    const uint32_t l2 = lin - n_win_all;
-    const uint32_t split = l2 % (uint32_t)n_split, r = l2 / (uint32_t)n_split;
-    block_role<NREP, MASKED>(a, n_main, tps, (int)split, w, (int)(r % (uint32_t)a.H),
-                             (int)(r / (uint32_t)a.H), L, &sm_k[w], &sm_v[w]);
+  const uint32_t s = lin / n_slabs;
+  const uint32_t sl = (lin % n_slabs + n_slabs - s % n_slabs) % n_slabs;
+  const int hk = (int)(sl % (uint32_t)a.H), b = (int)(sl / (uint32_t)a.H);
+  const int64_t nblk = n_main / kBT;
+  BlockShare sh;
+  sh.b0 = (int64_t)s * nblk / n_groups;
+  sh.nb = ((int64_t)s + 1) * nblk / n_groups - sh.b0;
+  // The blocks are visited from a starting block that a hash picks,
+  // wrapping around.  Every slab's records sit a multiple of the capacity
+  // apart, so workgroups walking their shares in lock-step from the first
+  // block hit HBM channels in step for some capacities (13% slower at 257 x
+  // 128 tokens); scattered starting points break that up.  The order only
+  // changes the rounding order of the online softmax.
+  sh.rot = sh.nb > 0 ? (int64_t)(((sl * 2654435761u) ^ (s * 2246822519u)) >> 8) % sh.nb : 0;
+  sh.n_skip = (int)s < n_window ? (n_window - 1 - (int)s) / n_groups + 1 : 0;
+  sh.ctr = &sm_ctr;
+  if (threadIdx.x == 0) sm_ctr = 0;
+  __syncthreads();
+  int item = draw_item(&sm_ctr, lane);
+  while (item < sh.n_skip) {
+    const int x = (int)s + item * n_groups;
+    window_role<NREP, MASKED>(a, n_main, x, n_groups * W + x, hk, b, L);
+    wave_lds_sync();   // the LDS reads of the chunk are done
+    item = draw_item(&sm_ctr, lane);
   }
+  block_role<NREP, MASKED>(a, sh, item - sh.n_skip, (int)s * W + w, hk, b, L, &sm_k[w], &sm_v[w]);
 }
 
 bool decode_matrix_supported(const DecodeArgs &a) {
-  // the value scale/zero DMA takes a 32-bit per-lane byte offset of cap * 4
-  // q is copied 16 bytes at a time
+  // records of the 2-bit / G 32 / head_dim 128 shape, copied 16 bytes at a
+  // time like the window rows and q
   return a.kb == 2 && a.vb == 2 && a.G == kG && a.D == kD &&
-         (a.n_rep == 1 || a.n_rep == 2 || a.n_rep == 4) && a.cap < ((int64_t)1 << 29) &&
+         (a.n_rep == 1 || a.n_rep == 2 || a.n_rep == 4) && a.L.rec == kRecBytes &&
+         a.L.kc == kRecKc && a.L.ks == kRecKs && a.L.kz == kRecKz && a.L.vc == kRecVc &&
+         a.L.vs == kRecVs && a.L.vz == kRecVz && ((uintptr_t)a.L.blocks & 15) == 0 &&
+         ((uintptr_t)a.k_res & 15) == 0 && ((uintptr_t)a.v_res & 15) == 0 &&
          ((uintptr_t)a.q & 15) == 0;
 }
 
@@ -879,26 +973,23 @@ int decode_matrix_window_chunks(const DecodeArgs &a, int64_t n_main) {
   return (int)((a.t - n_main + kWT - 1) / kWT);
 }
 
+int decode_matrix_waves(const DecodeArgs &a) { return a.mask ? 4 : 8; }
+
 template <int NREP>
-static void launch_rep(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main, int tps,
-                       int n_splits, int n_window) {
+static void launch_rep(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
+                       int n_groups, int n_window) {
   if (a.mask)
-    hipLaunchKernelGGL((decode_matrix_kernel<NREP, true>), grid, dim3(128), 0, s, a, n_main, tps,
-                       n_splits, n_window);
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, true>), grid, dim3(256), 0, s, a, n_main,
+                       n_groups, n_window);
   else
-    hipLaunchKernelGGL((decode_matrix_kernel<NREP, false>), grid, dim3(128), 0, s, a, n_main, tps,
-                       n_splits, n_window);
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, false>), grid, dim3(512), 0, s, a, n_main,
+                       n_groups, n_window);
 }
 
-hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int tokens_per_split,
-                                int n_splits, hipStream_t s) {
-  if (!decode_matrix_supported(a) || a.t <= 0 || n_main < 0 ||
-      n_main % kBT != 0 || n_main > a.n_vq || tokens_per_split <= 0 ||
-      tokens_per_split % kBT != 0 || n_splits < 0)
-    return hipErrorInvalidValue;
-  // every block is in some split, and every split holds at least one block
-  if ((int64_t)n_splits * tokens_per_split < n_main ||
-      (n_splits > 0 && (int64_t)(n_splits - 1) * tokens_per_split >= n_main))
+hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int n_groups,
+                                hipStream_t s) {
+  if (!decode_matrix_supported(a) || a.t <= 0 || n_main < 0 || n_main % kBT != 0 ||
+      n_main > a.n_vq || n_groups <= 0)
     return hipErrorInvalidValue;
   // the window role's key staging assumes whole key groups below n_kq
   if (a.n_kq % kG != 0) return hipErrorInvalidValue;
@@ -912,14 +1003,15 @@ hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int tokens_
     if (a.t % a.R == 0 && n_main > a.t - a.R) return hipErrorInvalidValue;
   }
   const int n_window = decode_matrix_window_chunks(a, n_main);
-  if (n_splits + n_window <= 0 || 2 * n_splits + n_window > a.S_total) return hipErrorInvalidValue;
-  const int64_t n_wg = (((int64_t)n_window + 1) / 2 + n_splits) * a.H * a.B;
-  if (n_wg > ((int64_t)1 << 25)) return hipErrorInvalidValue;   // 128-thread groups, 32-bit ids
+  const int W = decode_matrix_waves(a);
+  if ((int64_t)n_groups * W + n_window > a.S_total) return hipErrorInvalidValue;
+  const int64_t n_wg = (int64_t)n_groups * a.H * a.B;
+  if (n_wg > ((int64_t)1 << 25)) return hipErrorInvalidValue;   // 32-bit workgroup ids
   dim3 grid((unsigned)n_wg);
   switch (a.n_rep) {
-    case 1: launch_rep<1>(a, grid, s, n_main, tokens_per_split, n_splits, n_window); break;
-    case 2: launch_rep<2>(a, grid, s, n_main, tokens_per_split, n_splits, n_window); break;
-    default: launch_rep<4>(a, grid, s, n_main, tokens_per_split, n_splits, n_window); break;
+    case 1: launch_rep<1>(a, grid, s, n_main, n_groups, n_window); break;
+    case 2: launch_rep<2>(a, grid, s, n_main, n_groups, n_window); break;
+    default: launch_rep<4>(a, grid, s, n_main, n_groups, n_window); break;
   }
   return hipGetLastError();
 }

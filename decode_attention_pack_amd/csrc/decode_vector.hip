@@ -175,24 +175,24 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
     for (int c = 0; c < 32; ++c) acc[j][c] = 0.0f;
   }
 
-  // Slab base pointers (wave-uniform, so they stay in scalar registers) and
-  // 32-bit per-lane byte offsets: each load is a scalar base plus one
-  // 32-bit vector offset, with no 64-bit address arithmetic per lane.
-  const int64_t kgroups = a.cap / kVG;
-  const char *kcodes = (const char *)(a.k_codes + bh * kgroups * (kVD * KB));
-  const char *kscale = (const char *)(a.k_scale + bh * kgroups * kVD);
-  const char *kzero = (const char *)(a.k_zero + bh * kgroups * kVD);
+  // Slab base pointer (wave-uniform, so it stays in scalar registers) and
+  // 32-bit byte offsets: each load is a scalar base plus one 32-bit vector
+  // offset, with no 64-bit address arithmetic per lane.  A 32-token group g
+  // lies in record g / 4 of the slab, as its group g % 4; a slab's records
+  // span less than 4 GB (decode_vector_supported).
+  const Layout &L = a.L;
+  const char *slab = (const char *)L.blocks + bh * L.nrec * L.rec;
+  const uint32_t rec = (uint32_t)L.rec;
   const char *kres = (const char *)(a.k_res + bh * a.R * kVD);
-  const char *vcodes = (const char *)(a.v_codes + bh * a.cap * (kVD * VB / 32));
-  const char *vscale = (const char *)(a.v_scale + bh * (kVD / kVG) * a.cap);
-  const char *vzero = (const char *)(a.v_zero + bh * (kVD / kVG) * a.cap);
   const char *vres = (const char *)(a.v_res + bh * a.R * kVD);
   const char *mrow = a.mask ? (const char *)(a.mask + (int64_t)b * a.t) : nullptr;
-  const uint32_t kc_lane = (uint32_t)lane * (2 * KB) * 4u;
-  const uint32_t ks_lane = (uint32_t)lane * 8u;
+  const uint32_t kc_lane = (uint32_t)L.kc + (uint32_t)lane * (2 * KB) * 4u;
+  const uint32_t ks_lane = (uint32_t)L.ks + (uint32_t)lane * 8u;
+  const uint32_t kz_lane = (uint32_t)L.kz + (uint32_t)lane * 4u;
   const uint32_t kr_lane = (uint32_t)lane * 4u;
-  const uint32_t vc_lane = (uint32_t)qd * VWQ * 4u;
-  const uint32_t vs_lane = (uint32_t)qd * (uint32_t)a.cap * 4u;
+  const uint32_t vc_lane = (uint32_t)L.vc + (uint32_t)qd * VWQ * 4u;
+  const uint32_t vs_lane = (uint32_t)L.vs + (uint32_t)qd * (kRecTokens * 4u);
+  const uint32_t vz_lane = (uint32_t)L.vz + (uint32_t)qd * (kRecTokens * 2u);
   const uint32_t vr_lane = (uint32_t)qd * 64u;
 
   // The code, scale and zero words of a group (and the mask entries of the
@@ -207,14 +207,16 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
     float vs[2], vz[2], mk[2];
   };
   auto fetch = [&](int g, Raw &r) {
-    load_words<KB / 2>((const uint32_t *)(kcodes + ((uint32_t)g * (kVD * KB * 4u) + kc_lane)),
-                       r.kw);
-    r.ks = *(const float2 *)(kscale + ((uint32_t)g * (kVD * 4u) + ks_lane));
-    r.kz = *(const float2 *)(kzero + ((uint32_t)g * (kVD * 4u) + ks_lane));
+    const uint32_t r0 = (uint32_t)(g >> 2) * rec;        // record of the group
+    const uint32_t lg = (uint32_t)(g & 3);               // group within the record
+    load_words<KB / 2>((const uint32_t *)(slab + (r0 + lg * (kVD * KB * 4u) + kc_lane)), r.kw);
+    r.ks = *(const float2 *)(slab + (r0 + lg * (kVD * 4u) + ks_lane));
+    const uint32_t zz = *(const uint32_t *)(slab + (r0 + lg * (kVD * 2u) + kz_lane));
+    r.kz = make_float2(h2f((uint16_t)(zz & 0xFFFFu)), h2f((uint16_t)(zz >> 16)));
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const uint32_t tau = (uint32_t)(g * kVG + 16 * hh + tq);
-      const uint32_t *src = (const uint32_t *)(vcodes + (tau * (kVD * VB / 8u) + vc_lane));
+      const uint32_t tl = lg * kVG + 16 * hh + tq;       // token within the record
+      const uint32_t *src = (const uint32_t *)(slab + (r0 + tl * (kVD * VB / 8u) + vc_lane));
       if constexpr (VWQ == 4) {
         const uint4 v = *(const uint4 *)src;
         r.vw[hh][0] = v.x;
@@ -226,8 +228,9 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
         r.vw[hh][0] = v.x;
         r.vw[hh][1] = v.y;
       }
-      r.vs[hh] = *(const float *)(vscale + (vs_lane + tau * 4u));
-      r.vz[hh] = *(const float *)(vzero + (vs_lane + tau * 4u));
+      r.vs[hh] = *(const float *)(slab + (r0 + vs_lane + tl * 4u));
+      r.vz[hh] = h2f(*(const uint16_t *)(slab + (r0 + vz_lane + tl * 2u)));
+      const uint32_t tau = (uint32_t)(g * kVG + 16 * hh + tq);
       r.mk[hh] = mrow ? *(const float *)(mrow + (uint32_t)min((int)tau, t_all - 1) * 4u) : 0.0f;
     }
   };
@@ -437,15 +440,14 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
 }
 
 bool decode_vector_supported(const DecodeArgs &a) {
-  // 16-byte code loads: the slab offsets are multiples of 16 bytes when the
-  // arrays are; q is read 4 bytes at a time
-  const bool aligned = ((uintptr_t)a.k_codes & 15) == 0 && ((uintptr_t)a.v_codes & 15) == 0 &&
-                       ((uintptr_t)a.v_res & 15) == 0 && ((uintptr_t)a.k_res & 3) == 0 &&
-                       ((uintptr_t)a.k_scale & 7) == 0 &&
-                       ((uintptr_t)a.k_zero & 7) == 0 && ((uintptr_t)a.q & 3) == 0;
+  // 16-byte code loads (records and their sections are multiples of 16
+  // bytes); q is read 4 bytes at a time; 32-bit offsets within a slab's
+  // records and 32-bit token indices
+  const bool aligned = ((uintptr_t)a.L.blocks & 15) == 0 && ((uintptr_t)a.v_res & 15) == 0 &&
+                       ((uintptr_t)a.k_res & 3) == 0 && ((uintptr_t)a.q & 3) == 0;
   return a.D == kVD && a.G == kVG && (a.kb == 2 || a.kb == 4) && (a.vb == 2 || a.vb == 4) &&
          (a.n_rep == 1 || a.n_rep == 2) && a.R % kVG == 0 && a.cap % kVG == 0 &&
-         a.cap < ((int64_t)1 << 26) && aligned;
+         a.cap < ((int64_t)1 << 26) && a.L.nrec * a.L.rec < ((int64_t)1 << 32) && aligned;
 }
 
 template <int KB, int VB>

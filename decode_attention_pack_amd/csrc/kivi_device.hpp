@@ -15,6 +15,82 @@ __device__ __forceinline__ float h2f(uint16_t h) {
   return __half2float(__ushort_as_half(h));
 }
 
+// Bit pattern of an fp32 value that is exactly an fp16 value (a zero point:
+// the minimum of fp16 inputs), converted without rounding.
+__device__ __forceinline__ uint16_t f2h_bits(float f) {
+  return __half_as_ushort(__float2half_rn(f));
+}
+
+// Tokens per record of the packed store.
+constexpr int kRecTokens = 128;
+
+// The packed store of a cache (include/kivi.h): each (batch row, KV head)
+// slab is a run of records, one per 128 tokens, each holding the key codes,
+// key scales, key zeros (fp16), value codes, value scales and value zeros
+// (fp16) of its tokens, in that order.  Section offsets are multiples of 16
+// bytes.  Key groups (KIVI item 2, G tokens of one channel) and value groups
+// (KIVI item 3, G channels of one token) both lie inside one record, since G
+// divides 128.
+struct Layout {
+  uint8_t *blocks;
+  int64_t rec;        // bytes per record
+  int64_t nrec;       // records per slab (capacity / 128)
+  int32_t kc, ks, kz, vc, vs, vz;   // section offsets in bytes
+  int32_t D, G, kb, vb;
+
+  __host__ __device__ __forceinline__ uint8_t *record(int64_t bh, int64_t tau) const {
+    return blocks + (bh * nrec + tau / kRecTokens) * rec;
+  }
+  // key group g (tokens g G .. g G + G - 1) of channel c
+  __host__ __device__ __forceinline__ int64_t key_index(int64_t g, int c) const {
+    return ((g * G) % kRecTokens / G) * D + c;
+  }
+  __device__ __forceinline__ uint32_t *key_codes(int64_t bh, int64_t g, int c) const {
+    return (uint32_t *)(record(bh, g * G) + kc) + key_index(g, c) * (G * kb / 32);
+  }
+  __device__ __forceinline__ float *key_scale(int64_t bh, int64_t g, int c) const {
+    return (float *)(record(bh, g * G) + ks) + key_index(g, c);
+  }
+  __device__ __forceinline__ uint16_t *key_zero(int64_t bh, int64_t g, int c) const {
+    return (uint16_t *)(record(bh, g * G) + kz) + key_index(g, c);
+  }
+  // token tau: its code row, and the scale / zero of its channel group gc
+  __device__ __forceinline__ uint32_t *value_codes(int64_t bh, int64_t tau) const {
+    return (uint32_t *)(record(bh, tau) + vc) + (tau % kRecTokens) * (D * vb / 32);
+  }
+  __device__ __forceinline__ float *value_scale(int64_t bh, int64_t tau, int gc) const {
+    return (float *)(record(bh, tau) + vs) + gc * kRecTokens + tau % kRecTokens;
+  }
+  __device__ __forceinline__ uint16_t *value_zero(int64_t bh, int64_t tau, int gc) const {
+    return (uint16_t *)(record(bh, tau) + vz) + gc * kRecTokens + tau % kRecTokens;
+  }
+};
+
+// Section offsets and record size for a shape; rec = 0 if the layout does
+// not take it (bits other than 2 and 4, G not dividing 128 or D).
+inline Layout make_layout(uint8_t *blocks, int D, int kb, int vb, int G, int64_t cap) {
+  Layout L{};
+  L.blocks = blocks;
+  L.D = D;
+  L.G = G;
+  L.kb = kb;
+  L.vb = vb;
+  const bool ok = (kb == 2 || kb == 4) && (vb == 2 || vb == 4) && G > 0 && D > 0 &&
+                  kRecTokens % G == 0 && D % G == 0 && G % (32 / kb) == 0 &&
+                  G % (32 / vb) == 0;
+  if (!ok) return L;
+  const int groups = kRecTokens / G;
+  L.kc = 0;
+  L.ks = L.kc + kRecTokens * D * kb / 8;
+  L.kz = L.ks + groups * D * 4;
+  L.vc = L.kz + groups * D * 2;
+  L.vs = L.vc + kRecTokens * D * vb / 8;
+  L.vz = L.vs + (D / G) * kRecTokens * 4;
+  L.rec = L.vz + (D / G) * kRecTokens * 2;
+  L.nrec = cap / kRecTokens;
+  return L;
+}
+
 // Where token tau of one (batch, head) slab comes from when it is quantized:
 // tokens below `t0` are read from the fp16 window `res` (slot tau % R); tokens
 // from `t0` on are read from the caller's input `inp`, whose row 0 is token

@@ -13,11 +13,10 @@ namespace kivi {
 // Two passes over the group's tokens (min/max, then codes) keep the kernel
 // free of per-thread arrays; the second pass hits the caches.
 __global__ void __launch_bounds__(128)
-key_groups_kernel(TokenSource src, int64_t g_first, int bits, int G, int D, int64_t cap,
-                  uint32_t *__restrict__ codes, float *__restrict__ scale,
-                  float *__restrict__ zero) {
+key_groups_kernel(TokenSource src, int64_t g_first, Layout L) {
   const int64_t bh = blockIdx.y;
   const int64_t g = g_first + blockIdx.x;
+  const int G = L.G, D = L.D, bits = L.kb;
   const int64_t tau0 = g * G;
   const int per = 32 / bits;
   const int words = G / per;
@@ -30,8 +29,7 @@ key_groups_kernel(TokenSource src, int64_t g_first, int bits, int G, int D, int6
       mx = x > mx ? x : mx;
     }
     const float s = group_scale(mn, mx, bits);
-    const int64_t sz = (bh * (cap / G) + g) * D + c;
-    uint32_t *dst = codes + sz * words;
+    uint32_t *dst = L.key_codes(bh, g, c);
     for (int w = 0; w < words; ++w) {
       uint32_t word = 0;
       for (int e = 0; e < per; ++e) {
@@ -40,25 +38,24 @@ key_groups_kernel(TokenSource src, int64_t g_first, int bits, int G, int D, int6
       }
       dst[w] = word;
     }
-    scale[sz] = s;
-    zero[sz] = mn;
+    *L.key_scale(bh, g, c) = s;
+    *L.key_zero(bh, g, c) = f2h_bits(mn);
   }
 }
 
 // KIVI item 3: one thread per (token, value group).  A value group is G
 // consecutive channels of one token; its codes are packed along channels.
 __global__ void __launch_bounds__(256)
-value_rows_kernel(TokenSource src, int64_t tau_first, int64_t n_rows, int bits, int G, int D,
-                  int64_t cap, uint32_t *__restrict__ codes, float *__restrict__ scale,
-                  float *__restrict__ zero) {
+value_rows_kernel(TokenSource src, int64_t tau_first, int64_t n_rows, Layout L) {
   const int64_t bh = blockIdx.y;
   const int64_t r = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
   if (r >= n_rows) return;
+  const int G = L.G, D = L.D, bits = L.vb;
   const int64_t tau = tau_first + r;
   const int per = 32 / bits;
   const int n_groups = D / G;
   const uint16_t *row = src.row(bh, tau);
-  uint32_t *dst = codes + (bh * cap + tau) * (int64_t)(D / per);
+  uint32_t *dst = L.value_codes(bh, tau);
   for (int g = threadIdx.x >> 6; g < n_groups; g += 4) {
     float mn = h2f(row[g * G]);
     float mx = mn;
@@ -74,8 +71,8 @@ value_rows_kernel(TokenSource src, int64_t tau_first, int64_t n_rows, int bits, 
         word |= quant_code(h2f(row[g * G + w * per + e]), mn, s, bits) << (bits * e);
       dst[(g * G) / per + w] = word;
     }
-    scale[(bh * n_groups + g) * cap + tau] = s;
-    zero[(bh * n_groups + g) * cap + tau] = mn;
+    *L.value_scale(bh, tau, g) = s;
+    *L.value_zero(bh, tau, g) = f2h_bits(mn);
   }
 }
 
@@ -102,14 +99,12 @@ write_window_kernel(const uint16_t *__restrict__ k_new, const uint16_t *__restri
 // pack entry point): one wave per (key group, slab).  Lane l reads channels
 // [l D/64, (l + 1) D/64) of the group's G token rows straight from memory --
 // each load instruction of the wave covers one whole row -- then reduces and
-// packs them.  The code words of adjacent channels are adjacent, so the wave
-// stores one contiguous run (16 bytes per lane where the alignment allows).
+// packs them.  The code words of adjacent channels are adjacent in the
+// record, so the wave stores one contiguous run of 16-byte stores.
 // grid: (n_groups, BH); block: 64 threads.
 template <int G, int D, int BITS>
 __global__ void __launch_bounds__(64)
-key_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t g_first, int64_t cap,
-                 uint32_t *__restrict__ codes, float *__restrict__ scale,
-                 float *__restrict__ zero) {
+key_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t g_first, Layout L) {
   constexpr int CPT = D / 64;                       // channels per thread
   static_assert(CPT == 1 || CPT == 2 || CPT == 4, "head_dim 64, 128 or 256");
   const int64_t bh = blockIdx.y;
@@ -146,9 +141,10 @@ key_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t g_first, 
   }
   constexpr int per = 32 / BITS;
   constexpr int words = G / per;
-  const int64_t sz = (bh * (cap / G) + g_first + g) * D + c0;
+  const int64_t gd = g_first + g;                   // destination group
   uint32_t out[CPT * words];
-  float sv[CPT], zv[CPT];
+  float sv[CPT];
+  uint16_t zv[CPT];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
     float mn, mx;
@@ -164,40 +160,38 @@ key_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t g_first, 
       out[k * words + w] = word;
     }
     sv[k] = s;
-    zv[k] = mn;
+    zv[k] = f2h_bits(mn);
   }
-  uint32_t *dst = codes + sz * words;
+  uint32_t *dst = L.key_codes(bh, gd, c0);
   if constexpr ((CPT * words) % 4 == 0) {
-    if (((uintptr_t)codes & 15) == 0) {
+    // the lane's run starts at a multiple of 16 bytes of a record
 #pragma unroll
-      for (int w = 0; w < CPT * words; w += 4)
-        *(uint4 *)(dst + w) = make_uint4(out[w], out[w + 1], out[w + 2], out[w + 3]);
-    } else {
-#pragma unroll
-      for (int w = 0; w < CPT * words; ++w) dst[w] = out[w];
-    }
+    for (int w = 0; w < CPT * words; w += 4)
+      *(uint4 *)(dst + w) = make_uint4(out[w], out[w + 1], out[w + 2], out[w + 3]);
   } else {
 #pragma unroll
     for (int w = 0; w < CPT * words; ++w) dst[w] = out[w];
   }
+  float *ds = L.key_scale(bh, gd, c0);
+  uint16_t *dz = L.key_zero(bh, gd, c0);
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
-    scale[sz + k] = sv[k];
-    zero[sz + k] = zv[k];
+    ds[k] = sv[k];
+    dz[k] = zv[k];
   }
 }
 
 // KIVI item 3, fast path for a contiguous fp16 input: one workgroup per 64
-// tokens of one slab.  Thread (group g, token t) reads its G channels
+// tokens of one slab, which lie in one record (the first destination token
+// is a multiple of 64).  Thread (group g, token t) reads its G channels
 // straight from memory with 16-byte loads, then reduces and packs them, so
-// for each group the 64 scales / zeros of the tile are one contiguous store;
+// for each group the 64 scales / zeros of the tile are one contiguous run;
 // the code rows of the tile are staged in LDS and stored as one contiguous
-// run.  grid: (ceil(n_rows / 64), BH); block: 256.
+// run of 16-byte stores.  grid: (ceil(n_rows / 64), BH); block: 256.
 template <int D, int G, int BITS>
 __global__ void __launch_bounds__(256)
 value_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t n_rows,
-                   int64_t tau_first, int64_t cap, uint32_t *__restrict__ codes,
-                   float *__restrict__ scale, float *__restrict__ zero) {
+                   int64_t tau_first, Layout L) {
   const int64_t bh = blockIdx.y;
   const int64_t r0 = (int64_t)blockIdx.x * 64;
   const int rows = (int)(n_rows - r0 < 64 ? n_rows - r0 : 64);
@@ -205,8 +199,6 @@ value_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t n_rows,
   constexpr int per = 32 / BITS;
   constexpr int n_groups = D / G;
   constexpr int kWords = D / per;                   // code words per token row
-  // code rows of the tile, staged here and stored as one contiguous run
-  // (16-byte stores; the launcher checks the alignment)
   __shared__ __attribute__((aligned(16))) uint32_t out_s[64 * kWords];
   for (int g = threadIdx.x >> 6; g < n_groups; g += 4) {
     if (t >= rows) continue;
@@ -233,13 +225,12 @@ value_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t n_rows,
         word |= quant_code_r(v[w * per + e], mn, s, r, BITS) << (BITS * e);
       dst[w] = word;
     }
-    const int64_t sz = (bh * n_groups + g) * cap + tau;
-    scale[sz] = s;
-    zero[sz] = mn;
+    *L.value_scale(bh, tau, g) = s;
+    *L.value_zero(bh, tau, g) = f2h_bits(mn);
   }
   __syncthreads();
-  // the tile's rows are consecutive tokens of one slab: one contiguous run
-  uint32_t *run = codes + (bh * cap + tau_first + r0) * (int64_t)kWords;
+  // the tile's rows are consecutive tokens of one record: one contiguous run
+  uint32_t *run = L.value_codes(bh, tau_first + r0);
   for (int i = threadIdx.x; i < rows * kWords / 4; i += 256)
     *(uint4 *)(run + 4 * i) = *(const uint4 *)(out_s + 4 * i);
 }
@@ -253,8 +244,8 @@ bool pack_tiles_supported(int D, int G, int bits) {
 }
 
 hipError_t launch_key_tiles(const uint16_t *x, int64_t T_in, int64_t n_rows, int64_t g_first,
-                            int64_t BH, int bits, int G, int D, int64_t cap, uint32_t *codes,
-                            float *scale, float *zero, hipStream_t s) {
+                            int64_t BH, const Layout &L, hipStream_t s) {
+  const int G = L.G, D = L.D, bits = L.kb;
   const int64_t n_groups = n_rows / G;
   if (n_groups <= 0 || BH <= 0) return hipSuccess;
   if (!pack_tiles_supported(D, G, bits) || n_rows % G != 0 || n_rows > T_in)
@@ -264,10 +255,10 @@ hipError_t launch_key_tiles(const uint16_t *x, int64_t T_in, int64_t n_rows, int
   if (G == GG && D == DD) {                                                                     \
     if (bits == 2)                                                                              \
       hipLaunchKernelGGL((key_tiles_kernel<GG, DD, 2>), grid, dim3(64), 0, s, x, T_in,        \
-                         g_first, cap, codes, scale, zero);                                     \
+                         g_first, L);                                                           \
     else                                                                                        \
       hipLaunchKernelGGL((key_tiles_kernel<GG, DD, 4>), grid, dim3(64), 0, s, x, T_in,        \
-                         g_first, cap, codes, scale, zero);                                     \
+                         g_first, L);                                                           \
     return hipGetLastError();                                                                   \
   }
   KIVI_KT(16, 64) KIVI_KT(32, 64) KIVI_KT(64, 64)
@@ -278,25 +269,25 @@ hipError_t launch_key_tiles(const uint16_t *x, int64_t T_in, int64_t n_rows, int
 }
 
 hipError_t launch_value_tokens(const uint16_t *x, int64_t T_in, int64_t n_rows, int64_t tau_first,
-                               int64_t BH, int bits, int G, int D, int64_t cap, uint32_t *codes,
-                               float *scale, float *zero, hipStream_t s) {
+                               int64_t BH, const Layout &L, hipStream_t s) {
+  const int G = L.G, D = L.D, bits = L.vb;
   if (n_rows <= 0 || BH <= 0) return hipSuccess;
   if (!pack_tiles_supported(D, G, bits) || n_rows > T_in) return hipErrorInvalidValue;
-  if (((uintptr_t)codes & 15) != 0) {
-    // the tile kernel stores 16-byte runs of code rows; any other
+  if (tau_first % 64 != 0) {
+    // the tile kernel needs its 64 tokens in one record; any other
     // destination takes the per-row kernel
     TokenSource src{nullptr, x, tau_first, T_in, 1, D};
-    return launch_value_rows(src, tau_first, n_rows, BH, bits, G, D, cap, codes, scale, zero, s);
+    return launch_value_rows(src, tau_first, n_rows, BH, L, s);
   }
   dim3 grid((unsigned)((n_rows + 63) / 64), (unsigned)BH);
 #define KIVI_VT(DD, GG)                                                                         \
   if (D == DD && G == GG) {                                                                     \
     if (bits == 2)                                                                              \
       hipLaunchKernelGGL((value_tiles_kernel<DD, GG, 2>), grid, dim3(256), 0, s, x, T_in,      \
-                         n_rows, tau_first, cap, codes, scale, zero);                           \
+                         n_rows, tau_first, L);                                                 \
     else                                                                                        \
       hipLaunchKernelGGL((value_tiles_kernel<DD, GG, 4>), grid, dim3(256), 0, s, x, T_in,      \
-                         n_rows, tau_first, cap, codes, scale, zero);                           \
+                         n_rows, tau_first, L);                                                 \
     return hipGetLastError();                                                                   \
   }
   KIVI_VT(64, 16) KIVI_VT(64, 32) KIVI_VT(64, 64)
@@ -316,11 +307,10 @@ hipError_t launch_value_tokens(const uint16_t *x, int64_t T_in, int64_t n_rows, 
 __global__ void __launch_bounds__(256)
 append_one_kernel(const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
                   uint16_t *__restrict__ k_res, uint16_t *__restrict__ v_res, int64_t t0,
-                  int R, int D, int G, int bits, int64_t cap, bool key_to_window,
-                  uint32_t *__restrict__ codes, float *__restrict__ scale,
-                  float *__restrict__ zero) {
+                  int R, bool key_to_window, Layout L) {
   const int64_t bh = blockIdx.x;
   const int c = threadIdx.x;
+  const int D = L.D, G = L.G, bits = L.vb;
   const bool on = c < D;
   const int64_t slot = (bh * R + t0 % R) * D + c;
   if (t0 >= R) {
@@ -334,11 +324,10 @@ append_one_kernel(const uint16_t *__restrict__ k_new, const uint16_t *__restrict
     uint32_t w = quant_code(x, mn, sc, bits) << (bits * (c % per));
     for (int o = 1; o < per; o <<= 1) w |= __shfl_xor(w, o);
     const int64_t tau = t0 - R;
-    if (on && c % per == 0) codes[(bh * cap + tau) * (int64_t)(D / per) + c / per] = w;
+    if (on && c % per == 0) L.value_codes(bh, tau)[c / per] = w;
     if (on && c % G == 0) {
-      const int64_t sz = (bh * (D / G) + c / G) * cap + tau;
-      scale[sz] = sc;
-      zero[sz] = mn;
+      *L.value_scale(bh, tau, c / G) = sc;
+      *L.value_zero(bh, tau, c / G) = f2h_bits(mn);
     }
   }
   if (on) {
@@ -348,33 +337,28 @@ append_one_kernel(const uint16_t *__restrict__ k_new, const uint16_t *__restrict
 }
 
 hipError_t launch_append_one(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_res,
-                             uint16_t *v_res, int64_t t0, int64_t BH, int R, int D, int G,
-                             int bits, int64_t cap, bool key_to_window, uint32_t *codes,
-                             float *scale, float *zero, hipStream_t s) {
-  if (!append_one_supported(D, G, bits) || BH <= 0) return hipErrorInvalidValue;
-  const int threads = (D + 63) / 64 * 64;
+                             uint16_t *v_res, int64_t t0, int64_t BH, int R, bool key_to_window,
+                             const Layout &L, hipStream_t s) {
+  if (!append_one_supported(L.D, L.G, L.vb) || BH <= 0) return hipErrorInvalidValue;
+  const int threads = (L.D + 63) / 64 * 64;
   hipLaunchKernelGGL(append_one_kernel, dim3((unsigned)BH), dim3(threads), 0, s, k_new, v_new,
-                     k_res, v_res, t0, R, D, G, bits, cap, key_to_window, codes, scale, zero);
+                     k_res, v_res, t0, R, key_to_window, L);
   return hipGetLastError();
 }
 
 hipError_t launch_key_groups(const TokenSource &src, int64_t g_first, int64_t n_groups,
-                             int64_t BH, int bits, int G, int D, int64_t cap,
-                             uint32_t *codes, float *scale, float *zero, hipStream_t s) {
+                             int64_t BH, const Layout &L, hipStream_t s) {
   if (n_groups <= 0 || BH <= 0) return hipSuccess;
   dim3 grid((unsigned)n_groups, (unsigned)BH);
-  hipLaunchKernelGGL(key_groups_kernel, grid, dim3(128), 0, s, src, g_first, bits, G, D, cap,
-                     codes, scale, zero);
+  hipLaunchKernelGGL(key_groups_kernel, grid, dim3(128), 0, s, src, g_first, L);
   return hipGetLastError();
 }
 
 hipError_t launch_value_rows(const TokenSource &src, int64_t tau_first, int64_t n_rows,
-                             int64_t BH, int bits, int G, int D, int64_t cap,
-                             uint32_t *codes, float *scale, float *zero, hipStream_t s) {
+                             int64_t BH, const Layout &L, hipStream_t s) {
   if (n_rows <= 0 || BH <= 0) return hipSuccess;
   dim3 grid((unsigned)((n_rows + 63) / 64), (unsigned)BH);
-  hipLaunchKernelGGL(value_rows_kernel, grid, dim3(256), 0, s, src, tau_first, n_rows, bits, G,
-                     D, cap, codes, scale, zero);
+  hipLaunchKernelGGL(value_rows_kernel, grid, dim3(256), 0, s, src, tau_first, n_rows, L);
   return hipGetLastError();
 }
 

@@ -22,10 +22,11 @@ KIVI_ERR_WORKSPACE = -3
 KIVI_ERR_HIP = -4
 KIVI_PATH_AUTO, KIVI_PATH_GENERIC, KIVI_PATH_MATRIX, KIVI_PATH_VECTOR = 0, 1, 2, 3
 
-EXPORTED = ("kivi_pack_keys", "kivi_pack_values", "kivi_append", "kivi_decode_attn",
-            "kivi_decode_attn_ex", "kivi_decode_attn_workspace_bytes",
+EXPORTED = ("kivi_record_bytes", "kivi_pack_keys", "kivi_pack_values", "kivi_append",
+            "kivi_decode_attn", "kivi_decode_attn_ex", "kivi_decode_attn_workspace_bytes",
             "kivi_decode_attn_workspace_bytes_ex", "kivi_decode_step", "kivi_status_string",
             "kivi_last_error")
+TOKENS_PER_RECORD = 128
 
 
 class KiviError(RuntimeError):
@@ -40,9 +41,7 @@ class CCache(ctypes.Structure):
         ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32), ("group", ctypes.c_int32),
         ("residual", ctypes.c_int32),
         ("capacity", ctypes.c_int64), ("n_tokens", ctypes.c_int64),
-        ("k_codes", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("k_zero", ctypes.c_void_p),
-        ("v_codes", ctypes.c_void_p), ("v_scale", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
-        ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
+        ("blocks", ctypes.c_void_p), ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
     ]
 
 
@@ -59,9 +58,11 @@ def lib():
                            "`python -m decode_attention_pack_amd.build`")
     L = ctypes.CDLL(LIB_PATH)
     P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.kivi_record_bytes.argtypes = [i32, i32, i32, i32]
+    L.kivi_record_bytes.restype = sz
     for name in ("kivi_pack_keys", "kivi_pack_values"):
         fn = getattr(L, name)
-        fn.argtypes = [P, i32, i32, i64, i32, i32, i32, P, P, P, i64, i64, P]
+        fn.argtypes = [ctypes.POINTER(CCache), P, i64, i64, P]
         fn.restype = ctypes.c_int
     L.kivi_append.argtypes = [ctypes.POINTER(CCache), P, P, i64, P]
     L.kivi_append.restype = ctypes.c_int
@@ -108,36 +109,40 @@ def _dev(t: torch.Tensor, dtype, shape, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def record_bytes(D, kb, vb, G) -> int:
+    """Bytes of one 128-token record of the packed store (include/kivi.h)."""
+    n = int(lib().kivi_record_bytes(D, kb, vb, G))
+    if n == 0:
+        raise KiviError(KIVI_ERR_INVALID_ARG, f"no record layout for D={D} bits={kb}/{vb} G={G}")
+    return n
+
+
 def layout_shapes(B, H, D, kb, vb, G, R, cap):
     """Shapes of the cache arrays (include/kivi.h storage layout)."""
     return {
-        "k_codes": (B, H, cap // G, D, G * kb // 32),
-        "k_scale": (B, H, cap // G, D),
-        "k_zero": (B, H, cap // G, D),
-        "v_codes": (B, H, cap, D * vb // 32),
-        "v_scale": (B, H, D // G, cap),
-        "v_zero": (B, H, D // G, cap),
+        "blocks": (B, H, cap // TOKENS_PER_RECORD, record_bytes(D, kb, vb, G)),
         "k_res": (B, H, R, D),
         "v_res": (B, H, R, D),
     }
 
 
-_DT = {"k_codes": torch.int32, "k_scale": torch.float32, "k_zero": torch.float32,
-       "v_codes": torch.int32, "v_scale": torch.float32, "v_zero": torch.float32,
-       "k_res": torch.float16, "v_res": torch.float16}
-_ORDER = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero", "k_res", "v_res")
+_DT = {"blocks": torch.uint8, "k_res": torch.float16, "v_res": torch.float16}
+_ORDER = ("blocks", "k_res", "v_res")
 
 
 class Cache:
     """A KIVI cache in device memory (torch tensors) plus its C descriptor.
 
-    Codes are stored in int32 tensors holding the u32 words bit for bit.
-    """
+    ``blocks`` is the record array as raw bytes; ``k_res`` / ``v_res`` are the
+    fp16 windows."""
 
     def __init__(self, batch, n_kv_heads, head_dim, k_bits, v_bits, group, residual, capacity,
                  device="cuda", arrays=None):
         self.B, self.H, self.D = batch, n_kv_heads, head_dim
         self.kb, self.vb, self.G, self.R, self.cap = k_bits, v_bits, group, residual, capacity
+        if capacity % TOKENS_PER_RECORD:
+            raise KiviError(KIVI_ERR_INVALID_ARG,
+                            f"capacity {capacity} must be a multiple of {TOKENS_PER_RECORD}")
         shapes = layout_shapes(batch, n_kv_heads, head_dim, k_bits, v_bits, group, residual,
                                capacity)
         if arrays is None:
@@ -167,31 +172,22 @@ class Cache:
 
     def new_workspace(self, n_q_heads, tokens_per_split=0, path=KIVI_PATH_AUTO):
         n = self.workspace_bytes(n_q_heads, tokens_per_split, path)
-        return torch.empty(n, dtype=torch.uint8, device=self.k_codes.device)
+        return torch.empty(n, dtype=torch.uint8, device=self.blocks.device)
 
 
-def kivi_pack_keys(k, bits, group, codes, scale, zero, dst_capacity, dst_token_offset=0,
-                   stream=None):
-    B, H, T, D = k.shape
-    shp = layout_shapes(B, H, D, bits, bits, group, 1, dst_capacity)
-    args = [_dev(k, torch.float16, None, "k"), B, H, T, D, bits, group,
-            _dev(codes, torch.int32, shp["k_codes"], "codes"),
-            _dev(scale, torch.float32, shp["k_scale"], "scale"),
-            _dev(zero, torch.float32, shp["k_zero"], "zero"), dst_capacity, dst_token_offset,
-            _stream(stream)]
-    _check(lib().kivi_pack_keys(*args))
+def kivi_pack_keys(dst: Cache, k, dst_token_offset=0, stream=None):
+    """KIVI item 2: quantize k (fp16 [B][H][T][D]) into dst's records at
+    tokens [dst_token_offset, dst_token_offset + T)."""
+    T = k.shape[2]
+    kp = _dev(k, torch.float16, (dst.B, dst.H, T, dst.D), "k")
+    _check(lib().kivi_pack_keys(ctypes.byref(dst.c), kp, T, dst_token_offset, _stream(stream)))
 
 
-def kivi_pack_values(v, bits, group, codes, scale, zero, dst_capacity, dst_token_offset=0,
-                     stream=None):
-    B, H, T, D = v.shape
-    shp = layout_shapes(B, H, D, bits, bits, group, 1, dst_capacity)
-    args = [_dev(v, torch.float16, None, "v"), B, H, T, D, bits, group,
-            _dev(codes, torch.int32, shp["v_codes"], "codes"),
-            _dev(scale, torch.float32, shp["v_scale"], "scale"),
-            _dev(zero, torch.float32, shp["v_zero"], "zero"), dst_capacity, dst_token_offset,
-            _stream(stream)]
-    _check(lib().kivi_pack_values(*args))
+def kivi_pack_values(dst: Cache, v, dst_token_offset=0, stream=None):
+    """KIVI item 3: quantize v (fp16 [B][H][T][D]) into dst's records."""
+    T = v.shape[2]
+    vp = _dev(v, torch.float16, (dst.B, dst.H, T, dst.D), "v")
+    _check(lib().kivi_pack_values(ctypes.byref(dst.c), vp, T, dst_token_offset, _stream(stream)))
 
 
 def kivi_append(cache: Cache, k_new, v_new, stream=None):
@@ -269,21 +265,18 @@ def bind_append(cache: Cache, k_new, v_new, stream=None) -> BoundCall:
                      (cache, k_new, v_new))
 
 
-def bind_decode_attn(cache: Cache, q, out, workspace, mask=None, tokens_per_split=0,
-                     path=KIVI_PATH_AUTO, stream=None) -> BoundCall:
-    """Bound kivi_decode_attn; the mask, when given, must already cover every
-    token the cache will hold when the call is issued (its row length is the
-    token count at binding time)."""
+def bind_decode_attn(cache: Cache, q, out, workspace, tokens_per_split=0, path=KIVI_PATH_AUTO,
+                     stream=None) -> BoundCall:
+    """Bound kivi_decode_attn without a mask (a mask row's length follows the
+    token count, which changes between calls; masked calls go through
+    kivi_decode_attn)."""
     Hq = q.shape[1]
     qp = _dev(q, torch.float16, (cache.B, Hq, cache.D), "q")
-    mp = None
-    if mask is not None:
-        mp = _dev(mask, torch.float32, (cache.B, cache.n_tokens), "mask")
     op = _dev(out, torch.float32, (cache.B, Hq, cache.D), "out")
     wp = _dev(workspace, torch.uint8, None, "workspace")
     return BoundCall(lib().kivi_decode_attn_ex,
-                     [ctypes.byref(cache.c), qp, Hq, mp, op, wp, workspace.numel(), tokens_per_split,
-                      path, _stream(stream)], (cache, q, mask, out, workspace))
+                     [ctypes.byref(cache.c), qp, Hq, None, op, wp, workspace.numel(),
+                      tokens_per_split, path, _stream(stream)], (cache, q, out, workspace))
 
 
 def bind_decode_step(cache: Cache, k_new, v_new, q, out, workspace, stream=None) -> BoundCall:

@@ -24,6 +24,7 @@ the key-block quantization.
 from __future__ import annotations
 
 import dataclasses
+import math
 
 import numpy as np
 
@@ -46,9 +47,11 @@ class Workload:
 
     @property
     def capacity(self) -> int:
-        """Token capacity: prefill + steps rounded up to a multiple of R."""
+        """Token capacity: prefill + steps rounded up to a multiple of R and
+        of the 128-token record."""
         t = self.T0 + self.steps
-        return ((t + self.R - 1) // self.R) * self.R
+        m = self.R * 128 // math.gcd(self.R, 128)
+        return ((t + m - 1) // m) * m
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)

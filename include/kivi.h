@@ -21,27 +21,36 @@
  *     the token range is a fixed function of the shape.
  *
  * Storage layout of a cache (b < batch, h < n_kv_heads, G = group,
- * D = head_dim, R = residual, cap = capacity, kb/vb = key/value bits):
- *   k_codes  u32 [B][H][cap/G][D][G*kb/32]  key group g of channel c: token
- *                                           e (0 <= e < G) in word e/(32/kb),
- *                                           bits kb*(e % (32/kb)) (KIVI item
- *                                           2: per-channel groups of G
- *                                           tokens, packed along tokens)
- *   k_scale  f32 [B][H][cap/G][D]           one scale and one zero per key
- *   k_zero   f32 [B][H][cap/G][D]           group
- *   v_codes  u32 [B][H][cap][D*vb/32]       value token tau: channel e in
- *                                           word e/(32/vb), bits vb*(e %
- *                                           (32/vb)) (KIVI item 3: per-token
- *                                           groups of G channels, packed
- *                                           along channels)
- *   v_scale  f32 [B][H][D/G][cap]           one scale and one zero per value
- *   v_zero   f32 [B][H][D/G][cap]           group
+ * D = head_dim, R = residual, cap = capacity, kb/vb = key/value bits).  The
+ * quantized part of each (b, h) slab is a run of cap/128 records, one per
+ * 128 consecutive tokens; record j of slab (b, h) holds tokens [128 j,
+ * 128 j + 128) and starts at byte ((b * n_kv_heads + h) * (cap/128) + j) *
+ * RB of `blocks`, RB = kivi_record_bytes(D, kb, vb, G).  A record holds, in
+ * this order (each section a multiple of 16 bytes):
+ *   key codes    u32 [128/G][D][G*kb/32]  key group g of the record (tokens
+ *                                         128 j + G g ..) and channel c:
+ *                                         token e of the group in word
+ *                                         e/(32/kb), bits kb*(e % (32/kb))
+ *                                         (KIVI item 2: per-channel groups
+ *                                         of G tokens, packed along tokens)
+ *   key scales   f32 [128/G][D]
+ *   key zeros    f16 [128/G][D]           the group minimum, an fp16 input
+ *                                         value, stored exactly
+ *   value codes  u32 [128][D*vb/32]       token tau of the record: channel e
+ *                                         in word e/(32/vb), bits vb*(e %
+ *                                         (32/vb)) (KIVI item 3: per-token
+ *                                         groups of G channels, packed along
+ *                                         channels)
+ *   value scales f32 [D/G][128]           channel group, token of the record
+ *   value zeros  f16 [D/G][128]
  *   k_res    fp16 [B][H][R][D]              the fp16 residual window (KIVI
  *   v_res    fp16 [B][H][R][D]              item 4); token tau lives in slot
  *                                           tau % R
- * With t = n_tokens: keys [0, t - t%R) are in k_codes and keys [t - t%R, t)
- * in k_res; values [0, max(0, t-R)) are in v_codes and the last min(t, R)
- * values in v_res.
+ * Every byte a 128-token block of one slab needs is one contiguous record,
+ * so attention streams the store in long sequential runs.
+ * With t = n_tokens: keys [0, t - t%R) are in the records and keys
+ * [t - t%R, t) in k_res; values [0, max(0, t-R)) are in the records and the
+ * last min(t, R) values in v_res.
  *
  * Quantizer (KIVI item 1), bit-exact with an fp32 CPU reference: per group,
  * z = min x, s = (max x - min x) / (2^B - 1) (IEEE fp32 division), code =
@@ -69,10 +78,11 @@ enum {
 /* A KV cache for one attention layer.  Host struct; the array pointers are
  * (device) memory owned by the caller, laid out as described above.  A new
  * cache has n_tokens = 0 and needs no initialisation of its arrays.
- * Constraints: k_bits, v_bits in {2, 4}; group % (32/bits) == 0 for both;
- * head_dim % group == 0 and head_dim <= 256; residual % group == 0;
- * capacity % residual == 0; 0 <= n_tokens <= capacity;
- * batch * n_kv_heads <= 65535. */
+ * Constraints: k_bits, v_bits in {2, 4}; group divides 128 and head_dim and
+ * is a multiple of 32/bits for both; head_dim <= 256; residual % group == 0;
+ * capacity a positive multiple of 128 and of residual; 0 <= n_tokens <=
+ * capacity; batch * n_kv_heads <= 65535; blocks, k_res and v_res 16-byte
+ * aligned. */
 typedef struct kivi_cache {
   int32_t batch;
   int32_t n_kv_heads;
@@ -83,50 +93,43 @@ typedef struct kivi_cache {
   int32_t residual;  /* R: fp16 window length                              */
   int64_t capacity;  /* maximum number of tokens                           */
   int64_t n_tokens;  /* t: changed only by kivi_append, kivi_decode_step */
-  uint32_t *k_codes;
-  float *k_scale;
-  float *k_zero;
-  uint32_t *v_codes;
-  float *v_scale;
-  float *v_zero;
+  uint8_t *blocks;   /* [B][H][capacity/128] records                       */
   uint16_t *k_res;
   uint16_t *v_res;
 } kivi_cache;
 
+/* Bytes of one 128-token record for a shape (0 if the shape is invalid);
+ * a cache's `blocks` array holds batch * n_kv_heads * capacity/128 of them. */
+size_t kivi_record_bytes(int32_t head_dim, int32_t k_bits, int32_t v_bits, int32_t group);
+
 /* KIVI item 2: quantize keys per channel in groups of `group` consecutive
- * tokens and pack the codes along tokens.
- *   k_fp16   (device) fp16 [B][H][T][D], token-major.
- *   codes, scale, zero  (device) destination arrays in the k_codes / k_scale
- *            / k_zero layout above, sized for `dst_capacity` tokens.
- *   The T tokens become destination tokens [dst_token_offset,
- *   dst_token_offset + T).  Requires T % group == 0, dst_token_offset %
- *   group == 0, dst_capacity % group == 0, the range inside the capacity and
- *   B * H <= 65535.  T == 0 is a no-op. */
-int kivi_pack_keys(const void *k_fp16, int32_t B, int32_t H, int64_t T, int32_t D,
-                   int32_t bits, int32_t group, uint32_t *codes, float *scale,
-                   float *zero, int64_t dst_capacity, int64_t dst_token_offset,
-                   void *stream);
+ * tokens and store them in the records of `dst` (packed along tokens).
+ *   dst      a cache descriptor: its shape and `blocks` say where the codes,
+ *            scales and zeros go; n_tokens and the windows are neither read
+ *            nor changed.
+ *   k_fp16   (device) fp16 [batch][n_kv_heads][T][head_dim], token-major.
+ *   The T tokens become tokens [dst_token_offset, dst_token_offset + T).
+ *   Requires T % group == 0, dst_token_offset % group == 0 and the range
+ *   inside the capacity.  T == 0 is a no-op. */
+int kivi_pack_keys(const kivi_cache *dst, const void *k_fp16, int64_t T,
+                   int64_t dst_token_offset, void *stream);
 
 /* KIVI item 3: quantize values per token in groups of `group` consecutive
- * channels and pack the codes along channels.
- *   v_fp16   (device) fp16 [B][H][T][D].
- *   codes, scale, zero  (device) destination arrays in the v_codes / v_scale
- *            / v_zero layout above, sized for `dst_capacity` tokens.
- *   Tokens go to rows [dst_token_offset, dst_token_offset + T); the same
- *   constraints on shapes and B * H as for keys, without the multiples of
- *   the group on T and the offset. */
-int kivi_pack_values(const void *v_fp16, int32_t B, int32_t H, int64_t T, int32_t D,
-                     int32_t bits, int32_t group, uint32_t *codes, float *scale,
-                     float *zero, int64_t dst_capacity, int64_t dst_token_offset,
-                     void *stream);
+ * channels and store them in the records of `dst` (packed along channels).
+ *   v_fp16   (device) fp16 [batch][n_kv_heads][T][head_dim].
+ *   Tokens go to [dst_token_offset, dst_token_offset + T) (any offset); the
+ *   rest as for kivi_pack_keys. */
+int kivi_pack_values(const kivi_cache *dst, const void *v_fp16, int64_t T,
+                     int64_t dst_token_offset, void *stream);
 
 /* KIVI item 4: append n_new tokens to the cache through the fp16 window.
  * The result is bit-identical to appending them one at a time: for each
  * token tau, if tau >= R the value in slot tau % R (token tau - R) is
- * quantized into v_codes first; the new key and value then take slot tau % R;
- * when tau + 1 is a multiple of R the R keys of the window are quantized
- * into k_codes.  Appending T tokens to an empty cache is the prefill rule:
- * keys [0, T - T%R) and values [0, T - R) quantized, the rest kept in fp16.
+ * quantized into its record first; the new key and value then take slot
+ * tau % R; when tau + 1 is a multiple of R the R keys of the window are
+ * quantized into their records.  Appending T tokens to an empty cache is
+ * the prefill rule: keys [0, T - T%R) and values [0, T - R) quantized, the
+ * rest kept in fp16.
  *   k_new_fp16, v_new_fp16  (device) fp16 [B][H][n_new][D].
  *   n_new >= 0; KIVI_ERR_CAPACITY if n_tokens + n_new > capacity.
  * On success c->n_tokens grows by n_new (on the host, at once; the kernels
@@ -161,11 +164,11 @@ int kivi_decode_attn(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads,
  *                     the scalar kernel), KIVI_PATH_GENERIC (scalar kernel
  *                     for every token), KIVI_PATH_MATRIX (matrix-core
  *                     kernel: 2-bit codes, head_dim 128, G 32, 1, 2 or 4
- *                     query heads per KV head, capacity below 2^29 tokens,
- *                     16-byte aligned q) or KIVI_PATH_VECTOR (vector
- *                     kernel: 2- or 4-bit codes, head_dim 128, G 32, R a
- *                     multiple of 32, 1 or 2 query heads per KV head,
- *                     capacity below 2^26 tokens).  A
+ *                     query heads per KV head, 16-byte aligned q) or
+ *                     KIVI_PATH_VECTOR (vector kernel: 2- or 4-bit codes,
+ *                     head_dim 128, G 32, R a multiple of 32, 1 or 2 query
+ *                     heads per KV head, capacity below 2^26 tokens and a
+ *                     slab's records below 4 GB).  A
  *                     forced path the shape does not allow is rejected.
  * The workspace must hold kivi_decode_attn_workspace_bytes_ex() bytes. */
 enum { KIVI_PATH_AUTO = 0, KIVI_PATH_GENERIC = 1, KIVI_PATH_MATRIX = 2, KIVI_PATH_VECTOR = 3 };
@@ -181,9 +184,8 @@ size_t kivi_decode_attn_workspace_bytes_ex(const kivi_cache *c, int32_t n_q_head
  * (within the attention tolerance) the same output as
  *   kivi_append(c, k_new, v_new, 1); kivi_decode_attn(c, q, ...).
  * Where the matrix-core kernel takes the shape (2-bit keys and values,
- * head_dim 128, G 32, 1, 2 or 4 query heads per KV head, capacity below
- * 2^29 tokens, 16-byte aligned q, k_new and v_new), the append runs inside
- * the attention launch: the new
+ * head_dim 128, G 32, 1, 2 or 4 query heads per KV head, 16-byte aligned
+ * q, k_new and v_new), the append runs inside the attention launch: the new
  * key and value are read from k_new / v_new, the value that leaves the
  * window and a key block the token completes are quantized by the
  * workgroups that attend over them, and the cache writes happen where no

@@ -2,6 +2,9 @@
 (through the C ABI) and in the CPU oracle, and compare them."""
 from __future__ import annotations
 
+import concurrent.futures
+import math
+import os
 import sys
 
 import numpy as np
@@ -27,6 +30,26 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
+def cap_for(t: int, R: int) -> int:
+    """Smallest capacity >= t (at least one record) that is a multiple of R
+    and of the 128-token record."""
+    m = R * 128 // math.gcd(R, 128)
+    return max(m, -(-t // m) * m)
+
+
+_POOL = None
+
+
+def pool() -> concurrent.futures.ThreadPoolExecutor:
+    """Threads for the oracle: its C code runs behind ctypes, which releases
+    the GIL, so slabs are rebuilt in parallel on the host cores (at most 16,
+    the host share of one GPU)."""
+    global _POOL
+    if _POOL is None:
+        _POOL = concurrent.futures.ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1)))
+    return _POOL
+
+
 def gpu_cache(w, capacity=None) -> kivi.Cache:
     cap = w.capacity if capacity is None else capacity
     return kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, cap)
@@ -41,31 +64,113 @@ def b16(a: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(a).view(np.uint16)
 
 
-def compare_slab(g: kivi.Cache, b: int, h: int, o: oracle.Cache, ob: int = 0, oh: int = 0):
+def logical(c) -> dict:
+    """The logical arrays (k_codes, k_scale, k_zero, v_codes, v_scale, v_zero)
+    of a device cache, re-indexed on the host from its records."""
+    return oracle.unpack_records(host(c.blocks), c.B, c.H, c.cap, c.D, c.kb, c.vb, c.G)
+
+
+def compare_slab(g: kivi.Cache, b: int, h: int, o: oracle.Cache, ob: int = 0, oh: int = 0,
+                 gl: dict | None = None, ol: dict | None = None, gres=None):
     """Bitwise comparison of the valid part of slab (b, h) of the GPU cache
-    with slab (ob, oh) of the oracle cache."""
+    with slab (ob, oh) of the oracle cache.  gl / ol: logical views already
+    taken; gres: host copies (k_res, v_res) of the GPU windows (to compare
+    many slabs, from several threads, with one device copy each)."""
     t = g.n_tokens
     assert o.n_tokens == t
     R, G = g.R, g.G
     n_kq, n_vq = t - t % R, max(0, t - R)
-    gk = host(g.k_codes[b, h, :n_kq // G]).view(np.uint32)
-    assert np.array_equal(gk, o.k_codes[ob, oh, :n_kq // G]), "key codes"
-    assert np.array_equal(host(g.k_scale[b, h, :n_kq // G]).view(np.uint32),
-                          o.k_scale[ob, oh, :n_kq // G].view(np.uint32)), "key scales"
-    assert np.array_equal(host(g.k_zero[b, h, :n_kq // G]).view(np.uint32),
-                          o.k_zero[ob, oh, :n_kq // G].view(np.uint32)), "key zeros"
-    gv = host(g.v_codes[b, h, :n_vq]).view(np.uint32)
-    assert np.array_equal(gv, o.v_codes[ob, oh, :n_vq]), "value codes"
-    assert np.array_equal(host(g.v_scale[b, h, :, :n_vq]).view(np.uint32),
-                          o.v_scale[ob, oh, :, :n_vq].view(np.uint32)), "value scales"
-    assert np.array_equal(host(g.v_zero[b, h, :, :n_vq]).view(np.uint32),
-                          o.v_zero[ob, oh, :, :n_vq].view(np.uint32)), "value zeros"
+    gl = logical(g) if gl is None else gl
+    ol = o.logical() if ol is None else ol
+
+    def eq(name, gi, oi):
+        x, y = np.ascontiguousarray(gl[name][gi]), np.ascontiguousarray(ol[name][oi])
+        assert x.shape == y.shape, name
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), f"{name} of slab ({b}, {h})"
+
+    eq("k_codes", (b, h, slice(0, n_kq // G)), (ob, oh, slice(0, n_kq // G)))
+    eq("k_scale", (b, h, slice(0, n_kq // G)), (ob, oh, slice(0, n_kq // G)))
+    eq("k_zero", (b, h, slice(0, n_kq // G)), (ob, oh, slice(0, n_kq // G)))
+    eq("v_codes", (b, h, slice(0, n_vq)), (ob, oh, slice(0, n_vq)))
+    eq("v_scale", (b, h, slice(None), slice(0, n_vq)), (ob, oh, slice(None), slice(0, n_vq)))
+    eq("v_zero", (b, h, slice(None), slice(0, n_vq)), (ob, oh, slice(None), slice(0, n_vq)))
     kslots = [tau % R for tau in range(n_kq, t)]
     vslots = [tau % R for tau in range(n_vq, t)]
-    gkr = host(g.k_res[b, h]).view(np.uint16)
-    gvr = host(g.v_res[b, h]).view(np.uint16)
-    assert np.array_equal(gkr[kslots], o.k_res[ob, oh][kslots]), "key window"
-    assert np.array_equal(gvr[vslots], o.v_res[ob, oh][vslots]), "value window"
+    if gres is None:
+        gkr, gvr = host(g.k_res[b, h]).view(np.uint16), host(g.v_res[b, h]).view(np.uint16)
+    else:
+        gkr, gvr = gres[0][b, h], gres[1][b, h]
+    assert np.array_equal(gkr[kslots], o.k_res[ob, oh][kslots]), f"key window of slab ({b}, {h})"
+    assert np.array_equal(gvr[vslots], o.v_res[ob, oh][vslots]), f"value window of slab ({b}, {h})"
+
+
+def compare_rows(g: kivi.Cache, b0: int, o: oracle.Cache, gl: dict, gres):
+    """Batch rows [b0, b0 + o.B) of the GPU cache (every KV head) against an
+    oracle cache holding just those rows, bit for bit, in one comparison per
+    array (every slab has the same token count)."""
+    t = g.n_tokens
+    assert o.n_tokens == t
+    R, G, b1 = g.R, g.G, b0 + o.B
+    n_kq, n_vq = t - t % R, max(0, t - R)
+    ol = o.logical()
+    rows = slice(b0, b1)
+    for name, sl in (("k_codes", np.s_[:, :, :n_kq // G]), ("k_scale", np.s_[:, :, :n_kq // G]),
+                     ("k_zero", np.s_[:, :, :n_kq // G]), ("v_codes", np.s_[:, :, :n_vq]),
+                     ("v_scale", np.s_[:, :, :, :n_vq]), ("v_zero", np.s_[:, :, :, :n_vq])):
+        x = np.ascontiguousarray(gl[name][rows][sl])
+        y = np.ascontiguousarray(ol[name][sl])
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), f"{name} of rows [{b0}, {b1})"
+    kslots = [tau % R for tau in range(n_kq, t)]
+    vslots = [tau % R for tau in range(n_vq, t)]
+    assert np.array_equal(gres[0][rows][:, :, kslots], o.k_res[:, :, kslots]), "key window"
+    assert np.array_equal(gres[1][rows][:, :, vslots], o.v_res[:, :, vslots]), "value window"
+
+
+def host_windows(g: kivi.Cache):
+    return host(g.k_res).view(np.uint16), host(g.v_res).view(np.uint16)
+
+
+def oracle_slab(w, inp, b: int, h: int, n_steps: int = 0, capacity=None) -> oracle.Cache:
+    """The oracle's cache of slab (b, h) of workload w: the prefill, then the
+    first n_steps appended tokens."""
+    o = oracle.Cache(1, 1, w.D, w.k_bits, w.v_bits, w.G, w.R,
+                     w.capacity if capacity is None else capacity)
+    o.append(b16(inp["k0"][b:b + 1, h:h + 1]), b16(inp["v0"][b:b + 1, h:h + 1]))
+    for s in range(n_steps):
+        o.append(b16(inp["k_steps"][s][b:b + 1, h:h + 1]), b16(inp["v_steps"][s][b:b + 1, h:h + 1]))
+    return o
+
+
+def check_every_slab(w, g: kivi.Cache, orc: dict, outs: dict, q, mask=None, stores=True):
+    """Every (batch row, KV head) slab of workload w: the packed store and
+    the windows of the GPU cache bit for bit against the slab's oracle cache
+    (orc[(b, h)]), and every output of outs (label -> [B][Hq][D]) within the
+    tolerance of the oracle's attention.  The oracle runs in the thread pool."""
+    rep = w.Hq // w.Hkv
+    gl = logical(g) if stores else None
+    gres = host_windows(g) if stores else None
+
+    def one(bh):
+        b, h = bh
+        o = orc[bh]
+        if stores:
+            compare_slab(g, b, h, o, gl=gl, gres=gres)
+        m = None if mask is None else mask[b:b + 1]
+        return bh, o.decode_attn(b16(q[b:b + 1, h * rep:(h + 1) * rep]), m)[0]
+
+    ref = np.zeros((w.B, w.Hq, w.D), np.float32)
+    for (b, h), r in pool().map(one, sorted(orc)):
+        ref[b, h * rep:(h + 1) * rep] = r
+    for label, out in outs.items():
+        assert_close(out, ref, f"{w.name} {label}, all {len(orc)} slabs")
+    return ref
+
+
+def oracle_all_slabs(w, inp, n_steps: int = 0, capacity=None) -> dict:
+    """Oracle caches of every slab of workload w, built in the thread pool."""
+    slabs = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
+    caches = pool().map(lambda bh: oracle_slab(w, inp, bh[0], bh[1], n_steps, capacity), slabs)
+    return dict(zip(slabs, caches))
 
 
 def assert_close(got: np.ndarray, ref: np.ndarray, what: str = "", value_scale: float = 1.0):

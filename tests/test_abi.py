@@ -45,18 +45,40 @@ def test_status_strings(L):
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
 
 
-def _pack(L, fn, **kw):
-    a = dict(x=FAKE, B=1, H=1, T=64, D=128, bits=2, G=32, cap=128, off=0)
+def _cache(**kw):
+    from decode_attention_pack_amd.kivi import CCache
+    a = dict(batch=1, n_kv_heads=2, head_dim=128, k_bits=2, v_bits=2, group=32, residual=128,
+             capacity=1024, n_tokens=0, blocks=0x1000, k_res=0x1000, v_res=0x1000)
     a.update(kw)
-    return getattr(L, fn)(a["x"], a["B"], a["H"], a["T"], a["D"], a["bits"], a["G"], FAKE, FAKE,
-                          FAKE, a["cap"], a["off"], None)
+    return CCache(a["batch"], a["n_kv_heads"], a["head_dim"], a["k_bits"], a["v_bits"], a["group"],
+                  a["residual"], a["capacity"], a["n_tokens"], a["blocks"], a["k_res"], a["v_res"])
+
+
+def test_record_bytes(L):
+    """Record size of the packed store (include/kivi.h): 14336 bytes at 2-bit,
+    G 32, head_dim 128 (4096 + 2048 + 1024 + 4096 + 2048 + 1024); 0 for
+    shapes outside the layout."""
+    assert L.kivi_record_bytes(128, 2, 2, 32) == 14336
+    assert L.kivi_record_bytes(128, 4, 4, 32) == 8192 + 2048 + 1024 + 8192 + 2048 + 1024
+    assert L.kivi_record_bytes(64, 2, 4, 64) == 2048 + 512 + 256 + 4096 + 512 + 256
+    for bad in [(128, 3, 2, 32), (128, 2, 2, 48), (100, 2, 2, 32), (512, 2, 2, 32), (128, 2, 2, 8)]:
+        assert L.kivi_record_bytes(*bad) == 0, bad
+
+
+def _pack(L, fn, cache=None, x=FAKE, T=64, off=0):
+    c = _cache() if cache is None else cache
+    return getattr(L, fn)(ctypes.byref(c), x, T, off, None)
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(bits=3), -1), (dict(bits=8), -1), (dict(G=24), -1), (dict(D=100), -1),
-    (dict(D=512), -1), (dict(T=33), -1), (dict(off=16), -1), (dict(cap=100), -1),
-    (dict(T=-1), -1), (dict(B=0), -1), (dict(T=96, off=64), -2), (dict(x=None), -1),
-    (dict(B=65536), -1), (dict(B=256, H=256), -1),
+    (dict(cache=_cache(k_bits=3)), -1), (dict(cache=_cache(k_bits=8)), -1),
+    (dict(cache=_cache(group=24)), -1), (dict(cache=_cache(group=48)), -1),
+    (dict(cache=_cache(head_dim=100)), -1), (dict(cache=_cache(head_dim=512)), -1),
+    (dict(T=33), -1), (dict(off=16), -1), (dict(cache=_cache(capacity=1000)), -1),
+    (dict(T=-1), -1), (dict(cache=_cache(batch=0)), -1), (dict(T=96, off=960), -2),
+    (dict(x=None), -1), (dict(cache=_cache(batch=65536, n_kv_heads=1)), -1),
+    (dict(cache=_cache(batch=256, n_kv_heads=256)), -1),
+    (dict(cache=_cache(blocks=0x1008)), -1), (dict(cache=_cache(blocks=0)), -1),
 ])
 def test_pack_keys_rejects(L, kw, status):
     assert _pack(L, "kivi_pack_keys", **kw) == status
@@ -64,7 +86,8 @@ def test_pack_keys_rejects(L, kw, status):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(bits=1), -1), (dict(G=12, bits=4), -1), (dict(T=129), -2), (dict(T=65, off=64), -2),
+    (dict(cache=_cache(v_bits=1)), -1), (dict(cache=_cache(group=12, v_bits=4, k_bits=4)), -1),
+    (dict(T=1025), -2), (dict(T=65, off=960), -2),
 ])
 def test_pack_values_rejects(L, kw, status):
     assert _pack(L, "kivi_pack_values", **kw) == status
@@ -76,20 +99,12 @@ def test_zero_tokens_is_a_no_op(L):
     assert _pack(L, "kivi_pack_values", T=0) == 0
 
 
-def _cache(**kw):
-    from decode_attention_pack_amd.kivi import CCache
-    a = dict(batch=1, n_kv_heads=2, head_dim=128, k_bits=2, v_bits=2, group=32, residual=128,
-             capacity=1024, n_tokens=0)
-    a.update(kw)
-    c = CCache(a["batch"], a["n_kv_heads"], a["head_dim"], a["k_bits"], a["v_bits"], a["group"],
-               a["residual"], a["capacity"], a["n_tokens"], *([0x1000] * 8))
-    return c
-
-
 @pytest.mark.parametrize("kw", [dict(k_bits=3), dict(v_bits=5), dict(residual=48),
-                                dict(capacity=1000), dict(n_tokens=-1), dict(n_tokens=2048),
+                                dict(capacity=1000), dict(capacity=288, residual=96),
+                                dict(n_tokens=-1), dict(n_tokens=2048),
                                 dict(batch=0), dict(head_dim=100), dict(group=20),
-                                dict(batch=32768, n_kv_heads=2)])
+                                dict(batch=32768, n_kv_heads=2), dict(k_res=0x1004),
+                                dict(v_res=0x1002), dict(blocks=0x1001)])
 def test_append_rejects_bad_cache(L, kw):
     c = _cache(**kw)
     assert L.kivi_append(ctypes.byref(c), FAKE, FAKE, 1, None) == -1
@@ -136,6 +151,19 @@ def test_decode_rejects(L):
     assert call(tps=96) == -1
     assert call(path=5) == -1
     assert L.kivi_decode_attn(None, FAKE, 4, None, FAKE, FAKE, n, None) == -1
+
+
+@pytest.mark.parametrize("field", ["blocks", "k_res", "v_res"])
+def test_misaligned_cache_rejected_on_every_path(L, field):
+    """A cache array that is not 16-byte aligned is rejected before any
+    launch, also when the matrix-core path is forced (its global->LDS copies
+    move 16 bytes per lane)."""
+    c = _cache(n_tokens=300, **{field: 0x1008})
+    n = L.kivi_decode_attn_workspace_bytes_ex(ctypes.byref(_cache(n_tokens=300)), 4, 0, 2)
+    for path in (0, 1, 2, 3):
+        assert L.kivi_decode_attn_ex(ctypes.byref(c), FAKE, 4, None, FAKE, FAKE, n, 0, path,
+                                     None) == -1
+        assert b"aligned" in L.kivi_last_error()
 
 
 def test_decode_step_rejects(L):

@@ -7,7 +7,8 @@ import torch
 
 import oracle
 from decode_attention_pack_amd import kivi, synth
-from tests.gpu_util import assert_close, b16, compare_slab, dev, host, say
+from tests.gpu_util import (assert_close, b16, cap_for, check_every_slab, compare_slab, dev,
+                            gpu_cache, host, logical, oracle_all_slabs, pool, say)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -19,7 +20,7 @@ def test_append_random_chunks(kb, vb, R, D):
     rng = np.random.default_rng(kb * 1000 + vb * 100 + R)
     B, H, G = 2, 3, 32
     t_end = 3 * R + 5
-    cap = ((t_end + R - 1) // R) * R
+    cap = cap_for(t_end, R)
     K = rng.standard_normal((B, H, t_end, D)).astype(np.float16)
     V = rng.standard_normal((B, H, t_end, D)).astype(np.float16)
     g = kivi.Cache(B, H, D, kb, vb, G, R, cap)
@@ -38,7 +39,8 @@ def test_append_random_chunks(kb, vb, R, D):
 
 
 @pytest.mark.parametrize("kb,vb,G,D,R", [(2, 2, 16, 64, 32), (4, 4, 64, 128, 64), (2, 4, 32, 96, 64),
-                                         (4, 2, 48, 96, 48), (2, 2, 128, 256, 128)])
+                                         (4, 2, 16, 96, 48), (2, 2, 128, 256, 128),
+                                         (4, 4, 8, 64, 96)])
 def test_single_token_appends(kb, vb, G, D, R):
     """Decode-step appends (one token per call) through both the fused
     single-token kernel (G a power of two <= 64) and the general path (other
@@ -46,7 +48,7 @@ def test_single_token_appends(kb, vb, G, D, R):
     rng = np.random.default_rng(G * 7 + D + kb)
     B, H = 2, 2
     t_end = 2 * R + 3
-    cap = ((t_end + R - 1) // R) * R
+    cap = cap_for(t_end, R)
     K = rng.standard_normal((B, H, t_end, D)).astype(np.float16)
     V = (rng.standard_normal((B, H, t_end, D)) * 3).astype(np.float16)
     g = kivi.Cache(B, H, D, kb, vb, G, R, cap)
@@ -73,41 +75,39 @@ def test_prefill_equals_single_appends_on_gpu():
         kivi.kivi_append(s, K[:, :, t:t + 1].contiguous(), V[:, :, t:t + 1].contiguous())
     torch.cuda.synchronize()
     n_kq, n_vq = T - T % R, T - R
-    assert torch.equal(a.k_codes[:, :, :n_kq // G], s.k_codes[:, :, :n_kq // G])
-    assert torch.equal(a.k_scale[:, :, :n_kq // G], s.k_scale[:, :, :n_kq // G])
-    assert torch.equal(a.v_codes[:, :, :n_vq], s.v_codes[:, :, :n_vq])
-    assert torch.equal(a.v_zero[..., :n_vq], s.v_zero[..., :n_vq])
+    la, ls = logical(a), logical(s)
+    for name, sl in (("k_codes", np.s_[:, :, :n_kq // G]), ("k_scale", np.s_[:, :, :n_kq // G]),
+                     ("k_zero", np.s_[:, :, :n_kq // G]), ("v_codes", np.s_[:, :, :n_vq]),
+                     ("v_scale", np.s_[..., :n_vq]), ("v_zero", np.s_[..., :n_vq])):
+        assert np.array_equal(np.ascontiguousarray(la[name][sl]).view(np.uint8),
+                              np.ascontiguousarray(ls[name][sl]).view(np.uint8)), name
     assert torch.equal(a.k_res[:, :, :T % R], s.k_res[:, :, :T % R])
     assert torch.equal(a.v_res, s.v_res)
 
 
 def test_llama2_decode_steps():
     """The Llama-2-7B-shaped workload: 4064-token prefill then 64 decode steps
-    (append one token, attend).  Step 32 reaches t = 4096 and quantizes a key
-    block.  Three sampled (batch, head) slabs are checked bit for bit after
-    every step, and their attention against the oracle."""
+    (kivi_append of one token, then kivi_decode_attn).  Step 32 reaches
+    t = 4096 and quantizes a key block.  Every slab's attention after every
+    step, and every packed store and window at steps 0, 31, 32, 33, every 8th
+    and the last, against the oracle."""
     w = synth.WORKLOADS[2]
     inp = synth.make_inputs(w)
-    g = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
+    g = gpu_cache(w)
     say(f"{w.name}: prefill {w.T0}")
     kivi.kivi_append(g, dev(inp["k0"]), dev(inp["v0"]))
-    slabs = [(0, 0), (w.B - 1, w.Hkv - 1), (3, 17)]
-    orc = {}
-    for b, h in slabs:
-        o = oracle.Cache(1, 1, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
-        o.append(b16(inp["k0"][b:b + 1, h:h + 1]), b16(inp["v0"][b:b + 1, h:h + 1]))
-        orc[(b, h)] = o
+    orc = oracle_all_slabs(w, inp, n_steps=0)
     ws = g.new_workspace(w.Hq)
+    store_steps = {0, 31, 32, 33, w.steps - 1} | set(range(7, w.steps, 8))
     for step in range(w.steps):
         kivi.kivi_append(g, dev(inp["k_steps"][step]), dev(inp["v_steps"][step]))
         q = inp["q_steps"][step]
         out = host(kivi.kivi_decode_attn(g, dev(q), workspace=ws))
-        for (b, h), o in orc.items():
-            o.append(b16(inp["k_steps"][step][b:b + 1, h:h + 1]),
-                     b16(inp["v_steps"][step][b:b + 1, h:h + 1]))
-            compare_slab(g, b, h, o)
-            ref = o.decode_attn(b16(q[b:b + 1, h:h + 1]))
-            if step % 16 == 0 or step == 31 or step == w.steps - 1:
-                assert_close(out[b, h], ref[0, 0], f"step {step} t={g.n_tokens} b{b} h{h}")
-            else:
-                np.testing.assert_allclose(out[b, h], ref[0, 0], atol=2e-3, rtol=1e-3)
+
+        def one(bh, step=step):
+            b, h = bh
+            orc[bh].append(b16(inp["k_steps"][step][b:b + 1, h:h + 1]),
+                           b16(inp["v_steps"][step][b:b + 1, h:h + 1]))
+        list(pool().map(one, sorted(orc)))
+        check_every_slab(w, g, orc, {f"step {step} t={g.n_tokens}": out}, q,
+                         stores=step in store_steps)

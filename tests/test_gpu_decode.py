@@ -7,7 +7,8 @@ import torch
 
 import oracle
 from decode_attention_pack_amd import kivi, synth
-from tests.gpu_util import assert_close, b16, compare_slab, dev, host, say
+from tests.gpu_util import (assert_close, b16, cap_for, check_every_slab, compare_rows, dev,
+                            gpu_cache, host, host_windows, logical, oracle_all_slabs, pool, say)
 from tests.textbook import dense_attention
 
 pytestmark = [pytest.mark.gpu,
@@ -26,11 +27,12 @@ def paths_for(D, kb, vb, G, R, rep, cap):
     return PATHS + ([kivi.KIVI_PATH_VECTOR] if vector_ok(D, kb, vb, G, R, rep, cap) else [])
 
 
-def _run_workload(w, slabs, paths=None):
-    """Prefill + one decode step of workload w on the GPU; the oracle rebuilds
-    the sampled (batch, kv head) slabs alone and checks them."""
+def _run_workload(w, paths=None):
+    """Prefill + one decode step of workload w on the GPU, in the launch
+    configuration the benchmark times; the oracle rebuilds every (batch, kv
+    head) slab alone and checks its packed store, windows and attention."""
     inp = synth.make_inputs(w)
-    g = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
+    g = gpu_cache(w)
     say(f"{w.name}: prefill {w.T0} + 1 step")
     kivi.kivi_append(g, dev(inp["k0"]), dev(inp["v0"]))
     kivi.kivi_append(g, dev(inp["k_steps"][0]), dev(inp["v_steps"][0]))
@@ -38,42 +40,34 @@ def _run_workload(w, slabs, paths=None):
     rep = w.Hq // w.Hkv
     if paths is None:
         paths = paths_for(w.D, w.k_bits, w.v_bits, w.G, w.R, rep, w.capacity)
-    outs = {p: host(kivi.kivi_decode_attn(g, dev(q), path=p)) for p in paths}
-    for b, h in slabs:
-        o = oracle.Cache(1, 1, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
-        o.append(b16(inp["k0"][b:b + 1, h:h + 1]), b16(inp["v0"][b:b + 1, h:h + 1]))
-        o.append(b16(inp["k_steps"][0][b:b + 1, h:h + 1]), b16(inp["v_steps"][0][b:b + 1, h:h + 1]))
-        compare_slab(g, b, h, o)
-        ref = o.decode_attn(b16(q[b:b + 1, h * rep:(h + 1) * rep]))[0]
-        for p, out in outs.items():
-            assert_close(out[b, h * rep:(h + 1) * rep], ref, f"{w.name} path {p} b{b} kv{h}")
+    outs = {f"path {p}": host(kivi.kivi_decode_attn(g, dev(q), path=p)) for p in paths}
+    say(f"{w.name}: oracle over {w.B * w.Hkv} slabs")
+    orc = oracle_all_slabs(w, inp, n_steps=1)
+    check_every_slab(w, g, orc, outs, q)
     return g, outs
 
 
 def test_tiny():
-    _run_workload(synth.WORKLOADS[1], [(0, 0)])
+    _run_workload(synth.WORKLOADS[1])
 
 
 def test_kivi4_b64():
-    w = synth.WORKLOADS[3]
-    _run_workload(w, [(0, 0), (63, 31), (17, 9)])
+    _run_workload(synth.WORKLOADS[3])
 
 
 def test_llama3_gqa_32k():
-    w = synth.WORKLOADS[4]
-    _run_workload(w, [(0, 0), (3, 7), (2, 5)])
+    _run_workload(synth.WORKLOADS[4])
 
 
 def test_long_128k():
-    w = synth.WORKLOADS[5]
-    _run_workload(w, [(0, 0), (0, 7), (0, 3)])
+    _run_workload(synth.WORKLOADS[5])
 
 
 def _small_case(rng, B, H, rep, D, kb, vb, G, R, t):
     K = (rng.standard_normal((B, H, t, D)) * rng.uniform(0.5, 15, (1, H, 1, D))).astype(np.float16)
     V = rng.standard_normal((B, H, t, D)).astype(np.float16)
     q = rng.standard_normal((B, H * rep, D)).astype(np.float16)
-    cap = max(R, ((t + R - 1) // R) * R)
+    cap = cap_for(t, R)
     g = kivi.Cache(B, H, D, kb, vb, G, R, cap)
     o = oracle.Cache(B, H, D, kb, vb, G, R, cap)
     if t:
@@ -141,7 +135,8 @@ def test_mask(rep, kb, vb):
         assert not np.isnan(out).any() and not out[1].any()
         assert_close(out, ref, f"mask path={p}")
     zero = host(kivi.kivi_decode_attn(g, dev(q), mask=dev(np.zeros((2, t), np.float32))))
-    assert np.array_equal(zero, host(kivi.kivi_decode_attn(g, dev(q))))
+    # an all-zero mask changes nothing but the rounding order of the merges
+    np.testing.assert_allclose(zero, host(kivi.kivi_decode_attn(g, dev(q))), atol=1e-5, rtol=1e-5)
 
 
 # The matrix cores sum the fp16 products of one MFMA after aligning them to the
@@ -259,11 +254,12 @@ def test_vector_path_rejects_other_shapes():
 
 def test_most_slabs_append_and_decode():
     """65535 slabs (batch x KV heads), the most a cache may hold: prefill,
-    one appended token, and attention through every path the shape allows,
-    checked on three sampled slabs against the oracle."""
+    one appended token, and attention through every path the shape allows.
+    The oracle rebuilds every slab (in chunks of batch rows, in parallel) and
+    checks the packed stores bit for bit and every output."""
     rng = np.random.default_rng(4242)
     B, H, D, G, R, t0 = 65535, 1, 128, 32, 32, 40
-    cap = 64
+    cap = 128
     K = rng.standard_normal((B, H, t0 + 1, D), dtype=np.float32).astype(np.float16)
     V = rng.standard_normal((B, H, t0 + 1, D), dtype=np.float32).astype(np.float16)
     q = rng.standard_normal((B, H, D), dtype=np.float32).astype(np.float16)
@@ -273,24 +269,32 @@ def test_most_slabs_append_and_decode():
     kivi.kivi_append(g, dev(K[:, :, t0:]), dev(V[:, :, t0:]))
     outs = {p: host(kivi.kivi_decode_attn(g, dev(q), path=p))
             for p in paths_for(D, 2, 2, G, R, 1, cap) + [kivi.KIVI_PATH_MATRIX]}
-    for b in (0, B // 2 + 3, B - 1):
-        o = oracle.Cache(1, 1, D, 2, 2, G, R, cap)
-        o.append(b16(K[b:b + 1, :, :t0]), b16(V[b:b + 1, :, :t0]))
-        o.append(b16(K[b:b + 1, :, t0:]), b16(V[b:b + 1, :, t0:]))
-        compare_slab(g, b, 0, o)
-        ref = o.decode_attn(b16(q[b:b + 1]))
-        for p, out in outs.items():
-            assert_close(out[b:b + 1], ref, f"slab {b} path {p}")
+    gl, gres = logical(g), host_windows(g)
+    chunk = 4096
+
+    def rows(b0):
+        b1 = min(B, b0 + chunk)
+        o = oracle.Cache(b1 - b0, H, D, 2, 2, G, R, cap)
+        o.append(b16(K[b0:b1, :, :t0]), b16(V[b0:b1, :, :t0]))
+        o.append(b16(K[b0:b1, :, t0:]), b16(V[b0:b1, :, t0:]))
+        compare_rows(g, b0, o, gl, gres)
+        return b0, o.decode_attn(b16(q[b0:b1]))
+
+    ref = np.zeros((B, H, D), np.float32)
+    for b0, r in pool().map(rows, range(0, B, chunk)):
+        ref[b0:b0 + r.shape[0]] = r
+    for p, out in outs.items():
+        assert_close(out, ref, f"all {B} slabs, path {p}")
 
 
 def test_llama3_gqa_32k_masked():
     """The full 32k GQA workload with an additive mask (a fifth of the tokens
     at -inf, the rest N(0, 1)): the masked instantiation of the matrix kernel,
     whose workgroups stage each block's mask row by DMA, against the oracle on
-    three sampled slabs."""
+    every slab."""
     w = synth.WORKLOADS[4]
     inp = synth.make_inputs(w)
-    g = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
+    g = gpu_cache(w)
     say(f"{w.name}: prefill {w.T0} + 1 step, masked")
     kivi.kivi_append(g, dev(inp["k0"]), dev(inp["v0"]))
     kivi.kivi_append(g, dev(inp["k_steps"][0]), dev(inp["v_steps"][0]))
@@ -299,11 +303,6 @@ def test_llama3_gqa_32k_masked():
     mask = np.where(rng.random((w.B, t)) < 0.2, -np.inf,
                     rng.standard_normal((w.B, t))).astype(np.float32)
     q = inp["q_steps"][0]
-    rep = w.Hq // w.Hkv
     out = host(kivi.kivi_decode_attn(g, dev(q), mask=dev(mask)))
-    for b, h in [(0, 0), (w.B - 1, w.Hkv - 1), (2, 5)]:
-        o = oracle.Cache(1, 1, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
-        o.append(b16(inp["k0"][b:b + 1, h:h + 1]), b16(inp["v0"][b:b + 1, h:h + 1]))
-        o.append(b16(inp["k_steps"][0][b:b + 1, h:h + 1]), b16(inp["v_steps"][0][b:b + 1, h:h + 1]))
-        ref = o.decode_attn(b16(q[b:b + 1, h * rep:(h + 1) * rep]), mask[b:b + 1])[0]
-        assert_close(out[b, h * rep:(h + 1) * rep], ref, f"masked b{b} kv{h}")
+    orc = oracle_all_slabs(w, inp, n_steps=1)
+    check_every_slab(w, g, orc, {"masked": out}, q, mask=mask, stores=False)

@@ -7,32 +7,29 @@ import torch
 
 import oracle
 from decode_attention_pack_amd import kivi, synth
-from tests.gpu_util import b16, dev, host, say
+from tests.gpu_util import b16, cap_for, dev, host, logical, pool, say
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 
-def _gpu_pack(x16, bits, G, cap, off, keys, codes_offset=0):
-    """Pack on the GPU; codes_offset > 0 places the code array that many
-    words into a larger buffer (a destination that is not 16-byte aligned)."""
+def _gpu_pack(x16, bits, G, cap, off, keys):
+    """Pack on the GPU into the records of a fresh destination cache; returns
+    the logical (codes, scale, zero) of that destination."""
     B, H, T, D = x16.shape
-    shp = kivi.layout_shapes(B, H, D, bits, bits, G, 1, cap)
-    n = "k" if keys else "v"
-    n_codes = int(np.prod(shp[f"{n}_codes"]))
-    buf = torch.zeros(n_codes + codes_offset, dtype=torch.int32, device="cuda")
-    codes = buf[codes_offset:].view(shp[f"{n}_codes"])
-    scale = torch.zeros(shp[f"{n}_scale"], dtype=torch.float32, device="cuda")
-    zero = torch.zeros(shp[f"{n}_zero"], dtype=torch.float32, device="cuda")
+    dst = kivi.Cache(B, H, D, bits, bits, G, G, cap)
+    dst.blocks.zero_()
     fn = kivi.kivi_pack_keys if keys else kivi.kivi_pack_values
-    fn(dev(x16), bits, G, codes, scale, zero, cap, off)
+    fn(dst, dev(x16), off)
     torch.cuda.synchronize()
-    return host(codes).view(np.uint32), host(scale), host(zero)
+    lg = logical(dst)
+    n = "k" if keys else "v"
+    return lg[f"{n}_codes"], lg[f"{n}_scale"], lg[f"{n}_zero"]
 
 
 def _same(a, b):
-    return np.array_equal(np.ascontiguousarray(a).view(np.uint32),
-                          np.ascontiguousarray(b).view(np.uint32))
+    a, b = np.ascontiguousarray(a), np.ascontiguousarray(b)
+    return a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
 @pytest.mark.parametrize("bits", [2, 4])
@@ -43,7 +40,7 @@ def test_pack_small(bits, G, D):
     B, H = 2, 3
     T = 5 * G
     x = (rng.standard_normal((B, H, T, D)) * rng.uniform(0.01, 30, (1, 1, 1, D))).astype(np.float16)
-    cap, off = T + 2 * G, G
+    cap, off = cap_for(T + 2 * G, G), G
     for keys in (True, False):
         got = _gpu_pack(x, bits, G, cap, off, keys)
         fn = oracle.pack_keys if keys else oracle.pack_values
@@ -56,7 +53,7 @@ def test_pack_small(bits, G, D):
             assert _same(g_[sl], r_[sl])
 
 
-@pytest.mark.parametrize("bits,G,D", [(2, 16, 256), (4, 16, 64), (2, 48, 96), (4, 8, 64),
+@pytest.mark.parametrize("bits,G,D", [(2, 16, 256), (4, 16, 64), (2, 16, 96), (4, 8, 64),
                                       (2, 128, 256), (4, 64, 256), (2, 32, 256), (4, 32, 256),
                                       (4, 16, 256)])
 def test_pack_other_shapes(bits, G, D):
@@ -67,16 +64,17 @@ def test_pack_other_shapes(bits, G, D):
 
 
 @pytest.mark.parametrize("bits", [2, 4])
-def test_pack_values_unaligned_destination(bits):
-    """A code array 4 bytes past a 16-byte boundary takes the per-row kernel;
-    the result is the same bit for bit."""
+def test_pack_values_off_the_tile_grid(bits):
+    """Values packed from a token that is not a multiple of 64 take the
+    per-row kernel (the tile kernel needs its 64 tokens in one record); the
+    result is the same bit for bit, across a record boundary."""
     rng = np.random.default_rng(9 + bits)
-    x = rng.standard_normal((2, 3, 70, 128)).astype(np.float16)
-    got = _gpu_pack(x, bits, 32, 128, 5, False, codes_offset=1)
-    ref = oracle.pack_values(b16(x), bits, 32, cap=128, offset=5)
-    assert _same(got[0][:, :, 5:75], ref[0][:, :, 5:75])
-    assert _same(got[1][..., 5:75], ref[1][..., 5:75])
-    assert _same(got[2][..., 5:75], ref[2][..., 5:75])
+    x = rng.standard_normal((2, 3, 170, 128)).astype(np.float16)
+    got = _gpu_pack(x, bits, 32, 256, 5, False)
+    ref = oracle.pack_values(b16(x), bits, 32, cap=256, offset=5)
+    assert _same(got[0][:, :, 5:175], ref[0][:, :, 5:175])
+    assert _same(got[1][..., 5:175], ref[1][..., 5:175])
+    assert _same(got[2][..., 5:175], ref[2][..., 5:175])
 
 
 def test_pack_values_ragged_rows():
@@ -119,44 +117,55 @@ def _edge_tensor(rng, T, D):
 def test_pack_edge_values(bits):
     x = _edge_tensor(np.random.default_rng(1), 64, 128)
     for keys in (True, False):
-        got = _gpu_pack(x, bits, 32, 64, 0, keys)
-        ref = (oracle.pack_keys if keys else oracle.pack_values)(b16(x), bits, 32)
-        for g_, r_ in zip(got, ref):
-            assert _same(g_, r_)
-            assert not np.isnan(g_.view(np.float32)).any() if g_.dtype == np.float32 else True
+        got = _gpu_pack(x, bits, 32, 128, 0, keys)
+        ref = (oracle.pack_keys if keys else oracle.pack_values)(b16(x), bits, 32, cap=128)
+        sls = [np.s_[:, :, :2]] * 3 if keys else [np.s_[:, :, :64], np.s_[..., :64], np.s_[..., :64]]
+        for g_, r_, sl in zip(got, ref, sls):
+            assert _same(g_[sl], r_[sl])
+            if g_.dtype == np.float32:
+                assert not np.isnan(g_[sl]).any()
 
 
 @pytest.mark.parametrize("index", [4, 5])
 def test_pack_full_prefill(index):
     """The full prefill of the 32k and 128k workloads on the GPU; the oracle
-    checks every byte of three sampled (batch, head) slabs."""
+    packs every (batch, head) slab (in parallel) and checks every byte."""
     w = synth.WORKLOADS[index]
     inp = synth.make_inputs(w)
     cap = w.T0
     for keys in (True, False):
         x = inp["k0"] if keys else inp["v0"]
-        say(f"pack {'keys' if keys else 'values'} {w.name} T={w.T0}")
+        say(f"pack {'keys' if keys else 'values'} {w.name} T={w.T0}, all {w.B * w.Hkv} slabs")
         got = _gpu_pack(x, w.k_bits, w.G, cap, 0, keys)
-        for b, h in {(0, 0), (w.B - 1, w.Hkv - 1), (w.B // 2, w.Hkv // 2)}:
-            fn = oracle.pack_keys if keys else oracle.pack_values
+        fn = oracle.pack_keys if keys else oracle.pack_values
+
+        def one(bh):
+            b, h = bh
             ref = fn(b16(x[b:b + 1, h:h + 1]), w.k_bits, w.G, cap=cap)
             for g_, r_ in zip(got, ref):
                 assert _same(g_[b:b + 1, h:h + 1], r_), (keys, b, h)
 
+        list(pool().map(one, [(b, h) for b in range(w.B) for h in range(w.Hkv)]))
+
 
 def test_pack_most_slabs():
     """65535 slabs (batch x heads), the most a pack call accepts: every slab
-    is one workgroup row of the launch grid.  Three sampled slabs against the
-    oracle, bit for bit (one slab more is rejected on the host, which the
-    ABI tests check)."""
+    is one workgroup row of the launch grid.  The oracle packs every slab (in
+    chunks of batch rows, in parallel) and checks every byte (one slab more
+    is rejected on the host, which the ABI tests check)."""
     rng = np.random.default_rng(65535)
     B, H, T, D, G, bits = 65535, 1, 32, 64, 32, 2
     x = rng.standard_normal((B, H, T, D)).astype(np.float16)
     say(f"pack {B} slabs of {T} tokens")
     for keys in (True, False):
-        got = _gpu_pack(x, bits, G, T, 0, keys)
+        got = _gpu_pack(x, bits, G, 128, 0, keys)
         fn = oracle.pack_keys if keys else oracle.pack_values
-        for b in (0, B // 2 + 7, B - 1):
-            ref = fn(b16(x[b:b + 1]), bits, G, cap=T, offset=0)
-            for g_, r_ in zip(got, ref):
-                assert _same(g_[b:b + 1], r_), (keys, b)
+        sls = [np.s_[:, :, :1]] * 3 if keys else [np.s_[:, :, :T], np.s_[..., :T], np.s_[..., :T]]
+
+        def rows(b0, keys=keys, got=got, fn=fn, sls=sls):
+            b1 = min(B, b0 + 4096)
+            ref = fn(b16(x[b0:b1]), bits, G, cap=128)
+            for g_, r_, sl in zip(got, ref, sls):
+                assert _same(g_[b0:b1][sl], r_[sl]), (keys, b0)
+
+        list(pool().map(rows, range(0, B, 4096)))

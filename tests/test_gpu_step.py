@@ -14,7 +14,8 @@ import torch
 
 import oracle
 from decode_attention_pack_amd import kivi, synth
-from tests.gpu_util import assert_close, b16, compare_slab, dev, host, say
+from tests.gpu_util import (assert_close, b16, cap_for, check_every_slab, compare_slab, dev,
+                            gpu_cache, host, logical, oracle_all_slabs, pool, say)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -41,7 +42,7 @@ def _steps(rep, R, T0, n_steps, masked, kb=2, vb=2, B=2, H=2, D=128, G=32, seed=
            zeros=False):
     rng = np.random.default_rng(seed + 7 * rep + R + T0)
     t_end = T0 + n_steps
-    cap = ((t_end + R - 1) // R) * R
+    cap = cap_for(t_end, R)
     scale = rng.uniform(0.5, 15, (1, H, 1, D))
     K = (rng.standard_normal((B, H, t_end, D)) * scale).astype(np.float16)
     V = rng.standard_normal((B, H, t_end, D)).astype(np.float16)
@@ -113,7 +114,7 @@ def test_decode_step_equals_append_then_attend():
     rounding-order differences."""
     rng = np.random.default_rng(11)
     B, H, D, R, rep, T0, n = 2, 4, 128, 128, 4, 1000, 140
-    cap = ((T0 + n + R - 1) // R) * R
+    cap = cap_for(T0 + n, R)
     K = rng.standard_normal((B, H, T0 + n, D)).astype(np.float16)
     V = rng.standard_normal((B, H, T0 + n, D)).astype(np.float16)
     a = kivi.Cache(B, H, D, 2, 2, 32, R, cap)
@@ -130,8 +131,9 @@ def test_decode_step_equals_append_then_attend():
         np.testing.assert_allclose(fa, fu, atol=1e-4, rtol=1e-4, err_msg=f"t={t + 1}")
     torch.cuda.synchronize()
     assert a.n_tokens == u.n_tokens == T0 + n
+    la, lu = logical(a), logical(u)
     for name in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero"):
-        ga, gu = host(getattr(a, name)), host(getattr(u, name))
+        ga, gu = la[name], lu[name]
         if name.startswith("k"):
             n_kq = a.n_tokens - a.n_tokens % R
             sl = (slice(None), slice(None), slice(0, n_kq // 32))
@@ -139,15 +141,17 @@ def test_decode_step_equals_append_then_attend():
             sl = (slice(None), slice(None), slice(0, a.n_tokens - R))
         else:
             sl = (slice(None), slice(None), slice(None), slice(0, a.n_tokens - R))
-        assert np.array_equal(ga[sl].view(np.uint32), gu[sl].view(np.uint32)), name
+        assert np.array_equal(np.ascontiguousarray(ga[sl]).view(np.uint8),
+                              np.ascontiguousarray(gu[sl]).view(np.uint8)), name
 
 
 def test_decode_step_rejects_full_cache_and_small_workspace():
     rng = np.random.default_rng(3)
     B, H, D, R = 1, 1, 128, 32
-    g = kivi.Cache(B, H, D, 2, 2, 32, R, R)
-    x = rng.standard_normal((B, H, R, D)).astype(np.float16)
-    kivi.kivi_append(g, dev(x), dev(x))
+    g = kivi.Cache(B, H, D, 2, 2, 32, R, 128)
+    full = rng.standard_normal((B, H, 128, D)).astype(np.float16)
+    kivi.kivi_append(g, dev(full), dev(full))
+    x = full[:, :, :R]
     k1 = dev(x[:, :, :1])
     q = dev(rng.standard_normal((B, H, D)).astype(np.float16))
     with pytest.raises(kivi.KiviError):
@@ -164,84 +168,67 @@ def test_decode_step_rejects_full_cache_and_small_workspace():
 def test_decode_step_full_workload(index):
     """Two fused steps on the full tiny, 32k GQA and 128k single-stream
     workloads, in the configuration the benchmark times; the oracle rebuilds
-    up to three sampled slabs alone."""
-    w = synth.WORKLOADS[index]
-    inp = synth.make_inputs(w.replace(steps=2))
-    g = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
+    every slab and checks every output and, after the second step, every
+    packed store."""
+    w = synth.WORKLOADS[index].replace(steps=2)
+    inp = synth.make_inputs(w)
+    g = gpu_cache(w)
     say(f"{w.name}: prefill {w.T0} + 2 fused steps")
     kivi.kivi_append(g, dev(inp["k0"]), dev(inp["v0"]))
-    rep = w.Hq // w.Hkv
     outs = []
     for s in range(2):
         outs.append(host(kivi.kivi_decode_step(g, dev(inp["k_steps"][s]), dev(inp["v_steps"][s]),
                                                dev(inp["q_steps"][s]))))
-    for b, h in sorted({(0, 0), (w.B - 1, w.Hkv - 1), (w.B // 2, min(4, w.Hkv - 1))}):
-        o = oracle.Cache(1, 1, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
-        o.append(b16(inp["k0"][b:b + 1, h:h + 1]), b16(inp["v0"][b:b + 1, h:h + 1]))
-        for s in range(2):
-            o.append(b16(inp["k_steps"][s][b:b + 1, h:h + 1]),
-                     b16(inp["v_steps"][s][b:b + 1, h:h + 1]))
-            ref = o.decode_attn(b16(inp["q_steps"][s][b:b + 1, h * rep:(h + 1) * rep]))[0]
-            assert_close(outs[s][b, h * rep:(h + 1) * rep], ref, f"{w.name} step {s} b{b} kv{h}")
-        compare_slab(g, b, h, o, 0, 0)
+    orc = oracle_all_slabs(w, inp, n_steps=0)
+    _append_step(orc, inp, 0)
+    check_every_slab(w, g, orc, {"step 0": outs[0]}, inp["q_steps"][0], stores=False)
+    _append_step(orc, inp, 1)
+    check_every_slab(w, g, orc, {"step 1": outs[1]}, inp["q_steps"][1])
+
+
+def _append_step(orc, inp, step):
+    """Append token `step` of the workload to every slab's oracle cache."""
+    def one(bh):
+        b, h = bh
+        orc[bh].append(b16(inp["k_steps"][step][b:b + 1, h:h + 1]),
+                       b16(inp["v_steps"][step][b:b + 1, h:h + 1]))
+    list(pool().map(one, sorted(orc)))
+
+
+def _fused_sequence(w, store_steps):
+    """Prefill, then w.steps calls of kivi_decode_step; after every step the
+    oracle advances every slab and checks every output, and at the steps in
+    store_steps every packed store and window bit for bit."""
+    inp = synth.make_inputs(w)
+    g = gpu_cache(w)
+    say(f"{w.name}: prefill {w.T0} + {w.steps} fused steps")
+    kivi.kivi_append(g, dev(inp["k0"]), dev(inp["v0"]))
+    orc = oracle_all_slabs(w, inp, n_steps=0)
+    ws = g.new_workspace(w.Hq)
+    for step in range(w.steps):
+        q = inp["q_steps"][step]
+        out = host(kivi.kivi_decode_step(g, dev(inp["k_steps"][step]), dev(inp["v_steps"][step]),
+                                         dev(q), workspace=ws))
+        _append_step(orc, inp, step)
+        check_every_slab(w, g, orc, {f"step {step} t={g.n_tokens}": out}, q,
+                         stores=step in store_steps)
 
 
 def test_decode_step_llama2_sequence():
     """The Llama-2-7B-shaped workload as fused steps: 4064-token prefill, then
     64 calls of kivi_decode_step.  Step 32 reaches t = 4096, so its launch
-    quantizes a key block and every step pops a value.  Three sampled (batch,
-    head) slabs are checked bit for bit after every step, and their attention
-    against the oracle."""
+    quantizes a key block and every step pops a value.  Every slab's output
+    after every step; every packed store and window at steps 0, 31, 32, 33,
+    every 8th and the last."""
     w = synth.WORKLOADS[2]
-    inp = synth.make_inputs(w)
-    g = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
-    say(f"{w.name}: prefill {w.T0} + {w.steps} fused steps")
-    kivi.kivi_append(g, dev(inp["k0"]), dev(inp["v0"]))
-    slabs = [(0, 0), (w.B - 1, w.Hkv - 1), (3, 17)]
-    orc = {}
-    for b, h in slabs:
-        o = oracle.Cache(1, 1, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
-        o.append(b16(inp["k0"][b:b + 1, h:h + 1]), b16(inp["v0"][b:b + 1, h:h + 1]))
-        orc[(b, h)] = o
-    ws = g.new_workspace(w.Hq)
-    for step in range(w.steps):
-        q = inp["q_steps"][step]
-        out = host(kivi.kivi_decode_step(g, dev(inp["k_steps"][step]), dev(inp["v_steps"][step]),
-                                         dev(q), workspace=ws))
-        for (b, h), o in orc.items():
-            o.append(b16(inp["k_steps"][step][b:b + 1, h:h + 1]),
-                     b16(inp["v_steps"][step][b:b + 1, h:h + 1]))
-            compare_slab(g, b, h, o)
-            ref = o.decode_attn(b16(q[b:b + 1, h:h + 1]))
-            assert_close(out[b, h], ref[0, 0], f"step {step} t={g.n_tokens} b{b} h{h}")
+    _fused_sequence(w, {0, 31, 32, 33, w.steps - 1} | set(range(7, w.steps, 8)))
 
 
 def test_decode_step_32k_key_block():
     """The 32k GQA workload's shape from 8 tokens before a key-block boundary:
     ten fused steps, the eighth of which completes the block (t = 33024) and
-    quantizes it inside the launch.  Three sampled slabs bit for bit after
-    every step, and their attention against the oracle."""
+    quantizes it inside the launch.  Every slab's output and packed store
+    after every step."""
     w = synth.WORKLOADS[4].replace(T0=33024 - 8, steps=10)
     assert (w.T0 + 8) % w.R == 0
-    inp = synth.make_inputs(w)
-    g = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
-    say(f"{w.name}: prefill {w.T0} + {w.steps} fused steps across t = {w.T0 + 8}")
-    kivi.kivi_append(g, dev(inp["k0"]), dev(inp["v0"]))
-    rep = w.Hq // w.Hkv
-    slabs = [(0, 0), (w.B - 1, w.Hkv - 1), (2, 5)]
-    orc = {}
-    for b, h in slabs:
-        o = oracle.Cache(1, 1, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
-        o.append(b16(inp["k0"][b:b + 1, h:h + 1]), b16(inp["v0"][b:b + 1, h:h + 1]))
-        orc[(b, h)] = o
-    ws = g.new_workspace(w.Hq)
-    for step in range(w.steps):
-        q = inp["q_steps"][step]
-        out = host(kivi.kivi_decode_step(g, dev(inp["k_steps"][step]), dev(inp["v_steps"][step]),
-                                         dev(q), workspace=ws))
-        for (b, h), o in orc.items():
-            o.append(b16(inp["k_steps"][step][b:b + 1, h:h + 1]),
-                     b16(inp["v_steps"][step][b:b + 1, h:h + 1]))
-            compare_slab(g, b, h, o)
-            ref = o.decode_attn(b16(q[b:b + 1, h * rep:(h + 1) * rep]))[0]
-            assert_close(out[b, h * rep:(h + 1) * rep], ref, f"step {step} t={g.n_tokens} b{b} kv{h}")
+    _fused_sequence(w, set(range(w.steps)))
