@@ -10,6 +10,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "../../include/kivi.h"
@@ -369,10 +370,43 @@ namespace {
 // (the caller has checked that the matrix kernel takes the shape, and the
 // capacity) and attends over c->n_tokens + 1 tokens; the caller advances
 // n_tokens on success.
+// Partial slots of the no-allocation entry point: one array per GPU, held
+// from the first load of the library until the process ends.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of this GPU's `scratch`, looked up once per device with
+// that device current.  The array's name in host code is a host-side
+// stand-in, never a device address.
+int scratch_address(void **out, const char *who) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex m;
+  static void *ptrs[kMaxDevices] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, who);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: device %d outside [0, %d)", who, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(m);
+  if (!ptrs[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(KIVI_ERR_HIP, "%s: address of the scratch array: %s", who,
+                  hipGetErrorString(e));
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return KIVI_OK;
+}
+
+// With use_scratch, the partials go to this GPU's scratch array (workspace
+// and workspace_bytes are ignored) and the call fails with
+// KIVI_ERR_WORKSPACE when this call's plan needs more than kScratchBytes.
 int decode_call(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, const float *mask,
                 float *out, void *workspace, size_t workspace_bytes, int32_t tokens_per_split,
                 int32_t path, void *stream, const void *k_new, const void *v_new,
-                const char *who) {
+                const char *who, bool use_scratch = false) {
   int rc = check_cache(c, who);
   if (rc) return rc;
   if (n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0)
@@ -384,10 +418,13 @@ int decode_call(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, cons
                 who, tokens_per_split);
   if (path < KIVI_PATH_AUTO || path > KIVI_PATH_VECTOR)
     return fail(KIVI_ERR_INVALID_ARG, "%s: unknown path %d", who, path);
-  const size_t need = kivi_decode_attn_workspace_bytes_ex(c, n_q_heads, tokens_per_split, path);
-  if (!workspace || workspace_bytes < need)
-    return fail(KIVI_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes,
-                need);
+  if (!use_scratch) {
+    const size_t need =
+        kivi_decode_attn_workspace_bytes_ex(c, n_q_heads, tokens_per_split, path);
+    if (!workspace || workspace_bytes < need)
+      return fail(KIVI_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who,
+                  workspace_bytes, need);
+  }
 
   kivi::DecodeArgs a{};
   a.L = layout_of(c);
@@ -426,6 +463,20 @@ int decode_call(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, cons
   if (p.S_total > max_slots(c, tokens_per_split))
     return fail(KIVI_ERR_WORKSPACE, "%s: internal split plan exceeds the workspace bound", who);
   a.S_total = p.S_total;
+  if (use_scratch) {
+    // every slot the combine reads is written by this call: nothing in the
+    // array must start at zero
+    const size_t need =
+        (size_t)c->batch * n_q_heads * p.S_total * (c->head_dim + 4) * sizeof(float);
+    if (need > kScratchBytes)
+      return fail(KIVI_ERR_WORKSPACE,
+                  "%s: %zu bytes of partial results needed, the scratch array holds %zu", who,
+                  need, kScratchBytes);
+    void *sp = nullptr;
+    rc = scratch_address(&sp, who);
+    if (rc) return rc;
+    a.part = (float *)sp;
+  }
   hipStream_t s = (hipStream_t)stream;
   if (p.matrix)
     rc = hip_status(kivi::launch_decode_matrix(a, p.n_main, p.n_groups_matrix, s),
@@ -451,6 +502,12 @@ int kivi_decode_attn_ex(const kivi_cache *c, const void *q_fp16, int32_t n_q_hea
                         int32_t tokens_per_split, int32_t path, void *stream) {
   return decode_call(c, q_fp16, n_q_heads, mask, out, workspace, workspace_bytes,
                      tokens_per_split, path, stream, nullptr, nullptr, "kivi_decode_attn");
+}
+
+int kivi_decode_attn_noalloc(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads,
+                             const float *mask, float *out, void *stream) {
+  return decode_call(c, q_fp16, n_q_heads, mask, out, nullptr, 0, 0, KIVI_PATH_AUTO, stream,
+                     nullptr, nullptr, "kivi_decode_attn_noalloc", true);
 }
 
 int kivi_decode_attn(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, const float *mask,

@@ -24,8 +24,8 @@ KIVI_PATH_AUTO, KIVI_PATH_GENERIC, KIVI_PATH_MATRIX, KIVI_PATH_VECTOR = 0, 1, 2,
 
 EXPORTED = ("kivi_record_bytes", "kivi_pack_keys", "kivi_pack_values", "kivi_append",
             "kivi_decode_attn", "kivi_decode_attn_ex", "kivi_decode_attn_workspace_bytes",
-            "kivi_decode_attn_workspace_bytes_ex", "kivi_decode_step", "kivi_status_string",
-            "kivi_last_error")
+            "kivi_decode_attn_workspace_bytes_ex", "kivi_decode_step", "kivi_decode_attn_noalloc",
+            "kivi_status_string", "kivi_last_error")
 TOKENS_PER_RECORD = 128
 
 
@@ -72,6 +72,8 @@ def lib():
     L.kivi_decode_attn_ex.restype = ctypes.c_int
     L.kivi_decode_step.argtypes = [ctypes.POINTER(CCache), P, P, P, i32, P, P, P, sz, P]
     L.kivi_decode_step.restype = ctypes.c_int
+    L.kivi_decode_attn_noalloc.argtypes = [ctypes.POINTER(CCache), P, i32, P, P, P]
+    L.kivi_decode_attn_noalloc.restype = ctypes.c_int
     L.kivi_decode_attn_workspace_bytes.argtypes = [ctypes.POINTER(CCache), i32]
     L.kivi_decode_attn_workspace_bytes.restype = sz
     L.kivi_decode_attn_workspace_bytes_ex.argtypes = [ctypes.POINTER(CCache), i32, i32, i32]
@@ -213,6 +215,20 @@ def kivi_decode_attn(cache: Cache, q, mask=None, out=None, workspace=None, token
     wp = _dev(workspace, torch.uint8, None, "workspace")
     _check(lib().kivi_decode_attn_ex(ctypes.byref(cache.c), qp, Hq, mp, op, wp,
                                      workspace.numel(), tokens_per_split, path, _stream(stream)))
+    return out
+
+
+def kivi_decode_attn_noalloc(cache: Cache, q, out, mask=None, stream=None):
+    """kivi_decode_attn into a caller-given out ([B][Hq][D] float32), with
+    the partial results in the library's own scratch array (no workspace, no
+    allocation in the library call); returns out."""
+    Hq = q.shape[1]
+    qp = _dev(q, torch.float16, (cache.B, Hq, cache.D), "q")
+    mp = None
+    if mask is not None:
+        mp = _dev(mask, torch.float32, (cache.B, cache.n_tokens), "mask")
+    op = _dev(out, torch.float32, (cache.B, Hq, cache.D), "out")
+    _check(lib().kivi_decode_attn_noalloc(ctypes.byref(cache.c), qp, Hq, mp, op, _stream(stream)))
     return out
 
 

@@ -157,6 +157,24 @@ int kivi_decode_attn(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads,
                      const float *mask, float *out, void *workspace,
                      size_t workspace_bytes, void *stream);
 
+/* kivi_decode_attn without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The partial results go to a scratch
+ * array of 16 MiB that the library holds on each GPU it runs on until the
+ * process ends; the call allocates nothing.  Arguments as for
+ * kivi_decode_attn (automatic plan).  KIVI_ERR_WORKSPACE, before anything
+ * runs, when this call's partials pass 16 MiB: (D + 4) x 4 bytes for each
+ * of batch x n_q_heads x S partial slots, where the matrix kernel plans S =
+ * 8 per workgroup (about one workgroup per CU, shared out among the batch x
+ * n_kv_heads slabs) plus one per 32 tokens of the window (at most 10 for R
+ * = 128).  Every call on a
+ * GPU shares its array: calls that overlap on one GPU (several streams or
+ * threads) race and must be serialized by the caller.  Each call writes
+ * every slot it reads, so no state carries over between calls. */
+int kivi_decode_attn_noalloc(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads,
+                             const float *mask, float *out, void *stream);
+
+
 /* Same as kivi_decode_attn with explicit tuning, for tests and sweeps:
  *   tokens_per_split  0 = automatic, else a positive multiple of 64.
  *   path              KIVI_PATH_AUTO (the matrix-core kernel where the shape

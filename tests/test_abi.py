@@ -153,6 +153,18 @@ def test_decode_rejects(L):
     assert L.kivi_decode_attn(None, FAKE, 4, None, FAKE, FAKE, n, None) == -1
 
 
+def test_decode_noalloc_rejects(L):
+    """The no-allocation entry point checks its arguments before it plans,
+    looks up its scratch array or launches anything."""
+    c = _cache(n_tokens=300)
+    assert L.kivi_decode_attn_noalloc(ctypes.byref(c), None, 4, None, FAKE, None) == -1
+    assert L.kivi_decode_attn_noalloc(ctypes.byref(c), FAKE, 4, None, None, None) == -1
+    assert L.kivi_decode_attn_noalloc(ctypes.byref(c), FAKE, 3, None, FAKE, None) == -1
+    assert L.kivi_decode_attn_noalloc(None, FAKE, 4, None, FAKE, None) == -1
+    assert L.kivi_decode_attn_noalloc(ctypes.byref(_cache(k_bits=3)), FAKE, 4, None, FAKE,
+                                      None) == -1
+
+
 @pytest.mark.parametrize("field", ["blocks", "k_res", "v_res"])
 def test_misaligned_cache_rejected_on_every_path(L, field):
     """A cache array that is not 16-byte aligned is rejected before any
