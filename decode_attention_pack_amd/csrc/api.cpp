@@ -173,8 +173,8 @@ Plan make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
       groups = max64(1, ceil_div(p.n_main, tps));
     }
     p.n_groups_matrix = (int)groups;
-    // one partial slot per wave, then one per window chunk
-    p.S_total = (int)(groups * waves + p.n_window);
+    // one partial slot per workgroup, then one per window chunk
+    p.S_total = (int)(groups + p.n_window);
     return p;
   }
   p.vector = (path == KIVI_PATH_AUTO || path == KIVI_PATH_VECTOR) &&

@@ -333,12 +333,13 @@ struct BlockShare {
 
 // Matrix-core role: blocks of the workgroup's share (tokens whose key and
 // value are both quantized, 128 per block), starting with block `first` and
-// continuing with the blocks the wave draws, accumulated into the partial
-// in slot `slot`.
+// continuing with the blocks the wave draws, accumulated into one partial
+// per query head, left in the wave's probability buffer: row h holds acc[128]
+// of head h, then m (natural-log units) and l.
 template <int NREP, bool MASKED>
 __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare &sh,
-                                           int64_t first, int slot, int hk, int b,
-                                           const Lds &L, KStage *__restrict__ kbuf,
+                                           int64_t first, int hk, int b, const Lds &L,
+                                           KStage *__restrict__ kbuf,
                                            VStage *__restrict__ vbuf) {
   static_assert(NREP == 1 || NREP == 2 || NREP == 4, "query heads per KV head");
   constexpr int GA = 16 / NREP;       // key groups per A operand
@@ -349,11 +350,8 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
   const int kg = lane >> 4;
   const int64_t bh = (int64_t)b * a.H + hk;
   if (first >= sh.nb) {
-    // no block for this wave: an empty partial
-    if (lane < NREP) {
-      float *dst = a.part + (((int64_t)b * a.Hq + hk * NREP + lane) * a.S_total + slot) * (kD + 4);
-      *(float2 *)(dst + kD) = make_float2(-INFINITY, 0.0f);
-    }
+    // no block for this wave: an empty partial (m = -inf)
+    if (lane < NREP) *(float2 *)&L.p[lane][kD] = make_float2(-INFINITY, 0.0f);
     return;
   }
 
@@ -606,27 +604,22 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
   }
   block(std::false_type{}, 0);
 
-  // ---- write the partial (acc[128], m, l) of each query head
+  // ---- the wave's partial (acc[128], m, l) of each query head, into its
+  // probability buffer (rows of kPRow floats), for the workgroup's merge
   zt = group_sum(zt);
   wave_lds_sync();
   if (kg == 0) L.bias[i] = zt;
   const float l_head = row_sum(l_run);
   wave_lds_sync();
-  const int slot_stride = kD + 4;
   if (v_valid) {
     const f4 z4 = *(const f4 *)(L.bias + 4 * kg);
-    float *dst = a.part + (((int64_t)b * a.Hq + hk * NREP + kg) * a.S_total + slot) * slot_stride;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      *(float2 *)(dst + 32 * g + 2 * i) =
-          make_float2(dv[g][0][g] + z4[g], dv[g][1][g] + z4[g]);
-    }
+    for (int g = 0; g < 4; ++g)
+      *(float2 *)&L.p[kg][32 * g + 2 * i] = make_float2(dv[g][0][g] + z4[g], dv[g][1][g] + z4[g]);
   }
-  if (k_valid && i == 0) {
-    float *dst = a.part + (((int64_t)b * a.Hq + hk * NREP + h_s) * a.S_total + slot) * slot_stride;
-    *(float2 *)(dst + kD) = make_float2(m_run == -INFINITY ? -INFINITY : m_run * 0.6931471805599453f,
-                                        l_head);
-  }
+  if (k_valid && i == 0)
+    *(float2 *)&L.p[h_s][kD] =
+        make_float2(m_run == -INFINITY ? -INFINITY : m_run * 0.6931471805599453f, l_head);
 }
 
 // Window role: tokens [Ta, Tb) = [n_main + 32 chunk, min(t, n_main + 32 chunk + 32))
@@ -910,7 +903,8 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
 // [s nblk / n_groups, (s + 1) nblk / n_groups) and window chunks s, s +
 // n_groups, ...; its waves draw the chunks first, then the blocks, from the
 // counter in LDS, so waves that run faster take more of them.  Partial
-// slots: s W + w for wave w's blocks, n_groups W + x for window chunk x.
+// slots: s for the workgroup's blocks (its waves' partials merged in LDS),
+// n_groups + x for window chunk x.
 // The masked variant holds the block's mask in registers as well; it may
 // use more than half the register file rather than spill, since a spill
 // reload inside the block loop would wait for every DMA in flight.
@@ -951,11 +945,40 @@ __global__ void __launch_bounds__(MASKED ? 256 : 512)
   int item = draw_item(&sm_ctr, lane);
   while (item < sh.n_skip) {
     const int x = (int)s + item * n_groups;
-    window_role<NREP, MASKED>(a, n_main, x, n_groups * W + x, hk, b, L);
+    window_role<NREP, MASKED>(a, n_main, x, n_groups + x, hk, b, L);
     wave_lds_sync();   // the LDS reads of the chunk are done
     item = draw_item(&sm_ctr, lane);
   }
-  block_role<NREP, MASKED>(a, sh, item - sh.n_skip, (int)s * W + w, hk, b, L, &sm_k[w], &sm_v[w]);
+  block_role<NREP, MASKED>(a, sh, item - sh.n_skip, hk, b, L, &sm_k[w], &sm_v[w]);
+
+  // The W partials of the workgroup's waves, merged with the log-sum-exp
+  // rule into partial slot s of the slab: thread e takes channel e % 128 of
+  // head e / 128.  Partials with m = -inf (no block, or every score -inf)
+  // add nothing.
+  __syncthreads();
+  for (int e = threadIdx.x; e < NREP * kD; e += 64 * W) {
+    const int h = e / kD, c = e % kD;
+    float M = -INFINITY, Ls = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int v = 0; v < W; ++v) {
+      const float mv = sm_p[v][h][kD];
+      if (mv == -INFINITY) continue;
+      const float lv = sm_p[v][h][kD + 1], av = sm_p[v][h][c];
+      if (mv > M) {
+        const float f = __expf(M - mv);   // 0 while M is -inf
+        acc = fmaf(acc, f, av);
+        Ls = fmaf(Ls, f, lv);
+        M = mv;
+      } else {
+        const float f = __expf(mv - M);
+        acc = fmaf(av, f, acc);
+        Ls = fmaf(lv, f, Ls);
+      }
+    }
+    float *dst = a.part + (((int64_t)b * a.Hq + hk * NREP + h) * a.S_total + s) * (kD + 4);
+    dst[c] = acc;
+    if (c == 0) *(float2 *)(dst + kD) = make_float2(M, Ls);
+  }
 }
 
 bool decode_matrix_supported(const DecodeArgs &a) {
@@ -1003,8 +1026,7 @@ hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int n_group
     if (a.t % a.R == 0 && n_main > a.t - a.R) return hipErrorInvalidValue;
   }
   const int n_window = decode_matrix_window_chunks(a, n_main);
-  const int W = decode_matrix_waves(a);
-  if ((int64_t)n_groups * W + n_window > a.S_total) return hipErrorInvalidValue;
+  if ((int64_t)n_groups + n_window > a.S_total) return hipErrorInvalidValue;
   const int64_t n_wg = (int64_t)n_groups * a.H * a.B;
   if (n_wg > ((int64_t)1 << 25)) return hipErrorInvalidValue;   // 32-bit workgroup ids
   dim3 grid((unsigned)n_wg);

@@ -91,8 +91,8 @@ bool decode_matrix_supported(const DecodeArgs &a);
 int decode_matrix_window_chunks(const DecodeArgs &a, int64_t n_main);
 // One launch of n_groups workgroups per slab (n_groups * B * H in all); the
 // waves of a workgroup take window chunks of [n_main, t) and blocks of its
-// share of [0, n_main) from a counter in LDS.  Partial slots: one per wave
-// (n_groups * waves-per-group), then one per window chunk.
+// share of [0, n_main) from a counter in LDS.  Partial slots: one per
+// workgroup (its waves' blocks), then one per window chunk.
 int decode_matrix_waves(const DecodeArgs &a);
 hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int n_groups,
                                 hipStream_t s);

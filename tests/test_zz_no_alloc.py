@@ -50,14 +50,15 @@ def test_noalloc_with_mask():
 
 
 def test_noalloc_rejects_partials_past_the_scratch():
-    """128 x 32 query heads of partial slots pass 16 MiB: rejected on the
-    host before any launch, the output left untouched."""
-    c = kivi.Cache(128, 8, 128, 2, 2, 32, 128, 384)
+    """256 batch rows x 32 query heads x 7 partial slots (one workgroup and
+    six window chunks per slab) pass 16 MiB: rejected on the host before any
+    launch, the output left untouched."""
+    c = kivi.Cache(256, 8, 128, 2, 2, 32, 128, 384)
     for a in c.arrays.values():
         a.zero_()
     c.c.n_tokens = 300
-    q = torch.zeros((128, 32, 128), dtype=torch.float16, device="cuda")
-    out = torch.full((128, 32, 128), 7.0, dtype=torch.float32, device="cuda")
+    q = torch.zeros((256, 32, 128), dtype=torch.float16, device="cuda")
+    out = torch.full((256, 32, 128), 7.0, dtype=torch.float32, device="cuda")
     with pytest.raises(kivi.KiviError) as e:
         kivi.kivi_decode_attn_noalloc(c, q, out)
     assert e.value.status == -3
