@@ -214,6 +214,8 @@ int64_t max_slots(const kivi_cache *c, int32_t tps_req) {
   return std::max(m, g) + 8 + n_window + 1;
 }
 
+
+
 }  // namespace
 
 extern "C" {
@@ -464,8 +466,8 @@ int decode_call(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, cons
     return fail(KIVI_ERR_WORKSPACE, "%s: internal split plan exceeds the workspace bound", who);
   a.S_total = p.S_total;
   if (use_scratch) {
-    // every slot the combine reads is written by this call: nothing in the
-    // array must start at zero
+    // every slot a merge reads is written by this call: nothing in the array
+    // must start at zero
     const size_t need =
         (size_t)c->batch * n_q_heads * p.S_total * (c->head_dim + 4) * sizeof(float);
     if (need > kScratchBytes)
@@ -488,8 +490,9 @@ int decode_call(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, cons
     rc = hip_status(kivi::launch_decode_generic(a, 0, p.tps_generic, p.n_split_generic, 0, s),
                     "kivi_decode_attn (scalar)");
   if (rc) return rc;
-  // a single vector-kernel split writes the output itself
-  if (p.vector && p.n_split_generic == 1) return KIVI_OK;
+  // a matrix-kernel slab with one workgroup, and a single vector-kernel
+  // split, write the output themselves
+  if ((p.matrix && p.n_groups_matrix == 1) || (p.vector && p.n_split_generic == 1)) return KIVI_OK;
   return hip_status(kivi::launch_combine(a, s), "kivi_decode_attn (combine)");
 }
 

@@ -904,7 +904,8 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
 // n_groups, ...; its waves draw the chunks first, then the blocks, from the
 // counter in LDS, so waves that run faster take more of them.  Partial
 // slots: s for the workgroup's blocks (its waves' partials merged in LDS),
-// n_groups + x for window chunk x.
+// n_groups + x for window chunk x.  A slab with a single workgroup merges
+// them into out in the same launch.
 // The masked variant holds the block's mask in registers as well; it may
 // use more than half the register file rather than spill, since a spill
 // reload inside the block loop would wait for every DMA in flight.
@@ -978,6 +979,50 @@ __global__ void __launch_bounds__(MASKED ? 256 : 512)
     float *dst = a.part + (((int64_t)b * a.Hq + hk * NREP + h) * a.S_total + s) * (kD + 4);
     dst[c] = acc;
     if (c == 0) *(float2 *)(dst + kD) = make_float2(M, Ls);
+  }
+
+  // A slab with one workgroup: it merges its slot and the window chunks'
+  // slots (all written by its own waves) into out itself, and no combine
+  // launch follows.  With more, the combine kernel merges the slots.
+  if (n_groups > 1) return;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's slot stores are done
+  __syncthreads();
+  const int S = a.S_total;
+  for (int e = threadIdx.x; e < NREP * kD; e += 64 * W) {
+    const int h = e / kD, c = e % kD;
+    const int64_t row = (int64_t)b * a.Hq + hk * NREP + h;
+    const float *pr = a.part + row * S * (int64_t)(kD + 4);
+    float M = -INFINITY, Ls = 0.0f, acc = 0.0f;
+    for (int s0 = 0; s0 < S; s0 += 16) {
+      float mv[16], lv[16], av[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const float *ps = pr + (int64_t)min(s0 + u, S - 1) * (kD + 4);   // in bounds
+        const float2 ml = *(const float2 *)(ps + kD);
+        mv[u] = s0 + u < S ? ml.x : -INFINITY;
+        lv[u] = ml.y;
+        av[u] = ps[c];
+      }
+      float cm = mv[0];
+#pragma unroll
+      for (int u = 1; u < 16; ++u) cm = fmaxf(cm, mv[u]);
+      if (cm == -INFINITY) continue;
+      if (cm > M) {
+        const float f = __expf(M - cm);   // 0 while M is -inf
+        acc *= f;
+        Ls *= f;
+        M = cm;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (mv[u] == -INFINITY) continue;
+        const float f = __expf(mv[u] - M);
+        acc = fmaf(av[u], f, acc);
+        Ls = fmaf(lv[u], f, Ls);
+      }
+    }
+    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+    a.out[row * kD + c] = acc * inv;
   }
 }
 
