@@ -182,8 +182,9 @@ Plan make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
   int64_t tps = tps_req;
   if (tps == 0 && p.vector) {
     // whole 4-group steps (one group per wave), about kVectorWorkgroups
-    // workgroups
-    const int64_t splits = max64(1, kVectorWorkgroups / units);
+    // workgroups (a workgroup per two query heads of a slab)
+    const int64_t vunits = units * (n_rep == 1 ? 1 : n_rep / 2);
+    const int64_t splits = max64(1, kVectorWorkgroups / vunits);
     tps = max64(1, ((t + splits - 1) / splits + kVectorStep - 1) / kVectorStep) * kVectorStep;
   } else if (tps == 0) {
     const int64_t gunits = units * head_chunks(n_rep);

@@ -1,7 +1,8 @@
 // decode_vector.hip -- vector-unit decode attention over the KIVI cache for
-// head_dim 128, group size 32, 2- or 4-bit key and value codes and one or
-// two query heads per KV head (the MHA and 2-way GQA shapes, which give the
-// matrix cores too little to do).
+// head_dim 128, group size 32, 2- or 4-bit key and value codes and one or an
+// even number of query heads per KV head (the MHA and 2-way GQA shapes, which
+// give the matrix cores too little to do, and the 4-bit GQA shapes the matrix
+// kernel does not take).
 //
 // Method source: web page "Literature audit -- Group 2 (KV-cache compression
 // primary sources)", section "1. KIVI -- kivi2024", list "Core algorithm
@@ -446,18 +447,25 @@ bool decode_vector_supported(const DecodeArgs &a) {
   const bool aligned = ((uintptr_t)a.L.blocks & 15) == 0 && ((uintptr_t)a.v_res & 15) == 0 &&
                        ((uintptr_t)a.k_res & 3) == 0 && ((uintptr_t)a.q & 3) == 0;
   return a.D == kVD && a.G == kVG && (a.kb == 2 || a.kb == 4) && (a.vb == 2 || a.vb == 4) &&
-         (a.n_rep == 1 || a.n_rep == 2) && a.R % kVG == 0 && a.cap % kVG == 0 &&
+         (a.n_rep == 1 || (a.n_rep % 2 == 0 && a.n_rep <= 64)) && a.R % kVG == 0 &&
+         a.cap % kVG == 0 &&
          a.cap < ((int64_t)1 << 26) && a.L.nrec * a.L.rec < ((int64_t)1 << 32) && aligned;
 }
 
+// One query head per KV head: NH = 1.  An even number: NH = 2, and n_rep / 2
+// workgroups per (split, slab), each for two of the heads (four heads in one
+// workgroup would not fit two waves per SIMD).
 template <int KB, int VB>
 static void launch_bits(const DecodeArgs &a, dim3 grid, int tps, int direct, hipStream_t s) {
-  if (a.n_rep == 1)
+  if (a.n_rep == 1) {
     hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 1>), grid, dim3(kVThreads), 0, s, a, tps, 1,
                        direct);
-  else
-    hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 2>), grid, dim3(kVThreads), 0, s, a, tps, 1,
-                       direct);
+  } else {
+    const int chunks = a.n_rep / 2;
+    grid.y *= chunks;
+    hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 2>), grid, dim3(kVThreads), 0, s, a, tps,
+                       chunks, direct);
+  }
 }
 
 // With a single split (n_splits == 1) the kernel writes the normalized

@@ -184,9 +184,10 @@ int kivi_decode_attn_noalloc(const kivi_cache *c, const void *q_fp16, int32_t n_
  *                     kernel: 2-bit codes, head_dim 128, G 32, 1, 2 or 4
  *                     query heads per KV head, 16-byte aligned q) or
  *                     KIVI_PATH_VECTOR (vector kernel: 2- or 4-bit codes,
- *                     head_dim 128, G 32, R a multiple of 32, 1 or 2 query
- *                     heads per KV head, capacity below 2^26 tokens and a
- *                     slab's records below 4 GB).  A
+ *                     head_dim 128, G 32, R a multiple of 32, 1 or an even
+ *                     number (at most 64) of query heads per KV head,
+ *                     capacity below 2^26 tokens and a slab's records below
+ *                     4 GB).  A
  *                     forced path the shape does not allow is rejected.
  * The workspace must hold kivi_decode_attn_workspace_bytes_ex() bytes. */
 enum { KIVI_PATH_AUTO = 0, KIVI_PATH_GENERIC = 1, KIVI_PATH_MATRIX = 2, KIVI_PATH_VECTOR = 3 };

@@ -19,8 +19,8 @@ PATHS = [kivi.KIVI_PATH_AUTO, kivi.KIVI_PATH_GENERIC]
 
 def vector_ok(D, kb, vb, G, R, rep, cap):
     """Shapes the vector kernel takes (the ABI rejects it elsewhere)."""
-    return (D == 128 and G == 32 and kb in (2, 4) and vb in (2, 4) and rep in (1, 2)
-            and R % 32 == 0 and cap % 32 == 0)
+    return (D == 128 and G == 32 and kb in (2, 4) and vb in (2, 4)
+            and (rep == 1 or (rep % 2 == 0 and rep <= 64)) and R % 32 == 0 and cap % 32 == 0)
 
 
 def paths_for(D, kb, vb, G, R, rep, cap):
@@ -57,6 +57,12 @@ def test_kivi4_b64():
 
 def test_llama3_gqa_32k():
     _run_workload(synth.WORKLOADS[4])
+
+
+def test_llama3_gqa_32k_4bit():
+    """The 32k GQA shape (4 query heads per KV head) with 4-bit keys and
+    values: the vector kernel in workgroups of two query heads."""
+    _run_workload(synth.WORKLOADS[4].replace(name="llama3-8b-gqa-32k-kivi4", k_bits=4, v_bits=4))
 
 
 def test_long_128k():
@@ -235,7 +241,7 @@ def test_vector_and_scalar_paths_agree_closely(kb, vb):
     different rounding order) stays within 2e-4 of the scalar kernel, ten
     times inside the oracle tolerance, over many splits and a ragged window."""
     rng = np.random.default_rng(41 + kb + 3 * vb)
-    for rep, t in ((1, 4001), (2, 2500)):
+    for rep, t in ((1, 4001), (2, 2500), (4, 1800)):
         g, o, q = _small_case(rng, 2, 3, rep, 128, kb, vb, 32, 128, t)
         for tps in (0, 64, 192, 8192):   # 8192: one split, output written directly
             v = host(kivi.kivi_decode_attn(g, dev(q), tokens_per_split=tps,
@@ -247,7 +253,7 @@ def test_vector_and_scalar_paths_agree_closely(kb, vb):
 
 def test_vector_path_rejects_other_shapes():
     rng = np.random.default_rng(5)
-    g, _, q = _small_case(rng, 1, 2, 4, 128, 2, 2, 32, 128, 300)
+    g, _, q = _small_case(rng, 1, 2, 3, 128, 2, 2, 32, 128, 300)   # an odd head count above 1
     with pytest.raises(kivi.KiviError):
         kivi.kivi_decode_attn(g, dev(q), path=kivi.KIVI_PATH_VECTOR)
 
