@@ -71,9 +71,18 @@ int check_cache(const kivi_cache *c, const char *who) {
     return fail(KIVI_ERR_INVALID_ARG,
                 "%s: capacity %lld must be a positive multiple of residual %d and of %d", who,
                 (long long)c->capacity, c->residual, kivi::kRecTokens);
-  if (c->n_tokens < 0 || c->n_tokens > c->capacity)
+  if (c->row_tokens) {
+    if (c->batch > kivi::kMaxRows)
+      return fail(KIVI_ERR_INVALID_ARG, "%s: a ragged batch holds at most %d rows (batch %d)", who,
+                  kivi::kMaxRows, c->batch);
+    for (int32_t b = 0; b < c->batch; ++b)
+      if (c->row_tokens[b] < 0 || c->row_tokens[b] > c->capacity)
+        return fail(KIVI_ERR_INVALID_ARG, "%s: row_tokens[%d] = %lld outside [0, capacity]", who,
+                    b, (long long)c->row_tokens[b]);
+  } else if (c->n_tokens < 0 || c->n_tokens > c->capacity) {
     return fail(KIVI_ERR_INVALID_ARG, "%s: n_tokens %lld outside [0, capacity]", who,
                 (long long)c->n_tokens);
+  }
   if (!c->blocks || !c->k_res || !c->v_res)
     return fail(KIVI_ERR_INVALID_ARG, "%s: a cache array pointer is NULL", who);
   if (((uintptr_t)c->blocks & 15) != 0 || ((uintptr_t)c->k_res & 15) != 0 ||
@@ -84,6 +93,51 @@ int check_cache(const kivi_cache *c, const char *who) {
 
 kivi::Layout layout_of(const kivi_cache *c) {
   return kivi::make_layout(c->blocks, c->head_dim, c->k_bits, c->v_bits, c->group, c->capacity);
+}
+
+// Token counts of the rows of a checked cache: per row (ragged) or n_tokens
+// for every row.
+struct Rows {
+  bool ragged = false;
+  int64_t t_max = 0, t_sum = 0;
+  kivi::RowCounts n{};
+};
+Rows rows_of(const kivi_cache *c) {
+  Rows r;
+  r.ragged = c->row_tokens != nullptr;
+  if (!r.ragged) {
+    r.t_max = c->n_tokens;
+    r.t_sum = c->n_tokens * c->batch;
+    return r;
+  }
+  for (int32_t b = 0; b < c->batch; ++b) {
+    const int64_t t = c->row_tokens[b];
+    r.n.n[b] = (int32_t)t;
+    r.t_max = t > r.t_max ? t : r.t_max;
+    r.t_sum += t;
+  }
+  return r;
+}
+
+// After a call that changed a ragged cache's counts: n_tokens = the longest row.
+void set_longest(kivi_cache *c) {
+  int64_t m = 0;
+  for (int32_t b = 0; b < c->batch; ++b) m = c->row_tokens[b] > m ? c->row_tokens[b] : m;
+  c->n_tokens = m;
+}
+
+// Row b of a cache alone, as a uniform cache of batch 1 holding t tokens.
+kivi_cache row_view(const kivi_cache *c, int32_t b, int64_t t) {
+  kivi_cache v = *c;
+  const size_t rb = kivi::make_layout(nullptr, c->head_dim, c->k_bits, c->v_bits, c->group, 0).rec;
+  const int64_t slabs = (int64_t)b * c->n_kv_heads;
+  v.batch = 1;
+  v.n_tokens = t;
+  v.row_tokens = nullptr;
+  v.blocks = c->blocks + slabs * (c->capacity / kivi::kRecTokens) * (int64_t)rb;
+  v.k_res = c->k_res + slabs * c->residual * c->head_dim;
+  v.v_res = c->v_res + slabs * c->residual * c->head_dim;
+  return v;
 }
 
 int check_pack(const kivi_cache *dst, const void *x, int64_t T, int64_t off, bool keys,
@@ -136,27 +190,96 @@ struct Plan {
   int tps_generic = 0;          // vector / scalar kernel (shapes the matrix kernel does not cover)
   int n_split_generic = 0;
   int S_total = 0;
+  bool combine = true;          // a combine launch follows
+  // ragged batch, matrix kernel: the workgroup shares (per KV head) and the
+  // slots each row's combine merges (0: the row's single workgroup wrote it)
+  int n_shares = 0;
+  kivi::MatrixRows mrows{};
+  kivi::RowCounts slots{};
 };
 
 int head_chunks(int n_rep) { return (n_rep + 7) / 8; }
 
 int64_t ceil_div(int64_t x, int64_t y) { return (x + y - 1) / y; }
 
-// Split plan.  Deterministic in (shape, n_tokens, options).
-Plan make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
-               const kivi::DecodeArgs &a) {
-  Plan p;
+// Matrix-kernel plan of a ragged batch: each row gets workgroups per KV head
+// in proportion to its work (blocks plus window chunks), at least one and at
+// most one per `waves` items, about one workgroup per CU in all; the rest go
+// one at a time to the row with the most work per workgroup.  With tps_req,
+// a workgroup per tps_req tokens of a row.
+int plan_matrix_rows(const kivi_cache *c, const Rows &r, int32_t tps_req, int waves, bool fused,
+                     Plan &p, const char *who) {
+  const int B = c->batch, R = c->residual;
+  int64_t work[kivi::kMaxRows], cap[kivi::kMaxRows], groups[kivi::kMaxRows];
+  int nwin[kivi::kMaxRows];
+  int64_t total = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t t = r.n.n[b] + (fused ? 1 : 0);
+    p.mrows.t[b] = (int32_t)t;
+    const kivi::RowSpan rs = kivi::row_span(t, R, fused);
+    const int64_t nm = kivi::matrix_main(rs, R);
+    nwin[b] = kivi::matrix_window_chunks(t, nm);
+    work[b] = nm / kMatrixBlock + nwin[b];
+    cap[b] = max64(1, ceil_div(work[b], waves));
+    total += work[b];
+    if (tps_req > 0) {
+      const int64_t tps = ceil_div(tps_req, kMatrixBlock) * kMatrixBlock;
+      groups[b] = max64(1, ceil_div(nm, tps));
+    }
+  }
+  int64_t used = 0;
+  if (tps_req == 0) {
+    const int64_t target = std::min<int64_t>(
+        kivi::kMaxRows, max64(B, (int64_t)device_cus() * (8 / waves) / c->n_kv_heads));
+    for (int b = 0; b < B; ++b) {
+      groups[b] = 1 + (total > 0 ? (target - B) * work[b] / total : 0);
+      groups[b] = std::min(groups[b], cap[b]);
+      used += groups[b];
+    }
+    while (used < target) {
+      int best = -1;
+      for (int b = 0; b < B; ++b)
+        if (groups[b] < cap[b] &&
+            (best < 0 || work[b] * groups[best] > work[best] * groups[b]))
+          best = b;
+      if (best < 0) break;
+      ++groups[best];
+      ++used;
+    }
+  } else {
+    for (int b = 0; b < B; ++b) used += groups[b];
+    if (used > kivi::kMaxRows)
+      return fail(KIVI_ERR_INVALID_ARG,
+                  "%s: tokens_per_split %d gives %lld workgroups per KV head for a ragged batch; "
+                  "at most %d", who, tps_req, (long long)used, kivi::kMaxRows);
+  }
+  int u = 0;
+  p.S_total = 1;
+  p.combine = false;
+  for (int b = 0; b < B; ++b) {
+    for (int64_t g = 0; g < groups[b]; ++g)
+      p.mrows.share[u++] = (uint32_t)b | ((uint32_t)g << 8) | ((uint32_t)groups[b] << 20);
+    const int S = (int)groups[b] + nwin[b];
+    p.S_total = std::max(p.S_total, S);
+    p.slots.n[b] = groups[b] > 1 ? S : 0;
+    p.combine = p.combine || groups[b] > 1;
+  }
+  p.n_shares = u;
+  return KIVI_OK;
+}
+
+// Split plan.  Deterministic in (shape, token counts, options).
+int make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
+              const kivi::DecodeArgs &a, const Rows &r, Plan &p, const char *who) {
   const int64_t t = a.t;
   const int n_rep = Hq / c->n_kv_heads;
   const int64_t units = (int64_t)c->batch * c->n_kv_heads;
   p.matrix = (path == KIVI_PATH_AUTO || path == KIVI_PATH_MATRIX) && t > 0 &&
              kivi::decode_matrix_supported(a);
+  if (p.matrix && r.ragged)
+    return plan_matrix_rows(c, r, tps_req, kivi::decode_matrix_waves(a), a.t_new >= 0, p, who);
   if (p.matrix) {
-    // whole blocks of quantized keys and values; in a fused step the value
-    // leaving the window (token t_new - R) is quantized by the window role, so
-    // the blocks stop before it
-    const int64_t n_lim = a.t_new >= a.R ? a.t_new - a.R : a.n_vq;
-    p.n_main = (n_lim / kMatrixBlock) * kMatrixBlock;
+    p.n_main = kivi::matrix_main(kivi::row_span(t, a.R, a.t_new >= 0), a.R);
     p.n_window = kivi::decode_matrix_window_chunks(a, p.n_main);
     const int64_t blocks = p.n_main / kMatrixBlock;
     const int waves = kivi::decode_matrix_waves(a);
@@ -175,27 +298,35 @@ Plan make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
     p.n_groups_matrix = (int)groups;
     // one partial slot per workgroup, then one per window chunk
     p.S_total = (int)(groups + p.n_window);
-    return p;
+    // a slab with a single workgroup writes its output itself
+    p.combine = groups > 1;
+    return KIVI_OK;
   }
   p.vector = (path == KIVI_PATH_AUTO || path == KIVI_PATH_VECTOR) &&
              kivi::decode_vector_supported(a);
+  // a ragged batch sizes its splits by the mean row; rows shorter than the
+  // longest leave their last splits empty
+  const int64_t t_eff = r.ragged ? ceil_div(r.t_sum, c->batch) : t;
   int64_t tps = tps_req;
   if (tps == 0 && p.vector) {
     // whole 4-group steps (one group per wave), about kVectorWorkgroups
     // workgroups (a workgroup per two query heads of a slab)
     const int64_t vunits = units * (n_rep == 1 ? 1 : n_rep / 2);
     const int64_t splits = max64(1, kVectorWorkgroups / vunits);
-    tps = max64(1, ((t + splits - 1) / splits + kVectorStep - 1) / kVectorStep) * kVectorStep;
+    tps = max64(1, ((t_eff + splits - 1) / splits + kVectorStep - 1) / kVectorStep) * kVectorStep;
   } else if (tps == 0) {
     const int64_t gunits = units * head_chunks(n_rep);
     const int64_t splits = max64(1, kTargetWorkgroups / gunits);
-    tps = ((t + splits - 1) / splits + kGenericMinSplit - 1) / kGenericMinSplit * kGenericMinSplit;
+    tps = ((t_eff + splits - 1) / splits + kGenericMinSplit - 1) / kGenericMinSplit *
+          kGenericMinSplit;
     tps = max64(tps, kGenericMinSplit);
   }
   p.tps_generic = (int)tps;
   p.n_split_generic = (int)max64(1, (t + tps - 1) / tps);
   p.S_total = p.n_split_generic;
-  return p;
+  // a single vector-kernel split writes the output itself
+  p.combine = !(p.vector && p.n_split_generic == 1);
+  return KIVI_OK;
 }
 
 // Upper bound on partial slots for any n_tokens <= capacity.
@@ -274,6 +405,49 @@ int kivi_pack_values(const kivi_cache *dst, const void *v_fp16, int64_t T,
                     "kivi_pack_values");
 }
 
+}  // extern "C"
+
+namespace {
+
+int append_uniform(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp16, int64_t n_new,
+                   void *stream);
+
+// kivi_append on a ragged batch: every row takes n_new tokens at its own
+// length.  A single token per row (the decode step) is one launch; longer
+// appends run row by row, each row alone as a cache of batch 1.
+int append_rows(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp16, int64_t n_new,
+                void *stream) {
+  const Rows r = rows_of(c);
+  if (r.t_max + n_new > c->capacity)
+    return fail(KIVI_ERR_CAPACITY, "kivi_append: a row of %lld + %lld tokens passes capacity %lld",
+                (long long)r.t_max, (long long)n_new, (long long)c->capacity);
+  int rc;
+  if (n_new == 1 && kivi::append_one_supported(c->head_dim, c->group, c->v_bits)) {
+    rc = hip_status(kivi::launch_append_one_rows((const uint16_t *)k_new_fp16,
+                                                 (const uint16_t *)v_new_fp16, c->k_res, c->v_res,
+                                                 (int64_t)c->batch * c->n_kv_heads,
+                                                 c->n_kv_heads, c->residual, r.n, layout_of(c),
+                                                 (hipStream_t)stream),
+                    "kivi_append (rows)");
+    if (rc) return rc;
+  } else {
+    const int64_t per_row = (int64_t)c->n_kv_heads * n_new * c->head_dim;   // fp16 elements
+    for (int32_t b = 0; b < c->batch; ++b) {
+      kivi_cache v = row_view(c, b, c->row_tokens[b]);
+      rc = append_uniform(&v, (const uint16_t *)k_new_fp16 + b * per_row,
+                          (const uint16_t *)v_new_fp16 + b * per_row, n_new, stream);
+      if (rc) return rc;
+    }
+  }
+  for (int32_t b = 0; b < c->batch; ++b) c->row_tokens[b] += n_new;
+  set_longest(c);
+  return KIVI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int kivi_append(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp16, int64_t n_new,
                 void *stream) {
   int rc = check_cache(c, "kivi_append");
@@ -281,9 +455,44 @@ int kivi_append(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp16, i
   if (n_new < 0) return fail(KIVI_ERR_INVALID_ARG, "kivi_append: n_new must be >= 0");
   if (n_new == 0) return KIVI_OK;
   if (!k_new_fp16 || !v_new_fp16) return fail(KIVI_ERR_INVALID_ARG, "kivi_append: NULL input");
+  if (c->row_tokens) return append_rows(c, k_new_fp16, v_new_fp16, n_new, stream);
   if (c->n_tokens + n_new > c->capacity)
     return fail(KIVI_ERR_CAPACITY, "kivi_append: %lld + %lld tokens pass capacity %lld",
                 (long long)c->n_tokens, (long long)n_new, (long long)c->capacity);
+  return append_uniform(c, k_new_fp16, v_new_fp16, n_new, stream);
+}
+
+int kivi_append_row(kivi_cache *c, int32_t b, const void *k_new_fp16, const void *v_new_fp16,
+                    int64_t n_new, void *stream) {
+  const char *who = "kivi_append_row";
+  int rc = check_cache(c, who);
+  if (rc) return rc;
+  if (!c->row_tokens)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: the cache has no row_tokens (not a ragged batch)", who);
+  if (b < 0 || b >= c->batch)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: row %d outside [0, %d)", who, b, c->batch);
+  if (n_new < 0) return fail(KIVI_ERR_INVALID_ARG, "%s: n_new must be >= 0", who);
+  if (n_new == 0) return KIVI_OK;
+  if (!k_new_fp16 || !v_new_fp16) return fail(KIVI_ERR_INVALID_ARG, "%s: NULL input", who);
+  if (c->row_tokens[b] + n_new > c->capacity)
+    return fail(KIVI_ERR_CAPACITY, "%s: %lld + %lld tokens pass capacity %lld", who,
+                (long long)c->row_tokens[b], (long long)n_new, (long long)c->capacity);
+  kivi_cache v = row_view(c, b, c->row_tokens[b]);
+  rc = append_uniform(&v, k_new_fp16, v_new_fp16, n_new, stream);
+  if (rc) return rc;
+  c->row_tokens[b] = v.n_tokens;
+  set_longest(c);
+  return KIVI_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// kivi_append on a checked uniform cache with room for the n_new > 0 tokens.
+int append_uniform(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp16, int64_t n_new,
+                   void *stream) {
+  int rc;
   hipStream_t s = (hipStream_t)stream;
   const kivi::Layout L = layout_of(c);
   const int64_t R = c->residual, G = c->group, D = c->head_dim;
@@ -348,6 +557,10 @@ int kivi_append(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp16, i
   c->n_tokens = t1;
   return KIVI_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t kivi_decode_attn_workspace_bytes_ex(const kivi_cache *c, int32_t n_q_heads,
                                            int32_t tokens_per_split, int32_t path) {
@@ -448,10 +661,13 @@ int decode_call(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, cons
   a.n_rep = n_q_heads / c->n_kv_heads;
   a.cap = c->capacity;
   const bool fused = k_new != nullptr;
-  a.t = c->n_tokens + (fused ? 1 : 0);
+  // a ragged batch: the kernels take each row's count from the launch's
+  // tables; a.t is the longest row (the mask's row stride)
+  const Rows r = rows_of(c);
+  a.t = r.t_max + (fused ? 1 : 0);
   a.k_new = (const uint16_t *)k_new;
   a.v_new = (const uint16_t *)v_new;
-  a.t_new = fused ? c->n_tokens : -1;
+  a.t_new = fused ? a.t - 1 : -1;
   a.n_kq = a.t - a.t % a.R;
   a.n_vq = max64(0, a.t - a.R);
   a.sm_scale = 1.0f / sqrtf((float)a.D);
@@ -460,7 +676,9 @@ int decode_call(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, cons
     return fail(KIVI_ERR_INVALID_ARG, "%s: the matrix-core kernel does not handle this shape", who);
   if (path == KIVI_PATH_VECTOR && !kivi::decode_vector_supported(a))
     return fail(KIVI_ERR_INVALID_ARG, "%s: the vector kernel does not handle this shape", who);
-  const Plan p = make_plan(c, n_q_heads, tokens_per_split, path, a);
+  Plan p;
+  rc = make_plan(c, n_q_heads, tokens_per_split, path, a, r, p, who);
+  if (rc) return rc;
   if (fused && !p.matrix)
     return fail(KIVI_ERR_INVALID_ARG, "%s: internal: fused step without the matrix kernel", who);
   if (p.S_total > max_slots(c, tokens_per_split))
@@ -481,20 +699,23 @@ int decode_call(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, cons
     a.part = (float *)sp;
   }
   hipStream_t s = (hipStream_t)stream;
-  if (p.matrix)
+  const kivi::RowCounts *rows = r.ragged ? &r.n : nullptr;
+  if (p.matrix && r.ragged)
+    rc = hip_status(kivi::launch_decode_matrix_rows(a, p.mrows, p.n_shares, s),
+                    "kivi_decode_attn (matrix)");
+  else if (p.matrix)
     rc = hip_status(kivi::launch_decode_matrix(a, p.n_main, p.n_groups_matrix, s),
                     "kivi_decode_attn (matrix)");
   else if (p.vector)
-    rc = hip_status(kivi::launch_decode_vector(a, p.tps_generic, p.n_split_generic, s),
+    rc = hip_status(kivi::launch_decode_vector(a, p.tps_generic, p.n_split_generic, s, rows),
                     "kivi_decode_attn (vector)");
   else
-    rc = hip_status(kivi::launch_decode_generic(a, 0, p.tps_generic, p.n_split_generic, 0, s),
-                    "kivi_decode_attn (scalar)");
-  if (rc) return rc;
-  // a matrix-kernel slab with one workgroup, and a single vector-kernel
-  // split, write the output themselves
-  if ((p.matrix && p.n_groups_matrix == 1) || (p.vector && p.n_split_generic == 1)) return KIVI_OK;
-  return hip_status(kivi::launch_combine(a, s), "kivi_decode_attn (combine)");
+    rc = hip_status(
+        kivi::launch_decode_generic(a, 0, p.tps_generic, p.n_split_generic, 0, s, rows),
+        "kivi_decode_attn (scalar)");
+  if (rc || !p.combine) return rc;
+  return hip_status(kivi::launch_combine(a, s, p.matrix && r.ragged ? &p.slots : nullptr),
+                    "kivi_decode_attn (combine)");
 }
 
 }  // namespace
@@ -531,7 +752,7 @@ int kivi_decode_step(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp
   if (n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0)
     return fail(KIVI_ERR_INVALID_ARG, "%s: n_q_heads %d must be a positive multiple of n_kv_heads %d",
                 who, n_q_heads, c->n_kv_heads);
-  if (c->n_tokens + 1 > c->capacity)
+  if (rows_of(c).t_max + 1 > c->capacity)
     return fail(KIVI_ERR_CAPACITY, "%s: the cache is full (%lld tokens)", who,
                 (long long)c->capacity);
   // the workspace is checked before anything runs, so that a failing call
@@ -564,7 +785,12 @@ int kivi_decode_step(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp
   rc = decode_call(c, q_fp16, n_q_heads, mask, out, workspace, workspace_bytes, 0, KIVI_PATH_AUTO,
                    stream, k_new_fp16, v_new_fp16, who);
   if (rc) return rc;
-  c->n_tokens += 1;
+  if (c->row_tokens) {
+    for (int32_t b = 0; b < c->batch; ++b) c->row_tokens[b] += 1;
+    set_longest(c);
+  } else {
+    c->n_tokens += 1;
+  }
   return KIVI_OK;
 }
 

@@ -39,10 +39,12 @@ __device__ __forceinline__ float wave_sum(float v) {
 // grid: (n_splits, H * head_chunks, B); block: 256.  NH (1, 2, 4 or 8) query
 // heads per workgroup: the smallest power of two covering the heads per KV
 // head, up to 8, so that MHA shapes do not carry 8 heads' worth of products.
-template <int NH>
+// A ragged batch (RAGGED): row b holds rows.n[b] tokens; a.t is the mask's
+// row stride.
+template <int NH, bool RAGGED>
 __global__ void __launch_bounds__(kThreads)
 decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int slot_base,
-                      int head_chunks) {
+                      int head_chunks, RowArg<RAGGED> rows) {
   __shared__ float q_s[NH][256];
   __shared__ float p_s[NH][kChunk];
   __shared__ float stat_s[NH][2];   // new m, alpha
@@ -58,9 +60,14 @@ decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int
   const int nh = min(NH, a.n_rep - hc * NH);
   const int D = a.D;
 
+  RowSpan rs;
+  if constexpr (RAGGED)
+    rs = row_span(rows.n[b], a.R, false);
+  else
+    rs = RowSpan{a.t, a.n_kq, a.n_vq, -1};
   int64_t s0 = tok_begin + (int64_t)split * tokens_per_split;
   int64_t s1 = s0 + tokens_per_split;
-  if (s1 > a.t) s1 = a.t;
+  if (s1 > rs.t) s1 = rs.t;
 
   for (int i = tid; i < NH * D; i += kThreads) {
     const int j = i / D, c = i % D;
@@ -96,7 +103,7 @@ decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int
       // key channel c of token tau as attention sees it: code * scale + zero
       // (fp32 multiply, then add) below n_kq, else the fp16 window row; the
       // per-token index arithmetic (group, word, bit offset) is done once
-      if (tau < a.n_kq) {
+      if (tau < rs.n_kq) {
         const int per = 32 / a.kb;
         const int words = a.G / per;
         const int64_t g = tau / a.G;
@@ -169,7 +176,7 @@ decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int
     const int64_t cend = (c0 + kChunk < s1) ? c0 + kChunk : s1;
     for (int64_t tv = c0 + par; tv < cend; tv += n_par) {
       float v;
-      if (tv < a.n_vq) {
+      if (tv < rs.n_vq) {
         const uint32_t code = (L.value_codes(bh, tv)[vword] >> vsh) & vmsk;
         v = __fadd_rn(__fmul_rn((float)code, *L.value_scale(bh, tv, vgrp)),
                       h2f(*L.value_zero(bh, tv, vgrp)));
@@ -225,17 +232,25 @@ __device__ __forceinline__ void lse_merge(float &m, float &l, float4 &o, float m
 // 8 of its slots at once; the 8 slot groups of a wave merge through lane
 // shuffles and the 4 waves through LDS.  A workgroup covers 32 channels, so
 // most rows need one round trip to memory.
-__global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
+// With RAGGED, row b merges its first slots.n[b] slots (the partial stride
+// stays S_total) and a row with none is skipped.
+template <bool RAGGED>
+__global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, RowArg<RAGGED> slots) {
   __shared__ float red_m[4][8];
   __shared__ float red_l[4][8];
   __shared__ float4 red_o[4][8];
   const int64_t row = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sg = wave * 8 + (lane >> 3), cq = lane & 7;
-  const int D = a.D, S = a.S_total, stride = D + 4;
+  int S = a.S_total;
+  if constexpr (RAGGED) {
+    S = slots.n[row / a.Hq];
+    if (S == 0) return;   // the whole workgroup: S is uniform
+  }
+  const int D = a.D, stride = D + 4;
   const int c = blockIdx.y * 32 + cq * 4;
   const bool c_ok = c < D;               // D is a multiple of 8
-  const float *p = a.part + row * S * (int64_t)stride;
+  const float *p = a.part + row * a.S_total * (int64_t)stride;
 
   float M = -INFINITY, L = 0.0f;
   float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -284,30 +299,49 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a) {
   }
 }
 
+template <bool RAGGED>
+static void launch_generic(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t tok_begin,
+                           int tps, int slot_base, int head_chunks, const RowArg<RAGGED> &rows) {
+  if (a.n_rep == 1)
+    hipLaunchKernelGGL((decode_generic_kernel<1, RAGGED>), grid, dim3(kThreads), 0, s, a,
+                       tok_begin, tps, slot_base, head_chunks, rows);
+  else if (a.n_rep == 2)
+    hipLaunchKernelGGL((decode_generic_kernel<2, RAGGED>), grid, dim3(kThreads), 0, s, a,
+                       tok_begin, tps, slot_base, head_chunks, rows);
+  else if (a.n_rep <= 4)
+    hipLaunchKernelGGL((decode_generic_kernel<4, RAGGED>), grid, dim3(kThreads), 0, s, a,
+                       tok_begin, tps, slot_base, head_chunks, rows);
+  else
+    hipLaunchKernelGGL((decode_generic_kernel<kHeads, RAGGED>), grid, dim3(kThreads), 0, s, a,
+                       tok_begin, tps, slot_base, head_chunks, rows);
+}
+
 hipError_t launch_decode_generic(const DecodeArgs &a, int64_t tok_begin, int tokens_per_split,
-                                 int n_splits, int slot_base, hipStream_t s) {
+                                 int n_splits, int slot_base, hipStream_t s,
+                                 const RowCounts *rows) {
   if (n_splits <= 0) return hipSuccess;
+  if (rows && a.B > kMaxRows) return hipErrorInvalidValue;
   const int head_chunks = (a.n_rep + kHeads - 1) / kHeads;
   dim3 grid((unsigned)n_splits, (unsigned)(a.H * head_chunks), (unsigned)a.B);
-  if (a.n_rep == 1)
-    hipLaunchKernelGGL(decode_generic_kernel<1>, grid, dim3(kThreads), 0, s, a, tok_begin,
-                       tokens_per_split, slot_base, head_chunks);
-  else if (a.n_rep == 2)
-    hipLaunchKernelGGL(decode_generic_kernel<2>, grid, dim3(kThreads), 0, s, a, tok_begin,
-                       tokens_per_split, slot_base, head_chunks);
-  else if (a.n_rep <= 4)
-    hipLaunchKernelGGL(decode_generic_kernel<4>, grid, dim3(kThreads), 0, s, a, tok_begin,
-                       tokens_per_split, slot_base, head_chunks);
+  if (rows)
+    launch_generic<true>(a, grid, s, tok_begin, tokens_per_split, slot_base, head_chunks, *rows);
   else
-    hipLaunchKernelGGL(decode_generic_kernel<kHeads>, grid, dim3(kThreads), 0, s, a, tok_begin,
-                       tokens_per_split, slot_base, head_chunks);
+    launch_generic<false>(a, grid, s, tok_begin, tokens_per_split, slot_base, head_chunks,
+                          NoRows{});
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const DecodeArgs &a, hipStream_t s) {
+hipError_t launch_combine(const DecodeArgs &a, hipStream_t s, const RowCounts *slots) {
   if (a.D % 8 != 0 || a.S_total <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(a.B * a.Hq), (unsigned)((a.D + 31) / 32)),
-                     dim3(256), 0, s, a);
+  const dim3 grid((unsigned)(a.B * a.Hq), (unsigned)((a.D + 31) / 32));
+  if (slots) {
+    if (a.B > kMaxRows) return hipErrorInvalidValue;
+    for (int b = 0; b < a.B; ++b)
+      if (slots->n[b] < 0 || slots->n[b] > a.S_total) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((combine_kernel<true>), grid, dim3(256), 0, s, a, *slots);
+  } else {
+    hipLaunchKernelGGL((combine_kernel<false>), grid, dim3(256), 0, s, a, NoRows{});
+  }
   return hipGetLastError();
 }
 

@@ -628,22 +628,22 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
 // the value buffer, in one batch of DMA; then each lane scores one token over
 // half of the channels (scalar fp32) and accumulates two output channels.
 template <int NREP, bool MASKED>
-__device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main, int chunk,
-                                            int slot, int hk, int b, const Lds &L) {
+__device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &rs, int64_t n_main,
+                                            int chunk, int slot, int hk, int b, const Lds &L) {
   const int j = threadIdx.x & 63;
   const int64_t bh = (int64_t)b * a.H + hk;
   const int64_t Ta = n_main + (int64_t)kWT * chunk;
-  const int64_t Tb = Ta + kWT < a.t ? Ta + kWT : a.t;
+  const int64_t Tb = Ta + kWT < rs.t ? Ta + kWT : rs.t;
   const int n = (int)(Tb - Ta);
   // keys: Ta and n_kq are multiples of 32, so the chunk is one whole
   // quantized key group or consists of fp16 window rows
-  const bool kq = Ta < a.n_kq;
+  const bool kq = Ta < rs.n_kq;
   // A fused step whose token completes a key block quantizes keys [t - R, t)
   // in this launch: each of those chunks stages its 32 fp16 rows and turns
   // them into its key group below (kq_now).
-  const bool kq_now = a.t_new >= 0 && a.t % a.R == 0 && Ta >= a.t - a.R;
+  const bool kq_now = rs.t_new >= 0 && rs.t % a.R == 0 && Ta >= rs.t - a.R;
   // values: [Ta, vq_end) quantized, [vq_end, Tb) fp16
-  const int64_t vq_end = a.n_vq < Ta ? Ta : (a.n_vq > Tb ? Tb : a.n_vq);
+  const int64_t vq_end = rs.n_vq < Ta ? Ta : (rs.n_vq > Tb ? Tb : rs.n_vq);
   const int n_qv = (int)(vq_end - Ta), n_fv = (int)(Tb - vq_end);
   const int nqv4 = (n_qv + 3) / 4;    // 16-byte units of fp32 scales per channel group
   const int nqv8 = (n_qv + 7) / 8;    // 16-byte units of fp16 zeros per channel group
@@ -670,7 +670,7 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
           src = rec + kRecKz + lg * 256 + (u - 96) * 16;
       } else {
         const int64_t tok = Ta + u / 16;
-        src = tok == a.t_new ? a.k_new + (bh * kD + (u % 16) * 8)
+        src = tok == rs.t_new ? a.k_new + (bh * kD + (u % 16) * 8)
                              : a.k_res + ((bh * a.R + tok % a.R) * kD + (u % 16) * 8);
       }
       dma16(src, (lds_void *)(kl + (size_t)base * 16));
@@ -699,7 +699,7 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
       } else {
         const int x = u - u_vrow;
         const int64_t tok = vq_end + x / 16;
-        src = tok == a.t_new ? a.v_new + (bh * kD + (x % 16) * 8)
+        src = tok == rs.t_new ? a.v_new + (bh * kD + (x % 16) * 8)
                              : a.v_res + ((bh * a.R + tok % a.R) * kD + (x % 16) * 8);
       }
       dma16(src, (lds_void *)(vl + (size_t)base * 16));
@@ -709,10 +709,10 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
   // (t_pop = t_new - R, the last quantized value) is read from its window
   // slot -- lane j holds channels 2j, 2j + 1 -- and quantized below; the
   // new token's value and key are read from the inputs.
-  const int64_t t_pop = a.t_new >= a.R ? a.t_new - a.R : -1;
+  const int64_t t_pop = rs.t_new >= a.R ? rs.t_new - a.R : -1;
   const bool pop_here = t_pop >= Ta && t_pop < vq_end;
-  const bool new_here = a.t_new >= Ta && a.t_new < Tb;
-  const int64_t wslot = a.t_new >= 0 ? a.t_new % a.R : 0;   // window slot of the new token
+  const bool new_here = rs.t_new >= Ta && rs.t_new < Tb;
+  const int64_t wslot = rs.t_new >= 0 ? rs.t_new % a.R : 0;   // window slot of the new token
   uint16_t *slot_v = const_cast<uint16_t *>(a.v_res) + (bh * a.R + wslot) * kD + 2 * j;
   uint32_t popped = 0, nv = 0, nk = 0;
   if (pop_here) popped = *(const uint32_t *)slot_v;
@@ -906,13 +906,20 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, int64_t n_main,
 // slots: s for the workgroup's blocks (its waves' partials merged in LDS),
 // n_groups + x for window chunk x.  A slab with a single workgroup merges
 // them into out in the same launch.
+// Ragged batch (RAGGED): each row has its own token count rows.t[b] and
+// its own number of workgroups per KV head, planned on the host in
+// proportion to its work; workgroup lin serves share u = lin % n_shares of
+// KV head lin / n_shares, and rows.share[u] names the row, the share's
+// index s among the row's workgroups and their number.  n_main, n_groups
+// and n_window then follow per row (n_groups argument = n_shares).
 // The masked variant holds the block's mask in registers as well; it may
 // use more than half the register file rather than spill, since a spill
 // reload inside the block loop would wait for every DMA in flight.
-template <int NREP, bool MASKED>
+template <int NREP, bool MASKED, bool RAGGED>
 __global__ void __launch_bounds__(MASKED ? 256 : 512)
     __attribute__((amdgpu_waves_per_eu(MASKED ? 1 : 2)))
-    decode_matrix_kernel(DecodeArgs a, int64_t n_main, int n_groups, int n_window) {
+    decode_matrix_kernel(DecodeArgs a, int64_t n_main_all, int n_groups_all, int n_window_all,
+                         MatrixRowArg<RAGGED> rows) {
   constexpr int W = MASKED ? 4 : 8;
   __shared__ KStage sm_k[W];
   __shared__ VStage sm_v[W];
@@ -923,11 +930,37 @@ __global__ void __launch_bounds__(MASKED ? 256 : 512)
   __shared__ int sm_ctr;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const Lds L{&sm_k[w], &sm_v[w], sm_p[w], sm_mask[w], sm_bias[w], sm_alpha[w]};
-  const uint32_t n_slabs = (uint32_t)a.B * (uint32_t)a.H;
   const uint32_t lin = blockIdx.x;
-  const uint32_t s = lin / n_slabs;
-  const uint32_t sl = (lin % n_slabs + n_slabs - s % n_slabs) % n_slabs;
-  const int hk = (int)(sl % (uint32_t)a.H), b = (int)(sl / (uint32_t)a.H);
+  uint32_t s, sl;
+  int hk, b, n_groups, n_window;
+  int64_t n_main;
+  RowSpan rs;
+  if constexpr (RAGGED) {
+    const uint32_t n_shares = (uint32_t)n_groups_all;
+    const uint32_t u = lin % n_shares;
+    const uint32_t e = rows.share[u];
+    hk = (int)(lin / n_shares);
+    b = (int)(e & 255u);
+    s = (e >> 8) & 4095u;
+    n_groups = (int)(e >> 20);
+    sl = (uint32_t)b * (uint32_t)a.H + (uint32_t)hk;
+    rs = row_span(rows.t[b], a.R, a.t_new >= 0);
+    n_main = matrix_main(rs, a.R);
+    n_window = matrix_window_chunks(rs.t, n_main);
+  } else {
+    const uint32_t n_slabs = (uint32_t)a.B * (uint32_t)a.H;
+    s = lin / n_slabs;
+    sl = (lin % n_slabs + n_slabs - s % n_slabs) % n_slabs;
+    hk = (int)(sl % (uint32_t)a.H);
+    b = (int)(sl / (uint32_t)a.H);
+    n_groups = n_groups_all;
+    n_window = n_window_all;
+    n_main = n_main_all;
+    rs.t = a.t;
+    rs.n_kq = a.n_kq;
+    rs.n_vq = a.n_vq;
+    rs.t_new = a.t_new;
+  }
   const int64_t nblk = n_main / kBT;
   BlockShare sh;
   sh.b0 = (int64_t)s * nblk / n_groups;
@@ -946,7 +979,7 @@ __global__ void __launch_bounds__(MASKED ? 256 : 512)
   int item = draw_item(&sm_ctr, lane);
   while (item < sh.n_skip) {
     const int x = (int)s + item * n_groups;
-    window_role<NREP, MASKED>(a, n_main, x, n_groups + x, hk, b, L);
+    window_role<NREP, MASKED>(a, rs, n_main, x, n_groups + x, hk, b, L);
     wave_lds_sync();   // the LDS reads of the chunk are done
     item = draw_item(&sm_ctr, lane);
   }
@@ -987,11 +1020,11 @@ __global__ void __launch_bounds__(MASKED ? 256 : 512)
   if (n_groups > 1) return;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's slot stores are done
   __syncthreads();
-  const int S = a.S_total;
+  const int S = n_groups + n_window;   // slots of this slab; a.S_total is their stride
   for (int e = threadIdx.x; e < NREP * kD; e += 64 * W) {
     const int h = e / kD, c = e % kD;
     const int64_t row = (int64_t)b * a.Hq + hk * NREP + h;
-    const float *pr = a.part + row * S * (int64_t)(kD + 4);
+    const float *pr = a.part + row * a.S_total * (int64_t)(kD + 4);
     float M = -INFINITY, Ls = 0.0f, acc = 0.0f;
     for (int s0 = 0; s0 < S; s0 += 16) {
       float mv[16], lv[16], av[16];
@@ -1038,20 +1071,30 @@ bool decode_matrix_supported(const DecodeArgs &a) {
 }
 
 int decode_matrix_window_chunks(const DecodeArgs &a, int64_t n_main) {
-  return (int)((a.t - n_main + kWT - 1) / kWT);
+  return matrix_window_chunks(a.t, n_main);
 }
 
 int decode_matrix_waves(const DecodeArgs &a) { return a.mask ? 4 : 8; }
 
-template <int NREP>
+template <int NREP, bool RAGGED>
 static void launch_rep(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
-                       int n_groups, int n_window) {
+                       int n_groups, int n_window, const MatrixRowArg<RAGGED> &rows) {
   if (a.mask)
-    hipLaunchKernelGGL((decode_matrix_kernel<NREP, true>), grid, dim3(256), 0, s, a, n_main,
-                       n_groups, n_window);
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, true, RAGGED>), grid, dim3(256), 0, s, a,
+                       n_main, n_groups, n_window, rows);
   else
-    hipLaunchKernelGGL((decode_matrix_kernel<NREP, false>), grid, dim3(512), 0, s, a, n_main,
-                       n_groups, n_window);
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, false, RAGGED>), grid, dim3(512), 0, s, a,
+                       n_main, n_groups, n_window, rows);
+}
+
+template <bool RAGGED>
+static void launch_reps(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
+                        int n_groups, int n_window, const MatrixRowArg<RAGGED> &rows) {
+  switch (a.n_rep) {
+    case 1: launch_rep<1, RAGGED>(a, grid, s, n_main, n_groups, n_window, rows); break;
+    case 2: launch_rep<2, RAGGED>(a, grid, s, n_main, n_groups, n_window, rows); break;
+    default: launch_rep<4, RAGGED>(a, grid, s, n_main, n_groups, n_window, rows); break;
+  }
 }
 
 hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int n_groups,
@@ -1074,12 +1117,29 @@ hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int n_group
   if ((int64_t)n_groups + n_window > a.S_total) return hipErrorInvalidValue;
   const int64_t n_wg = (int64_t)n_groups * a.H * a.B;
   if (n_wg > ((int64_t)1 << 25)) return hipErrorInvalidValue;   // 32-bit workgroup ids
-  dim3 grid((unsigned)n_wg);
-  switch (a.n_rep) {
-    case 1: launch_rep<1>(a, grid, s, n_main, n_groups, n_window); break;
-    case 2: launch_rep<2>(a, grid, s, n_main, n_groups, n_window); break;
-    default: launch_rep<4>(a, grid, s, n_main, n_groups, n_window); break;
+  launch_reps<false>(a, dim3((unsigned)n_wg), s, n_main, n_groups, n_window, NoRows{});
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_matrix_rows(const DecodeArgs &a, const MatrixRows &rows, int n_shares,
+                                     hipStream_t s) {
+  if (!decode_matrix_supported(a) || a.B > kMaxRows || n_shares <= 0 || n_shares > kMaxRows)
+    return hipErrorInvalidValue;
+  if (a.t_new >= 0 && (!a.k_new || !a.v_new)) return hipErrorInvalidValue;
+  // every share names a row of the batch and a valid index among the row's
+  // workgroups, and every row's slots fit the partial stride
+  for (int u = 0; u < n_shares; ++u) {
+    const uint32_t e = rows.share[u];
+    const int b = (int)(e & 255u), si = (int)((e >> 8) & 4095u), n = (int)(e >> 20);
+    if (b >= a.B || n <= 0 || si >= n) return hipErrorInvalidValue;
+    const int64_t t = rows.t[b];
+    if (t < (a.t_new >= 0 ? 1 : 0) || t > a.cap || t > a.t) return hipErrorInvalidValue;
+    const RowSpan rs = row_span(t, a.R, a.t_new >= 0);
+    const int64_t nm = matrix_main(rs, a.R);
+    if ((int64_t)n + matrix_window_chunks(t, nm) > a.S_total) return hipErrorInvalidValue;
   }
+  const int64_t n_wg = (int64_t)n_shares * a.H;
+  launch_reps<true>(a, dim3((unsigned)n_wg), s, 0, n_shares, 0, rows);
   return hipGetLastError();
 }
 

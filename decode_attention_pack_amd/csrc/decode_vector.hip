@@ -126,11 +126,14 @@ __device__ __forceinline__ float uniform(float v) {
 
 }  // namespace
 
-// grid: (n_splits, H * head_chunks, B); block: 256 (4 waves).
-template <int KB, int VB, int NH>
+// grid: (n_splits, H * head_chunks, B); block: 256 (4 waves).  A ragged
+// batch (RAGGED): row b holds rows.n[b] tokens; a.t is the mask's row
+// stride.
+template <int KB, int VB, int NH, bool RAGGED>
 __global__ void __launch_bounds__(kVThreads)
     __attribute__((amdgpu_waves_per_eu(2)))   // two waves per SIMD: the compiler may use 256 VGPRs
-decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int direct) {
+decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int direct,
+                     RowArg<RAGGED> rows) {
   __shared__ float red_s[kVWaves][NH][kVD];
   __shared__ float stat_s[kVWaves][NH][2];
 
@@ -152,10 +155,15 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
   const int tq = lane >> 2;   // token of each 16-token half this lane scores and accumulates
 
   // token and group indices within a slab fit 32 bits (cap < 2^26)
+  RowSpan rs;
+  if constexpr (RAGGED)
+    rs = row_span(rows.n[b], a.R, false);
+  else
+    rs = RowSpan{a.t, a.n_kq, a.n_vq, -1};
   const int s0 = split * tokens_per_split;
-  const int s1 = (int)min((int64_t)s0 + tokens_per_split, a.t);
+  const int s1 = (int)min((int64_t)s0 + tokens_per_split, rs.t);
   const int g_end = (s1 + kVG - 1) / kVG;
-  const int t_all = (int)a.t, n_kq = (int)a.n_kq, n_vq = (int)a.n_vq, R = a.R;
+  const int t_all = (int)rs.t, n_kq = (int)rs.n_kq, n_vq = (int)rs.n_vq, R = a.R;
 
   // q of channels 2 lane, 2 lane + 1, times 1/sqrt(D)
   float q0[NH], q1[NH];
@@ -455,36 +463,47 @@ bool decode_vector_supported(const DecodeArgs &a) {
 // One query head per KV head: NH = 1.  An even number: NH = 2, and n_rep / 2
 // workgroups per (split, slab), each for two of the heads (four heads in one
 // workgroup would not fit two waves per SIMD).
-template <int KB, int VB>
-static void launch_bits(const DecodeArgs &a, dim3 grid, int tps, int direct, hipStream_t s) {
+template <int KB, int VB, bool RAGGED>
+static void launch_bits(const DecodeArgs &a, dim3 grid, int tps, int direct, hipStream_t s,
+                        const RowArg<RAGGED> &rows) {
   if (a.n_rep == 1) {
-    hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 1>), grid, dim3(kVThreads), 0, s, a, tps, 1,
-                       direct);
+    hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 1, RAGGED>), grid, dim3(kVThreads), 0, s,
+                       a, tps, 1, direct, rows);
   } else {
     const int chunks = a.n_rep / 2;
     grid.y *= chunks;
-    hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 2>), grid, dim3(kVThreads), 0, s, a, tps,
-                       chunks, direct);
+    hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 2, RAGGED>), grid, dim3(kVThreads), 0, s,
+                       a, tps, chunks, direct, rows);
   }
+}
+
+template <bool RAGGED>
+static void launch_all_bits(const DecodeArgs &a, dim3 grid, int tps, int direct, hipStream_t s,
+                            const RowArg<RAGGED> &rows) {
+  if (a.kb == 2 && a.vb == 2)
+    launch_bits<2, 2, RAGGED>(a, grid, tps, direct, s, rows);
+  else if (a.kb == 2)
+    launch_bits<2, 4, RAGGED>(a, grid, tps, direct, s, rows);
+  else if (a.vb == 2)
+    launch_bits<4, 2, RAGGED>(a, grid, tps, direct, s, rows);
+  else
+    launch_bits<4, 4, RAGGED>(a, grid, tps, direct, s, rows);
 }
 
 // With a single split (n_splits == 1) the kernel writes the normalized
 // output itself and no combine pass is needed; otherwise it writes one
 // partial per split.
 hipError_t launch_decode_vector(const DecodeArgs &a, int tokens_per_split, int n_splits,
-                                hipStream_t s) {
+                                hipStream_t s, const RowCounts *rows) {
   if (n_splits <= 0) return hipSuccess;
   if (!decode_vector_supported(a) || tokens_per_split % kVG != 0) return hipErrorInvalidValue;
+  if (rows && a.B > kMaxRows) return hipErrorInvalidValue;
   dim3 grid((unsigned)n_splits, (unsigned)a.H, (unsigned)a.B);
   const int direct = n_splits == 1;
-  if (a.kb == 2 && a.vb == 2)
-    launch_bits<2, 2>(a, grid, tokens_per_split, direct, s);
-  else if (a.kb == 2)
-    launch_bits<2, 4>(a, grid, tokens_per_split, direct, s);
-  else if (a.vb == 2)
-    launch_bits<4, 2>(a, grid, tokens_per_split, direct, s);
+  if (rows)
+    launch_all_bits<true>(a, grid, tokens_per_split, direct, s, *rows);
   else
-    launch_bits<4, 4>(a, grid, tokens_per_split, direct, s);
+    launch_all_bits<false>(a, grid, tokens_per_split, direct, s, NoRows{});
   return hipGetLastError();
 }
 

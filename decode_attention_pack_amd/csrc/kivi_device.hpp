@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kivi {
 
 __device__ __forceinline__ float h2f(uint16_t h) {
@@ -90,6 +92,33 @@ inline Layout make_layout(uint8_t *blocks, int D, int kb, int vb, int G, int64_t
   L.nrec = cap / kRecTokens;
   return L;
 }
+
+// Token accounting of a sequence holding t tokens (KIVI item 4): keys [0,
+// n_kq) and values [0, n_vq) are in the records, the rest in the fp16
+// window.  t_new >= 0 marks a launch that appends token t_new = t - 1 itself
+// (the fused decode step); -1 a plain attention call.
+struct RowSpan {
+  int64_t t, n_kq, n_vq, t_new;
+};
+__host__ __device__ __forceinline__ RowSpan row_span(int64_t t, int R, bool appends) {
+  RowSpan r;
+  r.t = t;
+  r.n_kq = t - t % R;
+  r.n_vq = t > R ? t - R : 0;
+  r.t_new = appends ? t - 1 : -1;
+  return r;
+}
+
+// A ragged batch: batch row b holds its own token count.  Per-row tables
+// travel in the kernel arguments of a launch (nothing is copied to the
+// device), which bounds a ragged batch at kMaxRows rows.
+constexpr int kMaxRows = 256;
+struct RowCounts {
+  int32_t n[kMaxRows];
+};
+struct NoRows {};
+template <bool RAGGED>
+using RowArg = typename std::conditional<RAGGED, RowCounts, NoRows>::type;
 
 // Where token tau of one (batch, head) slab comes from when it is quantized:
 // tokens below `t0` are read from the fp16 window `res` (slot tau % R); tokens

@@ -47,6 +47,11 @@ __host__ __device__ inline bool append_one_supported(int D, int G, int bits) {
 hipError_t launch_append_one(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_res,
                              uint16_t *v_res, int64_t t0, int64_t BH, int R, bool key_to_window,
                              const Layout &L, hipStream_t s);
+// The same for a ragged batch (row b = slab / H appends token rows.n[b]),
+// including the key block a row's token completes.
+hipError_t launch_append_one_rows(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_res,
+                                  uint16_t *v_res, int64_t BH, int H, int R,
+                                  const RowCounts &rows, const Layout &L, hipStream_t s);
 
 // Everything the decode kernels read.
 struct DecodeArgs {
@@ -77,17 +82,31 @@ struct DecodeArgs {
 
 // Scalar kernel over tokens [tok_begin, t): `n_splits` splits of
 // `tokens_per_split`, writing partial slots [slot_base, slot_base + n_splits).
+// With `rows` (a ragged batch), row b attends over rows->n[b] tokens; splits
+// past a row's end write empty partials.
 hipError_t launch_decode_generic(const DecodeArgs &a, int64_t tok_begin, int tokens_per_split,
-                                 int n_splits, int slot_base, hipStream_t s);
+                                 int n_splits, int slot_base, hipStream_t s,
+                                 const RowCounts *rows = nullptr);
 
-// Matrix-core kernel for 2-bit caches with G = 32, D = 128 and 1, 2 or 4
-// query heads per KV head.  Returns hipErrorInvalidValue for other shapes.
+// Vector kernel for 2/4-bit caches with G = 32 and D = 128 (shapes in
+// decode_vector_supported).  `rows` as for the scalar kernel.
 bool decode_vector_supported(const DecodeArgs &a);
 hipError_t launch_decode_vector(const DecodeArgs &a, int tokens_per_split, int n_splits,
-                                hipStream_t s);
+                                hipStream_t s, const RowCounts *rows = nullptr);
 
 bool decode_matrix_supported(const DecodeArgs &a);
+// Tokens [0, n_main) of a row go to the matrix kernel's block role: whole
+// 128-token blocks of quantized keys and values.  In a fused step the value
+// leaving the window (token t_new - R) is quantized by the window role, so
+// the blocks stop before it.
+__host__ __device__ inline int64_t matrix_main(const RowSpan &r, int R) {
+  const int64_t lim = r.t_new >= R ? r.t_new - R : r.n_vq;
+  return lim / kRecTokens * kRecTokens;
+}
 // Window chunks (32 tokens each) that cover tokens [n_main, t).
+__host__ __device__ inline int matrix_window_chunks(int64_t t, int64_t n_main) {
+  return (int)((t - n_main + 31) / 32);
+}
 int decode_matrix_window_chunks(const DecodeArgs &a, int64_t n_main);
 // One launch of n_groups workgroups per slab (n_groups * B * H in all); the
 // waves of a workgroup take window chunks of [n_main, t) and blocks of its
@@ -96,8 +115,23 @@ int decode_matrix_window_chunks(const DecodeArgs &a, int64_t n_main);
 int decode_matrix_waves(const DecodeArgs &a);
 hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int n_groups,
                                 hipStream_t s);
+// Ragged batch: row b attends over t[b] tokens (after the append of a
+// fused step); per KV head, share u of n_shares is workgroup
+// share[u] >> 8 & 4095 of the share[u] >> 20 workgroups of row share[u] &
+// 255.  a.t is the longest row (the mask's row stride); a.S_total must hold
+// every row's slots.
+struct MatrixRows {
+  int32_t t[kMaxRows];
+  uint32_t share[kMaxRows];
+};
+template <bool RAGGED>
+using MatrixRowArg = typename std::conditional<RAGGED, MatrixRows, NoRows>::type;
+hipError_t launch_decode_matrix_rows(const DecodeArgs &a, const MatrixRows &rows, int n_shares,
+                                     hipStream_t s);
 
-// Log-sum-exp merge of the S_total partial slots into `out`.
-hipError_t launch_combine(const DecodeArgs &a, hipStream_t s);
+// Log-sum-exp merge of the S_total partial slots into `out`.  With
+// `slots`, the rows of batch row b merge their first slots->n[b] slots, and
+// rows with none are left as they are (their output is already written).
+hipError_t launch_combine(const DecodeArgs &a, hipStream_t s, const RowCounts *slots = nullptr);
 
 }  // namespace kivi

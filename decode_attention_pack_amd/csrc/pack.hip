@@ -8,39 +8,43 @@
 
 namespace kivi {
 
+// KIVI item 2 for key group g (tokens g G .. g G + G - 1) of channel c of
+// slab bh.  Two passes over the group's tokens (min/max, then codes) keep
+// the code free of per-thread arrays; the second pass hits the caches.
+__device__ __forceinline__ void quantize_key_group(const TokenSource &src, int64_t bh, int64_t g,
+                                                   int c, const Layout &L) {
+  const int G = L.G, bits = L.kb;
+  const int64_t tau0 = g * G;
+  const int per = 32 / bits;
+  const int words = G / per;
+  float mn = h2f(src.row(bh, tau0)[c]);
+  float mx = mn;
+  for (int i = 1; i < G; ++i) {
+    const float x = h2f(src.row(bh, tau0 + i)[c]);
+    mn = x < mn ? x : mn;
+    mx = x > mx ? x : mx;
+  }
+  const float s = group_scale(mn, mx, bits);
+  uint32_t *dst = L.key_codes(bh, g, c);
+  for (int w = 0; w < words; ++w) {
+    uint32_t word = 0;
+    for (int e = 0; e < per; ++e) {
+      const float x = h2f(src.row(bh, tau0 + w * per + e)[c]);
+      word |= quant_code(x, mn, s, bits) << (bits * e);
+    }
+    dst[w] = word;
+  }
+  *L.key_scale(bh, g, c) = s;
+  *L.key_zero(bh, g, c) = f2h_bits(mn);
+}
+
 // KIVI item 2: one thread per (channel, key group).  A key group is G
 // consecutive tokens of one channel; its codes are packed along tokens.
-// Two passes over the group's tokens (min/max, then codes) keep the kernel
-// free of per-thread arrays; the second pass hits the caches.
 __global__ void __launch_bounds__(128)
 key_groups_kernel(TokenSource src, int64_t g_first, Layout L) {
   const int64_t bh = blockIdx.y;
   const int64_t g = g_first + blockIdx.x;
-  const int G = L.G, D = L.D, bits = L.kb;
-  const int64_t tau0 = g * G;
-  const int per = 32 / bits;
-  const int words = G / per;
-  for (int c = threadIdx.x; c < D; c += blockDim.x) {
-    float mn = h2f(src.row(bh, tau0)[c]);
-    float mx = mn;
-    for (int i = 1; i < G; ++i) {
-      const float x = h2f(src.row(bh, tau0 + i)[c]);
-      mn = x < mn ? x : mn;
-      mx = x > mx ? x : mx;
-    }
-    const float s = group_scale(mn, mx, bits);
-    uint32_t *dst = L.key_codes(bh, g, c);
-    for (int w = 0; w < words; ++w) {
-      uint32_t word = 0;
-      for (int e = 0; e < per; ++e) {
-        const float x = h2f(src.row(bh, tau0 + w * per + e)[c]);
-        word |= quant_code(x, mn, s, bits) << (bits * e);
-      }
-      dst[w] = word;
-    }
-    *L.key_scale(bh, g, c) = s;
-    *L.key_zero(bh, g, c) = f2h_bits(mn);
-  }
+  for (int c = threadIdx.x; c < L.D; c += blockDim.x) quantize_key_group(src, bh, g, c, L);
 }
 
 // KIVI item 3: one thread per (token, value group).  A value group is G
@@ -300,15 +304,16 @@ hipError_t launch_value_tokens(const uint16_t *x, int64_t T_in, int64_t n_rows, 
 // One decode step of append (one new token per slab), fused: quantize the
 // value that leaves the window (KIVI item 3; token t0 - R, when t0 >= R),
 // then put the new value -- and the new key, unless it completes a key block
-// -- into slot t0 % R (KIVI item 4).  grid: BH; block: D threads rounded up
-// to a wave, thread c owns channel c.  Group min/max and the packing of codes
-// into words are lane reductions, so G and 32 / bits must be powers of two
-// no larger than a wave.
-__global__ void __launch_bounds__(256)
-append_one_kernel(const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
-                  uint16_t *__restrict__ k_res, uint16_t *__restrict__ v_res, int64_t t0,
-                  int R, bool key_to_window, Layout L) {
-  const int64_t bh = blockIdx.x;
+// -- into slot t0 % R (KIVI item 4).  Block: D threads rounded up to a wave,
+// thread c owns channel c.  Group min/max and the packing of codes into
+// words are lane reductions, so G and 32 / bits must be powers of two no
+// larger than a wave.
+__device__ __forceinline__ void append_one_slab(const uint16_t *__restrict__ k_new,
+                                                const uint16_t *__restrict__ v_new,
+                                                uint16_t *__restrict__ k_res,
+                                                uint16_t *__restrict__ v_res, int64_t bh,
+                                                int64_t t0, int R, bool key_to_window,
+                                                const Layout &L) {
   const int c = threadIdx.x;
   const int D = L.D, G = L.G, bits = L.vb;
   const bool on = c < D;
@@ -336,6 +341,34 @@ append_one_kernel(const uint16_t *__restrict__ k_new, const uint16_t *__restrict
   }
 }
 
+// grid: BH; every slab appends token t0.
+__global__ void __launch_bounds__(256)
+append_one_kernel(const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
+                  uint16_t *__restrict__ k_res, uint16_t *__restrict__ v_res, int64_t t0,
+                  int R, bool key_to_window, Layout L) {
+  append_one_slab(k_new, v_new, k_res, v_res, blockIdx.x, t0, R, key_to_window, L);
+}
+
+// A decode step of a ragged batch: slab bh (row b = bh / H) appends token t0
+// = rows.n[b].  When that token completes a key block (t0 + 1 a multiple of
+// R), thread c then quantizes channel c of the block's key groups (KIVI
+// item 2) from the window slots and the new key, which never enters the
+// window.  grid: BH.
+__global__ void __launch_bounds__(256)
+append_one_rows_kernel(const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
+                       uint16_t *__restrict__ k_res, uint16_t *__restrict__ v_res, int H, int R,
+                       Layout L, RowCounts rows) {
+  const int64_t bh = blockIdx.x;
+  const int64_t t0 = rows.n[bh / H];
+  const bool completes = (t0 + 1) % R == 0;
+  append_one_slab(k_new, v_new, k_res, v_res, bh, t0, R, !completes, L);
+  if (completes && (int)threadIdx.x < L.D) {
+    const TokenSource src{k_res, k_new, t0, 1, R, L.D};
+    for (int64_t g = (t0 + 1 - R) / L.G; g < (t0 + 1) / L.G; ++g)
+      quantize_key_group(src, bh, g, threadIdx.x, L);
+  }
+}
+
 hipError_t launch_append_one(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_res,
                              uint16_t *v_res, int64_t t0, int64_t BH, int R, bool key_to_window,
                              const Layout &L, hipStream_t s) {
@@ -343,6 +376,20 @@ hipError_t launch_append_one(const uint16_t *k_new, const uint16_t *v_new, uint1
   const int threads = (L.D + 63) / 64 * 64;
   hipLaunchKernelGGL(append_one_kernel, dim3((unsigned)BH), dim3(threads), 0, s, k_new, v_new,
                      k_res, v_res, t0, R, key_to_window, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_one_rows(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_res,
+                                  uint16_t *v_res, int64_t BH, int H, int R,
+                                  const RowCounts &rows, const Layout &L, hipStream_t s) {
+  if (!append_one_supported(L.D, L.G, L.vb) || BH <= 0 || H <= 0 || BH % H != 0 ||
+      BH / H > kMaxRows || R % L.G != 0)
+    return hipErrorInvalidValue;
+  for (int64_t b = 0; b < BH / H; ++b)
+    if (rows.n[b] < 0 || rows.n[b] >= L.nrec * kRecTokens) return hipErrorInvalidValue;
+  const int threads = (L.D + 63) / 64 * 64;
+  hipLaunchKernelGGL(append_one_rows_kernel, dim3((unsigned)BH), dim3(threads), 0, s, k_new,
+                     v_new, k_res, v_res, H, R, L, rows);
   return hipGetLastError();
 }
 

@@ -23,10 +23,12 @@ KIVI_ERR_HIP = -4
 KIVI_PATH_AUTO, KIVI_PATH_GENERIC, KIVI_PATH_MATRIX, KIVI_PATH_VECTOR = 0, 1, 2, 3
 
 EXPORTED = ("kivi_record_bytes", "kivi_pack_keys", "kivi_pack_values", "kivi_append",
-            "kivi_decode_attn", "kivi_decode_attn_ex", "kivi_decode_attn_workspace_bytes",
+            "kivi_append_row", "kivi_decode_attn", "kivi_decode_attn_ex",
+            "kivi_decode_attn_workspace_bytes",
             "kivi_decode_attn_workspace_bytes_ex", "kivi_decode_step", "kivi_decode_attn_noalloc",
             "kivi_status_string", "kivi_last_error")
 TOKENS_PER_RECORD = 128
+MAX_RAGGED_ROWS = 256
 
 
 class KiviError(RuntimeError):
@@ -42,6 +44,7 @@ class CCache(ctypes.Structure):
         ("residual", ctypes.c_int32),
         ("capacity", ctypes.c_int64), ("n_tokens", ctypes.c_int64),
         ("blocks", ctypes.c_void_p), ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
+        ("row_tokens", ctypes.POINTER(ctypes.c_int64)),
     ]
 
 
@@ -66,6 +69,8 @@ def lib():
         fn.restype = ctypes.c_int
     L.kivi_append.argtypes = [ctypes.POINTER(CCache), P, P, i64, P]
     L.kivi_append.restype = ctypes.c_int
+    L.kivi_append_row.argtypes = [ctypes.POINTER(CCache), i32, P, P, i64, P]
+    L.kivi_append_row.restype = ctypes.c_int
     L.kivi_decode_attn.argtypes = [ctypes.POINTER(CCache), P, i32, P, P, P, sz, P]
     L.kivi_decode_attn.restype = ctypes.c_int
     L.kivi_decode_attn_ex.argtypes = [ctypes.POINTER(CCache), P, i32, P, P, P, sz, i32, i32, P]
@@ -136,10 +141,11 @@ class Cache:
     """A KIVI cache in device memory (torch tensors) plus its C descriptor.
 
     ``blocks`` is the record array as raw bytes; ``k_res`` / ``v_res`` are the
-    fp16 windows."""
+    fp16 windows.  ``ragged=True`` gives a ragged batch: each row keeps its own
+    token count (``row_tokens``), all rows starting empty."""
 
     def __init__(self, batch, n_kv_heads, head_dim, k_bits, v_bits, group, residual, capacity,
-                 device="cuda", arrays=None):
+                 device="cuda", arrays=None, ragged=False):
         self.B, self.H, self.D = batch, n_kv_heads, head_dim
         self.kb, self.vb, self.G, self.R, self.cap = k_bits, v_bits, group, residual, capacity
         if capacity % TOKENS_PER_RECORD:
@@ -152,8 +158,16 @@ class Cache:
         for n in _ORDER:
             _dev(arrays[n], _DT[n], shapes[n], n)
         self.arrays = arrays
+        self._rows = None
+        if ragged:
+            if not 0 < batch <= MAX_RAGGED_ROWS:
+                raise KiviError(KIVI_ERR_INVALID_ARG,
+                                f"a ragged batch holds 1 to {MAX_RAGGED_ROWS} rows (got {batch})")
+            self._rows = (ctypes.c_int64 * batch)()
         self.c = CCache(batch, n_kv_heads, head_dim, k_bits, v_bits, group, residual, capacity, 0,
-                        *[arrays[n].data_ptr() for n in _ORDER])
+                        *[arrays[n].data_ptr() for n in _ORDER],
+                        ctypes.cast(self._rows, ctypes.POINTER(ctypes.c_int64))
+                        if ragged else None)
 
     def __getattr__(self, name):
         arrays = self.__dict__.get("arrays")
@@ -163,7 +177,29 @@ class Cache:
 
     @property
     def n_tokens(self) -> int:
+        """Token count (the longest row of a ragged batch)."""
         return int(self.c.n_tokens)
+
+    @property
+    def ragged(self) -> bool:
+        return self._rows is not None
+
+    @property
+    def row_tokens(self) -> list:
+        """Per-row token counts (every row holds n_tokens unless ragged)."""
+        if self._rows is None:
+            return [self.n_tokens] * self.B
+        return [int(x) for x in self._rows]
+
+    def reset_row(self, b: int):
+        """Empty row b of a ragged batch (host-side count only: later appends
+        overwrite what the row's storage held)."""
+        if self._rows is None:
+            raise KiviError(KIVI_ERR_INVALID_ARG, "reset_row needs a ragged cache")
+        if not 0 <= b < self.B:
+            raise KiviError(KIVI_ERR_INVALID_ARG, f"row {b} outside [0, {self.B})")
+        self._rows[b] = 0
+        self.c.n_tokens = max(self._rows)
 
     def workspace_bytes(self, n_q_heads, tokens_per_split=0, path=KIVI_PATH_AUTO) -> int:
         n = lib().kivi_decode_attn_workspace_bytes_ex(ctypes.byref(self.c), n_q_heads,
@@ -198,6 +234,15 @@ def kivi_append(cache: Cache, k_new, v_new, stream=None):
     kp = _dev(k_new, torch.float16, shape, "k_new")
     vp = _dev(v_new, torch.float16, shape, "v_new")
     _check(lib().kivi_append(ctypes.byref(cache.c), kp, vp, n, _stream(stream)))
+
+
+def kivi_append_row(cache: Cache, b: int, k_new, v_new, stream=None):
+    """Append k_new / v_new (fp16 [H][n][D]) to row b of a ragged cache."""
+    n = k_new.shape[1]
+    shape = (cache.H, n, cache.D)
+    kp = _dev(k_new, torch.float16, shape, "k_new")
+    vp = _dev(v_new, torch.float16, shape, "v_new")
+    _check(lib().kivi_append_row(ctypes.byref(cache.c), b, kp, vp, n, _stream(stream)))
 
 
 def kivi_decode_attn(cache: Cache, q, mask=None, out=None, workspace=None, tokens_per_split=0,

@@ -13,6 +13,8 @@ datasets are involved -- seeded Gaussian activations stand in for them):
   3 kivi4-b64       B64, 32 / 32,        D128, 4-bit,     G32, R128, 2048-token prefill, 1 step
   4 llama3-8b-gqa   B4, 32 / 8,          D128, 2-bit,     G32, R128, 32768-token prefill, 1 step
   5 long-128k       B1, 32 / 8,          D128, 2-bit,     G32, R128, 131072-token prefill, 1 step
+  ragged            B8, 32 / 8,          D128, 2-bit,     G32, R128, prefills of 1024..32768
+                    tokens per row (ragged_lengths), 1 step
 
 q and V are N(0, 1).  K is N(0, 1) except 4 distinct "outlier" channels per
 KV head, drawn without replacement, which are multiplied by 15 (tiny) or by a
@@ -64,6 +66,22 @@ WORKLOADS = {
     4: Workload(4, "llama3-8b-gqa-32k", 4, 32, 8, 128, 2, 2, 32, 128, 32768, 1, None),
     5: Workload(5, "long-128k", 1, 32, 8, 128, 2, 2, 32, 128, 131072, 1, None),
 }
+
+
+# A ragged batch on the llama3-8b-gqa shape: 8 rows whose prefill lengths
+# spread over [1024, 32768] (ragged_lengths).  T0 is the longest row.
+RAGGED = Workload(6, "llama3-8b-gqa-ragged-b8", 8, 32, 8, 128, 2, 2, 32, 128, 32768, 1, None)
+
+
+def ragged_lengths(n: int, lo: int, hi: int, seed: int = 7) -> np.ndarray:
+    """n sequence lengths for a ragged batch, log-uniform over [lo, hi] (a
+    long-tailed mix like the request lengths of a serving trace), with the
+    first row at hi so that the batch spans the whole range.  int64 [n]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = np.exp(rng.uniform(np.log(lo), np.log(hi), size=n))
+    out = np.clip(np.rint(x), lo, hi).astype(np.int64)
+    out[0] = hi
+    return out
 
 
 def _normal_f16(rng: np.random.Generator, shape) -> np.ndarray:

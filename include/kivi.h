@@ -82,7 +82,23 @@ enum {
  * is a multiple of 32/bits for both; head_dim <= 256; residual % group == 0;
  * capacity a positive multiple of 128 and of residual; 0 <= n_tokens <=
  * capacity; batch * n_kv_heads <= 65535; blocks, k_res and v_res 16-byte
- * aligned. */
+ * aligned.
+ *
+ * Ragged batch (row_tokens != NULL): the rows are independent sequences of
+ * different lengths, as in serving, where the batch holds requests of
+ * different context lengths (the setting of the throughput measurement on
+ * the "Literature audit" page, section "1. KIVI -- kivi2024", "Original
+ * evaluation setting").  row_tokens is a host array of `batch` counts; row
+ * b holds row_tokens[b] tokens (0 <= row_tokens[b] <= capacity), stored by
+ * the rules above with t = row_tokens[b], and batch <= 256.  n_tokens is
+ * then not read: every call that changes the counts writes the longest one
+ * into it.  The records and windows of row b, taken alone, form a cache of
+ * batch 1 (blocks + b * n_kv_heads * (capacity/128) * RB, k_res and v_res +
+ * b * n_kv_heads * R * D elements), so a row's storage is independent of
+ * the others'.  A row is emptied by setting its count to 0 (nothing on the
+ * device changes; later appends overwrite what it held).  A mask for a
+ * ragged batch is f32 [B][max_b row_tokens[b]] (plus one for
+ * kivi_decode_step); entries past a row's length are not read. */
 typedef struct kivi_cache {
   int32_t batch;
   int32_t n_kv_heads;
@@ -96,6 +112,7 @@ typedef struct kivi_cache {
   uint8_t *blocks;   /* [B][H][capacity/128] records                       */
   uint16_t *k_res;
   uint16_t *v_res;
+  int64_t *row_tokens; /* NULL, or host [batch]: per-row token counts      */
 } kivi_cache;
 
 /* Bytes of one 128-token record for a shape (0 if the shape is invalid);
@@ -136,6 +153,16 @@ int kivi_pack_values(const kivi_cache *dst, const void *v_fp16, int64_t T,
  * run in stream order). */
 int kivi_append(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp16,
                 int64_t n_new, void *stream);
+
+/* KIVI item 4 for one row of a ragged batch (row_tokens != NULL): append
+ * n_new tokens to row b alone, by the rule of kivi_append, e.g. the prefill
+ * of a new request into an emptied row.
+ *   k_new_fp16, v_new_fp16  (device) fp16 [H][n_new][D].
+ * KIVI_ERR_CAPACITY if row_tokens[b] + n_new > capacity; KIVI_ERR_INVALID_ARG
+ * for a cache without row_tokens.  On success row_tokens[b] grows by n_new
+ * and n_tokens becomes the longest row. */
+int kivi_append_row(kivi_cache *c, int32_t b, const void *k_new_fp16, const void *v_new_fp16,
+                    int64_t n_new, void *stream);
 
 /* Bytes of workspace kivi_decode_attn needs for this cache shape and query
  * head count at any n_tokens up to the capacity. 0 on invalid arguments. */

@@ -75,9 +75,10 @@ def compare_slab(g: kivi.Cache, b: int, h: int, o: oracle.Cache, ob: int = 0, oh
     """Bitwise comparison of the valid part of slab (b, h) of the GPU cache
     with slab (ob, oh) of the oracle cache.  gl / ol: logical views already
     taken; gres: host copies (k_res, v_res) of the GPU windows (to compare
-    many slabs, from several threads, with one device copy each)."""
-    t = g.n_tokens
-    assert o.n_tokens == t
+    many slabs, from several threads, with one device copy each).  A ragged
+    cache compares row b's own token count."""
+    t = g.row_tokens[b]
+    assert o.n_tokens == t, (b, h, o.n_tokens, t)
     R, G = g.R, g.G
     n_kq, n_vq = t - t % R, max(0, t - R)
     gl = logical(g) if gl is None else gl
@@ -145,7 +146,9 @@ def check_every_slab(w, g: kivi.Cache, orc: dict, outs: dict, q, mask=None, stor
     """Every (batch row, KV head) slab of workload w: the packed store and
     the windows of the GPU cache bit for bit against the slab's oracle cache
     (orc[(b, h)]), and every output of outs (label -> [B][Hq][D]) within the
-    tolerance of the oracle's attention.  The oracle runs in the thread pool."""
+    tolerance of the oracle's attention.  The oracle runs in the thread pool.
+    A ragged batch's slabs hold their rows' own token counts; mask columns
+    past a row's count are not given to the oracle."""
     rep = w.Hq // w.Hkv
     gl = logical(g) if stores else None
     gres = host_windows(g) if stores else None
@@ -155,7 +158,7 @@ def check_every_slab(w, g: kivi.Cache, orc: dict, outs: dict, q, mask=None, stor
         o = orc[bh]
         if stores:
             compare_slab(g, b, h, o, gl=gl, gres=gres)
-        m = None if mask is None else mask[b:b + 1]
+        m = None if mask is None else np.ascontiguousarray(mask[b:b + 1, :o.n_tokens])
         return bh, o.decode_attn(b16(q[b:b + 1, h * rep:(h + 1) * rep]), m)[0]
 
     ref = np.zeros((w.B, w.Hq, w.D), np.float32)

@@ -213,3 +213,45 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(kivi, "LIB_PATH", str(tmp_path / "libkivi.so"))
     with pytest.raises(RuntimeError, match="missing"):
         kivi.lib()
+
+
+def _ragged(counts, **kw):
+    c = _cache(batch=len(counts), **kw)
+    arr = (ctypes.c_int64 * len(counts))(*counts)
+    c.row_tokens = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64))
+    return c, arr
+
+
+def test_ragged_rejects(L):
+    """A ragged batch (row_tokens set): counts outside [0, capacity], more
+    than 256 rows, per-row appends on a uniform cache or past a row's
+    capacity, and too many workgroups from an explicit split are rejected on
+    the host, leaving the counts as they were."""
+    big = 1 << 34
+    for counts in ([5, 2000], [-1, 3]):
+        c, arr = _ragged(counts)
+        assert L.kivi_decode_attn(ctypes.byref(c), FAKE, 2, None, FAKE, FAKE, big, None) == -1
+        assert b"row_tokens" in L.kivi_last_error()
+    c, arr = _ragged([0] * 257, n_kv_heads=1)
+    assert L.kivi_decode_attn(ctypes.byref(c), FAKE, 1, None, FAKE, FAKE, big, None) == -1
+    assert b"256" in L.kivi_last_error()
+    u = _cache()
+    assert L.kivi_append_row(ctypes.byref(u), 0, FAKE, FAKE, 1, None) == -1
+    c, arr = _ragged([10, 20])
+    for b in (2, -1):
+        assert L.kivi_append_row(ctypes.byref(c), b, FAKE, FAKE, 1, None) == -1
+    assert L.kivi_append_row(ctypes.byref(c), 1, FAKE, FAKE, 1005, None) == -2
+    assert L.kivi_append_row(ctypes.byref(c), 1, FAKE, FAKE, 0, None) == 0
+    # every row of a ragged append takes the tokens: the longest row decides
+    assert L.kivi_append(ctypes.byref(c), FAKE, FAKE, 1005, None) == -2
+    assert list(arr) == [10, 20]
+    c, arr = _ragged([1024, 3])
+    assert L.kivi_decode_step(ctypes.byref(c), FAKE, FAKE, FAKE, 2, None, FAKE, FAKE, big,
+                              None) == -2
+    assert list(arr) == [1024, 3]
+    # 64 rows of 1000 tokens, a workgroup per 64 tokens: 448 workgroups per
+    # KV head, more than a ragged launch's table holds
+    c, arr = _ragged([1000] * 64, n_kv_heads=1)
+    assert L.kivi_decode_attn_ex(ctypes.byref(c), FAKE, 1, None, FAKE, FAKE, big, 64, 2,
+                                 None) == -1
+    assert b"tokens_per_split" in L.kivi_last_error()

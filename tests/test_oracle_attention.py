@@ -154,3 +154,38 @@ def test_empty_cache_gives_zeros():
     c = oracle.Cache(1, 1, 32, 2, 2, 32, 32, 128)
     out = c.decode_attn(np.zeros((1, 1, 32), np.uint16))
     assert not out.any()
+
+
+@pytest.mark.parametrize("lengths", [(1, 31, 32, 33), (77, 128, 129, 96)])
+def test_ragged_rows_are_independent_sequences(lengths):
+    """A ragged batch is a set of independent sequences (the serving setting
+    of the KIVI section's "Original evaluation setting"): the reference for
+    row b is the oracle on that row alone.  Pinned two ways: each row's own
+    window split (keys [0, t - t%R) and values [0, t - R) quantized, the rest
+    the exact fp16 inputs) and its attention against dense attention over
+    its dequantized tokens; and row b of a batched oracle cache equals the
+    same sequence in a cache of batch 1."""
+    D, G, R = 64, 32, 32
+    rng = np.random.default_rng(sum(lengths))
+    for t in lengths:
+        c, K, V = _filled(1, 2, D, G, R, t, seed=t, kscale=3.0)
+        kh, vh = c.materialize()
+        n_kq, n_vq = t - t % R, max(0, t - R)
+        assert np.array_equal(kh[:, :, n_kq:], K[:, :, n_kq:].astype(np.float32))
+        assert np.array_equal(vh[:, :, n_vq:], V[:, :, n_vq:].astype(np.float32))
+        if n_kq:
+            assert not np.array_equal(kh[:, :, :n_kq], K[:, :, :n_kq].astype(np.float32))
+        if n_vq:
+            assert not np.array_equal(vh[:, :, :n_vq], V[:, :, :n_vq].astype(np.float32))
+        q = _rand(rng, (1, 4, D))
+        got = c.decode_attn(q.view(np.uint16))
+        np.testing.assert_allclose(got, dense_attention(q.astype(np.float32), kh, vh), **TOL)
+    t = max(lengths)
+    both, K, V = _filled(3, 2, D, G, R, t, seed=5)
+    q = _rand(rng, (3, 4, D)).view(np.uint16)
+    full = both.decode_attn(q)
+    for b in range(3):
+        one = oracle.Cache(1, 2, D, 2, 2, G, R, both.cap)
+        one.append(np.ascontiguousarray(K[b:b + 1]).view(np.uint16),
+                   np.ascontiguousarray(V[b:b + 1]).view(np.uint16))
+        assert np.array_equal(one.decode_attn(q[b:b + 1]), full[b:b + 1])
