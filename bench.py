@@ -68,29 +68,36 @@ def measured_traffic(workload_name: str):
     return rec.get("traffic_bytes_per_launch")
 
 
-def attn_bytes(w, t: int) -> int:
-    """Algorithmic bytes of one kivi_decode_attn call at context t."""
+def attn_bytes(w, t) -> int:
+    """Algorithmic bytes of one kivi_decode_attn call at context t (an int,
+    or one count per batch row of a ragged batch)."""
     R, G, D = w.R, w.G, w.D
-    n_kq = t - t % R
-    n_vq = max(0, t - R)
     rep = w.Hq // w.Hkv
-    # fp32 scale + fp16 zero per group
-    per = (n_kq * D * w.k_bits // 8 + (n_kq // G) * D * 6
-           + n_vq * D * w.v_bits // 8 + n_vq * (D // G) * 6
-           + ((t % R) + min(t, R)) * D * 2
-           + rep * D * 2 + rep * D * 4)
-    return per * w.B * w.Hkv
+    total = 0
+    for tb in ([t] * w.B if isinstance(t, int) else t):
+        n_kq = tb - tb % R
+        n_vq = max(0, tb - R)
+        # fp32 scale + fp16 zero per group
+        total += (n_kq * D * w.k_bits // 8 + (n_kq // G) * D * 6
+                  + n_vq * D * w.v_bits // 8 + n_vq * (D // G) * 6
+                  + ((tb % R) + min(tb, R)) * D * 2
+                  + rep * D * 2 + rep * D * 4)
+    return total * w.Hkv
 
 
-def append_bytes(w, t_before: int) -> int:
-    """Algorithmic bytes of appending one token to a cache holding t_before."""
+def append_bytes(w, t_before) -> int:
+    """Algorithmic bytes of appending one token to every row of a cache
+    holding t_before tokens (an int, or one count per row)."""
     R, G, D = w.R, w.G, w.D
-    per = 2 * D * 2 + 2 * D * 2                       # read k, v; write window slots
-    if t_before >= R:                                 # value leaves the window
-        per += D * 2 + D * w.v_bits // 8 + (D // G) * 6
-    if (t_before + 1) % R == 0:                       # key block quantized
-        per += R * D * 2 + R * D * w.k_bits // 8 + (R // G) * D * 6
-    return per * w.B * w.Hkv
+    total = 0
+    for tb in ([t_before] * w.B if isinstance(t_before, int) else t_before):
+        per = 2 * D * 2 + 2 * D * 2                       # read k, v; write window slots
+        if tb >= R:                                       # value leaves the window
+            per += D * 2 + D * w.v_bits // 8 + (D // G) * 6
+        if (tb + 1) % R == 0:                             # key block quantized
+            per += R * D * 2 + R * D * w.k_bits // 8 + (R // G) * D * 6
+        total += per
+    return total * w.Hkv
 
 
 def pack_bytes(w, T: int, bits: int) -> int:
@@ -145,22 +152,25 @@ def host_cpu():
     return model, cores
 
 
-def cpu_baseline(w, inp, budget_s: float = 10.0):
-    """Time the CPU oracle on (batch, KV head) slabs of the workload: first on
-    one thread until ~budget_s of work, then the same slabs on every host core
-    (one slab per thread; the oracle's C code runs outside the GIL)."""
+def cpu_baseline(w, inp, lengths, budget_s: float = 10.0):
+    """Time the CPU oracle on (batch, KV head) slabs of the workload (row b
+    prefilled with lengths[b] tokens): first on one thread until ~budget_s of
+    work, then the same slabs on every host core (one slab per thread; the
+    oracle's C code runs outside the GIL)."""
     import concurrent.futures
 
     import oracle
     rep = w.Hq // w.Hkv
-    t = w.T0 + 1
+    t = max(lengths) + 1
     q = inp["q_steps"][0]
     model, n_cores = host_cpu()
 
     def build(bh):
         b, h = bh
         o = oracle.Cache(1, 1, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
-        o.append(inp["k0"][b:b + 1, h:h + 1].view(np.uint16), inp["v0"][b:b + 1, h:h + 1].view(np.uint16))
+        T = lengths[b]
+        o.append(np.ascontiguousarray(inp["k0"][b:b + 1, h:h + 1, :T]).view(np.uint16),
+                 np.ascontiguousarray(inp["v0"][b:b + 1, h:h + 1, :T]).view(np.uint16))
         o.append(inp["k_steps"][0][b:b + 1, h:h + 1].view(np.uint16),
                  inp["v_steps"][0][b:b + 1, h:h + 1].view(np.uint16))
         return o
@@ -169,21 +179,26 @@ def cpu_baseline(w, inp, budget_s: float = 10.0):
         b, h = bh
         o.decode_attn(np.ascontiguousarray(q[b:b + 1, h * rep:(h + 1) * rep]).view(np.uint16))
 
+    def slab_bytes(bh):
+        return attn_bytes(w, [lengths[bh[0]] + 1]) / w.Hkv
+
     slabs = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
-    done, spent = [], 0.0
+    done, spent, n_bytes = [], 0.0, 0.0
     for bh in slabs:
         o = build(bh)
         t0 = time.perf_counter()
         attend(bh, o)
         spent += time.perf_counter() - t0
         done.append((bh, o))
+        n_bytes += slab_bytes(bh)
         if spent >= budget_s:
             break
-    slab_bytes = attn_bytes(w, t) / (w.B * w.Hkv)
-    res = {"value": round(slab_bytes * len(done) / spent / 1e9, 4), "unit": "GB/s", "cores": 1,
+    ctx = (f"context {t}" if min(lengths) == max(lengths) else
+           f"contexts {min(lengths) + 1}..{t} by row")
+    res = {"value": round(n_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1,
            "kind": "oracle",
            "sample": f"{len(done)} of {w.B * w.Hkv} (batch, kv-head) slabs of {w.name}, one decode "
-                     f"step at context {t} ({rep} query heads each), single-threaded C oracle, "
+                     f"step at {ctx} ({rep} query heads each), single-threaded C oracle, "
                      f"{spent:.1f} s",
            "host_cpu": model, "host_cores": n_cores}
     # the same sample on every core: each thread runs whole slabs
@@ -193,7 +208,7 @@ def cpu_baseline(w, inp, budget_s: float = 10.0):
         t0 = time.perf_counter()
         list(ex.map(lambda x: attend(*x), work))
         wall = time.perf_counter() - t0
-    res["all_cores"] = {"value": round(slab_bytes * len(work) / wall / 1e9, 4), "unit": "GB/s",
+    res["all_cores"] = {"value": round(n_bytes * reps / wall / 1e9, 4), "unit": "GB/s",
                         "cores": n_cores,
                         "sample": f"{len(work)} slab attention calls ({len(done)} slabs x {reps}) "
                                   f"on {n_cores} threads, {wall:.1f} s wall"}
@@ -205,7 +220,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", type=int, default=4)
+    ap.add_argument("--workload", type=int, default=4,
+                    help="1-5: the workloads of synth.WORKLOADS; 6: the ragged batch")
     ap.add_argument("--layers", type=int, default=0, help="layer replicas (0 = auto, >= 1 GiB)")
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 scalar kernel, 2 matrix kernel")
     ap.add_argument("--tokens-per-split", type=int, default=0,
@@ -229,8 +245,12 @@ def main():
 
     from decode_attention_pack_amd import kivi, synth
 
-    w = synth.WORKLOADS[args.workload]
+    ragged = args.workload == synth.RAGGED.index
+    w = synth.RAGGED if ragged else synth.WORKLOADS[args.workload]
     inp = synth.make_inputs(w.replace(steps=1))
+    # prefill length of each batch row (a ragged batch: its own per row)
+    lengths = ([int(x) for x in synth.ragged_lengths(w.B, 1024, w.T0)] if ragged
+               else [w.T0] * w.B)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
@@ -249,15 +269,41 @@ def main():
     print(f"# {w.name}: footprint {footprint / 1e6:.1f} MB/layer, {L} layers, capacity {cap}",
           file=sys.stderr, flush=True)
 
-    base = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, cap)
-    kivi.kivi_append(base, torch.from_numpy(inp["k0"]).to(dev), torch.from_numpy(inp["v0"]).to(dev))
+    base = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, cap, ragged=ragged)
+    if ragged:
+        # each row prefilled alone, as a request entering a serving batch
+        for b, T in enumerate(lengths):
+            kivi.kivi_append_row(base, b, torch.from_numpy(inp["k0"][b, :, :T]).to(dev),
+                                 torch.from_numpy(inp["v0"][b, :, :T]).to(dev))
+    else:
+        kivi.kivi_append(base, torch.from_numpy(inp["k0"]).to(dev),
+                         torch.from_numpy(inp["v0"]).to(dev))
     torch.cuda.synchronize()
     caches = [base]
     for _ in range(L - 1):
         arrays = {n: a.clone() for n, a in base.arrays.items()}
-        c = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, cap, arrays=arrays)
-        c.c.n_tokens = base.n_tokens
+        c = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, cap, arrays=arrays,
+                       ragged=ragged)
+        if ragged:
+            c.set_row_tokens(lengths)
+        else:
+            c.c.n_tokens = base.n_tokens
         caches.append(c)
+
+    def rewind(c):
+        if ragged:
+            c.set_row_tokens(lengths)
+        else:
+            c.c.n_tokens = w.T0
+
+    def offset(c):
+        """Decode steps the replica has taken since its prefill."""
+        return (c.row_tokens[0] if ragged else c.n_tokens) - lengths[0]
+
+    # algorithmic bytes by steps taken: attention over prefill + k tokens,
+    # and the append of token prefill + k
+    attn_by_off = [attn_bytes(w, [T + k for T in lengths]) for k in range(n_cyc + 1)]
+    app_by_off = [append_bytes(w, [T + k for T in lengths]) for k in range(n_cyc + 1)]
     k1 = torch.from_numpy(inp["k_steps"][0]).to(dev)
     v1 = torch.from_numpy(inp["v_steps"][0]).to(dev)
     q = torch.from_numpy(inp["q_steps"][0]).to(dev)
@@ -278,16 +324,16 @@ def main():
 
     def step(i):
         c = caches[i % L]
-        if c.n_tokens >= w.T0 + n_cyc:
-            c.c.n_tokens = w.T0
-        t_before = c.n_tokens
-        contexts.add(t_before + 1)
+        if offset(c) >= n_cyc:
+            rewind(c)
+        k = offset(c)
+        contexts.add(lengths[0] + k + 1)
         if fused:
             fused_steps[i % L]()
         else:
             appends[i % L]()
             decodes[i % L]()
-        return attn_bytes(w, t_before + 1), append_bytes(w, t_before)
+        return attn_by_off[k + 1], app_by_off[k]
 
     # warm-up: the requested steps, and at least ~1 s of back-to-back steps
     # (with fewer, the clocks have not settled and the first timed calls run
@@ -329,8 +375,8 @@ def main():
         for j in range(per_round):
             c = caches[(r * per_round + j) % L]
             decodes[(r * per_round + j) % L]()
-            a2_bytes += attn_bytes(w, c.n_tokens)
-            attn_contexts.add(c.n_tokens)
+            a2_bytes += attn_by_off[offset(c)]
+            attn_contexts.add(lengths[0] + offset(c))
         e1.record(stream)
         rounds_ms.append((e0, e1))
     torch.cuda.synchronize()
@@ -364,7 +410,8 @@ def main():
                          "accumulation, softmax and output"),
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
-                   "head_dim": w.D, "context": w.T0 + 1, "decode_steps": n_cyc,
+                   "head_dim": w.D, "context": max(lengths) + 1, "decode_steps": n_cyc,
+                   **({"row_contexts": [T + 1 for T in lengths]} if ragged else {}),
                    "k_bits": w.k_bits, "v_bits": w.v_bits,
                    "group": w.G, "residual": w.R, "layers_rotated": L,
                    "storage": "128-token records: packed codes, fp32 scales, fp16 zero points; "
@@ -383,12 +430,12 @@ def main():
                      "kernel": "kivi_decode_attn launch (split kernel + combine)",
                      "bytes_per_launch": a2_bytes // (n_rounds * per_round)},
     }
-    if not args.no_pack:
+    if not args.no_pack and not ragged:
         del caches, base, appends, decodes, fused_steps
         torch.cuda.empty_cache()
         line["pack_full_prefill"] = time_pack(w, inp, dev, stream)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, inp)
+        line["cpu_baseline"] = cpu_baseline(w, inp, lengths)
     print(json.dumps(line), flush=True)
 
 

@@ -202,26 +202,26 @@ int head_chunks(int n_rep) { return (n_rep + 7) / 8; }
 
 int64_t ceil_div(int64_t x, int64_t y) { return (x + y - 1) / y; }
 
-// Matrix-kernel plan of a ragged batch: each row gets workgroups per KV head
-// in proportion to its work (blocks plus window chunks), at least one and at
-// most one per `waves` items, about one workgroup per CU in all; the rest go
-// one at a time to the row with the most work per workgroup.  With tps_req,
-// a workgroup per tps_req tokens of a row.
+// Matrix-kernel plan of a ragged batch, about one workgroup per CU in all:
+// every row starts with one workgroup per KV head, and the others go one at
+// a time to the row with the most work per workgroup, a row taking at most
+// one per `waves` items (blocks and window chunks).  Work counts a window
+// chunk (32 tokens, scalar arithmetic and a load it waits for) as two
+// 128-token blocks, about what it costs a wave.  With tps_req, a workgroup
+// per tps_req tokens of a row.
 int plan_matrix_rows(const kivi_cache *c, const Rows &r, int32_t tps_req, int waves, bool fused,
                      Plan &p, const char *who) {
   const int B = c->batch, R = c->residual;
   int64_t work[kivi::kMaxRows], cap[kivi::kMaxRows], groups[kivi::kMaxRows];
   int nwin[kivi::kMaxRows];
-  int64_t total = 0;
   for (int b = 0; b < B; ++b) {
     const int64_t t = r.n.n[b] + (fused ? 1 : 0);
     p.mrows.t[b] = (int32_t)t;
     const kivi::RowSpan rs = kivi::row_span(t, R, fused);
     const int64_t nm = kivi::matrix_main(rs, R);
     nwin[b] = kivi::matrix_window_chunks(t, nm);
-    work[b] = nm / kMatrixBlock + nwin[b];
-    cap[b] = max64(1, ceil_div(work[b], waves));
-    total += work[b];
+    work[b] = nm / kMatrixBlock + 2 * nwin[b];
+    cap[b] = max64(1, ceil_div(nm / kMatrixBlock + nwin[b], waves));
     if (tps_req > 0) {
       const int64_t tps = ceil_div(tps_req, kMatrixBlock) * kMatrixBlock;
       groups[b] = max64(1, ceil_div(nm, tps));
@@ -231,11 +231,8 @@ int plan_matrix_rows(const kivi_cache *c, const Rows &r, int32_t tps_req, int wa
   if (tps_req == 0) {
     const int64_t target = std::min<int64_t>(
         kivi::kMaxRows, max64(B, (int64_t)device_cus() * (8 / waves) / c->n_kv_heads));
-    for (int b = 0; b < B; ++b) {
-      groups[b] = 1 + (total > 0 ? (target - B) * work[b] / total : 0);
-      groups[b] = std::min(groups[b], cap[b]);
-      used += groups[b];
-    }
+    for (int b = 0; b < B; ++b) groups[b] = 1;
+    used = B;
     while (used < target) {
       int best = -1;
       for (int b = 0; b < B; ++b)

@@ -625,32 +625,75 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
 // Window role: tokens [Ta, Tb) = [n_main + 32 chunk, min(t, n_main + 32 chunk + 32))
 // of one slab -- fp16 window tokens and quantized tokens past the last whole
 // block.  The chunk's key data goes to the key buffer and its value data to
-// the value buffer, in one batch of DMA; then each lane scores one token over
-// half of the channels (scalar fp32) and accumulates two output channels.
-template <int NREP, bool MASKED>
-__device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &rs, int64_t n_main,
-                                            int chunk, int slot, int hk, int b, const Lds &L) {
-  const int j = threadIdx.x & 63;
-  const int64_t bh = (int64_t)b * a.H + hk;
-  const int64_t Ta = n_main + (int64_t)kWT * chunk;
-  const int64_t Tb = Ta + kWT < rs.t ? Ta + kWT : rs.t;
-  const int n = (int)(Tb - Ta);
+// the value buffer, in one batch of DMA (window_issue); then each lane
+// scores one token over half of the channels (scalar fp32) and accumulates
+// two output channels (window_role).
+
+// Where a window chunk's data lies.
+struct WinChunk {
+  int64_t bh, Ta, Tb, vq_end, t_pop, wslot;
+  int n, n_qv, n_fv, nqv4, nqv8, lt, u_vs, u_vz, u_vrow;
+  bool kq, kq_now, pop_here, new_here;
+  const uint8_t *rec;
+};
+
+__device__ __forceinline__ WinChunk win_chunk(const DecodeArgs &a, const RowSpan &rs,
+                                              int64_t n_main, int chunk, int hk, int b) {
+  WinChunk c;
+  c.bh = (int64_t)b * a.H + hk;
+  c.Ta = n_main + (int64_t)kWT * chunk;
+  c.Tb = c.Ta + kWT < rs.t ? c.Ta + kWT : rs.t;
+  c.n = (int)(c.Tb - c.Ta);
   // keys: Ta and n_kq are multiples of 32, so the chunk is one whole
   // quantized key group or consists of fp16 window rows
-  const bool kq = Ta < rs.n_kq;
+  c.kq = c.Ta < rs.n_kq;
   // A fused step whose token completes a key block quantizes keys [t - R, t)
   // in this launch: each of those chunks stages its 32 fp16 rows and turns
-  // them into its key group below (kq_now).
-  const bool kq_now = rs.t_new >= 0 && rs.t % a.R == 0 && Ta >= rs.t - a.R;
+  // them into its key group (kq_now).
+  c.kq_now = rs.t_new >= 0 && rs.t % a.R == 0 && c.Ta >= rs.t - a.R;
   // values: [Ta, vq_end) quantized, [vq_end, Tb) fp16
-  const int64_t vq_end = rs.n_vq < Ta ? Ta : (rs.n_vq > Tb ? Tb : rs.n_vq);
-  const int n_qv = (int)(vq_end - Ta), n_fv = (int)(Tb - vq_end);
-  const int nqv4 = (n_qv + 3) / 4;    // 16-byte units of fp32 scales per channel group
-  const int nqv8 = (n_qv + 7) / 8;    // 16-byte units of fp16 zeros per channel group
+  c.vq_end = rs.n_vq < c.Ta ? c.Ta : (rs.n_vq > c.Tb ? c.Tb : rs.n_vq);
+  c.n_qv = (int)(c.vq_end - c.Ta);
+  c.n_fv = (int)(c.Tb - c.vq_end);
+  c.nqv4 = (c.n_qv + 3) / 4;    // 16-byte units of fp32 scales per channel group
+  c.nqv8 = (c.n_qv + 7) / 8;    // 16-byte units of fp16 zeros per channel group
   // the chunk lies in one record (Ta is a multiple of 32), at token lt of it
-  const uint8_t *rec = record_of(a, bh, Ta / kBT);
-  const int lt = (int)(Ta % kBT);
+  c.rec = record_of(a, c.bh, c.Ta / kBT);
+  c.lt = (int)(c.Ta % kBT);
+  // value buffer: codes (2 units per token), scales (4 channel groups x
+  // nqv4 units), fp16 zeros (4 x nqv8 units), then fp16 rows (16 units each)
+  c.u_vs = c.n_qv * 2;
+  c.u_vz = c.u_vs + 4 * c.nqv4;
+  c.u_vrow = c.u_vz + 4 * c.nqv8;
+  // Fused decode step: the value that leaves the window with this token
+  // (t_pop = t_new - R, the last quantized value) and the new token's slot.
+  c.t_pop = rs.t_new >= a.R ? rs.t_new - a.R : -1;
+  c.pop_here = c.t_pop >= c.Ta && c.t_pop < c.vq_end;
+  c.new_here = rs.t_new >= c.Ta && rs.t_new < c.Tb;
+  c.wslot = rs.t_new >= 0 ? rs.t_new % a.R : 0;
+  return c;
+}
 
+// What window_issue reads into registers: the fused step's popped value
+// and new key / value (lane j: channels 2j, 2j + 1), and q (lane j: channels
+// 2j, 2j + 1 of each head).
+template <int NREP>
+struct WinLoads {
+  uint32_t popped, nv, nk;
+  uint32_t q[NREP];
+};
+
+// The loads of one window chunk, issued and not waited for.
+template <int NREP>
+__device__ __forceinline__ WinLoads<NREP> window_issue(const DecodeArgs &a, const RowSpan &rs,
+                                                       int64_t n_main, int chunk, int hk, int b,
+                                                       const Lds &L) {
+  const int j = threadIdx.x & 63;
+  const WinChunk c = win_chunk(a, rs, n_main, chunk, hk, b);
+  const int64_t bh = c.bh, Ta = c.Ta, vq_end = c.vq_end;
+  const int n = c.n, nqv4 = c.nqv4, nqv8 = c.nqv8, lt = c.lt;
+  const bool kq = c.kq, kq_now = c.kq_now;
+  const uint8_t *rec = c.rec;
   // ---- DMA, in 16-byte units.  Key buffer: codes (64 units), scales (32)
   // and fp16 zeros (16), or n fp16 rows (16 units each) -- at most 512 units
   // = 8 KB.
@@ -669,21 +712,21 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
         else
           src = rec + kRecKz + lg * 256 + (u - 96) * 16;
       } else {
+        // row r = u / 16 of the chunk; its 16-byte unit k is stored at unit
+        // (k + r) % 16 of the row's LDS slot, so that lanes reading the same
+        // unit of different rows hit different banks
         const int64_t tok = Ta + u / 16;
-        src = tok == rs.t_new ? a.k_new + (bh * kD + (u % 16) * 8)
-                             : a.k_res + ((bh * a.R + tok % a.R) * kD + (u % 16) * 8);
+        const int k = ((u & 15) - (u >> 4)) & 15;
+        src = tok == rs.t_new ? a.k_new + (bh * kD + k * 8)
+                             : a.k_res + ((bh * a.R + tok % a.R) * kD + k * 8);
       }
       dma16(src, (lds_void *)(kl + (size_t)base * 16));
     }
   }
-  // value buffer: codes (2 units per token), scales (4 channel groups x
-  // nqv4 units), fp16 zeros (4 x nqv8 units), then fp16 rows (16 units each)
-  // -- at most 512
+  // value buffer (at most 512 units)
   char *vl = (char *)L.vs;
-  const int u_vs = n_qv * 2;
-  const int u_vz = u_vs + 4 * nqv4;
-  const int u_vrow = u_vz + 4 * nqv8;
-  const int vu_end = u_vrow + n_fv * 16;
+  const int u_vs = c.u_vs, u_vz = c.u_vz, u_vrow = c.u_vrow;
+  const int vu_end = u_vrow + c.n_fv * 16;
   for (int base = 0; base < vu_end; base += 64) {
     const int u = base + j;
     if (u < vu_end) {
@@ -705,23 +748,40 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
       dma16(src, (lds_void *)(vl + (size_t)base * 16));
     }
   }
-  // Fused decode step.  The value that leaves the window with this token
-  // (t_pop = t_new - R, the last quantized value) is read from its window
-  // slot -- lane j holds channels 2j, 2j + 1 -- and quantized below; the
-  // new token's value and key are read from the inputs.
-  const int64_t t_pop = rs.t_new >= a.R ? rs.t_new - a.R : -1;
-  const bool pop_here = t_pop >= Ta && t_pop < vq_end;
-  const bool new_here = rs.t_new >= Ta && rs.t_new < Tb;
-  const int64_t wslot = rs.t_new >= 0 ? rs.t_new % a.R : 0;   // window slot of the new token
-  uint16_t *slot_v = const_cast<uint16_t *>(a.v_res) + (bh * a.R + wslot) * kD + 2 * j;
-  uint32_t popped = 0, nv = 0, nk = 0;
-  if (pop_here) popped = *(const uint32_t *)slot_v;
-  if (pop_here || new_here) nv = *(const uint32_t *)(a.v_new + bh * kD + 2 * j);
-  if (new_here) nk = *(const uint32_t *)(a.k_new + bh * kD + 2 * j);
+  WinLoads<NREP> ld;
+  ld.popped = ld.nv = ld.nk = 0u;
+  uint16_t *slot_v = const_cast<uint16_t *>(a.v_res) + (bh * a.R + c.wslot) * kD + 2 * j;
+  if (c.pop_here) ld.popped = *(const uint32_t *)slot_v;
+  if (c.pop_here || c.new_here) ld.nv = *(const uint32_t *)(a.v_new + bh * kD + 2 * j);
+  if (c.new_here) ld.nk = *(const uint32_t *)(a.k_new + bh * kD + 2 * j);
+  const uint16_t *q = a.q + ((int64_t)b * a.Hq + hk * NREP) * kD;
+#pragma unroll
+  for (int h = 0; h < NREP; ++h) ld.q[h] = *(const uint32_t *)(q + h * kD + 2 * j);
+  return ld;
+}
+
+template <int NREP, bool MASKED>
+__device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &rs, int64_t n_main,
+                                            int chunk, int slot, int hk, int b, const Lds &L,
+                                            const WinLoads<NREP> &ld) {
+  const int j = threadIdx.x & 63;
+  const WinChunk c = win_chunk(a, rs, n_main, chunk, hk, b);
+  const int64_t bh = c.bh, Ta = c.Ta, t_pop = c.t_pop;
+  const int n = c.n, n_qv = c.n_qv, nqv4 = c.nqv4, nqv8 = c.nqv8;
+  const int u_vs = c.u_vs, u_vz = c.u_vz, u_vrow = c.u_vrow;
+  const bool kq = c.kq, kq_now = c.kq_now, pop_here = c.pop_here, new_here = c.new_here;
+  char *kl = (char *)L.ks;
+  char *vl = (char *)L.vs;
+  uint16_t *slot_v = const_cast<uint16_t *>(a.v_res) + (bh * a.R + c.wslot) * kD + 2 * j;
+  const uint32_t popped = ld.popped, nv = ld.nv, nk = ld.nk;
+  const int64_t wslot = c.wslot;
   // q of the NREP heads, kept in the probability buffer (unused by this role)
   float(*q_s)[kPRow] = L.p;
-  const uint16_t *q = a.q + ((int64_t)b * a.Hq + hk * NREP) * kD;
-  for (int e = j; e < NREP * kD; e += 64) q_s[e / kD][e % kD] = h2f(q[e]);
+#pragma unroll
+  for (int h = 0; h < NREP; ++h) {
+    q_s[h][2 * j] = h2f((uint16_t)(ld.q[h] & 0xFFFFu));
+    q_s[h][2 * j + 1] = h2f((uint16_t)(ld.q[h] >> 16));
+  }
   wait_vm<0>();
   if (pop_here) {
     // KIVI item 3 on the popped value: 16 lanes per 32-channel group, the
@@ -762,15 +822,17 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
     // codes, with the quantizer of the append path.  The codes, scales and
     // zeros replace the rows in LDS in the layout of a staged key group and
     // go to the cache.
-    const uint32_t *rows = (const uint32_t *)kl + j;   // row r at rows[r * 64]
+    // word j of row r (channels 2j, 2j + 1), in the rows' rotated layout
+    const uint32_t *kw = (const uint32_t *)kl;
+    auto row_word = [&](int r) { return kw[r * 64 + ((((j >> 2) + r) & 15) << 2) + (j & 3)]; };
     float mn0, mx0, mn1, mx1;
     {
-      const uint32_t w = rows[0];
+      const uint32_t w = row_word(0);
       mn0 = mx0 = h2f((uint16_t)(w & 0xFFFFu));
       mn1 = mx1 = h2f((uint16_t)(w >> 16));
     }
     for (int r = 1; r < kWT; ++r) {
-      const uint32_t w = rows[r * 64];
+      const uint32_t w = row_word(r);
       const float x0 = h2f((uint16_t)(w & 0xFFFFu)), x1 = h2f((uint16_t)(w >> 16));
       mn0 = x0 < mn0 ? x0 : mn0;
       mx0 = x0 > mx0 ? x0 : mx0;
@@ -780,7 +842,7 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
     const float sc0 = group_scale(mn0, mx0, 2), sc1 = group_scale(mn1, mx1, 2);
     uint32_t cw[4] = {0u, 0u, 0u, 0u};   // channel 2j: words 0, 1; channel 2j + 1: words 2, 3
     for (int r = 0; r < kWT; ++r) {
-      const uint32_t w = rows[r * 64];
+      const uint32_t w = row_word(r);
       const int sh = 2 * (r & 15), hw = r >> 4;
       cw[hw] |= quant_code(h2f((uint16_t)(w & 0xFFFFu)), mn0, sc0, 2) << sh;
       cw[2 + hw] |= quant_code(h2f((uint16_t)(w >> 16)), mn1, sc1, 2) << sh;
@@ -805,30 +867,57 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
 #pragma unroll
   for (int h = 0; h < NREP; ++h) sc[h] = 0.0f;
   if (tj < n) {
+    // 16-byte LDS reads throughout: the key group's words, scales and zeros
+    // and q are the same for all lanes of a half (broadcasts); channels are
+    // summed in increasing order
     if (kq) {
-      const uint32_t *kc = (const uint32_t *)kl + tj / 16;
+      const uint32_t *kc = (const uint32_t *)kl;   // channel c: words 2c, 2c + 1
       const float *ks = (const float *)(kl + 64 * 16);
       const uint16_t *kz = (const uint16_t *)(kl + 96 * 16);
       const int sh = 2 * (tj % 16);
+      const bool hi = tj >= 16;
+#pragma unroll 4
       for (int c = 64 * hf; c < 64 * hf + 64; c += 4) {
+        const uint4 wa = *(const uint4 *)(kc + 2 * c);
+        const uint4 wb = *(const uint4 *)(kc + 2 * c + 4);
+        const uint32_t cw[4] = {hi ? wa.y : wa.x, hi ? wa.w : wa.z, hi ? wb.y : wb.x,
+                                hi ? wb.w : wb.z};
         const f4 s4 = *(const f4 *)(ks + c);
         const uint2 zz = *(const uint2 *)(kz + c);
         const float z4[4] = {h2f((uint16_t)(zz.x & 0xFFFFu)), h2f((uint16_t)(zz.x >> 16)),
                              h2f((uint16_t)(zz.y & 0xFFFFu)), h2f((uint16_t)(zz.y >> 16))};
+        f4 q4[NREP];
+#pragma unroll
+        for (int h = 0; h < NREP; ++h) q4[h] = *(const f4 *)&q_s[h][c];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float code = (float)((kc[(c + u) * 2] >> sh) & 3u);
+          const float code = (float)((cw[u] >> sh) & 3u);
           const float kh = code * s4[u] + z4[u];
 #pragma unroll
-          for (int h = 0; h < NREP; ++h) sc[h] = fmaf(q_s[h][c + u], kh, sc[h]);
+          for (int h = 0; h < NREP; ++h) sc[h] = fmaf(q4[h][u], kh, sc[h]);
         }
       }
     } else {
-      const uint16_t *row = (const uint16_t *)kl + tj * kD;
-      for (int c = 64 * hf; c < 64 * hf + 64; ++c) {
-        const float kh = h2f(row[c]);
+      // row tj, units 8 hf .. 8 hf + 7 (8 channels each), rotated by tj
+      const uint4 *row = (const uint4 *)kl + tj * 16;
 #pragma unroll
-        for (int h = 0; h < NREP; ++h) sc[h] = fmaf(q_s[h][c], kh, sc[h]);
+      for (int k = 8 * hf; k < 8 * hf + 8; ++k) {
+        const uint4 w = row[(k + tj) & 15];
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        const int c = 8 * k;
+        f4 qa[NREP], qb[NREP];
+#pragma unroll
+        for (int h = 0; h < NREP; ++h) {
+          qa[h] = *(const f4 *)&q_s[h][c];
+          qb[h] = *(const f4 *)&q_s[h][c + 4];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t x = ww[e / 2];
+          const float kh = h2f((uint16_t)(e % 2 ? x >> 16 : x & 0xFFFFu));
+#pragma unroll
+          for (int h = 0; h < NREP; ++h) sc[h] = fmaf(e < 4 ? qa[h][e] : qb[h][e - 4], kh, sc[h]);
+        }
       }
     }
   }
@@ -866,23 +955,38 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
   const float *vsc = (const float *)(vl + (size_t)u_vs * 16) + gch * nqv4 * 4;
   const uint16_t *vz = (const uint16_t *)(vl + (size_t)u_vz * 16) + gch * nqv8 * 8;
   const uint16_t *vrow = (const uint16_t *)(vl + (size_t)u_vrow * 16);
-  for (int t = 0; t < n; ++t) {
-    float v0, v1;
-    if (t < n_qv) {
-      const uint32_t w = vc[t * 8 + c0 / 16] >> (2 * (c0 % 16));
-      const float zt = h2f(vz[t]);
-      v0 = (float)(w & 3u) * vsc[t] + zt;
-      v1 = (float)((w >> 2) & 3u) * vsc[t] + zt;
-    } else {
-      const uint32_t hv = *(const uint32_t *)(vrow + (t - n_qv) * kD + c0);
-      v0 = h2f((uint16_t)(hv & 0xFFFFu));
-      v1 = h2f((uint16_t)(hv >> 16));
+  // four tokens per step: their probabilities, scales and zeros in 16- and
+  // 8-byte reads (p_s is 0 for tokens past n, whose values are not read)
+  for (int t0 = 0; t0 < n; t0 += 4) {
+    f4 p4[NREP];
+#pragma unroll
+    for (int h = 0; h < NREP; ++h) p4[h] = *(const f4 *)(p_s + h * kWT + t0);
+    f4 s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    uint2 z2 = make_uint2(0u, 0u);
+    if (t0 < n_qv) {
+      s4 = *(const f4 *)(vsc + t0);
+      z2 = *(const uint2 *)(vz + t0);
     }
 #pragma unroll
-    for (int h = 0; h < NREP; ++h) {
-      const float pt = p_s[h * kWT + t];
-      o[h][0] = fmaf(pt, v0, o[h][0]);
-      o[h][1] = fmaf(pt, v1, o[h][1]);
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + u;
+      float v0 = 0.0f, v1 = 0.0f;
+      if (t < n_qv) {
+        const uint32_t w = vc[t * 8 + c0 / 16] >> (2 * (c0 % 16));
+        const uint32_t zw = u < 2 ? z2.x : z2.y;
+        const float zt = h2f((uint16_t)(u % 2 ? zw >> 16 : zw & 0xFFFFu));
+        v0 = (float)(w & 3u) * s4[u] + zt;
+        v1 = (float)((w >> 2) & 3u) * s4[u] + zt;
+      } else if (t < n) {
+        const uint32_t hv = *(const uint32_t *)(vrow + (t - n_qv) * kD + c0);
+        v0 = h2f((uint16_t)(hv & 0xFFFFu));
+        v1 = h2f((uint16_t)(hv >> 16));
+      }
+#pragma unroll
+      for (int h = 0; h < NREP; ++h) {
+        o[h][0] = fmaf(p4[h][u], v0, o[h][0]);
+        o[h][1] = fmaf(p4[h][u], v1, o[h][1]);
+      }
     }
   }
 #pragma unroll
@@ -979,7 +1083,8 @@ __global__ void __launch_bounds__(MASKED ? 256 : 512)
   int item = draw_item(&sm_ctr, lane);
   while (item < sh.n_skip) {
     const int x = (int)s + item * n_groups;
-    window_role<NREP, MASKED>(a, rs, n_main, x, n_groups + x, hk, b, L);
+    const WinLoads<NREP> ld = window_issue<NREP>(a, rs, n_main, x, hk, b, L);
+    window_role<NREP, MASKED>(a, rs, n_main, x, n_groups + x, hk, b, L, ld);
     wave_lds_sync();   // the LDS reads of the chunk are done
     item = draw_item(&sm_ctr, lane);
   }

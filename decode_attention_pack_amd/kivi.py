@@ -191,6 +191,15 @@ class Cache:
             return [self.n_tokens] * self.B
         return [int(x) for x in self._rows]
 
+    def set_row_tokens(self, counts):
+        """Set every row's token count of a ragged batch (host-side fields of
+        the descriptor; the storage must hold what the counts say)."""
+        if self._rows is None or len(counts) != self.B:
+            raise KiviError(KIVI_ERR_INVALID_ARG, "set_row_tokens needs a ragged cache and B counts")
+        for b, n in enumerate(counts):
+            self._rows[b] = int(n)
+        self.c.n_tokens = max(self._rows)
+
     def reset_row(self, b: int):
         """Empty row b of a ragged batch (host-side count only: later appends
         overwrite what the row's storage held)."""
