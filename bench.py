@@ -134,6 +134,67 @@ def time_pack(w, inp, dev, stream, reps: int = 5):
     return out
 
 
+def select_bytes(w, t: int, sel_union) -> int:
+    """Algorithmic bytes of one kivi_select_attn call at context t: every key
+    (codes, fp32 scales, fp16 zeros; fp16 window rows), the values of the
+    tokens any query head of a KV head selects (sel_union: bool [B][Hkv][t]),
+    q and out."""
+    R, G, D = w.R, w.G, w.D
+    n_kq, n_vq = t - t % R, max(0, t - R)
+    rep = w.Hq // w.Hkv
+    keys = n_kq * D * w.k_bits // 8 + (n_kq // G) * D * 6 + (t - n_kq) * D * 2
+    sel = sel_union.reshape(-1, t)
+    n_q = int(sel[:, :n_vq].sum())          # selected quantized values
+    n_f = int(sel[:, n_vq:].sum())          # selected fp16 values
+    vals = n_q * (D * w.v_bits // 8 + (D // G) * 6) + n_f * D * 2
+    return (keys + rep * D * 6) * w.B * w.Hkv + vals
+
+
+def time_select(w, caches, q, tau: float, stream, n_rounds: int = 5, per_round: int = 40):
+    """kivi_select_attn back to back over the layer replicas: us per call,
+    GB/s on the algorithmic bytes and the selected fraction."""
+    import torch
+
+    from decode_attention_pack_amd import kivi
+    L = len(caches)
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=q.device)
+    ws = kivi.select_workspace(caches[0], w.Hq)
+    nsel = torch.empty((w.B, w.Hq), dtype=torch.int32, device=q.device)
+    t = caches[0].n_tokens
+    words = (t + 31) // 32
+    smask = torch.zeros((w.B, w.Hq, words), dtype=torch.int32, device=q.device)
+    kivi.kivi_select_attn(caches[0], q, tau, out=out, n_selected=nsel, sel_mask=smask,
+                          workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    bits = np.unpackbits(smask.cpu().numpy().view(np.uint32).view(np.uint8), axis=-1,
+                         bitorder="little")[..., :t].astype(bool)
+    union = bits.reshape(w.B, w.Hkv, w.Hq // w.Hkv, t).any(axis=2)
+    n_bytes = select_bytes(w, t, union)
+    calls = [kivi.bind_select_attn(c, q, tau, out, ws, stream=stream) for c in caches]
+    for i in range(2 * L):
+        calls[i % L]()
+    torch.cuda.synchronize()
+    ms = []
+    for r in range(n_rounds):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for j in range(per_round):
+            calls[(r * per_round + j) % L]()
+        e1.record(stream)
+        ms.append((e0, e1))
+    torch.cuda.synchronize()
+    us = [e0.elapsed_time(e1) * 1e3 / per_round for e0, e1 in ms]
+    mean = float(np.mean(us))
+    return {"call": "kivi_select_attn", "tau": tau, "context": t,
+            "us": round(mean, 2),
+            "us_rounds_min_p50_max": [round(float(np.percentile(us, p)), 2) for p in (0, 50, 100)],
+            "GBps": round(n_bytes / mean / 1e3, 1),
+            "bytes_per_call": n_bytes,
+            "selected_fraction_mean": round(float(bits.sum()) / bits.size, 4),
+            "values_read_fraction": round(float(union.sum()) / union.size, 4)}
+
+
 def host_cpu():
     """CPU model and the cores this process may use."""
     model = "unknown"
@@ -230,6 +291,9 @@ def main():
                     help="time a step as kivi_append + kivi_decode_attn instead of kivi_decode_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-pack", action="store_true", help="skip the full-prefill pack pass")
+    ap.add_argument("--select", type=float, default=0.0,
+                    help="also time kivi_select_attn (token selection by attention mass tau, "
+                         "then attention over the selected tokens) on the same replicas")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device-to-device copy of this "
                          "many MiB (a known-size reference for hardware byte counters)")
@@ -430,6 +494,8 @@ def main():
                      "kernel": "kivi_decode_attn launch (split kernel + combine)",
                      "bytes_per_launch": a2_bytes // (n_rounds * per_round)},
     }
+    if args.select > 0.0 and not ragged:
+        line["select"] = time_select(w, caches, q, args.select, stream)
     if not args.no_pack and not ragged:
         del caches, base, appends, decodes, fused_steps
         torch.cuda.empty_cache()

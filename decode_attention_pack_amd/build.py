@@ -14,7 +14,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkivi.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["api.cpp", "pack.hip", "decode_generic.hip", "decode_vector.hip", "decode_matrix.hip"]
+SOURCES = ["api.cpp", "pack.hip", "decode_generic.hip", "decode_vector.hip", "decode_matrix.hip",
+           "select.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

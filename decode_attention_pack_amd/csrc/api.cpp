@@ -792,3 +792,120 @@ int kivi_decode_step(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp
 }
 
 }  // extern "C"
+
+namespace {
+
+// Byte offsets of the sections of kivi_select_attn's workspace: the scores
+// [B][Hq][cap] f32, the per-row selection rules, the partial slots of the
+// attention over the selected tokens (as kivi_decode_attn's); each section
+// 256-byte aligned.
+struct SelectWorkspace {
+  size_t scores, rows, part, total;
+};
+SelectWorkspace select_workspace(const kivi_cache *c, int32_t n_q_heads) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  SelectWorkspace w;
+  const size_t rows = (size_t)c->batch * n_q_heads;
+  w.scores = 0;
+  w.rows = up(rows * c->capacity * sizeof(float));
+  w.part = w.rows + up(rows * sizeof(kivi::SelectRow));
+  w.total = w.part + up(rows * (size_t)max_slots(c, 0) * (c->head_dim + 4) * sizeof(float));
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kivi_select_attn_workspace_bytes(const kivi_cache *c, int32_t n_q_heads) {
+  if (check_cache(c, "kivi_select_attn_workspace_bytes")) return 0;
+  if (n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0) return 0;
+  return select_workspace(c, n_q_heads).total;
+}
+
+int kivi_select_attn(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads,
+                     const float *mask, float tau, float *out, int32_t *n_selected,
+                     uint32_t *sel_mask, void *workspace, size_t workspace_bytes, void *stream) {
+  const char *who = "kivi_select_attn";
+  int rc = check_cache(c, who);
+  if (rc) return rc;
+  if (c->row_tokens)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: ragged batches are not supported", who);
+  if (n_q_heads <= 0 || n_q_heads % c->n_kv_heads != 0)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: n_q_heads %d must be a positive multiple of n_kv_heads %d",
+                who, n_q_heads, c->n_kv_heads);
+  if (!q_fp16 || !out) return fail(KIVI_ERR_INVALID_ARG, "%s: NULL q or out", who);
+  if (!(tau > 0.0f && tau <= 1.0f))
+    return fail(KIVI_ERR_INVALID_ARG, "%s: tau %g outside (0, 1]", who, (double)tau);
+  if (c->n_tokens >= ((int64_t)1 << 27))
+    return fail(KIVI_ERR_INVALID_ARG, "%s: at most 2^27 - 1 tokens", who);
+  const SelectWorkspace ws = select_workspace(c, n_q_heads);
+  if (!workspace || workspace_bytes < ws.total || ((uintptr_t)workspace & 255) != 0)
+    return fail(KIVI_ERR_WORKSPACE, "%s: workspace of %zu bytes (256-byte aligned), %zu needed",
+                who, workspace_bytes, ws.total);
+  kivi::DecodeArgs a{};
+  a.L = layout_of(c);
+  a.k_res = c->k_res;
+  a.v_res = c->v_res;
+  a.q = (const uint16_t *)q_fp16;
+  a.mask = mask;
+  a.out = out;
+  a.B = c->batch;
+  a.H = c->n_kv_heads;
+  a.D = c->head_dim;
+  a.kb = c->k_bits;
+  a.vb = c->v_bits;
+  a.G = c->group;
+  a.R = c->residual;
+  a.Hq = n_q_heads;
+  a.n_rep = n_q_heads / c->n_kv_heads;
+  a.cap = c->capacity;
+  a.t = c->n_tokens;
+  a.t_new = -1;
+  a.n_kq = a.t - a.t % a.R;
+  a.n_vq = max64(0, a.t - a.R);
+  a.sm_scale = 1.0f / sqrtf((float)a.D);
+  char *w = (char *)workspace;
+  a.scores = (float *)(w + ws.scores);
+  kivi::SelectRow *rows = (kivi::SelectRow *)(w + ws.rows);
+  a.sel = rows;
+  a.part = (float *)(w + ws.part);
+  hipStream_t s = (hipStream_t)stream;
+  // the vector kernel where it takes the shape, else the scalar one, both
+  // to score the tokens and to attend over the selected ones; splits as
+  // kivi_decode_attn plans them
+  const bool vec = kivi::decode_vector_supported(a);
+  Plan p;
+  const Rows r = rows_of(c);
+  rc = make_plan(c, n_q_heads, 0, vec ? KIVI_PATH_VECTOR : KIVI_PATH_GENERIC, a, r, p, who);
+  if (rc) return rc;
+  a.S_total = p.S_total;
+  // 1. scores of every token (KIVI item 5's scores); the vector kernel takes
+  // all heads of a KV head in one workgroup when there are 4 or 8
+  if (a.t > 0) {
+    const int64_t units = (int64_t)c->batch * c->n_kv_heads;
+    const bool whole = a.n_rep == 1 || a.n_rep == 4 || a.n_rep == 8;
+    const int step = vec ? kVectorStep : kGenericMinSplit;
+    const int64_t target = vec ? kVectorWorkgroups / (units * (whole ? 1 : a.n_rep / 2))
+                               : kTargetWorkgroups / (units * head_chunks(a.n_rep));
+    const int64_t tps = max64(1, ceil_div(ceil_div(a.t, max64(1, target)), step)) * step;
+    const int n_split = (int)ceil_div(a.t, tps);
+    rc = hip_status(vec ? kivi::launch_scores_vector(a, (int)tps, n_split, s)
+                        : kivi::launch_scores_generic(a, (int)tps, n_split, s),
+                    "kivi_select_attn (scores)");
+    if (rc) return rc;
+  }
+  // 2. the selection of every row
+  rc = hip_status(kivi::launch_select_rows(a, tau, rows, n_selected, sel_mask, s),
+                  "kivi_select_attn (select)");
+  if (rc) return rc;
+  // 3. attention over the selected tokens, then the merge of the splits
+  rc = hip_status(vec ? kivi::launch_selected_vector(a, p.tps_generic, p.n_split_generic, s)
+                      : kivi::launch_selected_generic(a, p.tps_generic, p.n_split_generic, s),
+                  "kivi_select_attn (attention)");
+  if (rc || !p.combine) return rc;
+  return hip_status(kivi::launch_combine(a, s), "kivi_select_attn (combine)");
+}
+
+}  // extern "C"
+

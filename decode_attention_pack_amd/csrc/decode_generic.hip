@@ -40,11 +40,15 @@ __device__ __forceinline__ float wave_sum(float v) {
 // heads per workgroup: the smallest power of two covering the heads per KV
 // head, up to 8, so that MHA shapes do not carry 8 heads' worth of products.
 // A ragged batch (RAGGED): row b holds rows.n[b] tokens; a.t is the mask's
-// row stride.
-template <int NH, bool RAGGED>
+// row stride.  MODE 1 (scores): only the scores s = q . K / sqrt(D) + mask of
+// every token, into a.scores[(b Hq + hq) cap + tau] (no softmax, no values).
+// MODE 2 (selected): attention whose scores are read from a.scores, with
+// -inf for a token that the row's selection rule (a.sel) does not take.
+template <int NH, bool RAGGED, int MODE>
 __global__ void __launch_bounds__(kThreads)
 decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int slot_base,
                       int head_chunks, RowArg<RAGGED> rows) {
+  constexpr bool SCORES = MODE == 1, SELECTED = MODE == 2;
   __shared__ float q_s[NH][256];
   __shared__ float p_s[NH][kChunk];
   __shared__ float stat_s[NH][2];   // new m, alpha
@@ -99,7 +103,14 @@ decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int
     float sc[NH];
 #pragma unroll
     for (int j = 0; j < NH; ++j) sc[j] = 0.0f;
-    if (tau < s1) {
+    if (SELECTED && tau < s1) {
+#pragma unroll
+      for (int j = 0; j < NH; ++j) {
+        const int64_t r = (int64_t)b * a.Hq + hq0 + (j < nh ? j : 0);
+        const float sv = a.scores[r * a.cap + tau];
+        sc[j] = j < nh && select_takes(a.sel[r], sv, tau) ? sv : -INFINITY;
+      }
+    } else if (tau < s1) {
       // key channel c of token tau as attention sees it: code * scale + zero
       // (fp32 multiply, then add) below n_kq, else the fp16 window row; the
       // per-token index arithmetic (group, word, bit offset) is done once
@@ -134,6 +145,12 @@ decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int
     } else {
 #pragma unroll
       for (int j = 0; j < NH; ++j) sc[j] = -INFINITY;
+    }
+    if constexpr (SCORES) {
+      if (tau < s1)
+        for (int j = 0; j < nh; ++j)
+          a.scores[((int64_t)b * a.Hq + hq0 + j) * a.cap + tau] = sc[j];
+      continue;
     }
 #pragma unroll
     for (int j = 0; j < NH; ++j) p_s[j][tid] = sc[j];
@@ -190,6 +207,7 @@ decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int
     __syncthreads();
   }
 
+  if constexpr (SCORES) return;
   // merge the n_par token parities of each channel, then write the partial
   for (int j = 0; j < nh; ++j) {
     red_s[tid] = acc[j];
@@ -299,21 +317,21 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, RowArg<RAGGE
   }
 }
 
-template <bool RAGGED>
+template <bool RAGGED, int MODE>
 static void launch_generic(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t tok_begin,
                            int tps, int slot_base, int head_chunks, const RowArg<RAGGED> &rows) {
   if (a.n_rep == 1)
-    hipLaunchKernelGGL((decode_generic_kernel<1, RAGGED>), grid, dim3(kThreads), 0, s, a,
+    hipLaunchKernelGGL((decode_generic_kernel<1, RAGGED, MODE>), grid, dim3(kThreads), 0, s, a,
                        tok_begin, tps, slot_base, head_chunks, rows);
   else if (a.n_rep == 2)
-    hipLaunchKernelGGL((decode_generic_kernel<2, RAGGED>), grid, dim3(kThreads), 0, s, a,
+    hipLaunchKernelGGL((decode_generic_kernel<2, RAGGED, MODE>), grid, dim3(kThreads), 0, s, a,
                        tok_begin, tps, slot_base, head_chunks, rows);
   else if (a.n_rep <= 4)
-    hipLaunchKernelGGL((decode_generic_kernel<4, RAGGED>), grid, dim3(kThreads), 0, s, a,
+    hipLaunchKernelGGL((decode_generic_kernel<4, RAGGED, MODE>), grid, dim3(kThreads), 0, s, a,
                        tok_begin, tps, slot_base, head_chunks, rows);
   else
-    hipLaunchKernelGGL((decode_generic_kernel<kHeads, RAGGED>), grid, dim3(kThreads), 0, s, a,
-                       tok_begin, tps, slot_base, head_chunks, rows);
+    hipLaunchKernelGGL((decode_generic_kernel<kHeads, RAGGED, MODE>), grid, dim3(kThreads), 0,
+                       s, a, tok_begin, tps, slot_base, head_chunks, rows);
 }
 
 hipError_t launch_decode_generic(const DecodeArgs &a, int64_t tok_begin, int tokens_per_split,
@@ -324,10 +342,31 @@ hipError_t launch_decode_generic(const DecodeArgs &a, int64_t tok_begin, int tok
   const int head_chunks = (a.n_rep + kHeads - 1) / kHeads;
   dim3 grid((unsigned)n_splits, (unsigned)(a.H * head_chunks), (unsigned)a.B);
   if (rows)
-    launch_generic<true>(a, grid, s, tok_begin, tokens_per_split, slot_base, head_chunks, *rows);
+    launch_generic<true, 0>(a, grid, s, tok_begin, tokens_per_split, slot_base, head_chunks,
+                                *rows);
   else
-    launch_generic<false>(a, grid, s, tok_begin, tokens_per_split, slot_base, head_chunks,
-                          NoRows{});
+    launch_generic<false, 0>(a, grid, s, tok_begin, tokens_per_split, slot_base, head_chunks,
+                                 NoRows{});
+  return hipGetLastError();
+}
+
+hipError_t launch_selected_generic(const DecodeArgs &a, int tokens_per_split, int n_splits,
+                                   hipStream_t s) {
+  if (n_splits <= 0) return hipSuccess;
+  if (!a.scores || !a.sel) return hipErrorInvalidValue;
+  const int head_chunks = (a.n_rep + kHeads - 1) / kHeads;
+  dim3 grid((unsigned)n_splits, (unsigned)(a.H * head_chunks), (unsigned)a.B);
+  launch_generic<false, 2>(a, grid, s, 0, tokens_per_split, 0, head_chunks, NoRows{});
+  return hipGetLastError();
+}
+
+hipError_t launch_scores_generic(const DecodeArgs &a, int tokens_per_split, int n_splits,
+                                 hipStream_t s) {
+  if (n_splits <= 0) return hipSuccess;
+  if (!a.scores) return hipErrorInvalidValue;
+  const int head_chunks = (a.n_rep + kHeads - 1) / kHeads;
+  dim3 grid((unsigned)n_splits, (unsigned)(a.H * head_chunks), (unsigned)a.B);
+  launch_generic<false, 1>(a, grid, s, 0, tokens_per_split, 0, head_chunks, NoRows{});
   return hipGetLastError();
 }
 

@@ -129,11 +129,17 @@ __device__ __forceinline__ float uniform(float v) {
 // grid: (n_splits, H * head_chunks, B); block: 256 (4 waves).  A ragged
 // batch (RAGGED): row b holds rows.n[b] tokens; a.t is the mask's row
 // stride.
-template <int KB, int VB, int NH, bool RAGGED>
+// MODE 1 (scores): only the scores s = q . K / sqrt(D) + mask of every
+// token, into a.scores[(b Hq + hq) cap + tau] (no softmax, no values).
+// MODE 2 (selected): attention whose scores are read from a.scores, with -inf
+// for a token that the row's selection rule (a.sel) does not take; no keys
+// are read.
+template <int KB, int VB, int NH, bool RAGGED, int MODE>
 __global__ void __launch_bounds__(kVThreads)
     __attribute__((amdgpu_waves_per_eu(2)))   // two waves per SIMD: the compiler may use 256 VGPRs
 decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int direct,
                      RowArg<RAGGED> rows) {
+  constexpr bool SCORES = MODE == 1, SELECTED = MODE == 2;
   __shared__ float red_s[kVWaves][NH][kVD];
   __shared__ float stat_s[kVWaves][NH][2];
 
@@ -194,7 +200,13 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
   const uint32_t rec = (uint32_t)L.rec;
   const char *kres = (const char *)(a.k_res + bh * a.R * kVD);
   const char *vres = (const char *)(a.v_res + bh * a.R * kVD);
-  const char *mrow = a.mask ? (const char *)(a.mask + (int64_t)b * a.t) : nullptr;
+  // (selected attention: the mask is part of the stored scores)
+  const char *mrow = a.mask && !SELECTED ? (const char *)(a.mask + (int64_t)b * a.t) : nullptr;
+  SelectRow selr[NH];
+  if constexpr (SELECTED) {
+#pragma unroll
+    for (int j = 0; j < NH; ++j) selr[j] = a.sel[(int64_t)b * a.Hq + hq0 + j];
+  }
   const uint32_t kc_lane = (uint32_t)L.kc + (uint32_t)lane * (2 * KB) * 4u;
   const uint32_t ks_lane = (uint32_t)L.ks + (uint32_t)lane * 8u;
   const uint32_t kz_lane = (uint32_t)L.kz + (uint32_t)lane * 4u;
@@ -214,17 +226,30 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
     float2 ks, kz;
     uint32_t vw[2][VWQ];
     float vs[2], vz[2], mk[2];
+    float ss[SELECTED ? NH : 1][2];   // stored scores (selected attention)
   };
   auto fetch = [&](int g, Raw &r) {
     const uint32_t r0 = (uint32_t)(g >> 2) * rec;        // record of the group
     const uint32_t lg = (uint32_t)(g & 3);               // group within the record
-    load_words<KB / 2>((const uint32_t *)(slab + (r0 + lg * (kVD * KB * 4u) + kc_lane)), r.kw);
-    r.ks = *(const float2 *)(slab + (r0 + lg * (kVD * 4u) + ks_lane));
-    const uint32_t zz = *(const uint32_t *)(slab + (r0 + lg * (kVD * 2u) + kz_lane));
-    r.kz = make_float2(h2f((uint16_t)(zz & 0xFFFFu)), h2f((uint16_t)(zz >> 16)));
+    if constexpr (!SELECTED) {
+      load_words<KB / 2>((const uint32_t *)(slab + (r0 + lg * (kVD * KB * 4u) + kc_lane)), r.kw);
+      r.ks = *(const float2 *)(slab + (r0 + lg * (kVD * 4u) + ks_lane));
+      const uint32_t zz = *(const uint32_t *)(slab + (r0 + lg * (kVD * 2u) + kz_lane));
+      r.kz = make_float2(h2f((uint16_t)(zz & 0xFFFFu)), h2f((uint16_t)(zz >> 16)));
+    }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const uint32_t tl = lg * kVG + 16 * hh + tq;       // token within the record
+      const uint32_t tau = (uint32_t)(g * kVG + 16 * hh + tq);
+      if constexpr (SELECTED) {
+        // groups below g_end lie inside the capacity, and so inside the row
+#pragma unroll
+        for (int j = 0; j < NH; ++j)
+          r.ss[j][hh] = a.scores[((int64_t)b * a.Hq + hq0 + j) * a.cap + tau];
+      } else {
+        r.mk[hh] = mrow ? *(const float *)(mrow + (uint32_t)min((int)tau, t_all - 1) * 4u) : 0.0f;
+      }
+      if constexpr (SCORES) continue;
       const uint32_t *src = (const uint32_t *)(slab + (r0 + tl * (kVD * VB / 8u) + vc_lane));
       if constexpr (VWQ == 4) {
         const uint4 v = *(const uint4 *)src;
@@ -239,69 +264,94 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
       }
       r.vs[hh] = *(const float *)(slab + (r0 + vs_lane + tl * 4u));
       r.vz[hh] = h2f(*(const uint16_t *)(slab + (r0 + vz_lane + tl * 2u)));
-      const uint32_t tau = (uint32_t)(g * kVG + 16 * hh + tq);
-      r.mk[hh] = mrow ? *(const float *)(mrow + (uint32_t)min((int)tau, t_all - 1) * 4u) : 0.0f;
     }
   };
 
   // one 32-token group: scores, online softmax update, value accumulation
   auto process = [&](int gi, const Raw &cur) __attribute__((always_inline)) {
     const int t0 = gi * kVG;
-    const bool quantized = t0 < n_kq;     // n_kq is a multiple of the group size
-    float qs0[NH], qs1[NH], qz[NH];
-#pragma unroll
-    for (int j = 0; j < NH; ++j) {
-      qs0[j] = q0[j] * cur.ks.x;
-      qs1[j] = q1[j] * cur.ks.y;
-      qz[j] = fmaf(q1[j], cur.kz.y, q0[j] * cur.kz.x);
-    }
-    // fp16 key window: token tau sits in row tau mod R; R is a multiple of
-    // the group size, so the group's tokens sit in consecutive rows
-    const int row0 = quantized ? 0 : (int)((uint32_t)t0 % (uint32_t)R);
-
     float sc[NH][2];
+    if constexpr (SELECTED) {
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      float part[NH][16];
-      if (quantized) {
+      for (int hh = 0; hh < 2; ++hh) {
+        const int tau = t0 + 16 * hh + tq;
 #pragma unroll
-        for (int j = 0; j < NH; ++j)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) part[j][e] = qz[j];
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch) {
-#pragma unroll
-          for (int wi = 0; wi < KWH; ++wi) {
-            float f[KPW];
-            unpack_word<KB>(cur.kw[ch * KB + hh * KWH + wi], f);
-#pragma unroll
-            for (int k = 0; k < KPW; ++k)
-#pragma unroll
-              for (int j = 0; j < NH; ++j)
-                part[j][wi * KPW + k] =
-                    fmaf(ch ? qs1[j] : qs0[j], f[k], part[j][wi * KPW + k]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int tau = t0 + 16 * hh + e;
-          // rows past the split end are inside the window array; their
-          // products are dropped
-          const uint32_t kk =
-              *(const uint32_t *)(kres + ((uint32_t)(row0 + 16 * hh + e) * (kVD * 2u) + kr_lane));
-          const float k0 = tau < s1 ? h2f((uint16_t)(kk & 0xFFFFu)) : 0.0f;
-          const float k1 = tau < s1 ? h2f((uint16_t)(kk >> 16)) : 0.0f;
-#pragma unroll
-          for (int j = 0; j < NH; ++j) part[j][e] = fmaf(q1[j], k1, q0[j] * k0);
+        for (int j = 0; j < NH; ++j) {
+          const float sv = cur.ss[j][hh];
+          sc[j][hh] = tau < s1 && select_takes(selr[j], sv, tau) ? sv : -INFINITY;
         }
       }
-      const bool valid = t0 + 16 * hh + tq < s1;
+    } else {
+      const bool quantized = t0 < n_kq;     // n_kq is a multiple of the group size
+      float qs0[NH], qs1[NH], qz[NH];
 #pragma unroll
       for (int j = 0; j < NH; ++j) {
-        const float v = reduce_tokens(part[j], lane) + cur.mk[hh];
-        sc[j][hh] = valid ? v : -INFINITY;
+        qs0[j] = q0[j] * cur.ks.x;
+        qs1[j] = q1[j] * cur.ks.y;
+        qz[j] = fmaf(q1[j], cur.kz.y, q0[j] * cur.kz.x);
       }
+      // fp16 key window: token tau sits in row tau mod R; R is a multiple of
+      // the group size, so the group's tokens sit in consecutive rows
+      const int row0 = quantized ? 0 : (int)((uint32_t)t0 % (uint32_t)R);
+
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        float part[NH][16];
+        if (quantized) {
+#pragma unroll
+          for (int j = 0; j < NH; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) part[j][e] = qz[j];
+#pragma unroll
+          for (int ch = 0; ch < 2; ++ch) {
+#pragma unroll
+            for (int wi = 0; wi < KWH; ++wi) {
+              float f[KPW];
+              unpack_word<KB>(cur.kw[ch * KB + hh * KWH + wi], f);
+#pragma unroll
+              for (int k = 0; k < KPW; ++k)
+#pragma unroll
+                for (int j = 0; j < NH; ++j)
+                  part[j][wi * KPW + k] =
+                      fmaf(ch ? qs1[j] : qs0[j], f[k], part[j][wi * KPW + k]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int tau = t0 + 16 * hh + e;
+            // rows past the split end are inside the window array; their
+            // products are dropped
+            const uint32_t kk =
+                *(const uint32_t *)(kres + ((uint32_t)(row0 + 16 * hh + e) * (kVD * 2u) + kr_lane));
+            const float k0 = tau < s1 ? h2f((uint16_t)(kk & 0xFFFFu)) : 0.0f;
+            const float k1 = tau < s1 ? h2f((uint16_t)(kk >> 16)) : 0.0f;
+#pragma unroll
+            for (int j = 0; j < NH; ++j) part[j][e] = fmaf(q1[j], k1, q0[j] * k0);
+          }
+        }
+        const bool valid = t0 + 16 * hh + tq < s1;
+#pragma unroll
+        for (int j = 0; j < NH; ++j) {
+          const float v = reduce_tokens(part[j], lane) + cur.mk[hh];
+          sc[j][hh] = valid ? v : -INFINITY;
+        }
+      }
+    }
+    if constexpr (SCORES) {
+      // every token's score sits in the four lanes of its tq; one writes it
+      if ((lane & 3) == 0) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int tau = t0 + 16 * hh + tq;
+          if (tau < s1) {
+#pragma unroll
+            for (int j = 0; j < NH; ++j)
+              a.scores[((int64_t)b * a.Hq + hq0 + j) * a.cap + tau] = sc[j][hh];
+          }
+        }
+      }
+      return;
     }
 
     // online softmax of this wave over the group's 32 tokens
@@ -380,6 +430,7 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
     process(gi, rb);
     gi += kVWaves;
   }
+  if constexpr (SCORES) return;
 
   // Per wave: fold in the zero-point sum, then sum acc over the 16 token
   // lanes of each channel quarter (lane bits 5..2).  Bits 5 and 4 scatter
@@ -463,31 +514,45 @@ bool decode_vector_supported(const DecodeArgs &a) {
 // One query head per KV head: NH = 1.  An even number: NH = 2, and n_rep / 2
 // workgroups per (split, slab), each for two of the heads (four heads in one
 // workgroup would not fit two waves per SIMD).
-template <int KB, int VB, bool RAGGED>
+template <int KB, int VB, bool RAGGED, int MODE>
 static void launch_bits(const DecodeArgs &a, dim3 grid, int tps, int direct, hipStream_t s,
                         const RowArg<RAGGED> &rows) {
   if (a.n_rep == 1) {
-    hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 1, RAGGED>), grid, dim3(kVThreads), 0, s,
-                       a, tps, 1, direct, rows);
+    hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 1, RAGGED, MODE>), grid, dim3(kVThreads),
+                       0, s, a, tps, 1, direct, rows);
   } else {
+    if constexpr (MODE == 1) {
+      // scores only: no value accumulators, so one workgroup takes every
+      // head of the KV head and reads its keys once
+      if (a.n_rep == 4) {
+        hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 4, RAGGED, MODE>), grid,
+                           dim3(kVThreads), 0, s, a, tps, 1, direct, rows);
+        return;
+      }
+      if (a.n_rep == 8) {
+        hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 8, RAGGED, MODE>), grid,
+                           dim3(kVThreads), 0, s, a, tps, 1, direct, rows);
+        return;
+      }
+    }
     const int chunks = a.n_rep / 2;
     grid.y *= chunks;
-    hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 2, RAGGED>), grid, dim3(kVThreads), 0, s,
-                       a, tps, chunks, direct, rows);
+    hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 2, RAGGED, MODE>), grid, dim3(kVThreads),
+                       0, s, a, tps, chunks, direct, rows);
   }
 }
 
-template <bool RAGGED>
+template <bool RAGGED, int MODE>
 static void launch_all_bits(const DecodeArgs &a, dim3 grid, int tps, int direct, hipStream_t s,
                             const RowArg<RAGGED> &rows) {
   if (a.kb == 2 && a.vb == 2)
-    launch_bits<2, 2, RAGGED>(a, grid, tps, direct, s, rows);
+    launch_bits<2, 2, RAGGED, MODE>(a, grid, tps, direct, s, rows);
   else if (a.kb == 2)
-    launch_bits<2, 4, RAGGED>(a, grid, tps, direct, s, rows);
+    launch_bits<2, 4, RAGGED, MODE>(a, grid, tps, direct, s, rows);
   else if (a.vb == 2)
-    launch_bits<4, 2, RAGGED>(a, grid, tps, direct, s, rows);
+    launch_bits<4, 2, RAGGED, MODE>(a, grid, tps, direct, s, rows);
   else
-    launch_bits<4, 4, RAGGED>(a, grid, tps, direct, s, rows);
+    launch_bits<4, 4, RAGGED, MODE>(a, grid, tps, direct, s, rows);
 }
 
 // With a single split (n_splits == 1) the kernel writes the normalized
@@ -501,9 +566,29 @@ hipError_t launch_decode_vector(const DecodeArgs &a, int tokens_per_split, int n
   dim3 grid((unsigned)n_splits, (unsigned)a.H, (unsigned)a.B);
   const int direct = n_splits == 1;
   if (rows)
-    launch_all_bits<true>(a, grid, tokens_per_split, direct, s, *rows);
+    launch_all_bits<true, 0>(a, grid, tokens_per_split, direct, s, *rows);
   else
-    launch_all_bits<false>(a, grid, tokens_per_split, direct, s, NoRows{});
+    launch_all_bits<false, 0>(a, grid, tokens_per_split, direct, s, NoRows{});
+  return hipGetLastError();
+}
+
+hipError_t launch_selected_vector(const DecodeArgs &a, int tokens_per_split, int n_splits,
+                                  hipStream_t s) {
+  if (n_splits <= 0) return hipSuccess;
+  if (!decode_vector_supported(a) || tokens_per_split % kVG != 0 || !a.scores || !a.sel)
+    return hipErrorInvalidValue;
+  dim3 grid((unsigned)n_splits, (unsigned)a.H, (unsigned)a.B);
+  launch_all_bits<false, 2>(a, grid, tokens_per_split, n_splits == 1, s, NoRows{});
+  return hipGetLastError();
+}
+
+hipError_t launch_scores_vector(const DecodeArgs &a, int tokens_per_split, int n_splits,
+                                hipStream_t s) {
+  if (n_splits <= 0) return hipSuccess;
+  if (!decode_vector_supported(a) || tokens_per_split % kVG != 0 || !a.scores)
+    return hipErrorInvalidValue;
+  dim3 grid((unsigned)n_splits, (unsigned)a.H, (unsigned)a.B);
+  launch_all_bits<false, 1>(a, grid, tokens_per_split, 0, s, NoRows{});
   return hipGetLastError();
 }
 

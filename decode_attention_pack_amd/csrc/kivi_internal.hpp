@@ -53,6 +53,24 @@ hipError_t launch_append_one_rows(const uint16_t *k_new, const uint16_t *v_new, 
                                   uint16_t *v_res, int64_t BH, int H, int R,
                                   const RowCounts &rows, const Layout &L, hipStream_t s);
 
+// The selection rule of one (b, hq) row: a token is selected when its score
+// key (an order-preserving map of the float, select_key) is above `key`, or
+// equal to it with index <= `cut`.
+struct SelectRow {
+  uint32_t key;
+  int32_t cut;
+  float m;          // the row's largest score (-inf: nothing selected)
+  int32_t count;    // tokens selected
+};
+__device__ __forceinline__ uint32_t select_key(float s) {
+  const uint32_t u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ bool select_takes(const SelectRow &r, float s, int64_t tau) {
+  const uint32_t k = select_key(s);
+  return s > -INFINITY && (k > r.key || (k == r.key && tau <= r.cut));
+}
+
 // Everything the decode kernels read.
 struct DecodeArgs {
   Layout L;              // the packed store
@@ -78,6 +96,11 @@ struct DecodeArgs {
   const uint16_t *k_new;
   const uint16_t *v_new;
   int64_t t_new;
+  // Scores-only launches: s = q . K / sqrt(D) + mask of token tau of
+  // (b, hq) at scores[(b Hq + hq) cap + tau].  Selected-attention launches
+  // read them there, and the selection rule of row (b, hq) at sel[b Hq + hq].
+  float *scores;
+  const SelectRow *sel;
 };
 
 // Scalar kernel over tokens [tok_begin, t): `n_splits` splits of
@@ -128,6 +151,29 @@ template <bool RAGGED>
 using MatrixRowArg = typename std::conditional<RAGGED, MatrixRows, NoRows>::type;
 hipError_t launch_decode_matrix_rows(const DecodeArgs &a, const MatrixRows &rows, int n_shares,
                                      hipStream_t s);
+
+// The scores of every token (DecodeArgs::scores), in splits of
+// tokens_per_split tokens: the vector kernel's shapes, and any shape.
+hipError_t launch_scores_vector(const DecodeArgs &a, int tokens_per_split, int n_splits,
+                                hipStream_t s);
+hipError_t launch_scores_generic(const DecodeArgs &a, int tokens_per_split, int n_splits,
+                                 hipStream_t s);
+
+// Token selection by attention mass on the scores (select.hip): per (b, hq)
+// row, the smallest set of tokens in decreasing score order (equal scores by
+// increasing index) whose softmax mass reaches tau.
+// sel_mask (optional) gets bit tau % 32 of word tau / 32 of its row's
+// ceil(t / 32) words for the selected tokens.
+hipError_t launch_select_rows(const DecodeArgs &a, float tau, SelectRow *rows,
+                              int32_t *n_selected, uint32_t *sel_mask, hipStream_t s);
+// Attention over the selected tokens of every row (a.scores, a.sel): the
+// scores are read instead of computed, and a token the row's rule does not
+// select scores -inf; otherwise as launch_decode_vector /
+// launch_decode_generic.
+hipError_t launch_selected_vector(const DecodeArgs &a, int tokens_per_split, int n_splits,
+                                  hipStream_t s);
+hipError_t launch_selected_generic(const DecodeArgs &a, int tokens_per_split, int n_splits,
+                                   hipStream_t s);
 
 // Log-sum-exp merge of the S_total partial slots into `out`.  With
 // `slots`, the rows of batch row b merge their first slots->n[b] slots, and

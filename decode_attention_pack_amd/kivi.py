@@ -26,6 +26,7 @@ EXPORTED = ("kivi_record_bytes", "kivi_pack_keys", "kivi_pack_values", "kivi_app
             "kivi_append_row", "kivi_decode_attn", "kivi_decode_attn_ex",
             "kivi_decode_attn_workspace_bytes",
             "kivi_decode_attn_workspace_bytes_ex", "kivi_decode_step", "kivi_decode_attn_noalloc",
+            "kivi_select_attn", "kivi_select_attn_workspace_bytes",
             "kivi_status_string", "kivi_last_error")
 TOKENS_PER_RECORD = 128
 MAX_RAGGED_ROWS = 256
@@ -83,6 +84,11 @@ def lib():
     L.kivi_decode_attn_workspace_bytes.restype = sz
     L.kivi_decode_attn_workspace_bytes_ex.argtypes = [ctypes.POINTER(CCache), i32, i32, i32]
     L.kivi_decode_attn_workspace_bytes_ex.restype = sz
+    L.kivi_select_attn.argtypes = [ctypes.POINTER(CCache), P, i32, P, ctypes.c_float, P, P, P, P,
+                                   sz, P]
+    L.kivi_select_attn.restype = ctypes.c_int
+    L.kivi_select_attn_workspace_bytes.argtypes = [ctypes.POINTER(CCache), i32]
+    L.kivi_select_attn_workspace_bytes.restype = sz
     L.kivi_status_string.argtypes = [ctypes.c_int]
     L.kivi_status_string.restype = ctypes.c_char_p
     L.kivi_last_error.argtypes = []
@@ -309,6 +315,31 @@ def kivi_decode_step(cache: Cache, k_new, v_new, q, mask=None, out=None, workspa
     return out
 
 
+def kivi_select_attn(cache: Cache, q, tau: float, mask=None, out=None, n_selected=None,
+                     sel_mask=None, workspace=None, stream=None):
+    """Token selection by attention mass (smallest top-score set reaching tau)
+    and attention over the selected tokens; returns out.  n_selected (int32
+    [B][Hq]) and sel_mask (int32 [B][Hq][ceil(t/32)], the bits as uint32)
+    are optional outputs."""
+    B, Hq, D = q.shape
+    qp = _dev(q, torch.float16, (cache.B, Hq, cache.D), "q")
+    mp = None
+    if mask is not None:
+        mp = _dev(mask, torch.float32, (cache.B, cache.n_tokens), "mask")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    op = _dev(out, torch.float32, (cache.B, Hq, cache.D), "out")
+    np_ = None if n_selected is None else _dev(n_selected, torch.int32, (cache.B, Hq), "n_selected")
+    words = (cache.n_tokens + 31) // 32
+    sp = None if sel_mask is None else _dev(sel_mask, torch.int32, (cache.B, Hq, words), "sel_mask")
+    if workspace is None:
+        workspace = select_workspace(cache, Hq)
+    wp = _dev(workspace, torch.uint8, None, "workspace")
+    _check(lib().kivi_select_attn(ctypes.byref(cache.c), qp, Hq, mp, ctypes.c_float(tau), op, np_,
+                                  sp, wp, workspace.numel(), _stream(stream)))
+    return out
+
+
 class BoundCall:
     """A library call whose arguments were checked and marshalled once.
 
@@ -347,6 +378,26 @@ def bind_decode_attn(cache: Cache, q, out, workspace, tokens_per_split=0, path=K
     return BoundCall(lib().kivi_decode_attn_ex,
                      [ctypes.byref(cache.c), qp, Hq, None, op, wp, workspace.numel(),
                       tokens_per_split, path, _stream(stream)], (cache, q, out, workspace))
+
+
+def bind_select_attn(cache: Cache, q, tau: float, out, workspace, n_selected=None,
+                     stream=None) -> BoundCall:
+    """Bound kivi_select_attn (no mask, no selection bits)."""
+    Hq = q.shape[1]
+    qp = _dev(q, torch.float16, (cache.B, Hq, cache.D), "q")
+    op = _dev(out, torch.float32, (cache.B, Hq, cache.D), "out")
+    np_ = None if n_selected is None else _dev(n_selected, torch.int32, (cache.B, Hq), "n_selected")
+    wp = _dev(workspace, torch.uint8, None, "workspace")
+    return BoundCall(lib().kivi_select_attn,
+                     [ctypes.byref(cache.c), qp, Hq, None, ctypes.c_float(tau), op, np_, None, wp,
+                      workspace.numel(), _stream(stream)], (cache, q, out, workspace, n_selected))
+
+
+def select_workspace(cache: Cache, n_q_heads: int):
+    n = int(lib().kivi_select_attn_workspace_bytes(ctypes.byref(cache.c), n_q_heads))
+    if n == 0:
+        raise KiviError(KIVI_ERR_INVALID_ARG, "invalid workspace query")
+    return torch.empty(n, dtype=torch.uint8, device=cache.blocks.device)
 
 
 def bind_decode_step(cache: Cache, k_new, v_new, q, out, workspace, stream=None) -> BoundCall:

@@ -246,6 +246,39 @@ int kivi_decode_step(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp
                      const void *q_fp16, int32_t n_q_heads, const float *mask,
                      float *out, void *workspace, size_t workspace_bytes, void *stream);
 
+/* A second workload on the packed cache: token selection by attention mass
+ * and attention over the selected tokens, after the web page "HCAttention:
+ * Extreme KV Cache Compression via Heterogeneous Attention Computing for
+ * LLMs" (a review), section "What carries the argument": approximate scores
+ * from quantized keys (Eq. 3), here the KIVI scores over the packed cache,
+ * and the smallest prefix of the tokens sorted by score whose mass reaches
+ * tau (Eq. 4); the output over the selected set (Eq. 5) renormalized, as the
+ * review's major comment 2 asks to state.  For every (b, hq), with s_j = q .
+ * K_j / sqrt(D) + mask[b][j] as in kivi_decode_attn and a = softmax(s):
+ *   S   = the smallest set of tokens, taken in decreasing order of s (equal
+ *         scores by increasing token index), whose mass sum_S a reaches
+ *         tau; tokens of mass zero (-inf scores) are never selected, and when
+ *         the others do not reach tau they are all selected;
+ *   out = sum_{j in S} a_j V_j / sum_{j in S} a_j.
+ * The selection is per call (per query); nothing leaves the cache.  Masses
+ * are summed in fixed point (units of 2^-36 of the largest e^(s - max)), so
+ * the selection is deterministic; a token whose mass is below 2^-37 of the
+ * largest counts as mass zero.  Uniform caches (row_tokens NULL) with fewer
+ * than 2^27 tokens.
+ *   tau         in (0, 1].
+ *   q_fp16, mask, out as for kivi_decode_attn.
+ *   n_selected  (device) int32 [B][n_q_heads] or NULL: |S| of each row.
+ *   sel_mask    (device) uint32 [B][n_q_heads][ceil(t / 32)] or NULL: bit
+ *               j % 32 of word j / 32 set when token j is in S.
+ *   workspace   (device, 256-byte aligned) at least
+ *               kivi_select_attn_workspace_bytes() bytes. */
+int kivi_select_attn(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads,
+                     const float *mask, float tau, float *out, int32_t *n_selected,
+                     uint32_t *sel_mask, void *workspace, size_t workspace_bytes, void *stream);
+/* Bytes of workspace kivi_select_attn needs for this cache shape at any
+ * n_tokens up to the capacity (0 on invalid arguments). */
+size_t kivi_select_attn_workspace_bytes(const kivi_cache *c, int32_t n_q_heads);
+
 /* Static description of a status code. */
 const char *kivi_status_string(int status);
 /* Detail of the last failing call on this thread ("" if none). */

@@ -255,3 +255,28 @@ def test_ragged_rejects(L):
     assert L.kivi_decode_attn_ex(ctypes.byref(c), FAKE, 1, None, FAKE, FAKE, big, 64, 2,
                                  None) == -1
     assert b"tokens_per_split" in L.kivi_last_error()
+
+
+def test_select_rejects(L):
+    """kivi_select_attn: tau outside (0, 1], a ragged cache, a NULL q, a small
+    or misaligned workspace -- rejected on the host."""
+    c = _cache(n_tokens=100)
+    ws = L.kivi_select_attn_workspace_bytes(ctypes.byref(c), 2)
+    assert ws > 0
+    big = 1 << 34
+    W = ctypes.c_void_p(0x10000)
+    for tau in (0.0, -0.5, 1.5, float("nan")):
+        assert L.kivi_select_attn(ctypes.byref(c), FAKE, 2, None, tau, FAKE, None, None, W, big,
+                                  None) == -1
+    assert L.kivi_select_attn(ctypes.byref(c), None, 2, None, 0.9, FAKE, None, None, W, big,
+                              None) == -1
+    assert L.kivi_select_attn(ctypes.byref(c), FAKE, 3, None, 0.9, FAKE, None, None, W, big,
+                              None) == -1
+    assert L.kivi_select_attn(ctypes.byref(c), FAKE, 2, None, 0.9, FAKE, None, None, W, ws - 1,
+                              None) == -3
+    assert L.kivi_select_attn(ctypes.byref(c), FAKE, 2, None, 0.9, FAKE, None, None,
+                              ctypes.c_void_p(0x10010), big, None) == -3
+    r, arr = _ragged([10, 20])
+    assert L.kivi_select_attn(ctypes.byref(r), FAKE, 2, None, 0.9, FAKE, None, None, W, big,
+                              None) == -1
+    assert b"ragged" in L.kivi_last_error()
