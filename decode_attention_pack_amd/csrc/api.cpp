@@ -85,6 +85,13 @@ int check_cache(const kivi_cache *c, const char *who) {
   }
   if (!c->blocks || !c->k_res || !c->v_res)
     return fail(KIVI_ERR_INVALID_ARG, "%s: a cache array pointer is NULL", who);
+  if (c->page_table) {
+    if (((uintptr_t)c->page_table & 3) != 0)
+      return fail(KIVI_ERR_INVALID_ARG, "%s: page_table must be 4-byte aligned", who);
+    if (c->n_pages <= 0 || c->n_pages > ((int64_t)1 << 40) / c->n_kv_heads)
+      return fail(KIVI_ERR_INVALID_ARG, "%s: n_pages %lld outside [1, 2^40 / n_kv_heads]", who,
+                  (long long)c->n_pages);
+  }
   if (((uintptr_t)c->blocks & 15) != 0 || ((uintptr_t)c->k_res & 15) != 0 ||
       ((uintptr_t)c->v_res & 15) != 0)
     return fail(KIVI_ERR_INVALID_ARG, "%s: blocks, k_res and v_res must be 16-byte aligned", who);
@@ -92,7 +99,12 @@ int check_cache(const kivi_cache *c, const char *who) {
 }
 
 kivi::Layout layout_of(const kivi_cache *c) {
-  return kivi::make_layout(c->blocks, c->head_dim, c->k_bits, c->v_bits, c->group, c->capacity);
+  kivi::Layout L =
+      kivi::make_layout(c->blocks, c->head_dim, c->k_bits, c->v_bits, c->group, c->capacity);
+  L.pt = c->page_table;
+  L.n_pages = c->n_pages;
+  L.H = c->n_kv_heads;
+  return L;
 }
 
 // Token counts of the rows of a checked cache: per row (ragged) or n_tokens
@@ -134,7 +146,10 @@ kivi_cache row_view(const kivi_cache *c, int32_t b, int64_t t) {
   v.batch = 1;
   v.n_tokens = t;
   v.row_tokens = nullptr;
-  v.blocks = c->blocks + slabs * (c->capacity / kivi::kRecTokens) * (int64_t)rb;
+  if (c->page_table)   // the same page pool; the row's line of the table
+    v.page_table = c->page_table + (int64_t)b * (c->capacity / kivi::kRecTokens);
+  else
+    v.blocks = c->blocks + slabs * (c->capacity / kivi::kRecTokens) * (int64_t)rb;
   v.k_res = c->k_res + slabs * c->residual * c->head_dim;
   v.v_res = c->v_res + slabs * c->residual * c->head_dim;
   return v;

@@ -174,17 +174,28 @@ struct DmaOffsets {
 };
 
 // Start of record `blk` (tokens [128 blk, 128 blk + 128)) of slab bh.
+// A paged cache (PAGED) finds it through the page table: record h of page
+// pt[b nrec + blk], the page index clamped into the pool.  The paged form is
+// a separate instantiation so that the contiguous one keeps its registers.
+template <bool PAGED>
 __device__ __forceinline__ const uint8_t *record_of(const DecodeArgs &a, int64_t bh, int64_t blk) {
-  return a.L.blocks + (bh * a.L.nrec + blk) * (int64_t)kRecBytes;
+  if constexpr (!PAGED) {
+    return a.L.blocks + (bh * a.L.nrec + blk) * (int64_t)kRecBytes;
+  } else {
+    const uint32_t b = (uint32_t)bh / (uint32_t)a.H, h = (uint32_t)bh - b * (uint32_t)a.H;
+    int64_t p = a.L.pt[(int64_t)b * a.L.nrec + blk];
+    p = p < 0 ? 0 : (p >= a.L.n_pages ? a.L.n_pages - 1 : p);
+    return a.L.blocks + (p * a.H + h) * (int64_t)kRecBytes;
+  }
 }
 
 // Key part of block `blk` (tokens [128 blk, 128 blk + 128)) of slab bh:
 // kStageDma DMA instructions, plus 2 for the mask when there is one.
-template <bool MASKED>
+template <bool MASKED, bool PAGED>
 __device__ __forceinline__ void stage_keys(const DecodeArgs &a, int64_t bh, int64_t blk,
                                            KStage *s, float *mask_s, const DmaOffsets &o,
                                            int lane) {
-  const uint8_t *rec = record_of(a, bh, blk);
+  const uint8_t *rec = record_of<PAGED>(a, bh, blk);
 #pragma unroll
   for (int i = 0; i < 4; ++i) dma16nt(rec + kRecKc + i * 1024, o.lin, (lds_void *)(s->kc + i * 256));
 #pragma unroll
@@ -200,9 +211,10 @@ __device__ __forceinline__ void stage_keys(const DecodeArgs &a, int64_t bh, int6
 }
 
 // Value part of block `blk`: kStageDma DMA instructions.
+template <bool PAGED>
 __device__ __forceinline__ void stage_values(const DecodeArgs &a, int64_t bh, int64_t blk,
                                              VStage *s, const DmaOffsets &o) {
-  const uint8_t *rec = record_of(a, bh, blk);
+  const uint8_t *rec = record_of<PAGED>(a, bh, blk);
 #pragma unroll
   for (int i = 0; i < 4; ++i) dma16nt(rec + kRecVc + i * 1024, o.lin, (lds_void *)(s->vc + i * 256));
 #pragma unroll
@@ -336,7 +348,7 @@ struct BlockShare {
 // continuing with the blocks the wave draws, accumulated into one partial
 // per query head, left in the wave's probability buffer: row h holds acc[128]
 // of head h, then m (natural-log units) and l.
-template <int NREP, bool MASKED>
+template <int NREP, bool MASKED, bool PAGED>
 __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare &sh,
                                            int64_t first, int hk, int b, const Lds &L,
                                            KStage *__restrict__ kbuf,
@@ -378,8 +390,8 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
          (lds_void *)&L.p[0][0]);
   {
     const int64_t blk = sh.b0 + (first + sh.rot) % sh.nb;
-    stage_keys<MASKED>(a, bh, blk, kbuf, L.mask, dmo, lane);
-    stage_values(a, bh, blk, vbuf, dmo);
+    stage_keys<MASKED, PAGED>(a, bh, blk, kbuf, L.mask, dmo, lane);
+    stage_values<PAGED>(a, bh, blk, vbuf, dmo);
   }
   wait_vm<KDMA + kStageDma>();   // q
 
@@ -474,7 +486,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
     }
     // every read of the key part has completed: request the next one
     wait_regs(xk);
-    if constexpr (has_next) stage_keys<MASKED>(a, bh, nxt, kbuf, L.mask, dmo, lane);
+    if constexpr (has_next) stage_keys<MASKED, PAGED>(a, bh, nxt, kbuf, L.mask, dmo, lane);
 
     bz = group_sum(bz);
     if (kg == 0) L.bias[i] = bz;
@@ -575,7 +587,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
     }
     // every read of the value part has completed: request the next one
     wait_regs(xv);
-    if constexpr (has_next) stage_values(a, bh, nxt, vbuf, dmo);
+    if constexpr (has_next) stage_values<PAGED>(a, bh, nxt, vbuf, dmo);
 
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -637,6 +649,7 @@ struct WinChunk {
   const uint8_t *rec;
 };
 
+template <bool PAGED>
 __device__ __forceinline__ WinChunk win_chunk(const DecodeArgs &a, const RowSpan &rs,
                                               int64_t n_main, int chunk, int hk, int b) {
   WinChunk c;
@@ -658,7 +671,7 @@ __device__ __forceinline__ WinChunk win_chunk(const DecodeArgs &a, const RowSpan
   c.nqv4 = (c.n_qv + 3) / 4;    // 16-byte units of fp32 scales per channel group
   c.nqv8 = (c.n_qv + 7) / 8;    // 16-byte units of fp16 zeros per channel group
   // the chunk lies in one record (Ta is a multiple of 32), at token lt of it
-  c.rec = record_of(a, c.bh, c.Ta / kBT);
+  c.rec = record_of<PAGED>(a, c.bh, c.Ta / kBT);
   c.lt = (int)(c.Ta % kBT);
   // value buffer: codes (2 units per token), scales (4 channel groups x
   // nqv4 units), fp16 zeros (4 x nqv8 units), then fp16 rows (16 units each)
@@ -684,12 +697,12 @@ struct WinLoads {
 };
 
 // The loads of one window chunk, issued and not waited for.
-template <int NREP>
+template <int NREP, bool PAGED>
 __device__ __forceinline__ WinLoads<NREP> window_issue(const DecodeArgs &a, const RowSpan &rs,
                                                        int64_t n_main, int chunk, int hk, int b,
                                                        const Lds &L) {
   const int j = threadIdx.x & 63;
-  const WinChunk c = win_chunk(a, rs, n_main, chunk, hk, b);
+  const WinChunk c = win_chunk<PAGED>(a, rs, n_main, chunk, hk, b);
   const int64_t bh = c.bh, Ta = c.Ta, vq_end = c.vq_end;
   const int n = c.n, nqv4 = c.nqv4, nqv8 = c.nqv8, lt = c.lt;
   const bool kq = c.kq, kq_now = c.kq_now;
@@ -760,12 +773,12 @@ __device__ __forceinline__ WinLoads<NREP> window_issue(const DecodeArgs &a, cons
   return ld;
 }
 
-template <int NREP, bool MASKED>
+template <int NREP, bool MASKED, bool PAGED>
 __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &rs, int64_t n_main,
                                             int chunk, int slot, int hk, int b, const Lds &L,
                                             const WinLoads<NREP> &ld) {
   const int j = threadIdx.x & 63;
-  const WinChunk c = win_chunk(a, rs, n_main, chunk, hk, b);
+  const WinChunk c = win_chunk<PAGED>(a, rs, n_main, chunk, hk, b);
   const int64_t bh = c.bh, Ta = c.Ta, t_pop = c.t_pop;
   const int n = c.n, n_qv = c.n_qv, nqv4 = c.nqv4, nqv8 = c.nqv8;
   const int u_vs = c.u_vs, u_vz = c.u_vz, u_vrow = c.u_vrow;
@@ -774,6 +787,8 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
   char *vl = (char *)L.vs;
   uint16_t *slot_v = const_cast<uint16_t *>(a.v_res) + (bh * a.R + c.wslot) * kD + 2 * j;
   const uint32_t popped = ld.popped, nv = ld.nv, nk = ld.nk;
+  // the chunk's record (it lies in one), where a fused step's cache writes go
+  uint8_t *recw = const_cast<uint8_t *>(c.rec);
   const int64_t wslot = c.wslot;
   // q of the NREP heads, kept in the probability buffer (unused by this role)
   float(*q_s)[kPRow] = L.p;
@@ -800,14 +815,14 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
     const int gch = j >> 4;
     if ((j & 7) == 0) {
       ((uint32_t *)vl)[xr * 8 + (j >> 3)] = w;
-      a.L.value_codes(bh, t_pop)[j >> 3] = w;
+      ((uint32_t *)(recw + kRecVc) + (t_pop % kBT) * 8)[j >> 3] = w;
     }
     if ((j & 15) == 0) {
       const uint16_t zh = f2h_bits(mn);
       ((float *)(vl + (size_t)u_vs * 16))[gch * nqv4 * 4 + xr] = sc;
       ((uint16_t *)(vl + (size_t)u_vz * 16))[gch * nqv8 * 8 + xr] = zh;
-      *a.L.value_scale(bh, t_pop, gch) = sc;
-      *a.L.value_zero(bh, t_pop, gch) = zh;
+      ((float *)(recw + kRecVs))[gch * kBT + t_pop % kBT] = sc;
+      ((uint16_t *)(recw + kRecVz))[gch * kBT + t_pop % kBT] = zh;
     }
     // the slot now takes the new value (this lane read its old contents above)
     *(uint32_t *)slot_v = nv;
@@ -854,9 +869,10 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
     *(float2 *)((float *)(kl + 64 * 16) + 2 * j) = make_float2(sc0, sc1);
     *((uint32_t *)(kl + 96 * 16) + j) = z2;
     const int64_t grp = Ta / kG;
-    *(uint4 *)a.L.key_codes(bh, grp, 2 * j) = c4;
-    *(float2 *)a.L.key_scale(bh, grp, 2 * j) = make_float2(sc0, sc1);
-    *(uint32_t *)a.L.key_zero(bh, grp, 2 * j) = z2;
+    const int lg = (int)(grp % (kBT / kG));   // the group within the record
+    *(uint4 *)((uint32_t *)(recw + kRecKc) + (lg * kD + 2 * j) * 2) = c4;
+    *(float2 *)((float *)(recw + kRecKs) + lg * kD + 2 * j) = make_float2(sc0, sc1);
+    *(uint32_t *)((uint16_t *)(recw + kRecKz) + lg * kD + 2 * j) = z2;
   }
   wave_lds_sync();
 
@@ -1019,7 +1035,7 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
 // The masked variant holds the block's mask in registers as well; it may
 // use more than half the register file rather than spill, since a spill
 // reload inside the block loop would wait for every DMA in flight.
-template <int NREP, bool MASKED, bool RAGGED>
+template <int NREP, bool MASKED, bool RAGGED, bool PAGED>
 __global__ void __launch_bounds__(MASKED ? 256 : 512)
     __attribute__((amdgpu_waves_per_eu(MASKED ? 1 : 2)))
     decode_matrix_kernel(DecodeArgs a, int64_t n_main_all, int n_groups_all, int n_window_all,
@@ -1083,12 +1099,12 @@ __global__ void __launch_bounds__(MASKED ? 256 : 512)
   int item = draw_item(&sm_ctr, lane);
   while (item < sh.n_skip) {
     const int x = (int)s + item * n_groups;
-    const WinLoads<NREP> ld = window_issue<NREP>(a, rs, n_main, x, hk, b, L);
-    window_role<NREP, MASKED>(a, rs, n_main, x, n_groups + x, hk, b, L, ld);
+    const WinLoads<NREP> ld = window_issue<NREP, PAGED>(a, rs, n_main, x, hk, b, L);
+    window_role<NREP, MASKED, PAGED>(a, rs, n_main, x, n_groups + x, hk, b, L, ld);
     wave_lds_sync();   // the LDS reads of the chunk are done
     item = draw_item(&sm_ctr, lane);
   }
-  block_role<NREP, MASKED>(a, sh, item - sh.n_skip, hk, b, L, &sm_k[w], &sm_v[w]);
+  block_role<NREP, MASKED, PAGED>(a, sh, item - sh.n_skip, hk, b, L, &sm_k[w], &sm_v[w]);
 
   // The W partials of the workgroup's waves, merged with the log-sum-exp
   // rule into partial slot s of the slab: thread e takes channel e % 128 of
@@ -1181,25 +1197,34 @@ int decode_matrix_window_chunks(const DecodeArgs &a, int64_t n_main) {
 
 int decode_matrix_waves(const DecodeArgs &a) { return a.mask ? 4 : 8; }
 
-template <int NREP, bool RAGGED>
+template <int NREP, bool RAGGED, bool PAGED>
 static void launch_rep(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
                        int n_groups, int n_window, const MatrixRowArg<RAGGED> &rows) {
   if (a.mask)
-    hipLaunchKernelGGL((decode_matrix_kernel<NREP, true, RAGGED>), grid, dim3(256), 0, s, a,
-                       n_main, n_groups, n_window, rows);
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, true, RAGGED, PAGED>), grid, dim3(256), 0, s,
+                       a, n_main, n_groups, n_window, rows);
   else
-    hipLaunchKernelGGL((decode_matrix_kernel<NREP, false, RAGGED>), grid, dim3(512), 0, s, a,
-                       n_main, n_groups, n_window, rows);
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, false, RAGGED, PAGED>), grid, dim3(512), 0, s,
+                       a, n_main, n_groups, n_window, rows);
+}
+
+template <bool RAGGED, bool PAGED>
+static void launch_paged(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
+                         int n_groups, int n_window, const MatrixRowArg<RAGGED> &rows) {
+  switch (a.n_rep) {
+    case 1: launch_rep<1, RAGGED, PAGED>(a, grid, s, n_main, n_groups, n_window, rows); break;
+    case 2: launch_rep<2, RAGGED, PAGED>(a, grid, s, n_main, n_groups, n_window, rows); break;
+    default: launch_rep<4, RAGGED, PAGED>(a, grid, s, n_main, n_groups, n_window, rows); break;
+  }
 }
 
 template <bool RAGGED>
 static void launch_reps(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
                         int n_groups, int n_window, const MatrixRowArg<RAGGED> &rows) {
-  switch (a.n_rep) {
-    case 1: launch_rep<1, RAGGED>(a, grid, s, n_main, n_groups, n_window, rows); break;
-    case 2: launch_rep<2, RAGGED>(a, grid, s, n_main, n_groups, n_window, rows); break;
-    default: launch_rep<4, RAGGED>(a, grid, s, n_main, n_groups, n_window, rows); break;
-  }
+  if (a.L.pt)
+    launch_paged<RAGGED, true>(a, grid, s, n_main, n_groups, n_window, rows);
+  else
+    launch_paged<RAGGED, false>(a, grid, s, n_main, n_groups, n_window, rows);
 }
 
 hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int n_groups,

@@ -134,7 +134,7 @@ __device__ __forceinline__ float uniform(float v) {
 // MODE 2 (selected): attention whose scores are read from a.scores, with -inf
 // for a token that the row's selection rule (a.sel) does not take; no keys
 // are read.
-template <int KB, int VB, int NH, bool RAGGED, int MODE>
+template <int KB, int VB, int NH, bool RAGGED, int MODE, bool PAGED>
 __global__ void __launch_bounds__(kVThreads)
     __attribute__((amdgpu_waves_per_eu(2)))   // two waves per SIMD: the compiler may use 256 VGPRs
 decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int direct,
@@ -228,13 +228,37 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
     float vs[2], vz[2], mk[2];
     float ss[SELECTED ? NH : 1][2];   // stored scores (selected attention)
   };
+  // paged cache: the row's line of the page table and the head's record in
+  // a page, set once.  The entries of 64 records from pg_first on sit one per
+  // lane in pg_v (one vector load per 64 records); a record's entry is read
+  // from its lane, so no fetch waits on a scalar load of the table.
+  const int32_t *pg_row = PAGED ? L.pt + (int64_t)b * L.nrec : nullptr;
+  const char *pg_base = PAGED ? (const char *)L.blocks + (int64_t)h * L.rec : nullptr;
+  const int64_t pg_stride = (int64_t)a.H * L.rec;
+  int pg_first = 0;
+  int32_t pg_v = 0;
+  auto pg_load = [&](int first) {
+    pg_first = first;
+    pg_v = pg_row[min(first + lane, (int)L.nrec - 1)];
+  };
+  if constexpr (PAGED) pg_load((s0 / kVG) >> 2);
   auto fetch = [&](int g, Raw &r) {
-    const uint32_t r0 = (uint32_t)(g >> 2) * rec;        // record of the group
+    // the group's record: an offset into the slab, or a page of a paged cache
+    const char *recp = slab;
+    uint32_t r0 = (uint32_t)(g >> 2) * rec;
+    if constexpr (PAGED) {
+      const int ri = g >> 2;
+      if (ri - pg_first >= 64) pg_load(ri);
+      int64_t p = __builtin_amdgcn_readlane(pg_v, ri - pg_first);
+      p = p < 0 ? 0 : (p >= L.n_pages ? L.n_pages - 1 : p);
+      recp = pg_base + p * pg_stride;
+      r0 = 0u;
+    }
     const uint32_t lg = (uint32_t)(g & 3);               // group within the record
     if constexpr (!SELECTED) {
-      load_words<KB / 2>((const uint32_t *)(slab + (r0 + lg * (kVD * KB * 4u) + kc_lane)), r.kw);
-      r.ks = *(const float2 *)(slab + (r0 + lg * (kVD * 4u) + ks_lane));
-      const uint32_t zz = *(const uint32_t *)(slab + (r0 + lg * (kVD * 2u) + kz_lane));
+      load_words<KB / 2>((const uint32_t *)(recp + (r0 + lg * (kVD * KB * 4u) + kc_lane)), r.kw);
+      r.ks = *(const float2 *)(recp + (r0 + lg * (kVD * 4u) + ks_lane));
+      const uint32_t zz = *(const uint32_t *)(recp + (r0 + lg * (kVD * 2u) + kz_lane));
       r.kz = make_float2(h2f((uint16_t)(zz & 0xFFFFu)), h2f((uint16_t)(zz >> 16)));
     }
 #pragma unroll
@@ -250,7 +274,7 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
         r.mk[hh] = mrow ? *(const float *)(mrow + (uint32_t)min((int)tau, t_all - 1) * 4u) : 0.0f;
       }
       if constexpr (SCORES) continue;
-      const uint32_t *src = (const uint32_t *)(slab + (r0 + tl * (kVD * VB / 8u) + vc_lane));
+      const uint32_t *src = (const uint32_t *)(recp + (r0 + tl * (kVD * VB / 8u) + vc_lane));
       if constexpr (VWQ == 4) {
         const uint4 v = *(const uint4 *)src;
         r.vw[hh][0] = v.x;
@@ -262,8 +286,8 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
         r.vw[hh][0] = v.x;
         r.vw[hh][1] = v.y;
       }
-      r.vs[hh] = *(const float *)(slab + (r0 + vs_lane + tl * 4u));
-      r.vz[hh] = h2f(*(const uint16_t *)(slab + (r0 + vz_lane + tl * 2u)));
+      r.vs[hh] = *(const float *)(recp + (r0 + vs_lane + tl * 4u));
+      r.vz[hh] = h2f(*(const uint16_t *)(recp + (r0 + vz_lane + tl * 2u)));
     }
   };
 
@@ -514,45 +538,56 @@ bool decode_vector_supported(const DecodeArgs &a) {
 // One query head per KV head: NH = 1.  An even number: NH = 2, and n_rep / 2
 // workgroups per (split, slab), each for two of the heads (four heads in one
 // workgroup would not fit two waves per SIMD).
-template <int KB, int VB, bool RAGGED, int MODE>
+template <int KB, int VB, bool RAGGED, int MODE, bool PAGED>
 static void launch_bits(const DecodeArgs &a, dim3 grid, int tps, int direct, hipStream_t s,
                         const RowArg<RAGGED> &rows) {
   if (a.n_rep == 1) {
-    hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 1, RAGGED, MODE>), grid, dim3(kVThreads),
+    hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 1, RAGGED, MODE, PAGED>), grid, dim3(kVThreads),
                        0, s, a, tps, 1, direct, rows);
   } else {
     if constexpr (MODE == 1) {
       // scores only: no value accumulators, so one workgroup takes every
       // head of the KV head and reads its keys once
       if (a.n_rep == 4) {
-        hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 4, RAGGED, MODE>), grid,
+        hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 4, RAGGED, MODE, PAGED>), grid,
                            dim3(kVThreads), 0, s, a, tps, 1, direct, rows);
         return;
       }
       if (a.n_rep == 8) {
-        hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 8, RAGGED, MODE>), grid,
+        hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 8, RAGGED, MODE, PAGED>), grid,
                            dim3(kVThreads), 0, s, a, tps, 1, direct, rows);
         return;
       }
     }
     const int chunks = a.n_rep / 2;
     grid.y *= chunks;
-    hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 2, RAGGED, MODE>), grid, dim3(kVThreads),
+    hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 2, RAGGED, MODE, PAGED>), grid, dim3(kVThreads),
                        0, s, a, tps, chunks, direct, rows);
   }
 }
 
+template <bool RAGGED, int MODE, bool PAGED>
+static void launch_bits_paged(const DecodeArgs &a, dim3 grid, int tps, int direct, hipStream_t s,
+                              const RowArg<RAGGED> &rows) {
+  if (a.kb == 2 && a.vb == 2)
+    launch_bits<2, 2, RAGGED, MODE, PAGED>(a, grid, tps, direct, s, rows);
+  else if (a.kb == 2)
+    launch_bits<2, 4, RAGGED, MODE, PAGED>(a, grid, tps, direct, s, rows);
+  else if (a.vb == 2)
+    launch_bits<4, 2, RAGGED, MODE, PAGED>(a, grid, tps, direct, s, rows);
+  else
+    launch_bits<4, 4, RAGGED, MODE, PAGED>(a, grid, tps, direct, s, rows);
+}
+
+// A paged cache takes its own instantiations (PAGED), so that the
+// contiguous ones keep their registers.
 template <bool RAGGED, int MODE>
 static void launch_all_bits(const DecodeArgs &a, dim3 grid, int tps, int direct, hipStream_t s,
                             const RowArg<RAGGED> &rows) {
-  if (a.kb == 2 && a.vb == 2)
-    launch_bits<2, 2, RAGGED, MODE>(a, grid, tps, direct, s, rows);
-  else if (a.kb == 2)
-    launch_bits<2, 4, RAGGED, MODE>(a, grid, tps, direct, s, rows);
-  else if (a.vb == 2)
-    launch_bits<4, 2, RAGGED, MODE>(a, grid, tps, direct, s, rows);
+  if (a.L.pt)
+    launch_bits_paged<RAGGED, MODE, true>(a, grid, tps, direct, s, rows);
   else
-    launch_bits<4, 4, RAGGED, MODE>(a, grid, tps, direct, s, rows);
+    launch_bits_paged<RAGGED, MODE, false>(a, grid, tps, direct, s, rows);
 }
 
 // With a single split (n_splits == 1) the kernel writes the normalized

@@ -33,15 +33,32 @@ constexpr int kRecTokens = 128;
 // bytes.  Key groups (KIVI item 2, G tokens of one channel) and value groups
 // (KIVI item 3, G channels of one token) both lie inside one record, since G
 // divides 128.
+// Paged cache (pt set): `blocks` is a pool of n_pages pages of H records (one
+// per KV head), and record j of slab (b, h) is record h of page
+// pt[b nrec + j].  A page index outside [0, n_pages) is clamped into the
+// pool: a caller error, whose results are unspecified, never makes an access
+// leave it.
 struct Layout {
   uint8_t *blocks;
   int64_t rec;        // bytes per record
   int64_t nrec;       // records per slab (capacity / 128)
   int32_t kc, ks, kz, vc, vs, vz;   // section offsets in bytes
   int32_t D, G, kb, vb;
+  const int32_t *pt;  // page table [B][nrec] (device) or nullptr
+  int64_t n_pages;
+  int32_t H;          // KV heads: records per page
 
+  // record of 128-token block j of slab bh
+  __host__ __device__ __forceinline__ uint8_t *record_at(int64_t bh, int64_t j) const {
+    if (pt == nullptr) return blocks + (bh * nrec + j) * rec;
+    // batch x heads fits 16 bits (the ABI's limit): 32-bit division
+    const uint32_t b = (uint32_t)bh / (uint32_t)H, h = (uint32_t)bh - b * (uint32_t)H;
+    int64_t p = pt[(int64_t)b * nrec + j];
+    p = p < 0 ? 0 : (p >= n_pages ? n_pages - 1 : p);
+    return blocks + (p * H + (int64_t)h) * rec;
+  }
   __host__ __device__ __forceinline__ uint8_t *record(int64_t bh, int64_t tau) const {
-    return blocks + (bh * nrec + tau / kRecTokens) * rec;
+    return record_at(bh, tau / kRecTokens);
   }
   // key group g (tokens g G .. g G + G - 1) of channel c
   __host__ __device__ __forceinline__ int64_t key_index(int64_t g, int c) const {

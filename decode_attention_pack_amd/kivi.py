@@ -46,6 +46,7 @@ class CCache(ctypes.Structure):
         ("capacity", ctypes.c_int64), ("n_tokens", ctypes.c_int64),
         ("blocks", ctypes.c_void_p), ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
         ("row_tokens", ctypes.POINTER(ctypes.c_int64)),
+        ("page_table", ctypes.c_void_p), ("n_pages", ctypes.c_int64),
     ]
 
 
@@ -130,16 +131,23 @@ def record_bytes(D, kb, vb, G) -> int:
     return n
 
 
-def layout_shapes(B, H, D, kb, vb, G, R, cap):
-    """Shapes of the cache arrays (include/kivi.h storage layout)."""
-    return {
-        "blocks": (B, H, cap // TOKENS_PER_RECORD, record_bytes(D, kb, vb, G)),
+def layout_shapes(B, H, D, kb, vb, G, R, cap, pages=None):
+    """Shapes of the cache arrays (include/kivi.h storage layout); with
+    `pages`, a paged cache: a pool of that many pages of H records and a page
+    table [B][cap/128]."""
+    rb = record_bytes(D, kb, vb, G)
+    shapes = {
+        "blocks": (B, H, cap // TOKENS_PER_RECORD, rb) if pages is None else (pages, H, rb),
         "k_res": (B, H, R, D),
         "v_res": (B, H, R, D),
     }
+    if pages is not None:
+        shapes["page_table"] = (B, cap // TOKENS_PER_RECORD)
+    return shapes
 
 
-_DT = {"blocks": torch.uint8, "k_res": torch.float16, "v_res": torch.float16}
+_DT = {"blocks": torch.uint8, "k_res": torch.float16, "v_res": torch.float16,
+       "page_table": torch.int32}
 _ORDER = ("blocks", "k_res", "v_res")
 
 
@@ -148,21 +156,27 @@ class Cache:
 
     ``blocks`` is the record array as raw bytes; ``k_res`` / ``v_res`` are the
     fp16 windows.  ``ragged=True`` gives a ragged batch: each row keeps its own
-    token count (``row_tokens``), all rows starting empty."""
+    token count (``row_tokens``), all rows starting empty.  ``pages=N`` gives a
+    paged cache: ``blocks`` is a pool of N pages of H records, and
+    ``page_table`` (int32 [B][cap/128], zero-filled) names the page of each
+    128-token block of each row; the caller fills it."""
 
     def __init__(self, batch, n_kv_heads, head_dim, k_bits, v_bits, group, residual, capacity,
-                 device="cuda", arrays=None, ragged=False):
+                 device="cuda", arrays=None, ragged=False, pages=None):
         self.B, self.H, self.D = batch, n_kv_heads, head_dim
         self.kb, self.vb, self.G, self.R, self.cap = k_bits, v_bits, group, residual, capacity
         if capacity % TOKENS_PER_RECORD:
             raise KiviError(KIVI_ERR_INVALID_ARG,
                             f"capacity {capacity} must be a multiple of {TOKENS_PER_RECORD}")
         shapes = layout_shapes(batch, n_kv_heads, head_dim, k_bits, v_bits, group, residual,
-                               capacity)
+                               capacity, pages)
         if arrays is None:
             arrays = {n: torch.empty(s, dtype=_DT[n], device=device) for n, s in shapes.items()}
-        for n in _ORDER:
+            if pages is not None:
+                arrays["page_table"].zero_()
+        for n in shapes:
             _dev(arrays[n], _DT[n], shapes[n], n)
+        self.pages = pages
         self.arrays = arrays
         self._rows = None
         if ragged:
@@ -173,7 +187,9 @@ class Cache:
         self.c = CCache(batch, n_kv_heads, head_dim, k_bits, v_bits, group, residual, capacity, 0,
                         *[arrays[n].data_ptr() for n in _ORDER],
                         ctypes.cast(self._rows, ctypes.POINTER(ctypes.c_int64))
-                        if ragged else None)
+                        if ragged else None,
+                        arrays["page_table"].data_ptr() if pages is not None else None,
+                        pages or 0)
 
     def __getattr__(self, name):
         arrays = self.__dict__.get("arrays")

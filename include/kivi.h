@@ -93,12 +93,25 @@ enum {
  * the rules above with t = row_tokens[b], and batch <= 256.  n_tokens is
  * then not read: every call that changes the counts writes the longest one
  * into it.  The records and windows of row b, taken alone, form a cache of
- * batch 1 (blocks + b * n_kv_heads * (capacity/128) * RB, k_res and v_res +
- * b * n_kv_heads * R * D elements), so a row's storage is independent of
- * the others'.  A row is emptied by setting its count to 0 (nothing on the
+ * batch 1 (blocks + b * n_kv_heads * (capacity/128) * RB unless paged, k_res
+ * and v_res + b * n_kv_heads * R * D elements), so a row's storage is
+ * independent of the others'.  A row is emptied by setting its count to 0 (nothing on the
  * device changes; later appends overwrite what it held).  A mask for a
  * ragged batch is f32 [B][max_b row_tokens[b]] (plus one for
- * kivi_decode_step); entries past a row's length are not read. */
+ * kivi_decode_step); entries past a row's length are not read.
+ *
+ * Paged cache (page_table != NULL): `blocks` is a pool of n_pages pages, a
+ * page being n_kv_heads consecutive records (one per KV head) of one
+ * 128-token block of one row; record j of slab (b, h) is record h of page
+ * page_table[b * (capacity/128) + j], i.e. at byte (page * n_kv_heads + h) *
+ * RB of `blocks`.  Rows then hold only the pages their tokens use, in any
+ * order, so that short rows of a ragged batch do not hold a long row's
+ * memory (the same serving setting).  The caller keeps, for every row, the
+ * entries of the blocks its tokens use -- and of the block an append writes
+ * into -- pointing at pages no other (row, block) uses.  The table lives in device memory and is not
+ * checked on the host: an entry outside [0, n_pages) is clamped into the
+ * pool (a caller error whose results are unspecified; no access leaves the
+ * pool).  page_table 4-byte aligned; n_pages * n_kv_heads * RB < 2^62. */
 typedef struct kivi_cache {
   int32_t batch;
   int32_t n_kv_heads;
@@ -113,6 +126,8 @@ typedef struct kivi_cache {
   uint16_t *k_res;
   uint16_t *v_res;
   int64_t *row_tokens; /* NULL, or host [batch]: per-row token counts      */
+  const int32_t *page_table; /* NULL, or (device) int32 [batch][capacity/128] */
+  int64_t n_pages;     /* pages in `blocks` when page_table is set         */
 } kivi_cache;
 
 /* Bytes of one 128-token record for a shape (0 if the shape is invalid);

@@ -64,10 +64,28 @@ def b16(a: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(a).view(np.uint16)
 
 
+def contiguous_blocks(c) -> np.ndarray:
+    """A device cache's records in the contiguous order [B][H][cap/128][RB]; a
+    paged cache's pages are gathered through its page table (blocks whose
+    entry is outside the pool stay zero)."""
+    blocks = host(c.blocks)
+    if getattr(c, "pages", None) is None:
+        return blocks
+    pt = host(c.page_table)
+    nrec = c.cap // kivi.TOKENS_PER_RECORD
+    out = np.zeros((c.B, c.H, nrec, blocks.shape[-1]), np.uint8)
+    for b in range(c.B):
+        for j in range(nrec):
+            p = int(pt[b, j])
+            if 0 <= p < blocks.shape[0]:
+                out[b, :, j] = blocks[p]
+    return out
+
+
 def logical(c) -> dict:
     """The logical arrays (k_codes, k_scale, k_zero, v_codes, v_scale, v_zero)
     of a device cache, re-indexed on the host from its records."""
-    return oracle.unpack_records(host(c.blocks), c.B, c.H, c.cap, c.D, c.kb, c.vb, c.G)
+    return oracle.unpack_records(contiguous_blocks(c), c.B, c.H, c.cap, c.D, c.kb, c.vb, c.G)
 
 
 def compare_slab(g: kivi.Cache, b: int, h: int, o: oracle.Cache, ob: int = 0, oh: int = 0,

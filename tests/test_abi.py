@@ -280,3 +280,19 @@ def test_select_rejects(L):
     assert L.kivi_select_attn(ctypes.byref(r), FAKE, 2, None, 0.9, FAKE, None, None, W, big,
                               None) == -1
     assert b"ragged" in L.kivi_last_error()
+
+
+def test_paged_rejects(L):
+    """A paged cache: a misaligned page table or a pool of no pages is
+    rejected on the host."""
+    c = _cache(n_tokens=100)
+    c.page_table = 0x1002
+    c.n_pages = 10
+    big = 1 << 34
+    assert L.kivi_decode_attn(ctypes.byref(c), FAKE, 2, None, FAKE, FAKE, big, None) == -1
+    assert b"page_table" in L.kivi_last_error()
+    c.page_table = 0x1000
+    for n in (0, -3, 1 << 45):
+        c.n_pages = n
+        assert L.kivi_decode_attn(ctypes.byref(c), FAKE, 2, None, FAKE, FAKE, big, None) == -1
+        assert b"n_pages" in L.kivi_last_error()
