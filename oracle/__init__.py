@@ -48,6 +48,12 @@ def _load():
     lib.kivi_oracle_float_to_half.restype = ctypes.c_int
     lib.kivi_oracle_record_bytes.argtypes = [i32, i32, i32, i32]
     lib.kivi_oracle_record_bytes.restype = i64
+    lib.kivi_oracle_record_bytes_s.argtypes = [i32, i32, i32, i32, i32]
+    lib.kivi_oracle_record_bytes_s.restype = i64
+    lib.kivi_oracle_half_rne.argtypes = [ctypes.c_float]
+    lib.kivi_oracle_half_rne.restype = ctypes.c_uint16
+    lib.kivi_oracle_quantize_group_s16.argtypes = [P, i32, i32, P, P, P]
+    lib.kivi_oracle_quantize_group_s16.restype = None
     lib.kivi_oracle_quantize_group.argtypes = [P, i32, i32, P, P, P]
     lib.kivi_oracle_quantize_group.restype = None
     lib.kivi_oracle_dequant.argtypes = [ctypes.c_uint32, ctypes.c_float, ctypes.c_float]
@@ -88,22 +94,24 @@ class _CCache(ctypes.Structure):
         ("residual", ctypes.c_int32),
         ("capacity", ctypes.c_int64), ("n_tokens", ctypes.c_int64),
         ("blocks", ctypes.c_void_p), ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
+        ("scale_fp16", ctypes.c_int32),
     ]
 
 
 TOKENS_PER_RECORD = 128
 
 
-def record_bytes(D: int, kb: int, vb: int, G: int) -> int:
+def record_bytes(D: int, kb: int, vb: int, G: int, scale_fp16: bool = False) -> int:
     """Bytes of one 128-token record (0 for a shape the layout does not take)."""
-    return int(_load().kivi_oracle_record_bytes(D, kb, vb, G))
+    return int(_load().kivi_oracle_record_bytes_s(D, kb, vb, G, int(bool(scale_fp16))))
 
 
-def record_sections(D: int, kb: int, vb: int, G: int):
+def record_sections(D: int, kb: int, vb: int, G: int, scale_fp16: bool = False):
     """(name, byte offset, byte size) of the sections of a record, in order."""
     n, g = TOKENS_PER_RECORD, TOKENS_PER_RECORD // G
-    sizes = [("k_codes", n * D * kb // 8), ("k_scale", g * D * 4), ("k_zero", g * D * 2),
-             ("v_codes", n * D * vb // 8), ("v_scale", (D // G) * n * 4),
+    sb = 2 if scale_fp16 else 4
+    sizes = [("k_codes", n * D * kb // 8), ("k_scale", g * D * sb), ("k_zero", g * D * 2),
+             ("v_codes", n * D * vb // 8), ("v_scale", (D // G) * n * sb),
              ("v_zero", (D // G) * n * 2)]
     out, off = [], 0
     for name, size in sizes:
@@ -112,27 +120,30 @@ def record_sections(D: int, kb: int, vb: int, G: int):
     return out
 
 
-def unpack_records(blocks, B, H, cap, D, kb, vb, G):
+def unpack_records(blocks, B, H, cap, D, kb, vb, G, scale_fp16: bool = False):
     """Re-index a record array ([B][H][cap/128][record] bytes) into the
     logical arrays: k_codes [B][H][cap/G][D][G*kb/32] u32, k_scale, k_zero
-    [B][H][cap/G][D] (f32, f16), v_codes [B][H][cap][D*vb/32] u32, v_scale,
-    v_zero [B][H][D/G][cap] (f32, f16).  Copies; no arithmetic."""
+    [B][H][cap/G][D] (f32 or f16, f16), v_codes [B][H][cap][D*vb/32] u32,
+    v_scale, v_zero [B][H][D/G][cap] (f32 or f16, f16).  Copies; no
+    arithmetic."""
     n = TOKENS_PER_RECORD
     nb = cap // n
-    rb = sum(size for _, _, size in record_sections(D, kb, vb, G))
+    secs = record_sections(D, kb, vb, G, scale_fp16)
+    rb = sum(size for _, _, size in secs)
     raw = np.ascontiguousarray(blocks).view(np.uint8).reshape(B, H, nb, rb)
-    sec = {name: raw[..., off:off + size] for name, off, size in record_sections(D, kb, vb, G)}
+    sec = {name: raw[..., off:off + size] for name, off, size in secs}
     g = n // G
+    st = np.float16 if scale_fp16 else np.float32
 
     def cast(x, dtype):
         return np.ascontiguousarray(x).view(dtype)
 
     out = {}
     out["k_codes"] = cast(sec["k_codes"], np.uint32).reshape(B, H, nb * g, D, G * kb // 32)
-    out["k_scale"] = cast(sec["k_scale"], np.float32).reshape(B, H, nb * g, D)
+    out["k_scale"] = cast(sec["k_scale"], st).reshape(B, H, nb * g, D)
     out["k_zero"] = cast(sec["k_zero"], np.float16).reshape(B, H, nb * g, D)
     out["v_codes"] = cast(sec["v_codes"], np.uint32).reshape(B, H, nb * n, D * vb // 32)
-    vs = cast(sec["v_scale"], np.float32).reshape(B, H, nb, D // G, n)
+    vs = cast(sec["v_scale"], st).reshape(B, H, nb, D // G, n)
     out["v_scale"] = np.ascontiguousarray(vs.transpose(0, 1, 3, 2, 4)).reshape(B, H, D // G, cap)
     vz = cast(sec["v_zero"], np.float16).reshape(B, H, nb, D // G, n)
     out["v_zero"] = np.ascontiguousarray(vz.transpose(0, 1, 3, 2, 4)).reshape(B, H, D // G, cap)
@@ -154,6 +165,22 @@ def quantize_group(x, bits: int):
     z = np.zeros(1, np.float32)
     _load().kivi_oracle_quantize_group(_ptr(x), x.size, bits, _ptr(codes), _ptr(s), _ptr(z))
     return codes, np.float32(s[0]), np.float32(z[0])
+
+
+def quantize_group_s16(x, bits: int):
+    """KIVI item 1 with an fp16 scale: (codes uint8[n], scale f16, zero f32)."""
+    x = _req(x, np.float32)
+    codes = np.zeros(x.size, np.uint8)
+    s = np.zeros(1, np.uint16)
+    z = np.zeros(1, np.float32)
+    _load().kivi_oracle_quantize_group_s16(_ptr(x), x.size, bits, _ptr(codes), _ptr(s), _ptr(z))
+    return codes, s.view(np.float16)[0], np.float32(z[0])
+
+
+def half_rne(value) -> int:
+    """Bit pattern of the binary16 value nearest to an fp32 value (ties to
+    even)."""
+    return int(_load().kivi_oracle_half_rne(float(np.float32(value))))
 
 
 def dequant(code: int, scale, zero) -> np.float32:
@@ -187,26 +214,28 @@ def _round_cap(t: int) -> int:
     return max(TOKENS_PER_RECORD, -(-t // TOKENS_PER_RECORD) * TOKENS_PER_RECORD)
 
 
-def pack_keys(k_fp16, bits: int, G: int, cap: int | None = None, offset: int = 0):
+def pack_keys(k_fp16, bits: int, G: int, cap: int | None = None, offset: int = 0,
+              scale_fp16: bool = False):
     """KIVI item 2 into a fresh zero-filled record array.  k_fp16: uint16
     [B][H][T][D] -> logical (codes, scale, zero) over the capacity (a multiple
     of 128, by default the smallest that holds offset + T)."""
     k = _req(k_fp16, np.uint16)
     B, H, T, D = k.shape
     cap = _round_cap(T + offset) if cap is None else cap
-    c = Cache(B, H, D, bits, bits, G, G, cap)
+    c = Cache(B, H, D, bits, bits, G, G, cap, scale_fp16=scale_fp16)
     if _load().kivi_oracle_pack_keys(ctypes.byref(c._c), _ptr(k), T, offset):
         raise ValueError("oracle pack_keys rejected its arguments")
     return c.k_codes, c.k_scale, c.k_zero
 
 
-def pack_values(v_fp16, bits: int, G: int, cap: int | None = None, offset: int = 0):
+def pack_values(v_fp16, bits: int, G: int, cap: int | None = None, offset: int = 0,
+                scale_fp16: bool = False):
     """KIVI item 3 into a fresh zero-filled record array.  v_fp16: uint16
     [B][H][T][D] -> logical (codes, scale, zero)."""
     v = _req(v_fp16, np.uint16)
     B, H, T, D = v.shape
     cap = _round_cap(T + offset) if cap is None else cap
-    c = Cache(B, H, D, bits, bits, G, G, cap)
+    c = Cache(B, H, D, bits, bits, G, G, cap, scale_fp16=scale_fp16)
     if _load().kivi_oracle_pack_values(ctypes.byref(c._c), _ptr(v), T, offset):
         raise ValueError("oracle pack_values rejected its arguments")
     return c.v_codes, c.v_scale, c.v_zero
@@ -219,10 +248,12 @@ class Cache:
     ``k_res`` and ``v_res``.  The logical arrays ``k_codes`` ... ``v_zero``
     are re-indexed copies of the records (see unpack_records)."""
 
-    def __init__(self, batch, n_kv_heads, head_dim, k_bits, v_bits, group, residual, capacity):
+    def __init__(self, batch, n_kv_heads, head_dim, k_bits, v_bits, group, residual, capacity,
+                 scale_fp16: bool = False):
         self.B, self.H, self.D = batch, n_kv_heads, head_dim
         self.kb, self.vb, self.G, self.R, self.cap = k_bits, v_bits, group, residual, capacity
-        rb = record_bytes(head_dim, k_bits, v_bits, group)
+        self.scale_fp16 = bool(scale_fp16)
+        rb = record_bytes(head_dim, k_bits, v_bits, group, self.scale_fp16)
         if rb == 0 or capacity % TOKENS_PER_RECORD:
             raise ValueError("shape or capacity outside the record layout")
         self.arrays = {
@@ -232,7 +263,7 @@ class Cache:
         }
         self._c = _CCache(batch, n_kv_heads, head_dim, k_bits, v_bits, group, residual,
                           capacity, 0, _ptr(self.arrays["blocks"]), _ptr(self.arrays["k_res"]),
-                          _ptr(self.arrays["v_res"]))
+                          _ptr(self.arrays["v_res"]), int(self.scale_fp16))
 
     def __getattr__(self, name):
         arrays = self.__dict__.get("arrays")
@@ -242,13 +273,13 @@ class Cache:
             return arrays[name]
         if name in LOGICAL:
             return unpack_records(arrays["blocks"], self.B, self.H, self.cap, self.D, self.kb,
-                                  self.vb, self.G)[name]
+                                  self.vb, self.G, self.scale_fp16)[name]
         raise AttributeError(name)
 
     def logical(self):
         """All six logical arrays at once."""
         return unpack_records(self.arrays["blocks"], self.B, self.H, self.cap, self.D, self.kb,
-                              self.vb, self.G)
+                              self.vb, self.G, self.scale_fp16)
 
     @property
     def n_tokens(self) -> int:

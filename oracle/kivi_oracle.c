@@ -16,6 +16,14 @@
  *   - codes are clamped to [0, 2^B - 1] (provably a no-op for finite input).
  *   - a scale is stored as fp32; a zero point (the group minimum, which is
  *     an fp16 input value) is stored as that fp16 value, exactly.
+ *   - fp16-scale layout (a cache with scale_fp16 set; the pages fix no
+ *     storage precision for s): s is computed in fp32 as above, rounded to
+ *     the nearest binary16 value (ties to even), and the codes are chosen
+ *     for that stored scale -- Q = round((X - z) / s16), clamped -- so that
+ *     dequantization reads exactly what quantization used.  A scale that
+ *     rounds to zero is stored as zero and gives all codes 0, as max == min
+ *     does.  s16 is finite for every fp16 input (max - min <= 131008, so s
+ *     <= 43670 for B >= 2).
  *   - prefill with t % R == 0 quantizes every key (the prose rule "keep the
  *     last t mod R keys"), leaving the key window empty.
  *   - the cache is updated before attention runs, so attention sees all t
@@ -71,6 +79,39 @@ int kivi_oracle_float_to_half(float f, uint16_t *out) {
   return 0;
 }
 
+/* fp32 -> binary16, rounded to nearest, ties to even (IEEE 754
+ * roundTiesToEven), written from the format's definition: magnitudes below
+ * 2^-14 are multiples of 2^-24 (subnormals), those in [2^e, 2^(e+1)) for
+ * e >= -14 multiples of 2^(e-10); a magnitude that rounds to 2^16 or more
+ * (65520 and up) becomes infinity.  NaN -> the quiet NaN 0x7e00. */
+uint16_t kivi_oracle_half_rne(float f) {
+  const uint16_t sign = signbit(f) ? 0x8000u : 0u;
+  if (isnan(f)) return 0x7e00u;
+  const double a = fabs((double)f);
+  if (isinf(a)) return (uint16_t)(sign | 0x7c00u);
+  int ex = -14;                                   /* exponent of the quantum's binade */
+  if (a >= ldexp(1.0, -14)) {
+    (void)frexp(a, &ex);                          /* a in [2^(ex-1), 2^ex) */
+    ex -= 1;
+  }
+  const double quantum = ldexp(1.0, ex - 10);
+  const double n = a / quantum;                   /* exact: a power-of-two scaling */
+  double r = floor(n);
+  const double frac = n - r;
+  if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+  /* subnormal: the pattern is r itself.  Normal: exponent field ex + 15
+   * and fraction r - 1024, i.e. (ex + 14) * 1024 + r; a round up to r = 2048
+   * gives the next binade's first pattern, and r = 1024 from the subnormal
+   * range the smallest normal one. */
+  long bits;
+  if (ex == -14 && r < 1024.0)
+    bits = (long)r;
+  else
+    bits = (long)(ex + 14) * 1024 + (long)r;
+  if (bits >= 0x7c00) return (uint16_t)(sign | 0x7c00u);
+  return (uint16_t)(sign | (uint16_t)bits);
+}
+
 /* -------------------------------------------------------------- quantizer */
 
 /* KIVI item 1: z = min(X), s = (max(X) - min(X)) / (2^B - 1),
@@ -96,6 +137,34 @@ void kivi_oracle_quantize_group(const float *x, int n, int bits, uint8_t *codes,
     codes[i] = (uint8_t)q;
   }
   *scale = s;
+  *zero = z;
+}
+
+/* KIVI item 1 for the fp16-scale layout: the same s and z as above, s then
+ * rounded to binary16 (s16), and the codes chosen for s16. */
+void kivi_oracle_quantize_group_s16(const float *x, int n, int bits, uint8_t *codes,
+                                    uint16_t *scale_bits, float *zero) {
+  float mn = x[0], mx = x[0];
+  for (int i = 1; i < n; ++i) {
+    if (x[i] < mn) mn = x[i];
+    if (x[i] > mx) mx = x[i];
+  }
+  const int qmax = (1 << bits) - 1;
+  const float s = (mx - mn) / (float)qmax;
+  const uint16_t sb = kivi_oracle_half_rne(s);
+  const float s16 = kivi_oracle_half_to_float(sb);
+  const float z = mn;
+  for (int i = 0; i < n; ++i) {
+    int q = 0;
+    if (s16 != 0.0f) {
+      float r = rintf((x[i] - z) / s16);
+      q = (int)r;
+      if (q < 0) q = 0;
+      if (q > qmax) q = qmax;
+    }
+    codes[i] = (uint8_t)q;
+  }
+  *scale_bits = sb;
   *zero = z;
 }
 
@@ -144,22 +213,36 @@ typedef struct {
   int64_t kc, ks, kz, vc, vs, vz, size;
 } record_t;
 
-static int record_of(int D, int kb, int vb, int G, record_t *r) {
-  if (!shape_ok(D, kb, G) || !shape_ok(D, vb, G)) return -1;
+/* sb: bytes per stored scale, 4 (fp32) or 2 (fp16-scale layout) */
+static int record_of(int D, int kb, int vb, int G, int sb, record_t *r) {
+  if (!shape_ok(D, kb, G) || !shape_ok(D, vb, G) || (sb != 4 && sb != 2)) return -1;
   const int64_t groups = TOKENS_PER_RECORD / G;
   r->kc = 0;
   r->ks = r->kc + (int64_t)TOKENS_PER_RECORD * D * kb / 8;
-  r->kz = r->ks + groups * D * 4;
+  r->kz = r->ks + groups * D * sb;
   r->vc = r->kz + groups * D * 2;
   r->vs = r->vc + (int64_t)TOKENS_PER_RECORD * D * vb / 8;
-  r->vz = r->vs + (int64_t)(D / G) * TOKENS_PER_RECORD * 4;
+  r->vz = r->vs + (int64_t)(D / G) * TOKENS_PER_RECORD * sb;
   r->size = r->vz + (int64_t)(D / G) * TOKENS_PER_RECORD * 2;
   return 0;
 }
 
+static int scale_bytes(const kivi_oracle_cache *c) { return c->scale_fp16 ? 2 : 4; }
+
 int64_t kivi_oracle_record_bytes(int D, int k_bits, int v_bits, int G) {
   record_t r;
-  return record_of(D, k_bits, v_bits, G, &r) ? 0 : r.size;
+  return record_of(D, k_bits, v_bits, G, 4, &r) ? 0 : r.size;
+}
+
+int64_t kivi_oracle_record_bytes_s(int D, int k_bits, int v_bits, int G, int scale_fp16) {
+  record_t r;
+  return record_of(D, k_bits, v_bits, G, scale_fp16 ? 2 : 4, &r) ? 0 : r.size;
+}
+
+/* A stored scale as a float: an fp32 word, or an fp16 one (exact). */
+static float scale_load(const kivi_oracle_cache *c, const uint8_t *p) {
+  if (c->scale_fp16) return kivi_oracle_half_to_float(*(const uint16_t *)p);
+  return *(const float *)p;
 }
 
 /* Start of the record holding token tau of slab bh. */
@@ -172,7 +255,7 @@ static uint8_t *record_at(const kivi_oracle_cache *c, const record_t *r, int64_t
  * stored: its code words, scale and zero. */
 typedef struct {
   uint32_t *codes;
-  float *scale;
+  uint8_t *scale;     /* fp32 or fp16 (scale_bytes) */
   uint16_t *zero;
 } key_slot_t;
 
@@ -184,7 +267,7 @@ static key_slot_t key_slot(const kivi_oracle_cache *c, const record_t *r, int64_
   const int64_t i = local * D + ch;
   key_slot_t k;
   k.codes = (uint32_t *)(rec + r->kc) + i * (G * c->k_bits / 32);
-  k.scale = (float *)(rec + r->ks) + i;
+  k.scale = rec + r->ks + i * scale_bytes(c);
   k.zero = (uint16_t *)(rec + r->kz) + i;
   return k;
 }
@@ -196,10 +279,21 @@ static uint32_t *value_codes(const kivi_oracle_cache *c, const record_t *r, int6
   uint8_t *rec = record_at(c, r, bh, tau);
   return (uint32_t *)(rec + r->vc) + (tau % TOKENS_PER_RECORD) * (c->head_dim * c->v_bits / 32);
 }
-static float *value_scale(const kivi_oracle_cache *c, const record_t *r, int64_t bh,
-                          int64_t tau, int gc) {
+static uint8_t *value_scale(const kivi_oracle_cache *c, const record_t *r, int64_t bh,
+                            int64_t tau, int gc) {
   uint8_t *rec = record_at(c, r, bh, tau);
-  return (float *)(rec + r->vs) + gc * TOKENS_PER_RECORD + tau % TOKENS_PER_RECORD;
+  return rec + r->vs + (gc * TOKENS_PER_RECORD + tau % TOKENS_PER_RECORD) * scale_bytes(c);
+}
+
+/* KIVI item 1 on one group of the cache's layout: codes, the stored scale
+ * (written at `scale`) and the zero point. */
+static void quantize_into(const kivi_oracle_cache *c, const float *x, int n, int bits,
+                          uint8_t *codes, uint8_t *scale, float *zero) {
+  if (c->scale_fp16) {
+    kivi_oracle_quantize_group_s16(x, n, bits, codes, (uint16_t *)scale, zero);
+  } else {
+    kivi_oracle_quantize_group(x, n, bits, codes, (float *)scale, zero);
+  }
 }
 static uint16_t *value_zero(const kivi_oracle_cache *c, const record_t *r, int64_t bh,
                             int64_t tau, int gc) {
@@ -212,11 +306,10 @@ static uint16_t *value_zero(const kivi_oracle_cache *c, const record_t *r, int64
 static int put_key_group(const kivi_oracle_cache *c, const record_t *r, const float *x,
                          int64_t bh, int64_t g, int ch) {
   uint8_t q[TOKENS_PER_RECORD];
-  float s, z;
-  kivi_oracle_quantize_group(x, c->group, c->k_bits, q, &s, &z);
+  float z;
   key_slot_t k = key_slot(c, r, bh, g, ch);
+  quantize_into(c, x, c->group, c->k_bits, q, k.scale, &z);
   kivi_oracle_pack_codes(q, c->group, c->k_bits, k.codes);
-  *k.scale = s;
   return kivi_oracle_float_to_half(z, k.zero);
 }
 
@@ -227,9 +320,8 @@ static int put_value_row(const kivi_oracle_cache *c, const record_t *r, const fl
   uint8_t q[1024];
   const int D = c->head_dim, G = c->group;
   for (int g = 0; g < D / G; ++g) {
-    float s, z;
-    kivi_oracle_quantize_group(x + g * G, G, c->v_bits, q + g * G, &s, &z);
-    *value_scale(c, r, bh, tau, g) = s;
+    float z;
+    quantize_into(c, x + g * G, G, c->v_bits, q + g * G, value_scale(c, r, bh, tau, g), &z);
     if (kivi_oracle_float_to_half(z, value_zero(c, r, bh, tau, g))) return -1;
   }
   kivi_oracle_pack_codes(q, D, c->v_bits, value_codes(c, r, bh, tau));
@@ -241,7 +333,7 @@ static int put_value_row(const kivi_oracle_cache *c, const record_t *r, const fl
 static int cache_ok(const kivi_oracle_cache *c) {
   record_t r;
   return c && c->blocks && c->k_res && c->v_res &&
-         record_of(c->head_dim, c->k_bits, c->v_bits, c->group, &r) == 0 &&
+         record_of(c->head_dim, c->k_bits, c->v_bits, c->group, scale_bytes(c), &r) == 0 &&
          c->residual > 0 && c->residual % c->group == 0 && c->capacity > 0 &&
          c->capacity % TOKENS_PER_RECORD == 0 && c->capacity % c->residual == 0 &&
          c->n_tokens >= 0 && c->n_tokens <= c->capacity;
@@ -253,7 +345,7 @@ int kivi_oracle_pack_keys(const kivi_oracle_cache *dst, const uint16_t *k, int64
   if (!cache_ok(dst) || T < 0 || off < 0 || T % dst->group || off % dst->group ||
       off + T > dst->capacity)
     return -1;
-  record_of(dst->head_dim, dst->k_bits, dst->v_bits, dst->group, &r);
+  record_of(dst->head_dim, dst->k_bits, dst->v_bits, dst->group, scale_bytes(dst), &r);
   const int D = dst->head_dim, G = dst->group;
   float x[TOKENS_PER_RECORD];
   for (int64_t bh = 0; bh < (int64_t)dst->batch * dst->n_kv_heads; ++bh)
@@ -270,7 +362,7 @@ int kivi_oracle_pack_values(const kivi_oracle_cache *dst, const uint16_t *v, int
                             int64_t off) {
   record_t r;
   if (!cache_ok(dst) || T < 0 || off < 0 || off + T > dst->capacity) return -1;
-  record_of(dst->head_dim, dst->k_bits, dst->v_bits, dst->group, &r);
+  record_of(dst->head_dim, dst->k_bits, dst->v_bits, dst->group, scale_bytes(dst), &r);
   const int D = dst->head_dim;
   float x[1024];
   for (int64_t bh = 0; bh < (int64_t)dst->batch * dst->n_kv_heads; ++bh)
@@ -293,7 +385,7 @@ int kivi_oracle_append(kivi_oracle_cache *c, const uint16_t *k_new,
                        const uint16_t *v_new, int64_t n_new) {
   record_t r;
   if (!cache_ok(c) || n_new < 0 || c->n_tokens + n_new > c->capacity) return -1;
-  record_of(c->head_dim, c->k_bits, c->v_bits, c->group, &r);
+  record_of(c->head_dim, c->k_bits, c->v_bits, c->group, scale_bytes(c), &r);
   const int D = c->head_dim, G = c->group, R = c->residual;
   const int64_t BH = (int64_t)c->batch * c->n_kv_heads;
   float *x = (float *)malloc(sizeof(float) * (size_t)(R > D ? R : D));
@@ -336,7 +428,7 @@ static float key_at(const kivi_oracle_cache *c, const record_t *r, int64_t bh, i
   if (tau < n_kq) {
     key_slot_t k = key_slot(c, r, bh, tau / G, ch);
     const uint32_t q = code_at(k.codes, (int)(tau % G), c->k_bits);
-    return kivi_oracle_dequant(q, *k.scale, kivi_oracle_half_to_float(*k.zero));
+    return kivi_oracle_dequant(q, scale_load(c, k.scale), kivi_oracle_half_to_float(*k.zero));
   }
   return kivi_oracle_half_to_float(c->k_res[(bh * R + tau % R) * D + ch]);
 }
@@ -348,7 +440,7 @@ static float value_at(const kivi_oracle_cache *c, const record_t *r, int64_t bh,
   if (tau < n_vq) {
     const uint32_t q = code_at(value_codes(c, r, bh, tau), ch, c->v_bits);
     const int gc = (int)(ch / G);
-    return kivi_oracle_dequant(q, *value_scale(c, r, bh, tau, gc),
+    return kivi_oracle_dequant(q, scale_load(c, value_scale(c, r, bh, tau, gc)),
                                kivi_oracle_half_to_float(*value_zero(c, r, bh, tau, gc)));
   }
   return kivi_oracle_half_to_float(c->v_res[(bh * R + tau % R) * D + ch]);
@@ -357,7 +449,7 @@ static float value_at(const kivi_oracle_cache *c, const record_t *r, int64_t bh,
 int kivi_oracle_materialize(const kivi_oracle_cache *c, float *k_hat, float *v_hat) {
   record_t r;
   if (!cache_ok(c)) return -1;
-  record_of(c->head_dim, c->k_bits, c->v_bits, c->group, &r);
+  record_of(c->head_dim, c->k_bits, c->v_bits, c->group, scale_bytes(c), &r);
   const int64_t BH = (int64_t)c->batch * c->n_kv_heads, t = c->n_tokens;
   const int D = c->head_dim;
   for (int64_t bh = 0; bh < BH; ++bh)
@@ -381,7 +473,7 @@ static int attend_one(const kivi_oracle_cache *c, const uint16_t *q, int n_q_hea
   const int n_rep = n_q_heads / c->n_kv_heads;
   const int64_t bh = (int64_t)b * c->n_kv_heads + hq / n_rep;
   record_t r;
-  record_of(D, c->k_bits, c->v_bits, c->group, &r);
+  record_of(D, c->k_bits, c->v_bits, c->group, scale_bytes(c), &r);
   float qv[1024];
   for (int ch = 0; ch < D; ++ch)
     qv[ch] = kivi_oracle_half_to_float(q[((int64_t)b * n_q_heads + hq) * D + ch]);

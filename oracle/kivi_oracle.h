@@ -32,7 +32,9 @@
  *                                        channels, packed along channels)
  *   value scales f32 [D/G][128]
  *   value zeros  f16 [D/G][128]
- * G divides 128; cap is a multiple of 128.
+ * G divides 128; cap is a multiple of 128.  With scale_fp16 set, both scale
+ * sections hold binary16 values instead ([128/G][D] and [D/G][128] of 2
+ * bytes), the sections after them moving up accordingly.
  *   key/value residual fp16 [B][H][R][D]  token tau in slot tau % R
  */
 #ifndef KIVI_ORACLE_H
@@ -51,10 +53,13 @@ typedef struct kivi_oracle_cache {
   int64_t n_tokens;
   uint8_t *blocks;             /* [B][H][cap/128] records */
   uint16_t *k_res, *v_res;
+  int32_t scale_fp16;          /* 0: fp32 scales; 1: fp16 scales */
 } kivi_oracle_cache;
 
-/* Bytes of one 128-token record; 0 for shapes the layout does not take. */
+/* Bytes of one 128-token record; 0 for shapes the layout does not take.
+ * _s: the same for fp32 (scale_fp16 0) or fp16 (1) scales. */
 int64_t kivi_oracle_record_bytes(int D, int k_bits, int v_bits, int G);
+int64_t kivi_oracle_record_bytes_s(int D, int k_bits, int v_bits, int G, int scale_fp16);
 
 /* binary16 bit pattern -> float (exact). */
 float kivi_oracle_half_to_float(uint16_t h);
@@ -64,6 +69,12 @@ int kivi_oracle_float_to_half(float f, uint16_t *out);
 /* KIVI item 1: asymmetric round-to-nearest group quantizer. */
 void kivi_oracle_quantize_group(const float *x, int n, int bits, uint8_t *codes,
                                 float *scale, float *zero);
+/* float -> binary16 bit pattern, round to nearest, ties to even. */
+uint16_t kivi_oracle_half_rne(float f);
+/* KIVI item 1 with the scale stored as binary16: s rounded to fp16 (its bit
+ * pattern in *scale_bits), codes chosen for the rounded scale. */
+void kivi_oracle_quantize_group_s16(const float *x, int n, int bits, uint8_t *codes,
+                                    uint16_t *scale_bits, float *zero);
 /* KIVI item 1: dequantization code*scale + zero (fp32 multiply, then add). */
 float kivi_oracle_dequant(uint32_t code, float scale, float zero);
 
