@@ -85,6 +85,8 @@ int check_cache(const kivi_cache *c, const char *who) {
   }
   if (!c->blocks || !c->k_res || !c->v_res)
     return fail(KIVI_ERR_INVALID_ARG, "%s: a cache array pointer is NULL", who);
+  if (c->scale_fp16 != 0 && c->scale_fp16 != 1)
+    return fail(KIVI_ERR_INVALID_ARG, "%s: scale_fp16 must be 0 or 1 (got %d)", who, c->scale_fp16);
   if (c->page_table) {
     if (((uintptr_t)c->page_table & 3) != 0)
       return fail(KIVI_ERR_INVALID_ARG, "%s: page_table must be 4-byte aligned", who);
@@ -99,8 +101,8 @@ int check_cache(const kivi_cache *c, const char *who) {
 }
 
 kivi::Layout layout_of(const kivi_cache *c) {
-  kivi::Layout L =
-      kivi::make_layout(c->blocks, c->head_dim, c->k_bits, c->v_bits, c->group, c->capacity);
+  kivi::Layout L = kivi::make_layout(c->blocks, c->head_dim, c->k_bits, c->v_bits, c->group,
+                                     c->capacity, c->scale_fp16 != 0);
   L.pt = c->page_table;
   L.n_pages = c->n_pages;
   L.H = c->n_kv_heads;
@@ -141,7 +143,9 @@ void set_longest(kivi_cache *c) {
 // Row b of a cache alone, as a uniform cache of batch 1 holding t tokens.
 kivi_cache row_view(const kivi_cache *c, int32_t b, int64_t t) {
   kivi_cache v = *c;
-  const size_t rb = kivi::make_layout(nullptr, c->head_dim, c->k_bits, c->v_bits, c->group, 0).rec;
+  const size_t rb = kivi::make_layout(nullptr, c->head_dim, c->k_bits, c->v_bits, c->group, 0,
+                                      c->scale_fp16 != 0)
+                        .rec;
   const int64_t slabs = (int64_t)b * c->n_kv_heads;
   v.batch = 1;
   v.n_tokens = t;
@@ -378,8 +382,14 @@ const char *kivi_status_string(int status) {
 const char *kivi_last_error(void) { return g_last_error.c_str(); }
 
 size_t kivi_record_bytes(int32_t head_dim, int32_t k_bits, int32_t v_bits, int32_t group) {
-  if (head_dim <= 0 || head_dim > 256) return 0;
-  return (size_t)kivi::make_layout(nullptr, head_dim, k_bits, v_bits, group, 0).rec;
+  return kivi_record_bytes_ex(head_dim, k_bits, v_bits, group, 0);
+}
+
+size_t kivi_record_bytes_ex(int32_t head_dim, int32_t k_bits, int32_t v_bits, int32_t group,
+                            int32_t scale_fp16) {
+  if (head_dim <= 0 || head_dim > 256 || (scale_fp16 != 0 && scale_fp16 != 1)) return 0;
+  return (size_t)kivi::make_layout(nullptr, head_dim, k_bits, v_bits, group, 0, scale_fp16 != 0)
+      .rec;
 }
 
 int kivi_pack_keys(const kivi_cache *dst, const void *k_fp16, int64_t T, int64_t dst_token_offset,

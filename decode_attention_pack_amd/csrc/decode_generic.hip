@@ -121,13 +121,13 @@ decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int
         const int e = (int)(tau - g * a.G);
         // the group's channels are consecutive in its record
         const uint32_t *cw = L.key_codes(bh, g, 0) + e / per;
-        const float *ks = L.key_scale(bh, g, 0);
+        const uint8_t *ks = L.key_scales(bh, g);
         const uint16_t *kz = L.key_zero(bh, g, 0);
         const int sh = a.kb * (e % per);
         const uint32_t msk = (1u << a.kb) - 1u;
         for (int c = 0; c < D; ++c) {
           const uint32_t code = (cw[c * words] >> sh) & msk;
-          const float k = __fadd_rn(__fmul_rn((float)code, ks[c]), h2f(kz[c]));
+          const float k = __fadd_rn(__fmul_rn((float)code, L.scale_at(ks, c)), h2f(kz[c]));
 #pragma unroll
           for (int j = 0; j < NH; ++j) sc[j] = fmaf(q_s[j][c], k, sc[j]);
         }
@@ -195,7 +195,7 @@ decode_generic_kernel(DecodeArgs a, int64_t tok_begin, int tokens_per_split, int
       float v;
       if (tv < rs.n_vq) {
         const uint32_t code = (L.value_codes(bh, tv)[vword] >> vsh) & vmsk;
-        v = __fadd_rn(__fmul_rn((float)code, *L.value_scale(bh, tv, vgrp)),
+        v = __fadd_rn(__fmul_rn((float)code, L.value_scale(bh, tv, vgrp)),
                       h2f(*L.value_zero(bh, tv, vgrp)));
       } else {
         v = h2f(a.v_res[(bh * a.R + tv % a.R) * D + c_own]);

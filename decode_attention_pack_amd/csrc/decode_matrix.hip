@@ -67,15 +67,26 @@ constexpr int kD = 128;
 constexpr int kG = 32;
 constexpr int kBT = 128;       // tokens per block (block role)
 constexpr int kWT = 32;        // tokens per chunk (window role)
-constexpr int kStageDma = 7;   // DMA instructions per key or value part
 // A record of the packed store at this shape (2-bit keys and values, G 32,
-// head_dim 128): byte offsets of its sections and its size.
-constexpr int kRecKc = 0, kRecKs = 4096, kRecKz = 6144;
-constexpr int kRecVc = 7168, kRecVs = 11264, kRecVz = 13312, kRecBytes = 14336;
+// head_dim 128): byte offsets of its sections and its size, with fp32
+// scales or (S16) fp16 scales; and the DMA instructions that copy the key or
+// the value part of a block (codes 4 KB, scales 2 or 1 KB, zeros 1 KB).
+template <bool S16>
+struct Rec {
+  static constexpr int kc = 0, ks = 4096;
+  static constexpr int kz = S16 ? 5120 : 6144;
+  static constexpr int vc = S16 ? 6144 : 7168;
+  static constexpr int vs = S16 ? 10240 : 11264;
+  static constexpr int vz = S16 ? 11264 : 13312;
+  static constexpr int bytes = S16 ? 12288 : 14336;
+  static constexpr int sb = S16 ? 2 : 4;    // bytes per scale
+  static constexpr int dma = S16 ? 6 : 7;
+};
 constexpr int kPRow = 132;     // floats per probability row in LDS (16-byte pad)
 
 // A block's key part and value part in LDS: codes as they sit in the
-// record, the scale and zero rows rotated (see rot_chunk, zrot_off).  The
+// record, the scale and zero rows rotated (see rot_chunk, zrot_off).  fp16
+// scales fill the first half of ks / vs, rotated like the zeros.  The
 // window role stages up to 8 KB in each (32 fp16 rows), hence the padding.
 struct alignas(16) KStage {
   uint32_t kc[1024];   // 4 key groups x 128 channels x 2 words
@@ -89,6 +100,7 @@ struct alignas(16) VStage {
   uint16_t vz[512];    // [4 channel groups][128 tokens], fp16
   uint32_t pad[256];
 };
+
 
 // Global->LDS copies (16 or 4 bytes per lane; lane l's bytes land at LDS
 // offset 16 l (4 l) from `l`).  They are written as inline assembly with the
@@ -151,6 +163,34 @@ __device__ __forceinline__ int rot_off(int r, int c) { return r * 128 + rot_chun
 // chunks: the half offset of columns [c, c + 8) (c a multiple of 8) of row r.
 __device__ __forceinline__ int zrot_off(int r, int c) { return r * 128 + (((c >> 3) + r) & 15) * 8; }
 
+// Eight consecutive scales of a rotated row in LDS, as floats: columns [c, c
+// + 8) of row r (c a multiple of 8) of fp32 rows (rot_off) or fp16 rows
+// (zrot_off, widened exactly).
+template <bool S16>
+__device__ __forceinline__ void scales8(const float *rows, int r, int c, float (&sv)[8]) {
+  if constexpr (S16) {
+    const h8 s8 = *(const h8 *)((const uint16_t *)rows + zrot_off(r, c));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sv[e] = (float)s8[e];
+  } else {
+    const f4 s0 = *(const f4 *)(rows + rot_off(r, c));
+    const f4 s1 = *(const f4 *)(rows + rot_off(r, c + 4));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sv[e] = s0[e];
+      sv[e + 4] = s1[e];
+    }
+  }
+}
+
+// The scale a group stores (KIVI item 1): s, or s rounded to the nearest
+// binary16 value in the fp16-scale layout (the codes are chosen for it).
+template <bool S16>
+__device__ __forceinline__ float rec_scale(float s) {
+  if constexpr (S16) return h2f(f2h_bits(s));
+  return s;
+}
+
 // Per-lane byte offsets of the block DMA.  One DMA instruction fills two
 // rotated rows of 128 floats (lanes 0-31 row 2i, lanes 32-63 row 2i + 1):
 // lane l writes LDS chunk l % 32 of its row, so it reads source chunk
@@ -177,31 +217,37 @@ struct DmaOffsets {
 // A paged cache (PAGED) finds it through the page table: record h of page
 // pt[b nrec + blk], the page index clamped into the pool.  The paged form is
 // a separate instantiation so that the contiguous one keeps its registers.
-template <bool PAGED>
+template <bool PAGED, bool S16>
 __device__ __forceinline__ const uint8_t *record_of(const DecodeArgs &a, int64_t bh, int64_t blk) {
+  constexpr int64_t RB = Rec<S16>::bytes;
   if constexpr (!PAGED) {
-    return a.L.blocks + (bh * a.L.nrec + blk) * (int64_t)kRecBytes;
+    return a.L.blocks + (bh * a.L.nrec + blk) * RB;
   } else {
     const uint32_t b = (uint32_t)bh / (uint32_t)a.H, h = (uint32_t)bh - b * (uint32_t)a.H;
     int64_t p = a.L.pt[(int64_t)b * a.L.nrec + blk];
     p = p < 0 ? 0 : (p >= a.L.n_pages ? a.L.n_pages - 1 : p);
-    return a.L.blocks + (p * a.H + h) * (int64_t)kRecBytes;
+    return a.L.blocks + (p * a.H + h) * RB;
   }
 }
 
 // Key part of block `blk` (tokens [128 blk, 128 blk + 128)) of slab bh:
-// kStageDma DMA instructions, plus 2 for the mask when there is one.
-template <bool MASKED, bool PAGED>
+// Rec<S16>::dma DMA instructions, plus 2 for the mask when there is one.
+template <bool MASKED, bool PAGED, bool S16>
 __device__ __forceinline__ void stage_keys(const DecodeArgs &a, int64_t bh, int64_t blk,
                                            KStage *s, float *mask_s, const DmaOffsets &o,
                                            int lane) {
-  const uint8_t *rec = record_of<PAGED>(a, bh, blk);
+  using RC = Rec<S16>;
+  const uint8_t *rec = record_of<PAGED, S16>(a, bh, blk);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dma16nt(rec + kRecKc + i * 1024, o.lin, (lds_void *)(s->kc + i * 256));
+  for (int i = 0; i < 4; ++i) dma16nt(rec + RC::kc + i * 1024, o.lin, (lds_void *)(s->kc + i * 256));
+  if constexpr (S16) {
+    dma16nt(rec + RC::ks, o.zrot, (lds_void *)s->ks);   // four rows of 128 fp16 scales
+  } else {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-    dma16nt(rec + kRecKs + i * 1024, o.rot[i], (lds_void *)(s->ks + i * 256));
-  dma16nt(rec + kRecKz, o.zrot, (lds_void *)s->kz);
+    for (int i = 0; i < 2; ++i)
+      dma16nt(rec + RC::ks + i * 1024, o.rot[i], (lds_void *)(s->ks + i * 256));
+  }
+  dma16nt(rec + RC::kz, o.zrot, (lds_void *)s->kz);
   if (MASKED) {
     // dword copies: a mask row need not be 16-byte aligned
     const float *m = a.mask + (bh / a.H) * a.t + blk * kBT;
@@ -210,17 +256,22 @@ __device__ __forceinline__ void stage_keys(const DecodeArgs &a, int64_t bh, int6
   }
 }
 
-// Value part of block `blk`: kStageDma DMA instructions.
-template <bool PAGED>
+// Value part of block `blk`: Rec<S16>::dma DMA instructions.
+template <bool PAGED, bool S16>
 __device__ __forceinline__ void stage_values(const DecodeArgs &a, int64_t bh, int64_t blk,
                                              VStage *s, const DmaOffsets &o) {
-  const uint8_t *rec = record_of<PAGED>(a, bh, blk);
+  using RC = Rec<S16>;
+  const uint8_t *rec = record_of<PAGED, S16>(a, bh, blk);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dma16nt(rec + kRecVc + i * 1024, o.lin, (lds_void *)(s->vc + i * 256));
+  for (int i = 0; i < 4; ++i) dma16nt(rec + RC::vc + i * 1024, o.lin, (lds_void *)(s->vc + i * 256));
+  if constexpr (S16) {
+    dma16nt(rec + RC::vs, o.zrot, (lds_void *)s->vs);
+  } else {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-    dma16nt(rec + kRecVs + i * 1024, o.rot[i], (lds_void *)(s->vs + i * 256));
-  dma16nt(rec + kRecVz, o.zrot, (lds_void *)s->vz);
+    for (int i = 0; i < 2; ++i)
+      dma16nt(rec + RC::vs + i * 1024, o.rot[i], (lds_void *)(s->vs + i * 256));
+  }
+  dma16nt(rec + RC::vz, o.zrot, (lds_void *)s->vz);
 }
 
 // LDS transpose read, issued as inline assembly: the compiler's builtin for it
@@ -348,14 +399,15 @@ struct BlockShare {
 // continuing with the blocks the wave draws, accumulated into one partial
 // per query head, left in the wave's probability buffer: row h holds acc[128]
 // of head h, then m (natural-log units) and l.
-template <int NREP, bool MASKED, bool PAGED>
+template <int NREP, bool MASKED, bool PAGED, bool S16>
 __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare &sh,
                                            int64_t first, int hk, int b, const Lds &L,
                                            KStage *__restrict__ kbuf,
                                            VStage *__restrict__ vbuf) {
   static_assert(NREP == 1 || NREP == 2 || NREP == 4, "query heads per KV head");
   constexpr int GA = 16 / NREP;       // key groups per A operand
-  constexpr int KDMA = kStageDma + (MASKED ? 2 : 0);
+  constexpr int SD = Rec<S16>::dma;
+  constexpr int KDMA = SD + (MASKED ? 2 : 0);
 
   const int lane = threadIdx.x & 63;
   const int i = lane & 15;
@@ -390,10 +442,10 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
          (lds_void *)&L.p[0][0]);
   {
     const int64_t blk = sh.b0 + (first + sh.rot) % sh.nb;
-    stage_keys<MASKED, PAGED>(a, bh, blk, kbuf, L.mask, dmo, lane);
-    stage_values<PAGED>(a, bh, blk, vbuf, dmo);
+    stage_keys<MASKED, PAGED, S16>(a, bh, blk, kbuf, L.mask, dmo, lane);
+    stage_values<PAGED, S16>(a, bh, blk, vbuf, dmo);
   }
-  wait_vm<KDMA + kStageDma>();   // q
+  wait_vm<KDMA + SD>();   // q
 
   // q of head h_a at this lane's 32 key channels c0(ks) + j, with
   // c0(ks) = 64 (ks / 2) + 16 kg + 8 (ks % 2)
@@ -473,10 +525,9 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int c0 = 64 * (ks >> 1) + 16 * kg + 8 * (ks & 1);
-      const f4 s0 = *(const f4 *)(kst.ks + rot_off(g_a, c0));
-      const f4 s1 = *(const f4 *)(kst.ks + rot_off(g_a, c0 + 4));
+      float sv[8];
+      scales8<S16>(kst.ks, g_a, c0, sv);
       const h8 zv = *(const h8 *)(kst.kz + zrot_off(g_a, c0));
-      const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
         split_mul2(qa[ks][j], sv[j], qa[ks][j + 1], sv[j + 1], ah[ks], al[ks], j);
@@ -486,7 +537,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
     }
     // every read of the key part has completed: request the next one
     wait_regs(xk);
-    if constexpr (has_next) stage_keys<MASKED, PAGED>(a, bh, nxt, kbuf, L.mask, dmo, lane);
+    if constexpr (has_next) stage_keys<MASKED, PAGED, S16>(a, bh, nxt, kbuf, L.mask, dmo, lane);
 
     bz = group_sum(bz);
     if (kg == 0) L.bias[i] = bz;
@@ -572,11 +623,10 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
         const int t0 = 32 * kg + 16 * u + 8 * d;
         const f4 p0 = *(const f4 *)(&L.p[h_v][t0]);
         const f4 p1 = *(const f4 *)(&L.p[h_v][t0 + 4]);
-        const f4 s0 = *(const f4 *)(vst.vs + rot_off(c_v, t0));
-        const f4 s1 = *(const f4 *)(vst.vs + rot_off(c_v, t0 + 4));
+        float sv[8];
+        scales8<S16>(vst.vs, c_v, t0, sv);
         const h8 zv = *(const h8 *)(vst.vz + zrot_off(c_v, t0));
         const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-        const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
 #pragma unroll
         for (int j = 0; j < 8; j += 2) {
           split_mul2(pv[j], sv[j], pv[j + 1], sv[j + 1], vh[u][d], vl[u][d], j);
@@ -587,7 +637,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
     }
     // every read of the value part has completed: request the next one
     wait_regs(xv);
-    if constexpr (has_next) stage_values<PAGED>(a, bh, nxt, vbuf, dmo);
+    if constexpr (has_next) stage_values<PAGED, S16>(a, bh, nxt, vbuf, dmo);
 
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -609,7 +659,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
   // The next block is drawn once this block's key part is in; the draw is an
   // LDS atomic, so its wait passes over the copies in flight.
   for (;;) {
-    wait_vm<kStageDma>();   // key part of this block in
+    wait_vm<SD>();   // key part of this block in
     const int64_t nxt = draw_item(sh.ctr, lane) - sh.n_skip;
     if (nxt >= sh.nb) break;
     block(std::true_type{}, sh.b0 + (nxt + sh.rot) % sh.nb);
@@ -644,12 +694,12 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
 // Where a window chunk's data lies.
 struct WinChunk {
   int64_t bh, Ta, Tb, vq_end, t_pop, wslot;
-  int n, n_qv, n_fv, nqv4, nqv8, lt, u_vs, u_vz, u_vrow;
+  int n, n_qv, n_fv, nqvs, nqv8, lt, u_vs, u_vz, u_vrow;
   bool kq, kq_now, pop_here, new_here;
   const uint8_t *rec;
 };
 
-template <bool PAGED>
+template <bool PAGED, bool S16>
 __device__ __forceinline__ WinChunk win_chunk(const DecodeArgs &a, const RowSpan &rs,
                                               int64_t n_main, int chunk, int hk, int b) {
   WinChunk c;
@@ -668,15 +718,16 @@ __device__ __forceinline__ WinChunk win_chunk(const DecodeArgs &a, const RowSpan
   c.vq_end = rs.n_vq < c.Ta ? c.Ta : (rs.n_vq > c.Tb ? c.Tb : rs.n_vq);
   c.n_qv = (int)(c.vq_end - c.Ta);
   c.n_fv = (int)(c.Tb - c.vq_end);
-  c.nqv4 = (c.n_qv + 3) / 4;    // 16-byte units of fp32 scales per channel group
   c.nqv8 = (c.n_qv + 7) / 8;    // 16-byte units of fp16 zeros per channel group
+  // 16-byte units of scales per channel group (fp32, or fp16 like the zeros)
+  c.nqvs = S16 ? c.nqv8 : (c.n_qv + 3) / 4;
   // the chunk lies in one record (Ta is a multiple of 32), at token lt of it
-  c.rec = record_of<PAGED>(a, c.bh, c.Ta / kBT);
+  c.rec = record_of<PAGED, S16>(a, c.bh, c.Ta / kBT);
   c.lt = (int)(c.Ta % kBT);
   // value buffer: codes (2 units per token), scales (4 channel groups x
-  // nqv4 units), fp16 zeros (4 x nqv8 units), then fp16 rows (16 units each)
+  // nqvs units), fp16 zeros (4 x nqv8 units), then fp16 rows (16 units each)
   c.u_vs = c.n_qv * 2;
-  c.u_vz = c.u_vs + 4 * c.nqv4;
+  c.u_vz = c.u_vs + 4 * c.nqvs;
   c.u_vrow = c.u_vz + 4 * c.nqv8;
   // Fused decode step: the value that leaves the window with this token
   // (t_pop = t_new - R, the last quantized value) and the new token's slot.
@@ -696,34 +747,42 @@ struct WinLoads {
   uint32_t q[NREP];
 };
 
+// Units (16 bytes) of a staged key group in the window role's key buffer:
+// codes (64 units), then scales (32 fp32 or 16 fp16 units), then zeros (16).
+template <bool S16>
+struct WinKeyUnits {
+  static constexpr int scales = 64, zeros = S16 ? 80 : 96, end = S16 ? 96 : 112;
+};
+
 // The loads of one window chunk, issued and not waited for.
-template <int NREP, bool PAGED>
+template <int NREP, bool PAGED, bool S16>
 __device__ __forceinline__ WinLoads<NREP> window_issue(const DecodeArgs &a, const RowSpan &rs,
                                                        int64_t n_main, int chunk, int hk, int b,
                                                        const Lds &L) {
+  using RC = Rec<S16>;
+  using KU = WinKeyUnits<S16>;
   const int j = threadIdx.x & 63;
-  const WinChunk c = win_chunk<PAGED>(a, rs, n_main, chunk, hk, b);
+  const WinChunk c = win_chunk<PAGED, S16>(a, rs, n_main, chunk, hk, b);
   const int64_t bh = c.bh, Ta = c.Ta, vq_end = c.vq_end;
-  const int n = c.n, nqv4 = c.nqv4, nqv8 = c.nqv8, lt = c.lt;
+  const int n = c.n, nqvs = c.nqvs, nqv8 = c.nqv8, lt = c.lt;
   const bool kq = c.kq, kq_now = c.kq_now;
   const uint8_t *rec = c.rec;
-  // ---- DMA, in 16-byte units.  Key buffer: codes (64 units), scales (32)
-  // and fp16 zeros (16), or n fp16 rows (16 units each) -- at most 512 units
-  // = 8 KB.
+  // ---- DMA, in 16-byte units.  Key buffer: a key group (WinKeyUnits), or
+  // n fp16 rows (16 units each) -- at most 512 units = 8 KB.
   char *kl = (char *)L.ks;
-  const int ku_end = kq && !kq_now ? 112 : n * 16;
+  const int ku_end = kq && !kq_now ? KU::end : n * 16;
   for (int base = 0; base < ku_end; base += 64) {
     const int u = base + j;
     if (u < ku_end) {
       const void *src;
       if (kq && !kq_now) {
         const int lg = lt / kG;    // key group within the record
-        if (u < 64)
-          src = rec + kRecKc + lg * 1024 + u * 16;
-        else if (u < 96)
-          src = rec + kRecKs + lg * 512 + (u - 64) * 16;
+        if (u < KU::scales)
+          src = rec + RC::kc + lg * 1024 + u * 16;
+        else if (u < KU::zeros)
+          src = rec + RC::ks + lg * (kD * RC::sb) + (u - KU::scales) * 16;
         else
-          src = rec + kRecKz + lg * 256 + (u - 96) * 16;
+          src = rec + RC::kz + lg * 256 + (u - KU::zeros) * 16;
       } else {
         // row r = u / 16 of the chunk; its 16-byte unit k is stored at unit
         // (k + r) % 16 of the row's LDS slot, so that lanes reading the same
@@ -745,13 +804,13 @@ __device__ __forceinline__ WinLoads<NREP> window_issue(const DecodeArgs &a, cons
     if (u < vu_end) {
       const void *src;
       if (u < u_vs) {
-        src = rec + kRecVc + (lt + u / 2) * 32 + (u % 2) * 16;
+        src = rec + RC::vc + (lt + u / 2) * 32 + (u % 2) * 16;
       } else if (u < u_vz) {
         const int x = u - u_vs;
-        src = rec + kRecVs + ((x / nqv4) * kBT + lt) * 4 + (x % nqv4) * 16;
+        src = rec + RC::vs + ((x / nqvs) * kBT + lt) * RC::sb + (x % nqvs) * 16;
       } else if (u < u_vrow) {
         const int x = u - u_vz;
-        src = rec + kRecVz + ((x / nqv8) * kBT + lt) * 2 + (x % nqv8) * 16;
+        src = rec + RC::vz + ((x / nqv8) * kBT + lt) * 2 + (x % nqv8) * 16;
       } else {
         const int x = u - u_vrow;
         const int64_t tok = vq_end + x / 16;
@@ -773,14 +832,16 @@ __device__ __forceinline__ WinLoads<NREP> window_issue(const DecodeArgs &a, cons
   return ld;
 }
 
-template <int NREP, bool MASKED, bool PAGED>
+template <int NREP, bool MASKED, bool PAGED, bool S16>
 __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &rs, int64_t n_main,
                                             int chunk, int slot, int hk, int b, const Lds &L,
                                             const WinLoads<NREP> &ld) {
+  using RC = Rec<S16>;
+  using KU = WinKeyUnits<S16>;
   const int j = threadIdx.x & 63;
-  const WinChunk c = win_chunk<PAGED>(a, rs, n_main, chunk, hk, b);
+  const WinChunk c = win_chunk<PAGED, S16>(a, rs, n_main, chunk, hk, b);
   const int64_t bh = c.bh, Ta = c.Ta, t_pop = c.t_pop;
-  const int n = c.n, n_qv = c.n_qv, nqv4 = c.nqv4, nqv8 = c.nqv8;
+  const int n = c.n, n_qv = c.n_qv, nqvs = c.nqvs, nqv8 = c.nqv8;
   const int u_vs = c.u_vs, u_vz = c.u_vz, u_vrow = c.u_vrow;
   const bool kq = c.kq, kq_now = c.kq_now, pop_here = c.pop_here, new_here = c.new_here;
   char *kl = (char *)L.ks;
@@ -806,7 +867,7 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
     const float x0 = h2f((uint16_t)(popped & 0xFFFFu)), x1 = h2f((uint16_t)(popped >> 16));
     float mn = first_min(x0, x1), mx = first_max(x0, x1);   // channel 2j comes first
     lanes_first_min_max(mn, mx, j, 16);
-    const float sc = group_scale(mn, mx, 2);
+    const float sc = rec_scale<S16>(group_scale(mn, mx, 2));
     uint32_t w = (quant_code(x0, mn, sc, 2) | (quant_code(x1, mn, sc, 2) << 2)) << (4 * (j & 7));
     w |= __shfl_xor(w, 1);
     w |= __shfl_xor(w, 2);
@@ -815,14 +876,20 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
     const int gch = j >> 4;
     if ((j & 7) == 0) {
       ((uint32_t *)vl)[xr * 8 + (j >> 3)] = w;
-      ((uint32_t *)(recw + kRecVc) + (t_pop % kBT) * 8)[j >> 3] = w;
+      ((uint32_t *)(recw + RC::vc) + (t_pop % kBT) * 8)[j >> 3] = w;
     }
     if ((j & 15) == 0) {
       const uint16_t zh = f2h_bits(mn);
-      ((float *)(vl + (size_t)u_vs * 16))[gch * nqv4 * 4 + xr] = sc;
+      if constexpr (S16) {
+        const uint16_t sh = f2h_bits(sc);
+        ((uint16_t *)(vl + (size_t)u_vs * 16))[gch * nqvs * 8 + xr] = sh;
+        ((uint16_t *)(recw + RC::vs))[gch * kBT + t_pop % kBT] = sh;
+      } else {
+        ((float *)(vl + (size_t)u_vs * 16))[gch * nqvs * 4 + xr] = sc;
+        ((float *)(recw + RC::vs))[gch * kBT + t_pop % kBT] = sc;
+      }
       ((uint16_t *)(vl + (size_t)u_vz * 16))[gch * nqv8 * 8 + xr] = zh;
-      ((float *)(recw + kRecVs))[gch * kBT + t_pop % kBT] = sc;
-      ((uint16_t *)(recw + kRecVz))[gch * kBT + t_pop % kBT] = zh;
+      ((uint16_t *)(recw + RC::vz))[gch * kBT + t_pop % kBT] = zh;
     }
     // the slot now takes the new value (this lane read its old contents above)
     *(uint32_t *)slot_v = nv;
@@ -854,7 +921,8 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
       mn1 = x1 < mn1 ? x1 : mn1;
       mx1 = x1 > mx1 ? x1 : mx1;
     }
-    const float sc0 = group_scale(mn0, mx0, 2), sc1 = group_scale(mn1, mx1, 2);
+    const float sc0 = rec_scale<S16>(group_scale(mn0, mx0, 2));
+    const float sc1 = rec_scale<S16>(group_scale(mn1, mx1, 2));
     uint32_t cw[4] = {0u, 0u, 0u, 0u};   // channel 2j: words 0, 1; channel 2j + 1: words 2, 3
     for (int r = 0; r < kWT; ++r) {
       const uint32_t w = row_word(r);
@@ -866,13 +934,19 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
     const uint4 c4 = make_uint4(cw[0], cw[1], cw[2], cw[3]);
     *(uint4 *)((uint32_t *)kl + 4 * j) = c4;                       // codes: 2 words per channel
     const uint32_t z2 = (uint32_t)f2h_bits(mn0) | ((uint32_t)f2h_bits(mn1) << 16);
-    *(float2 *)((float *)(kl + 64 * 16) + 2 * j) = make_float2(sc0, sc1);
-    *((uint32_t *)(kl + 96 * 16) + j) = z2;
     const int64_t grp = Ta / kG;
     const int lg = (int)(grp % (kBT / kG));   // the group within the record
-    *(uint4 *)((uint32_t *)(recw + kRecKc) + (lg * kD + 2 * j) * 2) = c4;
-    *(float2 *)((float *)(recw + kRecKs) + lg * kD + 2 * j) = make_float2(sc0, sc1);
-    *(uint32_t *)((uint16_t *)(recw + kRecKz) + lg * kD + 2 * j) = z2;
+    if constexpr (S16) {
+      const uint32_t s2 = (uint32_t)f2h_bits(sc0) | ((uint32_t)f2h_bits(sc1) << 16);
+      *((uint32_t *)(kl + KU::scales * 16) + j) = s2;
+      *(uint32_t *)((uint16_t *)(recw + RC::ks) + lg * kD + 2 * j) = s2;
+    } else {
+      *(float2 *)((float *)(kl + KU::scales * 16) + 2 * j) = make_float2(sc0, sc1);
+      *(float2 *)((float *)(recw + RC::ks) + lg * kD + 2 * j) = make_float2(sc0, sc1);
+    }
+    *((uint32_t *)(kl + KU::zeros * 16) + j) = z2;
+    *(uint4 *)((uint32_t *)(recw + RC::kc) + (lg * kD + 2 * j) * 2) = c4;
+    *(uint32_t *)((uint16_t *)(recw + RC::kz) + lg * kD + 2 * j) = z2;
   }
   wave_lds_sync();
 
@@ -888,8 +962,8 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
     // summed in increasing order
     if (kq) {
       const uint32_t *kc = (const uint32_t *)kl;   // channel c: words 2c, 2c + 1
-      const float *ks = (const float *)(kl + 64 * 16);
-      const uint16_t *kz = (const uint16_t *)(kl + 96 * 16);
+      const char *ks = kl + KU::scales * 16;
+      const uint16_t *kz = (const uint16_t *)(kl + KU::zeros * 16);
       const int sh = 2 * (tj % 16);
       const bool hi = tj >= 16;
 #pragma unroll 4
@@ -898,7 +972,14 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
         const uint4 wb = *(const uint4 *)(kc + 2 * c + 4);
         const uint32_t cw[4] = {hi ? wa.y : wa.x, hi ? wa.w : wa.z, hi ? wb.y : wb.x,
                                 hi ? wb.w : wb.z};
-        const f4 s4 = *(const f4 *)(ks + c);
+        f4 s4;
+        if constexpr (S16) {
+          const uint2 ss = *(const uint2 *)((const uint16_t *)ks + c);
+          s4 = (f4){h2f((uint16_t)(ss.x & 0xFFFFu)), h2f((uint16_t)(ss.x >> 16)),
+                    h2f((uint16_t)(ss.y & 0xFFFFu)), h2f((uint16_t)(ss.y >> 16))};
+        } else {
+          s4 = *(const f4 *)((const float *)ks + c);
+        }
         const uint2 zz = *(const uint2 *)(kz + c);
         const float z4[4] = {h2f((uint16_t)(zz.x & 0xFFFFu)), h2f((uint16_t)(zz.x >> 16)),
                              h2f((uint16_t)(zz.y & 0xFFFFu)), h2f((uint16_t)(zz.y >> 16))};
@@ -968,7 +1049,8 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
   const int c0 = 2 * j;
   const int gch = c0 / kG;
   const uint32_t *vc = (const uint32_t *)vl;
-  const float *vsc = (const float *)(vl + (size_t)u_vs * 16) + gch * nqv4 * 4;
+  // the group's scales: nqvs units (4 fp32 or 8 fp16 scales each)
+  const char *vsc = vl + (size_t)u_vs * 16 + (size_t)gch * nqvs * 16;
   const uint16_t *vz = (const uint16_t *)(vl + (size_t)u_vz * 16) + gch * nqv8 * 8;
   const uint16_t *vrow = (const uint16_t *)(vl + (size_t)u_vrow * 16);
   // four tokens per step: their probabilities, scales and zeros in 16- and
@@ -980,7 +1062,13 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
     f4 s4 = {0.0f, 0.0f, 0.0f, 0.0f};
     uint2 z2 = make_uint2(0u, 0u);
     if (t0 < n_qv) {
-      s4 = *(const f4 *)(vsc + t0);
+      if constexpr (S16) {
+        const uint2 ss = *(const uint2 *)((const uint16_t *)vsc + t0);
+        s4 = (f4){h2f((uint16_t)(ss.x & 0xFFFFu)), h2f((uint16_t)(ss.x >> 16)),
+                  h2f((uint16_t)(ss.y & 0xFFFFu)), h2f((uint16_t)(ss.y >> 16))};
+      } else {
+        s4 = *(const f4 *)((const float *)vsc + t0);
+      }
       z2 = *(const uint2 *)(vz + t0);
     }
 #pragma unroll
@@ -1035,7 +1123,7 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
 // The masked variant holds the block's mask in registers as well; it may
 // use more than half the register file rather than spill, since a spill
 // reload inside the block loop would wait for every DMA in flight.
-template <int NREP, bool MASKED, bool RAGGED, bool PAGED>
+template <int NREP, bool MASKED, bool RAGGED, bool PAGED, bool S16>
 __global__ void __launch_bounds__(MASKED ? 256 : 512)
     __attribute__((amdgpu_waves_per_eu(MASKED ? 1 : 2)))
     decode_matrix_kernel(DecodeArgs a, int64_t n_main_all, int n_groups_all, int n_window_all,
@@ -1099,12 +1187,12 @@ __global__ void __launch_bounds__(MASKED ? 256 : 512)
   int item = draw_item(&sm_ctr, lane);
   while (item < sh.n_skip) {
     const int x = (int)s + item * n_groups;
-    const WinLoads<NREP> ld = window_issue<NREP, PAGED>(a, rs, n_main, x, hk, b, L);
-    window_role<NREP, MASKED, PAGED>(a, rs, n_main, x, n_groups + x, hk, b, L, ld);
+    const WinLoads<NREP> ld = window_issue<NREP, PAGED, S16>(a, rs, n_main, x, hk, b, L);
+    window_role<NREP, MASKED, PAGED, S16>(a, rs, n_main, x, n_groups + x, hk, b, L, ld);
     wave_lds_sync();   // the LDS reads of the chunk are done
     item = draw_item(&sm_ctr, lane);
   }
-  block_role<NREP, MASKED, PAGED>(a, sh, item - sh.n_skip, hk, b, L, &sm_k[w], &sm_v[w]);
+  block_role<NREP, MASKED, PAGED, S16>(a, sh, item - sh.n_skip, hk, b, L, &sm_k[w], &sm_v[w]);
 
   // The W partials of the workgroup's waves, merged with the log-sum-exp
   // rule into partial slot s of the slab: thread e takes channel e % 128 of
@@ -1180,13 +1268,19 @@ __global__ void __launch_bounds__(MASKED ? 256 : 512)
   }
 }
 
+template <bool S16>
+static bool layout_is(const Layout &L) {
+  using RC = Rec<S16>;
+  return L.sb == RC::sb && L.rec == RC::bytes && L.kc == RC::kc && L.ks == RC::ks &&
+         L.kz == RC::kz && L.vc == RC::vc && L.vs == RC::vs && L.vz == RC::vz;
+}
+
 bool decode_matrix_supported(const DecodeArgs &a) {
-  // records of the 2-bit / G 32 / head_dim 128 shape, copied 16 bytes at a
-  // time like the window rows and q
+  // records of the 2-bit / G 32 / head_dim 128 shape (fp32 or fp16 scales),
+  // copied 16 bytes at a time like the window rows and q
   return a.kb == 2 && a.vb == 2 && a.G == kG && a.D == kD &&
-         (a.n_rep == 1 || a.n_rep == 2 || a.n_rep == 4) && a.L.rec == kRecBytes &&
-         a.L.kc == kRecKc && a.L.ks == kRecKs && a.L.kz == kRecKz && a.L.vc == kRecVc &&
-         a.L.vs == kRecVs && a.L.vz == kRecVz && ((uintptr_t)a.L.blocks & 15) == 0 &&
+         (a.n_rep == 1 || a.n_rep == 2 || a.n_rep == 4) &&
+         (layout_is<false>(a.L) || layout_is<true>(a.L)) && ((uintptr_t)a.L.blocks & 15) == 0 &&
          ((uintptr_t)a.k_res & 15) == 0 && ((uintptr_t)a.v_res & 15) == 0 &&
          ((uintptr_t)a.q & 15) == 0;
 }
@@ -1197,34 +1291,42 @@ int decode_matrix_window_chunks(const DecodeArgs &a, int64_t n_main) {
 
 int decode_matrix_waves(const DecodeArgs &a) { return a.mask ? 4 : 8; }
 
-template <int NREP, bool RAGGED, bool PAGED>
+template <int NREP, bool RAGGED, bool PAGED, bool S16>
 static void launch_rep(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
                        int n_groups, int n_window, const MatrixRowArg<RAGGED> &rows) {
   if (a.mask)
-    hipLaunchKernelGGL((decode_matrix_kernel<NREP, true, RAGGED, PAGED>), grid, dim3(256), 0, s,
-                       a, n_main, n_groups, n_window, rows);
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, true, RAGGED, PAGED, S16>), grid, dim3(256), 0,
+                       s, a, n_main, n_groups, n_window, rows);
   else
-    hipLaunchKernelGGL((decode_matrix_kernel<NREP, false, RAGGED, PAGED>), grid, dim3(512), 0, s,
-                       a, n_main, n_groups, n_window, rows);
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, false, RAGGED, PAGED, S16>), grid, dim3(512),
+                       0, s, a, n_main, n_groups, n_window, rows);
 }
 
-template <bool RAGGED, bool PAGED>
-static void launch_paged(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
-                         int n_groups, int n_window, const MatrixRowArg<RAGGED> &rows) {
+template <bool RAGGED, bool PAGED, bool S16>
+static void launch_layout(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
+                          int n_groups, int n_window, const MatrixRowArg<RAGGED> &rows) {
   switch (a.n_rep) {
-    case 1: launch_rep<1, RAGGED, PAGED>(a, grid, s, n_main, n_groups, n_window, rows); break;
-    case 2: launch_rep<2, RAGGED, PAGED>(a, grid, s, n_main, n_groups, n_window, rows); break;
-    default: launch_rep<4, RAGGED, PAGED>(a, grid, s, n_main, n_groups, n_window, rows); break;
+    case 1: launch_rep<1, RAGGED, PAGED, S16>(a, grid, s, n_main, n_groups, n_window, rows); break;
+    case 2: launch_rep<2, RAGGED, PAGED, S16>(a, grid, s, n_main, n_groups, n_window, rows); break;
+    default: launch_rep<4, RAGGED, PAGED, S16>(a, grid, s, n_main, n_groups, n_window, rows); break;
   }
 }
 
 template <bool RAGGED>
 static void launch_reps(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
                         int n_groups, int n_window, const MatrixRowArg<RAGGED> &rows) {
-  if (a.L.pt)
-    launch_paged<RAGGED, true>(a, grid, s, n_main, n_groups, n_window, rows);
-  else
-    launch_paged<RAGGED, false>(a, grid, s, n_main, n_groups, n_window, rows);
+  const bool s16 = a.L.sb == 2;
+  if (a.L.pt) {
+    if (s16)
+      launch_layout<RAGGED, true, true>(a, grid, s, n_main, n_groups, n_window, rows);
+    else
+      launch_layout<RAGGED, true, false>(a, grid, s, n_main, n_groups, n_window, rows);
+  } else {
+    if (s16)
+      launch_layout<RAGGED, false, true>(a, grid, s, n_main, n_groups, n_window, rows);
+    else
+      launch_layout<RAGGED, false, false>(a, grid, s, n_main, n_groups, n_window, rows);
+  }
 }
 
 hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int n_groups,

@@ -134,7 +134,7 @@ __device__ __forceinline__ float uniform(float v) {
 // MODE 2 (selected): attention whose scores are read from a.scores, with -inf
 // for a token that the row's selection rule (a.sel) does not take; no keys
 // are read.
-template <int KB, int VB, int NH, bool RAGGED, int MODE, bool PAGED>
+template <int KB, int VB, int NH, bool RAGGED, int MODE, bool PAGED, bool S16>
 __global__ void __launch_bounds__(kVThreads)
     __attribute__((amdgpu_waves_per_eu(2)))   // two waves per SIMD: the compiler may use 256 VGPRs
 decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int direct,
@@ -208,11 +208,13 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
     for (int j = 0; j < NH; ++j) selr[j] = a.sel[(int64_t)b * a.Hq + hq0 + j];
   }
   const uint32_t kc_lane = (uint32_t)L.kc + (uint32_t)lane * (2 * KB) * 4u;
-  const uint32_t ks_lane = (uint32_t)L.ks + (uint32_t)lane * 8u;
+  // fp16-scale layout (S16): scales of 2 bytes, the sections after them
+  // moved up
+  const uint32_t ks_lane = (uint32_t)L.ks + (uint32_t)lane * (S16 ? 4u : 8u);
   const uint32_t kz_lane = (uint32_t)L.kz + (uint32_t)lane * 4u;
   const uint32_t kr_lane = (uint32_t)lane * 4u;
   const uint32_t vc_lane = (uint32_t)L.vc + (uint32_t)qd * VWQ * 4u;
-  const uint32_t vs_lane = (uint32_t)L.vs + (uint32_t)qd * (kRecTokens * 4u);
+  const uint32_t vs_lane = (uint32_t)L.vs + (uint32_t)qd * (kRecTokens * (S16 ? 2u : 4u));
   const uint32_t vz_lane = (uint32_t)L.vz + (uint32_t)qd * (kRecTokens * 2u);
   const uint32_t vr_lane = (uint32_t)qd * 64u;
 
@@ -221,11 +223,15 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
   // arithmetic of the group before.  The loads are unconditional: every
   // group below g_end lies inside the capacity (the words of a window group
   // are loaded and not used) and the mask index is clamped to the last token.
+  // fp16 scales stay raw words until they are used, so that no fetch waits
+  // for its own loads to widen them
   struct Raw {
     uint32_t kw[2 * KB];
-    float2 ks, kz;
+    std::conditional_t<S16, uint32_t, float2> ks;
+    float2 kz;
     uint32_t vw[2][VWQ];
-    float vs[2], vz[2], mk[2];
+    std::conditional_t<S16, uint32_t, float> vs[2];
+    float vz[2], mk[2];
     float ss[SELECTED ? NH : 1][2];   // stored scores (selected attention)
   };
   // paged cache: the row's line of the page table and the head's record in
@@ -257,7 +263,10 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
     const uint32_t lg = (uint32_t)(g & 3);               // group within the record
     if constexpr (!SELECTED) {
       load_words<KB / 2>((const uint32_t *)(recp + (r0 + lg * (kVD * KB * 4u) + kc_lane)), r.kw);
-      r.ks = *(const float2 *)(recp + (r0 + lg * (kVD * 4u) + ks_lane));
+      if constexpr (S16)
+        r.ks = *(const uint32_t *)(recp + (r0 + lg * (kVD * 2u) + ks_lane));
+      else
+        r.ks = *(const float2 *)(recp + (r0 + lg * (kVD * 4u) + ks_lane));
       const uint32_t zz = *(const uint32_t *)(recp + (r0 + lg * (kVD * 2u) + kz_lane));
       r.kz = make_float2(h2f((uint16_t)(zz & 0xFFFFu)), h2f((uint16_t)(zz >> 16)));
     }
@@ -286,7 +295,10 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
         r.vw[hh][0] = v.x;
         r.vw[hh][1] = v.y;
       }
-      r.vs[hh] = *(const float *)(recp + (r0 + vs_lane + tl * 4u));
+      if constexpr (S16)
+        r.vs[hh] = *(const uint16_t *)(recp + (r0 + vs_lane + tl * 2u));
+      else
+        r.vs[hh] = *(const float *)(recp + (r0 + vs_lane + tl * 4u));
       r.vz[hh] = h2f(*(const uint16_t *)(recp + (r0 + vz_lane + tl * 2u)));
     }
   };
@@ -307,11 +319,19 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
       }
     } else {
       const bool quantized = t0 < n_kq;     // n_kq is a multiple of the group size
+      float ksx, ksy;
+      if constexpr (S16) {
+        ksx = h2f((uint16_t)(cur.ks & 0xFFFFu));
+        ksy = h2f((uint16_t)(cur.ks >> 16));
+      } else {
+        ksx = cur.ks.x;
+        ksy = cur.ks.y;
+      }
       float qs0[NH], qs1[NH], qz[NH];
 #pragma unroll
       for (int j = 0; j < NH; ++j) {
-        qs0[j] = q0[j] * cur.ks.x;
-        qs1[j] = q1[j] * cur.ks.y;
+        qs0[j] = q0[j] * ksx;
+        qs1[j] = q1[j] * ksy;
         qz[j] = fmaf(q1[j], cur.kz.y, q0[j] * cur.kz.x);
       }
       // fp16 key window: token tau sits in row tau mod R; R is a multiple of
@@ -403,9 +423,14 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
       if (tau < s1) {
         if (tau < n_vq) {
           float ps[NH];
+          float vsc;
+          if constexpr (S16)
+            vsc = h2f((uint16_t)cur.vs[hh]);
+          else
+            vsc = cur.vs[hh];
 #pragma unroll
           for (int j = 0; j < NH; ++j) {
-            ps[j] = p[j][hh] * cur.vs[hh];
+            ps[j] = p[j][hh] * vsc;
             az[j] = fmaf(p[j][hh], cur.vz[hh], az[j]);
           }
 #pragma unroll
@@ -538,56 +563,65 @@ bool decode_vector_supported(const DecodeArgs &a) {
 // One query head per KV head: NH = 1.  An even number: NH = 2, and n_rep / 2
 // workgroups per (split, slab), each for two of the heads (four heads in one
 // workgroup would not fit two waves per SIMD).
-template <int KB, int VB, bool RAGGED, int MODE, bool PAGED>
+template <int KB, int VB, bool RAGGED, int MODE, bool PAGED, bool S16>
 static void launch_bits(const DecodeArgs &a, dim3 grid, int tps, int direct, hipStream_t s,
                         const RowArg<RAGGED> &rows) {
   if (a.n_rep == 1) {
-    hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 1, RAGGED, MODE, PAGED>), grid, dim3(kVThreads),
+    hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 1, RAGGED, MODE, PAGED, S16>), grid, dim3(kVThreads),
                        0, s, a, tps, 1, direct, rows);
   } else {
     if constexpr (MODE == 1) {
       // scores only: no value accumulators, so one workgroup takes every
       // head of the KV head and reads its keys once
       if (a.n_rep == 4) {
-        hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 4, RAGGED, MODE, PAGED>), grid,
+        hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 4, RAGGED, MODE, PAGED, S16>), grid,
                            dim3(kVThreads), 0, s, a, tps, 1, direct, rows);
         return;
       }
       if (a.n_rep == 8) {
-        hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 8, RAGGED, MODE, PAGED>), grid,
+        hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 8, RAGGED, MODE, PAGED, S16>), grid,
                            dim3(kVThreads), 0, s, a, tps, 1, direct, rows);
         return;
       }
     }
     const int chunks = a.n_rep / 2;
     grid.y *= chunks;
-    hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 2, RAGGED, MODE, PAGED>), grid, dim3(kVThreads),
+    hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 2, RAGGED, MODE, PAGED, S16>), grid, dim3(kVThreads),
                        0, s, a, tps, chunks, direct, rows);
   }
 }
 
-template <bool RAGGED, int MODE, bool PAGED>
-static void launch_bits_paged(const DecodeArgs &a, dim3 grid, int tps, int direct, hipStream_t s,
-                              const RowArg<RAGGED> &rows) {
+template <bool RAGGED, int MODE, bool PAGED, bool S16>
+static void launch_bits_layout(const DecodeArgs &a, dim3 grid, int tps, int direct, hipStream_t s,
+                               const RowArg<RAGGED> &rows) {
   if (a.kb == 2 && a.vb == 2)
-    launch_bits<2, 2, RAGGED, MODE, PAGED>(a, grid, tps, direct, s, rows);
+    launch_bits<2, 2, RAGGED, MODE, PAGED, S16>(a, grid, tps, direct, s, rows);
   else if (a.kb == 2)
-    launch_bits<2, 4, RAGGED, MODE, PAGED>(a, grid, tps, direct, s, rows);
+    launch_bits<2, 4, RAGGED, MODE, PAGED, S16>(a, grid, tps, direct, s, rows);
   else if (a.vb == 2)
-    launch_bits<4, 2, RAGGED, MODE, PAGED>(a, grid, tps, direct, s, rows);
+    launch_bits<4, 2, RAGGED, MODE, PAGED, S16>(a, grid, tps, direct, s, rows);
   else
-    launch_bits<4, 4, RAGGED, MODE, PAGED>(a, grid, tps, direct, s, rows);
+    launch_bits<4, 4, RAGGED, MODE, PAGED, S16>(a, grid, tps, direct, s, rows);
 }
 
-// A paged cache takes its own instantiations (PAGED), so that the
-// contiguous ones keep their registers.
+// A paged cache (PAGED) and the fp16-scale layout (S16) take their own
+// instantiations, so that the contiguous fp32-scale ones keep their
+// registers and schedule.
 template <bool RAGGED, int MODE>
 static void launch_all_bits(const DecodeArgs &a, dim3 grid, int tps, int direct, hipStream_t s,
                             const RowArg<RAGGED> &rows) {
-  if (a.L.pt)
-    launch_bits_paged<RAGGED, MODE, true>(a, grid, tps, direct, s, rows);
-  else
-    launch_bits_paged<RAGGED, MODE, false>(a, grid, tps, direct, s, rows);
+  const bool s16 = a.L.sb == 2;
+  if (a.L.pt) {
+    if (s16)
+      launch_bits_layout<RAGGED, MODE, true, true>(a, grid, tps, direct, s, rows);
+    else
+      launch_bits_layout<RAGGED, MODE, true, false>(a, grid, tps, direct, s, rows);
+  } else {
+    if (s16)
+      launch_bits_layout<RAGGED, MODE, false, true>(a, grid, tps, direct, s, rows);
+    else
+      launch_bits_layout<RAGGED, MODE, false, false>(a, grid, tps, direct, s, rows);
+  }
 }
 
 // With a single split (n_splits == 1) the kernel writes the normalized

@@ -17,8 +17,8 @@ __device__ __forceinline__ float h2f(uint16_t h) {
   return __half2float(__ushort_as_half(h));
 }
 
-// Bit pattern of an fp32 value that is exactly an fp16 value (a zero point:
-// the minimum of fp16 inputs), converted without rounding.
+// fp32 -> binary16 bit pattern, round to nearest even: exact for a value
+// that is an fp16 value (a zero point, the minimum of fp16 inputs).
 __device__ __forceinline__ uint16_t f2h_bits(float f) {
   return __half_as_ushort(__float2half_rn(f));
 }
@@ -38,12 +38,16 @@ constexpr int kRecTokens = 128;
 // pt[b nrec + j].  A page index outside [0, n_pages) is clamped into the
 // pool: a caller error, whose results are unspecified, never makes an access
 // leave it.
+// Scales are fp32, or binary16 in the fp16-scale layout (sb == 2), where the
+// stored scale is s rounded to the nearest binary16 value and the codes are
+// chosen for it (stored_scale).
 struct Layout {
   uint8_t *blocks;
   int64_t rec;        // bytes per record
   int64_t nrec;       // records per slab (capacity / 128)
   int32_t kc, ks, kz, vc, vs, vz;   // section offsets in bytes
   int32_t D, G, kb, vb;
+  int32_t sb;         // bytes per stored scale: 4, or 2 (fp16 scales)
   const int32_t *pt;  // page table [B][nrec] (device) or nullptr
   int64_t n_pages;
   int32_t H;          // KV heads: records per page
@@ -67,8 +71,25 @@ struct Layout {
   __device__ __forceinline__ uint32_t *key_codes(int64_t bh, int64_t g, int c) const {
     return (uint32_t *)(record(bh, g * G) + kc) + key_index(g, c) * (G * kb / 32);
   }
-  __device__ __forceinline__ float *key_scale(int64_t bh, int64_t g, int c) const {
-    return (float *)(record(bh, g * G) + ks) + key_index(g, c);
+  __device__ __forceinline__ float key_scale(int64_t bh, int64_t g, int c) const {
+    const uint8_t *p = record(bh, g * G) + ks + key_index(g, c) * sb;
+    return sb == 2 ? h2f(*(const uint16_t *)p) : *(const float *)p;
+  }
+  // element i of a run of stored scales starting at p
+  __device__ __forceinline__ float scale_at(const uint8_t *p, int64_t i) const {
+    return sb == 2 ? h2f(((const uint16_t *)p)[i]) : ((const float *)p)[i];
+  }
+  // the scales of key group g, channels 0 .. D-1 (a run for scale_at)
+  __device__ __forceinline__ const uint8_t *key_scales(int64_t bh, int64_t g) const {
+    return record(bh, g * G) + ks + key_index(g, 0) * sb;
+  }
+  // s: a stored_scale value (exact in the layout's precision)
+  __device__ __forceinline__ void put_key_scale(int64_t bh, int64_t g, int c, float s) const {
+    uint8_t *p = record(bh, g * G) + ks + key_index(g, c) * sb;
+    if (sb == 2)
+      *(uint16_t *)p = f2h_bits(s);
+    else
+      *(float *)p = s;
   }
   __device__ __forceinline__ uint16_t *key_zero(int64_t bh, int64_t g, int c) const {
     return (uint16_t *)(record(bh, g * G) + kz) + key_index(g, c);
@@ -77,8 +98,17 @@ struct Layout {
   __device__ __forceinline__ uint32_t *value_codes(int64_t bh, int64_t tau) const {
     return (uint32_t *)(record(bh, tau) + vc) + (tau % kRecTokens) * (D * vb / 32);
   }
-  __device__ __forceinline__ float *value_scale(int64_t bh, int64_t tau, int gc) const {
-    return (float *)(record(bh, tau) + vs) + gc * kRecTokens + tau % kRecTokens;
+  __device__ __forceinline__ float value_scale(int64_t bh, int64_t tau, int gc) const {
+    const uint8_t *p = record(bh, tau) + vs + (gc * kRecTokens + tau % kRecTokens) * sb;
+    return sb == 2 ? h2f(*(const uint16_t *)p) : *(const float *)p;
+  }
+  __device__ __forceinline__ void put_value_scale(int64_t bh, int64_t tau, int gc,
+                                                  float s) const {
+    uint8_t *p = record(bh, tau) + vs + (gc * kRecTokens + tau % kRecTokens) * sb;
+    if (sb == 2)
+      *(uint16_t *)p = f2h_bits(s);
+    else
+      *(float *)p = s;
   }
   __device__ __forceinline__ uint16_t *value_zero(int64_t bh, int64_t tau, int gc) const {
     return (uint16_t *)(record(bh, tau) + vz) + gc * kRecTokens + tau % kRecTokens;
@@ -87,13 +117,15 @@ struct Layout {
 
 // Section offsets and record size for a shape; rec = 0 if the layout does
 // not take it (bits other than 2 and 4, G not dividing 128 or D).
-inline Layout make_layout(uint8_t *blocks, int D, int kb, int vb, int G, int64_t cap) {
+inline Layout make_layout(uint8_t *blocks, int D, int kb, int vb, int G, int64_t cap,
+                          bool scale_fp16 = false) {
   Layout L{};
   L.blocks = blocks;
   L.D = D;
   L.G = G;
   L.kb = kb;
   L.vb = vb;
+  L.sb = scale_fp16 ? 2 : 4;
   const bool ok = (kb == 2 || kb == 4) && (vb == 2 || vb == 4) && G > 0 && D > 0 &&
                   kRecTokens % G == 0 && D % G == 0 && G % (32 / kb) == 0 &&
                   G % (32 / vb) == 0;
@@ -101,10 +133,10 @@ inline Layout make_layout(uint8_t *blocks, int D, int kb, int vb, int G, int64_t
   const int groups = kRecTokens / G;
   L.kc = 0;
   L.ks = L.kc + kRecTokens * D * kb / 8;
-  L.kz = L.ks + groups * D * 4;
+  L.kz = L.ks + groups * D * L.sb;
   L.vc = L.kz + groups * D * 2;
   L.vs = L.vc + kRecTokens * D * vb / 8;
-  L.vz = L.vs + (D / G) * kRecTokens * 4;
+  L.vz = L.vs + (D / G) * kRecTokens * L.sb;
   L.rec = L.vz + (D / G) * kRecTokens * 2;
   L.nrec = cap / kRecTokens;
   return L;
@@ -209,6 +241,13 @@ __device__ __forceinline__ float group_scale(float mn, float mx, int bits) {
   return (mx - mn) / (float)((1 << bits) - 1);
 }
 
+// The scale a group stores and quantizes with: s, or in the fp16-scale
+// layout s rounded to the nearest binary16 value (v_cvt_f16_f32: round to
+// nearest even, subnormals kept); a scale that rounds to 0 gives all codes 0.
+__device__ __forceinline__ float stored_scale(float s, const Layout &L) {
+  return L.sb == 2 ? h2f(f2h_bits(s)) : s;
+}
+
 __device__ __forceinline__ uint32_t quant_code(float x, float z, float s, int bits) {
   if (s == 0.0f) return 0u;
   float r = rintf((x - z) / s);
@@ -219,9 +258,11 @@ __device__ __forceinline__ uint32_t quant_code(float x, float z, float s, int bi
 
 // The same code as quant_code, with the division done once per group: r is
 // v_rcp_f32(s) (relative error <= 2^-23).  q = (x - z) * r then lies within
-// |(x - z) / s| * 2^-21.5 < 1e-5 of the correctly rounded quotient (codes are
-// at most 15), so both round to the same integer unless q is within 1e-5 of
-// a half-integer; those rare elements take the exact IEEE division.
+// |(x - z) / s| * 2^-21.5 < 1e-5 of the correctly rounded quotient (the
+// quotient is at most 15, or 22.5 with an fp16 scale rounded down from a
+// subnormal value: 1.5 x 15), so both round to the same integer unless q is
+// within 1e-5 of a half-integer; those rare elements take the exact IEEE
+// division.
 __device__ __forceinline__ uint32_t quant_code_r(float x, float z, float s, float r, int bits) {
   if (s == 0.0f) return 0u;
   const float u = x - z;

@@ -24,7 +24,7 @@ __device__ __forceinline__ void quantize_key_group(const TokenSource &src, int64
     mn = x < mn ? x : mn;
     mx = x > mx ? x : mx;
   }
-  const float s = group_scale(mn, mx, bits);
+  const float s = stored_scale(group_scale(mn, mx, bits), L);
   uint32_t *dst = L.key_codes(bh, g, c);
   for (int w = 0; w < words; ++w) {
     uint32_t word = 0;
@@ -34,7 +34,7 @@ __device__ __forceinline__ void quantize_key_group(const TokenSource &src, int64
     }
     dst[w] = word;
   }
-  *L.key_scale(bh, g, c) = s;
+  L.put_key_scale(bh, g, c, s);
   *L.key_zero(bh, g, c) = f2h_bits(mn);
 }
 
@@ -68,14 +68,14 @@ value_rows_kernel(TokenSource src, int64_t tau_first, int64_t n_rows, Layout L) 
       mn = x < mn ? x : mn;
       mx = x > mx ? x : mx;
     }
-    const float s = group_scale(mn, mx, bits);
+    const float s = stored_scale(group_scale(mn, mx, bits), L);
     for (int w = 0; w < G / per; ++w) {
       uint32_t word = 0;
       for (int e = 0; e < per; ++e)
         word |= quant_code(h2f(row[g * G + w * per + e]), mn, s, bits) << (bits * e);
       dst[(g * G) / per + w] = word;
     }
-    *L.value_scale(bh, tau, g) = s;
+    L.put_value_scale(bh, tau, g, s);
     *L.value_zero(bh, tau, g) = f2h_bits(mn);
   }
 }
@@ -153,7 +153,7 @@ key_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t g_first, 
   for (int k = 0; k < CPT; ++k) {
     float mn, mx;
     group_first_min_max(v[k], mn, mx);
-    const float s = group_scale(mn, mx, BITS);
+    const float s = stored_scale(group_scale(mn, mx, BITS), L);
     const float r = __builtin_amdgcn_rcpf(s);
 #pragma unroll
     for (int w = 0; w < words; ++w) {
@@ -176,11 +176,10 @@ key_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t g_first, 
 #pragma unroll
     for (int w = 0; w < CPT * words; ++w) dst[w] = out[w];
   }
-  float *ds = L.key_scale(bh, gd, c0);
   uint16_t *dz = L.key_zero(bh, gd, c0);
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
-    ds[k] = sv[k];
+    L.put_key_scale(bh, gd, c0 + k, sv[k]);
     dz[k] = zv[k];
   }
 }
@@ -217,7 +216,7 @@ value_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t n_rows,
     for (int i = 0; i < G; ++i) v[i] = h2f(v16[i]);
     float mn, mx;
     group_first_min_max(v, mn, mx);
-    const float s = group_scale(mn, mx, BITS);
+    const float s = stored_scale(group_scale(mn, mx, BITS), L);
     const float r = __builtin_amdgcn_rcpf(s);
     const int64_t tau = tau_first + r0 + t;
     uint32_t *dst = out_s + t * kWords + (g * G) / per;
@@ -229,7 +228,7 @@ value_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t n_rows,
         word |= quant_code_r(v[w * per + e], mn, s, r, BITS) << (BITS * e);
       dst[w] = word;
     }
-    *L.value_scale(bh, tau, g) = s;
+    L.put_value_scale(bh, tau, g, s);
     *L.value_zero(bh, tau, g) = f2h_bits(mn);
   }
   __syncthreads();
@@ -324,14 +323,14 @@ __device__ __forceinline__ void append_one_slab(const uint16_t *__restrict__ k_n
     const float x = h2f(v_res[on ? slot : (bh * R + t0 % R) * D]);
     float mn = x, mx = x;
     lanes_first_min_max(mn, mx, c, G);
-    const float sc = group_scale(mn, mx, bits);
+    const float sc = stored_scale(group_scale(mn, mx, bits), L);
     const int per = 32 / bits;
     uint32_t w = quant_code(x, mn, sc, bits) << (bits * (c % per));
     for (int o = 1; o < per; o <<= 1) w |= __shfl_xor(w, o);
     const int64_t tau = t0 - R;
     if (on && c % per == 0) L.value_codes(bh, tau)[c / per] = w;
     if (on && c % G == 0) {
-      *L.value_scale(bh, tau, c / G) = sc;
+      L.put_value_scale(bh, tau, c / G, sc);
       *L.value_zero(bh, tau, c / G) = f2h_bits(mn);
     }
   }

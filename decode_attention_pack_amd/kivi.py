@@ -22,7 +22,7 @@ KIVI_ERR_WORKSPACE = -3
 KIVI_ERR_HIP = -4
 KIVI_PATH_AUTO, KIVI_PATH_GENERIC, KIVI_PATH_MATRIX, KIVI_PATH_VECTOR = 0, 1, 2, 3
 
-EXPORTED = ("kivi_record_bytes", "kivi_pack_keys", "kivi_pack_values", "kivi_append",
+EXPORTED = ("kivi_record_bytes", "kivi_record_bytes_ex", "kivi_pack_keys", "kivi_pack_values", "kivi_append",
             "kivi_append_row", "kivi_decode_attn", "kivi_decode_attn_ex",
             "kivi_decode_attn_workspace_bytes",
             "kivi_decode_attn_workspace_bytes_ex", "kivi_decode_step", "kivi_decode_attn_noalloc",
@@ -47,6 +47,7 @@ class CCache(ctypes.Structure):
         ("blocks", ctypes.c_void_p), ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
         ("row_tokens", ctypes.POINTER(ctypes.c_int64)),
         ("page_table", ctypes.c_void_p), ("n_pages", ctypes.c_int64),
+        ("scale_fp16", ctypes.c_int32),
     ]
 
 
@@ -65,6 +66,8 @@ def lib():
     P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     L.kivi_record_bytes.argtypes = [i32, i32, i32, i32]
     L.kivi_record_bytes.restype = sz
+    L.kivi_record_bytes_ex.argtypes = [i32, i32, i32, i32, i32]
+    L.kivi_record_bytes_ex.restype = sz
     for name in ("kivi_pack_keys", "kivi_pack_values"):
         fn = getattr(L, name)
         fn.argtypes = [ctypes.POINTER(CCache), P, i64, i64, P]
@@ -123,19 +126,20 @@ def _dev(t: torch.Tensor, dtype, shape, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def record_bytes(D, kb, vb, G) -> int:
-    """Bytes of one 128-token record of the packed store (include/kivi.h)."""
-    n = int(lib().kivi_record_bytes(D, kb, vb, G))
+def record_bytes(D, kb, vb, G, scale_fp16=False) -> int:
+    """Bytes of one 128-token record of the packed store (include/kivi.h),
+    with fp32 or (scale_fp16) fp16 scales."""
+    n = int(lib().kivi_record_bytes_ex(D, kb, vb, G, int(bool(scale_fp16))))
     if n == 0:
         raise KiviError(KIVI_ERR_INVALID_ARG, f"no record layout for D={D} bits={kb}/{vb} G={G}")
     return n
 
 
-def layout_shapes(B, H, D, kb, vb, G, R, cap, pages=None):
+def layout_shapes(B, H, D, kb, vb, G, R, cap, pages=None, scale_fp16=False):
     """Shapes of the cache arrays (include/kivi.h storage layout); with
     `pages`, a paged cache: a pool of that many pages of H records and a page
     table [B][cap/128]."""
-    rb = record_bytes(D, kb, vb, G)
+    rb = record_bytes(D, kb, vb, G, scale_fp16)
     shapes = {
         "blocks": (B, H, cap // TOKENS_PER_RECORD, rb) if pages is None else (pages, H, rb),
         "k_res": (B, H, R, D),
@@ -159,17 +163,19 @@ class Cache:
     token count (``row_tokens``), all rows starting empty.  ``pages=N`` gives a
     paged cache: ``blocks`` is a pool of N pages of H records, and
     ``page_table`` (int32 [B][cap/128], zero-filled) names the page of each
-    128-token block of each row; the caller fills it."""
+    128-token block of each row; the caller fills it.  ``scale_fp16=True``
+    stores the scales as binary16 (the fp16-scale layout)."""
 
     def __init__(self, batch, n_kv_heads, head_dim, k_bits, v_bits, group, residual, capacity,
-                 device="cuda", arrays=None, ragged=False, pages=None):
+                 device="cuda", arrays=None, ragged=False, pages=None, scale_fp16=False):
         self.B, self.H, self.D = batch, n_kv_heads, head_dim
         self.kb, self.vb, self.G, self.R, self.cap = k_bits, v_bits, group, residual, capacity
+        self.scale_fp16 = bool(scale_fp16)
         if capacity % TOKENS_PER_RECORD:
             raise KiviError(KIVI_ERR_INVALID_ARG,
                             f"capacity {capacity} must be a multiple of {TOKENS_PER_RECORD}")
         shapes = layout_shapes(batch, n_kv_heads, head_dim, k_bits, v_bits, group, residual,
-                               capacity, pages)
+                               capacity, pages, self.scale_fp16)
         if arrays is None:
             arrays = {n: torch.empty(s, dtype=_DT[n], device=device) for n, s in shapes.items()}
             if pages is not None:
@@ -189,7 +195,7 @@ class Cache:
                         ctypes.cast(self._rows, ctypes.POINTER(ctypes.c_int64))
                         if ragged else None,
                         arrays["page_table"].data_ptr() if pages is not None else None,
-                        pages or 0)
+                        pages or 0, int(self.scale_fp16))
 
     def __getattr__(self, name):
         arrays = self.__dict__.get("arrays")

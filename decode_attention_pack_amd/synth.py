@@ -46,6 +46,7 @@ class Workload:
     T0: int
     steps: int
     outlier_fixed: float | None  # fixed factor, or None for U[10, 20]
+    scale_fp16: bool = False     # the cache stores its scales as binary16
 
     @property
     def capacity(self) -> int:

@@ -43,6 +43,9 @@
  *                                         channels)
  *   value scales f32 [D/G][128]           channel group, token of the record
  *   value zeros  f16 [D/G][128]
+ * With scale_fp16 = 1 both scale sections hold binary16 values ([128/G][D]
+ * and [D/G][128] of 2 bytes; RB = kivi_record_bytes_ex(D, kb, vb, G, 1)),
+ * the sections after them moving up accordingly.
  *   k_res    fp16 [B][H][R][D]              the fp16 residual window (KIVI
  *   v_res    fp16 [B][H][R][D]              item 4); token tau lives in slot
  *                                           tau % R
@@ -55,7 +58,13 @@
  * Quantizer (KIVI item 1), bit-exact with an fp32 CPU reference: per group,
  * z = min x, s = (max x - min x) / (2^B - 1) (IEEE fp32 division), code =
  * clamp(round_half_even((x - z) / s), 0, 2^B - 1); a group with max == min
- * stores s = 0 and all-zero codes.
+ * stores s = 0 and all-zero codes.  fp16-scale layout (scale_fp16 = 1; the
+ * page fixes no storage precision for s, and its item 6 puts storage on the
+ * hyperparameter axis): s is rounded to the nearest binary16 value (ties to
+ * even) and the codes are chosen for that stored scale, code =
+ * clamp(round_half_even((x - z) / s16), 0, 2^B - 1); a scale that rounds to
+ * 0 gives all-zero codes.  At 2 bits, G 32, D 128 a record is 12,288 bytes
+ * instead of 14,336.
  */
 #ifndef KIVI_H
 #define KIVI_H
@@ -128,11 +137,16 @@ typedef struct kivi_cache {
   int64_t *row_tokens; /* NULL, or host [batch]: per-row token counts      */
   const int32_t *page_table; /* NULL, or (device) int32 [batch][capacity/128] */
   int64_t n_pages;     /* pages in `blocks` when page_table is set         */
+  int32_t scale_fp16;  /* 0: fp32 scales; 1: fp16 scales (see above)       */
 } kivi_cache;
 
 /* Bytes of one 128-token record for a shape (0 if the shape is invalid);
  * a cache's `blocks` array holds batch * n_kv_heads * capacity/128 of them. */
 size_t kivi_record_bytes(int32_t head_dim, int32_t k_bits, int32_t v_bits, int32_t group);
+/* The same for either scale precision: scale_fp16 0 (fp32 scales, as
+ * kivi_record_bytes) or 1 (fp16 scales); 0 for an invalid shape or flag. */
+size_t kivi_record_bytes_ex(int32_t head_dim, int32_t k_bits, int32_t v_bits, int32_t group,
+                            int32_t scale_fp16);
 
 /* KIVI item 2: quantize keys per channel in groups of `group` consecutive
  * tokens and store them in the records of `dst` (packed along tokens).

@@ -52,12 +52,14 @@ def pool() -> concurrent.futures.ThreadPoolExecutor:
 
 def gpu_cache(w, capacity=None) -> kivi.Cache:
     cap = w.capacity if capacity is None else capacity
-    return kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, cap)
+    return kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, cap,
+                      scale_fp16=w.scale_fp16)
 
 
 def oracle_cache(w, B=None, H=None, capacity=None) -> oracle.Cache:
     return oracle.Cache(w.B if B is None else B, w.Hkv if H is None else H, w.D, w.k_bits,
-                        w.v_bits, w.G, w.R, w.capacity if capacity is None else capacity)
+                        w.v_bits, w.G, w.R, w.capacity if capacity is None else capacity,
+                        scale_fp16=w.scale_fp16)
 
 
 def b16(a: np.ndarray) -> np.ndarray:
@@ -85,7 +87,8 @@ def contiguous_blocks(c) -> np.ndarray:
 def logical(c) -> dict:
     """The logical arrays (k_codes, k_scale, k_zero, v_codes, v_scale, v_zero)
     of a device cache, re-indexed on the host from its records."""
-    return oracle.unpack_records(contiguous_blocks(c), c.B, c.H, c.cap, c.D, c.kb, c.vb, c.G)
+    return oracle.unpack_records(contiguous_blocks(c), c.B, c.H, c.cap, c.D, c.kb, c.vb, c.G,
+                                 getattr(c, "scale_fp16", False))
 
 
 def compare_slab(g: kivi.Cache, b: int, h: int, o: oracle.Cache, ob: int = 0, oh: int = 0,
@@ -153,7 +156,7 @@ def oracle_slab(w, inp, b: int, h: int, n_steps: int = 0, capacity=None) -> orac
     """The oracle's cache of slab (b, h) of workload w: the prefill, then the
     first n_steps appended tokens."""
     o = oracle.Cache(1, 1, w.D, w.k_bits, w.v_bits, w.G, w.R,
-                     w.capacity if capacity is None else capacity)
+                     w.capacity if capacity is None else capacity, scale_fp16=w.scale_fp16)
     o.append(b16(inp["k0"][b:b + 1, h:h + 1]), b16(inp["v0"][b:b + 1, h:h + 1]))
     for s in range(n_steps):
         o.append(b16(inp["k_steps"][s][b:b + 1, h:h + 1]), b16(inp["v_steps"][s][b:b + 1, h:h + 1]))

@@ -296,3 +296,27 @@ def test_paged_rejects(L):
         c.n_pages = n
         assert L.kivi_decode_attn(ctypes.byref(c), FAKE, 2, None, FAKE, FAKE, big, None) == -1
         assert b"n_pages" in L.kivi_last_error()
+
+
+def test_record_bytes_fp16_scales(L):
+    """The fp16-scale layout's record: scale sections of 2 bytes per scale
+    (4096 + 1024 + 1024 + 4096 + 1024 + 1024 = 12288 at 2-bit, G 32,
+    head_dim 128); flag 0 is the fp32 layout; other flags give 0."""
+    assert L.kivi_record_bytes_ex(128, 2, 2, 32, 1) == 12288
+    assert L.kivi_record_bytes_ex(128, 2, 2, 32, 0) == L.kivi_record_bytes(128, 2, 2, 32)
+    assert L.kivi_record_bytes_ex(128, 4, 4, 32, 1) == 8192 + 1024 + 1024 + 8192 + 1024 + 1024
+    assert L.kivi_record_bytes_ex(64, 2, 4, 64, 1) == 2048 + 256 + 256 + 4096 + 256 + 256
+    assert L.kivi_record_bytes_ex(128, 2, 2, 32, 2) == 0
+    assert L.kivi_record_bytes_ex(128, 3, 2, 32, 1) == 0
+
+
+def test_scale_flag_rejected(L):
+    """A cache whose scale_fp16 flag is neither 0 nor 1 is rejected on the
+    host by every entry point that takes a cache."""
+    c = _cache(n_tokens=100)
+    c.scale_fp16 = 3
+    big = 1 << 34
+    assert L.kivi_decode_attn(ctypes.byref(c), FAKE, 2, None, FAKE, FAKE, big, None) == -1
+    assert b"scale_fp16" in L.kivi_last_error()
+    assert _pack(L, "kivi_pack_keys", cache=c) == -1
+    assert b"scale_fp16" in L.kivi_last_error()

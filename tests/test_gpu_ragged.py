@@ -45,7 +45,7 @@ def _oracle_rows(g, inp, lengths):
     """Oracle caches of every slab: row b's prefill alone."""
     def one(bh):
         b, h = bh
-        o = oracle.Cache(1, 1, g.D, g.kb, g.vb, g.G, g.R, g.cap)
+        o = oracle.Cache(1, 1, g.D, g.kb, g.vb, g.G, g.R, g.cap, scale_fp16=g.scale_fp16)
         T = int(lengths[b])
         if T:
             o.append(b16(inp["k0"][b:b + 1, h:h + 1, :T]), b16(inp["v0"][b:b + 1, h:h + 1, :T]))
