@@ -14,7 +14,8 @@ prefill length once it has taken the workload's decode steps, so the timed
 steps attend over the stated context, not a growing one.
 
 `value` is the algorithmic bytes a step must move (packed codes + fp32
-scales + fp16 zero points + fp16 window + q + out, plus the append's bytes)
+scales -- fp16 with --scale-fp16 -- + fp16 zero points + fp16 window + q +
+out, plus the append's bytes)
 divided by the measured step time (HIP events at the two ends of the K timed
 steps).  `roofline` covers the attention launch alone: a second timed loop
 issues kivi_decode_attn calls back to back over the same replicas, in at
@@ -68,6 +69,12 @@ def measured_traffic(workload_name: str):
     return rec.get("traffic_bytes_per_launch")
 
 
+def group_bytes(w) -> int:
+    """Bytes of one group's scale and zero point: an fp32 (or, in the
+    fp16-scale layout, fp16) scale and an fp16 zero point."""
+    return (2 if w.scale_fp16 else 4) + 2
+
+
 def attn_bytes(w, t) -> int:
     """Algorithmic bytes of one kivi_decode_attn call at context t (an int,
     or one count per batch row of a ragged batch)."""
@@ -77,9 +84,10 @@ def attn_bytes(w, t) -> int:
     for tb in ([t] * w.B if isinstance(t, int) else t):
         n_kq = tb - tb % R
         n_vq = max(0, tb - R)
-        # fp32 scale + fp16 zero per group
-        total += (n_kq * D * w.k_bits // 8 + (n_kq // G) * D * 6
-                  + n_vq * D * w.v_bits // 8 + n_vq * (D // G) * 6
+        # scale + fp16 zero per group
+        gb = group_bytes(w)
+        total += (n_kq * D * w.k_bits // 8 + (n_kq // G) * D * gb
+                  + n_vq * D * w.v_bits // 8 + n_vq * (D // G) * gb
                   + ((tb % R) + min(tb, R)) * D * 2
                   + rep * D * 2 + rep * D * 4)
     return total * w.Hkv
@@ -93,17 +101,17 @@ def append_bytes(w, t_before) -> int:
     for tb in ([t_before] * w.B if isinstance(t_before, int) else t_before):
         per = 2 * D * 2 + 2 * D * 2                       # read k, v; write window slots
         if tb >= R:                                       # value leaves the window
-            per += D * 2 + D * w.v_bits // 8 + (D // G) * 6
+            per += D * 2 + D * w.v_bits // 8 + (D // G) * group_bytes(w)
         if (tb + 1) % R == 0:                             # key block quantized
-            per += R * D * 2 + R * D * w.k_bits // 8 + (R // G) * D * 6
+            per += R * D * 2 + R * D * w.k_bits // 8 + (R // G) * D * group_bytes(w)
         total += per
     return total * w.Hkv
 
 
 def pack_bytes(w, T: int, bits: int) -> int:
     """Algorithmic bytes of packing T tokens of keys (or values): fp16 in,
-    codes + fp32 scales + fp16 zeros out."""
-    return w.B * w.Hkv * (T * w.D * 2 + T * w.D * bits // 8 + (T // w.G) * w.D * 6)
+    codes + scales + fp16 zeros out."""
+    return w.B * w.Hkv * (T * w.D * 2 + T * w.D * bits // 8 + (T // w.G) * w.D * group_bytes(w))
 
 
 def time_pack(w, inp, dev, stream, reps: int = 5):
@@ -115,7 +123,7 @@ def time_pack(w, inp, dev, stream, reps: int = 5):
     cap = -(-T // 128) * 128
     k = torch.from_numpy(inp["k0"][:, :, :T]).to(dev).contiguous()
     v = torch.from_numpy(inp["v0"][:, :, :T]).to(dev).contiguous()
-    dst = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.G, cap)
+    dst = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.G, cap, scale_fp16=w.scale_fp16)
     out = {}
     for name, x, bits in (("keys", k, w.k_bits), ("values", v, w.v_bits)):
         fn = kivi.kivi_pack_keys if name == "keys" else kivi.kivi_pack_values
@@ -142,11 +150,11 @@ def select_bytes(w, t: int, sel_union) -> int:
     R, G, D = w.R, w.G, w.D
     n_kq, n_vq = t - t % R, max(0, t - R)
     rep = w.Hq // w.Hkv
-    keys = n_kq * D * w.k_bits // 8 + (n_kq // G) * D * 6 + (t - n_kq) * D * 2
+    keys = n_kq * D * w.k_bits // 8 + (n_kq // G) * D * group_bytes(w) + (t - n_kq) * D * 2
     sel = sel_union.reshape(-1, t)
     n_q = int(sel[:, :n_vq].sum())          # selected quantized values
     n_f = int(sel[:, n_vq:].sum())          # selected fp16 values
-    vals = n_q * (D * w.v_bits // 8 + (D // G) * 6) + n_f * D * 2
+    vals = n_q * (D * w.v_bits // 8 + (D // G) * group_bytes(w)) + n_f * D * 2
     return (keys + rep * D * 6) * w.B * w.Hkv + vals
 
 
@@ -228,7 +236,8 @@ def cpu_baseline(w, inp, lengths, budget_s: float = 10.0):
 
     def build(bh):
         b, h = bh
-        o = oracle.Cache(1, 1, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity)
+        o = oracle.Cache(1, 1, w.D, w.k_bits, w.v_bits, w.G, w.R, w.capacity,
+                         scale_fp16=w.scale_fp16)
         T = lengths[b]
         o.append(np.ascontiguousarray(inp["k0"][b:b + 1, h:h + 1, :T]).view(np.uint16),
                  np.ascontiguousarray(inp["v0"][b:b + 1, h:h + 1, :T]).view(np.uint16))
@@ -294,6 +303,8 @@ def main():
     ap.add_argument("--select", type=float, default=0.0,
                     help="also time kivi_select_attn (token selection by attention mass tau, "
                          "then attention over the selected tokens) on the same replicas")
+    ap.add_argument("--scale-fp16", action="store_true",
+                    help="the fp16-scale layout: scales stored as binary16")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device-to-device copy of this "
                          "many MiB (a known-size reference for hardware byte counters)")
@@ -311,6 +322,7 @@ def main():
 
     ragged = args.workload == synth.RAGGED.index
     w = synth.RAGGED if ragged else synth.WORKLOADS[args.workload]
+    w = w.replace(scale_fp16=args.scale_fp16)
     inp = synth.make_inputs(w.replace(steps=1))
     # prefill length of each batch row (a ragged batch: its own per row)
     lengths = ([int(x) for x in synth.ragged_lengths(w.B, 1024, w.T0)] if ragged
@@ -326,14 +338,16 @@ def main():
     n_cyc = w.steps
     m = w.R * 128 // math.gcd(w.R, 128)
     cap = -(-(w.T0 + n_cyc) // m) * m
-    probe = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, cap)
+    probe = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, cap,
+                       scale_fp16=w.scale_fp16)
     footprint = sum(a.numel() * a.element_size() for a in probe.arrays.values())
     del probe
     L = args.layers or max(2, math.ceil((1 << 30) / footprint))
     print(f"# {w.name}: footprint {footprint / 1e6:.1f} MB/layer, {L} layers, capacity {cap}",
           file=sys.stderr, flush=True)
 
-    base = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, cap, ragged=ragged)
+    base = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, cap, ragged=ragged,
+                      scale_fp16=w.scale_fp16)
     if ragged:
         # each row prefilled alone, as a request entering a serving batch
         for b, T in enumerate(lengths):
@@ -347,7 +361,7 @@ def main():
     for _ in range(L - 1):
         arrays = {n: a.clone() for n, a in base.arrays.items()}
         c = kivi.Cache(w.B, w.Hkv, w.D, w.k_bits, w.v_bits, w.G, w.R, cap, arrays=arrays,
-                       ragged=ragged)
+                       ragged=ragged, scale_fp16=w.scale_fp16)
         if ragged:
             c.set_row_tokens(lengths)
         else:
@@ -478,8 +492,9 @@ def main():
                    **({"row_contexts": [T + 1 for T in lengths]} if ragged else {}),
                    "k_bits": w.k_bits, "v_bits": w.v_bits,
                    "group": w.G, "residual": w.R, "layers_rotated": L,
-                   "storage": "128-token records: packed codes, fp32 scales, fp16 zero points; "
-                              "fp16 window; fp16 q"},
+                   "storage": "128-token records: packed codes, "
+                              + ("fp16" if w.scale_fp16 else "fp32")
+                              + " scales, fp16 zero points; fp16 window; fp16 q"},
         "step_call": "kivi_decode_step" if fused else "kivi_append + kivi_decode_attn",
         "step_contexts_min_max": [step_contexts[0], step_contexts[-1]],
         "us_per_step": round(ms_step * 1e3, 2),
@@ -490,7 +505,8 @@ def main():
         "attn_pct_of_peak": round(100 * attn_gbps / HBM_PEAK_GBPS, 1),
         "roofline": {"bound": "hbm", "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(w.name),
+                     "traffic": measured_traffic(w.name + ("-fp16-scales" if w.scale_fp16
+                                                           else "")),
                      "kernel": "kivi_decode_attn launch (split kernel + combine)",
                      "bytes_per_launch": a2_bytes // (n_rounds * per_round)},
     }
