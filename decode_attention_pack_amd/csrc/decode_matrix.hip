@@ -117,11 +117,12 @@ struct alignas(16) VStage {
 //   dma16:   per-lane 64-bit source address
 //   dma16o:  uniform base + per-lane 32-bit byte offset (the base stays in
 //            scalar registers)
-//   dma16nt: the same with the nontemporal hint, for the record stream: each
+//   dma16nt_m0: the same with the nontemporal hint and the LDS destination
+//            given as a scalar LDS address, for the record stream: each
 //            record is read once per call, and streaming it past the caches
 //            measured ~13% more HBM bandwidth (6.6 against 5.85 TB/s for a
 //            plain read of the records)
-//   dma4o:   4 bytes per lane, uniform base + offset
+//   dma4o_m0: 4 bytes per lane, uniform base + offset
 __device__ __forceinline__ uint32_t lds_m0(lds_void *l) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l);
 }
@@ -141,15 +142,22 @@ __device__ __forceinline__ void dma16o(const void *base, uint32_t off, lds_void 
                "{m0}"(lds_m0(l))
                : "memory");
 }
-__device__ __forceinline__ void dma16nt(const void *base, uint32_t off, lds_void *l) {
+// The same copies with the LDS destination given as a wave-uniform LDS byte
+// address (a scalar value, so that no per-copy move from vector registers
+// or address-space check is needed).
+__device__ __forceinline__ void dma16nt_m0(const void *base, uint32_t off, uint32_t m0) {
   asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(off), "s"(uniform_ptr(base)),
-               "{m0}"(lds_m0(l))
+               "{m0}"(m0)
                : "memory");
 }
-__device__ __forceinline__ void dma4o(const void *base, uint32_t off, lds_void *l) {
+__device__ __forceinline__ void dma4o_m0(const void *base, uint32_t off, uint32_t m0) {
   asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
-               "{m0}"(lds_m0(l))
+               "{m0}"(m0)
                : "memory");
+}
+// LDS byte address of an LDS object reached through a generic pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(lds_void *)p;
 }
 
 // Rows of 128 floats (a key group's scales or zeros over channels, a value
@@ -213,6 +221,36 @@ struct DmaOffsets {
   }
 };
 
+// Per-lane source offsets of every copy of a block's key part and value
+// part, counted from the start of the record (section offset included), so
+// that all copies of a part share one scalar base address -- the record --
+// and no per-copy address arithmetic runs.  Set once per wave.
+template <bool S16>
+struct PartOffsets {
+  static constexpr int N = Rec<S16>::dma;
+  uint32_t k[N], v[N];
+  __device__ explicit PartOffsets(const DmaOffsets &o) {
+    using RC = Rec<S16>;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      k[i] = RC::kc + i * 1024 + o.lin;
+      v[i] = RC::vc + i * 1024 + o.lin;
+    }
+    if constexpr (S16) {
+      k[4] = RC::ks + o.zrot;
+      v[4] = RC::vs + o.zrot;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        k[4 + i] = RC::ks + i * 1024 + o.rot[i];
+        v[4 + i] = RC::vs + i * 1024 + o.rot[i];
+      }
+    }
+    k[N - 1] = RC::kz + o.zrot;
+    v[N - 1] = RC::vz + o.zrot;
+  }
+};
+
 // Start of record `blk` (tokens [128 blk, 128 blk + 128)) of slab bh.
 // A paged cache (PAGED) finds it through the page table: record h of page
 // pt[b nrec + blk], the page index clamped into the pool.  The paged form is
@@ -232,46 +270,48 @@ __device__ __forceinline__ const uint8_t *record_of(const DecodeArgs &a, int64_t
 
 // Key part of block `blk` (tokens [128 blk, 128 blk + 128)) of slab bh:
 // Rec<S16>::dma DMA instructions, plus 2 for the mask when there is one.
+// s, mask_s: LDS byte addresses of the wave's KStage and mask buffer.
 template <bool MASKED, bool PAGED, bool S16>
 __device__ __forceinline__ void stage_keys(const DecodeArgs &a, int64_t bh, int64_t blk,
-                                           KStage *s, float *mask_s, const DmaOffsets &o,
-                                           int lane) {
-  using RC = Rec<S16>;
-  const uint8_t *rec = record_of<PAGED, S16>(a, bh, blk);
+                                           uint32_t s, uint32_t mask_s,
+                                           const PartOffsets<S16> &o, int lane) {
+  const void *rec = uniform_ptr(record_of<PAGED, S16>(a, bh, blk));
+  constexpr uint32_t kc = offsetof(KStage, kc), ks = offsetof(KStage, ks),
+                     kz = offsetof(KStage, kz);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dma16nt(rec + RC::kc + i * 1024, o.lin, (lds_void *)(s->kc + i * 256));
+  for (int i = 0; i < 4; ++i) dma16nt_m0(rec, o.k[i], s + kc + i * 1024);
   if constexpr (S16) {
-    dma16nt(rec + RC::ks, o.zrot, (lds_void *)s->ks);   // four rows of 128 fp16 scales
+    dma16nt_m0(rec, o.k[4], s + ks);   // four rows of 128 fp16 scales
   } else {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      dma16nt(rec + RC::ks + i * 1024, o.rot[i], (lds_void *)(s->ks + i * 256));
+    for (int i = 0; i < 2; ++i) dma16nt_m0(rec, o.k[4 + i], s + ks + i * 1024);
   }
-  dma16nt(rec + RC::kz, o.zrot, (lds_void *)s->kz);
+  dma16nt_m0(rec, o.k[PartOffsets<S16>::N - 1], s + kz);
   if (MASKED) {
     // dword copies: a mask row need not be 16-byte aligned
     const float *m = a.mask + (bh / a.H) * a.t + blk * kBT;
-    dma4o(m, (uint32_t)lane * 4u, (lds_void *)mask_s);
-    dma4o(m + 64, (uint32_t)lane * 4u, (lds_void *)(mask_s + 64));
+    dma4o_m0(m, (uint32_t)lane * 4u, mask_s);
+    dma4o_m0(m + 64, (uint32_t)lane * 4u, mask_s + 256);
   }
 }
 
 // Value part of block `blk`: Rec<S16>::dma DMA instructions.
+// s: LDS byte address of the wave's VStage.
 template <bool PAGED, bool S16>
 __device__ __forceinline__ void stage_values(const DecodeArgs &a, int64_t bh, int64_t blk,
-                                             VStage *s, const DmaOffsets &o) {
-  using RC = Rec<S16>;
-  const uint8_t *rec = record_of<PAGED, S16>(a, bh, blk);
+                                             uint32_t s, const PartOffsets<S16> &o) {
+  const void *rec = uniform_ptr(record_of<PAGED, S16>(a, bh, blk));
+  constexpr uint32_t vc = offsetof(VStage, vc), vs = offsetof(VStage, vs),
+                     vz = offsetof(VStage, vz);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dma16nt(rec + RC::vc + i * 1024, o.lin, (lds_void *)(s->vc + i * 256));
+  for (int i = 0; i < 4; ++i) dma16nt_m0(rec, o.v[i], s + vc + i * 1024);
   if constexpr (S16) {
-    dma16nt(rec + RC::vs, o.zrot, (lds_void *)s->vs);
+    dma16nt_m0(rec, o.v[4], s + vs);
   } else {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      dma16nt(rec + RC::vs + i * 1024, o.rot[i], (lds_void *)(s->vs + i * 256));
+    for (int i = 0; i < 2; ++i) dma16nt_m0(rec, o.v[4 + i], s + vs + i * 1024);
   }
-  dma16nt(rec + RC::vz, o.zrot, (lds_void *)s->vz);
+  dma16nt_m0(rec, o.v[PartOffsets<S16>::N - 1], s + vz);
 }
 
 // LDS transpose read, issued as inline assembly: the compiler's builtin for it
@@ -388,10 +428,16 @@ __device__ __forceinline__ int draw_item(int *ctr, int lane) {
 
 // The blocks of one workgroup: block index j (0 <= j < nb) stands for block
 // b0 + (j + rot) % nb of the slab; the counter's item n_skip + j is block j.
+// Block indices within a slab fit 32 bits (capacity < 2^26 tokens).
 struct BlockShare {
-  int64_t b0, nb, rot;
+  int b0, nb, rot;
   int n_skip;
   int *ctr;
+  // block of the slab that index j (0 <= j < nb, rot < nb) stands for
+  __device__ __forceinline__ int block(int j) const {
+    const int x = j + rot;
+    return b0 + (x >= nb ? x - nb : x);
+  }
 };
 
 // Matrix-core role: blocks of the workgroup's share (tokens whose key and
@@ -413,6 +459,10 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
   const int i = lane & 15;
   const int kg = lane >> 4;
   const int64_t bh = (int64_t)b * a.H + hk;
+  // LDS byte addresses of the wave's staging buffers, as scalar values
+  const uint32_t k_lds = __builtin_amdgcn_readfirstlane(lds_addr(kbuf));
+  const uint32_t v_lds = __builtin_amdgcn_readfirstlane(lds_addr(vbuf));
+  const uint32_t mask_lds = __builtin_amdgcn_readfirstlane(lds_addr(L.mask));
   if (first >= sh.nb) {
     // no block for this wave: an empty partial (m = -inf)
     if (lane < NREP) *(float2 *)&L.p[lane][kD] = make_float2(-INFINITY, 0.0f);
@@ -436,14 +486,14 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
   // copies; the copies complete in order, so waiting for q alone lets the
   // block stream in meanwhile.  Lanes past the q rows re-read the last 16
   // bytes.
-  const DmaOffsets dmo(lane);
+  const PartOffsets<S16> dmo{DmaOffsets(lane)};
   const uint16_t *q_lds = (const uint16_t *)&L.p[0][0];
   dma16o(a.q + ((int64_t)b * a.Hq + hk * NREP) * kD, (uint32_t)min(lane, NREP * 16 - 1) * 16u,
          (lds_void *)&L.p[0][0]);
   {
-    const int64_t blk = sh.b0 + (first + sh.rot) % sh.nb;
-    stage_keys<MASKED, PAGED, S16>(a, bh, blk, kbuf, L.mask, dmo, lane);
-    stage_values<PAGED, S16>(a, bh, blk, vbuf, dmo);
+    const int64_t blk = sh.block((int)first);
+    stage_keys<MASKED, PAGED, S16>(a, bh, blk, k_lds, mask_lds, dmo, lane);
+    stage_values<PAGED, S16>(a, bh, blk, v_lds, dmo);
   }
   wait_vm<KDMA + SD>();   // q
 
@@ -537,7 +587,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
     }
     // every read of the key part has completed: request the next one
     wait_regs(xk);
-    if constexpr (has_next) stage_keys<MASKED, PAGED, S16>(a, bh, nxt, kbuf, L.mask, dmo, lane);
+    if constexpr (has_next) stage_keys<MASKED, PAGED, S16>(a, bh, nxt, k_lds, mask_lds, dmo, lane);
 
     bz = group_sum(bz);
     if (kg == 0) L.bias[i] = bz;
@@ -637,7 +687,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
     }
     // every read of the value part has completed: request the next one
     wait_regs(xv);
-    if constexpr (has_next) stage_values<PAGED, S16>(a, bh, nxt, vbuf, dmo);
+    if constexpr (has_next) stage_values<PAGED, S16>(a, bh, nxt, v_lds, dmo);
 
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -662,7 +712,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
     wait_vm<SD>();   // key part of this block in
     const int64_t nxt = draw_item(sh.ctr, lane) - sh.n_skip;
     if (nxt >= sh.nb) break;
-    block(std::true_type{}, sh.b0 + (nxt + sh.rot) % sh.nb);
+    block(std::true_type{}, sh.block((int)nxt));
   }
   block(std::false_type{}, 0);
 
@@ -1136,7 +1186,8 @@ __global__ void __launch_bounds__(MASKED ? 256 : 512)
   __shared__ __attribute__((aligned(16))) float sm_bias[W][16];
   __shared__ __attribute__((aligned(16))) float sm_alpha[W][4];
   __shared__ int sm_ctr;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave-uniform, so that the wave's LDS addresses stay scalar
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const Lds L{&sm_k[w], &sm_v[w], sm_p[w], sm_mask[w], sm_bias[w], sm_alpha[w]};
   const uint32_t lin = blockIdx.x;
   uint32_t s, sl;
@@ -1171,15 +1222,15 @@ __global__ void __launch_bounds__(MASKED ? 256 : 512)
   }
   const int64_t nblk = n_main / kBT;
   BlockShare sh;
-  sh.b0 = (int64_t)s * nblk / n_groups;
-  sh.nb = ((int64_t)s + 1) * nblk / n_groups - sh.b0;
+  sh.b0 = (int)((int64_t)s * nblk / n_groups);
+  sh.nb = (int)(((int64_t)s + 1) * nblk / n_groups - sh.b0);
   // The blocks are visited from a starting block that a hash picks,
   // wrapping around.  Every slab's records sit a multiple of the capacity
   // apart, so workgroups walking their shares in lock-step from the first
   // block hit HBM channels in step for some capacities (13% slower at 257 x
   // 128 tokens); scattered starting points break that up.  The order only
   // changes the rounding order of the online softmax.
-  sh.rot = sh.nb > 0 ? (int64_t)(((sl * 2654435761u) ^ (s * 2246822519u)) >> 8) % sh.nb : 0;
+  sh.rot = sh.nb > 0 ? (int)((((sl * 2654435761u) ^ (s * 2246822519u)) >> 8) % (uint32_t)sh.nb) : 0;
   sh.n_skip = (int)s < n_window ? (n_window - 1 - (int)s) / n_groups + 1 : 0;
   sh.ctr = &sm_ctr;
   if (threadIdx.x == 0) sm_ctr = 0;
