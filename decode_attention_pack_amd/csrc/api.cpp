@@ -896,15 +896,44 @@ int kivi_select_attn(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads,
   a.sel = rows;
   a.part = (float *)(w + ws.part);
   hipStream_t s = (hipStream_t)stream;
-  // the vector kernel where it takes the shape, else the scalar one, both
-  // to score the tokens and to attend over the selected ones; splits as
-  // kivi_decode_attn plans them
-  const bool vec = kivi::decode_vector_supported(a);
+  // the matrix kernel where it takes the shape (its scores mode, then its
+  // selected-attention mode), else the vector kernel, else the scalar one,
+  // both to score the tokens and to attend over the selected ones; plans as
+  // kivi_decode_attn makes them.  The selected attention reads the mask
+  // from the stored scores, so the matrix kernel's is planned unmasked.
+  const bool mat = a.t > 0 && kivi::decode_matrix_supported(a);
+  const bool vec = !mat && kivi::decode_vector_supported(a);
   Plan p;
   const Rows r = rows_of(c);
-  rc = make_plan(c, n_q_heads, 0, vec ? KIVI_PATH_VECTOR : KIVI_PATH_GENERIC, a, r, p, who);
+  {
+    kivi::DecodeArgs ap = a;
+    if (mat) ap.mask = nullptr;
+    rc = make_plan(c, n_q_heads, 0,
+                   mat ? KIVI_PATH_MATRIX : (vec ? KIVI_PATH_VECTOR : KIVI_PATH_GENERIC), ap, r, p,
+                   who);
+  }
   if (rc) return rc;
   a.S_total = p.S_total;
+  if (mat) {
+    // 1. scores (masked: the four-wave variant's plan)
+    Plan ps = p;
+    if (a.mask) {
+      rc = make_plan(c, n_q_heads, 0, KIVI_PATH_MATRIX, a, r, ps, who);
+      if (rc) return rc;
+    }
+    rc = hip_status(kivi::launch_scores_matrix(a, ps.n_main, ps.n_groups_matrix, s),
+                    "kivi_select_attn (scores)");
+    if (rc) return rc;
+    // 2. the selection of every row
+    rc = hip_status(kivi::launch_select_rows(a, tau, rows, n_selected, sel_mask, s),
+                    "kivi_select_attn (select)");
+    if (rc) return rc;
+    // 3. attention over the selected tokens, then the merge of the workgroups
+    rc = hip_status(kivi::launch_selected_matrix(a, p.n_main, p.n_groups_matrix, s),
+                    "kivi_select_attn (attention)");
+    if (rc || !p.combine) return rc;
+    return hip_status(kivi::launch_combine(a, s), "kivi_select_attn (combine)");
+  }
   // 1. scores of every token (KIVI item 5's scores); the vector kernel takes
   // all heads of a KV head in one workgroup when there are 4 or 8
   if (a.t > 0) {

@@ -314,6 +314,26 @@ __device__ __forceinline__ void stage_values(const DecodeArgs &a, int64_t bh, in
   dma16nt_m0(rec, o.v[PartOffsets<S16>::N - 1], s + vz);
 }
 
+// Selected attention (mode 2): the stored scores of block `blk` for the
+// NREP query heads of KV head hk (rows of 128 fp32 at a.scores + (b Hq +
+// hk NREP + h) cap + 128 blk) into the wave's key buffer ([NREP][128]):
+// ceil(NREP / 2) copies of 1 KB, lane l taking 16 bytes of row l / 32 (the
+// last row again past NREP rows).
+template <int NREP>
+__device__ __forceinline__ void stage_scores(const DecodeArgs &a, int b, int hk, int64_t blk,
+                                             uint32_t s, int lane) {
+#pragma unroll
+  for (int c = 0; c < (NREP + 1) / 2; ++c) {
+    // base: row 2c (uniform); lanes 32-63 add one row stride for row 2c + 1
+    const float *row = a.scores + ((int64_t)b * a.Hq + hk * NREP + 2 * c) * a.cap + blk * kBT;
+    const uint32_t second = 2 * c + 1 < NREP && lane >= 32 ? 1u : 0u;
+    dma16nt_m0(row, second * (uint32_t)a.cap * 4u + (uint32_t)(lane & 31) * 16u, s + c * 1024);
+  }
+}
+// DMA instructions of stage_scores.
+template <int NREP>
+constexpr int kScoreDma = (NREP + 1) / 2;
+
 // LDS transpose read, issued as inline assembly: the compiler's builtin for it
 // carries no information on which LDS object it reads, so the compiler would
 // wait for every DMA in flight (into either buffer) before it.  Its result is
@@ -339,6 +359,14 @@ __device__ __forceinline__ void q_reads(const uint16_t *p, uint4 (&w)[4]) {
       : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3])
       : "v"(addr)
       : "memory");
+}
+
+// Wait for this wave's LDS reads, including those whose results are in
+// x[0..7] (so that their buffer may be refilled after this point).
+__device__ __forceinline__ void wait_lds8(float (&x)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]),
+                 "+v"(x[6]), "+v"(x[7])::"memory");
 }
 
 // Wait for this wave's LDS reads, including the transpose reads whose
@@ -445,15 +473,25 @@ struct BlockShare {
 // continuing with the blocks the wave draws, accumulated into one partial
 // per query head, left in the wave's probability buffer: row h holds acc[128]
 // of head h, then m (natural-log units) and l.
-template <int NREP, bool MASKED, bool PAGED, bool S16>
+// MODE 1 (scores): only the key half; the score q . K / sqrt(D) + mask of
+// every token of the blocks goes to a.scores[(b Hq + hq) cap + tau] (no
+// softmax, no values, no partial).
+// MODE 2 (selected attention): the key half is replaced by the block's
+// stored scores (copied into the key buffer), -inf for the tokens the row's
+// selection rule (a.sel) does not take; then the softmax and values as in
+// MODE 0.  The mask is part of the stored scores.
+template <int NREP, bool MASKED, bool PAGED, bool S16, int MODE>
 __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare &sh,
                                            int64_t first, int hk, int b, const Lds &L,
                                            KStage *__restrict__ kbuf,
                                            VStage *__restrict__ vbuf) {
   static_assert(NREP == 1 || NREP == 2 || NREP == 4, "query heads per KV head");
+  static_assert(MODE != 2 || !MASKED, "selected attention takes the mask from the scores");
   constexpr int GA = 16 / NREP;       // key groups per A operand
   constexpr int SD = Rec<S16>::dma;
-  constexpr int KDMA = SD + (MASKED ? 2 : 0);
+  // copies of a block's key part (MODE 2: its scores) and value part
+  constexpr int KDMA = MODE == 2 ? kScoreDma<NREP> : SD + (MASKED ? 2 : 0);
+  constexpr int VDMA = MODE == 1 ? 0 : SD;
 
   const int lane = threadIdx.x & 63;
   const int i = lane & 15;
@@ -465,7 +503,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
   const uint32_t mask_lds = __builtin_amdgcn_readfirstlane(lds_addr(L.mask));
   if (first >= sh.nb) {
     // no block for this wave: an empty partial (m = -inf)
-    if (lane < NREP) *(float2 *)&L.p[lane][kD] = make_float2(-INFINITY, 0.0f);
+    if (MODE != 1 && lane < NREP) *(float2 *)&L.p[lane][kD] = make_float2(-INFINITY, 0.0f);
     return;
   }
 
@@ -488,28 +526,41 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
   // bytes.
   const PartOffsets<S16> dmo{DmaOffsets(lane)};
   const uint16_t *q_lds = (const uint16_t *)&L.p[0][0];
-  dma16o(a.q + ((int64_t)b * a.Hq + hk * NREP) * kD, (uint32_t)min(lane, NREP * 16 - 1) * 16u,
-         (lds_void *)&L.p[0][0]);
-  {
-    const int64_t blk = sh.block((int)first);
-    stage_keys<MASKED, PAGED, S16>(a, bh, blk, k_lds, mask_lds, dmo, lane);
-    stage_values<PAGED, S16>(a, bh, blk, v_lds, dmo);
+  int64_t cur = sh.block((int)first);   // the block being processed
+  if constexpr (MODE != 2)
+    dma16o(a.q + ((int64_t)b * a.Hq + hk * NREP) * kD, (uint32_t)min(lane, NREP * 16 - 1) * 16u,
+           (lds_void *)&L.p[0][0]);
+  if constexpr (MODE == 2) {
+    stage_scores<NREP>(a, b, hk, cur, k_lds, lane);
+  } else {
+    stage_keys<MASKED, PAGED, S16>(a, bh, cur, k_lds, mask_lds, dmo, lane);
   }
-  wait_vm<KDMA + SD>();   // q
+  if constexpr (MODE != 1) stage_values<PAGED, S16>(a, bh, cur, v_lds, dmo);
+  if constexpr (MODE != 2) wait_vm<KDMA + VDMA>();   // q
+  // the row's selection rule for the scores this lane holds (head h_s)
+  SelectRow selr{};
+  if constexpr (MODE == 2) selr = a.sel[(int64_t)b * a.Hq + hk * NREP + h_s];
 
   // q of head h_a at this lane's 32 key channels c0(ks) + j, with
   // c0(ks) = 64 (ks / 2) + 16 kg + 8 (ks % 2)
   float qa[4][8];
-  uint4 qw[4];
-  q_reads(q_lds + h_a * kD + 16 * kg, qw);
+  if constexpr (MODE != 2) {
+    uint4 qw[4];
+    q_reads(q_lds + h_a * kD + 16 * kg, qw);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const uint32_t ww[4] = {qw[ks].x, qw[ks].y, qw[ks].z, qw[ks].w};
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint32_t ww[4] = {qw[ks].x, qw[ks].y, qw[ks].z, qw[ks].w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      qa[ks][2 * j] = h2f((uint16_t)(ww[j] & 0xffffu));
-      qa[ks][2 * j + 1] = h2f((uint16_t)(ww[j] >> 16));
+      for (int j = 0; j < 4; ++j) {
+        qa[ks][2 * j] = h2f((uint16_t)(ww[j] & 0xffffu));
+        qa[ks][2 * j + 1] = h2f((uint16_t)(ww[j] >> 16));
+      }
     }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qa[ks][j] = 0.0f;
   }
   // The key A operand is q * s_k * 2^ek with one exponent ek for the whole
   // workgroup.  A key scale is (max - min) / 3 of fp16 values, so it is below
@@ -545,11 +596,46 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
 #pragma unroll
   for (int g = 0; g < 4; ++g) dv[g][0] = dv[g][1] = (f4){0, 0, 0, 0};
 
-  // One block, whose key part has arrived.  With a next block (block nxt),
-  // its key part and then its value part are requested as soon as this
-  // block's key part and value part have been read into registers.
+  // MODE 1: the scores of the previous block (head h_s, tokens 32 g + 2 i +
+  // e), kept in registers and stored while the next block is processed.
+  float sp[4][2] = {};
+  int64_t prev = -1;
+  auto store_prev = [&]() __attribute__((always_inline)) {
+    if (prev >= 0 && k_valid) {
+      float *dst = a.scores + ((int64_t)b * a.Hq + hk * NREP + h_s) * a.cap + prev * kBT + 2 * i;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) *(float2 *)(dst + 32 * g) = make_float2(sp[g][0], sp[g][1]);
+    }
+  };
+
+  // One block (block cur), whose key part has arrived.  With a next block
+  // (block nxt), its key part and then its value part are requested as soon
+  // as this block's key part and value part have been read into registers.
   auto block = [&](auto next_tag, int64_t nxt) __attribute__((always_inline)) {
     constexpr bool has_next = decltype(next_tag)::value;
+    float s2[4][2];   // this lane's scores in log2 units (MODE 1: natural)
+    if constexpr (MODE == 2) {
+    // ================= stored scores =================
+    const float *sc_l = (const float *)kbuf;   // [NREP][128]
+    float sv[8];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float2 v = *(const float2 *)(sc_l + h_s * kBT + 32 * g + 2 * i);
+      sv[2 * g] = v.x;
+      sv[2 * g + 1] = v.y;
+    }
+    wait_lds8(sv);   // read before the buffer is refilled
+    if constexpr (has_next) stage_scores<NREP>(a, b, hk, nxt, k_lds, lane);
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float v = sv[2 * g + e];
+        const int64_t tau = cur * kBT + 32 * g + 2 * i + e;
+        s2[g][e] = k_valid && select_takes(selr, v, tau) ? v * LOG2E : -INFINITY;
+      }
+    } else {
+    if constexpr (MODE == 1) store_prev();
     // ================= key half =================
     const KStage &kst = *kbuf;
     i2 xk[8];                        // [group g][64-channel half rho]
@@ -559,12 +645,13 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
       for (int rho = 0; rho < 2; ++rho)
         xk[2 * g + rho] = tr4(kst.kc + g * 256 + (64 * rho + 16 * kg + i) * 2);
     float mk[4][2];
+    constexpr float kMaskUnit = MODE == 1 ? 1.0f : 1.4426950408889634f;   // natural or log2
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       if (MASKED) {
         const float2 m2 = *(const float2 *)(L.mask + 32 * g + 2 * i);
-        mk[g][0] = m2.x * LOG2E;
-        mk[g][1] = m2.y * LOG2E;
+        mk[g][0] = m2.x * kMaskUnit;
+        mk[g][1] = m2.y * kMaskUnit;
       } else {
         mk[g][0] = mk[g][1] = 0.0f;
       }
@@ -613,18 +700,33 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
     }
     wave_lds_sync();
 
-    // scores (even / odd token of each pair) and online softmax, head h_s
+    // scores (even / odd token of each pair), head h_s
     if (k_valid) {
       const f4 bz4 = *(const f4 *)(L.bias + 4 * kg);
-      const float cs = c_bias * __builtin_amdgcn_ldexpf(1.0f, -ek);   // undo 2^ek
-      float s2[4][2];
-      float bmax = -INFINITY;
+      // undo 2^ek; log2 units, or natural ones for the stored scores
+      const float cs = (MODE == 1 ? a.sm_scale : c_bias) * __builtin_amdgcn_ldexpf(1.0f, -ek);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         s2[g][0] = fmaf(dk[g][0][g] + bz4[g], cs, mk[g][0]);
         s2[g][1] = fmaf(dk[g][1][g] + bz4[g], cs, mk[g][1]);
-        bmax = fmaxf(bmax, fmaxf(s2[g][0], s2[g][1]));
       }
+    }
+    if constexpr (MODE == 1) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        sp[g][0] = s2[g][0];
+        sp[g][1] = s2[g][1];
+      }
+      prev = cur;
+      return;
+    }
+    }   // key half
+
+    // online softmax, head h_s
+    if (k_valid) {
+      float bmax = -INFINITY;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) bmax = fmaxf(bmax, fmaxf(s2[g][0], s2[g][1]));
       bmax = row_max(bmax);
       const float m_new = fmaxf(m_run, bmax);
       const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -707,14 +809,24 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
     }
   };
   // The next block is drawn once this block's key part is in; the draw is an
-  // LDS atomic, so its wait passes over the copies in flight.
+  // LDS atomic, so its wait passes over the copies in flight.  (MODE 1 waits
+  // for everything: the score stores are vector-memory operations too.)
   for (;;) {
-    wait_vm<SD>();   // key part of this block in
+    if constexpr (MODE == 1)
+      wait_vm<0>();
+    else
+      wait_vm<VDMA>();   // key part of this block in
     const int64_t nxt = draw_item(sh.ctr, lane) - sh.n_skip;
     if (nxt >= sh.nb) break;
-    block(std::true_type{}, sh.block((int)nxt));
+    const int64_t nb2 = sh.block((int)nxt);
+    block(std::true_type{}, nb2);
+    cur = nb2;
   }
   block(std::false_type{}, 0);
+  if constexpr (MODE == 1) {
+    store_prev();
+    return;
+  }
 
   // ---- the wave's partial (acc[128], m, l) of each query head, into its
   // probability buffer (rows of kPRow floats), for the workgroup's merge
@@ -804,8 +916,9 @@ struct WinKeyUnits {
   static constexpr int scales = 64, zeros = S16 ? 80 : 96, end = S16 ? 96 : 112;
 };
 
-// The loads of one window chunk, issued and not waited for.
-template <int NREP, bool PAGED, bool S16>
+// The loads of one window chunk, issued and not waited for.  MODE 1 (scores)
+// stages no values; MODE 2 (selected attention) no keys and no q.
+template <int NREP, bool PAGED, bool S16, int MODE>
 __device__ __forceinline__ WinLoads<NREP> window_issue(const DecodeArgs &a, const RowSpan &rs,
                                                        int64_t n_main, int chunk, int hk, int b,
                                                        const Lds &L) {
@@ -820,7 +933,7 @@ __device__ __forceinline__ WinLoads<NREP> window_issue(const DecodeArgs &a, cons
   // ---- DMA, in 16-byte units.  Key buffer: a key group (WinKeyUnits), or
   // n fp16 rows (16 units each) -- at most 512 units = 8 KB.
   char *kl = (char *)L.ks;
-  const int ku_end = kq && !kq_now ? KU::end : n * 16;
+  const int ku_end = MODE == 2 ? 0 : (kq && !kq_now ? KU::end : n * 16);
   for (int base = 0; base < ku_end; base += 64) {
     const int u = base + j;
     if (u < ku_end) {
@@ -848,7 +961,7 @@ __device__ __forceinline__ WinLoads<NREP> window_issue(const DecodeArgs &a, cons
   // value buffer (at most 512 units)
   char *vl = (char *)L.vs;
   const int u_vs = c.u_vs, u_vz = c.u_vz, u_vrow = c.u_vrow;
-  const int vu_end = u_vrow + c.n_fv * 16;
+  const int vu_end = MODE == 1 ? 0 : u_vrow + c.n_fv * 16;
   for (int base = 0; base < vu_end; base += 64) {
     const int u = base + j;
     if (u < vu_end) {
@@ -878,11 +991,15 @@ __device__ __forceinline__ WinLoads<NREP> window_issue(const DecodeArgs &a, cons
   if (c.new_here) ld.nk = *(const uint32_t *)(a.k_new + bh * kD + 2 * j);
   const uint16_t *q = a.q + ((int64_t)b * a.Hq + hk * NREP) * kD;
 #pragma unroll
-  for (int h = 0; h < NREP; ++h) ld.q[h] = *(const uint32_t *)(q + h * kD + 2 * j);
+  for (int h = 0; h < NREP; ++h) ld.q[h] = MODE == 2 ? 0u : *(const uint32_t *)(q + h * kD + 2 * j);
   return ld;
 }
 
-template <int NREP, bool MASKED, bool PAGED, bool S16>
+// MODE 1 (scores): the scores of the chunk's tokens go to a.scores (natural
+// units, mask included); nothing else.  MODE 2 (selected attention): the
+// chunk's scores come from a.scores, -inf where the row's selection rule
+// does not take the token.
+template <int NREP, bool MASKED, bool PAGED, bool S16, int MODE>
 __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &rs, int64_t n_main,
                                             int chunk, int slot, int hk, int b, const Lds &L,
                                             const WinLoads<NREP> &ld) {
@@ -1006,7 +1123,7 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
   float sc[NREP];
 #pragma unroll
   for (int h = 0; h < NREP; ++h) sc[h] = 0.0f;
-  if (tj < n) {
+  if (MODE != 2 && tj < n) {
     // 16-byte LDS reads throughout: the key group's words, scales and zeros
     // and q are the same for all lanes of a half (broadcasts); channels are
     // summed in increasing order
@@ -1070,10 +1187,31 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
   }
 #pragma unroll
   for (int h = 0; h < NREP; ++h) sc[h] += __shfl_xor(sc[h], 32);
-  if (tj < n) {
-    const float mk = MASKED ? a.mask[(int64_t)b * a.t + Ta + tj] : 0.0f;
+  if constexpr (MODE == 1) {
+    // the scores, natural units, from the lanes of the first half
+    if (tj < n && hf == 0) {
+      const float mk = MASKED ? a.mask[(int64_t)b * a.t + Ta + tj] : 0.0f;
 #pragma unroll
-    for (int h = 0; h < NREP; ++h) sc[h] = (sc[h] * a.sm_scale + mk) * LOG2E;
+      for (int h = 0; h < NREP; ++h)
+        a.scores[((int64_t)b * a.Hq + hk * NREP + h) * a.cap + Ta + tj] = sc[h] * a.sm_scale + mk;
+    }
+    return;
+  }
+  if (tj < n) {
+    if constexpr (MODE == 2) {
+      // the stored scores (mask included), -inf where the rule does not take
+      // the token
+#pragma unroll
+      for (int h = 0; h < NREP; ++h) {
+        const int64_t r = (int64_t)b * a.Hq + hk * NREP + h;
+        const float v = a.scores[r * a.cap + Ta + tj];
+        sc[h] = select_takes(a.sel[r], v, Ta + tj) ? v * LOG2E : -INFINITY;
+      }
+    } else {
+      const float mk = MASKED ? a.mask[(int64_t)b * a.t + Ta + tj] : 0.0f;
+#pragma unroll
+      for (int h = 0; h < NREP; ++h) sc[h] = (sc[h] * a.sm_scale + mk) * LOG2E;
+    }
   } else {
 #pragma unroll
     for (int h = 0; h < NREP; ++h) sc[h] = -INFINITY;
@@ -1173,7 +1311,9 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
 // The masked variant holds the block's mask in registers as well; it may
 // use more than half the register file rather than spill, since a spill
 // reload inside the block loop would wait for every DMA in flight.
-template <int NREP, bool MASKED, bool RAGGED, bool PAGED, bool S16>
+// MODE 1 (scores) and MODE 2 (selected attention): see block_role; MODE 1
+// writes no partials.
+template <int NREP, bool MASKED, bool RAGGED, bool PAGED, bool S16, int MODE>
 __global__ void __launch_bounds__(MASKED ? 256 : 512)
     __attribute__((amdgpu_waves_per_eu(MASKED ? 1 : 2)))
     decode_matrix_kernel(DecodeArgs a, int64_t n_main_all, int n_groups_all, int n_window_all,
@@ -1238,12 +1378,14 @@ __global__ void __launch_bounds__(MASKED ? 256 : 512)
   int item = draw_item(&sm_ctr, lane);
   while (item < sh.n_skip) {
     const int x = (int)s + item * n_groups;
-    const WinLoads<NREP> ld = window_issue<NREP, PAGED, S16>(a, rs, n_main, x, hk, b, L);
-    window_role<NREP, MASKED, PAGED, S16>(a, rs, n_main, x, n_groups + x, hk, b, L, ld);
+    const WinLoads<NREP> ld = window_issue<NREP, PAGED, S16, MODE>(a, rs, n_main, x, hk, b, L);
+    window_role<NREP, MASKED, PAGED, S16, MODE>(a, rs, n_main, x, n_groups + x, hk, b, L, ld);
     wave_lds_sync();   // the LDS reads of the chunk are done
     item = draw_item(&sm_ctr, lane);
   }
-  block_role<NREP, MASKED, PAGED, S16>(a, sh, item - sh.n_skip, hk, b, L, &sm_k[w], &sm_v[w]);
+  block_role<NREP, MASKED, PAGED, S16, MODE>(a, sh, item - sh.n_skip, hk, b, L, &sm_k[w],
+                                             &sm_v[w]);
+  if constexpr (MODE == 1) return;   // the scores are stored; no partials
 
   // The W partials of the workgroup's waves, merged with the log-sum-exp
   // rule into partial slot s of the slab: thread e takes channel e % 128 of
@@ -1342,41 +1484,48 @@ int decode_matrix_window_chunks(const DecodeArgs &a, int64_t n_main) {
 
 int decode_matrix_waves(const DecodeArgs &a) { return a.mask ? 4 : 8; }
 
-template <int NREP, bool RAGGED, bool PAGED, bool S16>
+template <int NREP, bool RAGGED, bool PAGED, bool S16, int MODE = 0>
 static void launch_rep(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
                        int n_groups, int n_window, const MatrixRowArg<RAGGED> &rows) {
-  if (a.mask)
-    hipLaunchKernelGGL((decode_matrix_kernel<NREP, true, RAGGED, PAGED, S16>), grid, dim3(256), 0,
-                       s, a, n_main, n_groups, n_window, rows);
+  // selected attention takes the mask from the stored scores
+  if (a.mask && MODE != 2)
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, MODE != 2, RAGGED, PAGED, S16, MODE>), grid,
+                       dim3(256), 0, s, a, n_main, n_groups, n_window, rows);
   else
-    hipLaunchKernelGGL((decode_matrix_kernel<NREP, false, RAGGED, PAGED, S16>), grid, dim3(512),
-                       0, s, a, n_main, n_groups, n_window, rows);
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, false, RAGGED, PAGED, S16, MODE>), grid,
+                       dim3(512), 0, s, a, n_main, n_groups, n_window, rows);
 }
 
-template <bool RAGGED, bool PAGED, bool S16>
+template <bool RAGGED, bool PAGED, bool S16, int MODE>
 static void launch_layout(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
                           int n_groups, int n_window, const MatrixRowArg<RAGGED> &rows) {
   switch (a.n_rep) {
-    case 1: launch_rep<1, RAGGED, PAGED, S16>(a, grid, s, n_main, n_groups, n_window, rows); break;
-    case 2: launch_rep<2, RAGGED, PAGED, S16>(a, grid, s, n_main, n_groups, n_window, rows); break;
-    default: launch_rep<4, RAGGED, PAGED, S16>(a, grid, s, n_main, n_groups, n_window, rows); break;
+    case 1:
+      launch_rep<1, RAGGED, PAGED, S16, MODE>(a, grid, s, n_main, n_groups, n_window, rows);
+      break;
+    case 2:
+      launch_rep<2, RAGGED, PAGED, S16, MODE>(a, grid, s, n_main, n_groups, n_window, rows);
+      break;
+    default:
+      launch_rep<4, RAGGED, PAGED, S16, MODE>(a, grid, s, n_main, n_groups, n_window, rows);
+      break;
   }
 }
 
-template <bool RAGGED>
+template <bool RAGGED, int MODE = 0>
 static void launch_reps(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
                         int n_groups, int n_window, const MatrixRowArg<RAGGED> &rows) {
   const bool s16 = a.L.sb == 2;
   if (a.L.pt) {
     if (s16)
-      launch_layout<RAGGED, true, true>(a, grid, s, n_main, n_groups, n_window, rows);
+      launch_layout<RAGGED, true, true, MODE>(a, grid, s, n_main, n_groups, n_window, rows);
     else
-      launch_layout<RAGGED, true, false>(a, grid, s, n_main, n_groups, n_window, rows);
+      launch_layout<RAGGED, true, false, MODE>(a, grid, s, n_main, n_groups, n_window, rows);
   } else {
     if (s16)
-      launch_layout<RAGGED, false, true>(a, grid, s, n_main, n_groups, n_window, rows);
+      launch_layout<RAGGED, false, true, MODE>(a, grid, s, n_main, n_groups, n_window, rows);
     else
-      launch_layout<RAGGED, false, false>(a, grid, s, n_main, n_groups, n_window, rows);
+      launch_layout<RAGGED, false, false, MODE>(a, grid, s, n_main, n_groups, n_window, rows);
   }
 }
 
@@ -1401,6 +1550,43 @@ hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int n_group
   const int64_t n_wg = (int64_t)n_groups * a.H * a.B;
   if (n_wg > ((int64_t)1 << 25)) return hipErrorInvalidValue;   // 32-bit workgroup ids
   launch_reps<false>(a, dim3((unsigned)n_wg), s, n_main, n_groups, n_window, NoRows{});
+  return hipGetLastError();
+}
+
+// The selection workload on the matrix cores: the scores of every token
+// (MODE 1; a.scores [B][Hq][cap]) and the attention over the selected ones
+// (MODE 2; a.sel, partial slots as launch_decode_matrix).  Same plan as
+// launch_decode_matrix; no fused step.
+static hipError_t check_select_matrix(const DecodeArgs &a, int64_t n_main, int n_groups) {
+  if (!decode_matrix_supported(a) || a.t <= 0 || n_main < 0 || n_main % kBT != 0 ||
+      n_main > a.n_vq || n_groups <= 0 || a.t_new >= 0 || a.n_kq % kG != 0)
+    return hipErrorInvalidValue;
+  // score rows are copied 16 bytes at a time
+  if (!a.scores || ((uintptr_t)a.scores & 15) != 0 || a.cap % 4 != 0 || a.cap > ((int64_t)1 << 26))
+    return hipErrorInvalidValue;
+  if ((int64_t)n_groups * a.H * a.B > ((int64_t)1 << 25)) return hipErrorInvalidValue;
+  return hipSuccess;
+}
+
+hipError_t launch_scores_matrix(const DecodeArgs &a, int64_t n_main, int n_groups,
+                                hipStream_t s) {
+  const hipError_t e = check_select_matrix(a, n_main, n_groups);
+  if (e != hipSuccess) return e;
+  const int n_window = decode_matrix_window_chunks(a, n_main);
+  const int64_t n_wg = (int64_t)n_groups * a.H * a.B;
+  launch_reps<false, 1>(a, dim3((unsigned)n_wg), s, n_main, n_groups, n_window, NoRows{});
+  return hipGetLastError();
+}
+
+hipError_t launch_selected_matrix(const DecodeArgs &a, int64_t n_main, int n_groups,
+                                  hipStream_t s) {
+  const hipError_t e = check_select_matrix(a, n_main, n_groups);
+  if (e != hipSuccess) return e;
+  if (!a.sel || !a.part) return hipErrorInvalidValue;
+  const int n_window = decode_matrix_window_chunks(a, n_main);
+  if ((int64_t)n_groups + n_window > a.S_total) return hipErrorInvalidValue;
+  const int64_t n_wg = (int64_t)n_groups * a.H * a.B;
+  launch_reps<false, 2>(a, dim3((unsigned)n_wg), s, n_main, n_groups, n_window, NoRows{});
   return hipGetLastError();
 }
 

@@ -151,6 +151,14 @@ template <bool RAGGED>
 using MatrixRowArg = typename std::conditional<RAGGED, MatrixRows, NoRows>::type;
 hipError_t launch_decode_matrix_rows(const DecodeArgs &a, const MatrixRows &rows, int n_shares,
                                      hipStream_t s);
+// The selection workload on the matrix kernel's shapes, with the plan of
+// launch_decode_matrix (no fused step): the scores of every token into
+// DecodeArgs::scores, and the attention over the tokens DecodeArgs::sel
+// selects (partials as launch_decode_matrix, merged by launch_combine when
+// n_groups > 1).
+hipError_t launch_scores_matrix(const DecodeArgs &a, int64_t n_main, int n_groups, hipStream_t s);
+hipError_t launch_selected_matrix(const DecodeArgs &a, int64_t n_main, int n_groups,
+                                  hipStream_t s);
 
 // The scores of every token (DecodeArgs::scores), in splits of
 // tokens_per_split tokens: the vector kernel's shapes, and any shape.
