@@ -27,7 +27,9 @@ namespace kivi {
 
 namespace {
 
-constexpr int kSThreads = 256;
+// 16 waves per row: each pass over a row's scores keeps up to eight 16-byte
+// loads in flight per thread, so a 32k-token row is one round of loads.
+constexpr int kSThreads = 1024;
 
 // The score a key stands for (select_key's inverse).
 __device__ __forceinline__ float key_score(uint32_t k) {
@@ -40,7 +42,7 @@ __device__ __forceinline__ uint64_t fixed_mass(float s, float m) {
   return (uint64_t)rintf(expf(s - m) * 68719476736.0f);
 }
 
-// Inclusive scans over the 256 threads of a workgroup (counts and masses).
+// Inclusive scans over the threads of a workgroup (counts and masses).
 __device__ __forceinline__ void block_scan(uint32_t &c, uint64_t &w, uint32_t *sc, uint64_t *sw) {
   const int tid = threadIdx.x;
   sc[tid] = c;
@@ -76,20 +78,20 @@ __device__ __forceinline__ uint64_t token_mass(float s, float m) {
 }
 
 // f(i, s) for every score s = sr[i], i < t, of a row (16-byte aligned):
-// thread k takes the float4s k, k + 256, ..., four of them loaded before any
-// is used, so that each thread keeps several loads in flight.
+// thread k takes the float4s k, k + kSThreads, ..., eight of them loaded
+// before any is used, so that each thread keeps several loads in flight.
 template <typename F>
 __device__ __forceinline__ void for_scores(const float *sr, int t, F f) {
   const int tid = threadIdx.x;
   const int n4 = t / 4;
   const float4 *s4 = (const float4 *)sr;
   int v = tid;
-  for (; v + 3 * kSThreads < n4; v += 4 * kSThreads) {
-    float4 x[4];
+  for (; v + 7 * kSThreads < n4; v += 8 * kSThreads) {
+    float4 x[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) x[u] = s4[v + u * kSThreads];
+    for (int u = 0; u < 8; ++u) x[u] = s4[v + u * kSThreads];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       const int i = 4 * (v + u * kSThreads);
       f(i, x[u].x);
       f(i + 1, x[u].y);
@@ -107,7 +109,7 @@ __device__ __forceinline__ void for_scores(const float *sr, int t, F f) {
   for (int i = 4 * n4 + tid; i < t; i += kSThreads) f(i, sr[i]);
 }
 
-// The radix selection of one row (256 threads), given the row's largest
+// The radix selection of one row (kSThreads threads), given the row's largest
 // score m and the mass to reach: three passes over the keys (11, 11, 10
 // bits), each a histogram of counts and masses under the prefix fixed so
 // far, then the ties at the threshold key by index.
@@ -209,7 +211,7 @@ __device__ SelectRow select_rows_radix(const float *sr, int t, float m, float ta
   return SelectRow{prefix, cut, m, (int32_t)(c_above + n_tie)};
 }
 
-// grid: B * Hq rows; block: 256.  Row r = b Hq + hq over a.t scores.
+// grid: B * Hq rows; block: kSThreads.  Row r = b Hq + hq over a.t scores.
 // 1. the row's largest score m; 2. a histogram of token counts and masses
 // over kNB buckets of the distance m - s (bucket 0 the closest), and the
 // bucket where the mass counted from the top reaches tau; 3. that bucket's
@@ -240,7 +242,9 @@ select_rows_kernel(DecodeArgs a, float tau, SelectRow *rows, int32_t *n_selected
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   if ((tid & 63) == 0) s_max[tid >> 6] = m;
   __syncthreads();
-  m = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  m = s_max[0];
+#pragma unroll
+  for (int w8 = 1; w8 < kSThreads / 64; ++w8) m = fmaxf(m, s_max[w8]);
   const int words = (t + 31) / 32;
   if (m == -INFINITY) {   // no token (t == 0) or every score -inf: nothing selected
     if (tid == 0) {
@@ -268,7 +272,7 @@ select_rows_kernel(DecodeArgs a, float tau, SelectRow *rows, int32_t *n_selected
     }
   });
   __syncthreads();
-  // thread k: buckets 16 k .. 16 k + 15 (closest first)
+  // thread k: buckets per k .. per k + per - 1 (closest first)
   constexpr int per = kNB / kSThreads;
   uint32_t c = 0u;
   uint64_t w = 0u;
@@ -343,7 +347,7 @@ select_rows_kernel(DecodeArgs a, float tau, SelectRow *rows, int32_t *n_selected
       }
     }
     // the first entries whose masses reach `need`: a scan of the masses in
-    // sorted order, 8 entries per thread
+    // sorted order, per2 consecutive entries per thread
     const int per2 = (n_pad + kSThreads - 1) / kSThreads;
     uint32_t cnt = 0u;
     uint64_t acc = 0u;
