@@ -10,15 +10,18 @@
 // mass reaches tau); the same review's major comment 2 on Eq. (5) (the
 // output over the selected set, here renormalized).
 //
-// The selection of one (batch row, query head) row is a radix select over the
-// scores' order-preserving 32-bit keys in three passes (11, 11 and 10 bits),
-// each a histogram of token counts and of probability mass over the buckets
-// under the prefix fixed so far; the bucket where the mass counted from the
-// top reaches tau fixes the next bits.  Masses are e^(s - max) in fixed point
-// (units of 2^-36, 64-bit integer sums), so the histograms, and with them the
-// selection, do not depend on the order of the additions.  Equal scores are
-// taken by increasing token index.  The attention over the selected tokens
-// is the vector or scalar kernel reading these scores (MODE 2 there).
+// The selection of one (batch row, query head) row: the row's largest score,
+// a histogram of token counts and probability masses over buckets of the
+// distance to it, the bucket where the mass counted from the top reaches tau,
+// then that bucket's tokens sorted by (score, index) in LDS.  A bucket too
+// crowded to sort falls back to a radix select over the scores'
+// order-preserving 32-bit keys in three passes (11, 11 and 10 bits).  Masses
+// are e^(s - max) in fixed point (units of 2^-36, 64-bit integer sums), so
+// the histograms, and with them the selection, do not depend on the order of
+// the additions.  Equal scores are taken by increasing token index.  The
+// scores come from the matrix, vector or scalar kernel's scores mode, and the
+// attention over the selected tokens is the same kernel's selected-attention
+// mode reading them back.
 #include <math.h>
 
 #include "kivi_internal.hpp"
