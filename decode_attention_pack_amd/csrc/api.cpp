@@ -178,6 +178,7 @@ int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
 
 constexpr int kGenericMinSplit = 256;
 constexpr int kMatrixBlock = 128;   // tokens per block of the matrix-core kernel
+constexpr int kTailSplit = 128;     // tokens per vector-kernel split past the 4-bit blocks
 constexpr int kVectorStep = 128;    // tokens per step of the vector kernel's four waves
 // Vector kernel: workgroups to aim for.  Three waves per SIMD hold 768
 // workgroups at once; fewer, longer splits measure faster than twice as
@@ -205,6 +206,11 @@ struct Plan {
   int64_t n_main = 0;           // tokens [0, n_main) in the matrix kernel's block role
   int n_groups_matrix = 0;      // matrix-kernel workgroups per slab
   int n_window = 0;             // 32-token chunks of [n_main, t) in its window role
+  // 4-bit matrix kernel over the blocks of [0, n_main) (n_groups_matrix
+  // workgroups per slab, slots [0, n_groups_matrix)), then the vector kernel
+  // over [n_main, t) (n_split_generic splits of tps_generic tokens, the
+  // slots after them)
+  bool matrix4 = false;
   bool vector = false;          // vector kernel instead of the scalar one
   int tps_generic = 0;          // vector / scalar kernel (shapes the matrix kernel does not cover)
   int n_split_generic = 0;
@@ -317,6 +323,36 @@ int make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
     // a slab with a single workgroup writes its output itself
     p.combine = groups > 1;
     return KIVI_OK;
+  }
+  // 4-bit keys and values: the matrix kernel takes the whole 128-token blocks
+  // (by default where several query heads share a KV head, whose keys and
+  // values the vector kernel reads once per pair of heads), and the vector
+  // kernel the rest, kTailSplit tokens per split
+  if ((path == KIVI_PATH_MATRIX || (path == KIVI_PATH_AUTO && n_rep >= 2)) && t > 0 &&
+      !r.ragged && a.t_new < 0 && kivi::decode_matrix4_supported(a) &&
+      kivi::decode_vector_supported(a)) {
+    const int64_t n_main = kivi::matrix_main(kivi::row_span(t, a.R, false), a.R);
+    if (n_main >= kMatrixBlock) {
+      const int64_t blocks = n_main / kMatrixBlock;
+      const int waves = kivi::decode_matrix4_waves(a);
+      int64_t groups;
+      if (tps_req == 0) {
+        // one workgroup per CU (its LDS takes most of the CU's)
+        const int64_t target = max64(1, device_cus() / units);
+        groups = std::min(target, max64(1, ceil_div(blocks, waves)));
+      } else {
+        const int64_t tps = ceil_div(tps_req, kMatrixBlock) * kMatrixBlock;
+        groups = max64(1, ceil_div(n_main, tps));
+      }
+      p.matrix4 = true;
+      p.n_main = n_main;
+      p.n_groups_matrix = (int)groups;
+      p.tps_generic = kTailSplit;
+      p.n_split_generic = (int)ceil_div(t - n_main, kTailSplit);
+      p.S_total = (int)groups + p.n_split_generic;
+      p.combine = true;
+      return KIVI_OK;
+    }
   }
   p.vector = (path == KIVI_PATH_AUTO || path == KIVI_PATH_VECTOR) &&
              kivi::decode_vector_supported(a);
@@ -694,7 +730,8 @@ int decode_call(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, cons
   a.n_vq = max64(0, a.t - a.R);
   a.sm_scale = 1.0f / sqrtf((float)a.D);
 
-  if (path == KIVI_PATH_MATRIX && !kivi::decode_matrix_supported(a))
+  if (path == KIVI_PATH_MATRIX && !kivi::decode_matrix_supported(a) &&
+      !(kivi::decode_matrix4_supported(a) && !fused && !r.ragged))
     return fail(KIVI_ERR_INVALID_ARG, "%s: the matrix-core kernel does not handle this shape", who);
   if (path == KIVI_PATH_VECTOR && !kivi::decode_vector_supported(a))
     return fail(KIVI_ERR_INVALID_ARG, "%s: the vector kernel does not handle this shape", who);
@@ -703,6 +740,10 @@ int decode_call(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, cons
   if (rc) return rc;
   if (fused && !p.matrix)
     return fail(KIVI_ERR_INVALID_ARG, "%s: internal: fused step without the matrix kernel", who);
+  if (path == KIVI_PATH_MATRIX && !kivi::decode_matrix_supported(a) && !p.matrix4)
+    return fail(KIVI_ERR_INVALID_ARG,
+                "%s: the 4-bit matrix-core path needs a whole 128-token block of quantized "
+                "keys and values and a residual length that is a multiple of 32", who);
   if (p.S_total > max_slots(c, tokens_per_split))
     return fail(KIVI_ERR_WORKSPACE, "%s: internal split plan exceeds the workspace bound", who);
   a.S_total = p.S_total;
@@ -728,6 +769,14 @@ int decode_call(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, cons
   else if (p.matrix)
     rc = hip_status(kivi::launch_decode_matrix(a, p.n_main, p.n_groups_matrix, s),
                     "kivi_decode_attn (matrix)");
+  else if (p.matrix4) {
+    rc = hip_status(kivi::launch_decode_matrix4(a, p.n_main, p.n_groups_matrix, s),
+                    "kivi_decode_attn (matrix, 4-bit)");
+    if (!rc)
+      rc = hip_status(kivi::launch_decode_vector_range(a, p.n_main, p.tps_generic,
+                                                       p.n_split_generic, p.n_groups_matrix, s),
+                      "kivi_decode_attn (vector, past the blocks)");
+  }
   else if (p.vector)
     rc = hip_status(kivi::launch_decode_vector(a, p.tps_generic, p.n_split_generic, s, rows),
                     "kivi_decode_attn (vector)");

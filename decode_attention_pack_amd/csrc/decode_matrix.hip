@@ -67,20 +67,24 @@ constexpr int kD = 128;
 constexpr int kG = 32;
 constexpr int kBT = 128;       // tokens per block (block role)
 constexpr int kWT = 32;        // tokens per chunk (window role)
-// A record of the packed store at this shape (2-bit keys and values, G 32,
-// head_dim 128): byte offsets of its sections and its size, with fp32
+// A record of the packed store at this shape (BITS-bit keys and values, G
+// 32, head_dim 128): byte offsets of its sections and its size, with fp32
 // scales or (S16) fp16 scales; and the DMA instructions that copy the key or
-// the value part of a block (codes 4 KB, scales 2 or 1 KB, zeros 1 KB).
-template <bool S16>
+// the value part of a block (codes 4 or 8 KB, scales 2 or 1 KB, zeros 1 KB).
+template <bool S16, int BITS = 2>
 struct Rec {
-  static constexpr int kc = 0, ks = 4096;
-  static constexpr int kz = S16 ? 5120 : 6144;
-  static constexpr int vc = S16 ? 6144 : 7168;
-  static constexpr int vs = S16 ? 10240 : 11264;
-  static constexpr int vz = S16 ? 11264 : 13312;
-  static constexpr int bytes = S16 ? 12288 : 14336;
+  static_assert(BITS == 2 || BITS == 4, "2- or 4-bit codes");
+  static constexpr int code_bytes = 2048 * BITS;   // 128 tokens x 128 channels
+  static constexpr int scale_bytes = S16 ? 1024 : 2048;
+  static constexpr int kc = 0, ks = code_bytes;
+  static constexpr int kz = ks + scale_bytes;
+  static constexpr int vc = kz + 1024;
+  static constexpr int vs = vc + code_bytes;
+  static constexpr int vz = vs + scale_bytes;
+  static constexpr int bytes = vz + 1024;
   static constexpr int sb = S16 ? 2 : 4;    // bytes per scale
-  static constexpr int dma = S16 ? 6 : 7;
+  static constexpr int ncode = code_bytes / 1024;   // DMA instructions of the codes
+  static constexpr int dma = ncode + scale_bytes / 1024 + 1;
 };
 constexpr int kPRow = 132;     // floats per probability row in LDS (16-byte pad)
 
@@ -88,18 +92,23 @@ constexpr int kPRow = 132;     // floats per probability row in LDS (16-byte pad
 // record, the scale and zero rows rotated (see rot_chunk, zrot_off).  fp16
 // scales fill the first half of ks / vs, rotated like the zeros.  The
 // window role stages up to 8 KB in each (32 fp16 rows), hence the padding.
-struct alignas(16) KStage {
-  uint32_t kc[1024];   // 4 key groups x 128 channels x 2 words
-  float ks[512];       // [4 groups][128 channels]
-  uint16_t kz[512];    // [4 groups][128 channels], fp16
-  uint32_t pad[256];
+// The 4-bit stages hold twice the codes and are used by the block role only.
+template <int BITS>
+struct alignas(16) KStageT {
+  uint32_t kc[512 * BITS];   // 4 key groups x 128 channels x BITS words
+  float ks[512];             // [4 groups][128 channels]
+  uint16_t kz[512];          // [4 groups][128 channels], fp16
+  uint32_t pad[BITS == 2 ? 256 : 0];
 };
-struct alignas(16) VStage {
-  uint32_t vc[1024];   // 128 tokens x 8 words
-  float vs[512];       // [4 channel groups][128 tokens]
-  uint16_t vz[512];    // [4 channel groups][128 tokens], fp16
-  uint32_t pad[256];
+template <int BITS>
+struct alignas(16) VStageT {
+  uint32_t vc[512 * BITS];   // 128 tokens x 4 BITS words
+  float vs[512];             // [4 channel groups][128 tokens]
+  uint16_t vz[512];          // [4 channel groups][128 tokens], fp16
+  uint32_t pad[BITS == 2 ? 256 : 0];
 };
+using KStage = KStageT<2>;
+using VStage = VStageT<2>;
 
 
 // Global->LDS copies (16 or 4 bytes per lane; lane l's bytes land at LDS
@@ -225,25 +234,25 @@ struct DmaOffsets {
 // part, counted from the start of the record (section offset included), so
 // that all copies of a part share one scalar base address -- the record --
 // and no per-copy address arithmetic runs.  Set once per wave.
-template <bool S16>
+template <bool S16, int BITS = 2>
 struct PartOffsets {
-  static constexpr int N = Rec<S16>::dma;
+  using RC = Rec<S16, BITS>;
+  static constexpr int N = RC::dma, NC = RC::ncode;
   uint32_t k[N], v[N];
   __device__ explicit PartOffsets(const DmaOffsets &o) {
-    using RC = Rec<S16>;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NC; ++i) {
       k[i] = RC::kc + i * 1024 + o.lin;
       v[i] = RC::vc + i * 1024 + o.lin;
     }
     if constexpr (S16) {
-      k[4] = RC::ks + o.zrot;
-      v[4] = RC::vs + o.zrot;
+      k[NC] = RC::ks + o.zrot;
+      v[NC] = RC::vs + o.zrot;
     } else {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        k[4 + i] = RC::ks + i * 1024 + o.rot[i];
-        v[4 + i] = RC::vs + i * 1024 + o.rot[i];
+        k[NC + i] = RC::ks + i * 1024 + o.rot[i];
+        v[NC + i] = RC::vs + i * 1024 + o.rot[i];
       }
     }
     k[N - 1] = RC::kz + o.zrot;
@@ -255,9 +264,9 @@ struct PartOffsets {
 // A paged cache (PAGED) finds it through the page table: record h of page
 // pt[b nrec + blk], the page index clamped into the pool.  The paged form is
 // a separate instantiation so that the contiguous one keeps its registers.
-template <bool PAGED, bool S16>
+template <bool PAGED, bool S16, int BITS = 2>
 __device__ __forceinline__ const uint8_t *record_of(const DecodeArgs &a, int64_t bh, int64_t blk) {
-  constexpr int64_t RB = Rec<S16>::bytes;
+  constexpr int64_t RB = Rec<S16, BITS>::bytes;
   if constexpr (!PAGED) {
     return a.L.blocks + (bh * a.L.nrec + blk) * RB;
   } else {
@@ -269,24 +278,25 @@ __device__ __forceinline__ const uint8_t *record_of(const DecodeArgs &a, int64_t
 }
 
 // Key part of block `blk` (tokens [128 blk, 128 blk + 128)) of slab bh:
-// Rec<S16>::dma DMA instructions, plus 2 for the mask when there is one.
-// s, mask_s: LDS byte addresses of the wave's KStage and mask buffer.
-template <bool MASKED, bool PAGED, bool S16>
+// Rec<S16, BITS>::dma DMA instructions, plus 2 for the mask when there is one.
+// s, mask_s: LDS byte addresses of the wave's KStageT and mask buffer.
+template <bool MASKED, bool PAGED, bool S16, int BITS = 2>
 __device__ __forceinline__ void stage_keys(const DecodeArgs &a, int64_t bh, int64_t blk,
                                            uint32_t s, uint32_t mask_s,
-                                           const PartOffsets<S16> &o, int lane) {
-  const void *rec = uniform_ptr(record_of<PAGED, S16>(a, bh, blk));
-  constexpr uint32_t kc = offsetof(KStage, kc), ks = offsetof(KStage, ks),
-                     kz = offsetof(KStage, kz);
+                                           const PartOffsets<S16, BITS> &o, int lane) {
+  using KS = KStageT<BITS>;
+  constexpr int NC = PartOffsets<S16, BITS>::NC;
+  const void *rec = uniform_ptr(record_of<PAGED, S16, BITS>(a, bh, blk));
+  constexpr uint32_t kc = offsetof(KS, kc), ks = offsetof(KS, ks), kz = offsetof(KS, kz);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dma16nt_m0(rec, o.k[i], s + kc + i * 1024);
+  for (int i = 0; i < NC; ++i) dma16nt_m0(rec, o.k[i], s + kc + i * 1024);
   if constexpr (S16) {
-    dma16nt_m0(rec, o.k[4], s + ks);   // four rows of 128 fp16 scales
+    dma16nt_m0(rec, o.k[NC], s + ks);   // four rows of 128 fp16 scales
   } else {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16nt_m0(rec, o.k[4 + i], s + ks + i * 1024);
+    for (int i = 0; i < 2; ++i) dma16nt_m0(rec, o.k[NC + i], s + ks + i * 1024);
   }
-  dma16nt_m0(rec, o.k[PartOffsets<S16>::N - 1], s + kz);
+  dma16nt_m0(rec, o.k[PartOffsets<S16, BITS>::N - 1], s + kz);
   if (MASKED) {
     // dword copies: a mask row need not be 16-byte aligned
     const float *m = a.mask + (bh / a.H) * a.t + blk * kBT;
@@ -295,23 +305,24 @@ __device__ __forceinline__ void stage_keys(const DecodeArgs &a, int64_t bh, int6
   }
 }
 
-// Value part of block `blk`: Rec<S16>::dma DMA instructions.
-// s: LDS byte address of the wave's VStage.
-template <bool PAGED, bool S16>
+// Value part of block `blk`: Rec<S16, BITS>::dma DMA instructions.
+// s: LDS byte address of the wave's VStageT.
+template <bool PAGED, bool S16, int BITS = 2>
 __device__ __forceinline__ void stage_values(const DecodeArgs &a, int64_t bh, int64_t blk,
-                                             uint32_t s, const PartOffsets<S16> &o) {
-  const void *rec = uniform_ptr(record_of<PAGED, S16>(a, bh, blk));
-  constexpr uint32_t vc = offsetof(VStage, vc), vs = offsetof(VStage, vs),
-                     vz = offsetof(VStage, vz);
+                                             uint32_t s, const PartOffsets<S16, BITS> &o) {
+  using VS = VStageT<BITS>;
+  constexpr int NC = PartOffsets<S16, BITS>::NC;
+  const void *rec = uniform_ptr(record_of<PAGED, S16, BITS>(a, bh, blk));
+  constexpr uint32_t vc = offsetof(VS, vc), vs = offsetof(VS, vs), vz = offsetof(VS, vz);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dma16nt_m0(rec, o.v[i], s + vc + i * 1024);
+  for (int i = 0; i < NC; ++i) dma16nt_m0(rec, o.v[i], s + vc + i * 1024);
   if constexpr (S16) {
-    dma16nt_m0(rec, o.v[4], s + vs);
+    dma16nt_m0(rec, o.v[NC], s + vs);
   } else {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16nt_m0(rec, o.v[4 + i], s + vs + i * 1024);
+    for (int i = 0; i < 2; ++i) dma16nt_m0(rec, o.v[NC + i], s + vs + i * 1024);
   }
-  dma16nt_m0(rec, o.v[PartOffsets<S16>::N - 1], s + vz);
+  dma16nt_m0(rec, o.v[PartOffsets<S16, BITS>::N - 1], s + vz);
 }
 
 // Selected attention (mode 2): the stored scores of block `blk` for the
@@ -370,11 +381,17 @@ __device__ __forceinline__ void wait_lds8(float (&x)[8]) {
 }
 
 // Wait for this wave's LDS reads, including the transpose reads whose
-// results are in x[0..7].
-__device__ __forceinline__ void wait_regs(i2 (&x)[8]) {
+// results are in x[0..N).
+template <int N>
+__device__ __forceinline__ void wait_regs(i2 (&x)[N]) {
+  static_assert(N == 8 || N == 16, "8 or 16 transposed reads");
   asm volatile("s_waitcnt lgkmcnt(0)"
                : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]),
                  "+v"(x[6]), "+v"(x[7])::"memory");
+  if constexpr (N == 16)
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]), "+v"(x[13]),
+                   "+v"(x[14]), "+v"(x[15])::"memory");
 }
 
 // B operands from one transposed dword holding nibbles 0..7 (two codes
@@ -394,6 +411,27 @@ __device__ __forceinline__ void codes_to_b(uint32_t x, h8 &be, h8 &bo) {
   be = (h8){e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
   bo = (h8){o0[0], o0[1], o1[0], o1[1], o2[0], o2[1], o3[0], o3[1]};
 }
+
+// B operand from one transposed dword holding nibbles 0..7, one 4-bit code
+// each.  A byte 0..15 read as FP8 E4M3 is code * 2^-9, and the gfx950 packed
+// FP8 -> FP16 conversion with scale 2^9 returns the exact fp16 code, two per
+// instruction.  The bytes of x & 0x0F0F0F0F are nibbles 0, 2, 4, 6 and those
+// of (x >> 4) & 0x0F0F0F0F nibbles 1, 3, 5, 7, so element e of the operand
+// is the code of nibble perm4(e); the A operand is built in the same order
+// (the contraction index order within one MFMA is free).
+__device__ __forceinline__ h8 codes4_to_b(uint32_t x) {
+  const uint32_t ev = x & 0x0F0F0F0Fu;
+  const uint32_t od = (x >> 4) & 0x0F0F0F0Fu;
+  const h2v e0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ev, 512.0f, false);
+  const h2v e1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ev, 512.0f, true);
+  const h2v o0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(od, 512.0f, false);
+  const h2v o1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(od, 512.0f, true);
+  return (h8){e0[0], e0[1], e1[0], e1[1], o0[0], o0[1], o1[0], o1[1]};
+}
+__host__ __device__ constexpr int perm4(int e) { return e < 4 ? 2 * e : 2 * (e - 4) + 1; }
+// Contraction index of element e of a B operand built from 8 nibbles.
+template <int BITS>
+__host__ __device__ constexpr int k_order(int e) { return BITS == 2 ? e : perm4(e); }
 
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -480,15 +518,24 @@ struct BlockShare {
 // stored scores (copied into the key buffer), -inf for the tokens the row's
 // selection rule (a.sel) does not take; then the softmax and values as in
 // MODE 0.  The mask is part of the stored scores.
-template <int NREP, bool MASKED, bool PAGED, bool S16, int MODE>
+// BITS 4 (4-bit keys and values, attention only): a transposed read holds one
+// code per nibble, so a key tile of 16 columns is 16 consecutive tokens (2-bit:
+// 16 token pairs, split into even and odd tiles) and a value tile 16
+// consecutive channels.  Index e of the score and accumulator pairs below is
+// then that half of the key group or of the channel group instead of the token
+// or channel parity.
+template <int NREP, bool MASKED, bool PAGED, bool S16, int MODE, int BITS = 2>
 __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare &sh,
                                            int64_t first, int hk, int b, const Lds &L,
-                                           KStage *__restrict__ kbuf,
-                                           VStage *__restrict__ vbuf) {
+                                           KStageT<BITS> *__restrict__ kbuf,
+                                           VStageT<BITS> *__restrict__ vbuf) {
   static_assert(NREP == 1 || NREP == 2 || NREP == 4, "query heads per KV head");
   static_assert(MODE != 2 || !MASKED, "selected attention takes the mask from the scores");
+  static_assert(BITS == 2 || MODE == 0, "4-bit codes: attention only");
   constexpr int GA = 16 / NREP;       // key groups per A operand
-  constexpr int SD = Rec<S16>::dma;
+  constexpr int SD = Rec<S16, BITS>::dma;
+  // token of score pair element e of key group g held by lane i
+  auto tok = [](int g, int e, int i) { return BITS == 2 ? 32 * g + 2 * i + e : 32 * g + 16 * e + i; };
   // copies of a block's key part (MODE 2: its scores) and value part
   constexpr int KDMA = MODE == 2 ? kScoreDma<NREP> : SD + (MASKED ? 2 : 0);
   constexpr int VDMA = MODE == 1 ? 0 : SD;
@@ -524,7 +571,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
   // copies; the copies complete in order, so waiting for q alone lets the
   // block stream in meanwhile.  Lanes past the q rows re-read the last 16
   // bytes.
-  const PartOffsets<S16> dmo{DmaOffsets(lane)};
+  const PartOffsets<S16, BITS> dmo{DmaOffsets(lane)};
   const uint16_t *q_lds = (const uint16_t *)&L.p[0][0];
   int64_t cur = sh.block((int)first);   // the block being processed
   if constexpr (MODE != 2)
@@ -533,9 +580,9 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
   if constexpr (MODE == 2) {
     stage_scores<NREP>(a, b, hk, cur, k_lds, lane);
   } else {
-    stage_keys<MASKED, PAGED, S16>(a, bh, cur, k_lds, mask_lds, dmo, lane);
+    stage_keys<MASKED, PAGED, S16, BITS>(a, bh, cur, k_lds, mask_lds, dmo, lane);
   }
-  if constexpr (MODE != 1) stage_values<PAGED, S16>(a, bh, cur, v_lds, dmo);
+  if constexpr (MODE != 1) stage_values<PAGED, S16, BITS>(a, bh, cur, v_lds, dmo);
   if constexpr (MODE != 2) wait_vm<KDMA + VDMA>();   // q
   // the row's selection rule for the scores this lane holds (head h_s)
   SelectRow selr{};
@@ -637,21 +684,35 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
     } else {
     if constexpr (MODE == 1) store_prev();
     // ================= key half =================
-    const KStage &kst = *kbuf;
-    i2 xk[8];                        // [group g][64-channel half rho]
+    const KStageT<BITS> &kst = *kbuf;
+    // 2-bit: [group g][64-channel half rho]; 4-bit: [g][rho][16-token half u]
+    constexpr int NXK = BITS == 2 ? 8 : 16;
+    i2 xk[NXK];
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int rho = 0; rho < 2; ++rho)
-        xk[2 * g + rho] = tr4(kst.kc + g * 256 + (64 * rho + 16 * kg + i) * 2);
+      for (int rho = 0; rho < 2; ++rho) {
+        if constexpr (BITS == 2) {
+          xk[2 * g + rho] = tr4(kst.kc + g * 256 + (64 * rho + 16 * kg + i) * 2);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            xk[4 * g + 2 * rho + u] = tr4(kst.kc + g * 512 + (64 * rho + 16 * kg + i) * 4 + 2 * u);
+        }
+      }
     float mk[4][2];
     constexpr float kMaskUnit = MODE == 1 ? 1.0f : 1.4426950408889634f;   // natural or log2
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       if (MASKED) {
-        const float2 m2 = *(const float2 *)(L.mask + 32 * g + 2 * i);
-        mk[g][0] = m2.x * kMaskUnit;
-        mk[g][1] = m2.y * kMaskUnit;
+        if constexpr (BITS == 2) {
+          const float2 m2 = *(const float2 *)(L.mask + 32 * g + 2 * i);
+          mk[g][0] = m2.x * kMaskUnit;
+          mk[g][1] = m2.y * kMaskUnit;
+        } else {
+          mk[g][0] = L.mask[tok(g, 0, i)] * kMaskUnit;
+          mk[g][1] = L.mask[tok(g, 1, i)] * kMaskUnit;
+        }
       } else {
         mk[g][0] = mk[g][1] = 0.0f;
       }
@@ -667,14 +728,17 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
       const h8 zv = *(const h8 *)(kst.kz + zrot_off(g_a, c0));
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
-        split_mul2(qa[ks][j], sv[j], qa[ks][j + 1], sv[j + 1], ah[ks], al[ks], j);
+        // element j of the operands holds channel c0 + k_order(j)
+        const int j0 = k_order<BITS>(j), j1 = k_order<BITS>(j + 1);
+        split_mul2(qa[ks][j0], sv[j0], qa[ks][j1], sv[j1], ah[ks], al[ks], j);
         bz = fmaf(qa[ks][j], (float)zv[j], bz);
         bz = fmaf(qa[ks][j + 1], (float)zv[j + 1], bz);
       }
     }
     // every read of the key part has completed: request the next one
     wait_regs(xk);
-    if constexpr (has_next) stage_keys<MASKED, PAGED, S16>(a, bh, nxt, k_lds, mask_lds, dmo, lane);
+    if constexpr (has_next)
+      stage_keys<MASKED, PAGED, S16, BITS>(a, bh, nxt, k_lds, mask_lds, dmo, lane);
 
     bz = group_sum(bz);
     if (kg == 0) L.bias[i] = bz;
@@ -685,16 +749,30 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
       dk[g][0] = dk[g][1] = (f4){0, 0, 0, 0};
 #pragma unroll
       for (int rho = 0; rho < 2; ++rho) {
-        const i2 x = xk[2 * g + rho];
+        if constexpr (BITS == 2) {
+          const i2 x = xk[2 * g + rho];
 #pragma unroll
-        for (int d = 0; d < 2; ++d) {
-          h8 be, bo;
-          codes_to_b((uint32_t)x[d], be, bo);
-          const int ks = 2 * rho + d;
-          dk[g][0] = mfma(ah[ks], be, dk[g][0]);
-          dk[g][1] = mfma(ah[ks], bo, dk[g][1]);
-          dk[g][0] = mfma(al[ks], be, dk[g][0]);
-          dk[g][1] = mfma(al[ks], bo, dk[g][1]);
+          for (int d = 0; d < 2; ++d) {
+            h8 be, bo;
+            codes_to_b((uint32_t)x[d], be, bo);
+            const int ks = 2 * rho + d;
+            dk[g][0] = mfma(ah[ks], be, dk[g][0]);
+            dk[g][1] = mfma(ah[ks], bo, dk[g][1]);
+            dk[g][0] = mfma(al[ks], be, dk[g][0]);
+            dk[g][1] = mfma(al[ks], bo, dk[g][1]);
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const i2 x = xk[4 * g + 2 * rho + u];
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+              const h8 bq = codes4_to_b((uint32_t)x[d]);
+              const int ks = 2 * rho + d;
+              dk[g][u] = mfma(ah[ks], bq, dk[g][u]);
+              dk[g][u] = mfma(al[ks], bq, dk[g][u]);
+            }
+          }
         }
       }
     }
@@ -736,7 +814,12 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
         const float p0 = m_new == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s2[g][0] - m_new);
         const float p1 = m_new == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s2[g][1] - m_new);
         lsum += p0 + p1;
-        *(float2 *)(&L.p[h_s][32 * g + 2 * i]) = make_float2(p0, p1);
+        if constexpr (BITS == 2) {
+          *(float2 *)(&L.p[h_s][32 * g + 2 * i]) = make_float2(p0, p1);
+        } else {
+          L.p[h_s][tok(g, 0, i)] = p0;
+          L.p[h_s][tok(g, 1, i)] = p1;
+        }
       }
       l_run = fmaf(l_run, alpha, lsum);
       m_run = m_new;
@@ -749,13 +832,22 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
     else
       wait_vm<0>();
     wave_lds_sync();
-    const VStage &vst = *vbuf;
-    i2 xv[8];                        // [32-token half u][channel group g]
+    const VStageT<BITS> &vst = *vbuf;
+    // 2-bit: [16-token half u][channel group g]; 4-bit: [u][16-channel unit w]
+    constexpr int NXV = BITS == 2 ? 8 : 16;
+    i2 xv[NXV];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < 2; ++u) {
+      if constexpr (BITS == 2) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        xv[4 * u + g] = tr4(vst.vc + (32 * kg + 16 * u + i) * 8 + g * 2);
+        for (int g = 0; g < 4; ++g)
+          xv[4 * u + g] = tr4(vst.vc + (32 * kg + 16 * u + i) * 8 + g * 2);
+      } else {
+#pragma unroll
+        for (int w = 0; w < 8; ++w)
+          xv[8 * u + w] = tr4(vst.vc + (32 * kg + 16 * u + i) * 16 + w * 2);
+      }
+    }
     {
       // accumulators follow the running maximum
       const float av = v_valid ? L.alpha[kg] : 1.0f;
@@ -781,7 +873,8 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
         const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
 #pragma unroll
         for (int j = 0; j < 8; j += 2) {
-          split_mul2(pv[j], sv[j], pv[j + 1], sv[j + 1], vh[u][d], vl[u][d], j);
+          const int j0 = k_order<BITS>(j), j1 = k_order<BITS>(j + 1);
+          split_mul2(pv[j0], sv[j0], pv[j1], sv[j1], vh[u][d], vl[u][d], j);
           zt = fmaf(pv[j], (float)zv[j], zt);
           zt = fmaf(pv[j + 1], (float)zv[j + 1], zt);
         }
@@ -789,21 +882,36 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
     }
     // every read of the value part has completed: request the next one
     wait_regs(xv);
-    if constexpr (has_next) stage_values<PAGED, S16>(a, bh, nxt, v_lds, dmo);
+    if constexpr (has_next) stage_values<PAGED, S16, BITS>(a, bh, nxt, v_lds, dmo);
 
+    // dv[g][e]: channels 32 g + 2 j + e (2-bit) or 32 g + 16 e + j (4-bit)
+    // of column j
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const i2 x = xv[4 * u + g];
+        if constexpr (BITS == 2) {
+          const i2 x = xv[4 * u + g];
 #pragma unroll
-        for (int d = 0; d < 2; ++d) {
-          h8 be, bo;
-          codes_to_b((uint32_t)x[d], be, bo);
-          dv[g][0] = mfma(vh[u][d], be, dv[g][0]);
-          dv[g][1] = mfma(vh[u][d], bo, dv[g][1]);
-          dv[g][0] = mfma(vl[u][d], be, dv[g][0]);
-          dv[g][1] = mfma(vl[u][d], bo, dv[g][1]);
+          for (int d = 0; d < 2; ++d) {
+            h8 be, bo;
+            codes_to_b((uint32_t)x[d], be, bo);
+            dv[g][0] = mfma(vh[u][d], be, dv[g][0]);
+            dv[g][1] = mfma(vh[u][d], bo, dv[g][1]);
+            dv[g][0] = mfma(vl[u][d], be, dv[g][0]);
+            dv[g][1] = mfma(vl[u][d], bo, dv[g][1]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const i2 x = xv[8 * u + 2 * g + e];
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+              const h8 bq = codes4_to_b((uint32_t)x[d]);
+              dv[g][e] = mfma(vh[u][d], bq, dv[g][e]);
+              dv[g][e] = mfma(vl[u][d], bq, dv[g][e]);
+            }
+          }
         }
       }
     }
@@ -838,8 +946,15 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
   if (v_valid) {
     const f4 z4 = *(const f4 *)(L.bias + 4 * kg);
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      *(float2 *)&L.p[kg][32 * g + 2 * i] = make_float2(dv[g][0][g] + z4[g], dv[g][1][g] + z4[g]);
+    for (int g = 0; g < 4; ++g) {
+      if constexpr (BITS == 2) {
+        *(float2 *)&L.p[kg][32 * g + 2 * i] =
+            make_float2(dv[g][0][g] + z4[g], dv[g][1][g] + z4[g]);
+      } else {
+        L.p[kg][32 * g + i] = dv[g][0][g] + z4[g];
+        L.p[kg][32 * g + 16 + i] = dv[g][1][g] + z4[g];
+      }
+    }
   }
   if (k_valid && i == 0)
     *(float2 *)&L.p[h_s][kD] =
@@ -1313,14 +1428,19 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
 // reload inside the block loop would wait for every DMA in flight.
 // MODE 1 (scores) and MODE 2 (selected attention): see block_role; MODE 1
 // writes no partials.
-template <int NREP, bool MASKED, bool RAGGED, bool PAGED, bool S16, int MODE>
-__global__ void __launch_bounds__(MASKED ? 256 : 512)
+// BITS 4 (4-bit codes, attention only): blocks only, six waves (four
+// masked) so that their 11 KB stages fit the LDS; the tokens past the last
+// whole block are left to another launch (n_window_all is 0), so the
+// workgroups never merge into out themselves.
+template <int NREP, bool MASKED, bool RAGGED, bool PAGED, bool S16, int MODE, int BITS = 2>
+__global__ void __launch_bounds__(MASKED ? 256 : (BITS == 2 ? 512 : 384))
     __attribute__((amdgpu_waves_per_eu(MASKED ? 1 : 2)))
     decode_matrix_kernel(DecodeArgs a, int64_t n_main_all, int n_groups_all, int n_window_all,
                          MatrixRowArg<RAGGED> rows) {
-  constexpr int W = MASKED ? 4 : 8;
-  __shared__ KStage sm_k[W];
-  __shared__ VStage sm_v[W];
+  static_assert(BITS == 2 || (MODE == 0 && !RAGGED), "4-bit codes: uniform attention only");
+  constexpr int W = MASKED ? 4 : (BITS == 2 ? 8 : 6);
+  __shared__ KStageT<BITS> sm_k[W];
+  __shared__ VStageT<BITS> sm_v[W];
   __shared__ __attribute__((aligned(16))) float sm_p[W][4][kPRow];
   __shared__ __attribute__((aligned(16))) float sm_mask[W][kBT];
   __shared__ __attribute__((aligned(16))) float sm_bias[W][16];
@@ -1328,7 +1448,9 @@ __global__ void __launch_bounds__(MASKED ? 256 : 512)
   __shared__ int sm_ctr;
   // wave-uniform, so that the wave's LDS addresses stay scalar
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const Lds L{&sm_k[w], &sm_v[w], sm_p[w], sm_mask[w], sm_bias[w], sm_alpha[w]};
+  // (the window role, 2-bit only, is the one user of L.ks and L.vs)
+  const Lds L{reinterpret_cast<KStage *>(&sm_k[w]), reinterpret_cast<VStage *>(&sm_v[w]), sm_p[w],
+              sm_mask[w], sm_bias[w], sm_alpha[w]};
   const uint32_t lin = blockIdx.x;
   uint32_t s, sl;
   int hk, b, n_groups, n_window;
@@ -1376,15 +1498,17 @@ __global__ void __launch_bounds__(MASKED ? 256 : 512)
   if (threadIdx.x == 0) sm_ctr = 0;
   __syncthreads();
   int item = draw_item(&sm_ctr, lane);
-  while (item < sh.n_skip) {
-    const int x = (int)s + item * n_groups;
-    const WinLoads<NREP> ld = window_issue<NREP, PAGED, S16, MODE>(a, rs, n_main, x, hk, b, L);
-    window_role<NREP, MASKED, PAGED, S16, MODE>(a, rs, n_main, x, n_groups + x, hk, b, L, ld);
-    wave_lds_sync();   // the LDS reads of the chunk are done
-    item = draw_item(&sm_ctr, lane);
+  if constexpr (BITS == 2) {
+    while (item < sh.n_skip) {
+      const int x = (int)s + item * n_groups;
+      const WinLoads<NREP> ld = window_issue<NREP, PAGED, S16, MODE>(a, rs, n_main, x, hk, b, L);
+      window_role<NREP, MASKED, PAGED, S16, MODE>(a, rs, n_main, x, n_groups + x, hk, b, L, ld);
+      wave_lds_sync();   // the LDS reads of the chunk are done
+      item = draw_item(&sm_ctr, lane);
+    }
   }
-  block_role<NREP, MASKED, PAGED, S16, MODE>(a, sh, item - sh.n_skip, hk, b, L, &sm_k[w],
-                                             &sm_v[w]);
+  block_role<NREP, MASKED, PAGED, S16, MODE, BITS>(a, sh, item - sh.n_skip, hk, b, L, &sm_k[w],
+                                                   &sm_v[w]);
   if constexpr (MODE == 1) return;   // the scores are stored; no partials
 
   // The W partials of the workgroup's waves, merged with the log-sum-exp
@@ -1419,7 +1543,7 @@ __global__ void __launch_bounds__(MASKED ? 256 : 512)
   // A slab with one workgroup: it merges its slot and the window chunks'
   // slots (all written by its own waves) into out itself, and no combine
   // launch follows.  With more, the combine kernel merges the slots.
-  if (n_groups > 1) return;
+  if (BITS == 4 || n_groups > 1) return;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's slot stores are done
   __syncthreads();
   const int S = n_groups + n_window;   // slots of this slab; a.S_total is their stride
@@ -1461,9 +1585,9 @@ __global__ void __launch_bounds__(MASKED ? 256 : 512)
   }
 }
 
-template <bool S16>
+template <bool S16, int BITS = 2>
 static bool layout_is(const Layout &L) {
-  using RC = Rec<S16>;
+  using RC = Rec<S16, BITS>;
   return L.sb == RC::sb && L.rec == RC::bytes && L.kc == RC::kc && L.ks == RC::ks &&
          L.kz == RC::kz && L.vc == RC::vc && L.vs == RC::vs && L.vz == RC::vz;
 }
@@ -1477,6 +1601,17 @@ bool decode_matrix_supported(const DecodeArgs &a) {
          ((uintptr_t)a.k_res & 15) == 0 && ((uintptr_t)a.v_res & 15) == 0 &&
          ((uintptr_t)a.q & 15) == 0;
 }
+
+bool decode_matrix4_supported(const DecodeArgs &a) {
+  // records of the 4-bit / G 32 / head_dim 128 shape (fp32 or fp16 scales)
+  // in a contiguous cache; q copied 16 bytes at a time
+  return a.kb == 4 && a.vb == 4 && a.G == kG && a.D == kD &&
+         (a.n_rep == 1 || a.n_rep == 2 || a.n_rep == 4) && a.L.pt == nullptr &&
+         (layout_is<false, 4>(a.L) || layout_is<true, 4>(a.L)) &&
+         ((uintptr_t)a.L.blocks & 15) == 0 && ((uintptr_t)a.q & 15) == 0;
+}
+
+int decode_matrix4_waves(const DecodeArgs &a) { return a.mask ? 4 : 6; }
 
 int decode_matrix_window_chunks(const DecodeArgs &a, int64_t n_main) {
   return matrix_window_chunks(a.t, n_main);
@@ -1550,6 +1685,44 @@ hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int n_group
   const int64_t n_wg = (int64_t)n_groups * a.H * a.B;
   if (n_wg > ((int64_t)1 << 25)) return hipErrorInvalidValue;   // 32-bit workgroup ids
   launch_reps<false>(a, dim3((unsigned)n_wg), s, n_main, n_groups, n_window, NoRows{});
+  return hipGetLastError();
+}
+
+// 4-bit codes: the blocks of tokens [0, n_main) only, partial slots [0,
+// n_groups) of each query head; the caller covers [n_main, t) and merges.
+template <int NREP, bool S16>
+static void launch_rep4(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
+                        int n_groups) {
+  if (a.mask)
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, true, false, false, S16, 0, 4>), grid,
+                       dim3(256), 0, s, a, n_main, n_groups, 0, NoRows{});
+  else
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, false, false, false, S16, 0, 4>), grid,
+                       dim3(384), 0, s, a, n_main, n_groups, 0, NoRows{});
+}
+
+template <bool S16>
+static void launch_reps4(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
+                         int n_groups) {
+  switch (a.n_rep) {
+    case 1: launch_rep4<1, S16>(a, grid, s, n_main, n_groups); break;
+    case 2: launch_rep4<2, S16>(a, grid, s, n_main, n_groups); break;
+    default: launch_rep4<4, S16>(a, grid, s, n_main, n_groups); break;
+  }
+}
+
+hipError_t launch_decode_matrix4(const DecodeArgs &a, int64_t n_main, int n_groups,
+                                 hipStream_t s) {
+  if (!decode_matrix4_supported(a) || a.t <= 0 || a.t_new >= 0 || n_main < kBT ||
+      n_main % kBT != 0 || n_main > a.n_vq || n_main > a.n_kq || n_groups <= 0 ||
+      n_groups > a.S_total)
+    return hipErrorInvalidValue;
+  const int64_t n_wg = (int64_t)n_groups * a.H * a.B;
+  if (n_wg > ((int64_t)1 << 25)) return hipErrorInvalidValue;   // 32-bit workgroup ids
+  if (a.L.sb == 2)
+    launch_reps4<true>(a, dim3((unsigned)n_wg), s, n_main, n_groups);
+  else
+    launch_reps4<false>(a, dim3((unsigned)n_wg), s, n_main, n_groups);
   return hipGetLastError();
 }
 
