@@ -305,6 +305,9 @@ def main():
                          "then attention over the selected tokens) on the same replicas")
     ap.add_argument("--scale-fp16", action="store_true",
                     help="the fp16-scale layout: scales stored as binary16")
+    ap.add_argument("--kv-bits", type=int, default=0, choices=(0, 2, 4),
+                    help="code width of keys and values (0 = the workload's own); 4 on a 2-bit "
+                         "workload is its KIVI-4 variant, named with a -kivi4 suffix")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device-to-device copy of this "
                          "many MiB (a known-size reference for hardware byte counters)")
@@ -323,6 +326,9 @@ def main():
     ragged = args.workload == synth.RAGGED.index
     w = synth.RAGGED if ragged else synth.WORKLOADS[args.workload]
     w = w.replace(scale_fp16=args.scale_fp16)
+    if args.kv_bits and (args.kv_bits, args.kv_bits) != (w.k_bits, w.v_bits):
+        w = w.replace(k_bits=args.kv_bits, v_bits=args.kv_bits,
+                      name=w.name + f"-kivi{args.kv_bits}")
     inp = synth.make_inputs(w.replace(steps=1))
     # prefill length of each batch row (a ragged batch: its own per row)
     lengths = ([int(x) for x in synth.ragged_lengths(w.B, 1024, w.T0)] if ragged

@@ -325,16 +325,19 @@ int make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
     return KIVI_OK;
   }
   // 4-bit keys and values: the matrix kernel takes the whole 128-token blocks
-  // (by default where several query heads share a KV head, whose keys and
-  // values the vector kernel reads once per pair of heads), and the vector
-  // kernel the rest, kTailSplit tokens per split
-  if ((path == KIVI_PATH_MATRIX || (path == KIVI_PATH_AUTO && n_rep >= 2)) && t > 0 &&
-      !r.ragged && a.t_new < 0 && kivi::decode_matrix4_supported(a) &&
-      kivi::decode_vector_supported(a)) {
+  // (the vector kernel reads the keys and values once per pair of query
+  // heads), and the vector kernel the rest, kTailSplit tokens per split
+  if ((path == KIVI_PATH_MATRIX || path == KIVI_PATH_AUTO) && t > 0 && !r.ragged &&
+      a.t_new < 0 && kivi::decode_matrix4_supported(a) && kivi::decode_vector_supported(a)) {
     const int64_t n_main = kivi::matrix_main(kivi::row_span(t, a.R, false), a.R);
-    if (n_main >= kMatrixBlock) {
-      const int64_t blocks = n_main / kMatrixBlock;
-      const int waves = kivi::decode_matrix4_waves(a);
+    const int64_t blocks = n_main / kMatrixBlock;
+    const int waves = kivi::decode_matrix4_waves(a);
+    // one query head per KV head: the vector kernel reads everything once
+    // too, and is faster on short rows (measured: B64 x 32 heads at 2049
+    // tokens, 15 blocks, 138 against 177 us; B8 x 32 heads at 4065 tokens, 30
+    // blocks, 55 against 46 us)
+    const bool worth = path == KIVI_PATH_MATRIX || n_rep >= 2 || blocks >= 3 * waves;
+    if (blocks >= 1 && worth) {
       int64_t groups;
       if (tps_req == 0) {
         // one workgroup per CU (its LDS takes most of the CU's)
