@@ -178,7 +178,6 @@ int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
 
 constexpr int kGenericMinSplit = 256;
 constexpr int kMatrixBlock = 128;   // tokens per block of the matrix-core kernel
-constexpr int kTailSplit = 128;     // tokens per vector-kernel split past the 4-bit blocks
 constexpr int kVectorStep = 128;    // tokens per step of the vector kernel's four waves
 // Vector kernel: workgroups to aim for.  Three waves per SIMD hold 768
 // workgroups at once; fewer, longer splits measure faster than twice as
@@ -206,11 +205,6 @@ struct Plan {
   int64_t n_main = 0;           // tokens [0, n_main) in the matrix kernel's block role
   int n_groups_matrix = 0;      // matrix-kernel workgroups per slab
   int n_window = 0;             // 32-token chunks of [n_main, t) in its window role
-  // 4-bit matrix kernel over the blocks of [0, n_main) (n_groups_matrix
-  // workgroups per slab, slots [0, n_groups_matrix)), then the vector kernel
-  // over [n_main, t) (n_split_generic splits of tps_generic tokens, the
-  // slots after them)
-  bool matrix4 = false;
   bool vector = false;          // vector kernel instead of the scalar one
   int tps_generic = 0;          // vector / scalar kernel (shapes the matrix kernel does not cover)
   int n_split_generic = 0;
@@ -290,14 +284,30 @@ int plan_matrix_rows(const kivi_cache *c, const Rows &r, int32_t tps_req, int wa
   return KIVI_OK;
 }
 
+// Whether the matrix kernel takes this call: the 2-bit shapes it handles
+// (any batch), and 4-bit ones of a uniform batch -- by default where several
+// query heads share a KV head (the vector kernel reads the cache once per
+// pair of query heads), and with one from three blocks per wave of a
+// workgroup on (the vector kernel is faster on shorter rows; measured on B64
+// x 32 heads at 2049 tokens, 15 blocks: 138 against 177 us; on B8 x 32 heads
+// at 4065 tokens, 30 blocks: 55 against 46 us).
+bool matrix_wanted(const kivi::DecodeArgs &a, int32_t path, bool ragged) {
+  if (!(path == KIVI_PATH_AUTO || path == KIVI_PATH_MATRIX) || a.t <= 0) return false;
+  if (kivi::decode_matrix_supported(a)) return true;
+  if (ragged || !kivi::decode_matrix4_supported(a)) return false;
+  if (path == KIVI_PATH_MATRIX || a.n_rep >= 2) return true;
+  const int64_t blocks =
+      kivi::matrix_main(kivi::row_span(a.t, a.R, a.t_new >= 0), a.R) / kMatrixBlock;
+  return blocks >= 3 * kivi::decode_matrix_waves(a);
+}
+
 // Split plan.  Deterministic in (shape, token counts, options).
 int make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
               const kivi::DecodeArgs &a, const Rows &r, Plan &p, const char *who) {
   const int64_t t = a.t;
   const int n_rep = Hq / c->n_kv_heads;
   const int64_t units = (int64_t)c->batch * c->n_kv_heads;
-  p.matrix = (path == KIVI_PATH_AUTO || path == KIVI_PATH_MATRIX) && t > 0 &&
-             kivi::decode_matrix_supported(a);
+  p.matrix = matrix_wanted(a, path, r.ragged);
   if (p.matrix && r.ragged)
     return plan_matrix_rows(c, r, tps_req, kivi::decode_matrix_waves(a), a.t_new >= 0, p, who);
   if (p.matrix) {
@@ -307,9 +317,9 @@ int make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
     const int waves = kivi::decode_matrix_waves(a);
     int64_t groups;
     if (tps_req == 0) {
-      // one workgroup per CU (two for the four-wave masked variant), no more
-      // than the blocks and window chunks keep busy
-      const int64_t per_cu = 8 / waves;
+      // one workgroup per CU (two for the four-wave masked variant of 2-bit
+      // codes), no more than the blocks and window chunks keep busy
+      const int64_t per_cu = a.kb == 4 ? 1 : 8 / waves;
       const int64_t target = max64(1, device_cus() * per_cu / units);
       groups = std::min(target, max64(1, ceil_div(blocks + p.n_window, waves)));
     } else {
@@ -323,39 +333,6 @@ int make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
     // a slab with a single workgroup writes its output itself
     p.combine = groups > 1;
     return KIVI_OK;
-  }
-  // 4-bit keys and values: the matrix kernel takes the whole 128-token blocks
-  // (the vector kernel reads the keys and values once per pair of query
-  // heads), and the vector kernel the rest, kTailSplit tokens per split
-  if ((path == KIVI_PATH_MATRIX || path == KIVI_PATH_AUTO) && t > 0 && !r.ragged &&
-      a.t_new < 0 && kivi::decode_matrix4_supported(a) && kivi::decode_vector_supported(a)) {
-    const int64_t n_main = kivi::matrix_main(kivi::row_span(t, a.R, false), a.R);
-    const int64_t blocks = n_main / kMatrixBlock;
-    const int waves = kivi::decode_matrix4_waves(a);
-    // one query head per KV head: the vector kernel reads everything once
-    // too, and is faster on short rows (measured: B64 x 32 heads at 2049
-    // tokens, 15 blocks, 138 against 177 us; B8 x 32 heads at 4065 tokens, 30
-    // blocks, 55 against 46 us)
-    const bool worth = path == KIVI_PATH_MATRIX || n_rep >= 2 || blocks >= 3 * waves;
-    if (blocks >= 1 && worth) {
-      int64_t groups;
-      if (tps_req == 0) {
-        // one workgroup per CU (its LDS takes most of the CU's)
-        const int64_t target = max64(1, device_cus() / units);
-        groups = std::min(target, max64(1, ceil_div(blocks, waves)));
-      } else {
-        const int64_t tps = ceil_div(tps_req, kMatrixBlock) * kMatrixBlock;
-        groups = max64(1, ceil_div(n_main, tps));
-      }
-      p.matrix4 = true;
-      p.n_main = n_main;
-      p.n_groups_matrix = (int)groups;
-      p.tps_generic = kTailSplit;
-      p.n_split_generic = (int)ceil_div(t - n_main, kTailSplit);
-      p.S_total = (int)groups + p.n_split_generic;
-      p.combine = true;
-      return KIVI_OK;
-    }
   }
   p.vector = (path == KIVI_PATH_AUTO || path == KIVI_PATH_VECTOR) &&
              kivi::decode_vector_supported(a);
@@ -734,7 +711,7 @@ int decode_call(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, cons
   a.sm_scale = 1.0f / sqrtf((float)a.D);
 
   if (path == KIVI_PATH_MATRIX && !kivi::decode_matrix_supported(a) &&
-      !(kivi::decode_matrix4_supported(a) && !fused && !r.ragged))
+      !(kivi::decode_matrix4_supported(a) && !r.ragged))
     return fail(KIVI_ERR_INVALID_ARG, "%s: the matrix-core kernel does not handle this shape", who);
   if (path == KIVI_PATH_VECTOR && !kivi::decode_vector_supported(a))
     return fail(KIVI_ERR_INVALID_ARG, "%s: the vector kernel does not handle this shape", who);
@@ -743,10 +720,6 @@ int decode_call(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, cons
   if (rc) return rc;
   if (fused && !p.matrix)
     return fail(KIVI_ERR_INVALID_ARG, "%s: internal: fused step without the matrix kernel", who);
-  if (path == KIVI_PATH_MATRIX && !kivi::decode_matrix_supported(a) && !p.matrix4)
-    return fail(KIVI_ERR_INVALID_ARG,
-                "%s: the 4-bit matrix-core path needs a whole 128-token block of quantized "
-                "keys and values and a residual length that is a multiple of 32", who);
   if (p.S_total > max_slots(c, tokens_per_split))
     return fail(KIVI_ERR_WORKSPACE, "%s: internal split plan exceeds the workspace bound", who);
   a.S_total = p.S_total;
@@ -772,14 +745,6 @@ int decode_call(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, cons
   else if (p.matrix)
     rc = hip_status(kivi::launch_decode_matrix(a, p.n_main, p.n_groups_matrix, s),
                     "kivi_decode_attn (matrix)");
-  else if (p.matrix4) {
-    rc = hip_status(kivi::launch_decode_matrix4(a, p.n_main, p.n_groups_matrix, s),
-                    "kivi_decode_attn (matrix, 4-bit)");
-    if (!rc)
-      rc = hip_status(kivi::launch_decode_vector_range(a, p.n_main, p.tps_generic,
-                                                       p.n_split_generic, p.n_groups_matrix, s),
-                      "kivi_decode_attn (vector, past the blocks)");
-  }
   else if (p.vector)
     rc = hip_status(kivi::launch_decode_vector(a, p.tps_generic, p.n_split_generic, s, rows),
                     "kivi_decode_attn (vector)");
@@ -846,7 +811,11 @@ int kivi_decode_step(kivi_cache *c, const void *k_new_fp16, const void *v_new_fp
   probe.n_rep = n_q_heads / c->n_kv_heads;
   probe.cap = c->capacity;
   probe.q = (const uint16_t *)q_fp16;
-  const bool fused = kivi::decode_matrix_supported(probe) &&
+  probe.mask = mask;
+  probe.R = c->residual;
+  probe.t = rows_of(c).t_max + 1;
+  probe.t_new = probe.t - 1;
+  const bool fused = matrix_wanted(probe, KIVI_PATH_AUTO, c->row_tokens != nullptr) &&
                      ((uintptr_t)k_new_fp16 & 15) == 0 && ((uintptr_t)v_new_fp16 & 15) == 0;
   if (!fused) {
     // a shape the matrix kernel does not take: the append, then the

@@ -976,7 +976,7 @@ struct WinChunk {
   const uint8_t *rec;
 };
 
-template <bool PAGED, bool S16>
+template <bool PAGED, bool S16, int BITS>
 __device__ __forceinline__ WinChunk win_chunk(const DecodeArgs &a, const RowSpan &rs,
                                               int64_t n_main, int chunk, int hk, int b) {
   WinChunk c;
@@ -999,11 +999,11 @@ __device__ __forceinline__ WinChunk win_chunk(const DecodeArgs &a, const RowSpan
   // 16-byte units of scales per channel group (fp32, or fp16 like the zeros)
   c.nqvs = S16 ? c.nqv8 : (c.n_qv + 3) / 4;
   // the chunk lies in one record (Ta is a multiple of 32), at token lt of it
-  c.rec = record_of<PAGED, S16>(a, c.bh, c.Ta / kBT);
+  c.rec = record_of<PAGED, S16, BITS>(a, c.bh, c.Ta / kBT);
   c.lt = (int)(c.Ta % kBT);
-  // value buffer: codes (2 units per token), scales (4 channel groups x
+  // value buffer: codes (BITS units per token), scales (4 channel groups x
   // nqvs units), fp16 zeros (4 x nqv8 units), then fp16 rows (16 units each)
-  c.u_vs = c.n_qv * 2;
+  c.u_vs = c.n_qv * BITS;
   c.u_vz = c.u_vs + 4 * c.nqvs;
   c.u_vrow = c.u_vz + 4 * c.nqv8;
   // Fused decode step: the value that leaves the window with this token
@@ -1025,22 +1025,23 @@ struct WinLoads {
 };
 
 // Units (16 bytes) of a staged key group in the window role's key buffer:
-// codes (64 units), then scales (32 fp32 or 16 fp16 units), then zeros (16).
-template <bool S16>
+// codes (32 BITS units: channel c at words BITS c ..), then scales (32 fp32
+// or 16 fp16 units), then zeros (16).
+template <bool S16, int BITS>
 struct WinKeyUnits {
-  static constexpr int scales = 64, zeros = S16 ? 80 : 96, end = S16 ? 96 : 112;
+  static constexpr int scales = 32 * BITS, zeros = scales + (S16 ? 16 : 32), end = zeros + 16;
 };
 
 // The loads of one window chunk, issued and not waited for.  MODE 1 (scores)
 // stages no values; MODE 2 (selected attention) no keys and no q.
-template <int NREP, bool PAGED, bool S16, int MODE>
+template <int NREP, bool PAGED, bool S16, int MODE, int BITS>
 __device__ __forceinline__ WinLoads<NREP> window_issue(const DecodeArgs &a, const RowSpan &rs,
                                                        int64_t n_main, int chunk, int hk, int b,
                                                        const Lds &L) {
-  using RC = Rec<S16>;
-  using KU = WinKeyUnits<S16>;
+  using RC = Rec<S16, BITS>;
+  using KU = WinKeyUnits<S16, BITS>;
   const int j = threadIdx.x & 63;
-  const WinChunk c = win_chunk<PAGED, S16>(a, rs, n_main, chunk, hk, b);
+  const WinChunk c = win_chunk<PAGED, S16, BITS>(a, rs, n_main, chunk, hk, b);
   const int64_t bh = c.bh, Ta = c.Ta, vq_end = c.vq_end;
   const int n = c.n, nqvs = c.nqvs, nqv8 = c.nqv8, lt = c.lt;
   const bool kq = c.kq, kq_now = c.kq_now;
@@ -1056,7 +1057,7 @@ __device__ __forceinline__ WinLoads<NREP> window_issue(const DecodeArgs &a, cons
       if (kq && !kq_now) {
         const int lg = lt / kG;    // key group within the record
         if (u < KU::scales)
-          src = rec + RC::kc + lg * 1024 + u * 16;
+          src = rec + RC::kc + lg * (512 * BITS) + u * 16;
         else if (u < KU::zeros)
           src = rec + RC::ks + lg * (kD * RC::sb) + (u - KU::scales) * 16;
         else
@@ -1082,7 +1083,7 @@ __device__ __forceinline__ WinLoads<NREP> window_issue(const DecodeArgs &a, cons
     if (u < vu_end) {
       const void *src;
       if (u < u_vs) {
-        src = rec + RC::vc + (lt + u / 2) * 32 + (u % 2) * 16;
+        src = rec + RC::vc + (lt + u / BITS) * (16 * BITS) + (u % BITS) * 16;
       } else if (u < u_vz) {
         const int x = u - u_vs;
         src = rec + RC::vs + ((x / nqvs) * kBT + lt) * RC::sb + (x % nqvs) * 16;
@@ -1114,14 +1115,17 @@ __device__ __forceinline__ WinLoads<NREP> window_issue(const DecodeArgs &a, cons
 // units, mask included); nothing else.  MODE 2 (selected attention): the
 // chunk's scores come from a.scores, -inf where the row's selection rule
 // does not take the token.
-template <int NREP, bool MASKED, bool PAGED, bool S16, int MODE>
+template <int NREP, bool MASKED, bool PAGED, bool S16, int MODE, int BITS>
 __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &rs, int64_t n_main,
                                             int chunk, int slot, int hk, int b, const Lds &L,
                                             const WinLoads<NREP> &ld) {
-  using RC = Rec<S16>;
-  using KU = WinKeyUnits<S16>;
+  using RC = Rec<S16, BITS>;
+  using KU = WinKeyUnits<S16, BITS>;
+  constexpr int VW = 4 * BITS;            // code words per value token
+  constexpr int CPW = 32 / BITS;          // codes per word
+  constexpr uint32_t CM = (1u << BITS) - 1u;
   const int j = threadIdx.x & 63;
-  const WinChunk c = win_chunk<PAGED, S16>(a, rs, n_main, chunk, hk, b);
+  const WinChunk c = win_chunk<PAGED, S16, BITS>(a, rs, n_main, chunk, hk, b);
   const int64_t bh = c.bh, Ta = c.Ta, t_pop = c.t_pop;
   const int n = c.n, n_qv = c.n_qv, nqvs = c.nqvs, nqv8 = c.nqv8;
   const int u_vs = c.u_vs, u_vz = c.u_vz, u_vrow = c.u_vrow;
@@ -1149,16 +1153,18 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
     const float x0 = h2f((uint16_t)(popped & 0xFFFFu)), x1 = h2f((uint16_t)(popped >> 16));
     float mn = first_min(x0, x1), mx = first_max(x0, x1);   // channel 2j comes first
     lanes_first_min_max(mn, mx, j, 16);
-    const float sc = rec_scale<S16>(group_scale(mn, mx, 2));
-    uint32_t w = (quant_code(x0, mn, sc, 2) | (quant_code(x1, mn, sc, 2) << 2)) << (4 * (j & 7));
-    w |= __shfl_xor(w, 1);
-    w |= __shfl_xor(w, 2);
-    w |= __shfl_xor(w, 4);
+    const float sc = rec_scale<S16>(group_scale(mn, mx, BITS));
+    // lanes of one code word: CPW / 2 (two channels per lane)
+    constexpr int LW = CPW / 2;
+    uint32_t w = (quant_code(x0, mn, sc, BITS) | (quant_code(x1, mn, sc, BITS) << BITS))
+                 << (2 * BITS * (j & (LW - 1)));
+#pragma unroll
+    for (int o = 1; o < LW; o <<= 1) w |= __shfl_xor(w, o);
     const int xr = (int)(t_pop - Ta);
     const int gch = j >> 4;
-    if ((j & 7) == 0) {
-      ((uint32_t *)vl)[xr * 8 + (j >> 3)] = w;
-      ((uint32_t *)(recw + RC::vc) + (t_pop % kBT) * 8)[j >> 3] = w;
+    if ((j & (LW - 1)) == 0) {
+      ((uint32_t *)vl)[xr * VW + j / LW] = w;
+      ((uint32_t *)(recw + RC::vc) + (t_pop % kBT) * VW)[j / LW] = w;
     }
     if ((j & 15) == 0) {
       const uint16_t zh = f2h_bits(mn);
@@ -1203,18 +1209,26 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
       mn1 = x1 < mn1 ? x1 : mn1;
       mx1 = x1 > mx1 ? x1 : mx1;
     }
-    const float sc0 = rec_scale<S16>(group_scale(mn0, mx0, 2));
-    const float sc1 = rec_scale<S16>(group_scale(mn1, mx1, 2));
-    uint32_t cw[4] = {0u, 0u, 0u, 0u};   // channel 2j: words 0, 1; channel 2j + 1: words 2, 3
+    const float sc0 = rec_scale<S16>(group_scale(mn0, mx0, BITS));
+    const float sc1 = rec_scale<S16>(group_scale(mn1, mx1, BITS));
+    // channel 2j: words 0 .. BITS - 1; channel 2j + 1: words BITS .. 2 BITS - 1
+    uint32_t cw[2 * BITS];
+#pragma unroll
+    for (int k = 0; k < 2 * BITS; ++k) cw[k] = 0u;
     for (int r = 0; r < kWT; ++r) {
       const uint32_t w = row_word(r);
-      const int sh = 2 * (r & 15), hw = r >> 4;
-      cw[hw] |= quant_code(h2f((uint16_t)(w & 0xFFFFu)), mn0, sc0, 2) << sh;
-      cw[2 + hw] |= quant_code(h2f((uint16_t)(w >> 16)), mn1, sc1, 2) << sh;
+      const int sh = BITS * (r % CPW), hw = r / CPW;
+      cw[hw] |= quant_code(h2f((uint16_t)(w & 0xFFFFu)), mn0, sc0, BITS) << sh;
+      cw[BITS + hw] |= quant_code(h2f((uint16_t)(w >> 16)), mn1, sc1, BITS) << sh;
     }
     wave_lds_sync();   // every lane's row reads are done before the rows are overwritten
-    const uint4 c4 = make_uint4(cw[0], cw[1], cw[2], cw[3]);
-    *(uint4 *)((uint32_t *)kl + 4 * j) = c4;                       // codes: 2 words per channel
+    // codes: BITS words per channel, channels 2j and 2j + 1 at words 2 BITS j ..
+    uint4 c4[BITS / 2];
+#pragma unroll
+    for (int k = 0; k < BITS / 2; ++k) {
+      c4[k] = make_uint4(cw[4 * k], cw[4 * k + 1], cw[4 * k + 2], cw[4 * k + 3]);
+      *(uint4 *)((uint32_t *)kl + 2 * BITS * j + 4 * k) = c4[k];
+    }
     const uint32_t z2 = (uint32_t)f2h_bits(mn0) | ((uint32_t)f2h_bits(mn1) << 16);
     const int64_t grp = Ta / kG;
     const int lg = (int)(grp % (kBT / kG));   // the group within the record
@@ -1227,7 +1241,9 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
       *(float2 *)((float *)(recw + RC::ks) + lg * kD + 2 * j) = make_float2(sc0, sc1);
     }
     *((uint32_t *)(kl + KU::zeros * 16) + j) = z2;
-    *(uint4 *)((uint32_t *)(recw + RC::kc) + (lg * kD + 2 * j) * 2) = c4;
+#pragma unroll
+    for (int k = 0; k < BITS / 2; ++k)
+      *(uint4 *)((uint32_t *)(recw + RC::kc) + (lg * kD + 2 * j) * BITS + 4 * k) = c4[k];
     *(uint32_t *)((uint16_t *)(recw + RC::kz) + lg * kD + 2 * j) = z2;
   }
   wave_lds_sync();
@@ -1243,17 +1259,25 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
     // and q are the same for all lanes of a half (broadcasts); channels are
     // summed in increasing order
     if (kq) {
-      const uint32_t *kc = (const uint32_t *)kl;   // channel c: words 2c, 2c + 1
+      const uint32_t *kc = (const uint32_t *)kl;   // channel c: words BITS c ..
       const char *ks = kl + KU::scales * 16;
       const uint16_t *kz = (const uint16_t *)(kl + KU::zeros * 16);
-      const int sh = 2 * (tj % 16);
+      const int sh = BITS * (tj % CPW);
       const bool hi = tj >= 16;
 #pragma unroll 4
       for (int c = 64 * hf; c < 64 * hf + 64; c += 4) {
-        const uint4 wa = *(const uint4 *)(kc + 2 * c);
-        const uint4 wb = *(const uint4 *)(kc + 2 * c + 4);
-        const uint32_t cw[4] = {hi ? wa.y : wa.x, hi ? wa.w : wa.z, hi ? wb.y : wb.x,
-                                hi ? wb.w : wb.z};
+        uint32_t cw[4];
+        if constexpr (BITS == 2) {
+          const uint4 wa = *(const uint4 *)(kc + 2 * c);
+          const uint4 wb = *(const uint4 *)(kc + 2 * c + 4);
+          cw[0] = hi ? wa.y : wa.x;
+          cw[1] = hi ? wa.w : wa.z;
+          cw[2] = hi ? wb.y : wb.x;
+          cw[3] = hi ? wb.w : wb.z;
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) cw[u] = kc[4 * (c + u) + tj / CPW];
+        }
         f4 s4;
         if constexpr (S16) {
           const uint2 ss = *(const uint2 *)((const uint16_t *)ks + c);
@@ -1270,7 +1294,7 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
         for (int h = 0; h < NREP; ++h) q4[h] = *(const f4 *)&q_s[h][c];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float code = (float)((cw[u] >> sh) & 3u);
+          const float code = (float)((cw[u] >> sh) & CM);
           const float kh = code * s4[u] + z4[u];
 #pragma unroll
           for (int h = 0; h < NREP; ++h) sc[h] = fmaf(q4[h][u], kh, sc[h]);
@@ -1379,11 +1403,11 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
       const int t = t0 + u;
       float v0 = 0.0f, v1 = 0.0f;
       if (t < n_qv) {
-        const uint32_t w = vc[t * 8 + c0 / 16] >> (2 * (c0 % 16));
+        const uint32_t w = vc[t * VW + c0 / CPW] >> (BITS * (c0 % CPW));
         const uint32_t zw = u < 2 ? z2.x : z2.y;
         const float zt = h2f((uint16_t)(u % 2 ? zw >> 16 : zw & 0xFFFFu));
-        v0 = (float)(w & 3u) * s4[u] + zt;
-        v1 = (float)((w >> 2) & 3u) * s4[u] + zt;
+        v0 = (float)(w & CM) * s4[u] + zt;
+        v1 = (float)((w >> BITS) & CM) * s4[u] + zt;
       } else if (t < n) {
         const uint32_t hv = *(const uint32_t *)(vrow + (t - n_qv) * kD + c0);
         v0 = h2f((uint16_t)(hv & 0xFFFFu));
@@ -1428,10 +1452,8 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
 // reload inside the block loop would wait for every DMA in flight.
 // MODE 1 (scores) and MODE 2 (selected attention): see block_role; MODE 1
 // writes no partials.
-// BITS 4 (4-bit codes, attention only): blocks only, six waves (four
-// masked) so that their 11 KB stages fit the LDS; the tokens past the last
-// whole block are left to another launch (n_window_all is 0), so the
-// workgroups never merge into out themselves.
+// BITS 4 (4-bit codes, attention and the fused step of a uniform batch):
+// six waves (four masked) so that their 11 KB stages fit the LDS.
 template <int NREP, bool MASKED, bool RAGGED, bool PAGED, bool S16, int MODE, int BITS = 2>
 __global__ void __launch_bounds__(MASKED ? 256 : (BITS == 2 ? 512 : 384))
     __attribute__((amdgpu_waves_per_eu(MASKED ? 1 : 2)))
@@ -1448,7 +1470,7 @@ __global__ void __launch_bounds__(MASKED ? 256 : (BITS == 2 ? 512 : 384))
   __shared__ int sm_ctr;
   // wave-uniform, so that the wave's LDS addresses stay scalar
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  // (the window role, 2-bit only, is the one user of L.ks and L.vs)
+  // (the window role addresses the stages as bytes: at most 8 KB of rows)
   const Lds L{reinterpret_cast<KStage *>(&sm_k[w]), reinterpret_cast<VStage *>(&sm_v[w]), sm_p[w],
               sm_mask[w], sm_bias[w], sm_alpha[w]};
   const uint32_t lin = blockIdx.x;
@@ -1498,14 +1520,14 @@ __global__ void __launch_bounds__(MASKED ? 256 : (BITS == 2 ? 512 : 384))
   if (threadIdx.x == 0) sm_ctr = 0;
   __syncthreads();
   int item = draw_item(&sm_ctr, lane);
-  if constexpr (BITS == 2) {
-    while (item < sh.n_skip) {
-      const int x = (int)s + item * n_groups;
-      const WinLoads<NREP> ld = window_issue<NREP, PAGED, S16, MODE>(a, rs, n_main, x, hk, b, L);
-      window_role<NREP, MASKED, PAGED, S16, MODE>(a, rs, n_main, x, n_groups + x, hk, b, L, ld);
-      wave_lds_sync();   // the LDS reads of the chunk are done
-      item = draw_item(&sm_ctr, lane);
-    }
+  while (item < sh.n_skip) {
+    const int x = (int)s + item * n_groups;
+    const WinLoads<NREP> ld =
+        window_issue<NREP, PAGED, S16, MODE, BITS>(a, rs, n_main, x, hk, b, L);
+    window_role<NREP, MASKED, PAGED, S16, MODE, BITS>(a, rs, n_main, x, n_groups + x, hk, b, L,
+                                                      ld);
+    wave_lds_sync();   // the LDS reads of the chunk are done
+    item = draw_item(&sm_ctr, lane);
   }
   block_role<NREP, MASKED, PAGED, S16, MODE, BITS>(a, sh, item - sh.n_skip, hk, b, L, &sm_k[w],
                                                    &sm_v[w]);
@@ -1543,7 +1565,7 @@ __global__ void __launch_bounds__(MASKED ? 256 : (BITS == 2 ? 512 : 384))
   // A slab with one workgroup: it merges its slot and the window chunks'
   // slots (all written by its own waves) into out itself, and no combine
   // launch follows.  With more, the combine kernel merges the slots.
-  if (BITS == 4 || n_groups > 1) return;
+  if (n_groups > 1) return;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's slot stores are done
   __syncthreads();
   const int S = n_groups + n_window;   // slots of this slab; a.S_total is their stride
@@ -1604,20 +1626,20 @@ bool decode_matrix_supported(const DecodeArgs &a) {
 
 bool decode_matrix4_supported(const DecodeArgs &a) {
   // records of the 4-bit / G 32 / head_dim 128 shape (fp32 or fp16 scales)
-  // in a contiguous cache; q copied 16 bytes at a time
+  // in a contiguous cache, copied 16 bytes at a time like the window rows
+  // and q
   return a.kb == 4 && a.vb == 4 && a.G == kG && a.D == kD &&
          (a.n_rep == 1 || a.n_rep == 2 || a.n_rep == 4) && a.L.pt == nullptr &&
          (layout_is<false, 4>(a.L) || layout_is<true, 4>(a.L)) &&
-         ((uintptr_t)a.L.blocks & 15) == 0 && ((uintptr_t)a.q & 15) == 0;
+         ((uintptr_t)a.L.blocks & 15) == 0 && ((uintptr_t)a.k_res & 15) == 0 &&
+         ((uintptr_t)a.v_res & 15) == 0 && ((uintptr_t)a.q & 15) == 0;
 }
-
-int decode_matrix4_waves(const DecodeArgs &a) { return a.mask ? 4 : 6; }
 
 int decode_matrix_window_chunks(const DecodeArgs &a, int64_t n_main) {
   return matrix_window_chunks(a.t, n_main);
 }
 
-int decode_matrix_waves(const DecodeArgs &a) { return a.mask ? 4 : 8; }
+int decode_matrix_waves(const DecodeArgs &a) { return a.mask ? 4 : (a.kb == 4 ? 6 : 8); }
 
 template <int NREP, bool RAGGED, bool PAGED, bool S16, int MODE = 0>
 static void launch_rep(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
@@ -1647,6 +1669,29 @@ static void launch_layout(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t
   }
 }
 
+// 4-bit codes: a uniform batch in a contiguous cache, attention (and the
+// fused step) only.
+template <int NREP, bool S16>
+static void launch_rep4(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
+                        int n_groups, int n_window) {
+  if (a.mask)
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, true, false, false, S16, 0, 4>), grid,
+                       dim3(256), 0, s, a, n_main, n_groups, n_window, NoRows{});
+  else
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, false, false, false, S16, 0, 4>), grid,
+                       dim3(384), 0, s, a, n_main, n_groups, n_window, NoRows{});
+}
+
+template <bool S16>
+static void launch_reps4(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
+                         int n_groups, int n_window) {
+  switch (a.n_rep) {
+    case 1: launch_rep4<1, S16>(a, grid, s, n_main, n_groups, n_window); break;
+    case 2: launch_rep4<2, S16>(a, grid, s, n_main, n_groups, n_window); break;
+    default: launch_rep4<4, S16>(a, grid, s, n_main, n_groups, n_window); break;
+  }
+}
+
 template <bool RAGGED, int MODE = 0>
 static void launch_reps(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
                         int n_groups, int n_window, const MatrixRowArg<RAGGED> &rows) {
@@ -1666,7 +1711,8 @@ static void launch_reps(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n
 
 hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int n_groups,
                                 hipStream_t s) {
-  if (!decode_matrix_supported(a) || a.t <= 0 || n_main < 0 || n_main % kBT != 0 ||
+  const bool four = decode_matrix4_supported(a);
+  if (!(four || decode_matrix_supported(a)) || a.t <= 0 || n_main < 0 || n_main % kBT != 0 ||
       n_main > a.n_vq || n_groups <= 0)
     return hipErrorInvalidValue;
   // the window role's key staging assumes whole key groups below n_kq
@@ -1684,45 +1730,12 @@ hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int n_group
   if ((int64_t)n_groups + n_window > a.S_total) return hipErrorInvalidValue;
   const int64_t n_wg = (int64_t)n_groups * a.H * a.B;
   if (n_wg > ((int64_t)1 << 25)) return hipErrorInvalidValue;   // 32-bit workgroup ids
-  launch_reps<false>(a, dim3((unsigned)n_wg), s, n_main, n_groups, n_window, NoRows{});
-  return hipGetLastError();
-}
-
-// 4-bit codes: the blocks of tokens [0, n_main) only, partial slots [0,
-// n_groups) of each query head; the caller covers [n_main, t) and merges.
-template <int NREP, bool S16>
-static void launch_rep4(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
-                        int n_groups) {
-  if (a.mask)
-    hipLaunchKernelGGL((decode_matrix_kernel<NREP, true, false, false, S16, 0, 4>), grid,
-                       dim3(256), 0, s, a, n_main, n_groups, 0, NoRows{});
+  if (four && a.L.sb == 2)
+    launch_reps4<true>(a, dim3((unsigned)n_wg), s, n_main, n_groups, n_window);
+  else if (four)
+    launch_reps4<false>(a, dim3((unsigned)n_wg), s, n_main, n_groups, n_window);
   else
-    hipLaunchKernelGGL((decode_matrix_kernel<NREP, false, false, false, S16, 0, 4>), grid,
-                       dim3(384), 0, s, a, n_main, n_groups, 0, NoRows{});
-}
-
-template <bool S16>
-static void launch_reps4(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
-                         int n_groups) {
-  switch (a.n_rep) {
-    case 1: launch_rep4<1, S16>(a, grid, s, n_main, n_groups); break;
-    case 2: launch_rep4<2, S16>(a, grid, s, n_main, n_groups); break;
-    default: launch_rep4<4, S16>(a, grid, s, n_main, n_groups); break;
-  }
-}
-
-hipError_t launch_decode_matrix4(const DecodeArgs &a, int64_t n_main, int n_groups,
-                                 hipStream_t s) {
-  if (!decode_matrix4_supported(a) || a.t <= 0 || a.t_new >= 0 || n_main < kBT ||
-      n_main % kBT != 0 || n_main > a.n_vq || n_main > a.n_kq || n_groups <= 0 ||
-      n_groups > a.S_total)
-    return hipErrorInvalidValue;
-  const int64_t n_wg = (int64_t)n_groups * a.H * a.B;
-  if (n_wg > ((int64_t)1 << 25)) return hipErrorInvalidValue;   // 32-bit workgroup ids
-  if (a.L.sb == 2)
-    launch_reps4<true>(a, dim3((unsigned)n_wg), s, n_main, n_groups);
-  else
-    launch_reps4<false>(a, dim3((unsigned)n_wg), s, n_main, n_groups);
+    launch_reps<false>(a, dim3((unsigned)n_wg), s, n_main, n_groups, n_window, NoRows{});
   return hipGetLastError();
 }
 

@@ -138,7 +138,7 @@ template <int KB, int VB, int NH, bool RAGGED, int MODE, bool PAGED, bool S16>
 __global__ void __launch_bounds__(kVThreads)
     __attribute__((amdgpu_waves_per_eu(2)))   // two waves per SIMD: the compiler may use 256 VGPRs
 decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int direct,
-                     RowArg<RAGGED> rows, int tok_begin, int slot_base) {
+                     RowArg<RAGGED> rows) {
   constexpr bool SCORES = MODE == 1, SELECTED = MODE == 2;
   __shared__ float red_s[kVWaves][NH][kVD];
   __shared__ float stat_s[kVWaves][NH][2];
@@ -166,7 +166,7 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
     rs = row_span(rows.n[b], a.R, false);
   else
     rs = RowSpan{a.t, a.n_kq, a.n_vq, -1};
-  const int s0 = tok_begin + split * tokens_per_split;
+  const int s0 = split * tokens_per_split;
   const int s1 = (int)min((int64_t)s0 + tokens_per_split, rs.t);
   const int g_end = (s1 + kVG - 1) / kVG;
   const int t_all = (int)rs.t, n_kq = (int)rs.n_kq, n_vq = (int)rs.n_vq, R = a.R;
@@ -538,8 +538,7 @@ decode_vector_kernel(DecodeArgs a, int tokens_per_split, int head_chunks, int di
       a.out[((int64_t)b * a.Hq + hq0 + j) * kVD + c] = o * (L > 0.0f ? 1.0f / L : 0.0f);
     } else {
       float *dst =
-          a.part + (((int64_t)b * a.Hq + hq0 + j) * a.S_total + slot_base + split) *
-                       (int64_t)(kVD + 4);
+          a.part + (((int64_t)b * a.Hq + hq0 + j) * a.S_total + split) * (int64_t)(kVD + 4);
       dst[c] = o;
       if (c == 0) {
         dst[kVD] = M;
@@ -566,43 +565,43 @@ bool decode_vector_supported(const DecodeArgs &a) {
 // workgroup would not fit two waves per SIMD).
 template <int KB, int VB, bool RAGGED, int MODE, bool PAGED, bool S16>
 static void launch_bits(const DecodeArgs &a, dim3 grid, int tps, int direct, hipStream_t s,
-                        const RowArg<RAGGED> &rows, int tb, int sb) {
+                        const RowArg<RAGGED> &rows) {
   if (a.n_rep == 1) {
     hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 1, RAGGED, MODE, PAGED, S16>), grid, dim3(kVThreads),
-                       0, s, a, tps, 1, direct, rows, tb, sb);
+                       0, s, a, tps, 1, direct, rows);
   } else {
     if constexpr (MODE == 1) {
       // scores only: no value accumulators, so one workgroup takes every
       // head of the KV head and reads its keys once
       if (a.n_rep == 4) {
         hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 4, RAGGED, MODE, PAGED, S16>), grid,
-                           dim3(kVThreads), 0, s, a, tps, 1, direct, rows, tb, sb);
+                           dim3(kVThreads), 0, s, a, tps, 1, direct, rows);
         return;
       }
       if (a.n_rep == 8) {
         hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 8, RAGGED, MODE, PAGED, S16>), grid,
-                           dim3(kVThreads), 0, s, a, tps, 1, direct, rows, tb, sb);
+                           dim3(kVThreads), 0, s, a, tps, 1, direct, rows);
         return;
       }
     }
     const int chunks = a.n_rep / 2;
     grid.y *= chunks;
     hipLaunchKernelGGL((decode_vector_kernel<KB, VB, 2, RAGGED, MODE, PAGED, S16>), grid, dim3(kVThreads),
-                       0, s, a, tps, chunks, direct, rows, tb, sb);
+                       0, s, a, tps, chunks, direct, rows);
   }
 }
 
 template <bool RAGGED, int MODE, bool PAGED, bool S16>
 static void launch_bits_layout(const DecodeArgs &a, dim3 grid, int tps, int direct, hipStream_t s,
-                               const RowArg<RAGGED> &rows, int tb, int sb) {
+                               const RowArg<RAGGED> &rows) {
   if (a.kb == 2 && a.vb == 2)
-    launch_bits<2, 2, RAGGED, MODE, PAGED, S16>(a, grid, tps, direct, s, rows, tb, sb);
+    launch_bits<2, 2, RAGGED, MODE, PAGED, S16>(a, grid, tps, direct, s, rows);
   else if (a.kb == 2)
-    launch_bits<2, 4, RAGGED, MODE, PAGED, S16>(a, grid, tps, direct, s, rows, tb, sb);
+    launch_bits<2, 4, RAGGED, MODE, PAGED, S16>(a, grid, tps, direct, s, rows);
   else if (a.vb == 2)
-    launch_bits<4, 2, RAGGED, MODE, PAGED, S16>(a, grid, tps, direct, s, rows, tb, sb);
+    launch_bits<4, 2, RAGGED, MODE, PAGED, S16>(a, grid, tps, direct, s, rows);
   else
-    launch_bits<4, 4, RAGGED, MODE, PAGED, S16>(a, grid, tps, direct, s, rows, tb, sb);
+    launch_bits<4, 4, RAGGED, MODE, PAGED, S16>(a, grid, tps, direct, s, rows);
 }
 
 // A paged cache (PAGED) and the fp16-scale layout (S16) take their own
@@ -610,18 +609,18 @@ static void launch_bits_layout(const DecodeArgs &a, dim3 grid, int tps, int dire
 // registers and schedule.
 template <bool RAGGED, int MODE>
 static void launch_all_bits(const DecodeArgs &a, dim3 grid, int tps, int direct, hipStream_t s,
-                            const RowArg<RAGGED> &rows, int tb = 0, int sb = 0) {
+                            const RowArg<RAGGED> &rows) {
   const bool s16 = a.L.sb == 2;
   if (a.L.pt) {
     if (s16)
-      launch_bits_layout<RAGGED, MODE, true, true>(a, grid, tps, direct, s, rows, tb, sb);
+      launch_bits_layout<RAGGED, MODE, true, true>(a, grid, tps, direct, s, rows);
     else
-      launch_bits_layout<RAGGED, MODE, true, false>(a, grid, tps, direct, s, rows, tb, sb);
+      launch_bits_layout<RAGGED, MODE, true, false>(a, grid, tps, direct, s, rows);
   } else {
     if (s16)
-      launch_bits_layout<RAGGED, MODE, false, true>(a, grid, tps, direct, s, rows, tb, sb);
+      launch_bits_layout<RAGGED, MODE, false, true>(a, grid, tps, direct, s, rows);
     else
-      launch_bits_layout<RAGGED, MODE, false, false>(a, grid, tps, direct, s, rows, tb, sb);
+      launch_bits_layout<RAGGED, MODE, false, false>(a, grid, tps, direct, s, rows);
   }
 }
 
@@ -639,18 +638,6 @@ hipError_t launch_decode_vector(const DecodeArgs &a, int tokens_per_split, int n
     launch_all_bits<true, 0>(a, grid, tokens_per_split, direct, s, *rows);
   else
     launch_all_bits<false, 0>(a, grid, tokens_per_split, direct, s, NoRows{});
-  return hipGetLastError();
-}
-
-hipError_t launch_decode_vector_range(const DecodeArgs &a, int64_t tok_begin,
-                                     int tokens_per_split, int n_splits, int slot_base,
-                                     hipStream_t s) {
-  if (n_splits <= 0) return hipSuccess;
-  if (!decode_vector_supported(a) || tokens_per_split % kVG != 0 || tok_begin % kVG != 0 ||
-      tok_begin < 0 || tok_begin >= a.t || slot_base < 0 || slot_base + n_splits > a.S_total)
-    return hipErrorInvalidValue;
-  const dim3 grid((unsigned)n_splits, (unsigned)a.H, (unsigned)a.B);
-  launch_all_bits<false, 0>(a, grid, tokens_per_split, 0, s, NoRows{}, (int)tok_begin, slot_base);
   return hipGetLastError();
 }
 

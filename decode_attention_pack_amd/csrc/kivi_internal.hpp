@@ -116,12 +116,6 @@ hipError_t launch_decode_generic(const DecodeArgs &a, int64_t tok_begin, int tok
 bool decode_vector_supported(const DecodeArgs &a);
 hipError_t launch_decode_vector(const DecodeArgs &a, int tokens_per_split, int n_splits,
                                 hipStream_t s, const RowCounts *rows = nullptr);
-// Tokens [tok_begin, t) only (tok_begin a multiple of 32), in n_splits splits
-// of tokens_per_split tokens written to partial slots slot_base + split; a
-// uniform batch, always merged by the caller.
-hipError_t launch_decode_vector_range(const DecodeArgs &a, int64_t tok_begin,
-                                      int tokens_per_split, int n_splits, int slot_base,
-                                      hipStream_t s);
 
 bool decode_matrix_supported(const DecodeArgs &a);
 // Tokens [0, n_main) of a row go to the matrix kernel's block role: whole
@@ -144,15 +138,10 @@ int decode_matrix_window_chunks(const DecodeArgs &a, int64_t n_main);
 int decode_matrix_waves(const DecodeArgs &a);
 hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int n_groups,
                                 hipStream_t s);
-// 4-bit keys and values (G = 32, D = 128, 1, 2 or 4 query heads per KV head,
-// contiguous cache, no fused step): n_groups workgroups per slab of
-// decode_matrix4_waves waves over the blocks of [0, n_main) only, into
-// partial slots [0, n_groups); the caller covers [n_main, t) in other slots
-// and always merges.  n_main is a positive multiple of 128, at most n_vq.
+// launch_decode_matrix also takes 4-bit keys and values (G = 32, D = 128, 1,
+// 2 or 4 query heads per KV head) of a uniform batch in a contiguous cache,
+// attention and the fused step: decode_matrix4_supported.
 bool decode_matrix4_supported(const DecodeArgs &a);
-int decode_matrix4_waves(const DecodeArgs &a);
-hipError_t launch_decode_matrix4(const DecodeArgs &a, int64_t n_main, int n_groups,
-                                 hipStream_t s);
 // Ragged batch: row b attends over t[b] tokens (after the append of a
 // fused step); per KV head, share u of n_shares is workgroup
 // share[u] >> 8 & 4095 of the share[u] >> 20 workgroups of row share[u] &

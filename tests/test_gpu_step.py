@@ -91,16 +91,35 @@ def test_decode_step_matches_oracle(rep, R, T0, n_steps):
     _steps(rep, R, T0, n_steps, masked=False)
 
 
-@pytest.mark.parametrize("rep,R,bits", [(4, 32, 2), (1, 64, 2), (1, 64, 4)])
+@pytest.mark.parametrize("rep,R,bits", [(4, 32, 2), (1, 64, 2), (1, 64, 4), (4, 64, 4)])
 def test_decode_step_signed_zeros(rep, R, bits):
     """Groups whose minimum is a +0.0 / -0.0 tie, quantized by the prefill and
-    by the steps -- inside the fused launch at 2 bits (popped values,
-    completed key blocks), by kivi_append at 4 bits: bit for bit."""
+    by the steps -- inside the fused launch at 2 bits and at 4 bits with
+    several query heads per KV head (popped values, completed key blocks), by
+    kivi_append at 4 bits with one on short rows: bit for bit."""
     _steps(rep, R, 40, 3 * R, masked=False, zeros=True, kb=bits, vb=bits)
 
 
 def test_decode_step_masked():
     _steps(4, 128, 250, 12, masked=True)
+
+
+@pytest.mark.parametrize("rep,R,T0,n_steps", [
+    (4, 128, 120, 150),     # first pops, key blocks at 128 and 256
+    (2, 64, 500, 70),
+    (4, 96, 300, 200),      # key blocks and pops off the 128-token block grid
+    (4, 32, 3, 80),         # short window: many pops and key blocks
+    (1, 128, 2600, 40),     # one query head per KV head, long enough rows
+])
+def test_decode_step_4bit_matches_oracle(rep, R, T0, n_steps):
+    """4-bit keys and values: the step fused into the matrix launch, whose
+    window role quantizes the popped values and the completed key blocks to
+    4-bit codes; outputs within tolerance, packed stores bit for bit."""
+    _steps(rep, R, T0, n_steps, masked=False, kb=4, vb=4)
+
+
+def test_decode_step_4bit_masked():
+    _steps(4, 128, 250, 12, masked=True, kb=4, vb=4)
 
 
 @pytest.mark.parametrize("kb,vb,rep", [(4, 4, 1), (2, 2, 8)])
@@ -109,16 +128,17 @@ def test_decode_step_other_shapes(kb, vb, rep):
     _steps(rep, 64, 100, 20, masked=False, kb=kb, vb=vb)
 
 
-def test_decode_step_equals_append_then_attend():
+@pytest.mark.parametrize("bits", [2, 4])
+def test_decode_step_equals_append_then_attend(bits):
     """Fused and unfused steps leave bit-identical caches and outputs within
     rounding-order differences."""
-    rng = np.random.default_rng(11)
+    rng = np.random.default_rng(11 + bits)
     B, H, D, R, rep, T0, n = 2, 4, 128, 128, 4, 1000, 140
     cap = cap_for(T0 + n, R)
     K = rng.standard_normal((B, H, T0 + n, D)).astype(np.float16)
     V = rng.standard_normal((B, H, T0 + n, D)).astype(np.float16)
-    a = kivi.Cache(B, H, D, 2, 2, 32, R, cap)
-    u = kivi.Cache(B, H, D, 2, 2, 32, R, cap)
+    a = kivi.Cache(B, H, D, bits, bits, 32, R, cap)
+    u = kivi.Cache(B, H, D, bits, bits, 32, R, cap)
     for c in (a, u):
         kivi.kivi_append(c, dev(K[:, :, :T0]), dev(V[:, :, :T0]))
     for i in range(n):
