@@ -319,7 +319,7 @@ int make_plan(const kivi_cache *c, int32_t Hq, int32_t tps_req, int32_t path,
     if (tps_req == 0) {
       // one workgroup per CU (two for the four-wave masked variant of 2-bit
       // codes), no more than the blocks and window chunks keep busy
-      const int64_t per_cu = a.kb == 4 ? 1 : 8 / waves;
+      const int64_t per_cu = a.kb == 4 || a.vb == 4 ? 1 : 8 / waves;
       const int64_t target = max64(1, device_cus() * per_cu / units);
       groups = std::min(target, max64(1, ceil_div(blocks + p.n_window, waves)));
     } else {

@@ -67,24 +67,25 @@ constexpr int kD = 128;
 constexpr int kG = 32;
 constexpr int kBT = 128;       // tokens per block (block role)
 constexpr int kWT = 32;        // tokens per chunk (window role)
-// A record of the packed store at this shape (BITS-bit keys and values, G
+// A record of the packed store at this shape (KB-bit keys, VB-bit values, G
 // 32, head_dim 128): byte offsets of its sections and its size, with fp32
 // scales or (S16) fp16 scales; and the DMA instructions that copy the key or
 // the value part of a block (codes 4 or 8 KB, scales 2 or 1 KB, zeros 1 KB).
-template <bool S16, int BITS = 2>
+template <bool S16, int KB = 2, int VB = KB>
 struct Rec {
-  static_assert(BITS == 2 || BITS == 4, "2- or 4-bit codes");
-  static constexpr int code_bytes = 2048 * BITS;   // 128 tokens x 128 channels
+  static_assert((KB == 2 || KB == 4) && (VB == 2 || VB == 4), "2- or 4-bit codes");
   static constexpr int scale_bytes = S16 ? 1024 : 2048;
-  static constexpr int kc = 0, ks = code_bytes;
+  static constexpr int kc = 0, ks = 2048 * KB;   // codes: 128 tokens x 128 channels
   static constexpr int kz = ks + scale_bytes;
   static constexpr int vc = kz + 1024;
-  static constexpr int vs = vc + code_bytes;
+  static constexpr int vs = vc + 2048 * VB;
   static constexpr int vz = vs + scale_bytes;
   static constexpr int bytes = vz + 1024;
   static constexpr int sb = S16 ? 2 : 4;    // bytes per scale
-  static constexpr int ncode = code_bytes / 1024;   // DMA instructions of the codes
-  static constexpr int dma = ncode + scale_bytes / 1024 + 1;
+  // DMA instructions of the key and value codes, and of the key and value parts
+  static constexpr int kncode = 2 * KB, vncode = 2 * VB;
+  static constexpr int kdma = kncode + scale_bytes / 1024 + 1;
+  static constexpr int vdma = vncode + scale_bytes / 1024 + 1;
 };
 constexpr int kPRow = 132;     // floats per probability row in LDS (16-byte pad)
 
@@ -234,29 +235,28 @@ struct DmaOffsets {
 // part, counted from the start of the record (section offset included), so
 // that all copies of a part share one scalar base address -- the record --
 // and no per-copy address arithmetic runs.  Set once per wave.
-template <bool S16, int BITS = 2>
+template <bool S16, int KB = 2, int VB = KB>
 struct PartOffsets {
-  using RC = Rec<S16, BITS>;
-  static constexpr int N = RC::dma, NC = RC::ncode;
-  uint32_t k[N], v[N];
+  using RC = Rec<S16, KB, VB>;
+  static constexpr int NK = RC::kdma, NV = RC::vdma, NCK = RC::kncode, NCV = RC::vncode;
+  uint32_t k[NK], v[NV];
   __device__ explicit PartOffsets(const DmaOffsets &o) {
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      k[i] = RC::kc + i * 1024 + o.lin;
-      v[i] = RC::vc + i * 1024 + o.lin;
-    }
+    for (int i = 0; i < NCK; ++i) k[i] = RC::kc + i * 1024 + o.lin;
+#pragma unroll
+    for (int i = 0; i < NCV; ++i) v[i] = RC::vc + i * 1024 + o.lin;
     if constexpr (S16) {
-      k[NC] = RC::ks + o.zrot;
-      v[NC] = RC::vs + o.zrot;
+      k[NCK] = RC::ks + o.zrot;
+      v[NCV] = RC::vs + o.zrot;
     } else {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        k[NC + i] = RC::ks + i * 1024 + o.rot[i];
-        v[NC + i] = RC::vs + i * 1024 + o.rot[i];
+        k[NCK + i] = RC::ks + i * 1024 + o.rot[i];
+        v[NCV + i] = RC::vs + i * 1024 + o.rot[i];
       }
     }
-    k[N - 1] = RC::kz + o.zrot;
-    v[N - 1] = RC::vz + o.zrot;
+    k[NK - 1] = RC::kz + o.zrot;
+    v[NV - 1] = RC::vz + o.zrot;
   }
 };
 
@@ -264,9 +264,9 @@ struct PartOffsets {
 // A paged cache (PAGED) finds it through the page table: record h of page
 // pt[b nrec + blk], the page index clamped into the pool.  The paged form is
 // a separate instantiation so that the contiguous one keeps its registers.
-template <bool PAGED, bool S16, int BITS = 2>
+template <bool PAGED, bool S16, int KB = 2, int VB = KB>
 __device__ __forceinline__ const uint8_t *record_of(const DecodeArgs &a, int64_t bh, int64_t blk) {
-  constexpr int64_t RB = Rec<S16, BITS>::bytes;
+  constexpr int64_t RB = Rec<S16, KB, VB>::bytes;
   if constexpr (!PAGED) {
     return a.L.blocks + (bh * a.L.nrec + blk) * RB;
   } else {
@@ -278,15 +278,15 @@ __device__ __forceinline__ const uint8_t *record_of(const DecodeArgs &a, int64_t
 }
 
 // Key part of block `blk` (tokens [128 blk, 128 blk + 128)) of slab bh:
-// Rec<S16, BITS>::dma DMA instructions, plus 2 for the mask when there is one.
-// s, mask_s: LDS byte addresses of the wave's KStageT and mask buffer.
-template <bool MASKED, bool PAGED, bool S16, int BITS = 2>
+// Rec<S16, KB, VB>::kdma DMA instructions, plus 2 for the mask when there is
+// one.  s, mask_s: LDS byte addresses of the wave's KStageT and mask buffer.
+template <bool MASKED, bool PAGED, bool S16, int KB = 2, int VB = KB>
 __device__ __forceinline__ void stage_keys(const DecodeArgs &a, int64_t bh, int64_t blk,
                                            uint32_t s, uint32_t mask_s,
-                                           const PartOffsets<S16, BITS> &o, int lane) {
-  using KS = KStageT<BITS>;
-  constexpr int NC = PartOffsets<S16, BITS>::NC;
-  const void *rec = uniform_ptr(record_of<PAGED, S16, BITS>(a, bh, blk));
+                                           const PartOffsets<S16, KB, VB> &o, int lane) {
+  using KS = KStageT<KB>;
+  constexpr int NC = PartOffsets<S16, KB, VB>::NCK;
+  const void *rec = uniform_ptr(record_of<PAGED, S16, KB, VB>(a, bh, blk));
   constexpr uint32_t kc = offsetof(KS, kc), ks = offsetof(KS, ks), kz = offsetof(KS, kz);
 #pragma unroll
   for (int i = 0; i < NC; ++i) dma16nt_m0(rec, o.k[i], s + kc + i * 1024);
@@ -296,7 +296,7 @@ __device__ __forceinline__ void stage_keys(const DecodeArgs &a, int64_t bh, int6
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16nt_m0(rec, o.k[NC + i], s + ks + i * 1024);
   }
-  dma16nt_m0(rec, o.k[PartOffsets<S16, BITS>::N - 1], s + kz);
+  dma16nt_m0(rec, o.k[PartOffsets<S16, KB, VB>::NK - 1], s + kz);
   if (MASKED) {
     // dword copies: a mask row need not be 16-byte aligned
     const float *m = a.mask + (bh / a.H) * a.t + blk * kBT;
@@ -305,14 +305,14 @@ __device__ __forceinline__ void stage_keys(const DecodeArgs &a, int64_t bh, int6
   }
 }
 
-// Value part of block `blk`: Rec<S16, BITS>::dma DMA instructions.
+// Value part of block `blk`: Rec<S16, KB, VB>::vdma DMA instructions.
 // s: LDS byte address of the wave's VStageT.
-template <bool PAGED, bool S16, int BITS = 2>
+template <bool PAGED, bool S16, int KB = 2, int VB = KB>
 __device__ __forceinline__ void stage_values(const DecodeArgs &a, int64_t bh, int64_t blk,
-                                             uint32_t s, const PartOffsets<S16, BITS> &o) {
-  using VS = VStageT<BITS>;
-  constexpr int NC = PartOffsets<S16, BITS>::NC;
-  const void *rec = uniform_ptr(record_of<PAGED, S16, BITS>(a, bh, blk));
+                                             uint32_t s, const PartOffsets<S16, KB, VB> &o) {
+  using VS = VStageT<VB>;
+  constexpr int NC = PartOffsets<S16, KB, VB>::NCV;
+  const void *rec = uniform_ptr(record_of<PAGED, S16, KB, VB>(a, bh, blk));
   constexpr uint32_t vc = offsetof(VS, vc), vs = offsetof(VS, vs), vz = offsetof(VS, vz);
 #pragma unroll
   for (int i = 0; i < NC; ++i) dma16nt_m0(rec, o.v[i], s + vc + i * 1024);
@@ -322,7 +322,7 @@ __device__ __forceinline__ void stage_values(const DecodeArgs &a, int64_t bh, in
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16nt_m0(rec, o.v[NC + i], s + vs + i * 1024);
   }
-  dma16nt_m0(rec, o.v[PartOffsets<S16, BITS>::N - 1], s + vz);
+  dma16nt_m0(rec, o.v[PartOffsets<S16, KB, VB>::NV - 1], s + vz);
 }
 
 // Selected attention (mode 2): the stored scores of block `blk` for the
@@ -518,27 +518,27 @@ struct BlockShare {
 // stored scores (copied into the key buffer), -inf for the tokens the row's
 // selection rule (a.sel) does not take; then the softmax and values as in
 // MODE 0.  The mask is part of the stored scores.
-// BITS 4 (4-bit keys and values, attention only): a transposed read holds one
-// code per nibble, so a key tile of 16 columns is 16 consecutive tokens (2-bit:
-// 16 token pairs, split into even and odd tiles) and a value tile 16
+// KB / VB 4 (4-bit keys / values, attention only): a transposed read holds
+// one code per nibble, so a key tile of 16 columns is 16 consecutive tokens
+// (2-bit: 16 token pairs, split into even and odd tiles) and a value tile 16
 // consecutive channels.  Index e of the score and accumulator pairs below is
-// then that half of the key group or of the channel group instead of the token
-// or channel parity.
-template <int NREP, bool MASKED, bool PAGED, bool S16, int MODE, int BITS = 2>
+// then that half of the key group or of the channel group instead of the
+// token or channel parity.
+template <int NREP, bool MASKED, bool PAGED, bool S16, int MODE, int KB = 2, int VB = KB>
 __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare &sh,
                                            int64_t first, int hk, int b, const Lds &L,
-                                           KStageT<BITS> *__restrict__ kbuf,
-                                           VStageT<BITS> *__restrict__ vbuf) {
+                                           KStageT<KB> *__restrict__ kbuf,
+                                           VStageT<VB> *__restrict__ vbuf) {
   static_assert(NREP == 1 || NREP == 2 || NREP == 4, "query heads per KV head");
   static_assert(MODE != 2 || !MASKED, "selected attention takes the mask from the scores");
-  static_assert(BITS == 2 || MODE == 0, "4-bit codes: attention only");
+  static_assert((KB == 2 && VB == 2) || MODE == 0, "4-bit codes: attention only");
   constexpr int GA = 16 / NREP;       // key groups per A operand
-  constexpr int SD = Rec<S16, BITS>::dma;
+  using RC = Rec<S16, KB, VB>;
   // token of score pair element e of key group g held by lane i
-  auto tok = [](int g, int e, int i) { return BITS == 2 ? 32 * g + 2 * i + e : 32 * g + 16 * e + i; };
+  auto tok = [](int g, int e, int i) { return KB == 2 ? 32 * g + 2 * i + e : 32 * g + 16 * e + i; };
   // copies of a block's key part (MODE 2: its scores) and value part
-  constexpr int KDMA = MODE == 2 ? kScoreDma<NREP> : SD + (MASKED ? 2 : 0);
-  constexpr int VDMA = MODE == 1 ? 0 : SD;
+  constexpr int KDMA = MODE == 2 ? kScoreDma<NREP> : RC::kdma + (MASKED ? 2 : 0);
+  constexpr int VDMA = MODE == 1 ? 0 : RC::vdma;
 
   const int lane = threadIdx.x & 63;
   const int i = lane & 15;
@@ -571,7 +571,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
   // copies; the copies complete in order, so waiting for q alone lets the
   // block stream in meanwhile.  Lanes past the q rows re-read the last 16
   // bytes.
-  const PartOffsets<S16, BITS> dmo{DmaOffsets(lane)};
+  const PartOffsets<S16, KB, VB> dmo{DmaOffsets(lane)};
   const uint16_t *q_lds = (const uint16_t *)&L.p[0][0];
   int64_t cur = sh.block((int)first);   // the block being processed
   if constexpr (MODE != 2)
@@ -580,9 +580,9 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
   if constexpr (MODE == 2) {
     stage_scores<NREP>(a, b, hk, cur, k_lds, lane);
   } else {
-    stage_keys<MASKED, PAGED, S16, BITS>(a, bh, cur, k_lds, mask_lds, dmo, lane);
+    stage_keys<MASKED, PAGED, S16, KB, VB>(a, bh, cur, k_lds, mask_lds, dmo, lane);
   }
-  if constexpr (MODE != 1) stage_values<PAGED, S16, BITS>(a, bh, cur, v_lds, dmo);
+  if constexpr (MODE != 1) stage_values<PAGED, S16, KB, VB>(a, bh, cur, v_lds, dmo);
   if constexpr (MODE != 2) wait_vm<KDMA + VDMA>();   // q
   // the row's selection rule for the scores this lane holds (head h_s)
   SelectRow selr{};
@@ -684,15 +684,15 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
     } else {
     if constexpr (MODE == 1) store_prev();
     // ================= key half =================
-    const KStageT<BITS> &kst = *kbuf;
+    const KStageT<KB> &kst = *kbuf;
     // 2-bit: [group g][64-channel half rho]; 4-bit: [g][rho][16-token half u]
-    constexpr int NXK = BITS == 2 ? 8 : 16;
+    constexpr int NXK = KB == 2 ? 8 : 16;
     i2 xk[NXK];
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int rho = 0; rho < 2; ++rho) {
-        if constexpr (BITS == 2) {
+        if constexpr (KB == 2) {
           xk[2 * g + rho] = tr4(kst.kc + g * 256 + (64 * rho + 16 * kg + i) * 2);
         } else {
 #pragma unroll
@@ -705,7 +705,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       if (MASKED) {
-        if constexpr (BITS == 2) {
+        if constexpr (KB == 2) {
           const float2 m2 = *(const float2 *)(L.mask + 32 * g + 2 * i);
           mk[g][0] = m2.x * kMaskUnit;
           mk[g][1] = m2.y * kMaskUnit;
@@ -729,7 +729,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
         // element j of the operands holds channel c0 + k_order(j)
-        const int j0 = k_order<BITS>(j), j1 = k_order<BITS>(j + 1);
+        const int j0 = k_order<KB>(j), j1 = k_order<KB>(j + 1);
         split_mul2(qa[ks][j0], sv[j0], qa[ks][j1], sv[j1], ah[ks], al[ks], j);
         bz = fmaf(qa[ks][j], (float)zv[j], bz);
         bz = fmaf(qa[ks][j + 1], (float)zv[j + 1], bz);
@@ -738,7 +738,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
     // every read of the key part has completed: request the next one
     wait_regs(xk);
     if constexpr (has_next)
-      stage_keys<MASKED, PAGED, S16, BITS>(a, bh, nxt, k_lds, mask_lds, dmo, lane);
+      stage_keys<MASKED, PAGED, S16, KB, VB>(a, bh, nxt, k_lds, mask_lds, dmo, lane);
 
     bz = group_sum(bz);
     if (kg == 0) L.bias[i] = bz;
@@ -749,7 +749,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
       dk[g][0] = dk[g][1] = (f4){0, 0, 0, 0};
 #pragma unroll
       for (int rho = 0; rho < 2; ++rho) {
-        if constexpr (BITS == 2) {
+        if constexpr (KB == 2) {
           const i2 x = xk[2 * g + rho];
 #pragma unroll
           for (int d = 0; d < 2; ++d) {
@@ -814,7 +814,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
         const float p0 = m_new == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s2[g][0] - m_new);
         const float p1 = m_new == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s2[g][1] - m_new);
         lsum += p0 + p1;
-        if constexpr (BITS == 2) {
+        if constexpr (KB == 2) {
           *(float2 *)(&L.p[h_s][32 * g + 2 * i]) = make_float2(p0, p1);
         } else {
           L.p[h_s][tok(g, 0, i)] = p0;
@@ -832,13 +832,13 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
     else
       wait_vm<0>();
     wave_lds_sync();
-    const VStageT<BITS> &vst = *vbuf;
+    const VStageT<VB> &vst = *vbuf;
     // 2-bit: [16-token half u][channel group g]; 4-bit: [u][16-channel unit w]
-    constexpr int NXV = BITS == 2 ? 8 : 16;
+    constexpr int NXV = VB == 2 ? 8 : 16;
     i2 xv[NXV];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      if constexpr (BITS == 2) {
+      if constexpr (VB == 2) {
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           xv[4 * u + g] = tr4(vst.vc + (32 * kg + 16 * u + i) * 8 + g * 2);
@@ -873,7 +873,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
         const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
 #pragma unroll
         for (int j = 0; j < 8; j += 2) {
-          const int j0 = k_order<BITS>(j), j1 = k_order<BITS>(j + 1);
+          const int j0 = k_order<VB>(j), j1 = k_order<VB>(j + 1);
           split_mul2(pv[j0], sv[j0], pv[j1], sv[j1], vh[u][d], vl[u][d], j);
           zt = fmaf(pv[j], (float)zv[j], zt);
           zt = fmaf(pv[j + 1], (float)zv[j + 1], zt);
@@ -882,7 +882,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
     }
     // every read of the value part has completed: request the next one
     wait_regs(xv);
-    if constexpr (has_next) stage_values<PAGED, S16, BITS>(a, bh, nxt, v_lds, dmo);
+    if constexpr (has_next) stage_values<PAGED, S16, KB, VB>(a, bh, nxt, v_lds, dmo);
 
     // dv[g][e]: channels 32 g + 2 j + e (2-bit) or 32 g + 16 e + j (4-bit)
     // of column j
@@ -890,7 +890,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        if constexpr (BITS == 2) {
+        if constexpr (VB == 2) {
           const i2 x = xv[4 * u + g];
 #pragma unroll
           for (int d = 0; d < 2; ++d) {
@@ -947,7 +947,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
     const f4 z4 = *(const f4 *)(L.bias + 4 * kg);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      if constexpr (BITS == 2) {
+      if constexpr (VB == 2) {
         *(float2 *)&L.p[kg][32 * g + 2 * i] =
             make_float2(dv[g][0][g] + z4[g], dv[g][1][g] + z4[g]);
       } else {
@@ -976,7 +976,7 @@ struct WinChunk {
   const uint8_t *rec;
 };
 
-template <bool PAGED, bool S16, int BITS>
+template <bool PAGED, bool S16, int KB, int VB>
 __device__ __forceinline__ WinChunk win_chunk(const DecodeArgs &a, const RowSpan &rs,
                                               int64_t n_main, int chunk, int hk, int b) {
   WinChunk c;
@@ -999,11 +999,11 @@ __device__ __forceinline__ WinChunk win_chunk(const DecodeArgs &a, const RowSpan
   // 16-byte units of scales per channel group (fp32, or fp16 like the zeros)
   c.nqvs = S16 ? c.nqv8 : (c.n_qv + 3) / 4;
   // the chunk lies in one record (Ta is a multiple of 32), at token lt of it
-  c.rec = record_of<PAGED, S16, BITS>(a, c.bh, c.Ta / kBT);
+  c.rec = record_of<PAGED, S16, KB, VB>(a, c.bh, c.Ta / kBT);
   c.lt = (int)(c.Ta % kBT);
-  // value buffer: codes (BITS units per token), scales (4 channel groups x
+  // value buffer: codes (VB units per token), scales (4 channel groups x
   // nqvs units), fp16 zeros (4 x nqv8 units), then fp16 rows (16 units each)
-  c.u_vs = c.n_qv * BITS;
+  c.u_vs = c.n_qv * VB;
   c.u_vz = c.u_vs + 4 * c.nqvs;
   c.u_vrow = c.u_vz + 4 * c.nqv8;
   // Fused decode step: the value that leaves the window with this token
@@ -1025,23 +1025,23 @@ struct WinLoads {
 };
 
 // Units (16 bytes) of a staged key group in the window role's key buffer:
-// codes (32 BITS units: channel c at words BITS c ..), then scales (32 fp32
-// or 16 fp16 units), then zeros (16).
-template <bool S16, int BITS>
+// codes (32 KB units: channel c at words KB c ..), then scales (32 fp32 or
+// 16 fp16 units), then zeros (16).
+template <bool S16, int KB>
 struct WinKeyUnits {
-  static constexpr int scales = 32 * BITS, zeros = scales + (S16 ? 16 : 32), end = zeros + 16;
+  static constexpr int scales = 32 * KB, zeros = scales + (S16 ? 16 : 32), end = zeros + 16;
 };
 
 // The loads of one window chunk, issued and not waited for.  MODE 1 (scores)
 // stages no values; MODE 2 (selected attention) no keys and no q.
-template <int NREP, bool PAGED, bool S16, int MODE, int BITS>
+template <int NREP, bool PAGED, bool S16, int MODE, int KB, int VB>
 __device__ __forceinline__ WinLoads<NREP> window_issue(const DecodeArgs &a, const RowSpan &rs,
                                                        int64_t n_main, int chunk, int hk, int b,
                                                        const Lds &L) {
-  using RC = Rec<S16, BITS>;
-  using KU = WinKeyUnits<S16, BITS>;
+  using RC = Rec<S16, KB, VB>;
+  using KU = WinKeyUnits<S16, KB>;
   const int j = threadIdx.x & 63;
-  const WinChunk c = win_chunk<PAGED, S16, BITS>(a, rs, n_main, chunk, hk, b);
+  const WinChunk c = win_chunk<PAGED, S16, KB, VB>(a, rs, n_main, chunk, hk, b);
   const int64_t bh = c.bh, Ta = c.Ta, vq_end = c.vq_end;
   const int n = c.n, nqvs = c.nqvs, nqv8 = c.nqv8, lt = c.lt;
   const bool kq = c.kq, kq_now = c.kq_now;
@@ -1057,7 +1057,7 @@ __device__ __forceinline__ WinLoads<NREP> window_issue(const DecodeArgs &a, cons
       if (kq && !kq_now) {
         const int lg = lt / kG;    // key group within the record
         if (u < KU::scales)
-          src = rec + RC::kc + lg * (512 * BITS) + u * 16;
+          src = rec + RC::kc + lg * (512 * KB) + u * 16;
         else if (u < KU::zeros)
           src = rec + RC::ks + lg * (kD * RC::sb) + (u - KU::scales) * 16;
         else
@@ -1083,7 +1083,7 @@ __device__ __forceinline__ WinLoads<NREP> window_issue(const DecodeArgs &a, cons
     if (u < vu_end) {
       const void *src;
       if (u < u_vs) {
-        src = rec + RC::vc + (lt + u / BITS) * (16 * BITS) + (u % BITS) * 16;
+        src = rec + RC::vc + (lt + u / VB) * (16 * VB) + (u % VB) * 16;
       } else if (u < u_vz) {
         const int x = u - u_vs;
         src = rec + RC::vs + ((x / nqvs) * kBT + lt) * RC::sb + (x % nqvs) * 16;
@@ -1115,17 +1115,17 @@ __device__ __forceinline__ WinLoads<NREP> window_issue(const DecodeArgs &a, cons
 // units, mask included); nothing else.  MODE 2 (selected attention): the
 // chunk's scores come from a.scores, -inf where the row's selection rule
 // does not take the token.
-template <int NREP, bool MASKED, bool PAGED, bool S16, int MODE, int BITS>
+template <int NREP, bool MASKED, bool PAGED, bool S16, int MODE, int KB, int VB>
 __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &rs, int64_t n_main,
                                             int chunk, int slot, int hk, int b, const Lds &L,
                                             const WinLoads<NREP> &ld) {
-  using RC = Rec<S16, BITS>;
-  using KU = WinKeyUnits<S16, BITS>;
-  constexpr int VW = 4 * BITS;            // code words per value token
-  constexpr int CPW = 32 / BITS;          // codes per word
-  constexpr uint32_t CM = (1u << BITS) - 1u;
+  using RC = Rec<S16, KB, VB>;
+  using KU = WinKeyUnits<S16, KB>;
+  constexpr int VW = 4 * VB;              // code words per value token
+  constexpr int KCPW = 32 / KB, VCPW = 32 / VB;   // codes per word
+  constexpr uint32_t KCM = (1u << KB) - 1u, VCM = (1u << VB) - 1u;
   const int j = threadIdx.x & 63;
-  const WinChunk c = win_chunk<PAGED, S16, BITS>(a, rs, n_main, chunk, hk, b);
+  const WinChunk c = win_chunk<PAGED, S16, KB, VB>(a, rs, n_main, chunk, hk, b);
   const int64_t bh = c.bh, Ta = c.Ta, t_pop = c.t_pop;
   const int n = c.n, n_qv = c.n_qv, nqvs = c.nqvs, nqv8 = c.nqv8;
   const int u_vs = c.u_vs, u_vz = c.u_vz, u_vrow = c.u_vrow;
@@ -1153,11 +1153,11 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
     const float x0 = h2f((uint16_t)(popped & 0xFFFFu)), x1 = h2f((uint16_t)(popped >> 16));
     float mn = first_min(x0, x1), mx = first_max(x0, x1);   // channel 2j comes first
     lanes_first_min_max(mn, mx, j, 16);
-    const float sc = rec_scale<S16>(group_scale(mn, mx, BITS));
-    // lanes of one code word: CPW / 2 (two channels per lane)
-    constexpr int LW = CPW / 2;
-    uint32_t w = (quant_code(x0, mn, sc, BITS) | (quant_code(x1, mn, sc, BITS) << BITS))
-                 << (2 * BITS * (j & (LW - 1)));
+    const float sc = rec_scale<S16>(group_scale(mn, mx, VB));
+    // lanes of one code word: VCPW / 2 (two channels per lane)
+    constexpr int LW = VCPW / 2;
+    uint32_t w = (quant_code(x0, mn, sc, VB) | (quant_code(x1, mn, sc, VB) << VB))
+                 << (2 * VB * (j & (LW - 1)));
 #pragma unroll
     for (int o = 1; o < LW; o <<= 1) w |= __shfl_xor(w, o);
     const int xr = (int)(t_pop - Ta);
@@ -1209,25 +1209,25 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
       mn1 = x1 < mn1 ? x1 : mn1;
       mx1 = x1 > mx1 ? x1 : mx1;
     }
-    const float sc0 = rec_scale<S16>(group_scale(mn0, mx0, BITS));
-    const float sc1 = rec_scale<S16>(group_scale(mn1, mx1, BITS));
-    // channel 2j: words 0 .. BITS - 1; channel 2j + 1: words BITS .. 2 BITS - 1
-    uint32_t cw[2 * BITS];
+    const float sc0 = rec_scale<S16>(group_scale(mn0, mx0, KB));
+    const float sc1 = rec_scale<S16>(group_scale(mn1, mx1, KB));
+    // channel 2j: words 0 .. KB - 1; channel 2j + 1: words KB .. 2 KB - 1
+    uint32_t cw[2 * KB];
 #pragma unroll
-    for (int k = 0; k < 2 * BITS; ++k) cw[k] = 0u;
+    for (int k = 0; k < 2 * KB; ++k) cw[k] = 0u;
     for (int r = 0; r < kWT; ++r) {
       const uint32_t w = row_word(r);
-      const int sh = BITS * (r % CPW), hw = r / CPW;
-      cw[hw] |= quant_code(h2f((uint16_t)(w & 0xFFFFu)), mn0, sc0, BITS) << sh;
-      cw[BITS + hw] |= quant_code(h2f((uint16_t)(w >> 16)), mn1, sc1, BITS) << sh;
+      const int sh = KB * (r % KCPW), hw = r / KCPW;
+      cw[hw] |= quant_code(h2f((uint16_t)(w & 0xFFFFu)), mn0, sc0, KB) << sh;
+      cw[KB + hw] |= quant_code(h2f((uint16_t)(w >> 16)), mn1, sc1, KB) << sh;
     }
     wave_lds_sync();   // every lane's row reads are done before the rows are overwritten
-    // codes: BITS words per channel, channels 2j and 2j + 1 at words 2 BITS j ..
-    uint4 c4[BITS / 2];
+    // codes: KB words per channel, channels 2j and 2j + 1 at words 2 KB j ..
+    uint4 c4[KB / 2];
 #pragma unroll
-    for (int k = 0; k < BITS / 2; ++k) {
+    for (int k = 0; k < KB / 2; ++k) {
       c4[k] = make_uint4(cw[4 * k], cw[4 * k + 1], cw[4 * k + 2], cw[4 * k + 3]);
-      *(uint4 *)((uint32_t *)kl + 2 * BITS * j + 4 * k) = c4[k];
+      *(uint4 *)((uint32_t *)kl + 2 * KB * j + 4 * k) = c4[k];
     }
     const uint32_t z2 = (uint32_t)f2h_bits(mn0) | ((uint32_t)f2h_bits(mn1) << 16);
     const int64_t grp = Ta / kG;
@@ -1242,8 +1242,8 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
     }
     *((uint32_t *)(kl + KU::zeros * 16) + j) = z2;
 #pragma unroll
-    for (int k = 0; k < BITS / 2; ++k)
-      *(uint4 *)((uint32_t *)(recw + RC::kc) + (lg * kD + 2 * j) * BITS + 4 * k) = c4[k];
+    for (int k = 0; k < KB / 2; ++k)
+      *(uint4 *)((uint32_t *)(recw + RC::kc) + (lg * kD + 2 * j) * KB + 4 * k) = c4[k];
     *(uint32_t *)((uint16_t *)(recw + RC::kz) + lg * kD + 2 * j) = z2;
   }
   wave_lds_sync();
@@ -1259,15 +1259,15 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
     // and q are the same for all lanes of a half (broadcasts); channels are
     // summed in increasing order
     if (kq) {
-      const uint32_t *kc = (const uint32_t *)kl;   // channel c: words BITS c ..
+      const uint32_t *kc = (const uint32_t *)kl;   // channel c: words KB c ..
       const char *ks = kl + KU::scales * 16;
       const uint16_t *kz = (const uint16_t *)(kl + KU::zeros * 16);
-      const int sh = BITS * (tj % CPW);
+      const int sh = KB * (tj % KCPW);
       const bool hi = tj >= 16;
 #pragma unroll 4
       for (int c = 64 * hf; c < 64 * hf + 64; c += 4) {
         uint32_t cw[4];
-        if constexpr (BITS == 2) {
+        if constexpr (KB == 2) {
           const uint4 wa = *(const uint4 *)(kc + 2 * c);
           const uint4 wb = *(const uint4 *)(kc + 2 * c + 4);
           cw[0] = hi ? wa.y : wa.x;
@@ -1276,7 +1276,7 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
           cw[3] = hi ? wb.w : wb.z;
         } else {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) cw[u] = kc[4 * (c + u) + tj / CPW];
+          for (int u = 0; u < 4; ++u) cw[u] = kc[4 * (c + u) + tj / KCPW];
         }
         f4 s4;
         if constexpr (S16) {
@@ -1294,7 +1294,7 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
         for (int h = 0; h < NREP; ++h) q4[h] = *(const f4 *)&q_s[h][c];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float code = (float)((cw[u] >> sh) & CM);
+          const float code = (float)((cw[u] >> sh) & KCM);
           const float kh = code * s4[u] + z4[u];
 #pragma unroll
           for (int h = 0; h < NREP; ++h) sc[h] = fmaf(q4[h][u], kh, sc[h]);
@@ -1403,11 +1403,11 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
       const int t = t0 + u;
       float v0 = 0.0f, v1 = 0.0f;
       if (t < n_qv) {
-        const uint32_t w = vc[t * VW + c0 / CPW] >> (BITS * (c0 % CPW));
+        const uint32_t w = vc[t * VW + c0 / VCPW] >> (VB * (c0 % VCPW));
         const uint32_t zw = u < 2 ? z2.x : z2.y;
         const float zt = h2f((uint16_t)(u % 2 ? zw >> 16 : zw & 0xFFFFu));
-        v0 = (float)(w & CM) * s4[u] + zt;
-        v1 = (float)((w >> BITS) & CM) * s4[u] + zt;
+        v0 = (float)(w & VCM) * s4[u] + zt;
+        v1 = (float)((w >> VB) & VCM) * s4[u] + zt;
       } else if (t < n) {
         const uint32_t hv = *(const uint32_t *)(vrow + (t - n_qv) * kD + c0);
         v0 = h2f((uint16_t)(hv & 0xFFFFu));
@@ -1452,17 +1452,20 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
 // reload inside the block loop would wait for every DMA in flight.
 // MODE 1 (scores) and MODE 2 (selected attention): see block_role; MODE 1
 // writes no partials.
-// BITS 4 (4-bit codes, attention and the fused step of a uniform batch):
-// six waves (four masked) so that their 11 KB stages fit the LDS.
-template <int NREP, bool MASKED, bool RAGGED, bool PAGED, bool S16, int MODE, int BITS = 2>
-__global__ void __launch_bounds__(MASKED ? 256 : (BITS == 2 ? 512 : 384))
+// KB or VB 4 (4-bit keys or values: attention and the fused step of a
+// uniform batch): six waves (four masked) so that their 11 KB stages fit
+// the LDS.
+template <int NREP, bool MASKED, bool RAGGED, bool PAGED, bool S16, int MODE, int KB = 2,
+          int VB = KB>
+__global__ void __launch_bounds__(MASKED ? 256 : (KB == 2 && VB == 2 ? 512 : 384))
     __attribute__((amdgpu_waves_per_eu(MASKED ? 1 : 2)))
     decode_matrix_kernel(DecodeArgs a, int64_t n_main_all, int n_groups_all, int n_window_all,
                          MatrixRowArg<RAGGED> rows) {
-  static_assert(BITS == 2 || (MODE == 0 && !RAGGED), "4-bit codes: uniform attention only");
-  constexpr int W = MASKED ? 4 : (BITS == 2 ? 8 : 6);
-  __shared__ KStageT<BITS> sm_k[W];
-  __shared__ VStageT<BITS> sm_v[W];
+  static_assert((KB == 2 && VB == 2) || (MODE == 0 && !RAGGED),
+                "4-bit codes: uniform attention only");
+  constexpr int W = MASKED ? 4 : (KB == 2 && VB == 2 ? 8 : 6);
+  __shared__ KStageT<KB> sm_k[W];
+  __shared__ VStageT<VB> sm_v[W];
   __shared__ __attribute__((aligned(16))) float sm_p[W][4][kPRow];
   __shared__ __attribute__((aligned(16))) float sm_mask[W][kBT];
   __shared__ __attribute__((aligned(16))) float sm_bias[W][16];
@@ -1523,13 +1526,13 @@ __global__ void __launch_bounds__(MASKED ? 256 : (BITS == 2 ? 512 : 384))
   while (item < sh.n_skip) {
     const int x = (int)s + item * n_groups;
     const WinLoads<NREP> ld =
-        window_issue<NREP, PAGED, S16, MODE, BITS>(a, rs, n_main, x, hk, b, L);
-    window_role<NREP, MASKED, PAGED, S16, MODE, BITS>(a, rs, n_main, x, n_groups + x, hk, b, L,
+        window_issue<NREP, PAGED, S16, MODE, KB, VB>(a, rs, n_main, x, hk, b, L);
+    window_role<NREP, MASKED, PAGED, S16, MODE, KB, VB>(a, rs, n_main, x, n_groups + x, hk, b, L,
                                                       ld);
     wave_lds_sync();   // the LDS reads of the chunk are done
     item = draw_item(&sm_ctr, lane);
   }
-  block_role<NREP, MASKED, PAGED, S16, MODE, BITS>(a, sh, item - sh.n_skip, hk, b, L, &sm_k[w],
+  block_role<NREP, MASKED, PAGED, S16, MODE, KB, VB>(a, sh, item - sh.n_skip, hk, b, L, &sm_k[w],
                                                    &sm_v[w]);
   if constexpr (MODE == 1) return;   // the scores are stored; no partials
 
@@ -1607,9 +1610,9 @@ __global__ void __launch_bounds__(MASKED ? 256 : (BITS == 2 ? 512 : 384))
   }
 }
 
-template <bool S16, int BITS = 2>
+template <bool S16, int KB = 2, int VB = KB>
 static bool layout_is(const Layout &L) {
-  using RC = Rec<S16, BITS>;
+  using RC = Rec<S16, KB, VB>;
   return L.sb == RC::sb && L.rec == RC::bytes && L.kc == RC::kc && L.ks == RC::ks &&
          L.kz == RC::kz && L.vc == RC::vc && L.vs == RC::vs && L.vz == RC::vz;
 }
@@ -1624,13 +1627,20 @@ bool decode_matrix_supported(const DecodeArgs &a) {
          ((uintptr_t)a.q & 15) == 0;
 }
 
+template <int KB, int VB>
+static bool layout_is_any(const Layout &L) {
+  return layout_is<false, KB, VB>(L) || layout_is<true, KB, VB>(L);
+}
+
 bool decode_matrix4_supported(const DecodeArgs &a) {
-  // records of the 4-bit / G 32 / head_dim 128 shape (fp32 or fp16 scales)
-  // in a contiguous cache, copied 16 bytes at a time like the window rows
-  // and q
-  return a.kb == 4 && a.vb == 4 && a.G == kG && a.D == kD &&
+  // records of the G 32 / head_dim 128 shape with 4-bit keys, values or both
+  // (fp32 or fp16 scales) in a contiguous cache, copied 16 bytes at a time
+  // like the window rows and q
+  const bool widths = (a.kb == 4 && a.vb == 4 && layout_is_any<4, 4>(a.L)) ||
+                      (a.kb == 2 && a.vb == 4 && layout_is_any<2, 4>(a.L)) ||
+                      (a.kb == 4 && a.vb == 2 && layout_is_any<4, 2>(a.L));
+  return widths && a.G == kG && a.D == kD &&
          (a.n_rep == 1 || a.n_rep == 2 || a.n_rep == 4) && a.L.pt == nullptr &&
-         (layout_is<false, 4>(a.L) || layout_is<true, 4>(a.L)) &&
          ((uintptr_t)a.L.blocks & 15) == 0 && ((uintptr_t)a.k_res & 15) == 0 &&
          ((uintptr_t)a.v_res & 15) == 0 && ((uintptr_t)a.q & 15) == 0;
 }
@@ -1639,7 +1649,9 @@ int decode_matrix_window_chunks(const DecodeArgs &a, int64_t n_main) {
   return matrix_window_chunks(a.t, n_main);
 }
 
-int decode_matrix_waves(const DecodeArgs &a) { return a.mask ? 4 : (a.kb == 4 ? 6 : 8); }
+int decode_matrix_waves(const DecodeArgs &a) {
+  return a.mask ? 4 : (a.kb == 4 || a.vb == 4 ? 6 : 8);
+}
 
 template <int NREP, bool RAGGED, bool PAGED, bool S16, int MODE = 0>
 static void launch_rep(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
@@ -1669,27 +1681,38 @@ static void launch_layout(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t
   }
 }
 
-// 4-bit codes: a uniform batch in a contiguous cache, attention (and the
-// fused step) only.
-template <int NREP, bool S16>
+// 4-bit keys, values or both: a uniform batch in a contiguous cache,
+// attention (and the fused step) only.
+template <int NREP, bool S16, int KB, int VB>
 static void launch_rep4(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
                         int n_groups, int n_window) {
   if (a.mask)
-    hipLaunchKernelGGL((decode_matrix_kernel<NREP, true, false, false, S16, 0, 4>), grid,
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, true, false, false, S16, 0, KB, VB>), grid,
                        dim3(256), 0, s, a, n_main, n_groups, n_window, NoRows{});
   else
-    hipLaunchKernelGGL((decode_matrix_kernel<NREP, false, false, false, S16, 0, 4>), grid,
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, false, false, false, S16, 0, KB, VB>), grid,
                        dim3(384), 0, s, a, n_main, n_groups, n_window, NoRows{});
 }
 
-template <bool S16>
+template <bool S16, int KB, int VB>
 static void launch_reps4(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
                          int n_groups, int n_window) {
   switch (a.n_rep) {
-    case 1: launch_rep4<1, S16>(a, grid, s, n_main, n_groups, n_window); break;
-    case 2: launch_rep4<2, S16>(a, grid, s, n_main, n_groups, n_window); break;
-    default: launch_rep4<4, S16>(a, grid, s, n_main, n_groups, n_window); break;
+    case 1: launch_rep4<1, S16, KB, VB>(a, grid, s, n_main, n_groups, n_window); break;
+    case 2: launch_rep4<2, S16, KB, VB>(a, grid, s, n_main, n_groups, n_window); break;
+    default: launch_rep4<4, S16, KB, VB>(a, grid, s, n_main, n_groups, n_window); break;
   }
+}
+
+template <bool S16>
+static void launch_widths4(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
+                           int n_groups, int n_window) {
+  if (a.kb == 4 && a.vb == 4)
+    launch_reps4<S16, 4, 4>(a, grid, s, n_main, n_groups, n_window);
+  else if (a.kb == 2)
+    launch_reps4<S16, 2, 4>(a, grid, s, n_main, n_groups, n_window);
+  else
+    launch_reps4<S16, 4, 2>(a, grid, s, n_main, n_groups, n_window);
 }
 
 template <bool RAGGED, int MODE = 0>
@@ -1731,9 +1754,9 @@ hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int n_group
   const int64_t n_wg = (int64_t)n_groups * a.H * a.B;
   if (n_wg > ((int64_t)1 << 25)) return hipErrorInvalidValue;   // 32-bit workgroup ids
   if (four && a.L.sb == 2)
-    launch_reps4<true>(a, dim3((unsigned)n_wg), s, n_main, n_groups, n_window);
+    launch_widths4<true>(a, dim3((unsigned)n_wg), s, n_main, n_groups, n_window);
   else if (four)
-    launch_reps4<false>(a, dim3((unsigned)n_wg), s, n_main, n_groups, n_window);
+    launch_widths4<false>(a, dim3((unsigned)n_wg), s, n_main, n_groups, n_window);
   else
     launch_reps<false>(a, dim3((unsigned)n_wg), s, n_main, n_groups, n_window, NoRows{});
   return hipGetLastError();

@@ -1,6 +1,8 @@
 """GPU parity of the 4-bit matrix-core path of kivi_decode_attn: 4-bit keys
 and values (KIVI item 1 with B = 4, the KIVI-4 setting of the page
-"Literature audit -- Group 2", section 1), attention as item 5.  The matrix
+"Literature audit -- Group 2", section 1), and 2-bit keys with 4-bit values
+or the reverse (item 6 puts the widths on the hyperparameter axis),
+attention as item 5.  The matrix
 kernel's block role takes the whole 128-token blocks and its window role the
 tokens past them; outputs within 2e-3 + 1e-3*|ref| of the CPU oracle
 elementwise, on shapes that span several blocks, workgroups and a ragged
@@ -19,7 +21,10 @@ pytestmark = [pytest.mark.gpu,
 M = kivi.KIVI_PATH_MATRIX
 
 
-def _case(seed, B, H, rep, t, R=128, scale_fp16=False, kscale=15.0, extra=0):
+WIDTHS = [(4, 4), (2, 4), (4, 2)]
+
+
+def _case(seed, B, H, rep, t, R=128, scale_fp16=False, kscale=15.0, extra=0, kb=4, vb=4):
     """Gaussian keys with per-channel magnitudes up to `kscale` (outlier
     channels), Gaussian values and queries; the same cache on the GPU and in
     the oracle."""
@@ -29,8 +34,8 @@ def _case(seed, B, H, rep, t, R=128, scale_fp16=False, kscale=15.0, extra=0):
     V = rng.standard_normal((B, H, t, D)).astype(np.float16)
     q = rng.standard_normal((B, H * rep, D)).astype(np.float16)
     cap = cap_for(t + extra, R)
-    g = kivi.Cache(B, H, D, 4, 4, 32, R, cap, scale_fp16=scale_fp16)
-    o = oracle.Cache(B, H, D, 4, 4, 32, R, cap, scale_fp16=scale_fp16)
+    g = kivi.Cache(B, H, D, kb, vb, 32, R, cap, scale_fp16=scale_fp16)
+    o = oracle.Cache(B, H, D, kb, vb, 32, R, cap, scale_fp16=scale_fp16)
     if t:
         kivi.kivi_append(g, dev(K), dev(V))
         o.append(b16(K), b16(V))
@@ -125,3 +130,32 @@ def test_decode_steps_across_a_block():
         o.append(b16(k), b16(v))
         say(f"step {step}: t={g.n_tokens}")
         assert_close(out, o.decode_attn(b16(qs)), f"step {step}")
+
+
+@pytest.mark.parametrize("kb,vb", WIDTHS[1:])
+@pytest.mark.parametrize("t", [33, 255, 256, 385, 1000, 2049])
+@pytest.mark.parametrize("rep", [1, 2, 4])
+def test_mixed_widths(kb, vb, t, rep):
+    """2-bit keys with 4-bit values and the reverse: each half of the block
+    role and of the window role takes its own width."""
+    g, o, q, _ = _case(t * 10 + rep + kb, 2, 2, rep, t, kb=kb, vb=vb)
+    ref = o.decode_attn(b16(q))
+    for p in (M, kivi.KIVI_PATH_AUTO):
+        assert_close(host(kivi.kivi_decode_attn(g, dev(q), path=p)), ref,
+                     f"kb={kb} vb={vb} t={t} rep={rep} path={p}")
+
+
+@pytest.mark.parametrize("kb,vb", WIDTHS[1:])
+def test_mixed_widths_masked_fp16_scales_and_splits(kb, vb):
+    g, o, q, rng = _case(90 + kb, 2, 2, 4, 3000, kb=kb, vb=vb)
+    t = g.n_tokens
+    m = np.where(rng.random((2, t)) < 0.3, -np.inf, rng.standard_normal((2, t))).astype(np.float32)
+    assert_close(host(kivi.kivi_decode_attn(g, dev(q), mask=dev(m), path=M)),
+                 o.decode_attn(b16(q), m), f"mask kb={kb} vb={vb}")
+    ref = o.decode_attn(b16(q))
+    for tps in (256, 1024):
+        assert_close(host(kivi.kivi_decode_attn(g, dev(q), tokens_per_split=tps, path=M)), ref,
+                     f"tps={tps} kb={kb} vb={vb}")
+    g, o, q, _ = _case(95 + kb, 2, 2, 2, 1500, kb=kb, vb=vb, scale_fp16=True)
+    assert_close(host(kivi.kivi_decode_attn(g, dev(q), path=M)), o.decode_attn(b16(q)),
+                 f"fp16 scales kb={kb} vb={vb}")

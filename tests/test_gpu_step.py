@@ -122,6 +122,15 @@ def test_decode_step_4bit_masked():
     _steps(4, 128, 250, 12, masked=True, kb=4, vb=4)
 
 
+@pytest.mark.parametrize("kb,vb,rep,R,T0,n_steps", [
+    (2, 4, 4, 128, 120, 150), (4, 2, 4, 128, 120, 150), (2, 4, 2, 64, 500, 70),
+    (4, 2, 4, 32, 3, 80)])
+def test_decode_step_mixed_widths(kb, vb, rep, R, T0, n_steps):
+    """2-bit keys with 4-bit values and the reverse, fused: the popped value
+    quantized at the value width, a completed key block at the key width."""
+    _steps(rep, R, T0, n_steps, masked=False, kb=kb, vb=vb)
+
+
 @pytest.mark.parametrize("kb,vb,rep", [(4, 4, 1), (2, 2, 8)])
 def test_decode_step_other_shapes(kb, vb, rep):
     """Shapes the matrix kernel does not take run as append + attention."""
