@@ -231,6 +231,18 @@ struct DmaOffsets {
   }
 };
 
+// The value codes of a block sit in LDS with the 16-byte units of each token
+// row (VB of them) permuted: unit h of row r at unit h ^ f(r), f(r) = (r /
+// (16 / VB)) % VB.  The transposed reads of 16 consecutive rows then hit
+// distinct banks (rows are 8 or 16 words apart, so unpermuted they meet in
+// 8 or 4 bank groups).  The permutation is its own inverse: the copy that
+// fills LDS unit l of a 1 KB piece reads unit vcode_unit(l) of the source,
+// and the unit that holds source unit (r, h) is at LDS unit (r, h ^ f(r)).
+template <int VB>
+__host__ __device__ constexpr uint32_t vcode_unit(uint32_t l) {
+  return l ^ ((l >> 4) & (uint32_t)(VB - 1));
+}
+
 // Per-lane source offsets of every copy of a block's key part and value
 // part, counted from the start of the record (section offset included), so
 // that all copies of a part share one scalar base address -- the record --
@@ -244,7 +256,7 @@ struct PartOffsets {
 #pragma unroll
     for (int i = 0; i < NCK; ++i) k[i] = RC::kc + i * 1024 + o.lin;
 #pragma unroll
-    for (int i = 0; i < NCV; ++i) v[i] = RC::vc + i * 1024 + o.lin;
+    for (int i = 0; i < NCV; ++i) v[i] = RC::vc + i * 1024 + vcode_unit<VB>(o.lin >> 4) * 16u;
     if constexpr (S16) {
       k[NCK] = RC::ks + o.zrot;
       v[NCV] = RC::vs + o.zrot;
@@ -841,11 +853,13 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
       if constexpr (VB == 2) {
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-          xv[4 * u + g] = tr4(vst.vc + (32 * kg + 16 * u + i) * 8 + g * 2);
+          xv[4 * u + g] = tr4(vst.vc + (32 * kg + 16 * u + i) * 8 +
+                              4 * ((g >> 1) ^ ((i >> 3) & 1)) + 2 * (g & 1));
       } else {
 #pragma unroll
         for (int w = 0; w < 8; ++w)
-          xv[8 * u + w] = tr4(vst.vc + (32 * kg + 16 * u + i) * 16 + w * 2);
+          xv[8 * u + w] = tr4(vst.vc + (32 * kg + 16 * u + i) * 16 +
+                              4 * ((w >> 1) ^ ((i >> 2) & 3)) + 2 * (w & 1));
       }
     }
     {
