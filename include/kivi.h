@@ -221,9 +221,9 @@ int kivi_decode_attn(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads,
  * kivi_decode_attn (automatic plan).  KIVI_ERR_WORKSPACE, before anything
  * runs, when this call's partials pass 16 MiB: (D + 4) x 4 bytes for each
  * of batch x n_q_heads x S partial slots, where the matrix kernel plans S =
- * 8 per workgroup (about one workgroup per CU, shared out among the batch x
- * n_kv_heads slabs) plus one per 32 tokens of the window (at most 10 for R
- * = 128).  Every call on a
+ * its workgroups per slab (about one workgroup per CU, shared out among the
+ * batch x n_kv_heads slabs) plus one per 32 tokens of the window (at most 10
+ * for R = 128).  Every call on a
  * GPU shares its array: calls that overlap on one GPU (several streams or
  * threads) race and must be serialized by the caller.  Each call writes
  * every slot it reads, so no state carries over between calls. */
@@ -234,11 +234,16 @@ int kivi_decode_attn_noalloc(const kivi_cache *c, const void *q_fp16, int32_t n_
 /* Same as kivi_decode_attn with explicit tuning, for tests and sweeps:
  *   tokens_per_split  0 = automatic, else a positive multiple of 64.
  *   path              KIVI_PATH_AUTO (the matrix-core kernel where the shape
- *                     allows, else the vector kernel where it allows, else
- *                     the scalar kernel), KIVI_PATH_GENERIC (scalar kernel
- *                     for every token), KIVI_PATH_MATRIX (matrix-core
- *                     kernel: 2-bit codes, head_dim 128, G 32, 1, 2 or 4
- *                     query heads per KV head, 16-byte aligned q) or
+ *                     allows -- with 4-bit codes and one query head per KV
+ *                     head only from 18 blocks of 128 tokens per row on --
+ *                     else the vector kernel where it allows, else the
+ *                     scalar kernel), KIVI_PATH_GENERIC (scalar kernel for
+ *                     every token), KIVI_PATH_MATRIX (matrix-core kernel:
+ *                     head_dim 128, G 32, 1, 2 or 4 query heads per KV
+ *                     head, 16-byte aligned q, record array and windows;
+ *                     2-bit keys and values in any cache, or 4-bit keys,
+ *                     values or both in a contiguous cache of a uniform
+ *                     batch) or
  *                     KIVI_PATH_VECTOR (vector kernel: 2- or 4-bit codes,
  *                     head_dim 128, G 32, R a multiple of 32, 1 or an even
  *                     number (at most 64) of query heads per KV head,
@@ -258,9 +263,9 @@ size_t kivi_decode_attn_workspace_bytes_ex(const kivi_cache *c, int32_t n_q_head
  * and attends over the cache that results, i.e. the same cache state and
  * (within the attention tolerance) the same output as
  *   kivi_append(c, k_new, v_new, 1); kivi_decode_attn(c, q, ...).
- * Where the matrix-core kernel takes the shape (2-bit keys and values,
- * head_dim 128, G 32, 1, 2 or 4 query heads per KV head, 16-byte aligned
- * q, k_new and v_new), the append runs inside the attention launch: the new
+ * Where the default path takes the matrix-core kernel (KIVI_PATH_AUTO of
+ * kivi_decode_attn_ex, for the cache after the append) and q, k_new and
+ * v_new are 16-byte aligned, the append runs inside the attention launch: the new
  * key and value are read from k_new / v_new, the value that leaves the
  * window and a key block the token completes are quantized by the
  * workgroups that attend over them, and the cache writes happen where no
