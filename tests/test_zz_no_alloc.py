@@ -28,7 +28,9 @@ def _cache(rng, B, H, rep, T, kb=2, vb=2, R=128):
 def test_noalloc_matches_workspace_call_twice():
     rng = np.random.default_rng(2024)
     # the second call has a smaller cache: fewer slabs, tokens and slots
-    for B, H, rep, T, kb, vb in [(2, 4, 4, 5000, 2, 2), (1, 2, 2, 700, 2, 2),
+    # (4-bit GQA and mixed widths on the matrix kernel, 4-bit MHA on the vector one)
+    for B, H, rep, T, kb, vb in [(2, 4, 4, 5000, 2, 2), (2, 2, 4, 3000, 4, 4),
+                                 (1, 2, 2, 2000, 2, 4), (1, 2, 2, 700, 2, 2),
                                  (2, 2, 1, 1500, 4, 4)]:
         c, q = _cache(rng, B, H, rep, T, kb, vb)
         ref = host(kivi.kivi_decode_attn(c, q))
