@@ -273,4 +273,36 @@ __device__ __forceinline__ uint32_t quant_code_r(float x, float z, float s, floa
   return (uint32_t)q;
 }
 
+// quant_code_r over the n values of one group, with the same arithmetic: the
+// near-tie test of every value comes first, and the division runs only in a
+// lane that has a value near a tie, so the common path has no branch per
+// value.
+template <int N>
+__device__ __forceinline__ void quant_codes_r(const float (&x)[N], float z, float s, float r,
+                                              int bits, uint32_t (&c)[N]) {
+  if (s == 0.0f) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) c[i] = 0u;
+    return;
+  }
+  float q[N];
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float u = x[i] - z;
+    q[i] = rintf(u * r);
+    near = near || fabsf(u * r - q[i]) > 0.49999f;
+  }
+  if (near) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const float u = x[i] - z;
+      if (fabsf(u * r - q[i]) > 0.49999f) q[i] = rintf(u / s);
+    }
+  }
+  const float qmax = (float)((1 << bits) - 1);
+#pragma unroll
+  for (int i = 0; i < N; ++i) c[i] = (uint32_t)fminf(fmaxf(q[i], 0.0f), qmax);
+}
+
 }  // namespace kivi

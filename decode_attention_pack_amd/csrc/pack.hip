@@ -155,12 +155,13 @@ key_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t g_first, 
     group_first_min_max(v[k], mn, mx);
     const float s = stored_scale(group_scale(mn, mx, BITS), L);
     const float r = __builtin_amdgcn_rcpf(s);
+    uint32_t c[G];
+    quant_codes_r(v[k], mn, s, r, BITS, c);
 #pragma unroll
     for (int w = 0; w < words; ++w) {
       uint32_t word = 0;
 #pragma unroll
-      for (int e = 0; e < per; ++e)
-        word |= quant_code_r(v[k][w * per + e], mn, s, r, BITS) << (BITS * e);
+      for (int e = 0; e < per; ++e) word |= c[w * per + e] << (BITS * e);
       out[k * words + w] = word;
     }
     sv[k] = s;
@@ -220,6 +221,8 @@ value_tiles_kernel(const uint16_t *__restrict__ x, int64_t T_in, int64_t n_rows,
     const float r = __builtin_amdgcn_rcpf(s);
     const int64_t tau = tau_first + r0 + t;
     uint32_t *dst = out_s + t * kWords + (g * G) / per;
+    // (a branch per value: the branch-free form doubles this kernel's
+    // registers, and its occupancy matters more than the branches)
 #pragma unroll
     for (int w = 0; w < G / per; ++w) {
       uint32_t word = 0;
