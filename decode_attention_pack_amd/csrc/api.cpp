@@ -942,11 +942,17 @@ int kivi_select_attn(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads,
       rc = make_plan(c, n_q_heads, 0, KIVI_PATH_MATRIX, a, r, ps, who);
       if (rc) return rc;
     }
-    rc = hip_status(kivi::launch_scores_matrix(a, ps.n_main, ps.n_groups_matrix, s),
+    // with each wave's largest score per row in the partial-slot section
+    // (read by the selection before the attention writes its partials there)
+    kivi::DecodeArgs as = a;
+    as.rmax = a.part;
+    as.rmax_n = ps.n_groups_matrix * kivi::decode_matrix_waves(a) +
+                kivi::decode_matrix_window_chunks(a, ps.n_main);
+    rc = hip_status(kivi::launch_scores_matrix(as, ps.n_main, ps.n_groups_matrix, s),
                     "kivi_select_attn (scores)");
     if (rc) return rc;
     // 2. the selection of every row
-    rc = hip_status(kivi::launch_select_rows(a, tau, rows, n_selected, sel_mask, s),
+    rc = hip_status(kivi::launch_select_rows(as, tau, rows, n_selected, sel_mask, s),
                     "kivi_select_attn (select)");
     if (rc) return rc;
     // 3. attention over the selected tokens, then the merge of the workgroups

@@ -540,7 +540,7 @@ template <int NREP, bool MASKED, bool PAGED, bool S16, int MODE, int KB = 2, int
 __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare &sh,
                                            int64_t first, int hk, int b, const Lds &L,
                                            KStageT<KB> *__restrict__ kbuf,
-                                           VStageT<VB> *__restrict__ vbuf) {
+                                           VStageT<VB> *__restrict__ vbuf, int mslot = 0) {
   static_assert(NREP == 1 || NREP == 2 || NREP == 4, "query heads per KV head");
   static_assert(MODE != 2 || !MASKED, "selected attention takes the mask from the scores");
   static_assert((KB == 2 && VB == 2) || MODE == 0, "4-bit codes: attention only");
@@ -563,6 +563,8 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
   if (first >= sh.nb) {
     // no block for this wave: an empty partial (m = -inf)
     if (MODE != 1 && lane < NREP) *(float2 *)&L.p[lane][kD] = make_float2(-INFINITY, 0.0f);
+    if (MODE == 1 && a.rmax && lane < NREP)
+      a.rmax[((int64_t)b * a.Hq + hk * NREP + lane) * a.rmax_n + mslot] = -INFINITY;
     return;
   }
 
@@ -659,6 +661,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
   // e), kept in registers and stored while the next block is processed.
   float sp[4][2] = {};
   int64_t prev = -1;
+  float smax = -INFINITY;   // MODE 1: the largest score this lane stored
   auto store_prev = [&]() __attribute__((always_inline)) {
     if (prev >= 0 && k_valid) {
       float *dst = a.scores + ((int64_t)b * a.Hq + hk * NREP + h_s) * a.cap + prev * kBT + 2 * i;
@@ -806,6 +809,7 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
       for (int g = 0; g < 4; ++g) {
         sp[g][0] = s2[g][0];
         sp[g][1] = s2[g][1];
+        smax = fmaxf(smax, fmaxf(s2[g][0], s2[g][1]));
       }
       prev = cur;
       return;
@@ -947,6 +951,10 @@ __device__ __forceinline__ void block_role(const DecodeArgs &a, const BlockShare
   block(std::false_type{}, 0);
   if constexpr (MODE == 1) {
     store_prev();
+    // the wave's largest score of head h_s: the 16 lanes of its row
+    const float hm = row_max(smax);
+    if (a.rmax && k_valid && i == 0)
+      a.rmax[((int64_t)b * a.Hq + hk * NREP + h_s) * a.rmax_n + mslot] = hm;
     return;
   }
 
@@ -1341,12 +1349,19 @@ __device__ __forceinline__ void window_role(const DecodeArgs &a, const RowSpan &
 #pragma unroll
   for (int h = 0; h < NREP; ++h) sc[h] += __shfl_xor(sc[h], 32);
   if constexpr (MODE == 1) {
-    // the scores, natural units, from the lanes of the first half
-    if (tj < n && hf == 0) {
-      const float mk = MASKED ? a.mask[(int64_t)b * a.t + Ta + tj] : 0.0f;
+    // the scores, natural units, from the lanes of the first half (the
+    // second half holds the same); with rmax, the chunk's largest score of
+    // each head goes to entry `slot` of the head's row
+    const float mk = MASKED && tj < n ? a.mask[(int64_t)b * a.t + Ta + tj] : 0.0f;
 #pragma unroll
-      for (int h = 0; h < NREP; ++h)
-        a.scores[((int64_t)b * a.Hq + hk * NREP + h) * a.cap + Ta + tj] = sc[h] * a.sm_scale + mk;
+    for (int h = 0; h < NREP; ++h) {
+      const float v = tj < n ? sc[h] * a.sm_scale + mk : -INFINITY;
+      const int64_t row = (int64_t)b * a.Hq + hk * NREP + h;
+      if (tj < n && hf == 0) a.scores[row * a.cap + Ta + tj] = v;
+      if (a.rmax) {
+        const float cm = group_max(row_max(v));
+        if (j == 0) a.rmax[row * a.rmax_n + slot] = cm;
+      }
     }
     return;
   }
@@ -1541,13 +1556,16 @@ __global__ void __launch_bounds__(MASKED ? 256 : (KB == 2 && VB == 2 ? 512 : 384
     const int x = (int)s + item * n_groups;
     const WinLoads<NREP> ld =
         window_issue<NREP, PAGED, S16, MODE, KB, VB>(a, rs, n_main, x, hk, b, L);
-    window_role<NREP, MASKED, PAGED, S16, MODE, KB, VB>(a, rs, n_main, x, n_groups + x, hk, b, L,
+    window_role<NREP, MASKED, PAGED, S16, MODE, KB, VB>(a, rs, n_main, x,
+                                                        MODE == 1 ? n_groups * W + x
+                                                                  : n_groups + x,
+                                                        hk, b, L,
                                                       ld);
     wave_lds_sync();   // the LDS reads of the chunk are done
     item = draw_item(&sm_ctr, lane);
   }
   block_role<NREP, MASKED, PAGED, S16, MODE, KB, VB>(a, sh, item - sh.n_skip, hk, b, L, &sm_k[w],
-                                                   &sm_v[w]);
+                                                   &sm_v[w], (int)s * W + w);
   if constexpr (MODE == 1) return;   // the scores are stored; no partials
 
   // The W partials of the workgroup's waves, merged with the log-sum-exp
@@ -1796,6 +1814,9 @@ hipError_t launch_scores_matrix(const DecodeArgs &a, int64_t n_main, int n_group
   const hipError_t e = check_select_matrix(a, n_main, n_groups);
   if (e != hipSuccess) return e;
   const int n_window = decode_matrix_window_chunks(a, n_main);
+  // one largest-score entry per wave of every workgroup and per window chunk
+  if (a.rmax && a.rmax_n != n_groups * decode_matrix_waves(a) + n_window)
+    return hipErrorInvalidValue;
   const int64_t n_wg = (int64_t)n_groups * a.H * a.B;
   launch_reps<false, 1>(a, dim3((unsigned)n_wg), s, n_main, n_groups, n_window, NoRows{});
   return hipGetLastError();

@@ -101,6 +101,12 @@ struct DecodeArgs {
   // read them there, and the selection rule of row (b, hq) at sel[b Hq + hq].
   float *scores;
   const SelectRow *sel;
+  // Scores-only matrix launches, when rmax is set: the largest score each
+  // wave stored of row (b, hq) at rmax[(b Hq + hq) rmax_n + k] (k: the
+  // wave's item share, or a window chunk), -inf for a wave with none; the
+  // selection then takes the row's largest score from these rmax_n values.
+  float *rmax;
+  int32_t rmax_n;
 };
 
 // Scalar kernel over tokens [tok_begin, t): `n_splits` splits of

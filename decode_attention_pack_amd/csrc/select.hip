@@ -240,8 +240,14 @@ select_rows_kernel(DecodeArgs a, float tau, SelectRow *rows, int32_t *n_selected
   const int t = (int)a.t;
   const float *sr = a.scores + row * a.cap;
 
+  // the row's largest score: from the scores launch's per-wave maxima where
+  // it recorded them, else from the row itself
   float m = -INFINITY;
-  for_scores(sr, t, [&](int, float s) { m = fmaxf(m, s); });
+  if (a.rmax) {
+    for (int k = tid; k < a.rmax_n; k += kSThreads) m = fmaxf(m, a.rmax[row * a.rmax_n + k]);
+  } else {
+    for_scores(sr, t, [&](int, float s) { m = fmaxf(m, s); });
+  }
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   if ((tid & 63) == 0) s_max[tid >> 6] = m;
   __syncthreads();
