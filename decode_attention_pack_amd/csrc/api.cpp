@@ -249,7 +249,9 @@ int plan_matrix_rows(const kivi_cache *c, const Rows &r, int32_t tps_req, int wa
   int64_t used = 0;
   if (tps_req == 0) {
     const int64_t target = std::min<int64_t>(
-        kivi::kMaxRows, max64(B, (int64_t)device_cus() * (8 / waves) / c->n_kv_heads));
+        kivi::kMaxRows,
+        max64(B, (int64_t)device_cus() * (c->k_bits == 4 || c->v_bits == 4 ? 1 : 8 / waves) /
+                     c->n_kv_heads));
     for (int b = 0; b < B; ++b) groups[b] = 1;
     used = B;
     while (used < target) {
@@ -294,7 +296,7 @@ int plan_matrix_rows(const kivi_cache *c, const Rows &r, int32_t tps_req, int wa
 bool matrix_wanted(const kivi::DecodeArgs &a, int32_t path, bool ragged) {
   if (!(path == KIVI_PATH_AUTO || path == KIVI_PATH_MATRIX) || a.t <= 0) return false;
   if (kivi::decode_matrix_supported(a)) return true;
-  if (ragged || !kivi::decode_matrix4_supported(a)) return false;
+  if (!kivi::decode_matrix4_supported(a, ragged)) return false;
   if (path == KIVI_PATH_MATRIX || a.n_rep >= 2) return true;
   const int64_t blocks =
       kivi::matrix_main(kivi::row_span(a.t, a.R, a.t_new >= 0), a.R) / kMatrixBlock;
@@ -711,7 +713,7 @@ int decode_call(const kivi_cache *c, const void *q_fp16, int32_t n_q_heads, cons
   a.sm_scale = 1.0f / sqrtf((float)a.D);
 
   if (path == KIVI_PATH_MATRIX && !kivi::decode_matrix_supported(a) &&
-      !(kivi::decode_matrix4_supported(a) && !r.ragged))
+      !kivi::decode_matrix4_supported(a, r.ragged))
     return fail(KIVI_ERR_INVALID_ARG, "%s: the matrix-core kernel does not handle this shape", who);
   if (path == KIVI_PATH_VECTOR && !kivi::decode_vector_supported(a))
     return fail(KIVI_ERR_INVALID_ARG, "%s: the vector kernel does not handle this shape", who);

@@ -1490,8 +1490,8 @@ __global__ void __launch_bounds__(MASKED ? 256 : (KB == 2 && VB == 2 ? 512 : 384
     __attribute__((amdgpu_waves_per_eu(MASKED ? 1 : 2)))
     decode_matrix_kernel(DecodeArgs a, int64_t n_main_all, int n_groups_all, int n_window_all,
                          MatrixRowArg<RAGGED> rows) {
-  static_assert((KB == 2 && VB == 2) || (MODE == 0 && !RAGGED),
-                "4-bit codes: uniform attention only");
+  static_assert((KB == 2 && VB == 2) || MODE == 0, "4-bit codes: attention only");
+  static_assert(KB == VB || (!RAGGED && !PAGED), "mixed widths: a uniform contiguous cache");
   constexpr int W = MASKED ? 4 : (KB == 2 && VB == 2 ? 8 : 6);
   __shared__ KStageT<KB> sm_k[W];
   __shared__ VStageT<VB> sm_v[W];
@@ -1664,15 +1664,16 @@ static bool layout_is_any(const Layout &L) {
   return layout_is<false, KB, VB>(L) || layout_is<true, KB, VB>(L);
 }
 
-bool decode_matrix4_supported(const DecodeArgs &a) {
-  // records of the G 32 / head_dim 128 shape with 4-bit keys, values or both
-  // (fp32 or fp16 scales) in a contiguous cache, copied 16 bytes at a time
-  // like the window rows and q
-  const bool widths = (a.kb == 4 && a.vb == 4 && layout_is_any<4, 4>(a.L)) ||
-                      (a.kb == 2 && a.vb == 4 && layout_is_any<2, 4>(a.L)) ||
-                      (a.kb == 4 && a.vb == 2 && layout_is_any<4, 2>(a.L));
-  return widths && a.G == kG && a.D == kD &&
-         (a.n_rep == 1 || a.n_rep == 2 || a.n_rep == 4) && a.L.pt == nullptr &&
+bool decode_matrix4_supported(const DecodeArgs &a, bool ragged) {
+  // records of the G 32 / head_dim 128 shape with 4-bit keys and values (any
+  // batch, contiguous or paged) or with one of the two 4-bit (a uniform
+  // batch in a contiguous cache), fp32 or fp16 scales, copied 16 bytes at a
+  // time like the window rows and q
+  const bool both = a.kb == 4 && a.vb == 4 && layout_is_any<4, 4>(a.L);
+  const bool mixed = (a.kb == 2 && a.vb == 4 && layout_is_any<2, 4>(a.L)) ||
+                     (a.kb == 4 && a.vb == 2 && layout_is_any<4, 2>(a.L));
+  return (both || (mixed && !ragged && a.L.pt == nullptr)) && a.G == kG && a.D == kD &&
+         (a.n_rep == 1 || a.n_rep == 2 || a.n_rep == 4) &&
          ((uintptr_t)a.L.blocks & 15) == 0 && ((uintptr_t)a.k_res & 15) == 0 &&
          ((uintptr_t)a.v_res & 15) == 0 && ((uintptr_t)a.q & 15) == 0;
 }
@@ -1685,30 +1686,31 @@ int decode_matrix_waves(const DecodeArgs &a) {
   return a.mask ? 4 : (a.kb == 4 || a.vb == 4 ? 6 : 8);
 }
 
-template <int NREP, bool RAGGED, bool PAGED, bool S16, int MODE = 0>
+template <int NREP, bool RAGGED, bool PAGED, bool S16, int MODE = 0, int B4 = 2>
 static void launch_rep(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
                        int n_groups, int n_window, const MatrixRowArg<RAGGED> &rows) {
   // selected attention takes the mask from the stored scores
   if (a.mask && MODE != 2)
-    hipLaunchKernelGGL((decode_matrix_kernel<NREP, MODE != 2, RAGGED, PAGED, S16, MODE>), grid,
-                       dim3(256), 0, s, a, n_main, n_groups, n_window, rows);
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, MODE != 2, RAGGED, PAGED, S16, MODE, B4, B4>),
+                       grid, dim3(256), 0, s, a, n_main, n_groups, n_window, rows);
   else
-    hipLaunchKernelGGL((decode_matrix_kernel<NREP, false, RAGGED, PAGED, S16, MODE>), grid,
-                       dim3(512), 0, s, a, n_main, n_groups, n_window, rows);
+    hipLaunchKernelGGL((decode_matrix_kernel<NREP, false, RAGGED, PAGED, S16, MODE, B4, B4>), grid,
+                       dim3(B4 == 2 ? 512 : 384), 0, s, a, n_main, n_groups, n_window, rows);
 }
 
-template <bool RAGGED, bool PAGED, bool S16, int MODE>
+// B4: the code width of keys and values alike (2, or 4 for attention)
+template <bool RAGGED, bool PAGED, bool S16, int MODE, int B4 = 2>
 static void launch_layout(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
                           int n_groups, int n_window, const MatrixRowArg<RAGGED> &rows) {
   switch (a.n_rep) {
     case 1:
-      launch_rep<1, RAGGED, PAGED, S16, MODE>(a, grid, s, n_main, n_groups, n_window, rows);
+      launch_rep<1, RAGGED, PAGED, S16, MODE, B4>(a, grid, s, n_main, n_groups, n_window, rows);
       break;
     case 2:
-      launch_rep<2, RAGGED, PAGED, S16, MODE>(a, grid, s, n_main, n_groups, n_window, rows);
+      launch_rep<2, RAGGED, PAGED, S16, MODE, B4>(a, grid, s, n_main, n_groups, n_window, rows);
       break;
     default:
-      launch_rep<4, RAGGED, PAGED, S16, MODE>(a, grid, s, n_main, n_groups, n_window, rows);
+      launch_rep<4, RAGGED, PAGED, S16, MODE, B4>(a, grid, s, n_main, n_groups, n_window, rows);
       break;
   }
 }
@@ -1751,6 +1753,20 @@ template <bool RAGGED, int MODE = 0>
 static void launch_reps(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n_main,
                         int n_groups, int n_window, const MatrixRowArg<RAGGED> &rows) {
   const bool s16 = a.L.sb == 2;
+  if constexpr (MODE == 0) {
+    // 4-bit keys and values: any batch, contiguous or paged
+    if (a.kb == 4 && a.vb == 4) {
+      if (a.L.pt && s16)
+        launch_layout<RAGGED, true, true, 0, 4>(a, grid, s, n_main, n_groups, n_window, rows);
+      else if (a.L.pt)
+        launch_layout<RAGGED, true, false, 0, 4>(a, grid, s, n_main, n_groups, n_window, rows);
+      else if (s16)
+        launch_layout<RAGGED, false, true, 0, 4>(a, grid, s, n_main, n_groups, n_window, rows);
+      else
+        launch_layout<RAGGED, false, false, 0, 4>(a, grid, s, n_main, n_groups, n_window, rows);
+      return;
+    }
+  }
   if (a.L.pt) {
     if (s16)
       launch_layout<RAGGED, true, true, MODE>(a, grid, s, n_main, n_groups, n_window, rows);
@@ -1766,7 +1782,7 @@ static void launch_reps(const DecodeArgs &a, dim3 grid, hipStream_t s, int64_t n
 
 hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int n_groups,
                                 hipStream_t s) {
-  const bool four = decode_matrix4_supported(a);
+  const bool four = decode_matrix4_supported(a, false);
   if (!(four || decode_matrix_supported(a)) || a.t <= 0 || n_main < 0 || n_main % kBT != 0 ||
       n_main > a.n_vq || n_groups <= 0)
     return hipErrorInvalidValue;
@@ -1785,9 +1801,10 @@ hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int n_group
   if ((int64_t)n_groups + n_window > a.S_total) return hipErrorInvalidValue;
   const int64_t n_wg = (int64_t)n_groups * a.H * a.B;
   if (n_wg > ((int64_t)1 << 25)) return hipErrorInvalidValue;   // 32-bit workgroup ids
-  if (four && a.L.sb == 2)
+  const bool mixed = four && a.kb != a.vb;
+  if (mixed && a.L.sb == 2)
     launch_widths4<true>(a, dim3((unsigned)n_wg), s, n_main, n_groups, n_window);
-  else if (four)
+  else if (mixed)
     launch_widths4<false>(a, dim3((unsigned)n_wg), s, n_main, n_groups, n_window);
   else
     launch_reps<false>(a, dim3((unsigned)n_wg), s, n_main, n_groups, n_window, NoRows{});
@@ -1836,7 +1853,8 @@ hipError_t launch_selected_matrix(const DecodeArgs &a, int64_t n_main, int n_gro
 
 hipError_t launch_decode_matrix_rows(const DecodeArgs &a, const MatrixRows &rows, int n_shares,
                                      hipStream_t s) {
-  if (!decode_matrix_supported(a) || a.B > kMaxRows || n_shares <= 0 || n_shares > kMaxRows)
+  if (!(decode_matrix_supported(a) || decode_matrix4_supported(a, true)) || a.B > kMaxRows ||
+      n_shares <= 0 || n_shares > kMaxRows)
     return hipErrorInvalidValue;
   if (a.t_new >= 0 && (!a.k_new || !a.v_new)) return hipErrorInvalidValue;
   // every share names a row of the batch and a valid index among the row's

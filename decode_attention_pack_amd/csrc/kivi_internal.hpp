@@ -144,10 +144,11 @@ int decode_matrix_window_chunks(const DecodeArgs &a, int64_t n_main);
 int decode_matrix_waves(const DecodeArgs &a);
 hipError_t launch_decode_matrix(const DecodeArgs &a, int64_t n_main, int n_groups,
                                 hipStream_t s);
-// launch_decode_matrix also takes 4-bit keys, values or both (G = 32, D =
-// 128, 1, 2 or 4 query heads per KV head) of a uniform batch in a contiguous
-// cache, attention and the fused step: decode_matrix4_supported.
-bool decode_matrix4_supported(const DecodeArgs &a);
+// launch_decode_matrix and launch_decode_matrix_rows also take 4-bit codes
+// (G = 32, D = 128, 1, 2 or 4 query heads per KV head), attention and the
+// fused step: 4-bit keys and values in any cache, 4-bit keys or values alone
+// in a contiguous cache of a uniform batch (decode_matrix4_supported).
+bool decode_matrix4_supported(const DecodeArgs &a, bool ragged);
 // Ragged batch: row b attends over t[b] tokens (after the append of a
 // fused step); per KV head, share u of n_shares is workgroup
 // share[u] >> 8 & 4095 of the share[u] >> 20 workgroups of row share[u] &

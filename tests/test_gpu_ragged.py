@@ -74,6 +74,11 @@ def _paths(g, Hq):
     paths = [P.KIVI_PATH_AUTO, P.KIVI_PATH_GENERIC]
     if g.D == 128 and g.G == 32 and (rep == 1 or (rep % 2 == 0 and rep <= 64)) and g.R % 32 == 0:
         paths.append(P.KIVI_PATH_VECTOR)
+    # the matrix kernel forced where it takes the cache: 2-bit, or 4-bit keys
+    # and values (any batch, contiguous or paged), on the shape it serves
+    if (g.D == 128 and g.G == 32 and rep in (1, 2, 4) and (g.kb, g.vb) in ((2, 2), (4, 4))
+            and g.n_tokens > 0):
+        paths.append(P.KIVI_PATH_MATRIX)
     return paths
 
 
