@@ -331,10 +331,14 @@ select_rows_kernel(DecodeArgs a, float tau, SelectRow *rows, int32_t *n_selected
     __syncthreads();
     for (int i = tid; i < n_pad; i += kSThreads) list[i] = 0u;
     __syncthreads();
+    // (the bucket test first: the mass, an exponential, only for the few
+    // tokens in the bucket -- it is zero only in the last, clamped bucket)
     for_scores(sr, t, [&](int i, float s) {
-      if (token_mass(s, m) > 0u && bucket_of(s) == beta) {
-        const uint32_t slot = atomicAdd(&s_u[3], 1u);
-        list[slot] = ((uint64_t)select_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+      if (bucket_of(s) == beta) {
+        if (token_mass(s, m) > 0u) {
+          const uint32_t slot = atomicAdd(&s_u[3], 1u);
+          list[slot] = ((uint64_t)select_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+        }
       }
     });
     __syncthreads();
